@@ -1,0 +1,283 @@
+/*
+ * CPU oracle for single-token decode attention under Sparse Asymmetric
+ * Group-Query Attention (SAGA) with top-N selection.
+ *
+ * TEST INFRASTRUCTURE. Only the tests, the smoke check and the benchmark's
+ * CPU-baseline leg may load this library. It shares no code with the HIP
+ * path: it is a plain, slow, fp64 restatement of the definitions below.
+ *
+ * Source: "More Value per Key: Asymmetric Sparse Attention for Faster LLM
+ * Decoding" (arXiv 2610.04753):
+ *   - scaled dot-product attention, §2.1 Eqs. 2-4;
+ *   - decode with a KV cache (one query row), §2.2 Eq. 5;
+ *   - top-N attention: keep the N largest logits of the row, mask the rest
+ *     before the softmax, §2.5 Eq. 6;
+ *   - attention over the gathered entries, softmax(A[i]) V[i], §3.1 Eq. 7;
+ *   - SAGA: separate key and value head counts h_k <= h_v, §3.2;
+ *   - query head blocks: contiguous blocks of g = h_q / h_kv query heads share
+ *     one key (value) head, App. B Eq. 29 -- so query head i uses key head
+ *     i / (h_q / h_k) and value head i / (h_q / h_v).
+ *
+ * Readings where the pages leave a step open (all exact, no approximation):
+ *   - the threshold is fresh at every step, so exactly N_eff = min(N, L)
+ *     entries are kept (the pages' threshold reuse over n steps is a
+ *     different, history-dependent selector);
+ *   - ranking is on the scaled logits; equal logits are ordered by lower
+ *     position first; -0.0 equals +0.0 (fp64 comparison);
+ *   - N > L keeps all L entries; unused output slots hold index -1 and
+ *     score -inf;
+ *   - positions t >= L (= seq_lens[b]) are never read.
+ *
+ * Precision: inputs are the stored fp32 / bf16 values decoded exactly; all
+ * arithmetic is fp64 with the host libm exp().
+ *
+ * Parity pins live in tests/test_oracle_pins.py (closed forms, library
+ * reductions, brute force); every function below is pinned there.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+enum { ORACLE_F32 = 0, ORACLE_BF16 = 1 };
+
+typedef struct {
+    const void* q;         /* [B][h_q][d] */
+    const void* k;         /* [B][h_k][S_max][d] */
+    const void* v;         /* [B][h_v][S_max][d] */
+    const int32_t* lens;   /* [B] */
+    int B, h_q, h_k, h_v, d;
+    int64_t S_max;
+    int dtype;
+} problem_t;
+
+/* Decode one stored element to fp64 exactly. */
+static double elem(const void* base, int dtype, int64_t i) {
+    if (dtype == ORACLE_F32) return (double)((const float*)base)[i];
+    uint32_t u = (uint32_t)((const uint16_t*)base)[i] << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+}
+
+static int64_t seq_len(const problem_t* P, int b) {
+    int64_t L = P->lens[b];
+    if (L < 0) L = 0;
+    if (L > P->S_max) L = P->S_max;
+    return L;
+}
+
+/* Head mapping of App. B (contiguous query-head blocks). */
+static int key_head(const problem_t* P, int i) { return i / (P->h_q / P->h_k); }
+static int value_head(const problem_t* P, int i) { return i / (P->h_q / P->h_v); }
+
+/* Scaled logit of Eq. 2 for query (b, i) and cached position t. */
+static double logit(const problem_t* P, int b, int i, int64_t t) {
+    int d = P->d;
+    int kh = key_head(P, i);
+    int64_t qo = ((int64_t)b * P->h_q + i) * d;
+    int64_t ko = (((int64_t)b * P->h_k + kh) * P->S_max + t) * d;
+    double acc = 0.0;
+    for (int c = 0; c < d; ++c) acc += elem(P->q, P->dtype, qo + c) * elem(P->k, P->dtype, ko + c);
+    return acc / sqrt((double)d);
+}
+
+typedef struct { double s; int64_t t; } scored_t;
+
+/* Order of Eq. 6 with the tie rule: larger logit first, then lower position. */
+static int by_logit_desc(const void* a, const void* b) {
+    const scored_t* x = (const scored_t*)a;
+    const scored_t* y = (const scored_t*)b;
+    if (x->s > y->s) return -1;
+    if (x->s < y->s) return 1;
+    return (x->t > y->t) - (x->t < y->t);
+}
+
+static int by_pos(const void* a, const void* b) {
+    const scored_t* x = (const scored_t*)a;
+    const scored_t* y = (const scored_t*)b;
+    return (x->t > y->t) - (x->t < y->t);
+}
+
+/*
+ * Steps 4-5 (Eq. 7): softmax over the given entries (sorted by position),
+ * then the weighted sum of their value rows, summed in ascending position.
+ * Writes out[d] and returns sum(p) through psum.
+ */
+static void attend(const problem_t* P, int b, int i, const scored_t* sel, int64_t n,
+                   double* out, double* psum) {
+    int d = P->d;
+    for (int c = 0; c < d; ++c) out[c] = 0.0;
+    *psum = 0.0;
+    if (n <= 0) return;
+    double m = -INFINITY;
+    for (int64_t j = 0; j < n; ++j) if (sel[j].s > m) m = sel[j].s;
+    double z = 0.0;
+    for (int64_t j = 0; j < n; ++j) z += exp(sel[j].s - m);
+    int vh = value_head(P, i);
+    for (int64_t j = 0; j < n; ++j) {
+        double p = exp(sel[j].s - m) / z;
+        *psum += p;
+        int64_t vo = (((int64_t)b * P->h_v + vh) * P->S_max + sel[j].t) * d;
+        for (int c = 0; c < d; ++c) out[c] += p * elem(P->v, P->dtype, vo + c);
+    }
+}
+
+static int check(const problem_t* P) {
+    if (P->B < 1 || P->h_q < 1 || P->h_k < 1 || P->h_v < 1 || P->d < 1 || P->S_max < 1) return -1;
+    if (P->h_q % P->h_k || P->h_q % P->h_v) return -1;
+    if (P->dtype != ORACLE_F32 && P->dtype != ORACLE_BF16) return -1;
+    return 0;
+}
+
+static void pair_of(const problem_t* P, const int64_t* pairs, int64_t j, int* b, int* i) {
+    if (pairs) { *b = (int)pairs[2 * j]; *i = (int)pairs[2 * j + 1]; }
+    else { *b = (int)(j / P->h_q); *i = (int)(j % P->h_q); }
+}
+
+static int set_threads(int nthreads) {
+#ifdef _OPENMP
+    if (nthreads > 0) omp_set_num_threads(nthreads);
+    return omp_get_max_threads();
+#else
+    (void)nthreads;
+    return 1;
+#endif
+}
+
+/*
+ * Top-N decode attention (Eqs. 2, 6, 7) for `npairs` (b, i) pairs (pairs ==
+ * NULL: all B*h_q pairs in b-major order). Per pair:
+ *   out[d]        attention output
+ *   idx[N]        kept positions in ascending order, -1 padded
+ *   sel[N]        their logits, -inf padded
+ *   tN            the N_eff-th largest logit (NaN if L = 0)
+ *   psum          sum of the softmax weights
+ * Returns the thread count used, or -1 on bad arguments.
+ */
+int oracle_topn_attn(const void* q, const void* k, const void* v, const int32_t* lens,
+                     int B, int h_q, int h_k, int h_v, int d, int64_t S_max, int dtype, int N,
+                     const int64_t* pairs, int64_t npairs,
+                     double* out, int32_t* idx, double* sel, double* tN, double* psum,
+                     int nthreads) {
+    problem_t P = {q, k, v, lens, B, h_q, h_k, h_v, d, S_max, dtype};
+    if (check(&P) || N < 1) return -1;
+    if (!pairs) npairs = (int64_t)B * h_q;
+    int used = set_threads(nthreads);
+    int bad = 0;
+    #pragma omp parallel for schedule(dynamic, 1) reduction(|:bad)
+    for (int64_t j = 0; j < npairs; ++j) {
+        int b, i;
+        pair_of(&P, pairs, j, &b, &i);
+        if (b < 0 || b >= B || i < 0 || i >= h_q) { bad = 1; continue; }
+        int64_t L = seq_len(&P, b);
+        int64_t n = L < N ? L : N;
+        scored_t* all = (scored_t*)malloc(sizeof(scored_t) * (size_t)(L > 0 ? L : 1));
+        if (!all) { bad = 1; continue; }
+        for (int64_t t = 0; t < L; ++t) { all[t].s = logit(&P, b, i, t); all[t].t = t; }
+        qsort(all, (size_t)L, sizeof(scored_t), by_logit_desc);
+        tN[j] = n > 0 ? all[n - 1].s : NAN;
+        qsort(all, (size_t)n, sizeof(scored_t), by_pos);
+        for (int64_t r = 0; r < N; ++r) {
+            idx[j * N + r] = r < n ? (int32_t)all[r].t : -1;
+            sel[j * N + r] = r < n ? all[r].s : -INFINITY;
+        }
+        attend(&P, b, i, all, n, out + j * d, psum + j);
+        free(all);
+    }
+    return bad ? -1 : used;
+}
+
+/*
+ * Full decode attention (Eqs. 2-5) over all L positions: no selection step.
+ * Same pair convention as oracle_topn_attn. Returns threads used or -1.
+ */
+int oracle_dense_attn(const void* q, const void* k, const void* v, const int32_t* lens,
+                      int B, int h_q, int h_k, int h_v, int d, int64_t S_max, int dtype,
+                      const int64_t* pairs, int64_t npairs, double* out, int nthreads) {
+    problem_t P = {q, k, v, lens, B, h_q, h_k, h_v, d, S_max, dtype};
+    if (check(&P)) return -1;
+    if (!pairs) npairs = (int64_t)B * h_q;
+    int used = set_threads(nthreads);
+    int bad = 0;
+    #pragma omp parallel for schedule(dynamic, 1) reduction(|:bad)
+    for (int64_t j = 0; j < npairs; ++j) {
+        int b, i;
+        pair_of(&P, pairs, j, &b, &i);
+        if (b < 0 || b >= B || i < 0 || i >= h_q) { bad = 1; continue; }
+        int64_t L = seq_len(&P, b);
+        scored_t* all = (scored_t*)malloc(sizeof(scored_t) * (size_t)(L > 0 ? L : 1));
+        if (!all) { bad = 1; continue; }
+        for (int64_t t = 0; t < L; ++t) { all[t].s = logit(&P, b, i, t); all[t].t = t; }
+        double ps;
+        attend(&P, b, i, all, L, out + j * d, &ps);
+        free(all);
+    }
+    return bad ? -1 : used;
+}
+
+/*
+ * Scaled logits (Eq. 2) for each pair at every position: scores[npairs][S_max],
+ * NaN at t >= L. Returns threads used or -1.
+ */
+int oracle_logits(const void* q, const void* k, const int32_t* lens,
+                  int B, int h_q, int h_k, int d, int64_t S_max, int dtype,
+                  const int64_t* pairs, int64_t npairs, double* scores, int nthreads) {
+    problem_t P = {q, k, NULL, lens, B, h_q, h_k, h_k, d, S_max, dtype};
+    if (check(&P)) return -1;
+    if (!pairs) npairs = (int64_t)B * h_q;
+    int used = set_threads(nthreads);
+    int bad = 0;
+    #pragma omp parallel for schedule(dynamic, 1) reduction(|:bad)
+    for (int64_t j = 0; j < npairs; ++j) {
+        int b, i;
+        pair_of(&P, pairs, j, &b, &i);
+        if (b < 0 || b >= B || i < 0 || i >= h_q) { bad = 1; continue; }
+        int64_t L = seq_len(&P, b);
+        for (int64_t t = 0; t < S_max; ++t)
+            scores[j * S_max + t] = t < L ? logit(&P, b, i, t) : NAN;
+    }
+    return bad ? -1 : used;
+}
+
+/*
+ * Eq. 7 on a caller-supplied index set: idx[npairs][N] (entries < 0 are
+ * ignored; entries must be distinct positions < L). Logits are recomputed
+ * here. Returns threads used, or -1 on bad arguments / out-of-range indices.
+ */
+int oracle_attend_given(const void* q, const void* k, const void* v, const int32_t* lens,
+                        int B, int h_q, int h_k, int h_v, int d, int64_t S_max, int dtype,
+                        int N, const int64_t* pairs, int64_t npairs, const int32_t* idx,
+                        double* out, double* psum, int nthreads) {
+    problem_t P = {q, k, v, lens, B, h_q, h_k, h_v, d, S_max, dtype};
+    if (check(&P) || N < 1) return -1;
+    if (!pairs) npairs = (int64_t)B * h_q;
+    int used = set_threads(nthreads);
+    int bad = 0;
+    #pragma omp parallel for schedule(dynamic, 1) reduction(|:bad)
+    for (int64_t j = 0; j < npairs; ++j) {
+        int b, i;
+        pair_of(&P, pairs, j, &b, &i);
+        if (b < 0 || b >= B || i < 0 || i >= h_q) { bad = 1; continue; }
+        int64_t L = seq_len(&P, b);
+        scored_t* sel = (scored_t*)malloc(sizeof(scored_t) * (size_t)N);
+        if (!sel) { bad = 1; continue; }
+        int64_t n = 0;
+        for (int r = 0; r < N; ++r) {
+            int64_t t = idx[j * N + r];
+            if (t < 0) continue;
+            if (t >= L) { bad = 1; continue; }
+            sel[n].t = t;
+            sel[n].s = logit(&P, b, i, t);
+            ++n;
+        }
+        qsort(sel, (size_t)n, sizeof(scored_t), by_pos);
+        for (int64_t r = 1; r < n; ++r) if (sel[r].t == sel[r - 1].t) bad = 1;
+        attend(&P, b, i, sel, n, out + j * d, psum + j);
+        free(sel);
+    }
+    return bad ? -1 : used;
+}
