@@ -1,0 +1,124 @@
+/*
+ * libsaga -- single-token decode attention under Sparse Asymmetric
+ * Group-Query Attention (SAGA) with top-N selection, for AMD MI355X (gfx950).
+ *
+ * Method: "More Value per Key: Asymmetric Sparse Attention for Faster LLM
+ * Decoding" (arXiv 2610.04753).
+ *   - Query head i of h_q uses key head i / (h_q / h_k) and value head
+ *     i / (h_q / h_v): contiguous query-head blocks (App. B, Eq. 29), with the
+ *     key and value head counts decoupled, h_k <= h_v (§3.2).
+ *   - Logits s_t = <q, K_t> / sqrt(d) over the cached positions (§2.1 Eq. 2,
+ *     §2.2 Eq. 5).
+ *   - Keep the N largest logits of the row (§2.5 Eq. 6); the threshold is the
+ *     N-th largest value, found fresh at every call (§3.1), so exactly
+ *     N_eff = min(N, L) positions are kept, equal logits going to the lower
+ *     position.
+ *   - Softmax over the kept logits only, then the weighted sum of the kept
+ *     value rows (§3.1 Eq. 7; App. C.1).
+ *
+ * Conventions shared by every entry point:
+ *   - All tensor pointers are device pointers owned by the caller. The
+ *     library never allocates, frees or synchronises inside these calls; it
+ *     enqueues kernels on `stream` and returns. It keeps no state between
+ *     calls, so a call sequence can be captured in a HIP graph.
+ *   - Layouts (row-major, innermost dimension last, elements of `dtype`):
+ *       q        [B][h_q][d]
+ *       k_cache  [B][h_k][S_max][d]
+ *       v_cache  [B][h_v][S_max][d]
+ *       seq_lens int32 [B]        cached length L_b of batch row b
+ *       out      float32 [B][h_q][d]
+ *     q, k_cache and v_cache must be 16-byte aligned.
+ *   - Preconditions the host cannot check without a sync: 0 <= seq_lens[b]
+ *     <= S_max (kernels clamp to this range for memory safety; L_b = 0 gives
+ *     out = 0 and no kept index). Positions t >= L_b are never read.
+ *   - Scalar arguments are checked on the host before any HIP call; a bad
+ *     argument returns an error status and enqueues nothing.
+ *   - Results are deterministic: the same inputs give bitwise-equal outputs.
+ */
+#ifndef SAGA_H
+#define SAGA_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    SAGA_OK = 0,
+    SAGA_ERR_INVALID_ARG = -1,  /* null pointer, non-positive size, head counts that do not
+                                   divide h_q, h_k > h_v, unknown dtype, misaligned tensor */
+    SAGA_ERR_UNSUPPORTED = -2,  /* head dimension d other than 64 or 128; h_q / h_v > 64 */
+    SAGA_ERR_WORKSPACE = -3,    /* workspace null or smaller than the size functions return */
+    SAGA_ERR_HIP = -4           /* a kernel launch failed (hipGetLastError) */
+} saga_status;
+
+typedef enum {
+    SAGA_F32 = 0,   /* IEEE float32 inputs */
+    SAGA_BF16 = 1   /* bfloat16 inputs (stored as 16-bit patterns) */
+} saga_dtype;
+
+/*
+ * Bytes of device workspace saga_decode_attn needs for these sizes. Host only,
+ * no HIP call; returns 0 when the arguments are invalid. The workspace holds
+ * the fp32 logit rows, the kept index/logit lists and the per-split partial
+ * sums; it needs no initialisation and is fully rewritten by every call.
+ */
+size_t saga_workspace_size(int B, int h_q, int h_k, int h_v, int d, int N, int64_t S_max,
+                           saga_dtype dtype);
+
+/*
+ * SAGA decode attention with top-N selection (§3.1 Eq. 7 on the §2.5 Eq. 6
+ * set, §3.2 head counts).
+ *   q, k_cache, v_cache, seq_lens, out : as in the layouts above.
+ *   B, h_q, h_k, h_v, d : batch, query/key/value head counts, head dimension.
+ *                         h_q % h_k == 0, h_q % h_v == 0, h_k <= h_v, d in {64, 128}.
+ *   N        : positions kept per query head (N >= 1; N >= L_b keeps all L_b).
+ *   stream   : HIP stream the kernels are enqueued on (0 = null stream).
+ *   S_max    : capacity (stride) of the sequence axis of the caches.
+ *   dtype    : element type of q, k_cache and v_cache.
+ *   workspace, workspace_bytes : device scratch of at least saga_workspace_size(...) bytes,
+ *              256-byte aligned, not used by anything else while the call runs.
+ *   idx_out  : optional (may be NULL) int32 [B][h_q][N]: the kept positions of each query
+ *              head in ascending order; slots past N_eff = min(N, L_b) hold -1.
+ */
+saga_status saga_decode_attn(const void* q, const void* k_cache, const void* v_cache,
+                             const int32_t* seq_lens, float* out,
+                             int B, int h_q, int h_k, int h_v, int d, int N, hipStream_t stream,
+                             int64_t S_max, saga_dtype dtype,
+                             void* workspace, size_t workspace_bytes, int32_t* idx_out);
+
+/* Bytes of device workspace saga_dense_attn needs (host only; 0 on invalid arguments). */
+size_t saga_dense_workspace_size(int B, int h_q, int h_k, int h_v, int d, int64_t S_max,
+                                 saga_dtype dtype);
+
+/*
+ * Full (dense) decode attention over all L_b cached positions (§2.1 Eqs. 2-4,
+ * §2.2 Eq. 5): the GQA baseline when h_k == h_v and "SAGA full" when h_k < h_v
+ * (§5.1). Arguments as for saga_decode_attn, without N and idx_out.
+ */
+saga_status saga_dense_attn(const void* q, const void* k_cache, const void* v_cache,
+                            const int32_t* seq_lens, float* out,
+                            int B, int h_q, int h_k, int h_v, int d, hipStream_t stream,
+                            int64_t S_max, saga_dtype dtype,
+                            void* workspace, size_t workspace_bytes);
+
+/*
+ * The K-scan step alone (§2.1 Eq. 2 with the App. B key-head map): writes the
+ * fp32 logits scores[B][h_q][S_max] for t < L_b; entries t >= L_b are left
+ * untouched. Same argument rules as saga_decode_attn (h_v is not involved).
+ */
+saga_status saga_debug_scores(const void* q, const void* k_cache, const int32_t* seq_lens,
+                              float* scores, int B, int h_q, int h_k, int d, hipStream_t stream,
+                              int64_t S_max, saga_dtype dtype);
+
+/* Static English text for a status code (never NULL). */
+const char* saga_status_string(saga_status s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SAGA_H */

@@ -1,0 +1,13 @@
+"""libsaga: SAGA top-N decode attention for AMD MI355X (gfx950).
+
+The C ABI (include/saga.h) is bound 1:1 by `_binding` (same names); `tensors`
+adds torch-tensor convenience wrappers. Importing fails if libsaga.so has not
+been built: there is no CPU or eager fallback.
+"""
+from ._binding import (  # noqa: F401
+    EXPORTS, LIB_PATH, SAGA_BF16, SAGA_ERR_HIP, SAGA_ERR_INVALID_ARG, SAGA_ERR_UNSUPPORTED,
+    SAGA_ERR_WORKSPACE, SAGA_F32, SAGA_OK, SagaError, lib, saga_debug_scores, saga_decode_attn,
+    saga_dense_attn, saga_dense_workspace_size, saga_status_string, saga_workspace_size,
+    status_string)
+from .tensors import (  # noqa: F401
+    debug_scores, decode_attn, dense_attn, dense_workspace_size, new_workspace, workspace_size)

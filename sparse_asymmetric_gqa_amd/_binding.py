@@ -1,0 +1,100 @@
+"""ctypes binding of libsaga (argument marshalling only).
+
+The functions named like the C entry points take the same arguments, with
+device pointers given as ints (or torch tensors, whose data_ptr() is used)
+and the stream as an int handle. Every step of the computation runs in the
+HIP kernels of libsaga.so; there is no fallback: if the library is missing
+the import fails.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libsaga.so")
+
+SAGA_OK = 0
+SAGA_ERR_INVALID_ARG = -1
+SAGA_ERR_UNSUPPORTED = -2
+SAGA_ERR_WORKSPACE = -3
+SAGA_ERR_HIP = -4
+SAGA_F32 = 0
+SAGA_BF16 = 1
+
+EXPORTS = ("saga_workspace_size", "saga_decode_attn", "saga_dense_workspace_size",
+           "saga_dense_attn", "saga_debug_scores", "saga_status_string")
+
+
+class SagaError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {status_string(status)} ({status})")
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run sparse_asymmetric_gqa_amd/build.py "
+                          "(or __graft_entry__.build()) first")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i, i64, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t
+    lib.saga_workspace_size.argtypes = [i, i, i, i, i, i, i64, i]
+    lib.saga_workspace_size.restype = sz
+    lib.saga_dense_workspace_size.argtypes = [i, i, i, i, i, i64, i]
+    lib.saga_dense_workspace_size.restype = sz
+    lib.saga_decode_attn.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, vp, i64, i, vp, sz, vp]
+    lib.saga_decode_attn.restype = i
+    lib.saga_dense_attn.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, vp, i64, i, vp, sz]
+    lib.saga_dense_attn.restype = i
+    lib.saga_debug_scores.argtypes = [vp, vp, vp, vp, i, i, i, i, vp, i64, i]
+    lib.saga_debug_scores.restype = i
+    lib.saga_status_string.argtypes = [i]
+    lib.saga_status_string.restype = ctypes.c_char_p
+    return lib
+
+
+lib = _load()
+
+
+def _ptr(x):
+    if x is None:
+        return None
+    if hasattr(x, "data_ptr"):
+        return ctypes.c_void_p(x.data_ptr())
+    return ctypes.c_void_p(int(x))
+
+
+def status_string(status: int) -> str:
+    return lib.saga_status_string(int(status)).decode()
+
+
+def saga_status_string(status: int) -> str:
+    return status_string(status)
+
+
+def saga_workspace_size(B, h_q, h_k, h_v, d, N, S_max, dtype) -> int:
+    return int(lib.saga_workspace_size(B, h_q, h_k, h_v, d, N, S_max, dtype))
+
+
+def saga_dense_workspace_size(B, h_q, h_k, h_v, d, S_max, dtype) -> int:
+    return int(lib.saga_dense_workspace_size(B, h_q, h_k, h_v, d, S_max, dtype))
+
+
+def saga_decode_attn(q, k_cache, v_cache, seq_lens, out, B, h_q, h_k, h_v, d, N, stream,
+                     S_max, dtype, workspace, workspace_bytes, idx_out=None) -> int:
+    return int(lib.saga_decode_attn(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seq_lens),
+                                    _ptr(out), B, h_q, h_k, h_v, d, N, _ptr(stream), S_max,
+                                    dtype, _ptr(workspace), workspace_bytes, _ptr(idx_out)))
+
+
+def saga_dense_attn(q, k_cache, v_cache, seq_lens, out, B, h_q, h_k, h_v, d, stream, S_max,
+                    dtype, workspace, workspace_bytes) -> int:
+    return int(lib.saga_dense_attn(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seq_lens),
+                                   _ptr(out), B, h_q, h_k, h_v, d, _ptr(stream), S_max, dtype,
+                                   _ptr(workspace), workspace_bytes))
+
+
+def saga_debug_scores(q, k_cache, seq_lens, scores, B, h_q, h_k, d, stream, S_max,
+                      dtype) -> int:
+    return int(lib.saga_debug_scores(_ptr(q), _ptr(k_cache), _ptr(seq_lens), _ptr(scores), B,
+                                     h_q, h_k, d, _ptr(stream), S_max, dtype))

@@ -1,0 +1,159 @@
+// C ABI of libsaga: argument checks, workspace layout and the launch sequence.
+//
+// saga_decode_attn enqueues, on the caller's stream and without allocating:
+//   K-scan (logits, Eq. 2) -> top-N select (Eq. 6) -> sparse PV splits (Eq. 7)
+//   -> log-sum-exp merge.
+// saga_dense_attn enqueues K-scan -> dense PV splits -> merge (Eqs. 2-4).
+#include "saga.h"
+#include "saga_internal.h"
+
+#include <stdint.h>
+
+namespace saga {
+
+static size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+
+Workspace carve(void* base, int B, int h_q, int d, int N, int64_t S_max, bool dense) {
+    Workspace w{};
+    char* p = static_cast<char*>(base);
+    size_t off = 0;
+    const size_t rows = (size_t)B * (size_t)h_q;
+    auto take = [&](size_t bytes) -> char* {
+        char* r = p ? p + off : nullptr;
+        off += align256(bytes);
+        return r;
+    };
+    w.scores = reinterpret_cast<float*>(take(rows * (size_t)score_stride(S_max) * sizeof(float)));
+    int nsplit;
+    if (!dense) {
+        w.sel_idx = reinterpret_cast<int32_t*>(take(rows * (size_t)N * sizeof(int32_t)));
+        w.sel_val = reinterpret_cast<float*>(take(rows * (size_t)N * sizeof(float)));
+        w.row_max = reinterpret_cast<float*>(take(rows * sizeof(float)));
+        w.row_cnt = reinterpret_cast<int32_t*>(take(rows * sizeof(int32_t)));
+        nsplit = sparse_nsplit(N);
+    } else {
+        nsplit = dense_nsplit(S_max);
+    }
+    w.part = reinterpret_cast<float*>(take(rows * (size_t)nsplit * (size_t)(d + 2) * sizeof(float)));
+    w.bytes = off;
+    return w;
+}
+
+}  // namespace saga
+
+namespace {
+
+using saga::kMaxHeadGroup;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Scalar checks shared by all entry points (no HIP call).
+saga_status check_shape(int B, int h_q, int h_k, int h_v, int d, int64_t S_max, int dtype) {
+    if (B < 1 || h_q < 1 || h_k < 1 || h_v < 1 || S_max < 1) return SAGA_ERR_INVALID_ARG;
+    if (h_q % h_k != 0 || h_q % h_v != 0 || h_k > h_v) return SAGA_ERR_INVALID_ARG;
+    if (dtype != SAGA_F32 && dtype != SAGA_BF16) return SAGA_ERR_INVALID_ARG;
+    if (d != 64 && d != 128) return SAGA_ERR_UNSUPPORTED;
+    if (h_q / h_k > kMaxHeadGroup || h_q / h_v > kMaxHeadGroup) return SAGA_ERR_UNSUPPORTED;
+    // index arithmetic inside the kernels is 32-bit over rows and positions
+    if (S_max > (int64_t)INT32_MAX / 2 || (int64_t)B * h_q > (int64_t)INT32_MAX / 64)
+        return SAGA_ERR_UNSUPPORTED;
+    return SAGA_OK;
+}
+
+saga_status from_hip(hipError_t e) { return e == hipSuccess ? SAGA_OK : SAGA_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+size_t saga_workspace_size(int B, int h_q, int h_k, int h_v, int d, int N, int64_t S_max,
+                           saga_dtype dtype) {
+    if (check_shape(B, h_q, h_k, h_v, d, S_max, dtype) != SAGA_OK || N < 1) return 0;
+    return saga::carve(nullptr, B, h_q, d, N, S_max, false).bytes;
+}
+
+size_t saga_dense_workspace_size(int B, int h_q, int h_k, int h_v, int d, int64_t S_max,
+                                 saga_dtype dtype) {
+    if (check_shape(B, h_q, h_k, h_v, d, S_max, dtype) != SAGA_OK) return 0;
+    return saga::carve(nullptr, B, h_q, d, 1, S_max, true).bytes;
+}
+
+saga_status saga_decode_attn(const void* q, const void* k_cache, const void* v_cache,
+                             const int32_t* seq_lens, float* out,
+                             int B, int h_q, int h_k, int h_v, int d, int N, hipStream_t stream,
+                             int64_t S_max, saga_dtype dtype,
+                             void* workspace, size_t workspace_bytes, int32_t* idx_out) {
+    if (!q || !k_cache || !v_cache || !seq_lens || !out) return SAGA_ERR_INVALID_ARG;
+    saga_status s = check_shape(B, h_q, h_k, h_v, d, S_max, dtype);
+    if (s != SAGA_OK) return s;
+    if (N < 1) return SAGA_ERR_INVALID_ARG;
+    if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache)) return SAGA_ERR_INVALID_ARG;
+    const saga::Workspace need = saga::carve(nullptr, B, h_q, d, N, S_max, false);
+    if (!workspace || workspace_bytes < need.bytes || (reinterpret_cast<uintptr_t>(workspace) & 255u))
+        return SAGA_ERR_WORKSPACE;
+    const saga::Workspace w = saga::carve(workspace, B, h_q, d, N, S_max, false);
+    const bool bf16 = dtype == SAGA_BF16;
+    const int64_t ss = saga::score_stride(S_max);
+
+    s = from_hip(saga::launch_kscan(q, k_cache, seq_lens, w.scores, ss, B, h_q, h_k, d, S_max,
+                                    bf16, stream));
+    if (s != SAGA_OK) return s;
+    s = from_hip(saga::launch_select(w.scores, ss, seq_lens, B, h_q, N, S_max, w.sel_idx,
+                                     w.sel_val, w.row_max, w.row_cnt, idx_out, stream));
+    if (s != SAGA_OK) return s;
+    s = from_hip(saga::launch_pv_sparse(v_cache, w.sel_idx, w.sel_val, w.row_max, w.row_cnt,
+                                        w.part, B, h_q, h_v, d, N, S_max, bf16, stream));
+    if (s != SAGA_OK) return s;
+    return from_hip(saga::launch_merge(w.part, saga::sparse_nsplit(N), saga::kPvEntries,
+                                       w.row_cnt, seq_lens, S_max, out, B, h_q, d, stream));
+}
+
+saga_status saga_dense_attn(const void* q, const void* k_cache, const void* v_cache,
+                            const int32_t* seq_lens, float* out,
+                            int B, int h_q, int h_k, int h_v, int d, hipStream_t stream,
+                            int64_t S_max, saga_dtype dtype,
+                            void* workspace, size_t workspace_bytes) {
+    if (!q || !k_cache || !v_cache || !seq_lens || !out) return SAGA_ERR_INVALID_ARG;
+    saga_status s = check_shape(B, h_q, h_k, h_v, d, S_max, dtype);
+    if (s != SAGA_OK) return s;
+    if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache)) return SAGA_ERR_INVALID_ARG;
+    const saga::Workspace need = saga::carve(nullptr, B, h_q, d, 1, S_max, true);
+    if (!workspace || workspace_bytes < need.bytes || (reinterpret_cast<uintptr_t>(workspace) & 255u))
+        return SAGA_ERR_WORKSPACE;
+    const saga::Workspace w = saga::carve(workspace, B, h_q, d, 1, S_max, true);
+    const bool bf16 = dtype == SAGA_BF16;
+    const int64_t ss = saga::score_stride(S_max);
+
+    s = from_hip(saga::launch_kscan(q, k_cache, seq_lens, w.scores, ss, B, h_q, h_k, d, S_max,
+                                    bf16, stream));
+    if (s != SAGA_OK) return s;
+    s = from_hip(saga::launch_pv_dense(v_cache, w.scores, ss, seq_lens, w.part, B, h_q, h_v, d,
+                                       S_max, bf16, stream));
+    if (s != SAGA_OK) return s;
+    return from_hip(saga::launch_merge(w.part, saga::dense_nsplit(S_max), saga::kDenseRows,
+                                       nullptr, seq_lens, S_max, out, B, h_q, d, stream));
+}
+
+saga_status saga_debug_scores(const void* q, const void* k_cache, const int32_t* seq_lens,
+                              float* scores, int B, int h_q, int h_k, int d, hipStream_t stream,
+                              int64_t S_max, saga_dtype dtype) {
+    if (!q || !k_cache || !seq_lens || !scores) return SAGA_ERR_INVALID_ARG;
+    saga_status s = check_shape(B, h_q, h_k, h_k, d, S_max, dtype);
+    if (s != SAGA_OK) return s;
+    if (!aligned16(q) || !aligned16(k_cache)) return SAGA_ERR_INVALID_ARG;
+    return from_hip(saga::launch_kscan(q, k_cache, seq_lens, scores, S_max, B, h_q, h_k, d,
+                                       S_max, dtype == SAGA_BF16, stream));
+}
+
+const char* saga_status_string(saga_status s) {
+    switch (s) {
+        case SAGA_OK: return "ok";
+        case SAGA_ERR_INVALID_ARG: return "invalid argument";
+        case SAGA_ERR_UNSUPPORTED: return "unsupported shape (d must be 64 or 128; head groups <= 64)";
+        case SAGA_ERR_WORKSPACE: return "workspace missing, too small or not 256-byte aligned";
+        case SAGA_ERR_HIP: return "HIP launch failure";
+    }
+    return "unknown status";
+}
+
+}  // extern "C"

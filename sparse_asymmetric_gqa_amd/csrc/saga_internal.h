@@ -1,0 +1,104 @@
+// Internal declarations shared by the libsaga translation units (HIP, gfx950).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace saga {
+
+// ---- launch geometry (also used by the workspace-size functions) ----------
+constexpr int kScanChunk = 1024;     // positions per K-scan workgroup
+constexpr int kPvEntries = 256;      // kept entries per sparse PV workgroup
+constexpr int kDenseRows = 512;      // positions per dense PV workgroup
+constexpr int kSelectThreads = 1024; // threads of one select workgroup
+constexpr int kMaxHeadGroup = 64;    // largest h_q / h_k and h_q / h_v supported
+
+inline int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
+
+// Row stride (floats) of the logit workspace: padded so rows start 64-byte aligned.
+inline int64_t score_stride(int64_t S_max) { return round_up(S_max, 16); }
+
+struct Workspace {
+    float* scores;      // [B][h_q][score_stride]
+    int32_t* sel_idx;   // [B][h_q][N]
+    float* sel_val;     // [B][h_q][N]
+    float* row_max;     // [B][h_q]   largest kept logit
+    int32_t* row_cnt;   // [B][h_q]   N_eff
+    float* part;        // [B][h_q][nsplit][d + 2]  (m, l, acc[d])
+    size_t bytes;
+};
+
+// Carve the decode workspace (dense == false) or the dense one out of `base`
+// (base may be null to only compute the size).
+Workspace carve(void* base, int B, int h_q, int d, int N, int64_t S_max, bool dense);
+
+// number of partial-sum splits per (b, i) row
+int sparse_nsplit(int N);          // ceil(N / kPvEntries)
+int dense_nsplit(int64_t S_max);   // ceil(S_max / kDenseRows)
+
+// ---- launchers (defined next to their kernels) ------------------------------
+// All return hipGetLastError() after enqueueing.
+hipError_t launch_kscan(const void* q, const void* k, const int32_t* lens, float* scores,
+                        int64_t s_stride, int B, int h_q, int h_k, int d, int64_t S_max,
+                        bool bf16, hipStream_t st);
+
+hipError_t launch_select(const float* scores, int64_t s_stride, const int32_t* lens, int B,
+                         int h_q, int N, int64_t S_max, int32_t* sel_idx, float* sel_val,
+                         float* row_max, int32_t* row_cnt, int32_t* idx_out, hipStream_t st);
+
+hipError_t launch_pv_sparse(const void* v, const int32_t* sel_idx, const float* sel_val,
+                            const float* row_max, const int32_t* row_cnt, float* part, int B,
+                            int h_q, int h_v, int d, int N, int64_t S_max, bool bf16,
+                            hipStream_t st);
+
+hipError_t launch_pv_dense(const void* v, const float* scores, int64_t s_stride,
+                           const int32_t* lens, float* part, int B, int h_q, int h_v, int d,
+                           int64_t S_max, bool bf16, hipStream_t st);
+
+// Log-sum-exp merge of the split partials into out[B][h_q][d]. Split s of row
+// (b, i) is live when s * unit < count, count = row_cnt[b*h_q+i] if row_cnt is
+// given, else lens[b] clamped to [0, S_max].
+hipError_t launch_merge(const float* part, int nsplit, int unit, const int32_t* row_cnt,
+                        const int32_t* lens, int64_t S_max, float* out, int B, int h_q, int d,
+                        hipStream_t st);
+
+}  // namespace saga
+
+// ---- device helpers ---------------------------------------------------------
+#ifdef __HIPCC__
+namespace saga {
+namespace dev {
+
+typedef short bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ inline int64_t clamp_len(int32_t L, int64_t S_max) {
+    int64_t x = L;
+    return x < 0 ? 0 : (x > S_max ? S_max : x);
+}
+
+// Order-preserving map fp32 -> uint32 (larger float <=> larger key); -0.0 is
+// folded onto +0.0 first so the two compare equal.
+__device__ inline uint32_t float_key(float f) {
+    uint32_t u = __float_as_uint(f);
+    if (u == 0x80000000u) u = 0u;
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ inline float key_float(uint32_t k) {
+    uint32_t u = (k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k;
+    return __uint_as_float(u);
+}
+
+// popcount of the bits of a 64-lane mask that belong to lanes below this one
+__device__ inline uint32_t lanes_below(uint64_t m) {
+    return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                     __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
+
+__device__ inline uint64_t ballot(bool p) { return __ballot(p); }
+
+}  // namespace dev
+}  // namespace saga
+#endif

@@ -1,0 +1,114 @@
+"""Tensor-level wrappers over the libsaga C ABI.
+
+PyTorch supplies device memory and the current HIP stream; shapes and the
+dtype are read from the tensors and passed to the C entry points unchanged.
+These wrappers allocate the output and the workspace when the caller does
+not pass them (outside libsaga, which itself never allocates).
+"""
+from __future__ import annotations
+
+import torch
+
+from . import _binding as C
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return C.SAGA_F32
+    if t.dtype == torch.bfloat16:
+        return C.SAGA_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}; use float32 or bfloat16")
+
+
+def _shapes(q, k_cache, v_cache, seq_lens):
+    for name, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache), ("seq_lens", seq_lens)):
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a device tensor")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if seq_lens.dtype != torch.int32:
+        raise TypeError("seq_lens must be int32")
+    B, h_q, d = q.shape
+    kb, h_k, S_max, kd = k_cache.shape
+    if kb != B or kd != d:
+        raise ValueError("k_cache must be [B][h_k][S_max][d]")
+    h_v = h_k
+    if v_cache is not None:
+        vb, h_v, vS, vd = v_cache.shape
+        if vb != B or vS != S_max or vd != d:
+            raise ValueError("v_cache must be [B][h_v][S_max][d]")
+        if v_cache.dtype != q.dtype:
+            raise TypeError("q, k_cache and v_cache must share one dtype")
+    if k_cache.dtype != q.dtype:
+        raise TypeError("q, k_cache and v_cache must share one dtype")
+    if tuple(seq_lens.shape) != (B,):
+        raise ValueError("seq_lens must be [B]")
+    return B, h_q, h_k, h_v, d, S_max
+
+
+def _stream(stream):
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return getattr(stream, "cuda_stream", stream)
+
+
+def workspace_size(q, k_cache, v_cache, seq_lens, N) -> int:
+    B, h_q, h_k, h_v, d, S = _shapes(q, k_cache, v_cache, seq_lens)
+    return C.saga_workspace_size(B, h_q, h_k, h_v, d, N, S, _dtype_code(q))
+
+
+def dense_workspace_size(q, k_cache, v_cache, seq_lens) -> int:
+    B, h_q, h_k, h_v, d, S = _shapes(q, k_cache, v_cache, seq_lens)
+    return C.saga_dense_workspace_size(B, h_q, h_k, h_v, d, S, _dtype_code(q))
+
+
+def new_workspace(nbytes: int, device) -> torch.Tensor:
+    # torch's caching allocator hands out blocks aligned well beyond 256 bytes
+    return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
+
+
+def decode_attn(q, k_cache, v_cache, seq_lens, N, *, out=None, workspace=None, idx_out=None,
+                stream=None):
+    """SAGA top-N decode attention; returns out (float32 [B][h_q][d])."""
+    B, h_q, h_k, h_v, d, S = _shapes(q, k_cache, v_cache, seq_lens)
+    dt = _dtype_code(q)
+    need = C.saga_workspace_size(B, h_q, h_k, h_v, d, N, S, dt)
+    if workspace is None:
+        workspace = new_workspace(need, q.device)
+    if out is None:
+        out = torch.empty((B, h_q, d), dtype=torch.float32, device=q.device)
+    st = C.saga_decode_attn(q, k_cache, v_cache, seq_lens, out, B, h_q, h_k, h_v, d, N,
+                            _stream(stream), S, dt, workspace, workspace.numel(), idx_out)
+    if st != C.SAGA_OK:
+        raise C.SagaError(st, "saga_decode_attn")
+    return out
+
+
+def dense_attn(q, k_cache, v_cache, seq_lens, *, out=None, workspace=None, stream=None):
+    """Full decode attention (GQA when h_k == h_v, SAGA-full when h_k < h_v)."""
+    B, h_q, h_k, h_v, d, S = _shapes(q, k_cache, v_cache, seq_lens)
+    dt = _dtype_code(q)
+    need = C.saga_dense_workspace_size(B, h_q, h_k, h_v, d, S, dt)
+    if workspace is None:
+        workspace = new_workspace(need, q.device)
+    if out is None:
+        out = torch.empty((B, h_q, d), dtype=torch.float32, device=q.device)
+    st = C.saga_dense_attn(q, k_cache, v_cache, seq_lens, out, B, h_q, h_k, h_v, d,
+                           _stream(stream), S, dt, workspace, workspace.numel())
+    if st != C.SAGA_OK:
+        raise C.SagaError(st, "saga_dense_attn")
+    return out
+
+
+def debug_scores(q, k_cache, seq_lens, *, out=None, stream=None):
+    """fp32 logits [B][h_q][S_max] from the K-scan kernel alone (t >= L_b untouched)."""
+    B, h_q, h_k, _, d, S = _shapes(q, k_cache, None, seq_lens)
+    if out is None:
+        out = torch.full((B, h_q, S), float("nan"), dtype=torch.float32, device=q.device)
+    st = C.saga_debug_scores(q, k_cache, seq_lens, out, B, h_q, h_k, d, _stream(stream), S,
+                             _dtype_code(q))
+    if st != C.SAGA_OK:
+        raise C.SagaError(st, "saga_debug_scores")
+    return out

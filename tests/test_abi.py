@@ -1,0 +1,109 @@
+"""C-ABI checks that need no GPU.
+
+libsaga.so must load without a device, export every function include/saga.h
+declares, and reject every invalid scalar argument with its status code on
+the host, before any HIP call (so these run on a machine with no GPU).
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "saga.h")
+
+saga = pytest.importorskip("sparse_asymmetric_gqa_amd")
+
+FAKE = 0x10000   # a 16-byte-aligned non-null "device pointer" never dereferenced here
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(saga_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_match_header():
+    declared = _declared_functions()
+    assert set(declared) == set(saga.EXPORTS)
+    lib = ctypes.CDLL(saga.LIB_PATH)
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+def test_status_strings():
+    for code in (0, -1, -2, -3, -4):
+        s = saga.status_string(code)
+        assert s and s != "unknown status"
+    assert saga.status_string(7) == "unknown status"
+
+
+def _decode(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, lens=FAKE, out=FAKE, B=2, h_q=8, h_k=2, h_v=4, d=64, N=16,
+             stream=None, S=100, dt=saga.SAGA_BF16, ws=FAKE * 16, wsb=1 << 40, idx=None)
+    a.update(kw)
+    return saga.saga_decode_attn(a["q"], a["k"], a["v"], a["lens"], a["out"], a["B"], a["h_q"],
+                                 a["h_k"], a["h_v"], a["d"], a["N"], a["stream"], a["S"], a["dt"],
+                                 a["ws"], a["wsb"], a["idx"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), saga.SAGA_ERR_INVALID_ARG),
+    (dict(k=None), saga.SAGA_ERR_INVALID_ARG),
+    (dict(v=None), saga.SAGA_ERR_INVALID_ARG),
+    (dict(lens=None), saga.SAGA_ERR_INVALID_ARG),
+    (dict(out=None), saga.SAGA_ERR_INVALID_ARG),
+    (dict(B=0), saga.SAGA_ERR_INVALID_ARG),
+    (dict(h_q=0), saga.SAGA_ERR_INVALID_ARG),
+    (dict(N=0), saga.SAGA_ERR_INVALID_ARG),
+    (dict(S=0), saga.SAGA_ERR_INVALID_ARG),
+    (dict(h_q=9), saga.SAGA_ERR_INVALID_ARG),          # 9 % 2 != 0
+    (dict(h_v=3), saga.SAGA_ERR_INVALID_ARG),          # 8 % 3 != 0
+    (dict(h_k=8, h_v=4), saga.SAGA_ERR_INVALID_ARG),   # h_k > h_v
+    (dict(dt=5), saga.SAGA_ERR_INVALID_ARG),
+    (dict(q=FAKE + 2), saga.SAGA_ERR_INVALID_ARG),     # misaligned
+    (dict(d=96), saga.SAGA_ERR_UNSUPPORTED),
+    (dict(d=256), saga.SAGA_ERR_UNSUPPORTED),
+    (dict(h_q=128, h_k=1, h_v=128), saga.SAGA_ERR_UNSUPPORTED),   # key group of 128
+    (dict(ws=None), saga.SAGA_ERR_WORKSPACE),
+    (dict(wsb=1024), saga.SAGA_ERR_WORKSPACE),
+    (dict(ws=FAKE * 16 + 16), saga.SAGA_ERR_WORKSPACE),  # not 256-byte aligned
+])
+def test_decode_rejects_bad_arguments_on_host(kw, code):
+    assert _decode(**kw) == code
+
+
+def test_dense_and_debug_reject_bad_arguments_on_host():
+    d = saga.saga_dense_attn
+    ok = dict(B=2, h_q=8, h_k=2, h_v=4, d=64, S=100)
+    assert d(None, FAKE, FAKE, FAKE, FAKE, 2, 8, 2, 4, 64, None, 100, 1, FAKE * 16, 1 << 40) == -1
+    assert d(FAKE, FAKE, FAKE, FAKE, FAKE, 2, 8, 4, 2, 64, None, 100, 1, FAKE * 16, 1 << 40) == -1
+    assert d(FAKE, FAKE, FAKE, FAKE, FAKE, 2, 8, 2, 4, 80, None, 100, 1, FAKE * 16, 1 << 40) == -2
+    assert d(FAKE, FAKE, FAKE, FAKE, FAKE, 2, 8, 2, 4, 64, None, 100, 1, FAKE * 16, 64) == -3
+    s = saga.saga_debug_scores
+    assert s(FAKE, FAKE, FAKE, None, 2, 8, 2, 64, None, 100, 1) == -1
+    assert s(FAKE, FAKE, FAKE, FAKE, 2, 8, 3, 64, None, 100, 1) == -1
+    assert s(FAKE, FAKE, FAKE, FAKE, 2, 8, 2, 32, None, 100, 1) == -2
+    assert ok
+
+
+def test_workspace_sizes():
+    ws = saga.saga_workspace_size
+    assert ws(2, 8, 2, 4, 64, 16, 100, 1) > 0
+    assert ws(2, 8, 2, 4, 64, 0, 100, 1) == 0
+    assert ws(2, 8, 2, 4, 48, 16, 100, 1) == 0
+    assert ws(2, 8, 4, 2, 64, 16, 100, 1) == 0
+    for args in [(1, 4, 1, 2, 64, 64, 1024, 0), (64, 12, 1, 2, 128, 1024, 32768, 1),
+                 (8, 32, 4, 8, 64, 512, 8192, 1), (3, 6, 2, 2, 128, 7, 33, 1)]:
+        n = ws(*args)
+        assert n % 256 == 0
+        B, h_q, _, _, d, N, S, _ = args
+        # at least the fp32 logit rows, the kept lists and one partial per row
+        assert n >= B * h_q * (4 * S + 8 * N + 4 * (d + 2))
+        # growing any size never shrinks the workspace
+        assert ws(B, h_q, args[2], args[3], d, N + 300, S, 1) >= n
+        assert ws(B, h_q, args[2], args[3], d, N, S + 5000, 1) >= n
+    dw = saga.saga_dense_workspace_size
+    assert dw(64, 12, 2, 2, 128, 32768, 1) >= 64 * 12 * 32768 * 4
+    assert dw(1, 4, 1, 2, 72, 10, 1) == 0

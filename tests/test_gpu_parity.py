@@ -1,0 +1,223 @@
+"""GPU parity: libsaga (HIP, gfx950) against the fp64 CPU oracle.
+
+Every call goes through the C ABI (sparse_asymmetric_gqa_amd._binding via the
+tensor wrappers). Index sets must match the oracle exactly apart from
+near-threshold ties (see parity_helpers); outputs must be within 2e-3 (bf16
+inputs) or 1e-5 (fp32 inputs) of the oracle on the GPU's own kept set.
+The five workloads run at their full sizes; the largest is compared on a
+sample of (b, i) pairs in the same launch configuration the benchmark times.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from parity_helpers import (all_pairs, check_index_sets, check_outputs, sample_pairs,
+                            to_device, tol_for)
+
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():
+    pytest.skip("no GPU", allow_module_level=True)
+
+import sparse_asymmetric_gqa_amd as saga  # noqa: E402  (fails loudly if not built)
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+def _run_decode(x, dx, case, N, pairs, label):
+    _say(f"[decode] {label}: B={case.B} h_q={case.h_q} h_k={case.h_k} h_v={case.h_v} "
+         f"d={case.d} S={case.S_max} N={N} {case.dtype}")
+    idx = torch.empty((case.B, case.h_q, N), dtype=torch.int32, device="cuda")
+    out = saga.decode_attn(dx["q"], dx["k"], dx["v"], dx["seq_lens"], N, idx_out=idx)
+    torch.cuda.synchronize()
+    rows = [b * case.h_q + i for b, i in pairs]
+    g_idx = idx.reshape(-1, N).cpu().numpy()[rows]
+    g_out = out.reshape(-1, case.d).cpu().numpy()[rows]
+    ref = oracle.topn_attn(x["q"], x["k"], x["v"], x["seq_lens"], N, pairs=pairs)
+    nbad, ndiff = check_index_sets(g_idx, ref, x, pairs, N)
+    err = check_outputs(g_out, g_idx, x, pairs, tol_for(case.dtype))
+    if nbad == 0:
+        err2 = np.abs(g_out - ref["out"]).max()
+        assert err2 <= tol_for(case.dtype), err2
+    _say(f"    rows={len(pairs)} differing-rows={nbad} sym-diff={ndiff} max|err|={err:.2e}")
+    return g_idx, g_out
+
+
+WORKLOADS = ["tiny_fp32", "llama32_1b_8to4", "qwen25_1p5b_2to1_ragged", "smollm2_360m_1x8",
+             "qwen25_1p5b_b64_32k"]
+
+
+@pytest.mark.parametrize("name", WORKLOADS)
+def test_decode_workloads(name):
+    case = synth.CASES[name]
+    x = synth.make_inputs(case)
+    dx = to_device(x)
+    Ns = synth.SMOLLM_N_SWEEP if name == "smollm2_360m_1x8" else (case.N,)
+    big = name == "qwen25_1p5b_b64_32k"
+    pairs = sample_pairs(case.B, case.h_q, 64, seed=5) if big else all_pairs(case.B, case.h_q)
+    for N in Ns:
+        _run_decode(x, dx, case, N, pairs, name)
+
+
+@pytest.mark.parametrize("name", list(synth.DENSE_BASELINES))
+def test_dense_baselines(name):
+    base = synth.CASES[name]
+    for (hk, hv) in synth.DENSE_BASELINES[name]:
+        case = base.with_heads(hk, hv, seed=100 + base.seed)
+        _say(f"[dense] {name} ({hk},{hv})")
+        x = synth.make_inputs(case)
+        dx = to_device(x)
+        out = saga.dense_attn(dx["q"], dx["k"], dx["v"], dx["seq_lens"])
+        torch.cuda.synchronize()
+        big = case.B * case.h_q * case.S_max > 8_000_000
+        pairs = (sample_pairs(case.B, case.h_q, 48, seed=7) if big
+                 else all_pairs(case.B, case.h_q))
+        rows = [b * case.h_q + i for b, i in pairs]
+        ref, _ = oracle.dense_attn(x["q"], x["k"], x["v"], x["seq_lens"], pairs=pairs)
+        err = np.abs(out.reshape(-1, case.d).cpu().numpy()[rows] - ref).max()
+        _say(f"    rows={len(pairs)} max|err|={err:.2e}")
+        assert err <= tol_for(case.dtype)
+        del dx
+        torch.cuda.empty_cache()
+
+
+SMALL = [
+    # (B, h_q, h_k, h_v, d, S_max, N, dtype, ragged)
+    (2, 8, 2, 4, 64, 1030, 100, "bf16", True),
+    (2, 8, 2, 4, 128, 1030, 100, "f32", True),
+    (1, 4, 1, 2, 64, 777, 64, "f32", False),
+    (3, 12, 1, 2, 128, 2049, 300, "bf16", True),
+    (2, 6, 2, 2, 64, 513, 37, "bf16", False),       # h_k == h_v (GQA)
+    (1, 64, 1, 2, 64, 600, 50, "bf16", False),      # key group of 64, value group of 32
+    (2, 32, 2, 32, 128, 300, 16, "bf16", False),    # g_v = 1
+    (1, 16, 1, 8, 64, 4100, 1000, "bf16", False),   # select tile KPT=8
+]
+
+
+@pytest.mark.parametrize("shape", SMALL)
+def test_decode_small_shapes(shape):
+    B, h_q, h_k, h_v, d, S, N, dt, ragged = shape
+    case = synth.small_case(B=B, h_q=h_q, h_k=h_k, h_v=h_v, d=d, S_max=S, N=N, dtype=dt,
+                            ragged=ragged, seed=41)
+    x = synth.make_inputs(case)
+    _run_decode(x, to_device(x), case, N, all_pairs(B, h_q), f"small{shape}")
+
+
+def test_select_multi_tile_rows():
+    # rows longer than one register tile of the selector (32768 keys) take the
+    # tiled path that re-reads the logits each round
+    case = synth.small_case(B=1, h_q=4, h_k=1, h_v=2, d=64, S_max=40000, N=700, dtype="bf16",
+                            seed=43)
+    lens = np.array([39999], np.int32)
+    x = synth.make_inputs(case, lens)
+    _run_decode(x, to_device(x), case, 700, all_pairs(1, 4), "multi-tile")
+
+
+def test_ragged_edge_lengths_and_nan_tail():
+    case = synth.small_case(B=10, h_q=4, h_k=1, h_v=2, d=64, S_max=1030, N=16, dtype="bf16",
+                            seed=47)
+    lens = np.array([1, 15, 16, 17, 255, 1000, 1023, 1024, 1025, 1030], np.int32)
+    x = synth.make_inputs(case, lens)
+    g_idx, g_out = _run_decode(x, to_device(x), case, 16, all_pairs(10, 4), "ragged")
+    # cache rows past L_b filled with NaN must not change anything
+    xn = {k: v.copy() for k, v in x.items()}
+    for b, L in enumerate(lens):
+        xn["k"][b, :, L:] = 0x7FC0
+        xn["v"][b, :, L:] = 0x7FC0
+    dn = to_device(xn)
+    idx = torch.empty((10, 4, 16), dtype=torch.int32, device="cuda")
+    out = saga.decode_attn(dn["q"], dn["k"], dn["v"], dn["seq_lens"], 16, idx_out=idx)
+    assert np.array_equal(idx.reshape(-1, 16).cpu().numpy(), g_idx)
+    assert np.array_equal(out.reshape(-1, 64).cpu().numpy(), g_out)
+
+
+def test_zero_query_ties_and_N_edges():
+    case = synth.small_case(B=2, h_q=8, h_k=2, h_v=4, d=128, S_max=500, N=40, dtype="bf16",
+                            seed=53)
+    lens = np.array([500, 33], np.int32)
+    x = synth.make_inputs(case, lens)
+    x["q"][:] = 0
+    g_idx, g_out = _run_decode(x, to_device(x), case, 40, all_pairs(2, 8), "q=0")
+    for r in range(16):
+        n = min(40, int(lens[r // 8]))
+        assert list(g_idx[r, :n]) == list(range(n))
+    x = synth.make_inputs(case, lens)
+    dx = to_device(x)
+    for N in (1, 2, 499, 500, 501, 4096):
+        _run_decode(x, dx, case, N, all_pairs(2, 8), f"N={N}")
+    # N >= L_b is full attention
+    out = saga.decode_attn(dx["q"], dx["k"], dx["v"], dx["seq_lens"], 4096)
+    ref, _ = oracle.dense_attn(x["q"], x["k"], x["v"], lens)
+    assert np.abs(out.reshape(-1, 128).cpu().numpy() - ref).max() <= 2e-3
+
+
+def test_duplicated_key_row_at_threshold_goes_to_lower_position():
+    case = synth.small_case(B=1, h_q=1, h_k=1, h_v=1, d=64, S_max=300, N=20, dtype="bf16",
+                            seed=59)
+    x = synth.make_inputs(case)
+    sc = oracle.logits(x["q"], x["k"], x["seq_lens"])[0]
+    order = np.lexsort((np.arange(300), -sc))
+    u, w = int(order[19]), int(order[40])
+    x["k"][0, 0, w] = x["k"][0, 0, u]
+    g_idx, _ = _run_decode(x, to_device(x), case, 20, [(0, 0)], "dup-row")
+    kept = set(g_idx[0].tolist())
+    assert min(u, w) in kept and max(u, w) not in kept
+
+
+def test_zero_length_row():
+    case = synth.small_case(B=2, h_q=4, h_k=1, h_v=2, d=64, S_max=64, N=8, dtype="bf16",
+                            seed=61)
+    lens = np.array([0, 64], np.int32)
+    x = synth.make_inputs(case, lens)
+    dx = to_device(x)
+    idx = torch.empty((2, 4, 8), dtype=torch.int32, device="cuda")
+    out = saga.decode_attn(dx["q"], dx["k"], dx["v"], dx["seq_lens"], 8, idx_out=idx)
+    outd = saga.dense_attn(dx["q"], dx["k"], dx["v"], dx["seq_lens"])
+    assert (idx[0].cpu() == -1).all()
+    assert (out[0].cpu() == 0).all() and (outd[0].cpu() == 0).all()
+    assert torch.isfinite(out).all()
+
+
+def test_deterministic_and_workspace_reuse():
+    case = synth.CASES["llama32_1b_8to4"]
+    x = synth.make_inputs(case)
+    dx = to_device(x)
+    ws = saga.new_workspace(saga.workspace_size(dx["q"], dx["k"], dx["v"], dx["seq_lens"], 512)
+                            + 4096, "cuda")
+    ws.fill_(0xAB)   # contents left by someone else must not matter
+    outs, idxs = [], []
+    for _ in range(2):
+        idx = torch.empty((case.B, case.h_q, 512), dtype=torch.int32, device="cuda")
+        outs.append(saga.decode_attn(dx["q"], dx["k"], dx["v"], dx["seq_lens"], 512,
+                                     workspace=ws, idx_out=idx).cpu())
+        idxs.append(idx.cpu())
+    assert torch.equal(outs[0], outs[1]) and torch.equal(idxs[0], idxs[1])
+    small = synth.small_case(B=1, h_q=4, h_k=1, h_v=2, d=64, S_max=200, N=10, seed=3)
+    xs = synth.make_inputs(small)
+    _run_decode(xs, to_device(xs), small, 10, all_pairs(1, 4), "after-reuse")
+
+
+def test_kscan_scores_match_oracle_logits():
+    for (dt, d) in (("f32", 64), ("bf16", 128), ("f32", 128), ("bf16", 64)):
+        case = synth.small_case(B=2, h_q=12, h_k=3, h_v=3, d=d, S_max=1001, N=1, dtype=dt,
+                                ragged=True, seed=67)
+        x = synth.make_inputs(case)
+        dx = to_device(x)
+        sc = saga.debug_scores(dx["q"], dx["k"], dx["seq_lens"]).reshape(-1, 1001).cpu().numpy()
+        ref = oracle.logits(x["q"], x["k"], x["seq_lens"])
+        qa = np.abs(synth.as_f32(x["q"]).astype(np.float64))
+        ka = np.abs(synth.as_f32(x["k"]).astype(np.float64))
+        g = 12 // 3
+        for r in range(24):
+            b, i = divmod(r, 12)
+            L = int(x["seq_lens"][b])
+            # fp32 accumulation bound: (d + 2) u sum_c |q_c k_c| / sqrt(d), u = 2^-24
+            mag = (ka[b, i // g, :L] @ qa[b, i]) / np.sqrt(d)
+            bound = (d + 2) * 2.0 ** -24 * mag + 1e-30
+            err = np.abs(sc[r, :L] - ref[r, :L])
+            assert (err <= bound).all(), (dt, d, r, float((err / bound).max()))
+            assert np.isnan(sc[r, L:]).all()
