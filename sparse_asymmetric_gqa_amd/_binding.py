@@ -33,6 +33,11 @@ class SagaError(RuntimeError):
 
 
 def _load() -> ctypes.CDLL:
+    # torch ships its own HIP runtime (libamdhip64.so, same SONAME as ROCm's).
+    # Streams and device pointers handed to libsaga come from torch, so torch
+    # must be loaded first: libsaga's libamdhip64.so.7 dependency then binds to
+    # that same runtime instead of loading a second copy that sees no device.
+    import torch  # noqa: F401
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is not built; run sparse_asymmetric_gqa_amd/build.py "
                           "(or __graft_entry__.build()) first")

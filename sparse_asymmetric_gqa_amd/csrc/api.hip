@@ -8,6 +8,8 @@
 #include "saga_internal.h"
 
 #include <stdint.h>
+#include <stdio.h>
+#include <stdlib.h>
 
 namespace saga {
 
@@ -60,7 +62,18 @@ saga_status check_shape(int B, int h_q, int h_k, int h_v, int d, int64_t S_max, 
     return SAGA_OK;
 }
 
-saga_status from_hip(hipError_t e) { return e == hipSuccess ? SAGA_OK : SAGA_ERR_HIP; }
+// A failed launch maps to SAGA_ERR_HIP; with SAGA_DEBUG set in the environment the
+// failing step and HIP's error text are also written to stderr.
+// hipGetLastError reports the last error of any HIP runtime call on this thread;
+// clear one left pending by unrelated earlier calls so that a failure reported
+// here belongs to our own launches.
+void clear_stale_error() { (void)hipGetLastError(); }
+
+saga_status from_hip(hipError_t e, const char* step) {
+    if (e == hipSuccess) return SAGA_OK;
+    if (getenv("SAGA_DEBUG")) fprintf(stderr, "libsaga: %s: %s\n", step, hipGetErrorString(e));
+    return SAGA_ERR_HIP;
+}
 
 }  // namespace
 
@@ -95,17 +108,18 @@ saga_status saga_decode_attn(const void* q, const void* k_cache, const void* v_c
     const bool bf16 = dtype == SAGA_BF16;
     const int64_t ss = saga::score_stride(S_max);
 
+    clear_stale_error();
     s = from_hip(saga::launch_kscan(q, k_cache, seq_lens, w.scores, ss, B, h_q, h_k, d, S_max,
-                                    bf16, stream));
+                                    bf16, stream), "kscan");
     if (s != SAGA_OK) return s;
     s = from_hip(saga::launch_select(w.scores, ss, seq_lens, B, h_q, N, S_max, w.sel_idx,
-                                     w.sel_val, w.row_max, w.row_cnt, idx_out, stream));
+                                     w.sel_val, w.row_max, w.row_cnt, idx_out, stream), "select");
     if (s != SAGA_OK) return s;
     s = from_hip(saga::launch_pv_sparse(v_cache, w.sel_idx, w.sel_val, w.row_max, w.row_cnt,
-                                        w.part, B, h_q, h_v, d, N, S_max, bf16, stream));
+                                        w.part, B, h_q, h_v, d, N, S_max, bf16, stream), "pv_sparse");
     if (s != SAGA_OK) return s;
     return from_hip(saga::launch_merge(w.part, saga::sparse_nsplit(N), saga::kPvEntries,
-                                       w.row_cnt, seq_lens, S_max, out, B, h_q, d, stream));
+                                       w.row_cnt, seq_lens, S_max, out, B, h_q, d, stream), "merge");
 }
 
 saga_status saga_dense_attn(const void* q, const void* k_cache, const void* v_cache,
@@ -124,14 +138,15 @@ saga_status saga_dense_attn(const void* q, const void* k_cache, const void* v_ca
     const bool bf16 = dtype == SAGA_BF16;
     const int64_t ss = saga::score_stride(S_max);
 
+    clear_stale_error();
     s = from_hip(saga::launch_kscan(q, k_cache, seq_lens, w.scores, ss, B, h_q, h_k, d, S_max,
-                                    bf16, stream));
+                                    bf16, stream), "kscan");
     if (s != SAGA_OK) return s;
     s = from_hip(saga::launch_pv_dense(v_cache, w.scores, ss, seq_lens, w.part, B, h_q, h_v, d,
-                                       S_max, bf16, stream));
+                                       S_max, bf16, stream), "pv_dense");
     if (s != SAGA_OK) return s;
     return from_hip(saga::launch_merge(w.part, saga::dense_nsplit(S_max), saga::kDenseRows,
-                                       nullptr, seq_lens, S_max, out, B, h_q, d, stream));
+                                       nullptr, seq_lens, S_max, out, B, h_q, d, stream), "merge");
 }
 
 saga_status saga_debug_scores(const void* q, const void* k_cache, const int32_t* seq_lens,
@@ -141,8 +156,9 @@ saga_status saga_debug_scores(const void* q, const void* k_cache, const int32_t*
     saga_status s = check_shape(B, h_q, h_k, h_k, d, S_max, dtype);
     if (s != SAGA_OK) return s;
     if (!aligned16(q) || !aligned16(k_cache)) return SAGA_ERR_INVALID_ARG;
+    clear_stale_error();
     return from_hip(saga::launch_kscan(q, k_cache, seq_lens, scores, S_max, B, h_q, h_k, d,
-                                       S_max, dtype == SAGA_BF16, stream));
+                                       S_max, dtype == SAGA_BF16, stream), "kscan");
 }
 
 const char* saga_status_string(saga_status s) {
