@@ -16,6 +16,11 @@
  *   - Softmax over the kept logits only, then the weighted sum of the kept
  *     value rows (§3.1 Eq. 7; App. C.1).
  *
+ * The decode call never writes the full logit matrix to memory: the K-scan
+ * keeps each chunk's logits on chip and publishes only the keys at or above
+ * a per-chunk cutoff; the selector proves the union's N-th key exact from the
+ * cutoffs, or recomputes that head's logits when it cannot.
+ *
  * Conventions shared by every entry point:
  *   - All tensor pointers are device pointers owned by the caller. The
  *     library never allocates, frees or synchronises inside these calls; it
@@ -113,6 +118,18 @@ saga_status saga_dense_attn(const void* q, const void* k_cache, const void* v_ca
 saga_status saga_debug_scores(const void* q, const void* k_cache, const int32_t* seq_lens,
                               float* scores, int B, int h_q, int h_k, int d, hipStream_t stream,
                               int64_t S_max, saga_dtype dtype);
+
+/*
+ * Diagnostic for tests: after a saga_decode_attn call on `stream` with the same
+ * sizes and workspace, copies to host_flags[B*h_q] (host memory) 1 for every
+ * query head whose kept set was settled by recomputing all of its logits
+ * (its chunk candidate lists could not prove the top-N exact) and 0 otherwise.
+ * Synchronises `stream`. Heads take that path only when their largest logits
+ * crowd into a few chunks; the result is exact either way.
+ */
+saga_status saga_debug_fallback_rows(const void* workspace, size_t workspace_bytes, int B,
+                                     int h_q, int h_k, int h_v, int d, int N, int64_t S_max,
+                                     saga_dtype dtype, int32_t* host_flags, hipStream_t stream);
 
 /* Static English text for a status code (never NULL). */
 const char* saga_status_string(saga_status s);

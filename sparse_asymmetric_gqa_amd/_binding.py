@@ -23,7 +23,8 @@ SAGA_F32 = 0
 SAGA_BF16 = 1
 
 EXPORTS = ("saga_workspace_size", "saga_decode_attn", "saga_dense_workspace_size",
-           "saga_dense_attn", "saga_debug_scores", "saga_status_string")
+           "saga_dense_attn", "saga_debug_scores", "saga_debug_fallback_rows",
+           "saga_status_string")
 
 
 class SagaError(RuntimeError):
@@ -53,6 +54,8 @@ def _load() -> ctypes.CDLL:
     lib.saga_dense_attn.restype = i
     lib.saga_debug_scores.argtypes = [vp, vp, vp, vp, i, i, i, i, vp, i64, i]
     lib.saga_debug_scores.restype = i
+    lib.saga_debug_fallback_rows.argtypes = [vp, sz, i, i, i, i, i, i, i64, i, vp, vp]
+    lib.saga_debug_fallback_rows.restype = i
     lib.saga_status_string.argtypes = [i]
     lib.saga_status_string.restype = ctypes.c_char_p
     return lib
@@ -103,3 +106,11 @@ def saga_debug_scores(q, k_cache, seq_lens, scores, B, h_q, h_k, d, stream, S_ma
                       dtype) -> int:
     return int(lib.saga_debug_scores(_ptr(q), _ptr(k_cache), _ptr(seq_lens), _ptr(scores), B,
                                      h_q, h_k, d, _ptr(stream), S_max, dtype))
+
+
+def saga_debug_fallback_rows(workspace, workspace_bytes, B, h_q, h_k, h_v, d, N, S_max, dtype,
+                             host_flags, stream) -> int:
+    """host_flags: a writable int32 numpy array of B*h_q entries (host memory)."""
+    return int(lib.saga_debug_fallback_rows(_ptr(workspace), workspace_bytes, B, h_q, h_k, h_v,
+                                            d, N, S_max, dtype,
+                                            ctypes.c_void_p(host_flags.ctypes.data), _ptr(stream)))

@@ -28,9 +28,9 @@ CFLAGS = [
 ]
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(OBJDIR, os.path.basename(src).replace(".hip", ".o"))
-    cmd = [HIPCC, *CFLAGS, "-c", src, "-o", obj]
+def _compile(src: str, objdir: str = OBJDIR, extra=()) -> str:
+    obj = os.path.join(objdir, os.path.basename(src).replace(".hip", ".o"))
+    cmd = [HIPCC, *CFLAGS, "-I", os.path.dirname(src), *extra, "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     errs = "\n".join(l for l in r.stderr.splitlines()
                      if "packed-fp32-ops" not in l and l.strip())
@@ -41,21 +41,27 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    """Compile all HIP sources and link libsaga.so; returns the library path."""
-    os.makedirs(OBJDIR, exist_ok=True)
-    srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+def build(verbose: bool = False, out: str = LIB, objdir: str = OBJDIR, extra=(),
+          csrc: str = CSRC) -> str:
+    """Compile all HIP sources and link libsaga.so; returns the library path.
+
+    `extra` adds compiler flags (e.g. -D overrides of tile constants) and
+    `out` / `objdir` / `csrc` redirect the products and sources, for building
+    experimental variants next to the default library.
+    """
+    os.makedirs(objdir, exist_ok=True)
+    srcs = sorted(glob.glob(os.path.join(csrc, "*.hip")))
     with ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
-        objs = list(ex.map(_compile, srcs))
-    tmp = LIB + ".tmp"
+        objs = list(ex.map(lambda s_: _compile(s_, objdir, tuple(extra)), srcs))
+    tmp = out + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed:\n" + r.stderr)
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
     if verbose:
-        print(f"built {LIB}")
-    return LIB
+        print(f"built {out}")
+    return out
 
 
 if __name__ == "__main__":

@@ -28,6 +28,11 @@ Workspace carve(void* base, int B, int h_q, int d, int N, int64_t S_max, bool de
     w.scores = reinterpret_cast<float*>(take(rows * (size_t)score_stride(S_max) * sizeof(float)));
     int nsplit;
     if (!dense) {
+        const size_t nch = (size_t)num_chunks(S_max);
+        w.cand = reinterpret_cast<uint2*>(take(rows * nch * kScanChunk * sizeof(uint2)));
+        w.cand_cnt = reinterpret_cast<int32_t*>(take(rows * nch * sizeof(int32_t)));
+        w.cand_cut = reinterpret_cast<uint32_t*>(take(rows * nch * sizeof(uint32_t)));
+        w.row_flag = reinterpret_cast<int32_t*>(take(rows * sizeof(int32_t)));
         w.sel_idx = reinterpret_cast<int32_t*>(take(rows * (size_t)N * sizeof(int32_t)));
         w.sel_val = reinterpret_cast<float*>(take(rows * (size_t)N * sizeof(float)));
         w.row_max = reinterpret_cast<float*>(take(rows * sizeof(float)));
@@ -39,6 +44,10 @@ Workspace carve(void* base, int B, int h_q, int d, int N, int64_t S_max, bool de
     w.part = reinterpret_cast<float*>(take(rows * (size_t)nsplit * (size_t)(d + 2) * sizeof(float)));
     w.bytes = off;
     return w;
+}
+
+bool use_union_path(int h_q, int h_k, int64_t S_max) {
+    return h_q / h_k <= 16 && num_chunks(S_max) <= max_union_chunks();
 }
 
 }  // namespace saga
@@ -109,12 +118,25 @@ saga_status saga_decode_attn(const void* q, const void* k_cache, const void* v_c
     const int64_t ss = saga::score_stride(S_max);
 
     clear_stale_error();
-    s = from_hip(saga::launch_kscan(q, k_cache, seq_lens, w.scores, ss, B, h_q, h_k, d, S_max,
-                                    bf16, stream), "kscan");
-    if (s != SAGA_OK) return s;
-    s = from_hip(saga::launch_select(w.scores, ss, seq_lens, B, h_q, N, S_max, w.sel_idx,
-                                     w.sel_val, w.row_max, w.row_cnt, idx_out, stream), "select");
-    if (s != SAGA_OK) return s;
+    if (saga::use_union_path(h_q, h_k, S_max)) {
+        const saga::TopmOut tm{w.cand, w.cand_cnt, w.cand_cut, N};
+        s = from_hip(saga::launch_kscan_topm(q, k_cache, seq_lens, tm, B, h_q, h_k, d, S_max,
+                                             bf16, stream), "kscan_topm");
+        if (s != SAGA_OK) return s;
+        s = from_hip(saga::launch_select_union(tm, seq_lens, B, h_q, h_k, d, N, S_max,
+                                               w.sel_idx, w.sel_val, w.row_max, w.row_cnt,
+                                               idx_out, w.row_flag, q, k_cache, w.scores, ss,
+                                               bf16, stream), "select_union");
+        if (s != SAGA_OK) return s;
+    } else {
+        s = from_hip(saga::launch_kscan(q, k_cache, seq_lens, w.scores, ss, B, h_q, h_k, d,
+                                        S_max, bf16, stream), "kscan");
+        if (s != SAGA_OK) return s;
+        s = from_hip(saga::launch_select(w.scores, ss, seq_lens, B, h_q, N, S_max, w.sel_idx,
+                                         w.sel_val, w.row_max, w.row_cnt, idx_out, stream),
+                     "select");
+        if (s != SAGA_OK) return s;
+    }
     s = from_hip(saga::launch_pv_sparse(v_cache, w.sel_idx, w.sel_val, w.row_max, w.row_cnt,
                                         w.part, B, h_q, h_v, d, N, S_max, bf16, stream), "pv_sparse");
     if (s != SAGA_OK) return s;
@@ -159,6 +181,29 @@ saga_status saga_debug_scores(const void* q, const void* k_cache, const int32_t*
     clear_stale_error();
     return from_hip(saga::launch_kscan(q, k_cache, seq_lens, scores, S_max, B, h_q, h_k, d,
                                        S_max, dtype == SAGA_BF16, stream), "kscan");
+}
+
+saga_status saga_debug_fallback_rows(const void* workspace, size_t workspace_bytes, int B,
+                                     int h_q, int h_k, int h_v, int d, int N, int64_t S_max,
+                                     saga_dtype dtype, int32_t* host_flags, hipStream_t stream) {
+    if (!workspace || !host_flags) return SAGA_ERR_INVALID_ARG;
+    saga_status s = check_shape(B, h_q, h_k, h_v, d, S_max, dtype);
+    if (s != SAGA_OK) return s;
+    if (N < 1) return SAGA_ERR_INVALID_ARG;
+    const saga::Workspace need = saga::carve(nullptr, B, h_q, d, N, S_max, false);
+    if (workspace_bytes < need.bytes) return SAGA_ERR_WORKSPACE;
+    const size_t rows = (size_t)B * (size_t)h_q;
+    if (!saga::use_union_path(h_q, h_k, S_max)) {
+        for (size_t r = 0; r < rows; ++r) host_flags[r] = 0;
+        return SAGA_OK;
+    }
+    const saga::Workspace w = saga::carve(const_cast<void*>(workspace), B, h_q, d, N, S_max, false);
+    clear_stale_error();
+    if (hipMemcpyAsync(host_flags, w.row_flag, rows * sizeof(int32_t), hipMemcpyDeviceToHost,
+                       stream) != hipSuccess ||
+        hipStreamSynchronize(stream) != hipSuccess)
+        return SAGA_ERR_HIP;
+    return SAGA_OK;
 }
 
 const char* saga_status_string(saga_status s) {

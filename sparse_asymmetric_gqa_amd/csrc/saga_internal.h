@@ -7,7 +7,10 @@
 namespace saga {
 
 // ---- launch geometry (also used by the workspace-size functions) ----------
-constexpr int kScanChunk = 1024;     // positions per K-scan workgroup
+#ifndef SAGA_KSCAN_CHUNK
+#define SAGA_KSCAN_CHUNK 1024
+#endif
+constexpr int kScanChunk = SAGA_KSCAN_CHUNK;   // positions per K-scan workgroup
 constexpr int kPvEntries = 256;      // kept entries per sparse PV workgroup
 constexpr int kDenseRows = 512;      // positions per dense PV workgroup
 constexpr int kSelectThreads = 1024; // threads of one select workgroup
@@ -19,7 +22,11 @@ inline int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 inline int64_t score_stride(int64_t S_max) { return round_up(S_max, 16); }
 
 struct Workspace {
-    float* scores;      // [B][h_q][score_stride]
+    float* scores;      // [B][h_q][score_stride]  dense logits (dense path, fallback rows)
+    uint2* cand;        // [B][h_q][nchunk][kScanChunk]  top-M candidate lists
+    int32_t* cand_cnt;  // [B][h_q][nchunk]
+    uint32_t* cand_cut; // [B][h_q][nchunk]
+    int32_t* row_flag;  // [B][h_q]   1 if the row took the dense fallback in the last call
     int32_t* sel_idx;   // [B][h_q][N]
     float* sel_val;     // [B][h_q][N]
     float* row_max;     // [B][h_q]   largest kept logit
@@ -27,6 +34,12 @@ struct Workspace {
     float* part;        // [B][h_q][nsplit][d + 2]  (m, l, acc[d])
     size_t bytes;
 };
+
+inline int num_chunks(int64_t S_max) { return (int)((S_max + kScanChunk - 1) / kScanChunk); }
+
+// Whether saga_decode_attn takes the top-M K-scan + union select path.
+bool use_union_path(int h_q, int h_k, int64_t S_max);
+int max_union_chunks();
 
 // Carve the decode workspace (dense == false) or the dense one out of `base`
 // (base may be null to only compute the size).
@@ -36,15 +49,36 @@ Workspace carve(void* base, int B, int h_q, int d, int N, int64_t S_max, bool de
 int sparse_nsplit(int N);          // ceil(N / kPvEntries)
 int dense_nsplit(int64_t S_max);   // ceil(S_max / kDenseRows)
 
+// Candidate lists published by the top-M K-scan, per (b*h_q + i, chunk) slot:
+// cand[slot][0..cnt) = (position, key) ascending in position, cut[slot] = the
+// chunk's cutoff key (every key of the chunk left out is below it).
+struct TopmOut {
+    uint2* cand;       // [B*h_q][nchunk][kScanChunk]
+    int32_t* cnt;      // [B*h_q][nchunk]
+    uint32_t* cut;     // [B*h_q][nchunk]
+    int N;
+};
+
 // ---- launchers (defined next to their kernels) ------------------------------
 // All return hipGetLastError() after enqueueing.
 hipError_t launch_kscan(const void* q, const void* k, const int32_t* lens, float* scores,
                         int64_t s_stride, int B, int h_q, int h_k, int d, int64_t S_max,
                         bool bf16, hipStream_t st);
 
+// K-scan in top-M mode (h_q / h_k <= 16): candidate lists instead of logits.
+hipError_t launch_kscan_topm(const void* q, const void* k, const int32_t* lens, const TopmOut& tm,
+                             int B, int h_q, int h_k, int d, int64_t S_max, bool bf16,
+                             hipStream_t st);
+
 hipError_t launch_select(const float* scores, int64_t s_stride, const int32_t* lens, int B,
                          int h_q, int N, int64_t S_max, int32_t* sel_idx, float* sel_val,
                          float* row_max, int32_t* row_cnt, int32_t* idx_out, hipStream_t st);
+
+hipError_t launch_select_union(const TopmOut& tm, const int32_t* lens, int B, int h_q, int h_k,
+                               int d, int N, int64_t S_max, int32_t* sel_idx, float* sel_val,
+                               float* row_max, int32_t* row_cnt, int32_t* idx_out,
+                               int32_t* row_flag, const void* q, const void* k, float* scores,
+                               int64_t s_stride, bool bf16, hipStream_t st);
 
 hipError_t launch_pv_sparse(const void* v, const int32_t* sel_idx, const float* sel_val,
                             const float* row_max, const int32_t* row_cnt, float* part, int B,

@@ -107,14 +107,16 @@ def test_decode_small_shapes(shape):
     _run_decode(x, to_device(x), case, N, all_pairs(B, h_q), f"small{shape}")
 
 
-def test_select_multi_tile_rows():
-    # rows longer than one register tile of the selector (32768 keys) take the
-    # tiled path that re-reads the logits each round
-    case = synth.small_case(B=1, h_q=4, h_k=1, h_v=2, d=64, S_max=40000, N=700, dtype="bf16",
-                            seed=43)
+@pytest.mark.parametrize("h_q", [4, 32])
+def test_select_multi_tile_rows(h_q):
+    # rows longer than one register tile of the selector take the tiled path that
+    # re-reads keys each round: the dense selector (key group of 32: 32768 keys per
+    # tile) and the union selector's dense fallback / multi-tile candidate sets
+    case = synth.small_case(B=1, h_q=h_q, h_k=1, h_v=2, d=64, S_max=40000, N=700,
+                            dtype="bf16", seed=43)
     lens = np.array([39999], np.int32)
     x = synth.make_inputs(case, lens)
-    _run_decode(x, to_device(x), case, 700, all_pairs(1, 4), "multi-tile")
+    _run_decode(x, to_device(x), case, 700, all_pairs(1, h_q), "multi-tile")
 
 
 def test_ragged_edge_lengths_and_nan_tail():
@@ -221,3 +223,60 @@ def test_kscan_scores_match_oracle_logits():
             err = np.abs(sc[r, :L] - ref[r, :L])
             assert (err <= bound).all(), (dt, d, r, float((err / bound).max()))
             assert np.isnan(sc[r, L:]).all()
+
+
+def _fallback_flags(dx, ws, case, N):
+    flags = np.zeros(case.B * case.h_q, dtype=np.int32)
+    st = saga.saga_debug_fallback_rows(ws, ws.numel(), case.B, case.h_q, case.h_k, case.h_v,
+                                       case.d, N, case.S_max,
+                                       saga.SAGA_F32 if case.dtype == "f32" else saga.SAGA_BF16,
+                                       flags, torch.cuda.current_stream().cuda_stream)
+    assert st == saga.SAGA_OK
+    return flags
+
+
+def test_clustered_top_entries_take_exact_fallback():
+    # Batch row 0: the 300 largest logits of every head sit in the first chunk of
+    # 1024 positions, more than that chunk's candidate list can carry, so the
+    # selector cannot prove the union exact and must recompute those heads.
+    case = synth.small_case(B=2, h_q=4, h_k=1, h_v=2, d=64, S_max=8192, N=300, dtype="bf16",
+                            seed=71)
+    x = synth.make_inputs(case)
+    qsum = synth.as_f32(x["q"][0]).astype(np.float64).sum(axis=0)
+    rng = np.random.default_rng(3)
+    # logits spread geometrically over ~10 half-octave bins, so the bin of the
+    # chunk's M-th key cannot hold all 300 of them
+    alpha = 3.0 * 2.0 ** (np.arange(300) / 60.0)
+    rows = alpha[:, None] * qsum[None, :] / np.linalg.norm(qsum) * 8.0 + rng.standard_normal((300, 64))
+    x["k"][0, 0, :300] = synth.f32_to_bf16_bits(rows.astype(np.float32))
+    dx = to_device(x)
+    ws = saga.new_workspace(saga.workspace_size(dx["q"], dx["k"], dx["v"], dx["seq_lens"], 300),
+                            "cuda")
+    idx = torch.empty((2, 4, 300), dtype=torch.int32, device="cuda")
+    out = saga.decode_attn(dx["q"], dx["k"], dx["v"], dx["seq_lens"], 300, workspace=ws,
+                           idx_out=idx)
+    torch.cuda.synchronize()
+    flags = _fallback_flags(dx, ws, case, 300)
+    _say(f"    fallback flags {flags.tolist()}")
+    pairs = all_pairs(2, 4)
+    ref = oracle.topn_attn(x["q"], x["k"], x["v"], x["seq_lens"], 300, pairs=pairs)
+    g_idx = idx.reshape(-1, 300).cpu().numpy()
+    check_index_sets(g_idx, ref, x, pairs, 300)
+    check_outputs(out.reshape(-1, 64).cpu().numpy(), g_idx, x, pairs, 2e-3)
+    assert set(g_idx[0].tolist()) == set(range(300))
+    assert flags[:4].tolist() == [1, 1, 1, 1] and flags[4:].tolist() == [0, 0, 0, 0]
+
+
+def test_workloads_report_fallback_rows():
+    for name in ("llama32_1b_8to4", "qwen25_1p5b_2to1_ragged", "qwen25_1p5b_b64_32k"):
+        case = synth.CASES[name]
+        x = synth.make_inputs(case)
+        dx = to_device(x)
+        ws = saga.new_workspace(saga.workspace_size(dx["q"], dx["k"], dx["v"], dx["seq_lens"],
+                                                    case.N), "cuda")
+        saga.decode_attn(dx["q"], dx["k"], dx["v"], dx["seq_lens"], case.N, workspace=ws)
+        flags = _fallback_flags(dx, ws, case, case.N)
+        _say(f"    {name}: {int(flags.sum())} of {flags.size} heads took the dense fallback")
+        assert flags.sum() <= flags.size // 20
+        del dx, ws
+        torch.cuda.empty_cache()
