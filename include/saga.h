@@ -95,6 +95,21 @@ saga_status saga_decode_attn(const void* q, const void* k_cache, const void* v_c
                              int64_t S_max, saga_dtype dtype,
                              void* workspace, size_t workspace_bytes, int32_t* idx_out);
 
+/*
+ * saga_decode_attn with phase timing for benchmarks: identical work and
+ * results, and records events[i] on `stream` for i < n_events (0..5) at phase
+ * boundary i: 0 before the K-scan, 1 after the K-scan (with its per-chunk
+ * candidate extraction), 2 after top-N selection, 3 after the value gather,
+ * 4 after the final merge. The events are created by the caller (timing
+ * enabled); a null event or n_events outside 0..5 gives SAGA_ERR_INVALID_ARG.
+ */
+saga_status saga_decode_attn_timed(const void* q, const void* k_cache, const void* v_cache,
+                                   const int32_t* seq_lens, float* out,
+                                   int B, int h_q, int h_k, int h_v, int d, int N,
+                                   hipStream_t stream, int64_t S_max, saga_dtype dtype,
+                                   void* workspace, size_t workspace_bytes, int32_t* idx_out,
+                                   hipEvent_t* events, int n_events);
+
 /* Bytes of device workspace saga_dense_attn needs (host only; 0 on invalid arguments). */
 size_t saga_dense_workspace_size(int B, int h_q, int h_k, int h_v, int d, int64_t S_max,
                                  saga_dtype dtype);

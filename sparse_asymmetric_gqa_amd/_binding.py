@@ -22,7 +22,8 @@ SAGA_ERR_HIP = -4
 SAGA_F32 = 0
 SAGA_BF16 = 1
 
-EXPORTS = ("saga_workspace_size", "saga_decode_attn", "saga_dense_workspace_size",
+EXPORTS = ("saga_workspace_size", "saga_decode_attn", "saga_decode_attn_timed",
+           "saga_dense_workspace_size",
            "saga_dense_attn", "saga_debug_scores", "saga_debug_fallback_rows",
            "saga_status_string")
 
@@ -50,6 +51,9 @@ def _load() -> ctypes.CDLL:
     lib.saga_dense_workspace_size.restype = sz
     lib.saga_decode_attn.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, vp, i64, i, vp, sz, vp]
     lib.saga_decode_attn.restype = i
+    lib.saga_decode_attn_timed.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, vp, i64, i, vp,
+                                           sz, vp, vp, i]
+    lib.saga_decode_attn_timed.restype = i
     lib.saga_dense_attn.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, vp, i64, i, vp, sz]
     lib.saga_dense_attn.restype = i
     lib.saga_debug_scores.argtypes = [vp, vp, vp, vp, i, i, i, i, vp, i64, i]
@@ -93,6 +97,17 @@ def saga_decode_attn(q, k_cache, v_cache, seq_lens, out, B, h_q, h_k, h_v, d, N,
     return int(lib.saga_decode_attn(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seq_lens),
                                     _ptr(out), B, h_q, h_k, h_v, d, N, _ptr(stream), S_max,
                                     dtype, _ptr(workspace), workspace_bytes, _ptr(idx_out)))
+
+
+def saga_decode_attn_timed(q, k_cache, v_cache, seq_lens, out, B, h_q, h_k, h_v, d, N, stream,
+                           S_max, dtype, workspace, workspace_bytes, idx_out, events) -> int:
+    """events: a sequence of 0..5 raw hipEvent_t handles (ints)."""
+    n = len(events)
+    arr = (ctypes.c_void_p * max(n, 1))(*[ctypes.c_void_p(int(e)) for e in events])
+    return int(lib.saga_decode_attn_timed(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seq_lens),
+                                          _ptr(out), B, h_q, h_k, h_v, d, N, _ptr(stream), S_max,
+                                          dtype, _ptr(workspace), workspace_bytes,
+                                          _ptr(idx_out), arr, n))
 
 
 def saga_dense_attn(q, k_cache, v_cache, seq_lens, out, B, h_q, h_k, h_v, d, stream, S_max,

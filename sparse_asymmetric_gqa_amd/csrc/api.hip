@@ -100,11 +100,24 @@ size_t saga_dense_workspace_size(int B, int h_q, int h_k, int h_v, int d, int64_
     return saga::carve(nullptr, B, h_q, d, 1, S_max, true).bytes;
 }
 
-saga_status saga_decode_attn(const void* q, const void* k_cache, const void* v_cache,
-                             const int32_t* seq_lens, float* out,
-                             int B, int h_q, int h_k, int h_v, int d, int N, hipStream_t stream,
-                             int64_t S_max, saga_dtype dtype,
-                             void* workspace, size_t workspace_bytes, int32_t* idx_out) {
+}  // extern "C"
+
+namespace {
+
+// Records events[i] (i < n_events) at phase boundary i of the decode sequence.
+struct PhaseMarks {
+    hipEvent_t* ev;
+    int n;
+    saga_status mark(int i, hipStream_t st) const {
+        if (i >= n) return SAGA_OK;
+        return from_hip(hipEventRecord(ev[i], st), "event record");
+    }
+};
+
+saga_status decode(const void* q, const void* k_cache, const void* v_cache,
+                   const int32_t* seq_lens, float* out, int B, int h_q, int h_k, int h_v, int d,
+                   int N, hipStream_t stream, int64_t S_max, saga_dtype dtype, void* workspace,
+                   size_t workspace_bytes, int32_t* idx_out, PhaseMarks pm) {
     if (!q || !k_cache || !v_cache || !seq_lens || !out) return SAGA_ERR_INVALID_ARG;
     saga_status s = check_shape(B, h_q, h_k, h_v, d, S_max, dtype);
     if (s != SAGA_OK) return s;
@@ -118,11 +131,13 @@ saga_status saga_decode_attn(const void* q, const void* k_cache, const void* v_c
     const int64_t ss = saga::score_stride(S_max);
 
     clear_stale_error();
+    if ((s = pm.mark(0, stream)) != SAGA_OK) return s;
     if (saga::use_union_path(h_q, h_k, S_max)) {
         const saga::TopmOut tm{w.cand, w.cand_cnt, w.cand_cut, N};
         s = from_hip(saga::launch_kscan_topm(q, k_cache, seq_lens, tm, B, h_q, h_k, d, S_max,
                                              bf16, stream), "kscan_topm");
         if (s != SAGA_OK) return s;
+        if ((s = pm.mark(1, stream)) != SAGA_OK) return s;
         s = from_hip(saga::launch_select_union(tm, seq_lens, B, h_q, h_k, d, N, S_max,
                                                w.sel_idx, w.sel_val, w.row_max, w.row_cnt,
                                                idx_out, w.row_flag, q, k_cache, w.scores, ss,
@@ -132,16 +147,47 @@ saga_status saga_decode_attn(const void* q, const void* k_cache, const void* v_c
         s = from_hip(saga::launch_kscan(q, k_cache, seq_lens, w.scores, ss, B, h_q, h_k, d,
                                         S_max, bf16, stream), "kscan");
         if (s != SAGA_OK) return s;
+        if ((s = pm.mark(1, stream)) != SAGA_OK) return s;
         s = from_hip(saga::launch_select(w.scores, ss, seq_lens, B, h_q, N, S_max, w.sel_idx,
                                          w.sel_val, w.row_max, w.row_cnt, idx_out, stream),
                      "select");
         if (s != SAGA_OK) return s;
     }
+    if ((s = pm.mark(2, stream)) != SAGA_OK) return s;
     s = from_hip(saga::launch_pv_sparse(v_cache, w.sel_idx, w.sel_val, w.row_max, w.row_cnt,
                                         w.part, B, h_q, h_v, d, N, S_max, bf16, stream), "pv_sparse");
     if (s != SAGA_OK) return s;
-    return from_hip(saga::launch_merge(w.part, saga::sparse_nsplit(N), saga::kPvEntries,
-                                       w.row_cnt, seq_lens, S_max, out, B, h_q, d, stream), "merge");
+    if ((s = pm.mark(3, stream)) != SAGA_OK) return s;
+    s = from_hip(saga::launch_merge(w.part, saga::sparse_nsplit(N), saga::kPvEntries,
+                                    w.row_cnt, seq_lens, S_max, out, B, h_q, d, stream), "merge");
+    if (s != SAGA_OK) return s;
+    return pm.mark(4, stream);
+}
+
+}  // namespace
+
+extern "C" {
+
+saga_status saga_decode_attn(const void* q, const void* k_cache, const void* v_cache,
+                             const int32_t* seq_lens, float* out,
+                             int B, int h_q, int h_k, int h_v, int d, int N, hipStream_t stream,
+                             int64_t S_max, saga_dtype dtype,
+                             void* workspace, size_t workspace_bytes, int32_t* idx_out) {
+    return decode(q, k_cache, v_cache, seq_lens, out, B, h_q, h_k, h_v, d, N, stream, S_max,
+                  dtype, workspace, workspace_bytes, idx_out, PhaseMarks{nullptr, 0});
+}
+
+saga_status saga_decode_attn_timed(const void* q, const void* k_cache, const void* v_cache,
+                                   const int32_t* seq_lens, float* out,
+                                   int B, int h_q, int h_k, int h_v, int d, int N,
+                                   hipStream_t stream, int64_t S_max, saga_dtype dtype,
+                                   void* workspace, size_t workspace_bytes, int32_t* idx_out,
+                                   hipEvent_t* events, int n_events) {
+    if (n_events < 0 || n_events > 5 || (n_events > 0 && !events)) return SAGA_ERR_INVALID_ARG;
+    for (int i = 0; i < n_events; ++i)
+        if (!events[i]) return SAGA_ERR_INVALID_ARG;
+    return decode(q, k_cache, v_cache, seq_lens, out, B, h_q, h_k, h_v, d, N, stream, S_max,
+                  dtype, workspace, workspace_bytes, idx_out, PhaseMarks{events, n_events});
 }
 
 saga_status saga_dense_attn(const void* q, const void* k_cache, const void* v_cache,

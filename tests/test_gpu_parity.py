@@ -203,6 +203,35 @@ def test_deterministic_and_workspace_reuse():
     _run_decode(xs, to_device(xs), small, 10, all_pairs(1, 4), "after-reuse")
 
 
+def test_timed_entry_matches_plain_entry():
+    case = synth.CASES["llama32_1b_8to4"]
+    x = synth.make_inputs(case)
+    dx = to_device(x)
+    B, h_q, h_k, h_v, d, S, N = case.B, case.h_q, case.h_k, case.h_v, case.d, case.S_max, case.N
+    _say(f"[timed] B={B} h_q={h_q} h_k={h_k} h_v={h_v} d={d} S={S} N={N}")
+    st = torch.cuda.current_stream()
+    wsb = saga.saga_workspace_size(B, h_q, h_k, h_v, d, N, S, saga.SAGA_BF16)
+    ws = saga.new_workspace(wsb, "cuda")
+    res = []
+    for nev in (0, 2, 5):
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(nev)]
+        for e_ in evs:
+            e_.record(st)
+        out = torch.empty((B, h_q, d), dtype=torch.float32, device="cuda")
+        idx = torch.empty((B, h_q, N), dtype=torch.int32, device="cuda")
+        rc = saga.saga_decode_attn_timed(dx["q"], dx["k"], dx["v"], dx["seq_lens"], out, B, h_q,
+                                         h_k, h_v, d, N, st.cuda_stream, S, saga.SAGA_BF16, ws,
+                                         wsb, idx, [e_.cuda_event for e_ in evs])
+        assert rc == saga.SAGA_OK
+        torch.cuda.synchronize()
+        for a, b_ in zip(evs, evs[1:]):
+            assert a.elapsed_time(b_) >= 0.0
+        res.append((out.cpu(), idx.cpu()))
+    plain = saga.decode_attn(dx["q"], dx["k"], dx["v"], dx["seq_lens"], N).cpu()
+    for o, i in res:
+        assert torch.equal(o, plain) and torch.equal(i, res[0][1])
+
+
 def test_kscan_scores_match_oracle_logits():
     for (dt, d) in (("f32", 64), ("bf16", 128), ("f32", 128), ("bf16", 64)):
         case = synth.small_case(B=2, h_q=12, h_k=3, h_v=3, d=d, S_max=1001, N=1, dtype=dt,
