@@ -30,8 +30,7 @@ Workspace carve(void* base, int B, int h_q, int d, int N, int64_t S_max, bool de
     if (!dense) {
         const size_t nch = (size_t)num_chunks(S_max);
         w.cand = reinterpret_cast<uint2*>(take(rows * nch * kScanChunk * sizeof(uint2)));
-        w.cand_cnt = reinterpret_cast<int32_t*>(take(rows * nch * sizeof(int32_t)));
-        w.cand_cut = reinterpret_cast<uint32_t*>(take(rows * nch * sizeof(uint32_t)));
+        w.cand_meta = reinterpret_cast<uint4*>(take(rows * nch * sizeof(uint4)));
         w.row_flag = reinterpret_cast<int32_t*>(take(rows * sizeof(int32_t)));
         w.sel_idx = reinterpret_cast<int32_t*>(take(rows * (size_t)N * sizeof(int32_t)));
         w.sel_val = reinterpret_cast<float*>(take(rows * (size_t)N * sizeof(float)));
@@ -133,7 +132,7 @@ saga_status decode(const void* q, const void* k_cache, const void* v_cache,
     clear_stale_error();
     if ((s = pm.mark(0, stream)) != SAGA_OK) return s;
     if (saga::use_union_path(h_q, h_k, S_max)) {
-        const saga::TopmOut tm{w.cand, w.cand_cnt, w.cand_cut, N};
+        const saga::TopmOut tm{w.cand, w.cand_meta, N};
         s = from_hip(saga::launch_kscan_topm(q, k_cache, seq_lens, tm, B, h_q, h_k, d, S_max,
                                              bf16, stream), "kscan_topm");
         if (s != SAGA_OK) return s;

@@ -16,26 +16,28 @@
 // The query operand uses the same lane -> d mapping, so the contraction
 // covers every d exactly once whatever order the hardware sums in.
 //
-// Pipeline: two register stages of kTilesPerStage tiles each are in flight
-// per wave (ping-pong, no register copies), so a wave never waits for the
-// loads it has just issued. Workgroups loop over (key head, chunk) work items
-// so their start-up cost is paid once per workgroup, not once per chunk.
+// Work is split into (b, key head, 1024-position chunk) items, walked by
+// persistent workgroups. A streaming wave keeps NS register stages of K tiles
+// in flight (four, or two for fp32 at d = 128), consumed in rotation with no
+// register copies; the last round of an item already loads the next item's
+// first stages.
 //
-// Two output modes:
-//   dense  -- fp32 logits to a [B][h_q][stride] array (the dense baseline, the
-//             debug entry point, and key groups wider than one 16-head tile);
-//   top-M  -- logits stay on chip: as order-preserving keys in LDS, then for
-//             each query head a cutoff key with M <= count(key >= cutoff) (M
-//             from N and L_b) is found by bisection over the key bits, and every
-//             key at or above it is published as a position-sorted (position,
-//             key) list, with the cutoff. Every key left out is below its
-//             chunk's cutoff, which is what lets the selector prove its union
-//             result exact.
-//
-// Work items are software-pipelined: the next item's query and first K stages
-// are loaded before the current item's candidates are published, and the
-// LDS-reuse barriers wait on LDS only, so no wave ever waits for its own
-// global stores to drain.
+// Two kernels:
+//   kscan       -- fp32 logits to a [B][h_q][stride] array (the dense baseline,
+//                  the debug entry point, and key groups wider than 16 heads);
+//                  four streaming waves per workgroup.
+//   kscan_topm  -- the decode path: logits never leave the chip. One
+//                  workgroup per CU with two roles. Four producer waves
+//                  stream item t and write its logits as order-preserving keys
+//                  into one of two LDS buffers; meanwhile eight consumer waves
+//                  take item t-1 from the other buffer and, per query head,
+//                  find a cutoff key with M <= count(key >= cutoff) (M from N
+//                  and L_b) and publish every key at or above it as a
+//                  position-sorted (position, key) list, with the cutoff.
+//                  Every key left out is below its chunk's cutoff, which is
+//                  what lets the selector prove its union result exact. The
+//                  two roles meet at one barrier per item, so candidate
+//                  extraction overlaps the K stream instead of stalling it.
 #include "saga_internal.h"
 
 namespace saga {
@@ -49,8 +51,17 @@ namespace {
 #ifndef SAGA_KSCAN_NT
 #define SAGA_KSCAN_NT 1
 #endif
-constexpr int kWaves = 4;
+constexpr int kWaves = 4;          // streaming waves per workgroup (both kernels)
+constexpr int kConsumers = 8;      // extracting waves of kscan_topm
+constexpr int kTopmThreads = 64 * (kWaves + kConsumers);
 constexpr int kTilesPerStage = SAGA_KSCAN_U;
+// Register stages in flight per streaming wave: four when a stage is at most
+// 16 VGPRs (bf16 at d = 128, either dtype at d = 64), two for fp32 at d = 128.
+__host__ __device__ constexpr int stages_for(int nv) { return nv >= 8 ? 2 : 4; }
+// Candidates of one head staged in its own LDS row before the global write:
+// entries [0, kStageMax) hold data, [kStageMax, kStageMax + 64) are per-lane
+// sinks for the branch-free writes of entries that are not kept.
+constexpr uint32_t kStageMax = kScanChunk / 2 - 64;
 
 // K rows are read exactly once per call: mark the loads non-temporal.
 template <typename V>
@@ -80,54 +91,61 @@ template <> struct Mfma<float> {
 };
 
 // LDS-only barrier: orders LDS accesses of the workgroup without waiting for
-// outstanding global stores (a __syncthreads() would also drain those).
+// outstanding global loads or stores (a __syncthreads() would also drain those).
 __device__ inline void lds_barrier() {
     __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0); vmcnt / expcnt left as they are
     __builtin_amdgcn_s_barrier();
 }
 
+// One (b, key head, chunk) work item. Positions fit in int: S_max is capped on
+// the host at INT32_MAX / 2.
+template <typename T>
 struct Item {
+    const T* kb;       // K row c0 of this (b, kh)
     int bkh, b, kh, chunk;
-    int64_t L, c0, c1;
+    int L, c0, n;      // cached length, first position, positions in the chunk
 };
 
-template <typename T, int DH, int NHT, bool TOPM>
-__global__ __launch_bounds__(256, (TOPM && sizeof(T) == 2) ? 3 : 1) void kscan(const T* __restrict__ q, const T* __restrict__ k,
-                                             const int32_t* __restrict__ lens,
-                                             float* __restrict__ scores, int64_t s_stride,
-                                             int h_q, int h_k, int64_t S_max, int nchunk,
-                                             int nwork, float scale, bool vst, TopmOut tm) {
-    extern __shared__ uint32_t lds_keys[];   // top-M: [g][kScanChunk] keys of the chunk
-    constexpr int NV = DH * (int)sizeof(T) / 64;   // 16-byte vectors per lane per tile
-    constexpr int EV = 16 / (int)sizeof(T);        // elements per vector
-    constexpr int U = kTilesPerStage;
-    constexpr int STAGE = kWaves * U * 16;         // positions per stage of the workgroup
-    const int g = h_q / h_k;
-    const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
-    const int r16 = lane & 15;
-    const int grp = lane >> 4;
-
-    // first work item at or after w whose chunk starts inside its row
-    auto next_item = [&](int w, Item& it) -> int {
-        for (; w < nwork; w += gridDim.x) {
-            it.bkh = w / nchunk;
-            it.chunk = w - it.bkh * nchunk;
-            it.b = it.bkh / h_k;
-            it.kh = it.bkh - it.b * h_k;
-            it.L = clamp_len(lens[it.b], S_max);
-            it.c0 = (int64_t)it.chunk * kScanChunk;
-            if (it.c0 < it.L) {
-                it.c1 = it.c0 + kScanChunk < it.L ? it.c0 + kScanChunk : it.L;
-                return w;
-            }
+// First work item at or after w (stepping by `step`) whose chunk starts inside
+// its row; returns nwork when there is none.
+template <typename T, int DH, typename LenOf>
+__device__ inline int next_item(int w, int step, int nwork, int nchunk, int h_k, int64_t S_max,
+                                LenOf&& len_of, const T* __restrict__ k, Item<T>& it) {
+    for (; w < nwork; w += step) {
+        it.bkh = w / nchunk;
+        it.chunk = w - it.bkh * nchunk;
+        it.b = it.bkh / h_k;
+        it.kh = it.bkh - it.b * h_k;
+        it.L = (int)clamp_len(len_of(it.b), S_max);
+        it.c0 = it.chunk * kScanChunk;
+        if (it.c0 < it.L) {
+            it.n = it.L - it.c0 < kScanChunk ? it.L - it.c0 : kScanChunk;
+            it.kb = k + ((int64_t)it.bkh * S_max + it.c0) * DH;
+            return w;
         }
-        return nwork;
-    };
+    }
+    return nwork;
+}
 
+// The streaming side shared by both kernels: wave `sw` (0..kWaves-1) of the
+// streaming group loads and multiplies tiles 16 * (sw + kWaves * (u + U * st))
+// of an item, st = stage index.
+template <typename T, int DH, int NHT>
+struct Streamer {
+    static constexpr int NV = DH * (int)sizeof(T) / 64;   // 16-byte vectors per lane per tile
+    static constexpr int EV = 16 / (int)sizeof(T);        // elements per vector
+    static constexpr int U = kTilesPerStage;
+    static constexpr int NS = stages_for(NV);
+    static constexpr int STAGE = kWaves * U * 16;         // positions per stage
+
+    int sw, r16, grp;
     u32x4 bq[NHT][NV];
-    u32x4 A[U][NV], Bv[U][NV];
-    auto load_q = [&](const Item& it) {
+    u32x4 buf[NS][U][NV];
+
+    __device__ Streamer(int sw_, int lane) : sw(sw_), r16(lane & 15), grp(lane >> 4) {}
+
+    // Query operand from a [g][DH] array (global or LDS); heads >= g are 0.
+    __device__ inline void load_q(const T* qrow0, int g) {
 #pragma unroll
         for (int ht = 0; ht < NHT; ++ht) {
             const int n = ht * 16 + r16;
@@ -135,165 +153,394 @@ __global__ __launch_bounds__(256, (TOPM && sizeof(T) == 2) ? 3 : 1) void kscan(c
             for (int v = 0; v < NV; ++v) {
                 bq[ht][v] = u32x4{0u, 0u, 0u, 0u};
                 if (n < g)
-                    bq[ht][v] = *reinterpret_cast<const u32x4*>(
-                        q + (int64_t)(it.b * h_q + it.kh * g + n) * DH + v * 4 * EV + grp * EV);
+                    bq[ht][v] = *reinterpret_cast<const u32x4*>(qrow0 + (int64_t)n * DH +
+                                                                 v * 4 * EV + grp * EV);
             }
         }
-    };
-    auto load = [&](u32x4 (&dst)[U][NV], const Item& it, int st) {
-        const T* kb = k + (int64_t)it.bkh * S_max * DH + grp * EV;
-        const int64_t last = it.c1 - 1;
+    }
+    // 32-bit byte offsets from the item's uniform base (at most one chunk of rows)
+    __device__ inline void load(int s, const Item<T>& it, int st) {
+        const char* kb = reinterpret_cast<const char*>(it.kb);
+        const int last = it.n - 1;
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            int64_t row = it.c0 + 16 * (int64_t)(wave + kWaves * (u + U * st)) + r16;
+            int row = 16 * (sw + kWaves * (u + U * st)) + r16;
             row = row < last ? row : last;
-            const T* src = kb + row * DH;
+            const uint32_t off = (uint32_t)(row * DH + grp * EV) * (uint32_t)sizeof(T);
 #pragma unroll
             for (int v = 0; v < NV; ++v)
-                dst[u][v] = load_stream(reinterpret_cast<const u32x4*>(src + v * 4 * EV));
+                buf[s][u][v] = load_stream(reinterpret_cast<const u32x4*>(
+                    kb + off + v * 4 * EV * (int)sizeof(T)));
         }
-    };
-    auto consume = [&](const u32x4 (&src)[U][NV], const Item& it, int st) {
+    }
+    // Tile u of stage buffer s: acc[e] = scaled logit of head ht*16 + r16 at
+    // chunk offset r0 + 4 grp + e, handed to sink(ht, r0, off, acc) with
+    // off = r0 + 4 grp (the tile's first row r0 = 16 (sw + kWaves (u + U st))).
+    template <typename Sink>
+    __device__ inline void consume(int s, int st, float scale, Sink&& sink) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const int64_t t0 = it.c0 + 16 * (int64_t)(wave + kWaves * (u + U * st));
-            const int64_t p = t0 + 4 * grp;
+            const int r0 = 16 * (sw + kWaves * (u + U * st));
 #pragma unroll
             for (int ht = 0; ht < NHT; ++ht) {
                 f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int v = 0; v < NV; ++v) acc = Mfma<T>::step(src[u][v], bq[ht][v], acc);
-                acc = acc * scale;
-                const int n = ht * 16 + r16;
-                if (TOPM) {
-                    // keys of positions past the chunk are 0, below every real key
-                    const int off = (int)(p - it.c0);
-                    if (n < g && off < kScanChunk) {
-                        u32x4 kv;
-#pragma unroll
-                        for (int e = 0; e < 4; ++e)
-                            kv[e] = (p + e < it.c1) ? float_key(acc[e]) : 0u;
-                        *reinterpret_cast<u32x4*>(&lds_keys[n * kScanChunk + off]) = kv;
-                    }
-                } else {
-                    float* dst = scores + (int64_t)(it.b * h_q + it.kh * g + n) * s_stride + p;
-                    if (vst && t0 + 16 <= it.c1) {
-                        if (n < g) *reinterpret_cast<f32x4*>(dst) = acc;
-                    } else if (t0 < it.c1) {
-#pragma unroll
-                        for (int e = 0; e < 4; ++e)
-                            if (n < g && p + e < it.c1) dst[e] = acc[e];
-                    }
-                }
+                for (int v = 0; v < NV; ++v) acc = Mfma<T>::step(buf[s][u][v], bq[ht][v], acc);
+                sink(ht, r0, r0 + 4 * grp, acc * scale);
             }
+        }
+    }
+};
+
+// ---- dense mode: fp32 logits ------------------------------------------------------
+
+template <typename T, int DH, int NHT>
+__global__ __launch_bounds__(256) void kscan(const T* __restrict__ q, const T* __restrict__ k,
+                                             const int32_t* __restrict__ lens,
+                                             float* __restrict__ scores, int64_t s_stride,
+                                             int h_q, int h_k, int64_t S_max, int nchunk,
+                                             int nwork, float scale, bool vst) {
+    using S = Streamer<T, DH, NHT>;
+    constexpr int NS = S::NS;
+    const int g = h_q / h_k;
+    const int lane = threadIdx.x & 63;
+    S sm(threadIdx.x >> 6, lane);
+
+    auto len_of = [&](int b) { return lens[b]; };
+    Item<T> it;
+    int w = next_item<T, DH>(blockIdx.x, gridDim.x, nwork, nchunk, h_k, S_max, len_of, k, it);
+    if (w >= nwork) return;
+    sm.load_q(q + (int64_t)(it.b * h_q + it.kh * g) * DH, g);
+#pragma unroll
+    for (int s = 0; s < NS; ++s) sm.load(s, it, s);
+
+    auto sink = [&](int ht, int r0, int off, f32x4 acc) {
+        const int n = ht * 16 + sm.r16;
+        float* dst = scores + (int64_t)(it.b * h_q + it.kh * g + n) * s_stride + it.c0 + off;
+        if (vst && r0 + 16 <= it.n) {
+            if (n < g) *reinterpret_cast<f32x4*>(dst) = acc;
+        } else if (r0 < it.n) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                if (n < g && off + e < it.n) dst[e] = acc[e];
         }
     };
-
-    // Candidate extraction for one head (TOPM): the wave reads the head's keys
-    // (position lane + 64 e, conflict-free) into registers and finds a cutoff by
-    // MSB-first bisection on the key: count(key >= x) comes from ballots and
-    // scalar popcounts, so the search needs no LDS traffic and no atomics. It
-    // stops at the first prefix with M <= count <= M + M/8 (or at 20 bits). Every
-    // key >= cutoff is then staged in the head's LDS row in ascending position
-    // order and written out with 16-byte stores.
-    auto extract = [&](const Item& it, int n, uint32_t M) {
-        const int nvalid = (int)(it.c1 - it.c0);
-        uint32_t* row = &lds_keys[n * kScanChunk];
-        uint32_t kk[16];
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-            const int j = lane + 64 * e;
-            kk[e] = j < nvalid ? row[j] : 0u;
-        }
-        __builtin_amdgcn_s_waitcnt(0xc07f);   // keys are in registers before the row is reused
-        uint32_t cut = 0;   // publish everything when the chunk holds <= M keys
-        if ((uint32_t)nvalid > M) {
-            const uint32_t hi = M + (M >> 3);
-            uint32_t prefix = 0;
 #pragma unroll 1
-            for (int bit = 31; bit >= 12; --bit) {
-                const uint32_t x = prefix | (1u << bit);
-                uint32_t cnt = 0;
+    while (true) {
+        // stages cover the chunk's rows, rounded up to a multiple of NS
+        int nst = (it.n + S::STAGE - 1) / S::STAGE;
+        nst = (nst + NS - 1) / NS * NS;
+        // Loads are unconditional: past the chunk the rows clamp to its last row
+        // (a cache hit), and straight-line loads keep the wait counts exact. The
+        // first round is peeled off the loop: it is the one that waits for the
+        // item's query loads, so the loop header only ever waits for one stage.
+        auto round = [&](int st) {
 #pragma unroll
-                for (int e = 0; e < 16; ++e) cnt += (uint32_t)__popcll(ballot(kk[e] >= x));
-                if (cnt >= M) {
-                    prefix = x;
-                    if (cnt <= hi) break;
+            for (int s = 0; s < NS; ++s) {
+                sm.consume(s, st + s, scale, sink);
+                sm.load(s, it, st + s + NS);
+            }
+        };
+        int st = 0;
+        if (nst > NS) {
+            round(0);
+            st = NS;
+        }
+#pragma unroll 1
+        for (; st < nst - NS; st += NS) round(st);
+        Item<T> nx;
+        const int wn = next_item<T, DH>(w + gridDim.x, gridDim.x, nwork, nchunk, h_k, S_max,
+                                        len_of, k, nx);
+        if (wn >= nwork) nx = it;   // re-read this item's rows; never consumed
+        asm volatile("" : "+s"(st));   // keep the last round's offsets out of loop-invariant registers
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+            sm.consume(s, st + s, scale, sink);
+            sm.load(s, nx, s);
+        }
+        if (wn >= nwork) break;
+        sm.load_q(q + (int64_t)(nx.b * h_q + nx.kh * g) * DH, g);
+        w = wn;
+        it = nx;
+    }
+}
+
+// ---- top-M mode: producer / consumer workgroup --------------------------------------
+
+// Candidate extraction of head n of item `it` by one consumer wave, from the
+// head's key row in LDS (every offset of the row was written for this item, 0
+// past the chunk's end). Lane l takes offsets [16 l, 16 l + 16), so lane order
+// is position order. The cutoff is a key with M <= count(key >= cutoff) <=
+// M + M/4 where one is found within a bracket of 2^12, else the largest probed
+// key with count >= M. The search starts from the cutoff this wave found for
+// the same head on its previous item (the workgroup walks consecutive chunks
+// of a row, so that is usually close), gallops away from it and bisects;
+// without a previous cutoff it bisects the whole key range. Counts are
+// per-lane vector sums reduced once per probe.
+// The keys at or above the cutoff are then written in position order: a
+// prefix scan of the per-lane counts gives each lane its first slot.
+template <typename T>
+__device__ inline void extract(const Item<T>& it, int n, uint32_t M, uint32_t* row,
+                               uint32_t* warm, uint32_t* cursor, int lane, int g, int h_q,
+                               int nchunk, const TopmOut& tm) {
+    uint32_t kk[16];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const u32x4 v = *reinterpret_cast<const u32x4*>(row + 16 * lane + 4 * j);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) kk[4 * j + c] = v[c];
+    }
+    const uint32_t guess = warm[n];
+    __builtin_amdgcn_s_waitcnt(0xc07f);   // keys are in registers before the row is reused
+    auto count_ge = [&](uint32_t x) -> uint32_t {
+        uint32_t c = 0;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) c += kk[e] >= x ? 1u : 0u;
+        return wave_sum(c);
+    };
+    uint32_t cut = 0;   // publish everything when the chunk holds <= M keys
+    if ((uint32_t)it.n > M) {
+        const uint32_t hi = M + (M >> 2);
+        // Invariant of the search: count(key >= a) >= M (a = 0 counts every
+        // slot) and count(key >= z) < M (z = 2^32, as a 64-bit bound).
+        uint32_t a = 0;
+        uint64_t z = 1ull << 32;
+        bool done = false;
+        if (guess != 0u) {
+            // gallop from the previous cutoff in steps that double from 2^18
+            // (about 3 % of the value for an fp32 logit) until the count
+            // crosses M, then bisect between the last two probes
+            uint32_t c = count_ge(guess);
+            if (c >= M && c <= hi) {
+                cut = guess;
+                done = true;
+            } else if (c > hi) {
+                a = guess;
+                uint64_t step = 1ull << 18;
+#pragma unroll 1
+                while (true) {
+                    const uint64_t x = (uint64_t)a + step;
+                    if (x >= z) break;
+                    c = count_ge((uint32_t)x);
+                    if (c < M) { z = x; break; }
+                    a = (uint32_t)x;
+                    if (c <= hi) { cut = a; done = true; break; }
+                    step <<= 1;
+                }
+            } else {
+                z = guess;
+                uint64_t step = 1ull << 18;
+#pragma unroll 1
+                while (true) {
+                    if ((uint64_t)a + step >= z) break;
+                    const uint32_t x = (uint32_t)(z - step);
+                    c = count_ge(x);
+                    if (c >= M) {
+                        a = x;
+                        if (c <= hi) { cut = a; done = true; }
+                        break;
+                    }
+                    z = x;
+                    step <<= 1;
                 }
             }
-            cut = prefix;
         }
-        const int64_t slot = ((int64_t)(it.b * h_q + it.kh * g + n) * nchunk + it.chunk);
-        uint2* dst = tm.cand + slot * kScanChunk;
-        uint2* stage = reinterpret_cast<uint2*>(row);   // 512 entries
-        uint32_t base = 0;
+        if (!done) {
+            // bisection of [a, z) down to a width of 2^12
+#pragma unroll 1
+            while (z - a > (1ull << 12)) {
+                const uint32_t x = (uint32_t)(a + ((z - a) >> 1));
+                const uint32_t c = count_ge(x);
+                if (c >= M) {
+                    a = x;
+                    if (c <= hi) break;
+                } else {
+                    z = x;
+                }
+            }
+            cut = a;
+        }
+        if (lane == 0) warm[n] = cut;
+    }
+    const uint32_t lo = cut > 1u ? cut : 1u;   // key 0 marks an empty slot
+    uint32_t kc = 0;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) kc += kk[e] >= lo ? 1u : 0u;
+    uint32_t total;
+    const uint32_t first = wave_incl_scan(kc, total) - kc;
+    const int64_t slot = ((int64_t)(it.b * h_q + it.kh * g + n) * nchunk + it.chunk);
+    // the list goes to the next free (16-byte aligned) place of the item's pool region
+    uint32_t off = 0;
+    if (lane == 0) off = atomicAdd(cursor, (total + 1u) & ~1u);
+    off = __builtin_amdgcn_readfirstlane(off);
+    uint2* dst = tm.cand + ((int64_t)(it.bkh * nchunk + it.chunk) * g) * kScanChunk + off;
+    uint32_t pos0 = (uint32_t)(it.c0 + 16 * lane);
+    asm volatile("" : "+v"(pos0));   // positions are formed at each store, not held in registers
+    if (total <= kStageMax) {
+        uint2* stage = reinterpret_cast<uint2*>(row);
+        uint32_t at = first;
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-            const bool keep = kk[e] != 0u && kk[e] >= cut;
-            const uint64_t m = ballot(keep);
-            if (keep) {
-                const uint32_t at = base + lanes_below(m);
-                const uint2 v = make_uint2((uint32_t)(it.c0 + lane + 64 * e), kk[e]);
-                if (at < kScanChunk / 2) stage[at] = v; else dst[at] = v;
-            }
-            base += (uint32_t)__popcll(m);
+            const uint32_t keep = kk[e] >= lo ? 1u : 0u;
+            stage[keep ? at : kStageMax + lane] = make_uint2(pos0 + e, kk[e]);
+            at += keep;
         }
         __builtin_amdgcn_s_waitcnt(0xc07f);
-        const uint32_t staged = base < kScanChunk / 2 ? base : kScanChunk / 2;
-        for (uint32_t j = 2 * lane; j < staged; j += 128) {
+        for (uint32_t j = 2 * lane; j < total; j += 128) {
             u32x4 v2;
             const uint2 a0 = stage[j];
-            const uint2 a1 = j + 1 < staged ? stage[j + 1] : make_uint2(0u, 0u);
+            const uint2 a1 = j + 1 < total ? stage[j + 1] : make_uint2(0u, 0u);
             v2[0] = a0.x; v2[1] = a0.y; v2[2] = a1.x; v2[3] = a1.y;
             *reinterpret_cast<u32x4*>(dst + j) = v2;   // dst + j is 16-byte aligned (j even)
         }
-        if (lane == 0) {
-            tm.cnt[slot] = (int32_t)base;
-            tm.cut[slot] = cut;
-        }
-    };
+    } else {
+        uint32_t at = first;
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+            if (kk[e] >= lo) dst[at++] = make_uint2(pos0 + e, kk[e]);
+    }
+    if (lane == 0) tm.meta[slot] = make_uint4(off, total, cut, 0u);
+}
 
-    Item it;
-    int w = next_item(blockIdx.x, it);
-    if (w >= nwork) return;
-    load_q(it);
-    load(A, it, 0);
-    load(Bv, it, 1);
+// LDS layout of kscan_topm (32-bit words):
+//   keys [2][g][kScanChunk]   double-buffered key rows of the current items
+//   warm [g]                  previous cutoff per head
+//   cursor [2]                next free entry of the item's pool region (by item parity)
+__host__ __device__ constexpr size_t topm_lds_words(int g) {
+    return (size_t)2 * g * kScanChunk + g + 2;
+}
+
+template <typename T, int DH>
+__global__ __launch_bounds__(kTopmThreads, 1) void kscan_topm(
+        const T* __restrict__ q, const T* __restrict__ k, const int32_t* __restrict__ lens,
+        int h_q, int h_k, int64_t S_max, int nchunk, int nwork, float scale, TopmOut tm) {
+    using S = Streamer<T, DH, 1>;
+    constexpr int NS = S::NS;
+    extern __shared__ uint32_t lds[];
+    const int g = h_q / h_k;
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const bool producer = wave < kWaves;
+    uint32_t* keys = lds;
+    uint32_t* warm = lds + 2 * g * kScanChunk;
+    uint32_t* cursor = warm + g;
+
+    // The workgroup takes a contiguous range of items (consecutive chunks of a
+    // row), so that each head's previous cutoff is a good first guess.
+    const int per = (nwork + gridDim.x - 1) / gridDim.x;
+    const int wbeg = blockIdx.x * per;
+    const int wend = wbeg + per < nwork ? wbeg + per : nwork;
+    if (wbeg >= wend) return;   // uniform over the workgroup
+    auto len_of = [&](int b) { return lens[b]; };   // uniform index: a scalar load
+
+    Item<T> cur;
+    int w = next_item<T, DH>(wbeg, 1, wend, nchunk, h_k, S_max, len_of, k, cur);
+    if (w >= wend) return;   // uniform over the workgroup
+    S sm(wave, lane);
+    // producers: the next item's query operand is prefetched into bqn while
+    // the current item streams
+    u32x4 bqn[S::NV];
+    auto qrow = [&](const Item<T>& it) { return q + (int64_t)(it.b * h_q + it.kh * g) * DH; };
+    if (producer) {
+        sm.load_q(qrow(cur), g);
+#pragma unroll
+        for (int s = 0; s < NS; ++s) sm.load(s, cur, s);
+    } else {
+        for (int n = wave - kWaves; n < g; n += kConsumers)
+            if (lane == 0) warm[n] = 0u;
+        if (threadIdx.x == 64 * kWaves) cursor[0] = cursor[1] = 0u;
+    }
+    lds_barrier();
+
+    Item<T> prev = cur;
+    bool have_prev = false;
+    int t = 0;
 #pragma unroll 1
     while (true) {
-        // stages cover [c0, c1); an even count keeps the ping-pong loop simple
-        int nst = (int)((it.c1 - it.c0 + STAGE - 1) / STAGE);
-        nst += nst & 1;
+        const bool have_cur = w < wend;
+        if (!have_cur && !have_prev) break;   // uniform
+        Item<T> nx = cur;
+        const int wn = have_cur ? next_item<T, DH>(w + 1, 1, wend, nchunk, h_k, S_max, len_of, k,
+                                                   nx)
+                                : wend;
+        if (producer) {
+            if (have_cur) {
+                uint32_t* kbuf = keys + (t & 1) * g * kScanChunk;
+                {
+                    const int n = sm.r16;   // next item's query operand (nx == cur after the last)
+#pragma unroll
+                    for (int v = 0; v < S::NV; ++v)
+                        bqn[v] = n < g ? *reinterpret_cast<const u32x4*>(
+                                             qrow(nx) + (int64_t)n * DH + v * 4 * S::EV +
+                                             sm.grp * S::EV)
+                                       : u32x4{0u, 0u, 0u, 0u};
+                }
+                // keys of positions past the chunk are 0, below every real key;
+                // rem is opaque to the optimiser so that the per-stage offsets
+                // are not hoisted out of the item loop (they would be spilled)
+                auto sink = [&](int, int, int off, f32x4 acc) {
+                    int rem = cur.n - off;
+                    asm volatile("" : "+v"(rem));
+                    if (sm.r16 < g) {
+                        u32x4 kv;
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) kv[e] = (e < rem) ? float_key(acc[e]) : 0u;
+                        *reinterpret_cast<u32x4*>(&kbuf[sm.r16 * kScanChunk + off]) = kv;
+                    }
+                };
+                // Every stage of the chunk runs, so each key row is fully
+                // rewritten; rows past the chunk clamp to its last row (cache
+                // hits). The first round is peeled off the loop (it waits for
+                // the query operand); the last round loads the next item.
+                constexpr int nst = kScanChunk / S::STAGE;
+                static_assert(nst % NS == 0 && nst >= 2 * NS, "chunk must span >= 2 rounds");
+                auto round = [&](int st) {
+#pragma unroll
+                    for (int s = 0; s < NS; ++s) {
+                        sm.consume(s, st + s, scale, sink);
+                        sm.load(s, cur, st + s + NS);
+                    }
+                };
+                round(0);
+                int st = NS;
 #pragma unroll 1
-        for (int st = 0; st < nst; st += 2) {
-            // unconditional: past the chunk the rows clamp to its last row (a
-            // cache hit), and straight-line loads keep the wait counts exact
-            consume(A, it, st);
-            load(A, it, st + 2);
-            consume(Bv, it, st + 1);
-            load(Bv, it, st + 3);
-        }
-        // issue the next item's loads before this item's publishing stores, so
-        // that waiting for them never waits for the stores
-        Item nx;
-        const int wn = next_item(w + gridDim.x, nx);
-        if (wn < nwork) {
-            load_q(nx);
-            load(A, nx, 0);
-            load(Bv, nx, 1);
-        }
-        if (TOPM) {
-            lds_barrier();   // all keys of the chunk are in LDS
-            int64_t expct = ((int64_t)tm.N * kScanChunk + it.L - 1) / it.L;
-            int64_t M64 = 2 * expct + 32;   // twice the chunk's expected share, plus a margin
-            const uint32_t M = (uint32_t)(M64 < kScanChunk ? M64 : kScanChunk);
+                for (; st < nst - NS; st += NS) round(st);
+                asm volatile("" : "+s"(st));
+                // after the last item nx == cur: these re-reads are never consumed
+#pragma unroll
+                for (int s = 0; s < NS; ++s) {
+                    sm.consume(s, st + s, scale, sink);
+                    sm.load(s, nx, s);
+                }
+#pragma unroll
+                for (int v = 0; v < S::NV; ++v) sm.bq[0][v] = bqn[v];
+            }
+        } else {
+            if (have_prev) {
+                // M: 1.5 times the chunk's expected share of the row's top N, plus
+                // a margin (a heuristic: any M gives exact results, M only sets
+                // how often the selector has to recompute a head)
+                const float share = (float)tm.N * (float)kScanChunk / (float)prev.L;
+                const uint32_t M = share >= (float)(kScanChunk / 2)
+                                       ? (uint32_t)kScanChunk
+                                       : (uint32_t)__builtin_ceilf(1.5f * share) + 16u;
+                uint32_t* kbuf = keys + ((t + 1) & 1) * g * kScanChunk;
 #pragma unroll 1
-            for (int n = wave; n < g; n += kWaves) extract(it, n, M);
-            lds_barrier();   // LDS is rewritten by the next item
+                for (int n = wave - kWaves; n < g; n += kConsumers)
+                    extract(prev, n, M, kbuf + n * kScanChunk, warm, cursor + (t & 1), lane, g,
+                            h_q, nchunk, tm);
+            }
+            // the cursor of the next item's extraction starts from 0
+            if (threadIdx.x == 64 * kWaves) cursor[(t + 1) & 1] = 0u;
         }
-        if (wn >= nwork) break;
-        w = wn;
-        it = nx;
+        lds_barrier();   // keys of item t are complete; buffer (t - 1) & 1 is free again
+        prev = cur;
+        have_prev = have_cur;
+        if (have_cur) {
+            w = wn;
+            cur = nx;
+        }
+        ++t;
     }
 }
 
@@ -315,18 +562,21 @@ int cu_count() {
 // them waits for another to finish all of its work before starting), at most
 // one per work item. Residency per CU is queried once per kernel and LDS size.
 template <typename K>
-int resident_grid(K kern, size_t lds, int nwork) {
-    static int cached_lds[8] = {-1, -1, -1, -1, -1, -1, -1, -1};
-    static int cached_blocks[8] = {0};
+int resident_grid(K kern, int threads, size_t lds, int nwork) {
+    static const void* cached_k[16] = {nullptr};
+    static int cached_lds[16] = {0};
+    static int cached_blocks[16] = {0};
     int per_cu = 0;
-    for (int i = 0; i < 8; ++i)
-        if (cached_lds[i] == (int)lds) per_cu = cached_blocks[i];
+    for (int i = 0; i < 16; ++i)
+        if (cached_k[i] == (const void*)kern && cached_lds[i] == (int)lds) per_cu = cached_blocks[i];
     if (per_cu == 0) {
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, 256, lds) != hipSuccess ||
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, threads, lds) !=
+                hipSuccess ||
             per_cu <= 0)
             per_cu = 1;
-        for (int i = 0; i < 8; ++i)
-            if (cached_lds[i] < 0) {
+        for (int i = 0; i < 16; ++i)
+            if (cached_k[i] == nullptr) {
+                cached_k[i] = (const void*)kern;
                 cached_lds[i] = (int)lds;
                 cached_blocks[i] = per_cu;
                 break;
@@ -337,43 +587,46 @@ int resident_grid(K kern, size_t lds, int nwork) {
 }
 
 template <typename T, int DH>
-hipError_t go(int nht, const void* q, const void* k, const int32_t* lens, float* scores,
-              int64_t s_stride, int B, int h_q, int h_k, int64_t S_max, bool vst,
-              const TopmOut* tm, hipStream_t st) {
+hipError_t go_dense(int nht, const void* q, const void* k, const int32_t* lens, float* scores,
+                    int64_t s_stride, int B, int h_q, int h_k, int64_t S_max, bool vst,
+                    hipStream_t st) {
     const int nchunk = (int)((S_max + kScanChunk - 1) / kScanChunk);
     const int nwork = B * h_k * nchunk;
     const float scale = (float)(1.0 / __builtin_sqrt((double)DH));
-    const TopmOut none{};
-    if (tm) {
-        // top-M mode: one 16-head tile (g <= 16), keys of the chunk in LDS
-        auto kern = &kscan<T, DH, 1, true>;
-        const size_t lds = (size_t)(h_q / h_k) * kScanChunk * sizeof(uint32_t);
-        static bool attr_set = false;   // one per instantiation: allow > 64 KiB of dynamic LDS
-        if (!attr_set) {
-            if (hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                    hipFuncAttributeMaxDynamicSharedMemorySize,
-                                    (int)(16 * kScanChunk * sizeof(uint32_t))) != hipSuccess)
-                return hipGetLastError();
-            attr_set = true;
-        }
-        const int grid = resident_grid(kern, lds, nwork);
-        hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(256), lds, st, (const T*)q,
-                           (const T*)k, lens, nullptr, 0, h_q, h_k, S_max, nchunk, nwork, scale,
-                           false, *tm);
-        return hipGetLastError();
-    }
 #define SAGA_KS(NH)                                                                            \
     {                                                                                          \
-        auto kern = &kscan<T, DH, NH, false>;                                                  \
-        const int grid = resident_grid(kern, 0, nwork);                                        \
+        auto kern = &kscan<T, DH, NH>;                                                         \
+        const int grid = resident_grid(kern, 256, 0, nwork);                                   \
         hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(256), 0, st, (const T*)q,         \
                            (const T*)k, lens, scores, s_stride, h_q, h_k, S_max, nchunk,       \
-                           nwork, scale, vst, none);                                           \
+                           nwork, scale, vst);                                                 \
     }
     if (nht <= 1) SAGA_KS(1)
     else if (nht <= 2) SAGA_KS(2)
     else SAGA_KS(4)
 #undef SAGA_KS
+    return hipGetLastError();
+}
+
+template <typename T, int DH>
+hipError_t go_topm(const void* q, const void* k, const int32_t* lens, const TopmOut& tm, int B,
+                   int h_q, int h_k, int64_t S_max, hipStream_t st) {
+    const int nchunk = (int)((S_max + kScanChunk - 1) / kScanChunk);
+    const int nwork = B * h_k * nchunk;
+    const float scale = (float)(1.0 / __builtin_sqrt((double)DH));
+    auto kern = &kscan_topm<T, DH>;
+    const size_t lds = topm_lds_words(h_q / h_k) * sizeof(uint32_t);
+    static bool attr_set = false;   // one per instantiation: allow > 64 KiB of dynamic LDS
+    if (!attr_set) {
+        if (hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                hipFuncAttributeMaxDynamicSharedMemorySize,
+                                (int)(topm_lds_words(16) * sizeof(uint32_t))) != hipSuccess)
+            return hipGetLastError();
+        attr_set = true;
+    }
+    const int grid = resident_grid(kern, kTopmThreads, lds, nwork);
+    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kTopmThreads), lds, st, (const T*)q,
+                       (const T*)k, lens, h_q, h_k, S_max, nchunk, nwork, scale, tm);
     return hipGetLastError();
 }
 
@@ -385,20 +638,20 @@ hipError_t launch_kscan(const void* q, const void* k, const int32_t* lens, float
     const int nht = (h_q / h_k + 15) / 16;   // 16-head tiles: 1, 2 or 4 (g <= 64)
     const bool vst = (s_stride % 4 == 0) && ((reinterpret_cast<uintptr_t>(scores) & 15) == 0);
     if (bf16)
-        return d == 64 ? go<uint16_t, 64>(nht, q, k, lens, scores, s_stride, B, h_q, h_k, S_max, vst, nullptr, st)
-                       : go<uint16_t, 128>(nht, q, k, lens, scores, s_stride, B, h_q, h_k, S_max, vst, nullptr, st);
-    return d == 64 ? go<float, 64>(nht, q, k, lens, scores, s_stride, B, h_q, h_k, S_max, vst, nullptr, st)
-                   : go<float, 128>(nht, q, k, lens, scores, s_stride, B, h_q, h_k, S_max, vst, nullptr, st);
+        return d == 64 ? go_dense<uint16_t, 64>(nht, q, k, lens, scores, s_stride, B, h_q, h_k, S_max, vst, st)
+                       : go_dense<uint16_t, 128>(nht, q, k, lens, scores, s_stride, B, h_q, h_k, S_max, vst, st);
+    return d == 64 ? go_dense<float, 64>(nht, q, k, lens, scores, s_stride, B, h_q, h_k, S_max, vst, st)
+                   : go_dense<float, 128>(nht, q, k, lens, scores, s_stride, B, h_q, h_k, S_max, vst, st);
 }
 
 hipError_t launch_kscan_topm(const void* q, const void* k, const int32_t* lens, const TopmOut& tm,
                              int B, int h_q, int h_k, int d, int64_t S_max, bool bf16,
                              hipStream_t st) {
     if (bf16)
-        return d == 64 ? go<uint16_t, 64>(1, q, k, lens, nullptr, 0, B, h_q, h_k, S_max, false, &tm, st)
-                       : go<uint16_t, 128>(1, q, k, lens, nullptr, 0, B, h_q, h_k, S_max, false, &tm, st);
-    return d == 64 ? go<float, 64>(1, q, k, lens, nullptr, 0, B, h_q, h_k, S_max, false, &tm, st)
-                   : go<float, 128>(1, q, k, lens, nullptr, 0, B, h_q, h_k, S_max, false, &tm, st);
+        return d == 64 ? go_topm<uint16_t, 64>(q, k, lens, tm, B, h_q, h_k, S_max, st)
+                       : go_topm<uint16_t, 128>(q, k, lens, tm, B, h_q, h_k, S_max, st);
+    return d == 64 ? go_topm<float, 64>(q, k, lens, tm, B, h_q, h_k, S_max, st)
+                   : go_topm<float, 128>(q, k, lens, tm, B, h_q, h_k, S_max, st);
 }
 
 }  // namespace saga

@@ -23,9 +23,8 @@ inline int64_t score_stride(int64_t S_max) { return round_up(S_max, 16); }
 
 struct Workspace {
     float* scores;      // [B][h_q][score_stride]  dense logits (dense path, fallback rows)
-    uint2* cand;        // [B][h_q][nchunk][kScanChunk]  top-M candidate lists
-    int32_t* cand_cnt;  // [B][h_q][nchunk]
-    uint32_t* cand_cut; // [B][h_q][nchunk]
+    uint2* cand;        // candidate pool: B*h_k*nchunk items x g*kScanChunk entries
+    uint4* cand_meta;   // [B][h_q][nchunk]  {offset in the item's pool region, count, cutoff, 0}
     int32_t* row_flag;  // [B][h_q]   1 if the row took the dense fallback in the last call
     int32_t* sel_idx;   // [B][h_q][N]
     float* sel_val;     // [B][h_q][N]
@@ -49,13 +48,15 @@ Workspace carve(void* base, int B, int h_q, int d, int N, int64_t S_max, bool de
 int sparse_nsplit(int N);          // ceil(N / kPvEntries)
 int dense_nsplit(int64_t S_max);   // ceil(S_max / kDenseRows)
 
-// Candidate lists published by the top-M K-scan, per (b*h_q + i, chunk) slot:
-// cand[slot][0..cnt) = (position, key) ascending in position, cut[slot] = the
-// chunk's cutoff key (every key of the chunk left out is below it).
+// Candidate lists published by the top-M K-scan. Work item w = (b*h_k + kh) *
+// nchunk + chunk owns the pool region cand[w*g*kScanChunk, (w+1)*g*kScanChunk),
+// where the lists of its g heads are packed in any order. For slot
+// (b*h_q + i, chunk): meta = {off, cnt, cut, 0} with the list at
+// cand[w*g*kScanChunk + off, +cnt) = (position, key) ascending in position,
+// and cut = the chunk's cutoff key (every key of the chunk left out is below it).
 struct TopmOut {
-    uint2* cand;       // [B*h_q][nchunk][kScanChunk]
-    int32_t* cnt;      // [B*h_q][nchunk]
-    uint32_t* cut;     // [B*h_q][nchunk]
+    uint2* cand;
+    uint4* meta;       // [B*h_q][nchunk]
     int N;
 };
 
@@ -132,6 +133,36 @@ __device__ inline uint32_t lanes_below(uint64_t m) {
 }
 
 __device__ inline uint64_t ballot(bool p) { return __ballot(p); }
+
+// Inclusive prefix sum over the 64 lanes of a wave: row_shr DPP steps inside
+// each row of 16 lanes, then the row totals (read from lanes 15, 31, 47) are
+// added to the later rows. `total` receives the sum over all lanes.
+__device__ inline uint32_t wave_incl_scan(uint32_t v, uint32_t& total) {
+    int x = (int)v;
+    x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, false);   // row_shr:1
+    x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, false);   // row_shr:2
+    x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, false);   // row_shr:4
+    x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, false);   // row_shr:8
+    const uint32_t r0 = (uint32_t)__builtin_amdgcn_readlane(x, 15);
+    const uint32_t r1 = (uint32_t)__builtin_amdgcn_readlane(x, 31);
+    const uint32_t r2 = (uint32_t)__builtin_amdgcn_readlane(x, 47);
+    const uint32_t r3 = (uint32_t)__builtin_amdgcn_readlane(x, 63);
+    total = r0 + r1 + r2 + r3;
+    const int row = (int)(threadIdx.x & 63) >> 4;
+    const uint32_t add = (row >= 1 ? r0 : 0u) + (row >= 2 ? r1 : 0u) + (row >= 3 ? r2 : 0u);
+    return (uint32_t)x + add;
+}
+
+// Sum over the 64 lanes of a wave (uniform result).
+__device__ inline uint32_t wave_sum(uint32_t v) {
+    int x = (int)v;
+    x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, false);
+    x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, false);
+    x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, false);
+    x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, false);
+    return (uint32_t)__builtin_amdgcn_readlane(x, 15) + (uint32_t)__builtin_amdgcn_readlane(x, 31) +
+           (uint32_t)__builtin_amdgcn_readlane(x, 47) + (uint32_t)__builtin_amdgcn_readlane(x, 63);
+}
 
 }  // namespace dev
 }  // namespace saga

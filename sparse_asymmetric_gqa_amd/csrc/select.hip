@@ -93,16 +93,17 @@ struct DenseSrc {
     }
 };
 
-// Candidate lists of one row: chunk k holds cnt_k entries at base + k*kScanChunk;
-// pref[] (LDS) is the exclusive prefix of the counts. Element j of the union
-// (chunk-major, so ascending in position) sits in slot s of lane l of wave w
-// with j = tile*CAP + w*SEG + 64 s + l.
+// Candidate lists of one row: chunk k holds cnt_k entries at base + coff[k]
+// (coff in LDS, 64-bit pool offsets); pref[] (LDS) is the exclusive prefix of
+// the counts. Element j of the union (chunk-major, so ascending in position)
+// sits in slot s of lane l of wave w with j = tile*CAP + w*SEG + 64 s + l.
 template <int KPT, int NW>
 struct UnionSrc {
     static constexpr int GROUP = 1;
     static constexpr int SEG = KPT * 64;
     static constexpr int CAP = NW * SEG;
     const uint2* base;
+    const int64_t* coff;   // LDS, nch entries
     const int32_t* pref;   // LDS, nch + 1 entries
     int nch;
     int64_t n;             // total candidates
@@ -126,7 +127,7 @@ struct UnionSrc {
             pos[s] = -1;
             if (j < n) {
                 while (pref[kc + 1] <= j) ++kc;
-                const uint2 e = base[(int64_t)kc * kScanChunk + (j - pref[kc])];
+                const uint2 e = base[coff[kc] + (j - pref[kc])];
                 pos[s] = (int32_t)e.x;
                 key[s] = e.y;
             }
@@ -412,8 +413,8 @@ __device__ void head_logits(const T* __restrict__ q, const T* __restrict__ k, in
 
 template <typename T, int DH>
 __global__ __launch_bounds__(kUnionThreads) void select_union(
-    const uint2* __restrict__ cand, const int32_t* __restrict__ cand_cnt,
-    const uint32_t* __restrict__ cand_cut, const int32_t* __restrict__ lens, int h_q, int h_k,
+    const uint2* __restrict__ cand, const uint4* __restrict__ cand_meta,
+    const int32_t* __restrict__ lens, int h_q, int h_k,
     int N, int64_t S_max, int nchunk, int32_t* __restrict__ sel_idx, float* __restrict__ sel_val,
     float* __restrict__ row_max, int32_t* __restrict__ row_cnt, int32_t* __restrict__ idx_out,
     int32_t* __restrict__ row_flag, const T* __restrict__ q, const T* __restrict__ k,
@@ -423,6 +424,7 @@ __global__ __launch_bounds__(kUnionThreads) void select_union(
     constexpr int KPT = kUnionKPT;
     __shared__ SelShared sh;
     __shared__ int32_t pref[kMaxChunks + 1];
+    __shared__ int64_t coff[kMaxChunks];
     __shared__ uint32_t bad;
     const int row = blockIdx.x;
     const int b = row / h_q;
@@ -447,13 +449,19 @@ __global__ __launch_bounds__(kUnionThreads) void select_union(
         return;
     }
     const int nch = (int)((L + kScanChunk - 1) / kScanChunk);
-    const int32_t* cnt = cand_cnt + (int64_t)row * nchunk;
-    const uint32_t* cut = cand_cut + (int64_t)row * nchunk;
+    const uint4* meta = cand_meta + (int64_t)row * nchunk;
+    const int g = h_q / h_k;
+    // pool region of this row's chunk c: item (b*h_k + kh)*nchunk + c
+    const int64_t item0 = (int64_t)(b * h_k + i / g) * nchunk;
 
     // exclusive prefix of the chunk counts: each thread sums a contiguous run
     const int per = (nch + NT - 1) / NT;
     int32_t run = 0;
-    for (int c = tid * per; c < nch && c < (tid + 1) * per; ++c) run += cnt[c];
+    for (int c = tid * per; c < nch && c < (tid + 1) * per; ++c) {
+        const uint4 m = meta[c];
+        coff[c] = (item0 + c) * g * kScanChunk + m.x;
+        run += (int32_t)m.y;
+    }
     int32_t incl = run;
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
@@ -467,7 +475,7 @@ __global__ __launch_bounds__(kUnionThreads) void select_union(
     for (int w = 0; w < wave; ++w) off += (int32_t)sh.wtot[w];
     for (int c = tid * per; c < nch && c < (tid + 1) * per; ++c) {
         pref[c] = off;
-        off += cnt[c];
+        off += (int32_t)meta[c].y;
     }
     if (tid == NT - 1) pref[nch] = off;   // last thread's running sum = total
     __syncthreads();
@@ -480,7 +488,7 @@ __global__ __launch_bounds__(kUnionThreads) void select_union(
     bool ok = total >= n_eff;
     if (ok) {
         using Src = UnionSrc<KPT, NW>;
-        const Src src{cand + (int64_t)row * nchunk * kScanChunk, pref, nch, total};
+        const Src src{cand, coff, pref, nch, total};
         const int ntiles = (int)((total + Src::CAP - 1) / Src::CAP);
         if (ntiles == 1) {
             src.load(0, key, pos);
@@ -490,7 +498,7 @@ __global__ __launch_bounds__(kUnionThreads) void select_union(
         }
         // exact iff every chunk's cutoff is <= the union's threshold key
         for (int c = tid; c < nch; c += NT)
-            if (cut[c] > thr) bad = 1u;
+            if (meta[c].z > thr) bad = 1u;
         __syncthreads();
         ok = bad == 0u;
         if (ok) compact<NT, KPT>(src, ntiles, thr, krem, (uint32_t)n_eff, key, pos, sh, oi, ov, ou);
@@ -554,7 +562,7 @@ hipError_t launch_select_union(const TopmOut& tm, const int32_t* lens, int B, in
     const float scale = (float)(1.0 / __builtin_sqrt((double)d));
 #define SAGA_SU(T, D)                                                                            \
     hipLaunchKernelGGL((select_union<T, D>), dim3((unsigned)(B * h_q)), dim3(kUnionThreads), 0,   \
-                       st, tm.cand, tm.cnt, tm.cut, lens, h_q, h_k, N, S_max, nchunk, sel_idx,    \
+                       st, tm.cand, tm.meta, lens, h_q, h_k, N, S_max, nchunk, sel_idx,           \
                        sel_val, row_max, row_cnt, idx_out, row_flag, (const T*)q, (const T*)k,    \
                        scores, s_stride, scale)
     if (bf16) {
