@@ -17,8 +17,8 @@
 // covers every d exactly once whatever order the hardware sums in.
 //
 // Work is split into (b, key head, 1024-position chunk) items, walked by
-// persistent workgroups. A streaming wave keeps NS register stages of K tiles
-// in flight (four, or two for fp32 at d = 128), consumed in rotation with no
+// persistent workgroups. A streaming wave keeps NS = 2 register stages of K
+// tiles in flight, consumed in rotation with no
 // register copies; the last round of an item already loads the next item's
 // first stages.
 //
@@ -55,9 +55,9 @@ constexpr int kWaves = 4;          // streaming waves per workgroup (both kernel
 constexpr int kConsumers = 8;      // extracting waves of kscan_topm
 constexpr int kTopmThreads = 64 * (kWaves + kConsumers);
 constexpr int kTilesPerStage = SAGA_KSCAN_U;
-// Register stages in flight per streaming wave: four when a stage is at most
-// 16 VGPRs (bf16 at d = 128, either dtype at d = 64), two for fp32 at d = 128.
-__host__ __device__ constexpr int stages_for(int nv) { return nv >= 8 ? 2 : 4; }
+// Register stages in flight per streaming wave. Two measured faster than four
+// on the top-M K-scan (more loads in flight only raised their latency).
+__host__ __device__ constexpr int stages_for(int) { return 2; }
 // Candidates of one head staged in its own LDS row before the global write:
 // entries [0, kStageMax) hold data, [kStageMax, kStageMax + 64) are per-lane
 // sinks for the branch-free writes of entries that are not kept.
@@ -293,10 +293,10 @@ __device__ inline void extract(const Item<T>& it, int n, uint32_t M, uint32_t* r
     const uint32_t guess = warm[n];
     __builtin_amdgcn_s_waitcnt(0xc07f);   // keys are in registers before the row is reused
     auto count_ge = [&](uint32_t x) -> uint32_t {
-        uint32_t c = 0;
+        uint32_t c[4] = {0u, 0u, 0u, 0u};   // independent partial sums
 #pragma unroll
-        for (int e = 0; e < 16; ++e) c += kk[e] >= x ? 1u : 0u;
-        return wave_sum(c);
+        for (int e = 0; e < 16; ++e) c[e & 3] += kk[e] >= x ? 1u : 0u;
+        return wave_sum((c[0] + c[1]) + (c[2] + c[3]));
     };
     uint32_t cut = 0;   // publish everything when the chunk holds <= M keys
     if ((uint32_t)it.n > M) {
@@ -419,7 +419,7 @@ __global__ __launch_bounds__(kTopmThreads, 1) void kscan_topm(
     extern __shared__ uint32_t lds[];
     const int g = h_q / h_k;
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));   // wave-uniform
     const bool producer = wave < kWaves;
     uint32_t* keys = lds;
     uint32_t* warm = lds + 2 * g * kScanChunk;
