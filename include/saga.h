@@ -97,11 +97,11 @@ saga_status saga_decode_attn(const void* q, const void* k_cache, const void* v_c
 
 /*
  * saga_decode_attn with phase timing for benchmarks: identical work and
- * results, and records events[i] on `stream` for i < n_events (0..5) at phase
+ * results, and records events[i] on `stream` for i < n_events (0..4) at phase
  * boundary i: 0 before the K-scan, 1 after the K-scan (with its per-chunk
- * candidate extraction), 2 after top-N selection, 3 after the value gather,
- * 4 after the final merge. The events are created by the caller (timing
- * enabled); a null event or n_events outside 0..5 gives SAGA_ERR_INVALID_ARG.
+ * candidate extraction), 2 after top-N selection, 3 after the value gather
+ * (the end of the call). The events are created by the caller (timing
+ * enabled); a null event or n_events outside 0..4 gives SAGA_ERR_INVALID_ARG.
  */
 saga_status saga_decode_attn_timed(const void* q, const void* k_cache, const void* v_cache,
                                    const int32_t* seq_lens, float* out,

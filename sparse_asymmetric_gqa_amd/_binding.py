@@ -101,7 +101,7 @@ def saga_decode_attn(q, k_cache, v_cache, seq_lens, out, B, h_q, h_k, h_v, d, N,
 
 def saga_decode_attn_timed(q, k_cache, v_cache, seq_lens, out, B, h_q, h_k, h_v, d, N, stream,
                            S_max, dtype, workspace, workspace_bytes, idx_out, events) -> int:
-    """events: a sequence of 0..5 raw hipEvent_t handles (ints)."""
+    """events: a sequence of 0..4 raw hipEvent_t handles (ints)."""
     n = len(events)
     arr = (ctypes.c_void_p * max(n, 1))(*[ctypes.c_void_p(int(e)) for e in events])
     return int(lib.saga_decode_attn_timed(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seq_lens),

@@ -1,8 +1,7 @@
 // C ABI of libsaga: argument checks, workspace layout and the launch sequence.
 //
 // saga_decode_attn enqueues, on the caller's stream and without allocating:
-//   K-scan (logits, Eq. 2) -> top-N select (Eq. 6) -> sparse PV splits (Eq. 7)
-//   -> log-sum-exp merge.
+//   K-scan (logits, Eq. 2) -> top-N select (Eq. 6) -> sparse PV (Eq. 7).
 // saga_dense_attn enqueues K-scan -> dense PV splits -> merge (Eqs. 2-4).
 #include "saga.h"
 #include "saga_internal.h"
@@ -36,11 +35,13 @@ Workspace carve(void* base, int B, int h_q, int d, int N, int64_t S_max, bool de
         w.sel_val = reinterpret_cast<float*>(take(rows * (size_t)N * sizeof(float)));
         w.row_max = reinterpret_cast<float*>(take(rows * sizeof(float)));
         w.row_cnt = reinterpret_cast<int32_t*>(take(rows * sizeof(int32_t)));
-        nsplit = sparse_nsplit(N);
+        nsplit = 0;   // the sparse value gather writes out directly
     } else {
         nsplit = dense_nsplit(S_max);
     }
-    w.part = reinterpret_cast<float*>(take(rows * (size_t)nsplit * (size_t)(d + 2) * sizeof(float)));
+    w.part = nsplit ? reinterpret_cast<float*>(
+                          take(rows * (size_t)nsplit * (size_t)(d + 2) * sizeof(float)))
+                    : nullptr;
     w.bytes = off;
     return w;
 }
@@ -154,13 +155,9 @@ saga_status decode(const void* q, const void* k_cache, const void* v_cache,
     }
     if ((s = pm.mark(2, stream)) != SAGA_OK) return s;
     s = from_hip(saga::launch_pv_sparse(v_cache, w.sel_idx, w.sel_val, w.row_max, w.row_cnt,
-                                        w.part, B, h_q, h_v, d, N, S_max, bf16, stream), "pv_sparse");
+                                        out, B, h_q, h_v, d, N, S_max, bf16, stream), "pv_sparse");
     if (s != SAGA_OK) return s;
-    if ((s = pm.mark(3, stream)) != SAGA_OK) return s;
-    s = from_hip(saga::launch_merge(w.part, saga::sparse_nsplit(N), saga::kPvEntries,
-                                    w.row_cnt, seq_lens, S_max, out, B, h_q, d, stream), "merge");
-    if (s != SAGA_OK) return s;
-    return pm.mark(4, stream);
+    return pm.mark(3, stream);
 }
 
 }  // namespace
@@ -182,7 +179,7 @@ saga_status saga_decode_attn_timed(const void* q, const void* k_cache, const voi
                                    hipStream_t stream, int64_t S_max, saga_dtype dtype,
                                    void* workspace, size_t workspace_bytes, int32_t* idx_out,
                                    hipEvent_t* events, int n_events) {
-    if (n_events < 0 || n_events > 5 || (n_events > 0 && !events)) return SAGA_ERR_INVALID_ARG;
+    if (n_events < 0 || n_events > 4 || (n_events > 0 && !events)) return SAGA_ERR_INVALID_ARG;
     for (int i = 0; i < n_events; ++i)
         if (!events[i]) return SAGA_ERR_INVALID_ARG;
     return decode(q, k_cache, v_cache, seq_lens, out, B, h_q, h_k, h_v, d, N, stream, S_max,

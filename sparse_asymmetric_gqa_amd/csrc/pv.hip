@@ -4,13 +4,14 @@
 // value rows are read (App. C.1: gather, then a batched product), and each
 // query head uses value head i / (h_q / h_v) (§3.2, App. B Eq. 29).
 //
-// Sparse path: one workgroup per (b, i, split of kPvEntries kept entries).
-// Its 256 threads first stage positions and weights exp(s - m) in LDS (m =
-// the row's largest logit, so the partial sums of all splits share one
-// reference), then every wave streams its share of value rows with 16-byte
-// loads, LPR lanes per row, all rows of a wave in flight at once. The g_v
-// heads that share a value head are mapped to the same XCD at neighbouring
-// times so value rows they have in common are served from that XCD's L2.
+// Sparse path: one workgroup per (b, i) row, walking its kept list in blocks
+// of kPvEntries. Per block its 256 threads stage positions and weights
+// exp(s - m) in LDS (m = the row's largest kept logit), then every wave
+// streams its share of value rows with 16-byte loads, LPR lanes per row, all
+// rows of a wave in flight at once; the block sums stay in registers and the
+// row ends with out = acc / l, so no merge pass is needed. The g_v heads that
+// share a value head are mapped to the same XCD at neighbouring times so value
+// rows they have in common are served from that XCD's L2.
 //
 // Dense path (full attention over all L_b rows, §2.1 Eqs. 2-4): one
 // workgroup per (b, value head, group of <= 8 query heads, block of
@@ -60,13 +61,13 @@ template <typename T, int DH>
 __global__ __launch_bounds__(kPvThreads) void pv_sparse(
     const T* __restrict__ v, const int32_t* __restrict__ sel_idx, const float* __restrict__ sel_val,
     const float* __restrict__ row_max, const int32_t* __restrict__ row_cnt,
-    float* __restrict__ part, int h_q, int h_v, int N, int nsplit, int64_t S_max, int total) {
+    float* __restrict__ out, int h_q, int h_v, int N, int64_t S_max, int total) {
     using R = Row16<T>;
     constexpr int EPL = R::EPL;
     constexpr int LPR = DH / EPL;          // lanes per value row
     constexpr int RPI = 64 / LPR;          // rows per wave instruction
     constexpr int STEP = kPvWaves * RPI;   // rows per workgroup step
-    constexpr int PER = kPvEntries / STEP; // rows per row-group
+    constexpr int PER = kPvEntries / STEP; // rows per row-group and block
     constexpr int UNR = PER < 16 ? PER : 16;
     __shared__ int32_t s_pos[kPvEntries];
     __shared__ float s_w[kPvEntries];
@@ -75,94 +76,88 @@ __global__ __launch_bounds__(kPvThreads) void pv_sparse(
 
     const int lid = xcd_logical((int)blockIdx.x, total);
     if (lid >= total) return;
-    const int g_v = h_q / h_v;
-    // logical order: ((b*h_v + vh) * nsplit + split) * g_v + u
-    const int u = lid % g_v;
-    const int t1 = lid / g_v;
-    const int split = t1 % nsplit;
-    const int bvh = t1 / nsplit;
-    const int row = bvh * g_v + u;          // = b*h_q + i
+    const int row = lid;                     // = b*h_q + i; the g_v heads of a value head are adjacent
     const int b = row / h_q;
-    const int cnt = row_cnt[row];
-    const int e0 = split * kPvEntries;
-    if (e0 >= cnt) return;
-    const int ne = cnt - e0 < kPvEntries ? cnt - e0 : kPvEntries;
-    const float m = row_max[row];
     const int i = row - b * h_q;
+    const int g_v = h_q / h_v;
     const int vh = i / g_v;
-    const T* vb = v + (int64_t)(b * h_v + vh) * S_max * DH;
-
+    const int cnt = row_cnt[row];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
-    {
-        const int e = tid;
-        float w = 0.f;
-        int32_t pos = 0;
-        if (e < ne) {
-            pos = sel_idx[(int64_t)row * N + e0 + e];
-            // kept positions lie in [0, L_b); clamp anyway so a bad list cannot leave the cache
-            pos = pos < 0 ? 0 : (pos >= S_max ? (int32_t)(S_max - 1) : pos);
-            w = __expf(sel_val[(int64_t)row * N + e0 + e] - m);
-        }
-        s_pos[e] = pos;
-        s_w[e] = w;
-        // l = sum of weights, fixed order: lanes then waves
-        float l = w;
-#pragma unroll
-        for (int o = 32; o > 0; o >>= 1) l += __shfl_xor(l, o, 64);
-        if (lane == 0) s_l[wave] = l;
+    float* o = out + (int64_t)row * DH;
+    if (cnt <= 0) {   // no kept entry (L_b = 0): out = 0
+        for (int c = tid; c < DH; c += kPvThreads) o[c] = 0.f;
+        return;
     }
-    __syncthreads();
-
+    const float m = row_max[row];
+    const T* vb = v + (int64_t)(b * h_v + vh) * S_max * DH;
     const int rg = lane / LPR;
     const int sub = lane - rg * LPR;
+    const int first = wave * RPI + rg;
     float acc[EPL];
 #pragma unroll
     for (int c = 0; c < EPL; ++c) acc[c] = 0.f;
-    const int first = wave * RPI + rg;
+    float lsum = 0.f;   // thread tid's share of l, blocks in order
 #pragma unroll 1
-    for (int k0 = 0; k0 < PER; k0 += UNR) {
-        u32x4 raw[UNR];
-        float wt[UNR];
-#pragma unroll
-        for (int k = 0; k < UNR; ++k) {
-            const int e = first + (k0 + k) * STEP;
-            wt[k] = s_w[e];
-            const int32_t pos = s_pos[e];
-            raw[k] = u32x4{0u, 0u, 0u, 0u};
-            if (e < ne) raw[k] = *reinterpret_cast<const u32x4*>(vb + (int64_t)pos * DH + sub * EPL);
+    for (int e0 = 0; e0 < cnt; e0 += kPvEntries) {
+        const int ne = cnt - e0 < kPvEntries ? cnt - e0 : kPvEntries;
+        {
+            const int e = tid;
+            float w = 0.f;
+            int32_t pos = 0;
+            if (e < ne) {
+                pos = sel_idx[(int64_t)row * N + e0 + e];
+                // kept positions lie in [0, L_b); clamp anyway so a bad list cannot leave the cache
+                pos = pos < 0 ? 0 : (pos >= S_max ? (int32_t)(S_max - 1) : pos);
+                w = __expf(sel_val[(int64_t)row * N + e0 + e] - m);
+            }
+            s_pos[e] = pos;
+            s_w[e] = w;
+            lsum += w;
         }
+        __syncthreads();
+#pragma unroll 1
+        for (int k0 = 0; k0 < PER; k0 += UNR) {
+            u32x4 raw[UNR];
+            float wt[UNR];
 #pragma unroll
-        for (int k = 0; k < UNR; ++k) {
-            float f[EPL];
-            R::cvt(raw[k], f);
+            for (int k = 0; k < UNR; ++k) {
+                const int e = first + (k0 + k) * STEP;
+                wt[k] = s_w[e];   // 0 past ne
+                raw[k] = *reinterpret_cast<const u32x4*>(vb + (int64_t)s_pos[e] * DH + sub * EPL);
+            }
 #pragma unroll
-            for (int c = 0; c < EPL; ++c) acc[c] += wt[k] * f[c];
+            for (int k = 0; k < UNR; ++k) {
+                float f[EPL];
+                R::cvt(raw[k], f);
+#pragma unroll
+                for (int c = 0; c < EPL; ++c) acc[c] += wt[k] * f[c];
+            }
         }
+        __syncthreads();   // the block's LDS lists are reused by the next block
     }
-    // reduce over the row-groups of the wave, then over waves
+    // l: thread shares summed over lanes, then waves (fixed order)
 #pragma unroll
-    for (int o = LPR; o < 64; o <<= 1)
+    for (int off = 32; off > 0; off >>= 1) lsum += __shfl_xor(lsum, off, 64);
+    if (lane == 0) s_l[wave] = lsum;
+    // acc: reduce over the row-groups of the wave, then over waves
 #pragma unroll
-        for (int c = 0; c < EPL; ++c) acc[c] += __shfl_xor(acc[c], o, 64);
+    for (int off = LPR; off < 64; off <<= 1)
+#pragma unroll
+        for (int c = 0; c < EPL; ++c) acc[c] += __shfl_xor(acc[c], off, 64);
     if (rg == 0)
 #pragma unroll
         for (int c = 0; c < EPL; ++c) s_red[wave][sub * EPL + c] = acc[c];
     __syncthreads();
-    float* dst = part + ((int64_t)row * nsplit + split) * (DH + 2);
+    float l = 0.f;
+#pragma unroll
+    for (int w = 0; w < kPvWaves; ++w) l += s_l[w];
     for (int c = tid; c < DH; c += kPvThreads) {
-        float s = 0.f;
+        float sacc = 0.f;
 #pragma unroll
-        for (int w = 0; w < kPvWaves; ++w) s += s_red[w][c];
-        dst[2 + c] = s;
-    }
-    if (tid == 0) {
-        float l = 0.f;
-#pragma unroll
-        for (int w = 0; w < kPvWaves; ++w) l += s_l[w];
-        dst[0] = m;
-        dst[1] = l;
+        for (int w = 0; w < kPvWaves; ++w) sacc += s_red[w][c];
+        o[c] = sacc / l;   // l >= 1: the largest kept logit has weight 1
     }
 }
 
@@ -321,16 +316,14 @@ int sparse_nsplit(int N) { return (N + kPvEntries - 1) / kPvEntries; }
 int dense_nsplit(int64_t S_max) { return (int)((S_max + kDenseRows - 1) / kDenseRows); }
 
 hipError_t launch_pv_sparse(const void* v, const int32_t* sel_idx, const float* sel_val,
-                            const float* row_max, const int32_t* row_cnt, float* part, int B,
+                            const float* row_max, const int32_t* row_cnt, float* out, int B,
                             int h_q, int h_v, int d, int N, int64_t S_max, bool bf16,
                             hipStream_t st) {
-    const int nsplit = sparse_nsplit(N);
-    const int total = B * h_q * nsplit;
+    const int total = B * h_q;
     const unsigned grid = (unsigned)(((total + 7) / 8) * 8);
 #define SAGA_PV(T, D)                                                                        \
     hipLaunchKernelGGL((pv_sparse<T, D>), dim3(grid), dim3(kPvThreads), 0, st, (const T*)v,   \
-                       sel_idx, sel_val, row_max, row_cnt, part, h_q, h_v, N, nsplit, S_max, \
-                       total)
+                       sel_idx, sel_val, row_max, row_cnt, out, h_q, h_v, N, S_max, total)
     if (bf16) {
         if (d == 64) SAGA_PV(uint16_t, 64); else SAGA_PV(uint16_t, 128);
     } else {

@@ -82,7 +82,7 @@ hipError_t launch_select_union(const TopmOut& tm, const int32_t* lens, int B, in
                                int64_t s_stride, bool bf16, hipStream_t st);
 
 hipError_t launch_pv_sparse(const void* v, const int32_t* sel_idx, const float* sel_val,
-                            const float* row_max, const int32_t* row_cnt, float* part, int B,
+                            const float* row_max, const int32_t* row_cnt, float* out, int B,
                             int h_q, int h_v, int d, int N, int64_t S_max, bool bf16,
                             hipStream_t st);
 

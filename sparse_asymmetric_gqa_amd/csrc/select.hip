@@ -38,7 +38,7 @@ namespace {
 
 constexpr int kUnionThreads = 256;
 constexpr int kUnionKPT = 16;
-constexpr int kMaxChunks = 4096;
+constexpr int kMaxChunks = 512;   // chunks per row on the union path (S_max <= 512 Ki)
 
 __device__ inline uint32_t wave_sum(uint32_t x) {
 #pragma unroll
@@ -413,320 +413,11 @@ __device__ void head_logits(const T* __restrict__ q, const T* __restrict__ k, in
     __syncthreads();
 }
 
-// ---- union select, one wave per row (the common case) -------------------------------
-// Each wave takes one (b, i) row and holds the union of its chunks' candidate
-// lists in registers, lane-major: with P = ceil(total / 64), lane l holds
-// union elements [l P, l P + P) in slots 0..P-1 (the union is chunk-major,
-// so this is ascending position, lane by lane). The union's key of rank
-// N_eff, T, is found by bisection of the key range [max cutoff, max key]:
-// the count at the lower end being >= N_eff is exactly the proof that every
-// chunk cutoff is <= T, so the result is exact. Compaction needs only two
-// wave prefix scans (ties kept in position order, then output slots). Rows
-// that cannot be settled here -- count(key >= max cutoff) < N_eff, more
-// candidates than 64 KPT, or more than kFastChunks chunks -- are flagged
-// (row_flag = 2) for the workgroup kernel below.
-constexpr int kFastChunks = 128;       // chunk lists per row described in LDS
-constexpr int kFastBracket = 512;      // keys left in the bracket before packing
-
-// LDS of one wave: the union (element-major, 64 KPT entries), reused for the
-// bracket keys and then for the staged output (n_eff <= 32 KPT pairs).
-template <int KPT>
-struct FastWaveLds {
-    uint2 uni[64 * KPT];
-    uint32_t pref[kFastChunks + 1];
-    uint32_t coff[kFastChunks];
-};
-
-template <int KPT, int NWV>
-__global__ __launch_bounds__(64 * NWV) void select_union_fast(
-    const uint2* __restrict__ cand, const uint4* __restrict__ cand_meta,
-    const int32_t* __restrict__ lens, int rows, int h_q, int h_k, int N, int64_t S_max,
-    int nchunk, int32_t* __restrict__ sel_idx, float* __restrict__ sel_val,
-    float* __restrict__ row_max, int32_t* __restrict__ row_cnt, int32_t* __restrict__ idx_out,
-    int32_t* __restrict__ row_flag) {
-    __shared__ FastWaveLds<KPT> lds_all[NWV];
-    const int lane = threadIdx.x & 63;
-    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));   // wave-uniform
-    FastWaveLds<KPT>& W = lds_all[wave];
-    const int row = blockIdx.x * NWV + wave;
-    if (row >= rows) return;   // no workgroup barriers below
-    const int b = row / h_q;
-    const int i = row - b * h_q;
-    const int64_t L = clamp_len(lens[b], S_max);
-    const int n_eff = (int)((int64_t)N < L ? (int64_t)N : L);
-    int32_t* oi = sel_idx + (int64_t)row * N;
-    float* ov = sel_val + (int64_t)row * N;
-    int32_t* ou = idx_out ? idx_out + (int64_t)row * N : nullptr;
-    for (int s = n_eff + lane; s < N; s += 64) {
-        oi[s] = -1;
-        ov[s] = -__builtin_inff();
-        if (ou) ou[s] = -1;
-    }
-    if (n_eff == 0) {
-        if (lane == 0) {
-            row_max[row] = -__builtin_inff();
-            row_cnt[row] = 0;
-            row_flag[row] = 0;
-        }
-        return;
-    }
-    const int nch = (int)((L + kScanChunk - 1) / kScanChunk);
-    if (nch > kFastChunks) {
-        if (lane == 0) row_flag[row] = 2;
-        return;
-    }
-    // chunk lists: prefix of the counts and pool offsets (relative to the
-    // row's first item region) in this wave's LDS, largest cutoff
-    uint32_t* pref = W.pref;
-    uint32_t* coff = W.coff;
-    const uint4* meta = cand_meta + (int64_t)row * nchunk;
-    const int g = h_q / h_k;
-    const uint2* pool = cand + (int64_t)(b * h_k + i / g) * nchunk * g * kScanChunk;
-    uint32_t carry = 0, maxcut = 0;
-    for (int c0 = 0; c0 < nch; c0 += 64) {
-        const int c = c0 + lane;
-        uint4 m = make_uint4(0u, 0u, 0u, 0u);
-        if (c < nch) m = meta[c];
-        uint32_t tot;
-        const uint32_t incl = wave_incl_scan(m.y, tot);
-        if (c < nch) {
-            pref[c] = carry + incl - m.y;
-            coff[c] = (uint32_t)c * g * kScanChunk + m.x;
-        }
-        carry += tot;
-        maxcut = m.z > maxcut ? m.z : maxcut;
-    }
-    if (lane == 0) pref[nch] = carry;
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-        const uint32_t y = (uint32_t)__shfl_xor((int)maxcut, o, 64);
-        maxcut = y > maxcut ? y : maxcut;
-    }
-    maxcut = (uint32_t)__builtin_amdgcn_readfirstlane((int)maxcut);   // equal in every lane
-    const uint32_t total = carry;
-    if (total < (uint32_t)n_eff || total > 64u * KPT) {
-        if (lane == 0) row_flag[row] = 2;
-        return;
-    }
-    __builtin_amdgcn_s_waitcnt(0xc07f);   // this wave's LDS writes are visible to it
-
-    // The union, element-major (element j = lane + 64 t): coalesced loads,
-    // all issued before any is waited for (unconditional; slots past the
-    // union read entry 0 of the row's pool and are discarded), then written to
-    // LDS in union order.
-    const uint32_t P = (total + 63) / 64;
-    {
-        uint2 ev[KPT];
-        uint32_t kc = 0, cur = pref[0], nxt = pref[1], base = coff[0];
-#pragma unroll
-        for (int t = 0; t < KPT; ++t) {
-            const uint32_t j = (uint32_t)(lane + 64 * t);
-            const bool valid = j < total;
-            if (valid && j >= nxt) {   // chunk of element j (LDS only)
-                do {
-                    ++kc;
-                } while (pref[kc + 1] <= j);
-                cur = pref[kc];
-                nxt = pref[kc + 1];
-                base = coff[kc];
-            }
-            ev[t] = pool[valid ? base + (j - cur) : 0u];
-        }
-#pragma unroll
-        for (int t = 0; t < KPT; ++t)
-            if ((uint32_t)t < P) W.uni[lane + 64 * t] = ev[t];
-    }
-    __builtin_amdgcn_s_waitcnt(0xc07f);   // this wave's LDS writes are visible to it
-    // (position, key) lane-major: lane l holds elements [l P, l P + P) in
-    // slots 0..P-1 (ascending position); empty slots hold key 0, below every
-    // real key
-    const uint32_t j0 = (uint32_t)lane * P;
-    const uint32_t jend = j0 + P < total ? j0 + P : total;
-    uint32_t key[KPT];
-    int32_t pos[KPT];
-#pragma unroll
-    for (int s = 0; s < KPT; ++s) {
-        const uint32_t j = j0 + (uint32_t)s;
-        const bool valid = j < jend;
-        const uint2 v = W.uni[valid ? j : 0u];
-        pos[s] = valid ? (int32_t)v.x : -1;
-        key[s] = valid ? v.y : 0u;
-    }
-    uint32_t kmax = 0;
-#pragma unroll
-    for (int s = 0; s < KPT; ++s) kmax = key[s] > kmax ? key[s] : kmax;
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-        const uint32_t y = (uint32_t)__shfl_xor((int)kmax, o, 64);
-        kmax = y > kmax ? y : kmax;
-    }
-    kmax = (uint32_t)__builtin_amdgcn_readfirstlane((int)kmax);   // equal in every lane
-    // per-lane count of keys >= x (independent partial sums for latency)
-    auto lane_ge = [&](uint32_t x) -> uint32_t {
-        uint32_t c[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
-#pragma unroll
-        for (int s = 0; s < KPT; ++s) c[s & 7] += key[s] >= x ? 1u : 0u;
-        return ((c[0] + c[1]) + (c[2] + c[3])) + ((c[4] + c[5]) + (c[6] + c[7]));
-    };
-    auto wave_min = [&](uint32_t m) {
-#pragma unroll
-        for (int o = 32; o > 0; o >>= 1) {
-            const uint32_t y = (uint32_t)__shfl_xor((int)m, o, 64);
-            m = y < m ? y : m;
-        }
-        return (uint32_t)__builtin_amdgcn_readfirstlane((int)m);   // equal in every lane
-    };
-    // T: the largest x with count(key >= x) >= n_eff, searched in [a, z) with
-    // count(>= a) >= n_eff > count(>= z). Phase 1 bisects over every register
-    // slot until at most kFastBracket keys lie in the bracket; those are then
-    // packed through LDS into 8 registers per lane, and phase 2 bisects there.
-    uint32_t a = maxcut > 1u ? maxcut : 1u;
-    uint32_t la = lane_ge(a);
-    uint32_t ca = wave_sum(la);
-    if (ca < (uint32_t)n_eff) {
-        // some chunk's cutoff is above the union's N_eff-th key: not provable here
-        if (lane == 0) row_flag[row] = 2;
-        return;
-    }
-    uint64_t z = (uint64_t)kmax + 1;
-    uint32_t lz = 0, cz = 0;   // lane / wave counts of keys >= z
-    bool found = false;
-#pragma unroll 1
-    while (z - a > 1 && ca - cz > (uint32_t)kFastBracket) {
-        const uint32_t mid = (uint32_t)(a + ((z - a) >> 1));
-        const uint32_t lc = lane_ge(mid);
-        const uint32_t c = wave_sum(lc);
-        if (c == (uint32_t)n_eff) {
-            // exactly n_eff keys are >= mid: T is the smallest of them
-            uint32_t mn = 0xFFFFFFFFu;
-#pragma unroll
-            for (int s = 0; s < KPT; ++s)
-                if (key[s] >= mid && key[s] < mn) mn = key[s];
-            a = wave_min(mn);
-            found = true;
-            break;
-        }
-        if (c > (uint32_t)n_eff) {
-            a = mid;
-            la = lc;
-            ca = c;
-        } else {
-            z = mid;
-            lz = lc;
-            cz = c;
-        }
-    }
-    if (!found && z - a > 1) {
-        // pack the keys in [a, z) (lane by lane) into this wave's LDS area
-        uint32_t* bkt = reinterpret_cast<uint32_t*>(W.uni);   // the union is in registers now
-        const uint32_t nin = la - lz;
-        uint32_t ntot;
-        uint32_t at = wave_incl_scan(nin, ntot) - nin;
-#pragma unroll
-        for (int s = 0; s < KPT; ++s) {
-            const bool in = key[s] >= a && (uint64_t)key[s] < z;
-            if (in) bkt[at] = key[s];
-            at += in ? 1u : 0u;
-        }
-        __builtin_amdgcn_s_waitcnt(0xc07f);   // this wave's LDS writes are visible to it
-        uint32_t kb[kFastBracket / 64];
-#pragma unroll
-        for (int j = 0; j < kFastBracket / 64; ++j) {
-            const uint32_t e = (uint32_t)(lane + 64 * j);
-            kb[j] = e < ntot ? bkt[e] : 0u;   // 0 < a: never counted
-        }
-        // cz stays the count above the bracket at the time of the packing:
-        // kb keeps the keys that a lower z leaves above it
-#pragma unroll 1
-        while (z - a > 1) {
-            const uint32_t mid = (uint32_t)(a + ((z - a) >> 1));
-            uint32_t lc = 0;
-#pragma unroll
-            for (int j = 0; j < kFastBracket / 64; ++j) lc += kb[j] >= mid ? 1u : 0u;
-            const uint32_t c = cz + wave_sum(lc);
-            if (c == (uint32_t)n_eff) {
-                uint32_t mn = 0xFFFFFFFFu;
-#pragma unroll
-                for (int j = 0; j < kFastBracket / 64; ++j)
-                    if (kb[j] >= mid && kb[j] < mn) mn = kb[j];
-                a = wave_min(mn);
-                break;
-            }
-            if (c > (uint32_t)n_eff) a = mid; else z = mid;
-        }
-    }
-    const uint32_t T = a;
-
-    // Compaction. Keys > T are kept; of the keys == T, the first krem in
-    // position order, krem = n_eff - count(> T). Lane-major order is
-    // position order, so a scan of the per-lane tie counts ranks the ties and
-    // a scan of the per-lane kept counts gives each lane its first output
-    // slot. The kept (index, logit) pairs are staged in LDS when they fit and
-    // written out with 16-byte stores; otherwise they are stored directly.
-    uint32_t ngt = 0, neq = 0;
-#pragma unroll
-    for (int s = 0; s < KPT; ++s) {
-        ngt += key[s] > T ? 1u : 0u;
-        neq += key[s] == T ? 1u : 0u;
-    }
-    uint32_t tot_gt, tot_eq;
-    (void)wave_incl_scan(ngt, tot_gt);
-    const uint32_t eq_base = wave_incl_scan(neq, tot_eq) - neq;
-    const uint32_t krem = (uint32_t)n_eff - tot_gt;
-    const uint32_t eq_keep = krem > eq_base ? (krem - eq_base < neq ? krem - eq_base : neq) : 0u;
-    const uint32_t nkeep = ngt + eq_keep;
-    uint32_t tot_keep;
-    uint32_t slot = wave_incl_scan(nkeep, tot_keep) - nkeep;
-    const bool staged = n_eff <= 32 * KPT;   // two words per kept entry fit the union area
-    int32_t* st_idx = reinterpret_cast<int32_t*>(W.uni);
-    float* st_val = reinterpret_cast<float*>(W.uni) + 32 * KPT;
-    uint32_t eq_seen = 0;
-#pragma unroll
-    for (int s = 0; s < KPT; ++s) {
-        const bool eq = key[s] == T;
-        const bool keep = key[s] > T || (eq && eq_seen < eq_keep);
-        eq_seen += eq ? 1u : 0u;
-        if (keep && slot < (uint32_t)n_eff) {   // holds by construction; keeps stores in bounds
-            if (staged) {
-                st_idx[slot] = pos[s];
-                st_val[slot] = key_float(key[s]);
-            } else {
-                oi[slot] = pos[s];
-                ov[slot] = key_float(key[s]);
-                if (ou) ou[slot] = pos[s];
-            }
-        }
-        slot += keep ? 1u : 0u;
-    }
-    if (staged) {
-        __builtin_amdgcn_s_waitcnt(0xc07f);   // this wave's LDS writes are visible to it
-        // 16-byte stores where the rows start 16-byte aligned, else 4-byte ones
-        const bool v4 = (((uintptr_t)oi | (uintptr_t)ov | (uintptr_t)ou) & 15u) == 0;
-        const int n4 = v4 ? n_eff / 4 : 0;
-        for (int j = lane; j < n4; j += 64) {
-            const int4 vi = reinterpret_cast<const int4*>(st_idx)[j];
-            reinterpret_cast<int4*>(oi)[j] = vi;
-            reinterpret_cast<float4*>(ov)[j] = reinterpret_cast<const float4*>(st_val)[j];
-            if (ou) reinterpret_cast<int4*>(ou)[j] = vi;
-        }
-        for (int j = 4 * n4 + lane; j < n_eff; j += 64) {
-            oi[j] = st_idx[j];
-            ov[j] = st_val[j];
-            if (ou) ou[j] = st_idx[j];
-        }
-    }
-    if (lane == 0) {
-        row_max[row] = key_float(kmax);
-        row_cnt[row] = n_eff;
-        row_flag[row] = 0;
-    }
-}
-
-// ---- union select, one workgroup per row (deferred rows) ---------------------------
-// Rows the wave kernel flagged: the union select over any number of
-// candidates (register tiles), the cutoff check, and the dense fallback that
-// recomputes the head's logits when the check fails. row_flag becomes 0
-// (settled from the candidates) or 1 (dense fallback).
+// ---- union select, general code (one workgroup per row) ----------------------------
+// The union select over any number of candidates (register tiles), the
+// cutoff check, and the dense fallback that recomputes the head's logits when
+// the check fails. row_flag becomes 0 (settled from the candidates) or 1
+// (dense fallback).
 struct UnionShared {
     SelShared sh;
     int32_t pref[kMaxChunks + 1];
@@ -848,36 +539,265 @@ __device__ void union_row(
     }
 }
 
-template <typename T, int DH>
-__global__ __launch_bounds__(kUnionThreads) void select_union(
+// ---- union select, one workgroup per row -------------------------------------------
+// Fast path: the row's candidate union in registers across the workgroup,
+// thread-major: with P = ceil(total / 256), thread t holds union elements
+// [t P, t P + P) (ascending position, thread by thread). The union's key of
+// rank N_eff, T, is found by bisection of [max chunk cutoff, max key]; the
+// count at the lower end being >= N_eff is exactly the proof that every chunk
+// cutoff is <= T, so the result is exact. A probe is a per-thread count, a DPP
+// wave sum and one exchange of the four wave sums through LDS. Compaction is
+// two workgroup prefix scans (ties in position order, then output slots) and
+// LDS-staged 16-byte stores. Rows the fast path cannot take (more than 256 KPT
+// candidates, or count(key >= max cutoff) < N_eff) go through union_row in
+// the same workgroup: the multi-tile union select, or the dense recompute.
+template <int KPT>
+struct FastShared {
+    uint2 uni[kUnionThreads * KPT];       // union, then the staged output
+    uint32_t pref[kMaxChunks + 1];
+    uint32_t coff[kMaxChunks];
+    uint32_t red[2][kUnionThreads / 64];  // wave partials, double-buffered
+};
+template <int KPT>
+union SelectShared {
+    FastShared<KPT> f;
+    UnionShared u;
+};
+
+// Sum / max over the workgroup of one value per thread (uniform result); the
+// partials go to red[buf], so consecutive calls must alternate buf.
+__device__ inline uint32_t block_sum(uint32_t v, uint32_t* red) {
+    const uint32_t w = wave_sum(v);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = w;
+    __syncthreads();
+    uint32_t t = 0;
+#pragma unroll
+    for (int k = 0; k < kUnionThreads / 64; ++k) t += red[k];
+    return t;
+}
+__device__ inline uint32_t block_max(uint32_t v, uint32_t* red) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        const uint32_t y = (uint32_t)__shfl_xor((int)v, o, 64);
+        v = y > v ? y : v;
+    }
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+    __syncthreads();
+    uint32_t t = 0;
+#pragma unroll
+    for (int k = 0; k < kUnionThreads / 64; ++k) t = red[k] > t ? red[k] : t;
+    return t;
+}
+// Exclusive prefix over the workgroup (thread order) and the total.
+__device__ inline uint32_t block_excl_scan(uint32_t v, uint32_t* red, uint32_t& total) {
+    uint32_t wt;
+    const uint32_t incl = wave_incl_scan(v, wt);
+    const int wave = threadIdx.x >> 6;
+    if ((threadIdx.x & 63) == 0) red[wave] = wt;
+    __syncthreads();
+    uint32_t before = 0;
+    total = 0;
+#pragma unroll
+    for (int k = 0; k < kUnionThreads / 64; ++k) {
+        if (k < wave) before += red[k];
+        total += red[k];
+    }
+    return before + incl - v;
+}
+
+// Four workgroups per CU (<= 128 VGPRs): the general code spills at this
+// bound, which only costs the rare rows that need it.
+template <typename T, int DH, int KPT>
+__global__ __launch_bounds__(kUnionThreads, 4) void select_union(
     const uint2* __restrict__ cand, const uint4* __restrict__ cand_meta,
-    const int32_t* __restrict__ lens, int rows, int h_q, int h_k, int N, int64_t S_max,
-    int nchunk, int32_t* __restrict__ sel_idx, float* __restrict__ sel_val,
-    float* __restrict__ row_max, int32_t* __restrict__ row_cnt, int32_t* __restrict__ idx_out,
-    int32_t* __restrict__ row_flag, const T* __restrict__ q, const T* __restrict__ k,
-    float* __restrict__ scores, int64_t s_stride, float scale) {
-    __shared__ UnionShared us;
-    __shared__ uint32_t nflag;
-    __shared__ int32_t flagged[kUnionThreads];
-    // The rows of this workgroup are blockIdx.x + r * gridDim.x; their flags
-    // are read in parallel, kUnionThreads rows per round, and only the flagged
-    // ones are processed.
-#pragma unroll 1
-    for (int r0 = blockIdx.x; r0 < rows; r0 += gridDim.x * kUnionThreads) {
-        if (threadIdx.x == 0) nflag = 0u;
+    const int32_t* __restrict__ lens, int h_q, int h_k, int N, int64_t S_max, int nchunk,
+    int32_t* __restrict__ sel_idx, float* __restrict__ sel_val, float* __restrict__ row_max,
+    int32_t* __restrict__ row_cnt, int32_t* __restrict__ idx_out, int32_t* __restrict__ row_flag,
+    const T* __restrict__ q, const T* __restrict__ k, float* __restrict__ scores,
+    int64_t s_stride, float scale) {
+    constexpr int NT = kUnionThreads;
+    __shared__ SelectShared<KPT> sm;
+    FastShared<KPT>& F = sm.f;
+    const int row = blockIdx.x;
+    const int tid = threadIdx.x;
+    const int b = row / h_q;
+    const int i = row - b * h_q;
+    const int64_t L = clamp_len(lens[b], S_max);
+    const int n_eff = (int)((int64_t)N < L ? (int64_t)N : L);
+    const int nch = (int)((L + kScanChunk - 1) / kScanChunk);
+    if (n_eff == 0 || nch > kMaxChunks) {
+        // no kept entry, or too many chunks for the fast path: the general code
+        union_row<T, DH>(row, sm.u, cand, cand_meta, lens, h_q, h_k, N, S_max, nchunk, sel_idx,
+                         sel_val, row_max, row_cnt, idx_out, row_flag, q, k, scores, s_stride,
+                         scale);
+        return;
+    }
+    int32_t* oi = sel_idx + (int64_t)row * N;
+    float* ov = sel_val + (int64_t)row * N;
+    int32_t* ou = idx_out ? idx_out + (int64_t)row * N : nullptr;
+
+    // chunk lists: prefix of the counts and pool offsets (relative to the
+    // row's first item region) in LDS, largest cutoff
+    const uint4* meta = cand_meta + (int64_t)row * nchunk;
+    const int g = h_q / h_k;
+    const uint2* pool = cand + (int64_t)(b * h_k + i / g) * nchunk * g * kScanChunk;
+    uint32_t carry = 0, mcut = 0;
+    for (int c0 = 0; c0 < nch; c0 += NT) {   // uniform trip count
+        const int c = c0 + tid;
+        uint4 m = make_uint4(0u, 0u, 0u, 0u);
+        if (c < nch) m = meta[c];
+        uint32_t tot;
+        const uint32_t ex = block_excl_scan(m.y, F.red[(c0 / NT) & 1], tot);
+        if (c < nch) {
+            F.pref[c] = carry + ex;
+            F.coff[c] = (uint32_t)c * g * kScanChunk + m.x;
+        }
+        carry += tot;
+        mcut = m.z > mcut ? m.z : mcut;
+    }
+    if (tid == 0) F.pref[nch] = carry;
+    const uint32_t total = carry;
+    __syncthreads();   // pref / coff complete; red[0] is free again
+    const uint32_t maxcut = block_max(mcut, F.red[1]);
+    bool fast = total >= (uint32_t)n_eff && total <= (uint32_t)(NT * KPT);
+    uint32_t key[KPT];
+    int32_t pos[KPT];
+    uint32_t kmax = 0;
+    if (fast) {   // uniform
+        // The union, element-major (element j = tid + 256 u): coalesced loads,
+        // all issued before any is waited for, then written to LDS.
+        const uint32_t nu = (total + NT - 1) / NT;
+        {
+            uint2 ev[KPT];
+#pragma unroll
+            for (int u = 0; u < KPT; ++u) {
+                const uint32_t j = (uint32_t)(tid + NT * u);
+                const bool valid = j < total;
+                // chunk of element j: largest c with pref[c] <= j (binary search)
+                uint32_t lo = 0, hi = (uint32_t)nch;
+                if (valid)
+                    while (hi - lo > 1) {
+                        const uint32_t mid = (lo + hi) >> 1;
+                        if (F.pref[mid] <= j) lo = mid; else hi = mid;
+                    }
+                ev[u] = pool[valid ? F.coff[lo] + (j - F.pref[lo]) : 0u];
+            }
+#pragma unroll
+            for (int u = 0; u < KPT; ++u)
+                if ((uint32_t)u < nu) F.uni[tid + NT * u] = ev[u];
+        }
         __syncthreads();
-        const int rr = r0 + (int)threadIdx.x * gridDim.x;
-        if (rr < rows && row_flag[rr] != 0) flagged[atomicAdd(&nflag, 1u)] = rr;
-        __syncthreads();
-        const uint32_t nf = nflag;
+        // thread-major registers: thread t holds [t P, t P + P); empty slots
+        // hold key 0, below every real key
+        const uint32_t P = nu;
+        const uint32_t j0 = (uint32_t)tid * P;
+        const uint32_t jend = j0 + P < total ? j0 + P : total;
+#pragma unroll
+        for (int s = 0; s < KPT; ++s) {
+            const uint32_t j = j0 + (uint32_t)s;
+            const bool valid = (uint32_t)s < P && j < jend;
+            const uint2 v = F.uni[valid ? j : 0u];
+            pos[s] = valid ? (int32_t)v.x : -1;
+            key[s] = valid ? v.y : 0u;
+        }
+#pragma unroll
+        for (int s = 0; s < KPT; ++s) kmax = key[s] > kmax ? key[s] : kmax;
+        kmax = block_max(kmax, F.red[0]);
+        // the proof: count(key >= max cutoff) >= N_eff
+        auto lane_ge = [&](uint32_t x) -> uint32_t {
+            uint32_t c[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+            for (int s = 0; s < KPT; ++s) c[s & 3] += key[s] >= x ? 1u : 0u;
+            return (c[0] + c[1]) + (c[2] + c[3]);
+        };
+        const uint32_t a0 = maxcut > 1u ? maxcut : 1u;
+        int buf = 1;
+        fast = block_sum(lane_ge(a0), F.red[buf]) >= (uint32_t)n_eff;
+        buf ^= 1;
+        if (fast) {
+            // T: the largest x with count(key >= x) >= n_eff, in [a, z)
+            uint32_t a = a0;
+            uint64_t z = (uint64_t)kmax + 1;
 #pragma unroll 1
-        for (uint32_t f = 0; f < nf; ++f) {
-            union_row<T, DH>(flagged[f], us, cand, cand_meta, lens, h_q, h_k, N, S_max, nchunk,
-                             sel_idx, sel_val, row_max, row_cnt, idx_out, row_flag, q, k, scores,
-                             s_stride, scale);
-            __syncthreads();   // shared state is reused by the next row
+            while (z - a > 1) {
+                const uint32_t mid = (uint32_t)(a + ((z - a) >> 1));
+                const uint32_t c = block_sum(lane_ge(mid), F.red[buf]);
+                buf ^= 1;
+                if (c == (uint32_t)n_eff) {
+                    // exactly n_eff keys are >= mid: T is the smallest of them
+                    uint32_t mn = 0xFFFFFFFFu;
+#pragma unroll
+                    for (int s = 0; s < KPT; ++s)
+                        if (key[s] >= mid && key[s] < mn) mn = key[s];
+                    a = ~block_max(~mn, F.red[buf]);
+                    buf ^= 1;
+                    break;
+                }
+                if (c > (uint32_t)n_eff) a = mid; else z = mid;
+            }
+            const uint32_t Tk = a;
+            // Compaction: keys > T are kept; of the keys == T, the first krem in
+            // position order, krem = n_eff - count(> T).
+            uint32_t ngt = 0, neq = 0;
+#pragma unroll
+            for (int s = 0; s < KPT; ++s) {
+                ngt += key[s] > Tk ? 1u : 0u;
+                neq += key[s] == Tk ? 1u : 0u;
+            }
+            const uint32_t tot_gt = block_sum(ngt, F.red[buf]);
+            buf ^= 1;
+            uint32_t tot_eq;
+            const uint32_t eq_base = block_excl_scan(neq, F.red[buf], tot_eq);
+            buf ^= 1;
+            const uint32_t krem = (uint32_t)n_eff - tot_gt;
+            const uint32_t eq_keep =
+                krem > eq_base ? (krem - eq_base < neq ? krem - eq_base : neq) : 0u;
+            const uint32_t nkeep = ngt + eq_keep;
+            uint32_t tot_keep;
+            uint32_t slot = block_excl_scan(nkeep, F.red[buf], tot_keep);
+            buf ^= 1;
+            // staged output: indices in uni[0 .. ), logits after them (the
+            // union is in registers now; n_eff <= total <= 256 KPT <= 8192)
+            int32_t* st_idx = reinterpret_cast<int32_t*>(F.uni);
+            float* st_val = reinterpret_cast<float*>(F.uni) + NT * KPT;
+            uint32_t eq_seen = 0;
+#pragma unroll
+            for (int s = 0; s < KPT; ++s) {
+                const bool eq = key[s] == Tk;
+                const bool keep = key[s] > Tk || (eq && eq_seen < eq_keep);
+                eq_seen += eq ? 1u : 0u;
+                if (keep && slot < (uint32_t)n_eff) {   // holds by construction
+                    st_idx[slot] = pos[s];
+                    st_val[slot] = key_float(key[s]);
+                }
+                slot += keep ? 1u : 0u;
+            }
+            __syncthreads();
+            const bool v4 = (((uintptr_t)oi | (uintptr_t)ov | (uintptr_t)ou) & 15u) == 0;
+            const int n4 = v4 ? n_eff / 4 : 0;
+            for (int j = tid; j < n4; j += NT) {
+                const int4 vi = reinterpret_cast<const int4*>(st_idx)[j];
+                reinterpret_cast<int4*>(oi)[j] = vi;
+                reinterpret_cast<float4*>(ov)[j] = reinterpret_cast<const float4*>(st_val)[j];
+                if (ou) reinterpret_cast<int4*>(ou)[j] = vi;
+            }
+            for (int j = 4 * n4 + tid; j < N; j += NT) {
+                const bool kept = j < n_eff;
+                oi[j] = kept ? st_idx[j] : -1;
+                ov[j] = kept ? st_val[j] : -__builtin_inff();
+                if (ou) ou[j] = kept ? st_idx[j] : -1;
+            }
+            if (tid == 0) {
+                row_max[row] = key_float(kmax);
+                row_cnt[row] = n_eff;
+                row_flag[row] = 0;
+            }
+            return;
         }
     }
+    __syncthreads();   // the fast path's LDS is reused by the general code
+    union_row<T, DH>(row, sm.u, cand, cand_meta, lens, h_q, h_k, N, S_max, nchunk, sel_idx,
+                     sel_val, row_max, row_cnt, idx_out, row_flag, q, k, scores, s_stride, scale);
 }
 
 template <int KPT>
@@ -915,39 +835,28 @@ hipError_t launch_select_union(const TopmOut& tm, const int32_t* lens, int B, in
     const int nchunk = (int)((S_max + kScanChunk - 1) / kScanChunk);
     const int rows = B * h_q;
     const float scale = (float)(1.0 / __builtin_sqrt((double)d));
-    // Register slots per lane for the wave kernel: ceil(union size / 64), the
+    // Register slots per thread for the fast path: ceil(union size / 256), the
     // union holding up to 1.25 M = 1.25 (1.5 share + 16) keys per full chunk
-    // (share = N * 1024 / L); rows with a larger union are deferred.
+    // (share = N * 1024 / L); larger unions take the general code.
     const double share = (double)N * kScanChunk / (double)S_max;
     int64_t per_chunk = (int64_t)(1.25 * (1.5 * share + 16.0)) + 1;
     per_chunk = per_chunk < kScanChunk ? per_chunk : kScanChunk;
-    const int64_t slots = ((int64_t)nchunk * per_chunk + 63) / 64;
-#define SAGA_SF(KPT, NWV)                                                                        \
-    hipLaunchKernelGGL((select_union_fast<KPT, NWV>), dim3((unsigned)((rows + NWV - 1) / NWV)), \
-                       dim3(64 * NWV), 0, st, tm.cand, tm.meta, lens, rows, h_q, h_k, N, S_max,   \
-                       nchunk, sel_idx, sel_val, row_max, row_cnt, idx_out, row_flag)
-    // LDS per wave: 512 KPT bytes of union + 1 KiB of chunk data
-    if (slots <= 16) SAGA_SF(16, 4);
-    else if (slots <= 32) SAGA_SF(32, 4);
-    else if (slots <= 48) SAGA_SF(48, 4);
-    else if (slots <= 64) SAGA_SF(64, 2);
-    else if (slots <= 96) SAGA_SF(96, 2);
-    else SAGA_SF(128, 1);
-#undef SAGA_SF
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    // deferred rows: a persistent pass that skips the settled ones
-    const unsigned grid = (unsigned)(rows < 256 ? rows : 256);
-#define SAGA_SU(T, D)                                                                            \
-    hipLaunchKernelGGL((select_union<T, D>), dim3(grid), dim3(kUnionThreads), 0, st, tm.cand,    \
-                       tm.meta, lens, rows, h_q, h_k, N, S_max, nchunk, sel_idx, sel_val,         \
-                       row_max, row_cnt, idx_out, row_flag, (const T*)q, (const T*)k, scores,     \
+    const int64_t slots = ((int64_t)nchunk * per_chunk + kUnionThreads - 1) / kUnionThreads;
+#define SAGA_SU(T, D, KPT)                                                                       \
+    hipLaunchKernelGGL((select_union<T, D, KPT>), dim3((unsigned)rows), dim3(kUnionThreads), 0,  \
+                       st, tm.cand, tm.meta, lens, h_q, h_k, N, S_max, nchunk, sel_idx, sel_val,   \
+                       row_max, row_cnt, idx_out, row_flag, (const T*)q, (const T*)k, scores,      \
                        s_stride, scale)
+#define SAGA_SU_K(T, D)                                                                          \
+    if (slots <= 8) SAGA_SU(T, D, 8);                                                            \
+    else if (slots <= 16) SAGA_SU(T, D, 16);                                                     \
+    else SAGA_SU(T, D, 32);
     if (bf16) {
-        if (d == 64) SAGA_SU(uint16_t, 64); else SAGA_SU(uint16_t, 128);
+        if (d == 64) { SAGA_SU_K(uint16_t, 64) } else { SAGA_SU_K(uint16_t, 128) }
     } else {
-        if (d == 64) SAGA_SU(float, 64); else SAGA_SU(float, 128);
+        if (d == 64) { SAGA_SU_K(float, 64) } else { SAGA_SU_K(float, 128) }
     }
+#undef SAGA_SU_K
 #undef SAGA_SU
     return hipGetLastError();
 }

@@ -113,7 +113,7 @@ def test_timed_entry_rejects_bad_event_lists_on_host():
     t = saga.saga_decode_attn_timed
     args = (FAKE, FAKE, FAKE, FAKE, FAKE, 2, 8, 2, 4, 64, 16, None, 100, saga.SAGA_BF16,
             FAKE * 16, 1 << 40, None)
-    assert t(*args, [FAKE] * 6) == saga.SAGA_ERR_INVALID_ARG      # more than five boundaries
+    assert t(*args, [FAKE] * 5) == saga.SAGA_ERR_INVALID_ARG      # more than four boundaries
     assert t(*args, [FAKE, 0]) == saga.SAGA_ERR_INVALID_ARG       # a null event
     bad = list(args)
     bad[5] = 0                                                   # B = 0, checked before events
