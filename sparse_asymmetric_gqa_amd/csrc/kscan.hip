@@ -38,6 +38,10 @@
 //                  what lets the selector prove its union result exact. The
 //                  two roles meet at one barrier per item, so candidate
 //                  extraction overlaps the K stream instead of stalling it.
+//                  The lists are packed into the workgroup's pool range and
+//                  staged in the LDS left over by the key buffers; they are
+//                  written out after the last item, so list stores do not
+//                  compete with the K stream.
 #include "saga_internal.h"
 
 namespace saga {
@@ -279,9 +283,22 @@ __global__ __launch_bounds__(256) void kscan(const T* __restrict__ q, const T* _
 // per-lane vector sums reduced once per probe.
 // The keys at or above the cutoff are then written in position order: a
 // prefix scan of the per-lane counts gives each lane its first slot.
+// Destination of the candidate lists of one workgroup: the workgroup's pool
+// range (entries from `base`), filled in order through an LDS cursor; the
+// first `cap` entries are staged in LDS (`stg`) and written out once, at the
+// end of the kernel, so that no list store competes with the K stream.
+struct ListSink {
+    uint2* pool;        // global: the workgroup's range
+    uint64_t base;      // its first entry (absolute index into the pool)
+    uint2* stg;         // LDS staging of entries [0, cap)
+    uint32_t cap;
+    uint32_t* cursor;   // LDS: next free entry (relative to base)
+    uint32_t* used;     // LDS: end of the staged lists
+};
+
 template <typename T>
 __device__ inline void extract(const Item<T>& it, int n, uint32_t M, uint32_t* row,
-                               uint32_t* warm, uint32_t* cursor, int lane, int g, int h_q,
+                               uint32_t* warm, const ListSink& sink, int lane, int g, int h_q,
                                int nchunk, const TopmOut& tm) {
     uint32_t kk[16];
 #pragma unroll
@@ -369,11 +386,14 @@ __device__ inline void extract(const Item<T>& it, int n, uint32_t M, uint32_t* r
     uint32_t total;
     const uint32_t first = wave_incl_scan(kc, total) - kc;
     const int64_t slot = ((int64_t)(it.b * h_q + it.kh * g + n) * nchunk + it.chunk);
-    // the list goes to the next free (16-byte aligned) place of the item's pool region
+    // the list goes to the next free (16-byte aligned) place of the
+    // workgroup's range: staged in LDS while it fits, else stored directly
     uint32_t off = 0;
-    if (lane == 0) off = atomicAdd(cursor, (total + 1u) & ~1u);
+    if (lane == 0) off = atomicAdd(sink.cursor, (total + 1u) & ~1u);
     off = __builtin_amdgcn_readfirstlane(off);
-    uint2* dst = tm.cand + ((int64_t)(it.bkh * nchunk + it.chunk) * g) * kScanChunk + off;
+    const bool staged_lds = off + total <= sink.cap;
+    if (staged_lds && lane == 0) atomicMax(sink.used, off + total);
+    uint2* dst = staged_lds ? sink.stg + off : sink.pool + off;
     uint32_t pos0 = (uint32_t)(it.c0 + 16 * lane);
     asm volatile("" : "+v"(pos0));   // positions are formed at each store, not held in registers
     if (total <= kStageMax) {
@@ -393,27 +413,34 @@ __device__ inline void extract(const Item<T>& it, int n, uint32_t M, uint32_t* r
             v2[0] = a0.x; v2[1] = a0.y; v2[2] = a1.x; v2[3] = a1.y;
             *reinterpret_cast<u32x4*>(dst + j) = v2;   // dst + j is 16-byte aligned (j even)
         }
+        __builtin_amdgcn_s_waitcnt(0xc07f);   // the head's row is reused as soon as this returns
     } else {
         uint32_t at = first;
 #pragma unroll
         for (int e = 0; e < 16; ++e)
             if (kk[e] >= lo) dst[at++] = make_uint2(pos0 + e, kk[e]);
     }
-    if (lane == 0) tm.meta[slot] = make_uint4(off, total, cut, 0u);
+    if (lane == 0) {
+        const uint64_t abs_off = sink.base + off;
+        tm.meta[slot] = make_uint4((uint32_t)abs_off, total, cut, (uint32_t)(abs_off >> 32));
+    }
 }
 
 // LDS layout of kscan_topm (32-bit words):
 //   keys [2][g][kScanChunk]   double-buffered key rows of the current items
 //   warm [g]                  previous cutoff per head
-//   cursor [2]                next free entry of the item's pool region (by item parity)
+//   cursor, used, pad [4]     list cursor and end of the staged lists
+//   stg  [..]                 staged candidate lists (uint2), the rest of the LDS
+constexpr size_t kTopmLdsBytes = 160 * 1024;   // LDS of a gfx950 CU
 __host__ __device__ constexpr size_t topm_lds_words(int g) {
-    return (size_t)2 * g * kScanChunk + g + 2;
+    return (size_t)2 * g * kScanChunk + ((g + 4 + 3) & ~3);   // stg starts 16-byte aligned
 }
 
 template <typename T, int DH>
 __global__ __launch_bounds__(kTopmThreads, 1) void kscan_topm(
         const T* __restrict__ q, const T* __restrict__ k, const int32_t* __restrict__ lens,
-        int h_q, int h_k, int64_t S_max, int nchunk, int nwork, float scale, TopmOut tm) {
+        int h_q, int h_k, int64_t S_max, int nchunk, int nwork, float scale, TopmOut tm,
+        uint32_t lds_bytes) {
     using S = Streamer<T, DH, 1>;
     constexpr int NS = S::NS;
     extern __shared__ uint32_t lds[];
@@ -423,7 +450,8 @@ __global__ __launch_bounds__(kTopmThreads, 1) void kscan_topm(
     const bool producer = wave < kWaves;
     uint32_t* keys = lds;
     uint32_t* warm = lds + 2 * g * kScanChunk;
-    uint32_t* cursor = warm + g;
+    uint32_t* cursor = warm + g;   // cursor[0]: next free entry, cursor[1]: end of staged lists
+    const uint32_t fixed_words = (uint32_t)((2 * g * kScanChunk + ((g + 4 + 3) & ~3)));
 
     // The workgroup takes a contiguous range of items (consecutive chunks of a
     // row), so that each head's previous cutoff is a good first guess.
@@ -431,6 +459,15 @@ __global__ __launch_bounds__(kTopmThreads, 1) void kscan_topm(
     const int wbeg = blockIdx.x * per;
     const int wend = wbeg + per < nwork ? wbeg + per : nwork;
     if (wbeg >= wend) return;   // uniform over the workgroup
+    // The workgroup's pool range is the regions of its items (g kScanChunk
+    // entries each); its lists are packed from the start of that range.
+    ListSink sink;
+    sink.base = (uint64_t)wbeg * g * kScanChunk;
+    sink.pool = tm.cand + sink.base;
+    sink.stg = reinterpret_cast<uint2*>(lds + fixed_words);
+    sink.cap = ((lds_bytes / 4 - fixed_words) / 2) & ~1u;
+    sink.cursor = cursor;
+    sink.used = cursor + 1;
     auto len_of = [&](int b) { return lens[b]; };   // uniform index: a scalar load
 
     Item<T> cur;
@@ -527,11 +564,9 @@ __global__ __launch_bounds__(kTopmThreads, 1) void kscan_topm(
                 uint32_t* kbuf = keys + ((t + 1) & 1) * g * kScanChunk;
 #pragma unroll 1
                 for (int n = wave - kWaves; n < g; n += kConsumers)
-                    extract(prev, n, M, kbuf + n * kScanChunk, warm, cursor + (t & 1), lane, g,
-                            h_q, nchunk, tm);
+                    extract(prev, n, M, kbuf + n * kScanChunk, warm, sink, lane, g, h_q,
+                            nchunk, tm);
             }
-            // the cursor of the next item's extraction starts from 0
-            if (threadIdx.x == 64 * kWaves) cursor[(t + 1) & 1] = 0u;
         }
         lds_barrier();   // keys of item t are complete; buffer (t - 1) & 1 is free again
         prev = cur;
@@ -542,6 +577,12 @@ __global__ __launch_bounds__(kTopmThreads, 1) void kscan_topm(
         }
         ++t;
     }
+    // all lists are published: write the staged ones out (16-byte stores;
+    // entries past a list's end are the alignment pads of its allocation)
+    const uint32_t used = (sink.used[0] + 1u) & ~1u;
+    const u32x4* s4 = reinterpret_cast<const u32x4*>(sink.stg);
+    u32x4* d4 = reinterpret_cast<u32x4*>(sink.pool);
+    for (uint32_t j = threadIdx.x; j < used / 2; j += kTopmThreads) d4[j] = s4[j];
 }
 
 int cu_count() {
@@ -615,18 +656,20 @@ hipError_t go_topm(const void* q, const void* k, const int32_t* lens, const Topm
     const int nwork = B * h_k * nchunk;
     const float scale = (float)(1.0 / __builtin_sqrt((double)DH));
     auto kern = &kscan_topm<T, DH>;
-    const size_t lds = topm_lds_words(h_q / h_k) * sizeof(uint32_t);
+    // the whole LDS: the key buffers, and the rest stages candidate lists
+    const size_t lds = kTopmLdsBytes;
+    static_assert(topm_lds_words(16) * 4 + 16 * 1024 <= kTopmLdsBytes, "staging area too small");
     static bool attr_set = false;   // one per instantiation: allow > 64 KiB of dynamic LDS
     if (!attr_set) {
         if (hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                hipFuncAttributeMaxDynamicSharedMemorySize,
-                                (int)(topm_lds_words(16) * sizeof(uint32_t))) != hipSuccess)
+                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
             return hipGetLastError();
         attr_set = true;
     }
     const int grid = resident_grid(kern, kTopmThreads, lds, nwork);
     hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kTopmThreads), lds, st, (const T*)q,
-                       (const T*)k, lens, h_q, h_k, S_max, nchunk, nwork, scale, tm);
+                       (const T*)k, lens, h_q, h_k, S_max, nchunk, nwork, scale, tm,
+                       (uint32_t)lds);
     return hipGetLastError();
 }
 

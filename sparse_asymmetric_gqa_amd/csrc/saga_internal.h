@@ -24,7 +24,7 @@ inline int64_t score_stride(int64_t S_max) { return round_up(S_max, 16); }
 struct Workspace {
     float* scores;      // [B][h_q][score_stride]  dense logits (dense path, fallback rows)
     uint2* cand;        // candidate pool: B*h_k*nchunk items x g*kScanChunk entries
-    uint4* cand_meta;   // [B][h_q][nchunk]  {offset in the item's pool region, count, cutoff, 0}
+    uint4* cand_meta;   // [B][h_q][nchunk]  {pool offset lo, count, cutoff, pool offset hi}
     int32_t* row_flag;  // [B][h_q]   1 if the row took the dense fallback in the last call
     int32_t* sel_idx;   // [B][h_q][N]
     float* sel_val;     // [B][h_q][N]
@@ -48,12 +48,13 @@ Workspace carve(void* base, int B, int h_q, int d, int N, int64_t S_max, bool de
 int sparse_nsplit(int N);          // ceil(N / kPvEntries)
 int dense_nsplit(int64_t S_max);   // ceil(S_max / kDenseRows)
 
-// Candidate lists published by the top-M K-scan. Work item w = (b*h_k + kh) *
-// nchunk + chunk owns the pool region cand[w*g*kScanChunk, (w+1)*g*kScanChunk),
-// where the lists of its g heads are packed in any order. For slot
-// (b*h_q + i, chunk): meta = {off, cnt, cut, 0} with the list at
-// cand[w*g*kScanChunk + off, +cnt) = (position, key) ascending in position,
-// and cut = the chunk's cutoff key (every key of the chunk left out is below it).
+// Candidate lists published by the top-M K-scan. The workgroup that takes
+// work items [w0, w1) packs the lists of their heads, in any order, from pool
+// entry w0 * g * kScanChunk on (the items' regions bound the total). For slot
+// (b*h_q + i, chunk): meta = {off_lo, cnt, cut, off_hi} with the list at
+// cand[off, off + cnt) = (position, key) ascending in position, off the 64-bit
+// absolute pool index, and cut = the chunk's cutoff key (every key of the
+// chunk left out is below it).
 struct TopmOut {
     uint2* cand;
     uint4* meta;       // [B*h_q][nchunk]

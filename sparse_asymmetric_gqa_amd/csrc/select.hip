@@ -463,16 +463,13 @@ __device__ void union_row(
     }
     const int nch = (int)((L + kScanChunk - 1) / kScanChunk);
     const uint4* meta = cand_meta + (int64_t)row * nchunk;
-    const int g = h_q / h_k;
-    // pool region of this row's chunk c: item (b*h_k + kh)*nchunk + c
-    const int64_t item0 = (int64_t)(b * h_k + i / g) * nchunk;
 
     // exclusive prefix of the chunk counts: each thread sums a contiguous run
     const int per = (nch + NT - 1) / NT;
     int32_t run = 0;
     for (int c = tid * per; c < nch && c < (tid + 1) * per; ++c) {
         const uint4 m = meta[c];
-        coff[c] = (item0 + c) * g * kScanChunk + m.x;
+        coff[c] = (int64_t)(((uint64_t)m.w << 32) | m.x);
         run += (int32_t)m.y;
     }
     int32_t incl = run;
@@ -555,7 +552,7 @@ template <int KPT>
 struct FastShared {
     uint2 uni[kUnionThreads * KPT];       // union, then the staged output
     uint32_t pref[kMaxChunks + 1];
-    uint32_t coff[kMaxChunks];
+    uint64_t coff[kMaxChunks];            // absolute pool index of each chunk's list
     uint32_t red[2][kUnionThreads / 64];  // wave partials, double-buffered
 };
 template <int KPT>
@@ -621,7 +618,6 @@ __global__ __launch_bounds__(kUnionThreads, 4) void select_union(
     const int row = blockIdx.x;
     const int tid = threadIdx.x;
     const int b = row / h_q;
-    const int i = row - b * h_q;
     const int64_t L = clamp_len(lens[b], S_max);
     const int n_eff = (int)((int64_t)N < L ? (int64_t)N : L);
     const int nch = (int)((L + kScanChunk - 1) / kScanChunk);
@@ -639,8 +635,6 @@ __global__ __launch_bounds__(kUnionThreads, 4) void select_union(
     // chunk lists: prefix of the counts and pool offsets (relative to the
     // row's first item region) in LDS, largest cutoff
     const uint4* meta = cand_meta + (int64_t)row * nchunk;
-    const int g = h_q / h_k;
-    const uint2* pool = cand + (int64_t)(b * h_k + i / g) * nchunk * g * kScanChunk;
     uint32_t carry = 0, mcut = 0;
     for (int c0 = 0; c0 < nch; c0 += NT) {   // uniform trip count
         const int c = c0 + tid;
@@ -650,7 +644,7 @@ __global__ __launch_bounds__(kUnionThreads, 4) void select_union(
         const uint32_t ex = block_excl_scan(m.y, F.red[(c0 / NT) & 1], tot);
         if (c < nch) {
             F.pref[c] = carry + ex;
-            F.coff[c] = (uint32_t)c * g * kScanChunk + m.x;
+            F.coff[c] = ((uint64_t)m.w << 32) | m.x;
         }
         carry += tot;
         mcut = m.z > mcut ? m.z : mcut;
@@ -680,7 +674,7 @@ __global__ __launch_bounds__(kUnionThreads, 4) void select_union(
                         const uint32_t mid = (lo + hi) >> 1;
                         if (F.pref[mid] <= j) lo = mid; else hi = mid;
                     }
-                ev[u] = pool[valid ? F.coff[lo] + (j - F.pref[lo]) : 0u];
+                ev[u] = cand[valid ? F.coff[lo] + (j - F.pref[lo]) : 0u];
             }
 #pragma unroll
             for (int u = 0; u < KPT; ++u)
