@@ -294,12 +294,15 @@ struct ListSink {
     uint32_t cap;
     uint32_t* cursor;   // LDS: next free entry (relative to base)
     uint32_t* used;     // LDS: end of the staged lists
+    uint4* meta_stg;    // LDS: metadata records of the first kMetaStage (item, head) pairs
+    uint32_t* meta_slot;   // LDS: their slots
 };
+constexpr int kMetaStage = 256;
 
 template <typename T>
 __device__ inline void extract(const Item<T>& it, int n, uint32_t M, uint32_t* row,
-                               uint32_t* warm, const ListSink& sink, int lane, int g, int h_q,
-                               int nchunk, const TopmOut& tm) {
+                               uint32_t* warm, const ListSink& sink, int local, int lane, int g,
+                               int h_q, int nchunk, const TopmOut& tm) {
     uint32_t kk[16];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -422,7 +425,14 @@ __device__ inline void extract(const Item<T>& it, int n, uint32_t M, uint32_t* r
     }
     if (lane == 0) {
         const uint64_t abs_off = sink.base + off;
-        tm.meta[slot] = make_uint4((uint32_t)abs_off, total, cut, (uint32_t)(abs_off >> 32));
+        const uint4 m = make_uint4((uint32_t)abs_off, total, cut, (uint32_t)(abs_off >> 32));
+        const int e = local * g + n;   // staged while it fits, like the lists
+        if (e < kMetaStage) {
+            sink.meta_stg[e] = m;
+            sink.meta_slot[e] = (uint32_t)slot;
+        } else {
+            tm.meta[slot] = m;
+        }
     }
 }
 
@@ -430,10 +440,12 @@ __device__ inline void extract(const Item<T>& it, int n, uint32_t M, uint32_t* r
 //   keys [2][g][kScanChunk]   double-buffered key rows of the current items
 //   warm [g]                  previous cutoff per head
 //   cursor, used, pad [4]     list cursor and end of the staged lists
+//   meta_stg [kMetaStage] uint4, meta_slot [kMetaStage]   staged metadata
 //   stg  [..]                 staged candidate lists (uint2), the rest of the LDS
 constexpr size_t kTopmLdsBytes = 160 * 1024;   // LDS of a gfx950 CU
 __host__ __device__ constexpr size_t topm_lds_words(int g) {
-    return (size_t)2 * g * kScanChunk + ((g + 4 + 3) & ~3);   // stg starts 16-byte aligned
+    // stg and meta_stg start 16-byte aligned
+    return (size_t)2 * g * kScanChunk + ((g + 4 + 3) & ~3) + 5 * kMetaStage;
 }
 
 template <typename T, int DH>
@@ -451,7 +463,8 @@ __global__ __launch_bounds__(kTopmThreads, 1) void kscan_topm(
     uint32_t* keys = lds;
     uint32_t* warm = lds + 2 * g * kScanChunk;
     uint32_t* cursor = warm + g;   // cursor[0]: next free entry, cursor[1]: end of staged lists
-    const uint32_t fixed_words = (uint32_t)((2 * g * kScanChunk + ((g + 4 + 3) & ~3)));
+    uint32_t* meta_words = lds + 2 * g * kScanChunk + ((g + 4 + 3) & ~3);
+    const uint32_t fixed_words = (uint32_t)topm_lds_words(g);
 
     // The workgroup takes a contiguous range of items (consecutive chunks of a
     // row), so that each head's previous cutoff is a good first guess.
@@ -468,6 +481,8 @@ __global__ __launch_bounds__(kTopmThreads, 1) void kscan_topm(
     sink.cap = ((lds_bytes / 4 - fixed_words) / 2) & ~1u;
     sink.cursor = cursor;
     sink.used = cursor + 1;
+    sink.meta_stg = reinterpret_cast<uint4*>(meta_words);
+    sink.meta_slot = meta_words + 4 * kMetaStage;
     auto len_of = [&](int b) { return lens[b]; };   // uniform index: a scalar load
 
     Item<T> cur;
@@ -564,8 +579,8 @@ __global__ __launch_bounds__(kTopmThreads, 1) void kscan_topm(
                 uint32_t* kbuf = keys + ((t + 1) & 1) * g * kScanChunk;
 #pragma unroll 1
                 for (int n = wave - kWaves; n < g; n += kConsumers)
-                    extract(prev, n, M, kbuf + n * kScanChunk, warm, sink, lane, g, h_q,
-                            nchunk, tm);
+                    extract(prev, n, M, kbuf + n * kScanChunk, warm, sink, t - 1, lane, g,
+                            h_q, nchunk, tm);
             }
         }
         lds_barrier();   // keys of item t are complete; buffer (t - 1) & 1 is free again
@@ -583,6 +598,10 @@ __global__ __launch_bounds__(kTopmThreads, 1) void kscan_topm(
     const u32x4* s4 = reinterpret_cast<const u32x4*>(sink.stg);
     u32x4* d4 = reinterpret_cast<u32x4*>(sink.pool);
     for (uint32_t j = threadIdx.x; j < used / 2; j += kTopmThreads) d4[j] = s4[j];
+    // and the staged metadata records (items 0 .. t-2 of this workgroup)
+    const int nmeta = (t - 1) * g < kMetaStage ? (t - 1) * g : kMetaStage;
+    for (int e = (int)threadIdx.x; e < nmeta; e += kTopmThreads)
+        tm.meta[sink.meta_slot[e]] = sink.meta_stg[e];
 }
 
 int cu_count() {
