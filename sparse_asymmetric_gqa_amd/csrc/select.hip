@@ -24,11 +24,12 @@
 //   union  -- the candidate lists the top-M K-scan published per chunk. The
 //             union's key of rank N_eff, T, is the true one when every chunk
 //             cutoff is <= T (all keys a chunk left out are below its cutoff,
-//             hence below T, so exactly the keys >= T are all present). A
-//             wave per row settles the common case with all keys in
-//             registers; rows it cannot settle go to a workgroup per row,
-//             which recomputes the head's logits and selects on them densely
-//             when the check fails, so the result is always exact.
+//             hence below T, so exactly the keys >= T are all present). One
+//             workgroup per row: rows of at most 256 chunks whose lists fit
+//             the registers settle with a histogram descent (select_union);
+//             the rest take the general code (union_row), which also
+//             recomputes the head's logits and selects on them densely when
+//             the check fails, so the result is always exact.
 #include "saga_internal.h"
 
 namespace saga {
@@ -537,261 +538,248 @@ __device__ void union_row(
 }
 
 // ---- union select, one workgroup per row -------------------------------------------
-// Fast path: the row's candidate union in registers across the workgroup,
-// thread-major: with P = ceil(total / 256), thread t holds union elements
-// [t P, t P + P) (ascending position, thread by thread). The union's key of
-// rank N_eff, T, is found by bisection of [max chunk cutoff, max key]; the
-// count at the lower end being >= N_eff is exactly the proof that every chunk
-// cutoff is <= T, so the result is exact. A probe is a per-thread count, a DPP
-// wave sum and one exchange of the four wave sums through LDS. Compaction is
-// two workgroup prefix scans (ties in position order, then output slots) and
-// LDS-staged 16-byte stores. Rows the fast path cannot take (more than 256 KPT
-// candidates, or count(key >= max cutoff) < N_eff) go through union_row in
-// the same workgroup: the multi-tile union select, or the dense recompute.
-template <int KPT>
+// Fast path, for rows of at most 256 chunks. tpc = floor(256 / chunks) threads
+// share each chunk's list: thread t takes chunk t / tpc and, within it, a run
+// of P consecutive entries (P even, so the run starts on a 16-byte boundary
+// and is read with 16-byte loads straight from the list the chunk's meta entry
+// points at). Thread order is therefore position order. The union's key of
+// rank N_eff, T, is searched in [max chunk cutoff, max key]: the count of keys
+// at or above the lower end being >= N_eff is exactly the proof that every
+// chunk cutoff is <= T, so the result is exact. The search is a histogram
+// descent: each pass spreads the keys of the current range over 256 LDS bins
+// (shared-memory atomics), and every wave then scans the 256 bins itself to
+// pick the bin holding rank N_eff, so a pass costs one barrier and narrows
+// the range by 8 bits (at most four passes); it stops early as soon as the
+// keys at or above a bin's lower end are exactly N_eff. Compaction is one
+// workgroup prefix scan of the packed (above T, equal to T) counts: equal keys
+// at T are taken in position order. The kept entries are staged in LDS and
+// written with 16-byte stores. Rows the fast path cannot take (a run longer
+// than KPT, or the proof failing) go through union_row in the same workgroup:
+// the multi-tile union select, or the dense recompute.
 struct FastShared {
-    uint2 uni[kUnionThreads * KPT];       // union, then the staged output
-    uint32_t pref[kMaxChunks + 1];
-    uint64_t coff[kMaxChunks];            // absolute pool index of each chunk's list
-    uint32_t red[2][kUnionThreads / 64];  // wave partials, double-buffered
+    uint32_t hist[3][kUnionThreads];       // one bin per thread, three in rotation
+    uint4 red[kUnionThreads / 64];         // wave maxima: max key, max cutoff, overflow
+    uint32_t scan[kUnionThreads / 64];     // wave totals of the compaction scan
 };
-template <int KPT>
-union SelectShared {
-    FastShared<KPT> f;
-    UnionShared u;
-};
+// The fast path's output staging (indices, then logits) follows FastShared.
+__host__ __device__ constexpr size_t select_stage_offset() {
+    return (sizeof(FastShared) + 15) & ~(size_t)15;
+}
 
-// Sum / max over the workgroup of one value per thread (uniform result); the
-// partials go to red[buf], so consecutive calls must alternate buf.
-__device__ inline uint32_t block_sum(uint32_t v, uint32_t* red) {
-    const uint32_t w = wave_sum(v);
-    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = w;
-    __syncthreads();
-    uint32_t t = 0;
-#pragma unroll
-    for (int k = 0; k < kUnionThreads / 64; ++k) t += red[k];
-    return t;
-}
-__device__ inline uint32_t block_max(uint32_t v, uint32_t* red) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-        const uint32_t y = (uint32_t)__shfl_xor((int)v, o, 64);
-        v = y > v ? y : v;
-    }
-    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
-    __syncthreads();
-    uint32_t t = 0;
-#pragma unroll
-    for (int k = 0; k < kUnionThreads / 64; ++k) t = red[k] > t ? red[k] : t;
-    return t;
-}
-// Exclusive prefix over the workgroup (thread order) and the total.
-__device__ inline uint32_t block_excl_scan(uint32_t v, uint32_t* red, uint32_t& total) {
-    uint32_t wt;
-    const uint32_t incl = wave_incl_scan(v, wt);
-    const int wave = threadIdx.x >> 6;
-    if ((threadIdx.x & 63) == 0) red[wave] = wt;
-    __syncthreads();
-    uint32_t before = 0;
-    total = 0;
-#pragma unroll
-    for (int k = 0; k < kUnionThreads / 64; ++k) {
-        if (k < wave) before += red[k];
-        total += red[k];
-    }
-    return before + incl - v;
+__device__ inline uint32_t wave_umax(uint32_t v) {
+    // lanes without a source keep 0, the identity of an unsigned maximum
+    int x = (int)v, y;
+    y = __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, false); x = (uint32_t)y > (uint32_t)x ? y : x;
+    y = __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, false); x = (uint32_t)y > (uint32_t)x ? y : x;
+    y = __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, false); x = (uint32_t)y > (uint32_t)x ? y : x;
+    y = __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, false); x = (uint32_t)y > (uint32_t)x ? y : x;
+    uint32_t r = (uint32_t)__builtin_amdgcn_readlane(x, 15);
+    uint32_t t = (uint32_t)__builtin_amdgcn_readlane(x, 31); r = t > r ? t : r;
+    t = (uint32_t)__builtin_amdgcn_readlane(x, 47); r = t > r ? t : r;
+    t = (uint32_t)__builtin_amdgcn_readlane(x, 63); r = t > r ? t : r;
+    return r;
 }
 
 // Four workgroups per CU (<= 128 VGPRs): the general code spills at this
-// bound, which only costs the rare rows that need it.
+// bound, which only costs the rare rows that need it. Dynamic LDS:
+// max(sizeof(UnionShared), select_stage_offset() + 8 nst) bytes, nst >= the
+// kept entries of any fast-path row, a multiple of 4.
 template <typename T, int DH, int KPT>
 __global__ __launch_bounds__(kUnionThreads, 4) void select_union(
     const uint2* __restrict__ cand, const uint4* __restrict__ cand_meta,
-    const int32_t* __restrict__ lens, int h_q, int h_k, int N, int64_t S_max, int nchunk,
+    const int32_t* __restrict__ lens, int h_q, int h_k, int N, int64_t S_max, int nchunk, int nst,
     int32_t* __restrict__ sel_idx, float* __restrict__ sel_val, float* __restrict__ row_max,
     int32_t* __restrict__ row_cnt, int32_t* __restrict__ idx_out, int32_t* __restrict__ row_flag,
     const T* __restrict__ q, const T* __restrict__ k, float* __restrict__ scores,
     int64_t s_stride, float scale) {
+    static_assert(KPT % 2 == 0, "entries are loaded in pairs");
     constexpr int NT = kUnionThreads;
-    __shared__ SelectShared<KPT> sm;
-    FastShared<KPT>& F = sm.f;
+    extern __shared__ __attribute__((aligned(16))) unsigned char sel_lds[];
+    FastShared& F = *reinterpret_cast<FastShared*>(sel_lds);
+    UnionShared& U = *reinterpret_cast<UnionShared*>(sel_lds);
     const int row = blockIdx.x;
     const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int b = row / h_q;
     const int64_t L = clamp_len(lens[b], S_max);
     const int n_eff = (int)((int64_t)N < L ? (int64_t)N : L);
     const int nch = (int)((L + kScanChunk - 1) / kScanChunk);
-    if (n_eff == 0 || nch > kMaxChunks) {
-        // no kept entry, or too many chunks for the fast path: the general code
-        union_row<T, DH>(row, sm.u, cand, cand_meta, lens, h_q, h_k, N, S_max, nchunk, sel_idx,
+    auto general = [&] {
+        union_row<T, DH>(row, U, cand, cand_meta, lens, h_q, h_k, N, S_max, nchunk, sel_idx,
                          sel_val, row_max, row_cnt, idx_out, row_flag, q, k, scores, s_stride,
                          scale);
+    };
+    if (n_eff == 0 || nch > NT) {   // no kept entry, or too many chunks: the general code
+        general();
         return;
     }
     int32_t* oi = sel_idx + (int64_t)row * N;
     float* ov = sel_val + (int64_t)row * N;
     int32_t* ou = idx_out ? idx_out + (int64_t)row * N : nullptr;
+    int32_t* st_idx = reinterpret_cast<int32_t*>(sel_lds + select_stage_offset());
+    float* st_val = reinterpret_cast<float*>(st_idx + nst);
 
-    // chunk lists: prefix of the counts and pool offsets (relative to the
-    // row's first item region) in LDS, largest cutoff
-    const uint4* meta = cand_meta + (int64_t)row * nchunk;
-    uint32_t carry = 0, mcut = 0;
-    for (int c0 = 0; c0 < nch; c0 += NT) {   // uniform trip count
-        const int c = c0 + tid;
-        uint4 m = make_uint4(0u, 0u, 0u, 0u);
-        if (c < nch) m = meta[c];
-        uint32_t tot;
-        const uint32_t ex = block_excl_scan(m.y, F.red[(c0 / NT) & 1], tot);
-        if (c < nch) {
-            F.pref[c] = carry + ex;
-            F.coff[c] = ((uint64_t)m.w << 32) | m.x;
-        }
-        carry += tot;
-        mcut = m.z > mcut ? m.z : mcut;
+    F.hist[0][tid] = 0u;
+    // this thread's run of its chunk's list
+    const int tpc = NT / nch;
+    const int c = tid / tpc;
+    const int sub = tid - c * tpc;
+    const bool cv = c < nch;
+    const uint4 m = cand_meta[(int64_t)row * nchunk + (cv ? c : nch - 1)];
+    const uint32_t cnt = cv ? m.y : 0u;
+    const uint32_t P = (((cnt + (uint32_t)tpc - 1u) / (uint32_t)tpc) + 1u) & ~1u;
+    const uint32_t j0 = (uint32_t)sub * P;
+    const uint32_t mine = cnt > j0 ? (cnt - j0 < P ? cnt - j0 : P) : 0u;
+    const uint32_t npair = (mine + 1u) >> 1;
+    // lists start at even pool entries and runs at even offsets: 16-byte
+    // aligned; pairs past the run re-read its last pair (an empty run reads
+    // the pool's first pair), so every load is unconditional and in bounds
+    const uint4* run = reinterpret_cast<const uint4*>(cand + ((((uint64_t)m.w << 32) | m.x) + j0));
+    uint4 ev[KPT / 2];
+#pragma unroll
+    for (int p = 0; p < KPT / 2; ++p) {
+        const uint4* a = npair ? run + ((uint32_t)p < npair ? (uint32_t)p : npair - 1u)
+                               : reinterpret_cast<const uint4*>(cand);
+        ev[p] = *a;
     }
-    if (tid == 0) F.pref[nch] = carry;
-    const uint32_t total = carry;
-    __syncthreads();   // pref / coff complete; red[0] is free again
-    const uint32_t maxcut = block_max(mcut, F.red[1]);
-    bool fast = total >= (uint32_t)n_eff && total <= (uint32_t)(NT * KPT);
     uint32_t key[KPT];
     int32_t pos[KPT];
     uint32_t kmax = 0;
-    if (fast) {   // uniform
-        // The union, element-major (element j = tid + 256 u): coalesced loads,
-        // all issued before any is waited for, then written to LDS.
-        const uint32_t nu = (total + NT - 1) / NT;
-        {
-            uint2 ev[KPT];
 #pragma unroll
-            for (int u = 0; u < KPT; ++u) {
-                const uint32_t j = (uint32_t)(tid + NT * u);
-                const bool valid = j < total;
-                // chunk of element j: largest c with pref[c] <= j (binary search)
-                uint32_t lo = 0, hi = (uint32_t)nch;
-                if (valid)
-                    while (hi - lo > 1) {
-                        const uint32_t mid = (lo + hi) >> 1;
-                        if (F.pref[mid] <= j) lo = mid; else hi = mid;
-                    }
-                ev[u] = cand[valid ? F.coff[lo] + (j - F.pref[lo]) : 0u];
-            }
+    for (int s = 0; s < KPT; ++s) {
+        const uint4 e = ev[s >> 1];
+        const bool v = (uint32_t)s < mine;   // empty slots hold key 0, below every real key
+        pos[s] = (int32_t)((s & 1) ? e.z : e.x);
+        key[s] = v ? ((s & 1) ? e.w : e.y) : 0u;
+        kmax = key[s] > kmax ? key[s] : kmax;
+    }
+    {
+        const uint32_t wk = wave_umax(kmax);
+        const uint32_t wc = wave_umax(cv ? m.z : 0u);
+        const uint32_t wo = wave_umax(P > (uint32_t)KPT ? 1u : 0u);
+        if (lane == 0) F.red[wave] = make_uint4(wk, wc, wo, 0u);
+    }
+    __syncthreads();
+    uint32_t maxcut = 0, ovf = 0;
+    kmax = 0;
 #pragma unroll
-            for (int u = 0; u < KPT; ++u)
-                if ((uint32_t)u < nu) F.uni[tid + NT * u] = ev[u];
-        }
+    for (int w = 0; w < NT / 64; ++w) {
+        const uint4 r = F.red[w];
+        kmax = r.x > kmax ? r.x : kmax;
+        maxcut = r.y > maxcut ? r.y : maxcut;
+        ovf |= r.z;
+    }
+    uint32_t lo = maxcut > 1u ? maxcut : 1u;
+    uint32_t hi = kmax;
+    if (ovf != 0u || hi < lo) {   // uniform; hi < lo: no key reaches the largest cutoff
         __syncthreads();
-        // thread-major registers: thread t holds [t P, t P + P); empty slots
-        // hold key 0, below every real key
-        const uint32_t P = nu;
-        const uint32_t j0 = (uint32_t)tid * P;
-        const uint32_t jend = j0 + P < total ? j0 + P : total;
-#pragma unroll
-        for (int s = 0; s < KPT; ++s) {
-            const uint32_t j = j0 + (uint32_t)s;
-            const bool valid = (uint32_t)s < P && j < jend;
-            const uint2 v = F.uni[valid ? j : 0u];
-            pos[s] = valid ? (int32_t)v.x : -1;
-            key[s] = valid ? v.y : 0u;
-        }
-#pragma unroll
-        for (int s = 0; s < KPT; ++s) kmax = key[s] > kmax ? key[s] : kmax;
-        kmax = block_max(kmax, F.red[0]);
-        // the proof: count(key >= max cutoff) >= N_eff
-        auto lane_ge = [&](uint32_t x) -> uint32_t {
-            uint32_t c[4] = {0u, 0u, 0u, 0u};
-#pragma unroll
-            for (int s = 0; s < KPT; ++s) c[s & 3] += key[s] >= x ? 1u : 0u;
-            return (c[0] + c[1]) + (c[2] + c[3]);
-        };
-        const uint32_t a0 = maxcut > 1u ? maxcut : 1u;
-        int buf = 1;
-        fast = block_sum(lane_ge(a0), F.red[buf]) >= (uint32_t)n_eff;
-        buf ^= 1;
-        if (fast) {
-            // T: the largest x with count(key >= x) >= n_eff, in [a, z)
-            uint32_t a = a0;
-            uint64_t z = (uint64_t)kmax + 1;
+        general();
+        return;
+    }
+
+    // histogram descent for T
+    uint32_t need = (uint32_t)n_eff, Tk = 0;
 #pragma unroll 1
-            while (z - a > 1) {
-                const uint32_t mid = (uint32_t)(a + ((z - a) >> 1));
-                const uint32_t c = block_sum(lane_ge(mid), F.red[buf]);
-                buf ^= 1;
-                if (c == (uint32_t)n_eff) {
-                    // exactly n_eff keys are >= mid: T is the smallest of them
-                    uint32_t mn = 0xFFFFFFFFu;
+    for (int pass = 0;; ++pass) {
+        uint32_t* h = F.hist[pass % 3];
+        F.hist[(pass + 1) % 3][tid] = 0u;   // last read two passes ago
+        const uint32_t span = hi - lo;
+        const int nb = span ? 32 - __clz((int)span) : 0;
+        const int shift = nb > 8 ? nb - 8 : 0;
 #pragma unroll
-                    for (int s = 0; s < KPT; ++s)
-                        if (key[s] >= mid && key[s] < mn) mn = key[s];
-                    a = ~block_max(~mn, F.red[buf]);
-                    buf ^= 1;
-                    break;
-                }
-                if (c > (uint32_t)n_eff) a = mid; else z = mid;
-            }
-            const uint32_t Tk = a;
-            // Compaction: keys > T are kept; of the keys == T, the first krem in
-            // position order, krem = n_eff - count(> T).
-            uint32_t ngt = 0, neq = 0;
-#pragma unroll
-            for (int s = 0; s < KPT; ++s) {
-                ngt += key[s] > Tk ? 1u : 0u;
-                neq += key[s] == Tk ? 1u : 0u;
-            }
-            const uint32_t tot_gt = block_sum(ngt, F.red[buf]);
-            buf ^= 1;
-            uint32_t tot_eq;
-            const uint32_t eq_base = block_excl_scan(neq, F.red[buf], tot_eq);
-            buf ^= 1;
-            const uint32_t krem = (uint32_t)n_eff - tot_gt;
-            const uint32_t eq_keep =
-                krem > eq_base ? (krem - eq_base < neq ? krem - eq_base : neq) : 0u;
-            const uint32_t nkeep = ngt + eq_keep;
-            uint32_t tot_keep;
-            uint32_t slot = block_excl_scan(nkeep, F.red[buf], tot_keep);
-            buf ^= 1;
-            // staged output: indices in uni[0 .. ), logits after them (the
-            // union is in registers now; n_eff <= total <= 256 KPT <= 8192)
-            int32_t* st_idx = reinterpret_cast<int32_t*>(F.uni);
-            float* st_val = reinterpret_cast<float*>(F.uni) + NT * KPT;
-            uint32_t eq_seen = 0;
-#pragma unroll
-            for (int s = 0; s < KPT; ++s) {
-                const bool eq = key[s] == Tk;
-                const bool keep = key[s] > Tk || (eq && eq_seen < eq_keep);
-                eq_seen += eq ? 1u : 0u;
-                if (keep && slot < (uint32_t)n_eff) {   // holds by construction
-                    st_idx[slot] = pos[s];
-                    st_val[slot] = key_float(key[s]);
-                }
-                slot += keep ? 1u : 0u;
-            }
+        for (int s = 0; s < KPT; ++s)
+            if (key[s] >= lo && key[s] <= hi)
+                __hip_atomic_fetch_add(h + ((key[s] - lo) >> shift), 1u, __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_WORKGROUP);
+        __syncthreads();
+        // lane l holds bins 255-4l (top) down to 252-4l; every wave scans all
+        const uint4 hv = reinterpret_cast<const uint4*>(h)[63 - lane];
+        const uint32_t lsum = (hv.x + hv.y) + (hv.z + hv.w);
+        uint32_t total;
+        const uint32_t incl = wave_incl_scan(lsum, total);   // keys in bins >= 252-4l
+        if (pass == 0 && total < need) {   // uniform: the proof fails
             __syncthreads();
-            const bool v4 = (((uintptr_t)oi | (uintptr_t)ov | (uintptr_t)ou) & 15u) == 0;
-            const int n4 = v4 ? n_eff / 4 : 0;
-            for (int j = tid; j < n4; j += NT) {
-                const int4 vi = reinterpret_cast<const int4*>(st_idx)[j];
-                reinterpret_cast<int4*>(oi)[j] = vi;
-                reinterpret_cast<float4*>(ov)[j] = reinterpret_cast<const float4*>(st_val)[j];
-                if (ou) reinterpret_cast<int4*>(ou)[j] = vi;
-            }
-            for (int j = 4 * n4 + tid; j < N; j += NT) {
-                const bool kept = j < n_eff;
-                oi[j] = kept ? st_idx[j] : -1;
-                ov[j] = kept ? st_val[j] : -__builtin_inff();
-                if (ou) ou[j] = kept ? st_idx[j] : -1;
-            }
-            if (tid == 0) {
-                row_max[row] = key_float(kmax);
-                row_cnt[row] = n_eff;
-                row_flag[row] = 0;
-            }
+            general();
             return;
         }
+        const uint32_t above0 = incl - lsum;
+        const uint64_t hit = ballot(incl >= need && above0 < need);
+        const int hl = (int)__builtin_ctzll(hit);   // exactly one lane
+        uint32_t bin = 255u - 4u * (uint32_t)lane, above = above0, inbin = hv.w;
+        if (above + hv.w < need) {
+            above += hv.w; bin -= 1u; inbin = hv.z;
+            if (above + hv.z < need) {
+                above += hv.z; bin -= 1u; inbin = hv.y;
+                if (above + hv.y < need) { above += hv.y; bin -= 1u; inbin = hv.x; }
+            }
+        }
+        bin = (uint32_t)__builtin_amdgcn_readlane((int)bin, hl);
+        above = (uint32_t)__builtin_amdgcn_readlane((int)above, hl);
+        inbin = (uint32_t)__builtin_amdgcn_readlane((int)inbin, hl);
+        need -= above;
+        lo += bin << shift;
+        const uint32_t wmask = (1u << shift) - 1u;
+        hi = hi - lo <= wmask ? hi : lo + wmask;
+        if (inbin == need || shift == 0) {   // keys >= lo are exactly N_eff, or the bin is one key
+            Tk = lo;
+            break;
+        }
     }
-    __syncthreads();   // the fast path's LDS is reused by the general code
-    union_row<T, DH>(row, sm.u, cand, cand_meta, lens, h_q, h_k, N, S_max, nchunk, sel_idx,
-                     sel_val, row_max, row_cnt, idx_out, row_flag, q, k, scores, s_stride, scale);
+
+    // compaction: keys > T, then the first krem keys == T in position order
+    uint32_t ngt = 0, neq = 0;
+#pragma unroll
+    for (int s = 0; s < KPT; ++s) {
+        ngt += key[s] > Tk ? 1u : 0u;
+        neq += key[s] == Tk ? 1u : 0u;
+    }
+    const uint32_t packed = ngt | (neq << 16);   // each sum <= 256 KPT < 2^16
+    uint32_t wtot;
+    const uint32_t pincl = wave_incl_scan(packed, wtot);
+    if (lane == 0) F.scan[wave] = wtot;
+    __syncthreads();
+    uint32_t before = pincl - packed, tot = 0;
+#pragma unroll
+    for (int w = 0; w < NT / 64; ++w) {
+        const uint32_t x = F.scan[w];
+        before += w < wave ? x : 0u;
+        tot += x;
+    }
+    const uint32_t krem = (uint32_t)n_eff - (tot & 0xFFFFu);
+    uint32_t eq_seen = before >> 16;
+    uint32_t slot = (before & 0xFFFFu) + (eq_seen < krem ? eq_seen : krem);
+#pragma unroll
+    for (int s = 0; s < KPT; ++s) {
+        const bool eq = key[s] == Tk;
+        const bool keep = key[s] > Tk || (eq && eq_seen < krem);
+        eq_seen += eq ? 1u : 0u;
+        if (keep) {   // slot < N_eff by construction
+            st_idx[slot] = pos[s];
+            st_val[slot] = key_float(key[s]);
+        }
+        slot += keep ? 1u : 0u;
+    }
+    __syncthreads();
+    const bool v4 = (((uintptr_t)oi | (uintptr_t)ov | (uintptr_t)ou) & 15u) == 0;
+    const int n4 = v4 ? n_eff / 4 : 0;
+    for (int j = tid; j < n4; j += NT) {
+        const int4 vi = reinterpret_cast<const int4*>(st_idx)[j];
+        reinterpret_cast<int4*>(oi)[j] = vi;
+        reinterpret_cast<float4*>(ov)[j] = reinterpret_cast<const float4*>(st_val)[j];
+        if (ou) reinterpret_cast<int4*>(ou)[j] = vi;
+    }
+    for (int j = 4 * n4 + tid; j < N; j += NT) {
+        const bool kept = j < n_eff;
+        oi[j] = kept ? st_idx[j] : -1;
+        ov[j] = kept ? st_val[j] : -__builtin_inff();
+        if (ou) ou[j] = kept ? st_idx[j] : -1;
+    }
+    if (tid == 0) {
+        row_max[row] = key_float(kmax);
+        row_cnt[row] = n_eff;
+        row_flag[row] = 0;
+    }
 }
 
 template <int KPT>
@@ -829,18 +817,31 @@ hipError_t launch_select_union(const TopmOut& tm, const int32_t* lens, int B, in
     const int nchunk = (int)((S_max + kScanChunk - 1) / kScanChunk);
     const int rows = B * h_q;
     const float scale = (float)(1.0 / __builtin_sqrt((double)d));
-    // Register slots per thread for the fast path: ceil(union size / 256), the
-    // union holding up to 1.25 M = 1.25 (1.5 share + 16) keys per full chunk
-    // (share = N * 1024 / L); larger unions take the general code.
+    // Registers per thread for the fast path: the longest run, an even
+    // ceil(per_chunk / tpc) with tpc = floor(256 / chunks) threads per chunk
+    // and up to per_chunk = 1.25 (1.5 share + 16) keys in a full chunk's list
+    // (share = N * 1024 / L); rows with longer runs take the general code.
     const double share = (double)N * kScanChunk / (double)S_max;
     int64_t per_chunk = (int64_t)(1.25 * (1.5 * share + 16.0)) + 1;
     per_chunk = per_chunk < kScanChunk ? per_chunk : kScanChunk;
-    const int64_t slots = ((int64_t)nchunk * per_chunk + kUnionThreads - 1) / kUnionThreads;
+    const int64_t tpc = nchunk <= kUnionThreads ? kUnionThreads / nchunk : 1;
+    const int64_t slots = (((per_chunk + tpc - 1) / tpc) + 1) & ~(int64_t)1;
+    // staged kept entries: N_eff <= N, and <= the 256 KPT keys in registers
+    auto lds_for = [&](int kpt) -> size_t {
+        int64_t nst = (int64_t)N < (int64_t)kUnionThreads * kpt ? (int64_t)N : (int64_t)kUnionThreads * kpt;
+        nst = (nst + 3) & ~(int64_t)3;
+        const size_t fast = select_stage_offset() + (size_t)nst * 8;
+        return fast > sizeof(UnionShared) ? fast : sizeof(UnionShared);
+    };
+    auto nst_for = [&](int kpt) -> int {
+        int64_t nst = (int64_t)N < (int64_t)kUnionThreads * kpt ? (int64_t)N : (int64_t)kUnionThreads * kpt;
+        return (int)((nst + 3) & ~(int64_t)3);
+    };
 #define SAGA_SU(T, D, KPT)                                                                       \
-    hipLaunchKernelGGL((select_union<T, D, KPT>), dim3((unsigned)rows), dim3(kUnionThreads), 0,  \
-                       st, tm.cand, tm.meta, lens, h_q, h_k, N, S_max, nchunk, sel_idx, sel_val,   \
-                       row_max, row_cnt, idx_out, row_flag, (const T*)q, (const T*)k, scores,      \
-                       s_stride, scale)
+    hipLaunchKernelGGL((select_union<T, D, KPT>), dim3((unsigned)rows), dim3(kUnionThreads),       \
+                       (unsigned)lds_for(KPT), st, tm.cand, tm.meta, lens, h_q, h_k, N, S_max,     \
+                       nchunk, nst_for(KPT), sel_idx, sel_val, row_max, row_cnt, idx_out, row_flag, \
+                       (const T*)q, (const T*)k, scores, s_stride, scale)
 #define SAGA_SU_K(T, D)                                                                          \
     if (slots <= 8) SAGA_SU(T, D, 8);                                                            \
     else if (slots <= 16) SAGA_SU(T, D, 16);                                                     \

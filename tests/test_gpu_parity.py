@@ -119,6 +119,23 @@ def test_select_multi_tile_rows(h_q):
     _run_decode(x, to_device(x), case, 700, all_pairs(1, h_q), "multi-tile")
 
 
+def test_union_rows_routed_to_the_general_code():
+    # q = 0: every logit ties, each chunk list holds all 1024 keys, longer than
+    # the union selector's register runs -> general code; the first N positions
+    # win the ties
+    case = synth.small_case(B=1, h_q=4, h_k=1, h_v=2, d=64, S_max=5000, N=1000, dtype="bf16",
+                            seed=59)
+    x = synth.make_inputs(case)
+    x["q"][:] = 0
+    g_idx, _ = _run_decode(x, to_device(x), case, 1000, all_pairs(1, 4), "q=0 long")
+    assert all(list(g_idx[r]) == list(range(1000)) for r in range(4))
+    # more than 256 chunks in a row -> general code
+    case = synth.small_case(B=1, h_q=4, h_k=1, h_v=2, d=64, S_max=263000, N=512, dtype="bf16",
+                            seed=61)
+    x = synth.make_inputs(case)
+    _run_decode(x, to_device(x), case, 512, all_pairs(1, 4), "257 chunks")
+
+
 def test_ragged_edge_lengths_and_nan_tail():
     case = synth.small_case(B=10, h_q=4, h_k=1, h_v=2, d=64, S_max=1030, N=16, dtype="bf16",
                             seed=47)
