@@ -110,14 +110,21 @@ saga_status saga_decode_attn_timed(const void* q, const void* k_cache, const voi
                                    void* workspace, size_t workspace_bytes, int32_t* idx_out,
                                    hipEvent_t* events, int n_events);
 
-/* Bytes of device workspace saga_dense_attn needs (host only; 0 on invalid arguments). */
+/*
+ * Bytes of device workspace saga_dense_attn needs (host only; 0 on invalid
+ * arguments): one (max logit, weight sum, weighted value sum[d]) fp32 partial
+ * per (b, query head) and chunk of 512 cached positions (256 when
+ * h_q / h_k > 16); logits never go to memory.
+ */
 size_t saga_dense_workspace_size(int B, int h_q, int h_k, int h_v, int d, int64_t S_max,
                                  saga_dtype dtype);
 
 /*
  * Full (dense) decode attention over all L_b cached positions (§2.1 Eqs. 2-4,
  * §2.2 Eq. 5): the GQA baseline when h_k == h_v and "SAGA full" when h_k < h_v
- * (§5.1). Arguments as for saga_decode_attn, without N and idx_out.
+ * (§5.1). Arguments as for saga_decode_attn, without N and idx_out. Two
+ * kernels on `stream`: the fused per-chunk pass (K rows, softmax, V rows)
+ * and the log-sum-exp merge of the chunks. A row with L_b = 0 gets out = 0.
  */
 saga_status saga_dense_attn(const void* q, const void* k_cache, const void* v_cache,
                             const int32_t* seq_lens, float* out,

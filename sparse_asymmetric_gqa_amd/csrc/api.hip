@@ -2,7 +2,7 @@
 //
 // saga_decode_attn enqueues, on the caller's stream and without allocating:
 //   K-scan (logits, Eq. 2) -> top-N select (Eq. 6) -> sparse PV (Eq. 7).
-// saga_dense_attn enqueues K-scan -> dense PV splits -> merge (Eqs. 2-4).
+// saga_dense_attn enqueues the fused dense pass -> chunk merge (Eqs. 2-4).
 #include "saga.h"
 #include "saga_internal.h"
 
@@ -14,7 +14,8 @@ namespace saga {
 
 static size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
-Workspace carve(void* base, int B, int h_q, int d, int N, int64_t S_max, bool dense) {
+Workspace carve(void* base, int B, int h_q, int h_k, int d, int N, int64_t S_max,
+                bool dense) {
     Workspace w{};
     char* p = static_cast<char*>(base);
     size_t off = 0;
@@ -24,9 +25,9 @@ Workspace carve(void* base, int B, int h_q, int d, int N, int64_t S_max, bool de
         off += align256(bytes);
         return r;
     };
-    w.scores = reinterpret_cast<float*>(take(rows * (size_t)score_stride(S_max) * sizeof(float)));
-    int nsplit;
     if (!dense) {
+        w.scores = reinterpret_cast<float*>(
+            take(rows * (size_t)score_stride(S_max) * sizeof(float)));
         const size_t nch = (size_t)num_chunks(S_max);
         w.cand = reinterpret_cast<uint2*>(take(rows * nch * kScanChunk * sizeof(uint2)));
         w.cand_meta = reinterpret_cast<uint4*>(take(rows * nch * sizeof(uint4)));
@@ -35,13 +36,10 @@ Workspace carve(void* base, int B, int h_q, int d, int N, int64_t S_max, bool de
         w.sel_val = reinterpret_cast<float*>(take(rows * (size_t)N * sizeof(float)));
         w.row_max = reinterpret_cast<float*>(take(rows * sizeof(float)));
         w.row_cnt = reinterpret_cast<int32_t*>(take(rows * sizeof(int32_t)));
-        nsplit = 0;   // the sparse value gather writes out directly
     } else {
-        nsplit = dense_nsplit(S_max);
+        const size_t nsplit = (size_t)dense_nsplit(S_max, h_q / h_k);
+        w.part = reinterpret_cast<float*>(take(rows * nsplit * (size_t)(d + 2) * sizeof(float)));
     }
-    w.part = nsplit ? reinterpret_cast<float*>(
-                          take(rows * (size_t)nsplit * (size_t)(d + 2) * sizeof(float)))
-                    : nullptr;
     w.bytes = off;
     return w;
 }
@@ -91,13 +89,13 @@ extern "C" {
 size_t saga_workspace_size(int B, int h_q, int h_k, int h_v, int d, int N, int64_t S_max,
                            saga_dtype dtype) {
     if (check_shape(B, h_q, h_k, h_v, d, S_max, dtype) != SAGA_OK || N < 1) return 0;
-    return saga::carve(nullptr, B, h_q, d, N, S_max, false).bytes;
+    return saga::carve(nullptr, B, h_q, h_k, d, N, S_max, false).bytes;
 }
 
 size_t saga_dense_workspace_size(int B, int h_q, int h_k, int h_v, int d, int64_t S_max,
                                  saga_dtype dtype) {
     if (check_shape(B, h_q, h_k, h_v, d, S_max, dtype) != SAGA_OK) return 0;
-    return saga::carve(nullptr, B, h_q, d, 1, S_max, true).bytes;
+    return saga::carve(nullptr, B, h_q, h_k, d, 1, S_max, true).bytes;
 }
 
 }  // extern "C"
@@ -123,10 +121,10 @@ saga_status decode(const void* q, const void* k_cache, const void* v_cache,
     if (s != SAGA_OK) return s;
     if (N < 1) return SAGA_ERR_INVALID_ARG;
     if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache)) return SAGA_ERR_INVALID_ARG;
-    const saga::Workspace need = saga::carve(nullptr, B, h_q, d, N, S_max, false);
+    const saga::Workspace need = saga::carve(nullptr, B, h_q, h_k, d, N, S_max, false);
     if (!workspace || workspace_bytes < need.bytes || (reinterpret_cast<uintptr_t>(workspace) & 255u))
         return SAGA_ERR_WORKSPACE;
-    const saga::Workspace w = saga::carve(workspace, B, h_q, d, N, S_max, false);
+    const saga::Workspace w = saga::carve(workspace, B, h_q, h_k, d, N, S_max, false);
     const bool bf16 = dtype == SAGA_BF16;
     const int64_t ss = saga::score_stride(S_max);
 
@@ -195,22 +193,16 @@ saga_status saga_dense_attn(const void* q, const void* k_cache, const void* v_ca
     saga_status s = check_shape(B, h_q, h_k, h_v, d, S_max, dtype);
     if (s != SAGA_OK) return s;
     if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache)) return SAGA_ERR_INVALID_ARG;
-    const saga::Workspace need = saga::carve(nullptr, B, h_q, d, 1, S_max, true);
+    const saga::Workspace need = saga::carve(nullptr, B, h_q, h_k, d, 1, S_max, true);
     if (!workspace || workspace_bytes < need.bytes || (reinterpret_cast<uintptr_t>(workspace) & 255u))
         return SAGA_ERR_WORKSPACE;
-    const saga::Workspace w = saga::carve(workspace, B, h_q, d, 1, S_max, true);
+    const saga::Workspace w = saga::carve(workspace, B, h_q, h_k, d, 1, S_max, true);
     const bool bf16 = dtype == SAGA_BF16;
-    const int64_t ss = saga::score_stride(S_max);
 
     clear_stale_error();
-    s = from_hip(saga::launch_kscan(q, k_cache, seq_lens, w.scores, ss, B, h_q, h_k, d, S_max,
-                                    bf16, stream), "kscan");
-    if (s != SAGA_OK) return s;
-    s = from_hip(saga::launch_pv_dense(v_cache, w.scores, ss, seq_lens, w.part, B, h_q, h_v, d,
-                                       S_max, bf16, stream), "pv_dense");
-    if (s != SAGA_OK) return s;
-    return from_hip(saga::launch_merge(w.part, saga::dense_nsplit(S_max), saga::kDenseRows,
-                                       nullptr, seq_lens, S_max, out, B, h_q, d, stream), "merge");
+    return from_hip(saga::launch_dense_attn(q, k_cache, v_cache, seq_lens, w.part, out, B, h_q,
+                                            h_k, h_v, d, S_max, bf16, stream),
+                    "dense_attn");
 }
 
 saga_status saga_debug_scores(const void* q, const void* k_cache, const int32_t* seq_lens,
@@ -232,14 +224,15 @@ saga_status saga_debug_fallback_rows(const void* workspace, size_t workspace_byt
     saga_status s = check_shape(B, h_q, h_k, h_v, d, S_max, dtype);
     if (s != SAGA_OK) return s;
     if (N < 1) return SAGA_ERR_INVALID_ARG;
-    const saga::Workspace need = saga::carve(nullptr, B, h_q, d, N, S_max, false);
+    const saga::Workspace need = saga::carve(nullptr, B, h_q, h_k, d, N, S_max, false);
     if (workspace_bytes < need.bytes) return SAGA_ERR_WORKSPACE;
     const size_t rows = (size_t)B * (size_t)h_q;
     if (!saga::use_union_path(h_q, h_k, S_max)) {
         for (size_t r = 0; r < rows; ++r) host_flags[r] = 0;
         return SAGA_OK;
     }
-    const saga::Workspace w = saga::carve(const_cast<void*>(workspace), B, h_q, d, N, S_max, false);
+    const saga::Workspace w =
+        saga::carve(const_cast<void*>(workspace), B, h_q, h_k, d, N, S_max, false);
     clear_stale_error();
     if (hipMemcpyAsync(host_flags, w.row_flag, rows * sizeof(int32_t), hipMemcpyDeviceToHost,
                        stream) != hipSuccess ||

@@ -1,0 +1,365 @@
+// Dense attention over every cached position: the full-attention baseline
+// that top-N attention is measured against ("More Value per Key" §2.1 Eqs.
+// 2-4; §3.2 and Table 5 compare GQA and SAGA with and without top-N).
+//
+// One fused pass per (b, key head, chunk of C positions) work item, one
+// workgroup each:
+//   1. K stream: the item's logits for the g query heads of the key head, on
+//      the matrix cores (the K-scan's streaming waves), into LDS only;
+//   2. per head: m = largest logit of the chunk, p = exp(s - m) in place,
+//      l = sum of p;
+//   3. V stream: for every value head the group's query heads use (one for
+//      GQA, h_v / h_k for SAGA), acc[d] = sum_t p_t V[t][d] in fp32 on the
+//      vector ALUs, up to 8 query heads per pass over the rows;
+//   4. the partial (m, l, acc[d]) of each head and chunk goes to the
+//      workspace.
+// A log-sum-exp merge over the chunks then gives out = sum acc e^(m - M) /
+// sum l e^(m - M). Logits never leave the chip, so the bytes moved are the K
+// and V rows once each, plus the partials (d + 2 floats per head and chunk).
+#include "kstream.h"
+
+namespace saga {
+
+namespace {
+
+constexpr int kDenseThreads = 64 * kWaves;
+constexpr int kDenseMaxHeadsPerPass = 8;   // query heads accumulated per pass over V
+
+// positions per work item: the chunk's logits of 16 NHT heads stay in LDS
+__host__ __device__ constexpr int dense_chunk_for(int nht) { return nht == 1 ? 512 : 256; }
+
+template <typename T, int DH>
+constexpr bool dense_xp() { return sizeof(T) == 2; }
+
+// LDS: logits / weights [g][C] floats, then a buffer shared by the K
+// stream's transpose tiles (bf16) and the cross-wave reduction of step 3.
+template <typename T, int DH>
+constexpr size_t dense_aux_bytes() {
+    constexpr size_t red = (size_t)kWaves * kDenseMaxHeadsPerPass * DH * sizeof(float);
+    constexpr size_t xt = dense_xp<T, DH>() ? (size_t)kWaves * 16 * DH * sizeof(T) : 0;
+    return red > xt ? red : xt;
+}
+__host__ __device__ inline size_t dense_logit_bytes(int g, int C) {
+    return ((size_t)g * C * sizeof(float) + 15) & ~(size_t)15;
+}
+
+__device__ inline float wave_fmax(float x) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, 64));
+    return x;
+}
+__device__ inline float wave_fsum(float x) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, 64);
+    return x;
+}
+
+// HP: query heads accumulated per pass over the value rows (a pass may use
+// fewer; the others accumulate unused sums).
+template <typename T, int DH, int NHT, int HP>
+__global__ __launch_bounds__(kDenseThreads) void dense_attn(
+    const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
+    const int32_t* __restrict__ lens, float* __restrict__ part, int h_q, int h_k, int h_v,
+    int64_t S_max, int nchunk, float scale) {
+    constexpr bool XP = dense_xp<T, DH>();
+    using S = Streamer<T, DH, NHT, XP>;
+    constexpr int NS = S::NS;
+    constexpr int C = dense_chunk_for(NHT);
+    constexpr int nst = C / S::STAGE;
+    static_assert(C % S::STAGE == 0 && nst % NS == 0 && nst >= 2 * NS,
+                  "a chunk must span at least two rounds of stages");
+    static_assert(HP >= 1 && HP <= kDenseMaxHeadsPerPass, "heads per pass");
+    extern __shared__ __attribute__((aligned(16))) unsigned char dense_lds[];
+
+    const int g = h_q / h_k;
+    const int item = blockIdx.x;
+    const int bkh = item / nchunk;
+    const int chunk = item - bkh * nchunk;
+    const int b = bkh / h_k;
+    const int kh = bkh - b * h_k;
+    const int64_t L = clamp_len(lens[b], S_max);
+    const int64_t c0 = (int64_t)chunk * C;
+    if (c0 >= L) return;   // uniform: the chunk starts past the row's end
+    const int n = (int)(L - c0 < C ? L - c0 : C);
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    float* sc = reinterpret_cast<float*>(dense_lds);   // [g][C]
+    unsigned char* aux = dense_lds + dense_logit_bytes(g, C);
+
+    // ---- 1. logits of the chunk into LDS (rows past n: -inf, weight 0)
+    {
+        Item<T> it;
+        it.kb = k + ((int64_t)bkh * S_max + c0) * DH;
+        it.n = n;
+        S sm(wave, lane, XP ? reinterpret_cast<u32x4*>(aux) + wave * (S::TILE_BYTES / 16) : nullptr);
+        sm.load_q(q + (int64_t)(b * h_q + kh * g) * DH, g);
+#pragma unroll
+        for (int s = 0; s < NS; ++s) sm.load(s, it, s);
+        auto sink = [&](int ht, int, int off, f32x4 acc) {
+            const int h = ht * 16 + sm.r16;
+            if (h < g) {
+                f32x4 x;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) x[e] = off + e < n ? acc[e] : -__builtin_inff();
+                *reinterpret_cast<f32x4*>(&sc[h * C + off]) = x;
+            }
+        };
+        // loads are unconditional (rows past the chunk clamp to its last row)
+#pragma unroll 1
+        for (int st = 0; st < nst - NS; st += NS)
+#pragma unroll
+            for (int s = 0; s < NS; ++s)
+                sm.consume(s, st + s, scale, sink, [&] { sm.load(s, it, st + s + NS); });
+#pragma unroll
+        for (int s = 0; s < NS; ++s) sm.consume(s, nst - NS + s, scale, sink, [] {});
+    }
+    __syncthreads();
+
+    // ---- value-row geometry of step 3. The passes are (value head, group of
+    // <= HP of its query heads); each pass walks the chunk's rows in batches
+    // of UNR row steps. Batches are double-buffered across passes: batch f+1
+    // is requested before batch f is used, and the first batch before step 2.
+    using R = Row16<T>;
+    constexpr int EPL = R::EPL;            // values per lane per row
+    constexpr int LPR = DH / EPL;          // lanes per row
+    constexpr int RPI = 64 / LPR;          // rows per wave instruction
+    constexpr int STEP = kWaves * RPI;
+    constexpr int UNR = 4;
+    constexpr int BATCH = STEP * UNR;
+    const int rg = lane / LPR;
+    const int sub = lane - rg * LPR;
+    const int first = wave * RPI + rg;
+    const int g_v = h_q / h_v;
+    const int i0 = kh * g;                 // first query head of the key head
+    const int vlo = i0 / g_v;
+    const int ng = (g_v + HP - 1) / HP;    // head groups per value head
+    const int np = ((i0 + g - 1) / g_v - vlo + 1) * ng;
+    const int nb = (n + BATCH - 1) / BATCH;
+    const int nbt = np * nb;
+    const T* vbase = v + ((int64_t)b * h_v * S_max + c0) * DH + sub * EPL;
+    // rows of batch f (clamped: past the chunk, or past the last batch, the
+    // loads re-read a live row and are never used)
+    auto issue = [&](u32x4 (&dst)[UNR], int f) {
+        f = f < nbt ? f : nbt - 1;
+        const int vh = vlo + (f / nb) / ng;
+        const int r0 = (f % nb) * BATCH;
+        const T* vb = vbase + (int64_t)vh * S_max * DH;
+#pragma unroll
+        for (int j = 0; j < UNR; ++j) {
+            int r = r0 + first + j * STEP;
+            r = r < n ? r : n - 1;
+            dst[j] = load_stream(reinterpret_cast<const u32x4*>(vb + (int64_t)r * DH));
+        }
+    };
+    u32x4 ra[UNR], rb[UNR];
+    issue(ra, 0);
+
+    // ---- 2. softmax statistics of the chunk, per query head
+    const int64_t rec_stride = (int64_t)nchunk * (DH + 2);   // next head's record
+    float* rec0 = part + ((int64_t)(b * h_q + kh * g) * nchunk + chunk) * (DH + 2);
+    for (int u = wave; u < g; u += kWaves) {
+        float* s = sc + u * C;
+        float mx = -__builtin_inff();
+#pragma unroll
+        for (int t = lane; t < C; t += 64) mx = fmaxf(mx, s[t]);
+        mx = wave_fmax(mx);   // finite: row 0 of the chunk is live
+        float l = 0.f;
+#pragma unroll
+        for (int t = lane; t < C; t += 64) {
+            const float p = __expf(s[t] - mx);
+            s[t] = p;
+            l += p;
+        }
+        l = wave_fsum(l);
+        if (lane == 0) {
+            rec0[u * rec_stride] = mx;
+            rec0[u * rec_stride + 1] = l;
+        }
+    }
+    __syncthreads();
+
+    // ---- 3. weighted sums of the value rows
+    float* red = reinterpret_cast<float*>(aux);   // [kWaves][HP][DH]
+    float acc[HP][EPL];
+#pragma unroll
+    for (int u = 0; u < HP; ++u)
+#pragma unroll
+        for (int c = 0; c < EPL; ++c) acc[u][c] = 0.f;
+    // batch f: accumulate its rows; after a pass's last batch, reduce over the
+    // row groups and the waves and write the pass's partial sums
+    auto use = [&](const u32x4 (&raw)[UNR], int f) {
+        const int pi = f / nb;
+        const int kb = f - pi * nb;
+        const int vh = vlo + pi / ng;
+        const int ulo = (vh * g_v > i0 ? vh * g_v : i0) - i0;
+        const int uhi = ((vh + 1) * g_v < i0 + g ? (vh + 1) * g_v : i0 + g) - i0;
+        const int u0 = ulo + (pi % ng) * HP;
+        const int nh = uhi - u0 < HP ? uhi - u0 : HP;   // <= 0: an empty group
+        const int r0 = kb * BATCH;
+        // weights of the batch's rows (rows past n hold 0), all read before
+        // any is used; heads past the pass's last read a valid row of the
+        // logit array and accumulate sums that are never written
+        float wv[UNR][HP];
+#pragma unroll
+        for (int u = 0; u < HP; ++u) {
+            const int hu = u0 + u < g - 1 ? u0 + u : g - 1;
+            const float* pw = sc + hu * C + r0 + first;
+#pragma unroll
+            for (int j = 0; j < UNR; ++j) wv[j][u] = pw[j * STEP];
+        }
+#pragma unroll
+        for (int j = 0; j < UNR; ++j) {
+            float fv[EPL];
+            R::cvt(raw[j], fv);
+#pragma unroll
+            for (int u = 0; u < HP; ++u)
+#pragma unroll
+                for (int c = 0; c < EPL; ++c) acc[u][c] += wv[j][u] * fv[c];
+        }
+        if (kb == nb - 1) {   // uniform: the pass is complete
+#pragma unroll
+            for (int o = LPR; o < 64; o <<= 1)
+#pragma unroll
+                for (int u = 0; u < HP; ++u)
+#pragma unroll
+                    for (int c = 0; c < EPL; ++c) acc[u][c] += __shfl_xor(acc[u][c], o, 64);
+            if (rg == 0)
+#pragma unroll
+                for (int u = 0; u < HP; ++u)
+#pragma unroll
+                    for (int c = 0; c < EPL; ++c)
+                        red[(wave * HP + u) * DH + sub * EPL + c] = acc[u][c];
+#pragma unroll
+            for (int u = 0; u < HP; ++u)
+#pragma unroll
+                for (int c = 0; c < EPL; ++c) acc[u][c] = 0.f;
+            __syncthreads();
+            for (int x = tid; x < nh * DH; x += kDenseThreads) {
+                const int u = x / DH;
+                const int c = x - u * DH;
+                float sum = 0.f;
+#pragma unroll
+                for (int w = 0; w < kWaves; ++w) sum += red[(w * HP + u) * DH + c];
+                rec0[(u0 + u) * rec_stride + 2 + c] = sum;
+            }
+            __syncthreads();   // red is rewritten by the next pass
+        }
+    };
+#pragma unroll 1
+    for (int f = 0; f < nbt; f += 2) {
+        issue(rb, f + 1);
+        use(ra, f);
+        issue(ra, f + 2);
+        if (f + 1 < nbt) use(rb, f + 1);   // uniform
+    }
+}
+
+// out[row] = sum_s acc_s e^(m_s - M) / sum_s l_s e^(m_s - M) over the live
+// chunks s of the row (every live chunk has l >= 1: its largest logit has
+// weight 1); a row with no live chunk (L_b = 0) gets 0.
+template <int DH>
+__global__ __launch_bounds__(DH) void dense_merge(const float* __restrict__ part, int nchunk,
+                                                 int C, const int32_t* __restrict__ lens,
+                                                 int64_t S_max, float* __restrict__ out,
+                                                 int h_q) {
+    const int row = blockIdx.x;
+    const int c = threadIdx.x;
+    const int64_t L = clamp_len(lens[row / h_q], S_max);
+    const int64_t live = (L + C - 1) / C;
+    const int ns = (int)(live < nchunk ? live : nchunk);
+    const float* p = part + (int64_t)row * nchunk * (DH + 2);
+    float M = -__builtin_inff();
+#pragma unroll 8
+    for (int s = 0; s < ns; ++s) M = fmaxf(M, p[s * (DH + 2)]);
+    float num = 0.f, den = 0.f;
+#pragma unroll 8
+    for (int s = 0; s < ns; ++s) {
+        const float* r = p + s * (DH + 2);
+        const float f = __expf(r[0] - M);
+        den += r[1] * f;
+        num += r[2 + c] * f;
+    }
+    out[(int64_t)row * DH + c] = den > 0.f ? num / den : 0.f;
+}
+
+template <typename T, int DH, int NHT, int HP>
+hipError_t go_dense(const void* q, const void* k, const void* v, const int32_t* lens, float* part,
+                    int B, int h_q, int h_k, int h_v, int64_t S_max, hipStream_t st) {
+    constexpr int C = dense_chunk_for(NHT);
+    const int g = h_q / h_k;
+    const int nchunk = dense_nsplit(S_max, g);
+    const size_t lds = dense_logit_bytes(g, C) + dense_aux_bytes<T, DH>();
+    static_assert(16 * NHT * C * sizeof(float) + dense_aux_bytes<T, DH>() <= 160 * 1024,
+                  "logits of 16 NHT heads must fit the LDS");
+    auto kern = &dense_attn<T, DH, NHT, HP>;
+    if (lds > 64 * 1024) {
+        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                                 hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                 (int)lds);
+        if (e != hipSuccess) return e;
+    }
+    const int64_t nwork = (int64_t)B * h_k * nchunk;
+    const float scale = (float)(1.0 / __builtin_sqrt((double)DH));
+    hipLaunchKernelGGL(kern, dim3((unsigned)nwork), dim3(kDenseThreads), lds, st, (const T*)q,
+                       (const T*)k, (const T*)v, lens, part, h_q, h_k, h_v, S_max, nchunk, scale);
+    return hipGetLastError();
+}
+
+// heads per pass: g_v rounded up to an even count (at most 8) for bf16; the
+// fp32 path (small shapes) always takes 8
+template <typename T, int DH, int NHT>
+hipError_t go_dense_hp(const void* q, const void* k, const void* v, const int32_t* lens,
+                       float* part, int B, int h_q, int h_k, int h_v, int64_t S_max,
+                       hipStream_t st) {
+    const int g_v = h_q / h_v;
+    if (sizeof(T) == 2) {
+        if (g_v <= 2) return go_dense<T, DH, NHT, 2>(q, k, v, lens, part, B, h_q, h_k, h_v, S_max, st);
+        if (g_v <= 4) return go_dense<T, DH, NHT, 4>(q, k, v, lens, part, B, h_q, h_k, h_v, S_max, st);
+        if (g_v <= 6) return go_dense<T, DH, NHT, 6>(q, k, v, lens, part, B, h_q, h_k, h_v, S_max, st);
+    }
+    return go_dense<T, DH, NHT, 8>(q, k, v, lens, part, B, h_q, h_k, h_v, S_max, st);
+}
+
+template <typename T, int DH>
+hipError_t go_dense_g(const void* q, const void* k, const void* v, const int32_t* lens,
+                      float* part, int B, int h_q, int h_k, int h_v, int64_t S_max,
+                      hipStream_t st) {
+    const int g = h_q / h_k;
+    if (g <= 16) return go_dense_hp<T, DH, 1>(q, k, v, lens, part, B, h_q, h_k, h_v, S_max, st);
+    if (g <= 32) return go_dense_hp<T, DH, 2>(q, k, v, lens, part, B, h_q, h_k, h_v, S_max, st);
+    return go_dense_hp<T, DH, 4>(q, k, v, lens, part, B, h_q, h_k, h_v, S_max, st);
+}
+
+}  // namespace
+
+int dense_chunk(int g) { return dense_chunk_for(g <= 16 ? 1 : g <= 32 ? 2 : 4); }
+int dense_nsplit(int64_t S_max, int g) {
+    const int C = dense_chunk(g);
+    return (int)((S_max + C - 1) / C);
+}
+
+hipError_t launch_dense_attn(const void* q, const void* k, const void* v, const int32_t* lens,
+                             float* part, float* out, int B, int h_q, int h_k, int h_v, int d,
+                             int64_t S_max, bool bf16, hipStream_t st) {
+    hipError_t e;
+    if (bf16)
+        e = d == 64 ? go_dense_g<uint16_t, 64>(q, k, v, lens, part, B, h_q, h_k, h_v, S_max, st)
+                    : go_dense_g<uint16_t, 128>(q, k, v, lens, part, B, h_q, h_k, h_v, S_max, st);
+    else
+        e = d == 64 ? go_dense_g<float, 64>(q, k, v, lens, part, B, h_q, h_k, h_v, S_max, st)
+                    : go_dense_g<float, 128>(q, k, v, lens, part, B, h_q, h_k, h_v, S_max, st);
+    if (e != hipSuccess) return e;
+    const int g = h_q / h_k;
+    const int nchunk = dense_nsplit(S_max, g);
+    const int C = dense_chunk(g);
+    if (d == 64)
+        hipLaunchKernelGGL((dense_merge<64>), dim3((unsigned)(B * h_q)), dim3(64), 0, st, part,
+                           nchunk, C, lens, S_max, out, h_q);
+    else
+        hipLaunchKernelGGL((dense_merge<128>), dim3((unsigned)(B * h_q)), dim3(128), 0, st, part,
+                           nchunk, C, lens, S_max, out, h_q);
+    return hipGetLastError();
+}
+
+}  // namespace saga

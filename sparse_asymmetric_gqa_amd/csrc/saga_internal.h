@@ -12,7 +12,6 @@ namespace saga {
 #endif
 constexpr int kScanChunk = SAGA_KSCAN_CHUNK;   // positions per K-scan workgroup
 constexpr int kPvEntries = 256;      // kept entries per sparse PV workgroup
-constexpr int kDenseRows = 512;      // positions per dense PV workgroup
 constexpr int kSelectThreads = 1024; // threads of one select workgroup
 constexpr int kMaxHeadGroup = 64;    // largest h_q / h_k and h_q / h_v supported
 
@@ -22,7 +21,7 @@ inline int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 inline int64_t score_stride(int64_t S_max) { return round_up(S_max, 16); }
 
 struct Workspace {
-    float* scores;      // [B][h_q][score_stride]  dense logits (dense path, fallback rows)
+    float* scores;      // [B][h_q][score_stride]  logits (decode: wide key groups, fallback rows)
     uint2* cand;        // candidate pool: B*h_k*nchunk items x g*kScanChunk entries
     uint4* cand_meta;   // [B][h_q][nchunk]  {pool offset lo, count, cutoff, pool offset hi}
     int32_t* row_flag;  // [B][h_q]   1 if the row took the dense fallback in the last call
@@ -30,7 +29,7 @@ struct Workspace {
     float* sel_val;     // [B][h_q][N]
     float* row_max;     // [B][h_q]   largest kept logit
     int32_t* row_cnt;   // [B][h_q]   N_eff
-    float* part;        // [B][h_q][nsplit][d + 2]  (m, l, acc[d])
+    float* part;        // dense: [B][h_q][nchunk][d + 2]  (m, l, acc[d]) per chunk
     size_t bytes;
 };
 
@@ -42,11 +41,12 @@ int max_union_chunks();
 
 // Carve the decode workspace (dense == false) or the dense one out of `base`
 // (base may be null to only compute the size).
-Workspace carve(void* base, int B, int h_q, int d, int N, int64_t S_max, bool dense);
+Workspace carve(void* base, int B, int h_q, int h_k, int d, int N, int64_t S_max, bool dense);
 
-// number of partial-sum splits per (b, i) row
-int sparse_nsplit(int N);          // ceil(N / kPvEntries)
-int dense_nsplit(int64_t S_max);   // ceil(S_max / kDenseRows)
+// Dense attention: positions per work item for a key group of g query heads,
+// and chunks (partials) per (b, i) row.
+int dense_chunk(int g);
+int dense_nsplit(int64_t S_max, int g);   // ceil(S_max / dense_chunk(g))
 
 // Candidate lists published by the top-M K-scan. The workgroup that takes
 // work items [w0, w1) packs the lists of their heads, in any order, from pool
@@ -87,16 +87,12 @@ hipError_t launch_pv_sparse(const void* v, const int32_t* sel_idx, const float* 
                             int h_q, int h_v, int d, int N, int64_t S_max, bool bf16,
                             hipStream_t st);
 
-hipError_t launch_pv_dense(const void* v, const float* scores, int64_t s_stride,
-                           const int32_t* lens, float* part, int B, int h_q, int h_v, int d,
-                           int64_t S_max, bool bf16, hipStream_t st);
-
-// Log-sum-exp merge of the split partials into out[B][h_q][d]. Split s of row
-// (b, i) is live when s * unit < count, count = row_cnt[b*h_q+i] if row_cnt is
-// given, else lens[b] clamped to [0, S_max].
-hipError_t launch_merge(const float* part, int nsplit, int unit, const int32_t* row_cnt,
-                        const int32_t* lens, int64_t S_max, float* out, int B, int h_q, int d,
-                        hipStream_t st);
+// Dense attention (every position, Eqs. 2-4): fused K stream, chunk softmax
+// and V stream into part [B][h_q][nchunk][d + 2], then the log-sum-exp merge
+// of the chunks into out[B][h_q][d].
+hipError_t launch_dense_attn(const void* q, const void* k, const void* v, const int32_t* lens,
+                             float* part, float* out, int B, int h_q, int h_k, int h_v, int d,
+                             int64_t S_max, bool bf16, hipStream_t st);
 
 }  // namespace saga
 
@@ -164,6 +160,27 @@ __device__ inline uint32_t wave_sum(uint32_t v) {
     return (uint32_t)__builtin_amdgcn_readlane(x, 15) + (uint32_t)__builtin_amdgcn_readlane(x, 31) +
            (uint32_t)__builtin_amdgcn_readlane(x, 47) + (uint32_t)__builtin_amdgcn_readlane(x, 63);
 }
+
+
+// 16 bytes of a value row -> EPL fp32 values
+template <typename T> struct Row16;
+template <> struct Row16<uint16_t> {
+    static constexpr int EPL = 8;
+    __device__ static inline void cvt(const u32x4& r, float* f) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            f[2 * c] = __uint_as_float(r[c] << 16);
+            f[2 * c + 1] = __uint_as_float(r[c] & 0xFFFF0000u);
+        }
+    }
+};
+template <> struct Row16<float> {
+    static constexpr int EPL = 4;
+    __device__ static inline void cvt(const u32x4& r, float* f) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) f[c] = __uint_as_float(r[c]);
+    }
+};
 
 }  // namespace dev
 }  // namespace saga

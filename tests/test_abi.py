@@ -105,7 +105,11 @@ def test_workspace_sizes():
         assert ws(B, h_q, args[2], args[3], d, N + 300, S, 1) >= n
         assert ws(B, h_q, args[2], args[3], d, N, S + 5000, 1) >= n
     dw = saga.saga_dense_workspace_size
-    assert dw(64, 12, 2, 2, 128, 32768, 1) >= 64 * 12 * 32768 * 4
+    # one (m, l, acc[d]) partial per row and chunk of 512 positions (key groups
+    # of up to 16 heads) or 256 positions (wider key groups)
+    assert dw(64, 12, 2, 2, 128, 32768, 1) >= 64 * 12 * 64 * 130 * 4
+    assert dw(1, 64, 1, 2, 64, 1000, 1) >= 64 * 4 * 66 * 4
+    assert dw(1, 4, 1, 2, 64, 1025, 0) >= dw(1, 4, 1, 2, 64, 1000, 0)
     assert dw(1, 4, 1, 2, 72, 10, 1) == 0
 
 

@@ -85,6 +85,37 @@ def test_dense_baselines(name):
         torch.cuda.empty_cache()
 
 
+DENSE_SMALL = [
+    # (B, h_q, h_k, h_v, d, S_max, dtype, lens)
+    (3, 6, 2, 3, 64, 700, "bf16", [700, 513, 1]),       # a value head spans two key heads
+    (2, 12, 1, 2, 128, 1300, "bf16", [1300, 511]),      # SAGA (1, 2), partial chunks
+    (2, 8, 4, 4, 128, 300, "f32", [300, 17]),           # GQA, fp32, rows shorter than a chunk
+    (1, 32, 1, 4, 64, 900, "bf16", [900]),              # key group of 32 (256-position chunks)
+    (1, 64, 1, 2, 128, 600, "f32", [600]),              # key group of 64, value group of 32
+    (2, 16, 1, 8, 64, 1024, "bf16", [1024, 0]),         # empty row -> 0
+]
+
+
+@pytest.mark.parametrize("shape", DENSE_SMALL)
+def test_dense_small_shapes(shape):
+    B, h_q, h_k, h_v, d, S, dt, lens = shape
+    case = synth.small_case(B=B, h_q=h_q, h_k=h_k, h_v=h_v, d=d, S_max=S, N=1, dtype=dt, seed=67)
+    lens = np.array(lens, np.int32)
+    x = synth.make_inputs(case, np.maximum(lens, 1))
+    x["seq_lens"] = lens
+    _say(f"[dense] small {shape}")
+    dx = to_device(x)
+    out = saga.dense_attn(dx["q"], dx["k"], dx["v"], dx["seq_lens"]).reshape(-1, d).cpu().numpy()
+    live = [(b, i) for b in range(B) for i in range(h_q) if lens[b] > 0]
+    ref, _ = oracle.dense_attn(x["q"], x["k"], x["v"], np.maximum(lens, 1), pairs=live)
+    err = np.abs(out[[b * h_q + i for b, i in live]] - ref).max()
+    _say(f"    max|err|={err:.2e}")
+    assert err <= tol_for(dt)
+    for b in range(B):
+        if lens[b] == 0:
+            assert not out[b * h_q:(b + 1) * h_q].any()
+
+
 SMALL = [
     # (B, h_q, h_k, h_v, d, S_max, N, dtype, ragged)
     (2, 8, 2, 4, 64, 1030, 100, "bf16", True),
