@@ -9,8 +9,12 @@
 //   2. per head: m = largest logit of the chunk, p = exp(s - m) in place,
 //      l = sum of p;
 //   3. V stream: for every value head the group's query heads use (one for
-//      GQA, h_v / h_k for SAGA), acc[d] = sum_t p_t V[t][d] in fp32 on the
-//      vector ALUs, up to 8 query heads per pass over the rows;
+//      GQA, h_v / h_k for SAGA), acc[d] = sum_t p_t V[t][d], up to 8 query
+//      heads per pass over the rows. bf16: on the matrix cores, P (heads x
+//      positions, as bf16 hi + lo parts, so the weights keep ~16 bits) times
+//      V (positions x d); the V operand needs positions contiguous per lane,
+//      so each wave stages 32-row tiles of V in LDS and reads them back with
+//      the gfx950 transposing LDS read. fp32: fp32 FMAs on the vector ALUs;
 //   4. the partial (m, l, acc[d]) of each head and chunk goes to the
 //      workspace.
 // A log-sum-exp merge over the chunks then gives out = sum acc e^(m - M) /
@@ -37,11 +41,48 @@ template <typename T, int DH>
 constexpr size_t dense_aux_bytes() {
     constexpr size_t red = (size_t)kWaves * kDenseMaxHeadsPerPass * DH * sizeof(float);
     constexpr size_t xt = dense_xp<T, DH>() ? (size_t)kWaves * 16 * DH * sizeof(T) : 0;
-    return red > xt ? red : xt;
+    constexpr size_t vt = sizeof(T) == 2 ? (size_t)kWaves * 32 * 128 : 0;   // V tiles
+    constexpr size_t m = red > xt ? red : xt;
+    return m > vt ? m : vt;
 }
+// Logit rows are padded to C + 32 floats: after the softmax, a head's bf16
+// weight rows (hi and lo parts, C + 32 entries each) take exactly the bytes
+// of its own logit row, and rows of neighbouring heads start in different
+// LDS banks.
+__host__ __device__ constexpr int dense_row_stride(int C) { return C + 32; }
 __host__ __device__ inline size_t dense_logit_bytes(int g, int C) {
-    return ((size_t)g * C * sizeof(float) + 15) & ~(size_t)15;
+    return (size_t)g * dense_row_stride(C) * sizeof(float);
 }
+
+// bf16 round-to-nearest-even of a finite float
+__device__ inline uint32_t bf16_rne(float x) {
+    const uint32_t u = __float_as_uint(x);
+    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+typedef short v4s __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4s lds_v4s;
+
+// Step 3 on the matrix cores (bf16 V). Weights are in LDS as bf16 rows
+// whi / wlo = base + h * (row_bytes) [+ lo_off], positions contiguous. Wave
+// `wave` takes the 32-row blocks kb = wave, wave + 4, ... of the chunk; per
+// block the 4 or 8 row-coalesced 16-byte loads per lane (32 rows x DH) go
+// through the wave's 4 KB LDS tile one 128-byte half-row at a time. In the
+// tile, row r (128 bytes) keeps 32-byte block c at (c ^ sw(r)) * 32 with
+// sw(r) = ((r >> 1) ^ (r >> 3)) & 3, so the row-wise writes and the
+// transposing reads (16 lanes: 4 rows x 32 bytes) spread over the banks. The
+// transposing read hands lane i of a 16-lane group element i % 4 of the
+// 8-byte pieces addressed by lanes i / 4 + 4 j: with lane a + 4 j addressing
+// row j, columns 4 a .. 4 a + 3 of a 16-column block, lane i receives that
+// block's column i for 4 consecutive rows -- the MFMA B operand layout
+// (lane l: positions 8 (l / 16) .. + 7 of column l % 16) after two reads.
+template <int DH>
+struct PvTile {
+    static constexpr int NHALF = DH / 64;   // 128-byte halves of a bf16 row
+    static constexpr int NT = DH / 16;      // 16-column output tiles
+    static __device__ inline int sw(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
+};
+
 
 __device__ inline float wave_fmax(float x) {
 #pragma unroll
@@ -54,9 +95,7 @@ __device__ inline float wave_fsum(float x) {
     return x;
 }
 
-// HP: query heads accumulated per pass over the value rows (a pass may use
-// fewer; the others accumulate unused sums).
-template <typename T, int DH, int NHT, int HP>
+template <typename T, int DH, int NHT>
 __global__ __launch_bounds__(kDenseThreads) void dense_attn(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const int32_t* __restrict__ lens, float* __restrict__ part, int h_q, int h_k, int h_v,
@@ -68,7 +107,6 @@ __global__ __launch_bounds__(kDenseThreads) void dense_attn(
     constexpr int nst = C / S::STAGE;
     static_assert(C % S::STAGE == 0 && nst % NS == 0 && nst >= 2 * NS,
                   "a chunk must span at least two rounds of stages");
-    static_assert(HP >= 1 && HP <= kDenseMaxHeadsPerPass, "heads per pass");
     extern __shared__ __attribute__((aligned(16))) unsigned char dense_lds[];
 
     const int g = h_q / h_k;
@@ -84,7 +122,8 @@ __global__ __launch_bounds__(kDenseThreads) void dense_attn(
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    float* sc = reinterpret_cast<float*>(dense_lds);   // [g][C]
+    constexpr int SR = dense_row_stride(C);
+    float* sc = reinterpret_cast<float*>(dense_lds);   // [g][SR]
     unsigned char* aux = dense_lds + dense_logit_bytes(g, C);
 
     // ---- 1. logits of the chunk into LDS (rows past n: -inf, weight 0)
@@ -102,7 +141,7 @@ __global__ __launch_bounds__(kDenseThreads) void dense_attn(
                 f32x4 x;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) x[e] = off + e < n ? acc[e] : -__builtin_inff();
-                *reinterpret_cast<f32x4*>(&sc[h * C + off]) = x;
+                *reinterpret_cast<f32x4*>(&sc[h * SR + off]) = x;
             }
         };
         // loads are unconditional (rows past the chunk clamp to its last row)
@@ -116,142 +155,297 @@ __global__ __launch_bounds__(kDenseThreads) void dense_attn(
     }
     __syncthreads();
 
-    // ---- value-row geometry of step 3. The passes are (value head, group of
-    // <= HP of its query heads); each pass walks the chunk's rows in batches
-    // of UNR row steps. Batches are double-buffered across passes: batch f+1
-    // is requested before batch f is used, and the first batch before step 2.
-    using R = Row16<T>;
-    constexpr int EPL = R::EPL;            // values per lane per row
-    constexpr int LPR = DH / EPL;          // lanes per row
-    constexpr int RPI = 64 / LPR;          // rows per wave instruction
-    constexpr int STEP = kWaves * RPI;
-    constexpr int UNR = 4;
-    constexpr int BATCH = STEP * UNR;
-    const int rg = lane / LPR;
-    const int sub = lane - rg * LPR;
-    const int first = wave * RPI + rg;
-    const int g_v = h_q / h_v;
-    const int i0 = kh * g;                 // first query head of the key head
-    const int vlo = i0 / g_v;
-    const int ng = (g_v + HP - 1) / HP;    // head groups per value head
-    const int np = ((i0 + g - 1) / g_v - vlo + 1) * ng;
-    const int nb = (n + BATCH - 1) / BATCH;
-    const int nbt = np * nb;
-    const T* vbase = v + ((int64_t)b * h_v * S_max + c0) * DH + sub * EPL;
-    // rows of batch f (clamped: past the chunk, or past the last batch, the
-    // loads re-read a live row and are never used)
-    auto issue = [&](u32x4 (&dst)[UNR], int f) {
-        f = f < nbt ? f : nbt - 1;
-        const int vh = vlo + (f / nb) / ng;
-        const int r0 = (f % nb) * BATCH;
-        const T* vb = vbase + (int64_t)vh * S_max * DH;
+    if constexpr (sizeof(T) == 2) {
+        // ---- steps 2 and 3 on the matrix cores
+        using PT = PvTile<DH>;
+        constexpr int NHALF = PT::NHALF;
+        constexpr int NT = PT::NT;
+        constexpr int NL = 4 * NHALF;                 // 16-byte loads per lane per block
+        constexpr int HPM = kDenseMaxHeadsPerPass;
+        const int g_v = h_q / h_v;
+        const int i0 = kh * g;                        // first query head of the key head
+        const int vlo = i0 / g_v;
+        const int ng = (g_v + HPM - 1) / HPM;         // head groups per value head
+        const int np = ((i0 + g - 1) / g_v - vlo + 1) * ng;
+        const int nkb = (n + 31) / 32;                // 32-row blocks of the chunk
+        const int nkw = wave < nkb ? (nkb - wave + kWaves - 1) / kWaves : 0;   // this wave's
+        const int total = np * nkw;
+        const int lr = lane >> 3;                     // loads: row 8 v + lr, chunk lc of a half
+        const int lc = lane & 7;
+        const char* vbase = reinterpret_cast<const char*>(v + ((int64_t)b * h_v * S_max + c0) * DH);
+        u32x4 raw[NL];
+        // block f of this wave (pass f / nkw, block wave + 4 (f % nkw)); past
+        // the last one it re-reads that one, and rows past n clamp to n - 1
+        auto issue = [&](int f) {
+            f = f < total ? f : total - 1;
+            const int pi = f / nkw;
+            const int vh = vlo + pi / ng;
+            const int t0 = 32 * (wave + kWaves * (f - pi * nkw));
+            const char* vb = vbase + (int64_t)vh * S_max * DH * 2;
 #pragma unroll
-        for (int j = 0; j < UNR; ++j) {
-            int r = r0 + first + j * STEP;
-            r = r < n ? r : n - 1;
-            dst[j] = load_stream(reinterpret_cast<const u32x4*>(vb + (int64_t)r * DH));
-        }
-    };
-    u32x4 ra[UNR], rb[UNR];
-    issue(ra, 0);
+            for (int hh = 0; hh < NHALF; ++hh)
+#pragma unroll
+                for (int vv = 0; vv < 4; ++vv) {
+                    int r = t0 + 8 * vv + lr;
+                    r = r < n ? r : n - 1;
+                    raw[hh * 4 + vv] = load_stream(reinterpret_cast<const u32x4*>(
+                        vb + (int64_t)r * (DH * 2) + hh * 128 + lc * 16));
+                }
+        };
+        if (total > 0) issue(0);   // uniform over the wave
 
-    // ---- 2. softmax statistics of the chunk, per query head
-    const int64_t rec_stride = (int64_t)nchunk * (DH + 2);   // next head's record
-    float* rec0 = part + ((int64_t)(b * h_q + kh * g) * nchunk + chunk) * (DH + 2);
-    for (int u = wave; u < g; u += kWaves) {
-        float* s = sc + u * C;
-        float mx = -__builtin_inff();
+        // ---- 2. softmax statistics; the weights replace the logits in place
+        // as bf16 rows hi = rne(p), lo = rne(p - hi) (hi at bytes [0, 2 SR)
+        // of the head's row, lo at [2 SR, 4 SR)); a wave owns whole rows
+        const int64_t rec_stride = (int64_t)nchunk * (DH + 2);   // next head's record
+        float* rec0 = part + ((int64_t)(b * h_q + kh * g) * nchunk + chunk) * (DH + 2);
+        constexpr int PR = C / 128;                   // position pairs per lane
+        for (int u = wave; u < g; u += kWaves) {
+            float* srow = sc + u * SR;
+            float2 x[PR];
 #pragma unroll
-        for (int t = lane; t < C; t += 64) mx = fmaxf(mx, s[t]);
-        mx = wave_fmax(mx);   // finite: row 0 of the chunk is live
-        float l = 0.f;
+            for (int j = 0; j < PR; ++j) x[j] = *reinterpret_cast<const float2*>(srow + 128 * j + 2 * lane);
+            float mx = -__builtin_inff();
 #pragma unroll
-        for (int t = lane; t < C; t += 64) {
-            const float p = __expf(s[t] - mx);
-            s[t] = p;
-            l += p;
+            for (int j = 0; j < PR; ++j) mx = fmaxf(mx, fmaxf(x[j].x, x[j].y));
+            mx = wave_fmax(mx);   // finite: row 0 of the chunk is live
+            float l = 0.f;
+            uint32_t whi[PR], wlo[PR];
+#pragma unroll
+            for (int j = 0; j < PR; ++j) {
+                const float p0 = __expf(x[j].x - mx);
+                const float p1 = __expf(x[j].y - mx);
+                l += p0 + p1;
+                const uint32_t h0 = bf16_rne(p0), h1 = bf16_rne(p1);
+                const uint32_t l0 = bf16_rne(p0 - __uint_as_float(h0 << 16));
+                const uint32_t l1 = bf16_rne(p1 - __uint_as_float(h1 << 16));
+                whi[j] = h0 | (h1 << 16);
+                wlo[j] = l0 | (l1 << 16);
+            }
+            l = wave_fsum(l);
+            uint32_t* wrow = reinterpret_cast<uint32_t*>(srow);
+#pragma unroll
+            for (int j = 0; j < PR; ++j) {
+                wrow[64 * j + lane] = whi[j];
+                wrow[SR / 2 + 64 * j + lane] = wlo[j];
+            }
+            if (lane == 0) {
+                rec0[u * rec_stride] = mx;
+                rec0[u * rec_stride + 1] = l;
+            }
         }
-        l = wave_fsum(l);
-        if (lane == 0) {
-            rec0[u * rec_stride] = mx;
-            rec0[u * rec_stride + 1] = l;
-        }
-    }
-    __syncthreads();
+        __syncthreads();
 
-    // ---- 3. weighted sums of the value rows
-    float* red = reinterpret_cast<float*>(aux);   // [kWaves][HP][DH]
-    float acc[HP][EPL];
+        // ---- 3. P (heads x positions) times V (positions x d) per pass
+        unsigned char* tile = aux + wave * 4096;
+        float* red = reinterpret_cast<float*>(aux);   // [kWaves][HPM][DH]
+        const int q4 = lane >> 4;
+        const int i16 = lane & 15;
+        const int ta = i16 & 3;                       // transposing read: row tj, piece ta
+        const int tj = i16 >> 2;
+        int f = 0;
+        for (int pi = 0; pi < np; ++pi) {
+            const int vh = vlo + pi / ng;
+            const int ulo = (vh * g_v > i0 ? vh * g_v : i0) - i0;
+            const int uhi = ((vh + 1) * g_v < i0 + g ? (vh + 1) * g_v : i0 + g) - i0;
+            const int u0 = ulo + (pi % ng) * HPM;
+            const int nh = uhi - u0 < HPM ? uhi - u0 : HPM;   // <= 0: an empty group
+            // A operand rows: heads u0 + lane % 16 (clamped to the array; rows
+            // of other heads produce outputs that are never written)
+            const int hu = u0 + i16 < g - 1 ? u0 + i16 : g - 1;
+            const char* wr = reinterpret_cast<const char*>(sc + hu * SR) + 16 * q4;
+            f32x4 acc[NT];
 #pragma unroll
-    for (int u = 0; u < HP; ++u)
+            for (int nt = 0; nt < NT; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll 1
+            for (int i = 0; i < nkw; ++i, ++f) {
+                const int t0 = 32 * (wave + kWaves * i);
+                const u32x4 ahi = *reinterpret_cast<const u32x4*>(wr + 2 * t0);
+                const u32x4 alo = *reinterpret_cast<const u32x4*>(wr + 2 * SR + 2 * t0);
 #pragma unroll
-        for (int c = 0; c < EPL; ++c) acc[u][c] = 0.f;
-    // batch f: accumulate its rows; after a pass's last batch, reduce over the
-    // row groups and the waves and write the pass's partial sums
-    auto use = [&](const u32x4 (&raw)[UNR], int f) {
-        const int pi = f / nb;
-        const int kb = f - pi * nb;
-        const int vh = vlo + pi / ng;
-        const int ulo = (vh * g_v > i0 ? vh * g_v : i0) - i0;
-        const int uhi = ((vh + 1) * g_v < i0 + g ? (vh + 1) * g_v : i0 + g) - i0;
-        const int u0 = ulo + (pi % ng) * HP;
-        const int nh = uhi - u0 < HP ? uhi - u0 : HP;   // <= 0: an empty group
-        const int r0 = kb * BATCH;
-        // weights of the batch's rows (rows past n hold 0), all read before
-        // any is used; heads past the pass's last read a valid row of the
-        // logit array and accumulate sums that are never written
-        float wv[UNR][HP];
+                for (int hh = 0; hh < NHALF; ++hh) {
 #pragma unroll
-        for (int u = 0; u < HP; ++u) {
-            const int hu = u0 + u < g - 1 ? u0 + u : g - 1;
-            const float* pw = sc + hu * C + r0 + first;
+                    for (int vv = 0; vv < 4; ++vv) {
+                        const int r = 8 * vv + lr;
+                        *reinterpret_cast<u32x4*>(tile + r * 128 + (((lc >> 1) ^ PT::sw(r)) << 5) +
+                                                  ((lc & 1) << 4)) = raw[hh * 4 + vv];
+                    }
+                    if (hh == NHALF - 1) issue(f + 1);   // the registers are free
 #pragma unroll
-            for (int j = 0; j < UNR; ++j) wv[j][u] = pw[j * STEP];
-        }
+                    for (int c = 0; c < 4; ++c) {
+                        u32x4 bop;
 #pragma unroll
-        for (int j = 0; j < UNR; ++j) {
-            float fv[EPL];
-            R::cvt(raw[j], fv);
+                        for (int hr = 0; hr < 2; ++hr) {
+                            const int r = 8 * q4 + 4 * hr + tj;
+                            // generic -> LDS address space (the tile is in LDS)
+                            const v4s t = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                (lds_v4s*)(tile + r * 128 + ((c ^ PT::sw(r)) << 5) + (ta << 3)));
+                            bop[2 * hr] = (uint32_t)(uint16_t)t[0] | ((uint32_t)(uint16_t)t[1] << 16);
+                            bop[2 * hr + 1] = (uint32_t)(uint16_t)t[2] | ((uint32_t)(uint16_t)t[3] << 16);
+                        }
+                        acc[hh * 4 + c] = Mfma<uint16_t>::step(ahi, bop, acc[hh * 4 + c]);
+                        acc[hh * 4 + c] = Mfma<uint16_t>::step(alo, bop, acc[hh * 4 + c]);
+                    }
+                }
+            }
+            // lane: out[head u0 + 4 q4 + e][column 16 nt + i16] of its rows
+            __syncthreads();   // every wave is done with its tile (red overlays them)
 #pragma unroll
-            for (int u = 0; u < HP; ++u)
+            for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-                for (int c = 0; c < EPL; ++c) acc[u][c] += wv[j][u] * fv[c];
-        }
-        if (kb == nb - 1) {   // uniform: the pass is complete
-#pragma unroll
-            for (int o = LPR; o < 64; o <<= 1)
-#pragma unroll
-                for (int u = 0; u < HP; ++u)
-#pragma unroll
-                    for (int c = 0; c < EPL; ++c) acc[u][c] += __shfl_xor(acc[u][c], o, 64);
-            if (rg == 0)
-#pragma unroll
-                for (int u = 0; u < HP; ++u)
-#pragma unroll
-                    for (int c = 0; c < EPL; ++c)
-                        red[(wave * HP + u) * DH + sub * EPL + c] = acc[u][c];
-#pragma unroll
-            for (int u = 0; u < HP; ++u)
-#pragma unroll
-                for (int c = 0; c < EPL; ++c) acc[u][c] = 0.f;
+                for (int e = 0; e < 4; ++e)
+                    if (4 * q4 + e < HPM) red[(wave * HPM + 4 * q4 + e) * DH + 16 * nt + i16] = acc[nt][e];
             __syncthreads();
             for (int x = tid; x < nh * DH; x += kDenseThreads) {
                 const int u = x / DH;
                 const int c = x - u * DH;
                 float sum = 0.f;
 #pragma unroll
-                for (int w = 0; w < kWaves; ++w) sum += red[(w * HP + u) * DH + c];
+                for (int w = 0; w < kWaves; ++w) sum += red[(w * HPM + u) * DH + c];
                 rec0[(u0 + u) * rec_stride + 2 + c] = sum;
             }
-            __syncthreads();   // red is rewritten by the next pass
+            __syncthreads();   // red is rewritten by the next pass's tiles
         }
-    };
-#pragma unroll 1
-    for (int f = 0; f < nbt; f += 2) {
-        issue(rb, f + 1);
-        use(ra, f);
-        issue(ra, f + 2);
-        if (f + 1 < nbt) use(rb, f + 1);   // uniform
+    } else {
+        // ---- value-row geometry of step 3. The passes are (value head, group of
+        // <= HP of its query heads); each pass walks the chunk's rows in batches
+        // of UNR row steps. Batches are double-buffered across passes: batch f+1
+        // is requested before batch f is used, and the first batch before step 2.
+        constexpr int HP = kDenseMaxHeadsPerPass;   // heads per pass (unused ones idle)
+        using R = Row16<T>;
+        constexpr int EPL = R::EPL;            // values per lane per row
+        constexpr int LPR = DH / EPL;          // lanes per row
+        constexpr int RPI = 64 / LPR;          // rows per wave instruction
+        constexpr int STEP = kWaves * RPI;
+        constexpr int UNR = 4;
+        constexpr int BATCH = STEP * UNR;
+        const int rg = lane / LPR;
+        const int sub = lane - rg * LPR;
+        const int first = wave * RPI + rg;
+        const int g_v = h_q / h_v;
+        const int i0 = kh * g;                 // first query head of the key head
+        const int vlo = i0 / g_v;
+        const int ng = (g_v + HP - 1) / HP;    // head groups per value head
+        const int np = ((i0 + g - 1) / g_v - vlo + 1) * ng;
+        const int nb = (n + BATCH - 1) / BATCH;
+        const int nbt = np * nb;
+        const T* vbase = v + ((int64_t)b * h_v * S_max + c0) * DH + sub * EPL;
+        // rows of batch f (clamped: past the chunk, or past the last batch, the
+        // loads re-read a live row and are never used)
+        auto issue = [&](u32x4 (&dst)[UNR], int f) {
+            f = f < nbt ? f : nbt - 1;
+            const int vh = vlo + (f / nb) / ng;
+            const int r0 = (f % nb) * BATCH;
+            const T* vb = vbase + (int64_t)vh * S_max * DH;
+    #pragma unroll
+            for (int j = 0; j < UNR; ++j) {
+                int r = r0 + first + j * STEP;
+                r = r < n ? r : n - 1;
+                dst[j] = load_stream(reinterpret_cast<const u32x4*>(vb + (int64_t)r * DH));
+            }
+        };
+        u32x4 ra[UNR], rb[UNR];
+        issue(ra, 0);
+
+        // ---- 2. softmax statistics of the chunk, per query head
+        const int64_t rec_stride = (int64_t)nchunk * (DH + 2);   // next head's record
+        float* rec0 = part + ((int64_t)(b * h_q + kh * g) * nchunk + chunk) * (DH + 2);
+        for (int u = wave; u < g; u += kWaves) {
+            float* s = sc + u * SR;
+            float mx = -__builtin_inff();
+    #pragma unroll
+            for (int t = lane; t < C; t += 64) mx = fmaxf(mx, s[t]);
+            mx = wave_fmax(mx);   // finite: row 0 of the chunk is live
+            float l = 0.f;
+    #pragma unroll
+            for (int t = lane; t < C; t += 64) {
+                const float p = __expf(s[t] - mx);
+                s[t] = p;
+                l += p;
+            }
+            l = wave_fsum(l);
+            if (lane == 0) {
+                rec0[u * rec_stride] = mx;
+                rec0[u * rec_stride + 1] = l;
+            }
+        }
+        __syncthreads();
+
+        // ---- 3. weighted sums of the value rows
+        float* red = reinterpret_cast<float*>(aux);   // [kWaves][HP][DH]
+        float acc[HP][EPL];
+    #pragma unroll
+        for (int u = 0; u < HP; ++u)
+    #pragma unroll
+            for (int c = 0; c < EPL; ++c) acc[u][c] = 0.f;
+        // batch f: accumulate its rows; after a pass's last batch, reduce over the
+        // row groups and the waves and write the pass's partial sums
+        auto use = [&](const u32x4 (&raw)[UNR], int f) {
+            const int pi = f / nb;
+            const int kb = f - pi * nb;
+            const int vh = vlo + pi / ng;
+            const int ulo = (vh * g_v > i0 ? vh * g_v : i0) - i0;
+            const int uhi = ((vh + 1) * g_v < i0 + g ? (vh + 1) * g_v : i0 + g) - i0;
+            const int u0 = ulo + (pi % ng) * HP;
+            const int nh = uhi - u0 < HP ? uhi - u0 : HP;   // <= 0: an empty group
+            const int r0 = kb * BATCH;
+            // weights of the batch's rows (rows past n hold 0), all read before
+            // any is used; heads past the pass's last read a valid row of the
+            // logit array and accumulate sums that are never written
+            float wv[UNR][HP];
+    #pragma unroll
+            for (int u = 0; u < HP; ++u) {
+                const int hu = u0 + u < g - 1 ? u0 + u : g - 1;
+                const float* pw = sc + hu * SR + r0 + first;
+    #pragma unroll
+                for (int j = 0; j < UNR; ++j) wv[j][u] = pw[j * STEP];
+            }
+    #pragma unroll
+            for (int j = 0; j < UNR; ++j) {
+                float fv[EPL];
+                R::cvt(raw[j], fv);
+    #pragma unroll
+                for (int u = 0; u < HP; ++u)
+    #pragma unroll
+                    for (int c = 0; c < EPL; ++c) acc[u][c] += wv[j][u] * fv[c];
+            }
+            if (kb == nb - 1) {   // uniform: the pass is complete
+    #pragma unroll
+                for (int o = LPR; o < 64; o <<= 1)
+    #pragma unroll
+                    for (int u = 0; u < HP; ++u)
+    #pragma unroll
+                        for (int c = 0; c < EPL; ++c) acc[u][c] += __shfl_xor(acc[u][c], o, 64);
+                if (rg == 0)
+    #pragma unroll
+                    for (int u = 0; u < HP; ++u)
+    #pragma unroll
+                        for (int c = 0; c < EPL; ++c)
+                            red[(wave * HP + u) * DH + sub * EPL + c] = acc[u][c];
+    #pragma unroll
+                for (int u = 0; u < HP; ++u)
+    #pragma unroll
+                    for (int c = 0; c < EPL; ++c) acc[u][c] = 0.f;
+                __syncthreads();
+                for (int x = tid; x < nh * DH; x += kDenseThreads) {
+                    const int u = x / DH;
+                    const int c = x - u * DH;
+                    float sum = 0.f;
+    #pragma unroll
+                    for (int w = 0; w < kWaves; ++w) sum += red[(w * HP + u) * DH + c];
+                    rec0[(u0 + u) * rec_stride + 2 + c] = sum;
+                }
+                __syncthreads();   // red is rewritten by the next pass
+            }
+        };
+    #pragma unroll 1
+        for (int f = 0; f < nbt; f += 2) {
+            issue(rb, f + 1);
+            use(ra, f);
+            issue(ra, f + 2);
+            if (f + 1 < nbt) use(rb, f + 1);   // uniform
+        }
+
     }
 }
 
@@ -283,7 +477,7 @@ __global__ __launch_bounds__(DH) void dense_merge(const float* __restrict__ part
     out[(int64_t)row * DH + c] = den > 0.f ? num / den : 0.f;
 }
 
-template <typename T, int DH, int NHT, int HP>
+template <typename T, int DH, int NHT>
 hipError_t go_dense(const void* q, const void* k, const void* v, const int32_t* lens, float* part,
                     int B, int h_q, int h_k, int h_v, int64_t S_max, hipStream_t st) {
     constexpr int C = dense_chunk_for(NHT);
@@ -292,7 +486,7 @@ hipError_t go_dense(const void* q, const void* k, const void* v, const int32_t* 
     const size_t lds = dense_logit_bytes(g, C) + dense_aux_bytes<T, DH>();
     static_assert(16 * NHT * C * sizeof(float) + dense_aux_bytes<T, DH>() <= 160 * 1024,
                   "logits of 16 NHT heads must fit the LDS");
-    auto kern = &dense_attn<T, DH, NHT, HP>;
+    auto kern = &dense_attn<T, DH, NHT>;
     if (lds > 64 * 1024) {
         const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                                  hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -306,29 +500,14 @@ hipError_t go_dense(const void* q, const void* k, const void* v, const int32_t* 
     return hipGetLastError();
 }
 
-// heads per pass: g_v rounded up to an even count (at most 8) for bf16; the
-// fp32 path (small shapes) always takes 8
-template <typename T, int DH, int NHT>
-hipError_t go_dense_hp(const void* q, const void* k, const void* v, const int32_t* lens,
-                       float* part, int B, int h_q, int h_k, int h_v, int64_t S_max,
-                       hipStream_t st) {
-    const int g_v = h_q / h_v;
-    if (sizeof(T) == 2) {
-        if (g_v <= 2) return go_dense<T, DH, NHT, 2>(q, k, v, lens, part, B, h_q, h_k, h_v, S_max, st);
-        if (g_v <= 4) return go_dense<T, DH, NHT, 4>(q, k, v, lens, part, B, h_q, h_k, h_v, S_max, st);
-        if (g_v <= 6) return go_dense<T, DH, NHT, 6>(q, k, v, lens, part, B, h_q, h_k, h_v, S_max, st);
-    }
-    return go_dense<T, DH, NHT, 8>(q, k, v, lens, part, B, h_q, h_k, h_v, S_max, st);
-}
-
 template <typename T, int DH>
 hipError_t go_dense_g(const void* q, const void* k, const void* v, const int32_t* lens,
                       float* part, int B, int h_q, int h_k, int h_v, int64_t S_max,
                       hipStream_t st) {
     const int g = h_q / h_k;
-    if (g <= 16) return go_dense_hp<T, DH, 1>(q, k, v, lens, part, B, h_q, h_k, h_v, S_max, st);
-    if (g <= 32) return go_dense_hp<T, DH, 2>(q, k, v, lens, part, B, h_q, h_k, h_v, S_max, st);
-    return go_dense_hp<T, DH, 4>(q, k, v, lens, part, B, h_q, h_k, h_v, S_max, st);
+    if (g <= 16) return go_dense<T, DH, 1>(q, k, v, lens, part, B, h_q, h_k, h_v, S_max, st);
+    if (g <= 32) return go_dense<T, DH, 2>(q, k, v, lens, part, B, h_q, h_k, h_v, S_max, st);
+    return go_dense<T, DH, 4>(q, k, v, lens, part, B, h_q, h_k, h_v, S_max, st);
 }
 
 }  // namespace
