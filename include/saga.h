@@ -98,10 +98,12 @@ saga_status saga_decode_attn(const void* q, const void* k_cache, const void* v_c
 /*
  * saga_decode_attn with phase timing for benchmarks: identical work and
  * results, and records events[i] on `stream` for i < n_events (0..4) at phase
- * boundary i: 0 before the K-scan, 1 after the K-scan (with its per-chunk
- * candidate extraction), 2 after top-N selection, 3 after the value gather
- * (the end of the call). The events are created by the caller (timing
- * enabled); a null event or n_events outside 0..4 gives SAGA_ERR_INVALID_ARG.
+ * boundary i: 0 the start and 1 the end of the K-scan kernel (with its
+ * per-chunk candidate extraction; on the top-M path both are stamped by that
+ * dispatch itself, so 1 - 0 is the kernel's run time, without launch
+ * latency), 2 after top-N selection, 3 after the value gather (the end of the
+ * call). The events are created by the caller (timing enabled); a null event
+ * or n_events outside 0..4 gives SAGA_ERR_INVALID_ARG.
  */
 saga_status saga_decode_attn_timed(const void* q, const void* k_cache, const void* v_cache,
                                    const int32_t* seq_lens, float* out,

@@ -129,19 +129,21 @@ saga_status decode(const void* q, const void* k_cache, const void* v_cache,
     const int64_t ss = saga::score_stride(S_max);
 
     clear_stale_error();
-    if ((s = pm.mark(0, stream)) != SAGA_OK) return s;
     if (saga::use_union_path(h_q, h_k, S_max)) {
+        // events 0 and 1 carry the K-scan dispatch's own start and end
         const saga::TopmOut tm{w.cand, w.cand_meta, N};
         s = from_hip(saga::launch_kscan_topm(q, k_cache, seq_lens, tm, B, h_q, h_k, d, S_max,
-                                             bf16, stream), "kscan_topm");
+                                             bf16, stream, pm.n > 0 ? pm.ev[0] : nullptr,
+                                             pm.n > 1 ? pm.ev[1] : nullptr),
+                     "kscan_topm");
         if (s != SAGA_OK) return s;
-        if ((s = pm.mark(1, stream)) != SAGA_OK) return s;
         s = from_hip(saga::launch_select_union(tm, seq_lens, B, h_q, h_k, d, N, S_max,
                                                w.sel_idx, w.sel_val, w.row_max, w.row_cnt,
                                                idx_out, w.row_flag, q, k_cache, w.scores, ss,
                                                bf16, stream), "select_union");
         if (s != SAGA_OK) return s;
     } else {
+        if ((s = pm.mark(0, stream)) != SAGA_OK) return s;
         s = from_hip(saga::launch_kscan(q, k_cache, seq_lens, w.scores, ss, B, h_q, h_k, d,
                                         S_max, bf16, stream), "kscan");
         if (s != SAGA_OK) return s;

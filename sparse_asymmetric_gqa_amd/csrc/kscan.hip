@@ -44,6 +44,8 @@
 //                  compete with the K stream.
 #include "kstream.h"
 
+#include <hip/hip_ext.h>
+
 namespace saga {
 using namespace dev;
 
@@ -532,7 +534,8 @@ hipError_t go_dense(int nht, const void* q, const void* k, const int32_t* lens, 
 
 template <typename T, int DH>
 hipError_t go_topm(const void* q, const void* k, const int32_t* lens, const TopmOut& tm, int B,
-                   int h_q, int h_k, int64_t S_max, hipStream_t st) {
+                   int h_q, int h_k, int64_t S_max, hipStream_t st, hipEvent_t ev0,
+                   hipEvent_t ev1) {
     const int nchunk = (int)((S_max + kScanChunk - 1) / kScanChunk);
     const int nwork = B * h_k * nchunk;
     const float scale = (float)(1.0 / __builtin_sqrt((double)DH));
@@ -549,9 +552,14 @@ hipError_t go_topm(const void* q, const void* k, const int32_t* lens, const Topm
         attr_set = true;
     }
     const int grid = resident_grid(kern, kTopmThreads, lds, nwork);
-    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kTopmThreads), lds, st, (const T*)q,
-                       (const T*)k, lens, h_q, h_k, S_max, nchunk, nwork, scale, tm,
-                       (uint32_t)lds);
+    if (ev0 || ev1)   // events stamped with the dispatch's own start and end
+        hipExtLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kTopmThreads), lds, st, ev0, ev1, 0,
+                              (const T*)q, (const T*)k, lens, h_q, h_k, S_max, nchunk, nwork,
+                              scale, tm, (uint32_t)lds);
+    else
+        hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kTopmThreads), lds, st, (const T*)q,
+                           (const T*)k, lens, h_q, h_k, S_max, nchunk, nwork, scale, tm,
+                           (uint32_t)lds);
     return hipGetLastError();
 }
 
@@ -571,12 +579,12 @@ hipError_t launch_kscan(const void* q, const void* k, const int32_t* lens, float
 
 hipError_t launch_kscan_topm(const void* q, const void* k, const int32_t* lens, const TopmOut& tm,
                              int B, int h_q, int h_k, int d, int64_t S_max, bool bf16,
-                             hipStream_t st) {
+                             hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
     if (bf16)
-        return d == 64 ? go_topm<uint16_t, 64>(q, k, lens, tm, B, h_q, h_k, S_max, st)
-                       : go_topm<uint16_t, 128>(q, k, lens, tm, B, h_q, h_k, S_max, st);
-    return d == 64 ? go_topm<float, 64>(q, k, lens, tm, B, h_q, h_k, S_max, st)
-                   : go_topm<float, 128>(q, k, lens, tm, B, h_q, h_k, S_max, st);
+        return d == 64 ? go_topm<uint16_t, 64>(q, k, lens, tm, B, h_q, h_k, S_max, st, ev0, ev1)
+                       : go_topm<uint16_t, 128>(q, k, lens, tm, B, h_q, h_k, S_max, st, ev0, ev1);
+    return d == 64 ? go_topm<float, 64>(q, k, lens, tm, B, h_q, h_k, S_max, st, ev0, ev1)
+                   : go_topm<float, 128>(q, k, lens, tm, B, h_q, h_k, S_max, st, ev0, ev1);
 }
 
 }  // namespace saga

@@ -5,11 +5,13 @@
 // query head uses value head i / (h_q / h_v) (§3.2, App. B Eq. 29).
 //
 // One workgroup per (b, i) row, walking its kept list in blocks of
-// kPvEntries. Per block its 256 threads stage positions and weights
-// exp(s - m) in LDS (m = the row's largest kept logit), then every wave
-// streams its share of value rows with 16-byte loads, LPR lanes per row, all
-// rows of a wave in flight at once; the block sums stay in registers and the
-// row ends with out = acc / l, so no merge pass is needed. The g_v heads that
+// kPvEntries (a whole list of N <= 1024 is one block). Per block its 256
+// threads stage positions and weights exp(s - m) in LDS (m = the row's
+// largest kept logit), then every wave streams its share of value rows with
+// 16-byte loads, LPR lanes per row, in batches of 8 rows per lane that are
+// double-buffered (the next batch is in flight while one is summed); the sums
+// stay in registers and the row ends with out = acc / l, so no merge pass is
+// needed. The g_v heads that
 // share a value head are mapped to the same XCD at neighbouring times so value
 // rows they have in common are served from that XCD's L2.
 #include "saga_internal.h"
@@ -39,8 +41,9 @@ __global__ __launch_bounds__(kPvThreads) void pv_sparse(
     constexpr int LPR = DH / EPL;          // lanes per value row
     constexpr int RPI = 64 / LPR;          // rows per wave instruction
     constexpr int STEP = kPvWaves * RPI;   // rows per workgroup step
-    constexpr int PER = kPvEntries / STEP; // rows per row-group and block
-    constexpr int UNR = PER < 16 ? PER : 16;
+    constexpr int UNR = 8;                 // row steps per batch (one load each per lane)
+    constexpr int BATCH = STEP * UNR;
+    static_assert(kPvEntries % BATCH == 0, "a block is whole batches");
     __shared__ int32_t s_pos[kPvEntries];
     __shared__ float s_w[kPvEntries];
     __shared__ float s_red[kPvWaves][DH];
@@ -74,8 +77,9 @@ __global__ __launch_bounds__(kPvThreads) void pv_sparse(
 #pragma unroll 1
     for (int e0 = 0; e0 < cnt; e0 += kPvEntries) {
         const int ne = cnt - e0 < kPvEntries ? cnt - e0 : kPvEntries;
-        {
-            const int e = tid;
+        // the block's positions and weights exp(s - m) into LDS; entries past
+        // ne read row 0 with weight 0
+        for (int e = tid; e < kPvEntries; e += kPvThreads) {
             float w = 0.f;
             int32_t pos = 0;
             if (e < ne) {
@@ -89,23 +93,35 @@ __global__ __launch_bounds__(kPvThreads) void pv_sparse(
             lsum += w;
         }
         __syncthreads();
-#pragma unroll 1
-        for (int k0 = 0; k0 < PER; k0 += UNR) {
-            u32x4 raw[UNR];
-            float wt[UNR];
+        // value rows in batches of UNR steps, double-buffered: batch j + 1 is
+        // requested before batch j is used
+        const int nb = (ne + BATCH - 1) / BATCH;
+        u32x4 ra[UNR], rb[UNR];
+        auto issue = [&](u32x4 (&dst)[UNR], int j) {
+            j = j < nb ? j : nb - 1;   // past the last batch: re-read it (never used)
 #pragma unroll
             for (int k = 0; k < UNR; ++k) {
-                const int e = first + (k0 + k) * STEP;
-                wt[k] = s_w[e];   // 0 past ne
-                raw[k] = *reinterpret_cast<const u32x4*>(vb + (int64_t)s_pos[e] * DH + sub * EPL);
+                const int e = j * BATCH + first + k * STEP;
+                dst[k] = *reinterpret_cast<const u32x4*>(vb + (int64_t)s_pos[e] * DH + sub * EPL);
             }
+        };
+        auto use = [&](const u32x4 (&src)[UNR], int j) {
 #pragma unroll
             for (int k = 0; k < UNR; ++k) {
+                const float wt = s_w[j * BATCH + first + k * STEP];   // 0 past ne
                 float f[EPL];
-                R::cvt(raw[k], f);
+                R::cvt(src[k], f);
 #pragma unroll
-                for (int c = 0; c < EPL; ++c) acc[c] += wt[k] * f[c];
+                for (int c = 0; c < EPL; ++c) acc[c] += wt * f[c];
             }
+        };
+        issue(ra, 0);
+#pragma unroll 1
+        for (int j = 0; j < nb; j += 2) {
+            issue(rb, j + 1);
+            use(ra, j);
+            issue(ra, j + 2);
+            if (j + 1 < nb) use(rb, j + 1);   // uniform
         }
         __syncthreads();   // the block's LDS lists are reused by the next block
     }

@@ -11,7 +11,7 @@ namespace saga {
 #define SAGA_KSCAN_CHUNK 1024
 #endif
 constexpr int kScanChunk = SAGA_KSCAN_CHUNK;   // positions per K-scan workgroup
-constexpr int kPvEntries = 256;      // kept entries per sparse PV workgroup
+constexpr int kPvEntries = 1024;     // kept entries staged per block of the sparse PV
 constexpr int kSelectThreads = 1024; // threads of one select workgroup
 constexpr int kMaxHeadGroup = 64;    // largest h_q / h_k and h_q / h_v supported
 
@@ -68,9 +68,10 @@ hipError_t launch_kscan(const void* q, const void* k, const int32_t* lens, float
                         bool bf16, hipStream_t st);
 
 // K-scan in top-M mode (h_q / h_k <= 16): candidate lists instead of logits.
+// ev0 / ev1 (nullable) are stamped with the kernel's own start and end.
 hipError_t launch_kscan_topm(const void* q, const void* k, const int32_t* lens, const TopmOut& tm,
                              int B, int h_q, int h_k, int d, int64_t S_max, bool bf16,
-                             hipStream_t st);
+                             hipStream_t st, hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr);
 
 hipError_t launch_select(const float* scores, int64_t s_stride, const int32_t* lens, int B,
                          int h_q, int N, int64_t S_max, int32_t* sel_idx, float* sel_val,
