@@ -50,8 +50,12 @@ def _load():
         lib.oracle_logits.argtypes = [vp, vp, vp, i, i, i, i, i64, i, vp, i64, vp, i]
         lib.oracle_attend_given.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i64, i, i, vp, i64,
                                             vp, vp, vp, i]
+        lib.oracle_atopn_calibrate.argtypes = [vp, vp, vp, i, i, i, i, i64, i, i, vp, i64, vp,
+                                               vp, i]
+        lib.oracle_atopn_attn.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i64, i, i, vp, vp, i64,
+                                          vp, vp, vp, vp, vp, vp, i]
         for f in (lib.oracle_topn_attn, lib.oracle_dense_attn, lib.oracle_logits,
-                  lib.oracle_attend_given):
+                  lib.oracle_attend_given, lib.oracle_atopn_calibrate, lib.oracle_atopn_attn):
             f.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -151,3 +155,44 @@ def attend_given(q, k, v, seq_lens, idx, pairs=None, threads=0):
     if rc < 0:
         raise ValueError("oracle_attend_given: bad arguments or invalid index set")
     return out, psum
+
+
+def atopn_calibrate(q, k, seq_lens, N, pairs=None, threads=0):
+    """Atop-N calibration: tau [P] (the N_eff-th largest softmax probability of
+    each row, NaN if L = 0) and lse [P] (log-sum-exp of the row's logits)."""
+    q, k, _, lens, dt, B, h_q, h_k, _, d, S = _prep(q, k, None, seq_lens)
+    pr, P = _pairs(pairs, B, h_q)
+    tau = np.empty(P)
+    lse = np.empty(P)
+    rc = _load().oracle_atopn_calibrate(_p(q), _p(k), _p(lens), B, h_q, h_k, d, S, dt, int(N),
+                                        _p(pr), P, _p(tau), _p(lse), int(threads))
+    if rc < 0:
+        raise ValueError("oracle_atopn_calibrate: bad arguments")
+    return tau, lse
+
+
+def atopn_attn(q, k, v, seq_lens, N, tau, pairs=None, threads=0):
+    """Atop-N step with stale thresholds tau [P] (one per listed pair).
+
+    Returns dict: out [P][d], idx [P][2N] int32 (ascending, -1 pad),
+    sel [P][2N] (-inf pad), above [P] (positions reaching the threshold,
+    before the 2N cap), theta [P] (logit threshold), psum [P], threads.
+    """
+    q, k, v, lens, dt, B, h_q, h_k, h_v, d, S = _prep(q, k, v, seq_lens)
+    pr, P = _pairs(pairs, B, h_q)
+    tau = np.ascontiguousarray(np.asarray(tau, dtype=np.float64).reshape(-1))
+    assert tau.shape == (P,)
+    cap = 2 * int(N)
+    out = np.empty((P, d))
+    idx = np.empty((P, cap), dtype=np.int32)
+    sel = np.empty((P, cap))
+    above = np.empty(P, dtype=np.int64)
+    theta = np.empty(P)
+    psum = np.empty(P)
+    rc = _load().oracle_atopn_attn(_p(q), _p(k), _p(v), _p(lens), B, h_q, h_k, h_v, d, S, dt,
+                                   int(N), _p(tau), _p(pr), P, _p(out), _p(idx), _p(sel),
+                                   _p(above), _p(theta), _p(psum), int(threads))
+    if rc < 0:
+        raise ValueError("oracle_atopn_attn: bad arguments")
+    return {"out": out, "idx": idx, "sel": sel, "above": above, "theta": theta, "psum": psum,
+            "threads": rc}

@@ -31,6 +31,21 @@
  * Precision: inputs are the stored fp32 / bf16 values decoded exactly; all
  * arithmetic is fp64 with the host libm exp().
  *
+ * Atop-N with a stale threshold (§3.1, App. C.1), the two functions at the
+ * end of this file. Readings where the pages leave a step open:
+ *   - calibration keeps tau = the N_eff-th largest probability of the exact
+ *     softmax over all L positions (probability space, per (b, i));
+ *   - a later step keeps the positions whose probability reaches tau,
+ *     p_t = exp(z_t - LSE(z)) >= tau (compared here in probability space,
+ *     computed exactly as tau was); in logit space that is
+ *     z_t >= log(tau) + LSE(z), the pages' approximate max logit only
+ *     stabilising the sum; ">=" (not ">") so that the calibration step's own
+ *     inputs give back exactly its top-N set;
+ *   - at most 2N positions are kept, the first 2N in ascending position (the
+ *     pages drop the excess in the order of an atomic counter);
+ *   - no position reaching tau: the output is 0 (a softmax over an empty set
+ *     is undefined).
+ *
  * Parity pins live in tests/test_oracle_pins.py (closed forms, library
  * reductions, brute force); every function below is pinned there.
  */
@@ -278,6 +293,100 @@ int oracle_attend_given(const void* q, const void* k, const void* v, const int32
         for (int64_t r = 1; r < n; ++r) if (sel[r].t == sel[r - 1].t) bad = 1;
         attend(&P, b, i, sel, n, out + j * d, psum + j);
         free(sel);
+    }
+    return bad ? -1 : used;
+}
+
+/* log sum_t exp(z_t) over the row, stabilised by its largest logit. */
+static double log_sum_exp(const scored_t* all, int64_t L) {
+    double m = -INFINITY;
+    for (int64_t t = 0; t < L; ++t) if (all[t].s > m) m = all[t].s;
+    double z = 0.0;
+    for (int64_t t = 0; t < L; ++t) z += exp(all[t].s - m);
+    return m + log(z);
+}
+
+/*
+ * Atop-N calibration step (App. C.1): the exact softmax probabilities of the
+ * row and the N_eff-th largest of them, tau[j] (NaN if L = 0); lse[j] is the
+ * row's log-sum-exp of the logits. Same pair convention as oracle_topn_attn.
+ * Returns threads used or -1.
+ */
+int oracle_atopn_calibrate(const void* q, const void* k, const int32_t* lens,
+                           int B, int h_q, int h_k, int d, int64_t S_max, int dtype, int N,
+                           const int64_t* pairs, int64_t npairs, double* tau, double* lse,
+                           int nthreads) {
+    problem_t P = {q, k, NULL, lens, B, h_q, h_k, h_k, d, S_max, dtype};
+    if (check(&P) || N < 1) return -1;
+    if (!pairs) npairs = (int64_t)B * h_q;
+    int used = set_threads(nthreads);
+    int bad = 0;
+    #pragma omp parallel for schedule(dynamic, 1) reduction(|:bad)
+    for (int64_t j = 0; j < npairs; ++j) {
+        int b, i;
+        pair_of(&P, pairs, j, &b, &i);
+        if (b < 0 || b >= B || i < 0 || i >= h_q) { bad = 1; continue; }
+        int64_t L = seq_len(&P, b);
+        if (L <= 0) { tau[j] = NAN; lse[j] = NAN; continue; }
+        scored_t* all = (scored_t*)malloc(sizeof(scored_t) * (size_t)L);
+        if (!all) { bad = 1; continue; }
+        for (int64_t t = 0; t < L; ++t) { all[t].s = logit(&P, b, i, t); all[t].t = t; }
+        const double z = log_sum_exp(all, L);
+        qsort(all, (size_t)L, sizeof(scored_t), by_logit_desc);
+        const int64_t n = L < N ? L : N;
+        tau[j] = exp(all[n - 1].s - z);
+        lse[j] = z;
+        free(all);
+    }
+    return bad ? -1 : used;
+}
+
+/*
+ * Atop-N step with the stale thresholds tau[npairs] (§3.1, App. C.1): keep
+ * the positions t < L with exp(z_t - LSE(z)) >= tau, in ascending position,
+ * at most the first 2N of them; then Eq. 7 over the kept entries (out = 0
+ * when none is kept). Per pair:
+ *   out[d]; idx[2N] kept positions (-1 pad); sel[2N] their logits (-inf pad);
+ *   above[j] = count of positions reaching tau (before the 2N cap);
+ *   theta[j] = log(tau) + LSE(z), the same threshold in logit space;
+ *   psum[j] = sum of the softmax weights (0 when none is kept).
+ * Returns threads used or -1.
+ */
+int oracle_atopn_attn(const void* q, const void* k, const void* v, const int32_t* lens,
+                      int B, int h_q, int h_k, int h_v, int d, int64_t S_max, int dtype, int N,
+                      const double* tau, const int64_t* pairs, int64_t npairs,
+                      double* out, int32_t* idx, double* sel, int64_t* above, double* theta,
+                      double* psum, int nthreads) {
+    problem_t P = {q, k, v, lens, B, h_q, h_k, h_v, d, S_max, dtype};
+    if (check(&P) || N < 1) return -1;
+    if (!pairs) npairs = (int64_t)B * h_q;
+    const int64_t cap = 2 * (int64_t)N;
+    int used = set_threads(nthreads);
+    int bad = 0;
+    #pragma omp parallel for schedule(dynamic, 1) reduction(|:bad)
+    for (int64_t j = 0; j < npairs; ++j) {
+        int b, i;
+        pair_of(&P, pairs, j, &b, &i);
+        if (b < 0 || b >= B || i < 0 || i >= h_q) { bad = 1; continue; }
+        int64_t L = seq_len(&P, b);
+        scored_t* all = (scored_t*)malloc(sizeof(scored_t) * (size_t)(L > 0 ? L : 1));
+        if (!all) { bad = 1; continue; }
+        for (int64_t t = 0; t < L; ++t) { all[t].s = logit(&P, b, i, t); all[t].t = t; }
+        const double z = L > 0 ? log_sum_exp(all, L) : NAN;
+        theta[j] = log(tau[j]) + z;
+        int64_t n = 0, cnt = 0;
+        for (int64_t t = 0; t < L; ++t) {       /* ascending position */
+            if (!(exp(all[t].s - z) >= tau[j])) continue;
+            ++cnt;
+            if (n < cap) all[n++] = all[t];     /* n <= t: in-place compaction */
+        }
+        above[j] = cnt;
+        for (int64_t r = 0; r < cap; ++r) {
+            idx[j * cap + r] = r < n ? (int32_t)all[r].t : -1;
+            sel[j * cap + r] = r < n ? all[r].s : -INFINITY;
+        }
+        attend(&P, b, i, all, n, out + j * d, psum + j);
+        free(all);
     }
     return bad ? -1 : used;
 }
