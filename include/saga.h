@@ -135,6 +135,45 @@ saga_status saga_dense_attn(const void* q, const void* k_cache, const void* v_ca
                             void* workspace, size_t workspace_bytes);
 
 /*
+ * Atop-N, the pages' production selector with a stale threshold ("More Value
+ * per Key" §3.1, App. C.1). A calibration step (every n steps in the pages,
+ * n = 32) is the exact top-N step and also records, per (b, query head), tau
+ * = the N_eff-th largest attention probability of the row. The steps in
+ * between keep the positions whose probability reaches tau,
+ * p_t = exp(z_t - LSE(z)) >= tau (compared as z_t >= log(tau) + LSE), at most
+ * the first 2N in position order (the pages drop the excess in the order of
+ * an atomic counter), and attend over them (Eq. 7); a row keeping none gets
+ * out = 0. tau is state owned by the caller: device memory, fp32
+ * [B][h_q], written by saga_atopn_calibrate and read by saga_atopn_attn.
+ *
+ * Both take the saga_decode_attn arguments plus tau, and need a workspace of
+ * saga_atopn_workspace_size bytes (the decode workspace with 2N kept slots
+ * per row). Supported for h_q / h_k <= 16 and S_max <= 512 Ki (the top-M
+ * K-scan path); other shapes give SAGA_ERR_UNSUPPORTED. Errors as for
+ * saga_decode_attn; a null tau is SAGA_ERR_INVALID_ARG.
+ */
+size_t saga_atopn_workspace_size(int B, int h_q, int h_k, int h_v, int d, int N,
+                                 int64_t S_max, saga_dtype dtype);
+
+/* Calibration: the exact top-N step (same out and idx_out [B][h_q][N] as
+ * saga_decode_attn) plus tau. Rows with L_b = 0 get tau = NaN. */
+saga_status saga_atopn_calibrate(const void* q, const void* k_cache, const void* v_cache,
+                                 const int32_t* seq_lens, float* out, int B, int h_q, int h_k,
+                                 int h_v, int d, int N, hipStream_t stream, int64_t S_max,
+                                 saga_dtype dtype, void* workspace, size_t workspace_bytes,
+                                 float* tau, int32_t* idx_out);
+
+/* Stale-threshold step. idx_out (nullable): [B][h_q][2N] kept positions in
+ * ascending order, -1 padded. count_out (nullable): int32 [B][h_q], the
+ * positions reaching the threshold before the 2N cap. tau = 0 keeps every
+ * position (up to the cap); tau = NaN keeps none. */
+saga_status saga_atopn_attn(const void* q, const void* k_cache, const void* v_cache,
+                            const int32_t* seq_lens, float* out, int B, int h_q, int h_k,
+                            int h_v, int d, int N, hipStream_t stream, int64_t S_max,
+                            saga_dtype dtype, void* workspace, size_t workspace_bytes,
+                            const float* tau, int32_t* idx_out, int32_t* count_out);
+
+/*
  * The K-scan step alone (§2.1 Eq. 2 with the App. B key-head map): writes the
  * fp32 logits scores[B][h_q][S_max] for t < L_b; entries t >= L_b are left
  * untouched. Same argument rules as saga_decode_attn (h_v is not involved).

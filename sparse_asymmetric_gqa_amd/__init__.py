@@ -6,9 +6,11 @@ been built: there is no CPU or eager fallback.
 """
 from ._binding import (  # noqa: F401
     EXPORTS, LIB_PATH, SAGA_BF16, SAGA_ERR_HIP, SAGA_ERR_INVALID_ARG, SAGA_ERR_UNSUPPORTED,
-    SAGA_ERR_WORKSPACE, SAGA_F32, SAGA_OK, SagaError, lib, saga_debug_fallback_rows,
+    SAGA_ERR_WORKSPACE, SAGA_F32, SAGA_OK, SagaError, lib, saga_atopn_attn, saga_atopn_calibrate,
+    saga_atopn_workspace_size, saga_debug_fallback_rows,
     saga_debug_scores, saga_decode_attn, saga_decode_attn_timed,
     saga_dense_attn, saga_dense_workspace_size, saga_status_string, saga_workspace_size,
     status_string)
 from .tensors import (  # noqa: F401
-    debug_scores, decode_attn, dense_attn, dense_workspace_size, new_workspace, workspace_size)
+    atopn_attn, atopn_calibrate, atopn_workspace_size, debug_scores, decode_attn, dense_attn,
+    dense_workspace_size, new_workspace, workspace_size)

@@ -23,7 +23,8 @@ SAGA_F32 = 0
 SAGA_BF16 = 1
 
 EXPORTS = ("saga_workspace_size", "saga_decode_attn", "saga_decode_attn_timed",
-           "saga_dense_workspace_size",
+           "saga_dense_workspace_size", "saga_atopn_workspace_size", "saga_atopn_calibrate",
+           "saga_atopn_attn",
            "saga_dense_attn", "saga_debug_scores", "saga_debug_fallback_rows",
            "saga_status_string")
 
@@ -60,6 +61,14 @@ def _load() -> ctypes.CDLL:
     lib.saga_debug_scores.restype = i
     lib.saga_debug_fallback_rows.argtypes = [vp, sz, i, i, i, i, i, i, i64, i, vp, vp]
     lib.saga_debug_fallback_rows.restype = i
+    lib.saga_atopn_workspace_size.argtypes = [i, i, i, i, i, i, i64, i]
+    lib.saga_atopn_workspace_size.restype = sz
+    lib.saga_atopn_calibrate.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, vp, i64, i, vp, sz,
+                                         vp, vp]
+    lib.saga_atopn_calibrate.restype = i
+    lib.saga_atopn_attn.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, vp, i64, i, vp, sz, vp,
+                                    vp, vp]
+    lib.saga_atopn_attn.restype = i
     lib.saga_status_string.argtypes = [i]
     lib.saga_status_string.restype = ctypes.c_char_p
     return lib
@@ -129,3 +138,23 @@ def saga_debug_fallback_rows(workspace, workspace_bytes, B, h_q, h_k, h_v, d, N,
     return int(lib.saga_debug_fallback_rows(_ptr(workspace), workspace_bytes, B, h_q, h_k, h_v,
                                             d, N, S_max, dtype,
                                             ctypes.c_void_p(host_flags.ctypes.data), _ptr(stream)))
+
+
+def saga_atopn_workspace_size(B, h_q, h_k, h_v, d, N, S_max, dtype) -> int:
+    return int(lib.saga_atopn_workspace_size(B, h_q, h_k, h_v, d, N, S_max, dtype))
+
+
+def saga_atopn_calibrate(q, k_cache, v_cache, seq_lens, out, B, h_q, h_k, h_v, d, N, stream,
+                         S_max, dtype, workspace, workspace_bytes, tau, idx_out=None) -> int:
+    return int(lib.saga_atopn_calibrate(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seq_lens),
+                                        _ptr(out), B, h_q, h_k, h_v, d, N, _ptr(stream), S_max,
+                                        dtype, _ptr(workspace), workspace_bytes, _ptr(tau),
+                                        _ptr(idx_out)))
+
+
+def saga_atopn_attn(q, k_cache, v_cache, seq_lens, out, B, h_q, h_k, h_v, d, N, stream, S_max,
+                    dtype, workspace, workspace_bytes, tau, idx_out=None, count_out=None) -> int:
+    return int(lib.saga_atopn_attn(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seq_lens),
+                                   _ptr(out), B, h_q, h_k, h_v, d, N, _ptr(stream), S_max, dtype,
+                                   _ptr(workspace), workspace_bytes, _ptr(tau), _ptr(idx_out),
+                                   _ptr(count_out)))

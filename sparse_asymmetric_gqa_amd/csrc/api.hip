@@ -31,6 +31,7 @@ Workspace carve(void* base, int B, int h_q, int h_k, int d, int N, int64_t S_max
         const size_t nch = (size_t)num_chunks(S_max);
         w.cand = reinterpret_cast<uint2*>(take(rows * nch * kScanChunk * sizeof(uint2)));
         w.cand_meta = reinterpret_cast<uint4*>(take(rows * nch * sizeof(uint4)));
+        w.cand_stat = reinterpret_cast<float2*>(take(rows * nch * sizeof(float2)));
         w.row_flag = reinterpret_cast<int32_t*>(take(rows * sizeof(int32_t)));
         w.sel_idx = reinterpret_cast<int32_t*>(take(rows * (size_t)N * sizeof(int32_t)));
         w.sel_val = reinterpret_cast<float*>(take(rows * (size_t)N * sizeof(float)));
@@ -131,7 +132,7 @@ saga_status decode(const void* q, const void* k_cache, const void* v_cache,
     clear_stale_error();
     if (saga::use_union_path(h_q, h_k, S_max)) {
         // events 0 and 1 carry the K-scan dispatch's own start and end
-        const saga::TopmOut tm{w.cand, w.cand_meta, N};
+        const saga::TopmOut tm{w.cand, w.cand_meta, N, nullptr};
         s = from_hip(saga::launch_kscan_topm(q, k_cache, seq_lens, tm, B, h_q, h_k, d, S_max,
                                              bf16, stream, pm.n > 0 ? pm.ev[0] : nullptr,
                                              pm.n > 1 ? pm.ev[1] : nullptr),
@@ -205,6 +206,100 @@ saga_status saga_dense_attn(const void* q, const void* k_cache, const void* v_ca
     return from_hip(saga::launch_dense_attn(q, k_cache, v_cache, seq_lens, w.part, out, B, h_q,
                                             h_k, h_v, d, S_max, bf16, stream),
                     "dense_attn");
+}
+
+size_t saga_atopn_workspace_size(int B, int h_q, int h_k, int h_v, int d, int N,
+                                int64_t S_max, saga_dtype dtype) {
+    if (check_shape(B, h_q, h_k, h_v, d, S_max, dtype) != SAGA_OK || N < 1 || N > (1 << 29))
+        return 0;
+    // the decode workspace with kept lists of 2N slots per row
+    return saga::carve(nullptr, B, h_q, h_k, d, 2 * N, S_max, false).bytes;
+}
+
+}  // extern "C"
+
+namespace {
+
+// Shared argument checks and workspace carve of the two Atop-N entry points.
+saga_status atopn_prepare(const void* q, const void* k_cache, const void* v_cache,
+                          const int32_t* seq_lens, const float* out, int B, int h_q, int h_k,
+                          int h_v, int d, int N, int64_t S_max, saga_dtype dtype, void* workspace,
+                          size_t workspace_bytes, const float* tau, saga::Workspace& w) {
+    if (!q || !k_cache || !v_cache || !seq_lens || !out || !tau) return SAGA_ERR_INVALID_ARG;
+    saga_status s = check_shape(B, h_q, h_k, h_v, d, S_max, dtype);
+    if (s != SAGA_OK) return s;
+    if (N < 1 || N > (1 << 29)) return SAGA_ERR_INVALID_ARG;
+    if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache)) return SAGA_ERR_INVALID_ARG;
+    if (!saga::use_union_path(h_q, h_k, S_max)) return SAGA_ERR_UNSUPPORTED;
+    const saga::Workspace need = saga::carve(nullptr, B, h_q, h_k, d, 2 * N, S_max, false);
+    if (!workspace || workspace_bytes < need.bytes ||
+        (reinterpret_cast<uintptr_t>(workspace) & 255u))
+        return SAGA_ERR_WORKSPACE;
+    w = saga::carve(workspace, B, h_q, h_k, d, 2 * N, S_max, false);
+    return SAGA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+saga_status saga_atopn_calibrate(const void* q, const void* k_cache, const void* v_cache,
+                                 const int32_t* seq_lens, float* out, int B, int h_q, int h_k,
+                                 int h_v, int d, int N, hipStream_t stream, int64_t S_max,
+                                 saga_dtype dtype, void* workspace, size_t workspace_bytes,
+                                 float* tau, int32_t* idx_out) {
+    saga::Workspace w;
+    saga_status s = atopn_prepare(q, k_cache, v_cache, seq_lens, out, B, h_q, h_k, h_v, d, N,
+                                  S_max, dtype, workspace, workspace_bytes, tau, w);
+    if (s != SAGA_OK) return s;
+    const bool bf16 = dtype == SAGA_BF16;
+    const int64_t ss = saga::score_stride(S_max);
+    clear_stale_error();
+    // the exact top-N step, with per-chunk softmax statistics for tau
+    const saga::TopmOut tm{w.cand, w.cand_meta, N, w.cand_stat};
+    s = from_hip(saga::launch_kscan_topm(q, k_cache, seq_lens, tm, B, h_q, h_k, d, S_max, bf16,
+                                         stream), "kscan_topm");
+    if (s != SAGA_OK) return s;
+    s = from_hip(saga::launch_select_union(tm, seq_lens, B, h_q, h_k, d, N, S_max, w.sel_idx,
+                                           w.sel_val, w.row_max, w.row_cnt, idx_out, w.row_flag,
+                                           q, k_cache, w.scores, ss, bf16, stream),
+                 "select_union");
+    if (s != SAGA_OK) return s;
+    s = from_hip(saga::launch_atopn_tau(w.sel_val, w.row_cnt, tm, seq_lens, B, h_q, N, S_max,
+                                        tau, stream), "atopn_tau");
+    if (s != SAGA_OK) return s;
+    return from_hip(saga::launch_pv_sparse(v_cache, w.sel_idx, w.sel_val, w.row_max, w.row_cnt,
+                                           out, B, h_q, h_v, d, N, S_max, bf16, stream),
+                    "pv_sparse");
+}
+
+saga_status saga_atopn_attn(const void* q, const void* k_cache, const void* v_cache,
+                            const int32_t* seq_lens, float* out, int B, int h_q, int h_k,
+                            int h_v, int d, int N, hipStream_t stream, int64_t S_max,
+                            saga_dtype dtype, void* workspace, size_t workspace_bytes,
+                            const float* tau, int32_t* idx_out, int32_t* count_out) {
+    saga::Workspace w;
+    saga_status s = atopn_prepare(q, k_cache, v_cache, seq_lens, out, B, h_q, h_k, h_v, d, N,
+                                  S_max, dtype, workspace, workspace_bytes, tau, w);
+    if (s != SAGA_OK) return s;
+    const bool bf16 = dtype == SAGA_BF16;
+    const int64_t ss = saga::score_stride(S_max);
+    const int cap = 2 * N;
+    clear_stale_error();
+    // candidate lists sized for up to 2N kept positions, with chunk statistics
+    const saga::TopmOut tm{w.cand, w.cand_meta, cap, w.cand_stat};
+    s = from_hip(saga::launch_kscan_topm(q, k_cache, seq_lens, tm, B, h_q, h_k, d, S_max, bf16,
+                                         stream), "kscan_topm");
+    if (s != SAGA_OK) return s;
+    s = from_hip(saga::launch_select_thresh(tm, seq_lens, tau, B, h_q, h_k, d, cap, S_max,
+                                            w.sel_idx, w.sel_val, w.row_max, w.row_cnt, idx_out,
+                                            count_out, w.row_flag, q, k_cache, w.scores, ss,
+                                            bf16, stream),
+                 "select_thresh");
+    if (s != SAGA_OK) return s;
+    return from_hip(saga::launch_pv_sparse(v_cache, w.sel_idx, w.sel_val, w.row_max, w.row_cnt,
+                                           out, B, h_q, h_v, d, cap, S_max, bf16, stream),
+                    "pv_sparse");
 }
 
 saga_status saga_debug_scores(const void* q, const void* k_cache, const int32_t* seq_lens,

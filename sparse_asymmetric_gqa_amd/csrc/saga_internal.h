@@ -24,6 +24,7 @@ struct Workspace {
     float* scores;      // [B][h_q][score_stride]  logits (decode: wide key groups, fallback rows)
     uint2* cand;        // candidate pool: B*h_k*nchunk items x g*kScanChunk entries
     uint4* cand_meta;   // [B][h_q][nchunk]  {pool offset lo, count, cutoff, pool offset hi}
+    float2* cand_stat;  // [B][h_q][nchunk]  {max logit, sum exp(logit - max)} (Atop-N)
     int32_t* row_flag;  // [B][h_q]   1 if the row took the dense fallback in the last call
     int32_t* sel_idx;   // [B][h_q][N]
     float* sel_val;     // [B][h_q][N]
@@ -58,7 +59,8 @@ int dense_nsplit(int64_t S_max, int g);   // ceil(S_max / dense_chunk(g))
 struct TopmOut {
     uint2* cand;
     uint4* meta;       // [B*h_q][nchunk]
-    int N;
+    int N;             // the M of each chunk's list is sized for this N
+    float2* stat;      // nullable: [B*h_q][nchunk] {max logit, sum of exp(logit - max)}
 };
 
 // ---- launchers (defined next to their kernels) ------------------------------
@@ -82,6 +84,22 @@ hipError_t launch_select_union(const TopmOut& tm, const int32_t* lens, int B, in
                                float* row_max, int32_t* row_cnt, int32_t* idx_out,
                                int32_t* row_flag, const void* q, const void* k, float* scores,
                                int64_t s_stride, bool bf16, hipStream_t st);
+
+// Atop-N stale-threshold selection (lists from launch_kscan_topm with stat):
+// keeps the positions with logit >= log(tau) + LSE, the first cap in position
+// order, into sel_idx / sel_val [B*h_q][cap]; count_out (nullable) gets the
+// count before the cap.
+hipError_t launch_select_thresh(const TopmOut& tm, const int32_t* lens, const float* tau, int B,
+                                int h_q, int h_k, int d, int cap, int64_t S_max, int32_t* sel_idx,
+                                float* sel_val, float* row_max, int32_t* row_cnt,
+                                int32_t* idx_out, int32_t* count_out, int32_t* row_flag,
+                                const void* q, const void* k, float* scores, int64_t s_stride,
+                                bool bf16, hipStream_t st);
+
+// Atop-N calibration after an exact top-N select: tau = exp(T - LSE) per row.
+hipError_t launch_atopn_tau(const float* sel_val, const int32_t* row_cnt, const TopmOut& tm,
+                            const int32_t* lens, int B, int h_q, int N, int64_t S_max, float* tau,
+                            hipStream_t st);
 
 hipError_t launch_pv_sparse(const void* v, const int32_t* sel_idx, const float* sel_val,
                             const float* row_max, const int32_t* row_cnt, float* out, int B,

@@ -782,6 +782,279 @@ __global__ __launch_bounds__(kUnionThreads, 4) void select_union(
     }
 }
 
+// ---- Atop-N: stale-threshold selection and calibration ---------------------------
+// "More Value per Key" §3.1 and App. C.1: a calibration step keeps, per
+// head, the N-th largest attention probability tau; later steps keep every
+// position whose probability reaches tau -- logit z >= log(tau) + LSE(z), the
+// log-sum-exp of the row's logits -- at most 2N of them (the first 2N in
+// position order here), and attend over those.
+
+// LSE of a row from its chunks' {max, sum exp(z - max)}: M + log sum_c s_c
+// e^(m_c - M), M = max_c m_c. Also the largest chunk cutoff. Uniform results.
+struct RowStats {
+    float M, lse;
+    uint32_t maxcut;
+};
+__device__ inline RowStats row_stats(const float2* __restrict__ stat, const uint4* __restrict__ meta,
+                                     int nch, uint4* red, float* redf) {
+    constexpr int NT = kUnionThreads;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    uint32_t km = 0, cm = 0;
+    for (int c = tid; c < nch; c += NT) {
+        const uint32_t kx = float_key(stat[c].x);
+        km = kx > km ? kx : km;
+        const uint32_t cu = meta[c].z;
+        cm = cu > cm ? cu : cm;
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        const uint32_t y = (uint32_t)__shfl_xor((int)km, o, 64);
+        const uint32_t z = (uint32_t)__shfl_xor((int)cm, o, 64);
+        km = y > km ? y : km;
+        cm = z > cm ? z : cm;
+    }
+    if (lane == 0) red[wave] = make_uint4(km, cm, 0u, 0u);
+    __syncthreads();
+    km = 0;
+    cm = 0;
+#pragma unroll
+    for (int w = 0; w < NT / 64; ++w) {
+        km = red[w].x > km ? red[w].x : km;
+        cm = red[w].y > cm ? red[w].y : cm;
+    }
+    RowStats r;
+    r.M = key_float(km);
+    r.maxcut = cm;
+    float se = 0.f;
+    for (int c = tid; c < nch; c += NT) {
+        const float2 st = stat[c];
+        se += st.y * __expf(st.x - r.M);
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) se += __shfl_xor(se, o, 64);
+    if (lane == 0) redf[wave] = se;
+    __syncthreads();
+    float S = 0.f;
+#pragma unroll
+    for (int w = 0; w < NT / 64; ++w) S += redf[w];
+    r.lse = r.M + __logf(S);
+    return r;
+}
+
+struct ThreshShared {
+    uint4 red[kUnionThreads / 64];
+    float redf[kUnionThreads / 64];
+    uint32_t scan[kUnionThreads / 64];
+};
+__host__ __device__ constexpr size_t thresh_stage_offset() {
+    return (sizeof(ThreshShared) + 15) & ~(size_t)15;
+}
+
+// Stale-threshold selection, one workgroup per (b, i) row. cap = 2N output
+// slots per row. Fast path: the row's chunk lists are complete for the
+// threshold (every chunk cutoff <= theta: every key a chunk left out is below
+// its cutoff), at most 256 chunks, and runs of at most KPT entries per
+// thread (the layout of select_union); keys >= theta are counted, slotted by
+// one workgroup prefix scan (position order) and the first cap written.
+// Otherwise the head's logits are recomputed over all L positions and the
+// same rule applied to them (row_flag = 1). count_out = positions reaching
+// the threshold before the cap; a row keeping none gets row_cnt = 0.
+// Dynamic LDS: max(sizeof(UnionShared), thresh_stage_offset() + 8 cap4).
+template <typename T, int DH, int KPT>
+__global__ __launch_bounds__(kUnionThreads, 4) void select_thresh(
+    const uint2* __restrict__ cand, const uint4* __restrict__ cand_meta,
+    const float2* __restrict__ cand_stat, const int32_t* __restrict__ lens,
+    const float* __restrict__ tau, int h_q, int h_k, int cap, int cap4, int64_t S_max,
+    int nchunk, int32_t* __restrict__ sel_idx, float* __restrict__ sel_val,
+    float* __restrict__ row_max, int32_t* __restrict__ row_cnt, int32_t* __restrict__ idx_out,
+    int32_t* __restrict__ count_out, int32_t* __restrict__ row_flag, const T* __restrict__ q,
+    const T* __restrict__ k, float* __restrict__ scores, int64_t s_stride, float scale) {
+    static_assert(KPT % 2 == 0, "entries are loaded in pairs");
+    constexpr int NT = kUnionThreads;
+    extern __shared__ __attribute__((aligned(16))) unsigned char thr_lds[];
+    ThreshShared& F = *reinterpret_cast<ThreshShared*>(thr_lds);
+    UnionShared& U = *reinterpret_cast<UnionShared*>(thr_lds);
+    const int row = blockIdx.x;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int b = row / h_q;
+    const int64_t L = clamp_len(lens[b], S_max);
+    const int nch = (int)((L + kScanChunk - 1) / kScanChunk);
+    int32_t* oi = sel_idx + (int64_t)row * cap;
+    float* ov = sel_val + (int64_t)row * cap;
+    int32_t* ou = idx_out ? idx_out + (int64_t)row * cap : nullptr;
+    auto finish = [&](int64_t total, float mx, int flag) {   // padding and row records
+        const int kept = (int)(total < cap ? total : cap);
+        for (int j = kept + tid; j < cap; j += NT) {
+            oi[j] = -1;
+            ov[j] = -__builtin_inff();
+            if (ou) ou[j] = -1;
+        }
+        if (tid == 0) {
+            row_max[row] = mx;
+            row_cnt[row] = kept;
+            if (count_out) count_out[row] = (int32_t)(total < 0x7FFFFFFF ? total : 0x7FFFFFFF);
+            row_flag[row] = flag;
+        }
+    };
+    if (L == 0) {
+        finish(0, -__builtin_inff(), 0);
+        return;
+    }
+    const uint4* meta = cand_meta + (int64_t)row * nchunk;
+    const RowStats rs = row_stats(cand_stat + (int64_t)row * nchunk, meta, nch, F.red, F.redf);
+    const float t = tau[row];
+    // theta = log(tau) + LSE; tau = 0 keeps every position, NaN keeps none
+    const float theta = t == t ? __logf(t) + rs.lse : __builtin_inff();
+    const uint32_t tk = float_key(theta);
+    const uint32_t lo = tk > 1u ? tk : 1u;   // key 0 marks an empty slot
+    const bool complete = rs.maxcut <= tk;
+    // this thread's run of its chunk's list (as in select_union)
+    const bool fast_shape = complete && nch <= NT;
+    uint32_t key[KPT];
+    int32_t pos[KPT];
+    uint32_t ovf = 0;
+    if (fast_shape) {   // uniform
+        const int tpc = NT / nch;
+        const int c = tid / tpc;
+        const int sub = tid - c * tpc;
+        const bool cv = c < nch;
+        const uint4 m = meta[cv ? c : nch - 1];
+        const uint32_t cnt = cv ? m.y : 0u;
+        const uint32_t P = (((cnt + (uint32_t)tpc - 1u) / (uint32_t)tpc) + 1u) & ~1u;
+        const uint32_t j0 = (uint32_t)sub * P;
+        const uint32_t mine = cnt > j0 ? (cnt - j0 < P ? cnt - j0 : P) : 0u;
+        const uint32_t npair = (mine + 1u) >> 1;
+        const uint4* run = reinterpret_cast<const uint4*>(cand + ((((uint64_t)m.w << 32) | m.x) + j0));
+        uint4 ev[KPT / 2];
+#pragma unroll
+        for (int p2 = 0; p2 < KPT / 2; ++p2) {
+            const uint4* a = npair ? run + ((uint32_t)p2 < npair ? (uint32_t)p2 : npair - 1u)
+                                   : reinterpret_cast<const uint4*>(cand);
+            ev[p2] = *a;
+        }
+#pragma unroll
+        for (int e = 0; e < KPT; ++e) {
+            const uint4 x = ev[e >> 1];
+            pos[e] = (int32_t)((e & 1) ? x.z : x.x);
+            key[e] = (uint32_t)e < mine ? ((e & 1) ? x.w : x.y) : 0u;
+        }
+        ovf = P > (uint32_t)KPT ? 1u : 0u;
+    }
+    // uniform: is the fast path usable (no thread's run overflows)?
+    const uint32_t any_ovf = __syncthreads_or((int)ovf);
+    if (fast_shape && !any_ovf) {
+        uint32_t ng = 0;
+#pragma unroll
+        for (int e = 0; e < KPT; ++e) ng += key[e] >= lo ? 1u : 0u;
+        uint32_t wt;
+        const uint32_t incl = wave_incl_scan(ng, wt);
+        if (lane == 0) F.scan[wave] = wt;
+        __syncthreads();
+        uint32_t before = incl - ng, total = 0;
+#pragma unroll
+        for (int w = 0; w < NT / 64; ++w) {
+            before += w < wave ? F.scan[w] : 0u;
+            total += F.scan[w];
+        }
+        int32_t* st_idx = reinterpret_cast<int32_t*>(thr_lds + thresh_stage_offset());
+        float* st_val = reinterpret_cast<float*>(st_idx + cap4);
+        uint32_t slot = before;
+#pragma unroll
+        for (int e = 0; e < KPT; ++e) {
+            const bool keep = key[e] >= lo;
+            if (keep && slot < (uint32_t)cap) {
+                st_idx[slot] = pos[e];
+                st_val[slot] = key_float(key[e]);
+            }
+            slot += keep ? 1u : 0u;
+        }
+        __syncthreads();
+        const int kept = (int)(total < (uint32_t)cap ? total : (uint32_t)cap);
+        for (int j = tid; j < kept; j += NT) {
+            oi[j] = st_idx[j];
+            ov[j] = st_val[j];
+            if (ou) ou[j] = st_idx[j];
+        }
+        finish(total, rs.M, 0);
+        return;
+    }
+    // general: the head's logits over all L positions, then the same rule
+    __syncthreads();
+    constexpr int KG = kUnionKPT;
+    constexpr int NW = NT / 64;
+    SelShared& sh = U.sh;
+    const int i = row - b * h_q;
+    float* srow = scores + (int64_t)row * s_stride;
+    head_logits<T, DH>(q, k, b, i, h_q, h_k, S_max, L, scale, srow,
+                       reinterpret_cast<float*>(sh.hist));
+    using Src = DenseSrc<KG, NW>;
+    const Src src{srow, L};
+    const int ntiles = (int)((L + Src::CAP - 1) / Src::CAP);
+    uint32_t gk[KG];
+    int32_t gp[KG];
+    int64_t total = 0;
+#pragma unroll 1
+    for (int tile = 0; tile < ntiles; ++tile) {
+        src.load(tile, gk, gp);
+        uint32_t c = 0;
+#pragma unroll
+        for (int e = 0; e < KG; ++e) c += gk[e] >= lo ? 1u : 0u;
+        c = wave_sum(c);
+        if (lane == 0) sh.wtot[wave] = c;
+        __syncthreads();
+#pragma unroll
+        for (int w = 0; w < NW; ++w) total += sh.wtot[w];
+        __syncthreads();
+    }
+    // keys > lo - 1 = keys >= lo, first cap in position order
+    compact<NT, KG>(src, ntiles, lo - 1u, 0u, (uint32_t)cap, gk, gp, sh, oi, ov, ou);
+    __syncthreads();
+    finish(total, rs.M, 1);
+}
+
+// Calibration: tau = exp(T - LSE) per row, T = the smallest kept logit of the
+// exact top-N step (its N_eff-th largest), LSE from the chunk statistics.
+// Rows with nothing kept get NaN.
+__global__ __launch_bounds__(kUnionThreads) void atopn_tau(
+    const float* __restrict__ sel_val, const int32_t* __restrict__ row_cnt,
+    const float2* __restrict__ cand_stat, const uint4* __restrict__ cand_meta,
+    const int32_t* __restrict__ lens, int h_q, int N, int64_t S_max, int nchunk,
+    float* __restrict__ tau) {
+    __shared__ ThreshShared F;
+    const int row = blockIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int cnt = row_cnt[row];
+    const int64_t L = clamp_len(lens[row / h_q], S_max);
+    if (cnt <= 0 || L == 0) {   // uniform
+        if (tid == 0) tau[row] = __builtin_nanf("");
+        return;
+    }
+    const int nch = (int)((L + kScanChunk - 1) / kScanChunk);
+    const RowStats rs = row_stats(cand_stat + (int64_t)row * nchunk, cand_meta + (int64_t)row * nchunk,
+                                  nch, F.red, F.redf);
+    uint32_t mk = 0xFFFFFFFFu;   // smallest kept key
+    for (int j = tid; j < cnt; j += kUnionThreads) {
+        const uint32_t kx = float_key(sel_val[(int64_t)row * N + j]);
+        mk = kx < mk ? kx : mk;
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        const uint32_t y = (uint32_t)__shfl_xor((int)mk, o, 64);
+        mk = y < mk ? y : mk;
+    }
+    if (lane == 0) F.scan[wave] = mk;
+    __syncthreads();
+    if (tid == 0) {
+#pragma unroll
+        for (int w = 0; w < kUnionThreads / 64; ++w) mk = F.scan[w] < mk ? F.scan[w] : mk;
+        tau[row] = __expf(key_float(mk) - rs.lse);
+    }
+}
+
 template <int KPT>
 hipError_t go_dense(const float* scores, int64_t s_stride, const int32_t* lens, int B, int h_q,
                     int N, int64_t S_max, int32_t* sel_idx, float* sel_val, float* row_max,
@@ -853,6 +1126,61 @@ hipError_t launch_select_union(const TopmOut& tm, const int32_t* lens, int B, in
     }
 #undef SAGA_SU_K
 #undef SAGA_SU
+    return hipGetLastError();
+}
+
+hipError_t launch_select_thresh(const TopmOut& tm, const int32_t* lens, const float* tau, int B,
+                                int h_q, int h_k, int d, int cap, int64_t S_max, int32_t* sel_idx,
+                                float* sel_val, float* row_max, int32_t* row_cnt,
+                                int32_t* idx_out, int32_t* count_out, int32_t* row_flag,
+                                const void* q, const void* k, float* scores, int64_t s_stride,
+                                bool bf16, hipStream_t st) {
+    const int nchunk = (int)((S_max + kScanChunk - 1) / kScanChunk);
+    const int rows = B * h_q;
+    const float scale = (float)(1.0 / __builtin_sqrt((double)d));
+    // registers per thread: as for the union select, the lists sized for tm.N
+    const double share = (double)tm.N * kScanChunk / (double)S_max;
+    int64_t per_chunk = (int64_t)(1.25 * (1.5 * share + 16.0)) + 1;
+    per_chunk = per_chunk < kScanChunk ? per_chunk : kScanChunk;
+    const int64_t tpc = nchunk <= kUnionThreads ? kUnionThreads / nchunk : 1;
+    const int64_t slots = (((per_chunk + tpc - 1) / tpc) + 1) & ~(int64_t)1;
+    const int cap4 = (cap + 3) & ~3;
+    size_t lds = thresh_stage_offset() + (size_t)cap4 * 8;
+    lds = lds > sizeof(UnionShared) ? lds : sizeof(UnionShared);
+#define SAGA_ST(T, D, KPT)                                                                       \
+    {                                                                                            \
+        auto kern = &select_thresh<T, D, KPT>;                                                   \
+        if (lds > 64 * 1024) {                                                                   \
+            const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),        \
+                                                     hipFuncAttributeMaxDynamicSharedMemorySize, \
+                                                     (int)lds);                                  \
+            if (e != hipSuccess) return e;                                                       \
+        }                                                                                        \
+        hipLaunchKernelGGL(kern, dim3((unsigned)rows), dim3(kUnionThreads), (unsigned)lds, st,   \
+                           tm.cand, tm.meta, tm.stat, lens, tau, h_q, h_k, cap, cap4, S_max,     \
+                           nchunk, sel_idx, sel_val, row_max, row_cnt, idx_out, count_out,       \
+                           row_flag, (const T*)q, (const T*)k, scores, s_stride, scale);         \
+    }
+#define SAGA_ST_K(T, D)                                                                          \
+    if (slots <= 8) SAGA_ST(T, D, 8)                                                             \
+    else if (slots <= 16) SAGA_ST(T, D, 16)                                                      \
+    else SAGA_ST(T, D, 32)
+    if (bf16) {
+        if (d == 64) { SAGA_ST_K(uint16_t, 64) } else { SAGA_ST_K(uint16_t, 128) }
+    } else {
+        if (d == 64) { SAGA_ST_K(float, 64) } else { SAGA_ST_K(float, 128) }
+    }
+#undef SAGA_ST_K
+#undef SAGA_ST
+    return hipGetLastError();
+}
+
+hipError_t launch_atopn_tau(const float* sel_val, const int32_t* row_cnt, const TopmOut& tm,
+                            const int32_t* lens, int B, int h_q, int N, int64_t S_max, float* tau,
+                            hipStream_t st) {
+    const int nchunk = (int)((S_max + kScanChunk - 1) / kScanChunk);
+    hipLaunchKernelGGL(atopn_tau, dim3((unsigned)(B * h_q)), dim3(kUnionThreads), 0, st, sel_val,
+                       row_cnt, tm.stat, tm.meta, lens, h_q, N, S_max, nchunk, tau);
     return hipGetLastError();
 }
 

@@ -112,3 +112,46 @@ def debug_scores(q, k_cache, seq_lens, *, out=None, stream=None):
     if st != C.SAGA_OK:
         raise C.SagaError(st, "saga_debug_scores")
     return out
+
+
+def atopn_workspace_size(q, k_cache, v_cache, seq_lens, N) -> int:
+    B, h_q, h_k, h_v, d, S = _shapes(q, k_cache, v_cache, seq_lens)
+    return C.saga_atopn_workspace_size(B, h_q, h_k, h_v, d, N, S, _dtype_code(q))
+
+
+def atopn_calibrate(q, k_cache, v_cache, seq_lens, N, *, tau=None, out=None, workspace=None,
+                    idx_out=None, stream=None):
+    """Atop-N calibration step: the exact top-N step; returns (out, tau [B][h_q] float32)."""
+    B, h_q, h_k, h_v, d, S = _shapes(q, k_cache, v_cache, seq_lens)
+    dt = _dtype_code(q)
+    if workspace is None:
+        workspace = new_workspace(C.saga_atopn_workspace_size(B, h_q, h_k, h_v, d, N, S, dt),
+                                  q.device)
+    if out is None:
+        out = torch.empty((B, h_q, d), dtype=torch.float32, device=q.device)
+    if tau is None:
+        tau = torch.empty((B, h_q), dtype=torch.float32, device=q.device)
+    st = C.saga_atopn_calibrate(q, k_cache, v_cache, seq_lens, out, B, h_q, h_k, h_v, d, N,
+                                _stream(stream), S, dt, workspace, workspace.numel(), tau,
+                                idx_out)
+    if st != C.SAGA_OK:
+        raise C.SagaError(st, "saga_atopn_calibrate")
+    return out, tau
+
+
+def atopn_attn(q, k_cache, v_cache, seq_lens, N, tau, *, out=None, workspace=None, idx_out=None,
+               count_out=None, stream=None):
+    """Atop-N step with the stale thresholds tau [B][h_q]; returns out."""
+    B, h_q, h_k, h_v, d, S = _shapes(q, k_cache, v_cache, seq_lens)
+    dt = _dtype_code(q)
+    if workspace is None:
+        workspace = new_workspace(C.saga_atopn_workspace_size(B, h_q, h_k, h_v, d, N, S, dt),
+                                  q.device)
+    if out is None:
+        out = torch.empty((B, h_q, d), dtype=torch.float32, device=q.device)
+    st = C.saga_atopn_attn(q, k_cache, v_cache, seq_lens, out, B, h_q, h_k, h_v, d, N,
+                           _stream(stream), S, dt, workspace, workspace.numel(), tau, idx_out,
+                           count_out)
+    if st != C.SAGA_OK:
+        raise C.SagaError(st, "saga_atopn_attn")
+    return out

@@ -122,3 +122,40 @@ def test_timed_entry_rejects_bad_event_lists_on_host():
     bad = list(args)
     bad[5] = 0                                                   # B = 0, checked before events
     assert t(*bad, []) == saga.SAGA_ERR_INVALID_ARG
+
+
+def _atopn(fn, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, lens=FAKE, out=FAKE, B=2, h_q=8, h_k=2, h_v=4, d=64, N=16,
+             stream=None, S=100, dt=saga.SAGA_BF16, ws=FAKE * 16, wsb=1 << 40, tau=FAKE)
+    a.update(kw)
+    args = (a["q"], a["k"], a["v"], a["lens"], a["out"], a["B"], a["h_q"], a["h_k"], a["h_v"],
+            a["d"], a["N"], a["stream"], a["S"], a["dt"], a["ws"], a["wsb"], a["tau"])
+    return fn(*args)
+
+
+@pytest.mark.parametrize("fn", ["saga_atopn_calibrate", "saga_atopn_attn"])
+@pytest.mark.parametrize("kw,code", [
+    (dict(tau=None), saga.SAGA_ERR_INVALID_ARG),
+    (dict(q=None), saga.SAGA_ERR_INVALID_ARG),
+    (dict(out=None), saga.SAGA_ERR_INVALID_ARG),
+    (dict(N=0), saga.SAGA_ERR_INVALID_ARG),
+    (dict(h_k=8, h_v=4), saga.SAGA_ERR_INVALID_ARG),
+    (dict(q=FAKE + 2), saga.SAGA_ERR_INVALID_ARG),
+    (dict(d=96), saga.SAGA_ERR_UNSUPPORTED),
+    (dict(h_q=64, h_k=2, h_v=4), saga.SAGA_ERR_UNSUPPORTED),     # key group of 32
+    (dict(S=600000), saga.SAGA_ERR_UNSUPPORTED),                  # > 512 chunks
+    (dict(ws=None), saga.SAGA_ERR_WORKSPACE),
+    (dict(wsb=1024), saga.SAGA_ERR_WORKSPACE),
+])
+def test_atopn_rejects_bad_arguments_on_host(fn, kw, code):
+    assert _atopn(getattr(saga, fn), **kw) == code
+
+
+def test_atopn_workspace_holds_2N_slots():
+    aw, ws = saga.saga_atopn_workspace_size, saga.saga_workspace_size
+    for args in [(64, 12, 1, 2, 128, 1024, 32768, 1), (3, 6, 2, 2, 128, 7, 33, 1)]:
+        B, h_q, h_k, h_v, d, N, S, dt = args
+        n = aw(*args)
+        assert n % 256 == 0 and n >= ws(*args)
+        assert n >= ws(B, h_q, h_k, h_v, d, 2 * N, S, dt) - 256
+    assert aw(1, 4, 1, 2, 72, 10, 100, 1) == 0 and aw(1, 4, 1, 2, 64, 0, 100, 1) == 0
