@@ -89,11 +89,6 @@ __device__ inline float wave_fmax(float x) {
     for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, 64));
     return x;
 }
-__device__ inline float wave_fsum(float x) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, 64);
-    return x;
-}
 
 template <typename T, int DH, int NHT>
 __global__ __launch_bounds__(kDenseThreads) void dense_attn(

@@ -176,17 +176,11 @@ __device__ inline void extract(const Item<T>& it, int n, uint32_t M, uint32_t* r
         uint32_t kx = 0;
 #pragma unroll
         for (int e = 0; e < 16; ++e) kx = kk[e] > kx ? kk[e] : kx;
-#pragma unroll
-        for (int o = 32; o > 0; o >>= 1) {
-            const uint32_t y = (uint32_t)__shfl_xor((int)kx, o, 64);
-            kx = y > kx ? y : kx;
-        }
-        const float mx = key_float(kx);
+        const float mx = key_float(wave_umax(kx));
         float se = 0.f;
 #pragma unroll
         for (int e = 0; e < 16; ++e) se += kk[e] != 0u ? __expf(key_float(kk[e]) - mx) : 0.f;
-#pragma unroll
-        for (int o = 32; o > 0; o >>= 1) se += __shfl_xor(se, o, 64);
+        se = wave_fsum(se);
         if (lane == 0)
             tm.stat[(int64_t)(it.b * h_q + it.kh * g + n) * nchunk + it.chunk] = make_float2(mx, se);
     }

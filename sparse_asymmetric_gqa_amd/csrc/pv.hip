@@ -5,7 +5,7 @@
 // query head uses value head i / (h_q / h_v) (§3.2, App. B Eq. 29).
 //
 // One workgroup per (b, i) row, walking its kept list in blocks of
-// kPvEntries (a whole list of N <= 1024 is one block). Per block its 256
+// kPvEntries (a whole list of up to 2048 is one block). Per block its 256
 // threads stage positions and weights exp(s - m) in LDS (m = the row's
 // largest kept logit), then every wave streams its share of value rows with
 // 16-byte loads, LPR lanes per row, in batches of 8 rows per lane that are

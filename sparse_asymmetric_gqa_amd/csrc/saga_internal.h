@@ -11,7 +11,7 @@ namespace saga {
 #define SAGA_KSCAN_CHUNK 1024
 #endif
 constexpr int kScanChunk = SAGA_KSCAN_CHUNK;   // positions per K-scan workgroup
-constexpr int kPvEntries = 1024;     // kept entries staged per block of the sparse PV
+constexpr int kPvEntries = 2048;     // kept entries staged per block of the sparse PV
 constexpr int kSelectThreads = 1024; // threads of one select workgroup
 constexpr int kMaxHeadGroup = 64;    // largest h_q / h_k and h_q / h_v supported
 
@@ -200,6 +200,37 @@ template <> struct Row16<float> {
         for (int c = 0; c < 4; ++c) f[c] = __uint_as_float(r[c]);
     }
 };
+
+// Maximum over the wave of an unsigned value (uniform result). DPP row
+// shifts build each 16-lane row's running maximum; lanes without a source
+// keep 0, the identity.
+__device__ inline uint32_t wave_umax(uint32_t v) {
+    // lanes without a source keep 0, the identity of an unsigned maximum
+    int x = (int)v, y;
+    y = __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, false); x = (uint32_t)y > (uint32_t)x ? y : x;
+    y = __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, false); x = (uint32_t)y > (uint32_t)x ? y : x;
+    y = __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, false); x = (uint32_t)y > (uint32_t)x ? y : x;
+    y = __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, false); x = (uint32_t)y > (uint32_t)x ? y : x;
+    uint32_t r = (uint32_t)__builtin_amdgcn_readlane(x, 15);
+    uint32_t t = (uint32_t)__builtin_amdgcn_readlane(x, 31); r = t > r ? t : r;
+    t = (uint32_t)__builtin_amdgcn_readlane(x, 47); r = t > r ? t : r;
+    t = (uint32_t)__builtin_amdgcn_readlane(x, 63); r = t > r ? t : r;
+    return r;
+}
+
+// Sum over the wave of a float (uniform result; same DPP pattern, +0.0 for
+// lanes without a source).
+__device__ inline float wave_fsum(float v) {
+    float x = v;
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x111, 0xf, 0xf, false));
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x112, 0xf, 0xf, false));
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x114, 0xf, 0xf, false));
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x118, 0xf, 0xf, false));
+    return (__int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 15)) +
+            __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 31))) +
+           (__int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 47)) +
+            __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 63)));
+}
 
 }  // namespace dev
 }  // namespace saga

@@ -566,19 +566,6 @@ __host__ __device__ constexpr size_t select_stage_offset() {
     return (sizeof(FastShared) + 15) & ~(size_t)15;
 }
 
-__device__ inline uint32_t wave_umax(uint32_t v) {
-    // lanes without a source keep 0, the identity of an unsigned maximum
-    int x = (int)v, y;
-    y = __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, false); x = (uint32_t)y > (uint32_t)x ? y : x;
-    y = __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, false); x = (uint32_t)y > (uint32_t)x ? y : x;
-    y = __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, false); x = (uint32_t)y > (uint32_t)x ? y : x;
-    y = __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, false); x = (uint32_t)y > (uint32_t)x ? y : x;
-    uint32_t r = (uint32_t)__builtin_amdgcn_readlane(x, 15);
-    uint32_t t = (uint32_t)__builtin_amdgcn_readlane(x, 31); r = t > r ? t : r;
-    t = (uint32_t)__builtin_amdgcn_readlane(x, 47); r = t > r ? t : r;
-    t = (uint32_t)__builtin_amdgcn_readlane(x, 63); r = t > r ? t : r;
-    return r;
-}
 
 // Four workgroups per CU (<= 128 VGPRs): the general code spills at this
 // bound, which only costs the rare rows that need it. Dynamic LDS:
@@ -904,24 +891,18 @@ __global__ __launch_bounds__(kUnionThreads, 4) void select_thresh(
         return;
     }
     const uint4* meta = cand_meta + (int64_t)row * nchunk;
-    const RowStats rs = row_stats(cand_stat + (int64_t)row * nchunk, meta, nch, F.red, F.redf);
+    const float2* stat = cand_stat + (int64_t)row * nchunk;
     const float t = tau[row];
-    // theta = log(tau) + LSE; tau = 0 keeps every position, NaN keeps none
-    const float theta = t == t ? __logf(t) + rs.lse : __builtin_inff();
-    const uint32_t tk = float_key(theta);
-    const uint32_t lo = tk > 1u ? tk : 1u;   // key 0 marks an empty slot
-    const bool complete = rs.maxcut <= tk;
-    // this thread's run of its chunk's list (as in select_union)
-    const bool fast_shape = complete && nch <= NT;
-    uint32_t key[KPT];
-    int32_t pos[KPT];
-    uint32_t ovf = 0;
-    if (fast_shape) {   // uniform
+    if (nch <= NT) {
+        // Fast path, rows of at most 256 chunks: each thread's chunk record and
+        // statistics in one round, then its run of the chunk's list (as in
+        // select_union) requested before the reductions that give the LSE.
         const int tpc = NT / nch;
         const int c = tid / tpc;
         const int sub = tid - c * tpc;
         const bool cv = c < nch;
         const uint4 m = meta[cv ? c : nch - 1];
+        const float2 cs = stat[cv ? c : nch - 1];
         const uint32_t cnt = cv ? m.y : 0u;
         const uint32_t P = (((cnt + (uint32_t)tpc - 1u) / (uint32_t)tpc) + 1u) & ~1u;
         const uint32_t j0 = (uint32_t)sub * P;
@@ -935,52 +916,83 @@ __global__ __launch_bounds__(kUnionThreads, 4) void select_thresh(
                                    : reinterpret_cast<const uint4*>(cand);
             ev[p2] = *a;
         }
-#pragma unroll
-        for (int e = 0; e < KPT; ++e) {
-            const uint4 x = ev[e >> 1];
-            pos[e] = (int32_t)((e & 1) ? x.z : x.x);
-            key[e] = (uint32_t)e < mine ? ((e & 1) ? x.w : x.y) : 0u;
+        // max chunk logit, max cutoff and overflow over the workgroup
+        const bool lead = cv && sub == 0;
+        {
+            const uint32_t wk = wave_umax(lead ? float_key(cs.x) : 0u);
+            const uint32_t wc = wave_umax(lead ? m.z : 0u);
+            const uint32_t wo = wave_umax(P > (uint32_t)KPT ? 1u : 0u);
+            if (lane == 0) F.red[wave] = make_uint4(wk, wc, wo, 0u);
         }
-        ovf = P > (uint32_t)KPT ? 1u : 0u;
-    }
-    // uniform: is the fast path usable (no thread's run overflows)?
-    const uint32_t any_ovf = __syncthreads_or((int)ovf);
-    if (fast_shape && !any_ovf) {
-        uint32_t ng = 0;
-#pragma unroll
-        for (int e = 0; e < KPT; ++e) ng += key[e] >= lo ? 1u : 0u;
-        uint32_t wt;
-        const uint32_t incl = wave_incl_scan(ng, wt);
-        if (lane == 0) F.scan[wave] = wt;
         __syncthreads();
-        uint32_t before = incl - ng, total = 0;
+        uint32_t km = 0, maxcut = 0, ovf = 0;
 #pragma unroll
         for (int w = 0; w < NT / 64; ++w) {
-            before += w < wave ? F.scan[w] : 0u;
-            total += F.scan[w];
+            const uint4 r = F.red[w];
+            km = r.x > km ? r.x : km;
+            maxcut = r.y > maxcut ? r.y : maxcut;
+            ovf |= r.z;
         }
-        int32_t* st_idx = reinterpret_cast<int32_t*>(thr_lds + thresh_stage_offset());
-        float* st_val = reinterpret_cast<float*>(st_idx + cap4);
-        uint32_t slot = before;
-#pragma unroll
-        for (int e = 0; e < KPT; ++e) {
-            const bool keep = key[e] >= lo;
-            if (keep && slot < (uint32_t)cap) {
-                st_idx[slot] = pos[e];
-                st_val[slot] = key_float(key[e]);
-            }
-            slot += keep ? 1u : 0u;
+        const float M = key_float(km);
+        {
+            const float se = wave_fsum(lead ? cs.y * __expf(cs.x - M) : 0.f);
+            if (lane == 0) F.redf[wave] = se;
         }
         __syncthreads();
-        const int kept = (int)(total < (uint32_t)cap ? total : (uint32_t)cap);
-        for (int j = tid; j < kept; j += NT) {
-            oi[j] = st_idx[j];
-            ov[j] = st_val[j];
-            if (ou) ou[j] = st_idx[j];
+        float S = 0.f;
+#pragma unroll
+        for (int w = 0; w < NT / 64; ++w) S += F.redf[w];
+        // theta = log(tau) + LSE; tau = 0 keeps every position, NaN keeps none
+        const float theta = t == t ? __logf(t) + (M + __logf(S)) : __builtin_inff();
+        const uint32_t tk = float_key(theta);
+        const uint32_t lo = tk > 1u ? tk : 1u;   // key 0 marks an empty slot
+        if (ovf == 0u && maxcut <= tk) {   // uniform: lists fit and are complete for theta
+            uint32_t key[KPT];
+            int32_t pos[KPT];
+            uint32_t ng = 0;
+#pragma unroll
+            for (int e = 0; e < KPT; ++e) {
+                const uint4 x = ev[e >> 1];
+                pos[e] = (int32_t)((e & 1) ? x.z : x.x);
+                key[e] = (uint32_t)e < mine ? ((e & 1) ? x.w : x.y) : 0u;
+                ng += key[e] >= lo ? 1u : 0u;
+            }
+            uint32_t wt;
+            const uint32_t incl = wave_incl_scan(ng, wt);
+            if (lane == 0) F.scan[wave] = wt;
+            __syncthreads();
+            uint32_t before = incl - ng, total = 0;
+#pragma unroll
+            for (int w = 0; w < NT / 64; ++w) {
+                before += w < wave ? F.scan[w] : 0u;
+                total += F.scan[w];
+            }
+            int32_t* st_idx = reinterpret_cast<int32_t*>(thr_lds + thresh_stage_offset());
+            float* st_val = reinterpret_cast<float*>(st_idx + cap4);
+            uint32_t slot = before;
+#pragma unroll
+            for (int e = 0; e < KPT; ++e) {
+                const bool keep = key[e] >= lo;
+                if (keep && slot < (uint32_t)cap) {
+                    st_idx[slot] = pos[e];
+                    st_val[slot] = key_float(key[e]);
+                }
+                slot += keep ? 1u : 0u;
+            }
+            __syncthreads();
+            const int kept = (int)(total < (uint32_t)cap ? total : (uint32_t)cap);
+            for (int j = tid; j < kept; j += NT) {
+                oi[j] = st_idx[j];
+                ov[j] = st_val[j];
+                if (ou) ou[j] = st_idx[j];
+            }
+            finish(total, M, 0);
+            return;
         }
-        finish(total, rs.M, 0);
-        return;
     }
+    const RowStats rs = row_stats(stat, meta, nch, F.red, F.redf);
+    const float theta = t == t ? __logf(t) + rs.lse : __builtin_inff();
+    const uint32_t lo = float_key(theta) > 1u ? float_key(theta) : 1u;
     // general: the head's logits over all L positions, then the same rule
     __syncthreads();
     constexpr int KG = kUnionKPT;
