@@ -1,0 +1,160 @@
+#!/usr/bin/env python3
+"""Decode-attention latency grid on one MI355X, in the form of the pages'
+Table 7 ("More Value per Key", App.: decode speedup of the Qwen2.5-1.5B
+attention shape relative to GQA with full attention at the same batch size,
+N = 1024) at kernel level: one layer's attention step, no projections.
+
+Grid: batch B in {1, 4, 16} x context S in {8K, 16K, 32K, 64K, 128K} x
+  heads  GQA (h_k = h_v = 2) | SAGA (h_k = 1, h_v = 2), h_q = 12, d = 128, bf16
+  attn   full (saga_dense_attn) | exact top-N (saga_decode_attn, the
+         threshold fresh every step) | Atop-N (saga_atopn_*, one calibration
+         every 32 steps, the query drifting by 0.1 N(0,1) between them).
+Every row is full (L_b = S). Inputs are the seeded synthetic caches of
+synth/ (N(0,1) values, 1% heavy-hitter key rows); SAGA's key cache is the
+GQA cache's first key head. Each timing cycles through enough copies of the
+layer's caches to exceed 512 MB, so no call finds the previous call's data in
+the last-level cache. Prints one JSON line per cell and a table of per-step
+latency (us) and speedup over GQA full.
+
+Usage: python bench_grid.py [--steps K] [--batches 1,4,16] [--contexts 8192,...]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+ATOPN_EVERY = 32
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--steps", type=int, default=32)
+    ap.add_argument("--batches", default="1,4,16")
+    ap.add_argument("--contexts", default="8192,16384,32768,65536,131072")
+    args = ap.parse_args()
+
+    import numpy as np
+    import torch
+
+    import synth
+    import sparse_asymmetric_gqa_amd as saga
+    from sparse_asymmetric_gqa_amd import _binding as C
+
+    if not torch.cuda.is_available():
+        print("bench_grid.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+    h_q, d, N = 12, 128, 1024
+    dt = C.SAGA_BF16
+
+    def bf16_dev(a):
+        return torch.from_numpy(np.ascontiguousarray(a)).view(torch.bfloat16).to(dev)
+
+    def timed(fn, n):
+        for i in range(3):
+            fn(i)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(n):
+            fn(i)
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) * 1e6 / n
+
+    cells = []
+    for B in [int(v) for v in args.batches.split(",")]:
+        for S in [int(v) for v in args.contexts.split(",")]:
+            case = synth.Case(f"grid_b{B}_s{S}", B, h_q, 2, 2, d, S, N, "bf16", 1000 + B,
+                              "pct1", 3.0, False)
+            x = synth.make_inputs(case)
+            q = bf16_dev(x["q"])
+            rng = np.random.default_rng(B * 1000003 + S)
+            qd = bf16_dev(synth.f32_to_bf16_bits(
+                synth.as_f32(x["q"]) + np.float32(0.1) *
+                rng.standard_normal(x["q"].shape).astype(np.float32)))
+            k22 = bf16_dev(x["k"])
+            v = bf16_dev(x["v"])
+            lens = torch.from_numpy(x["seq_lens"]).to(dev)
+            del x
+            out = torch.empty((B, h_q, d), dtype=torch.float32, device=dev)
+            for heads, h_k in (("GQA", 2), ("SAGA", 1)):
+                k = k22 if h_k == 2 else k22[:, :1].contiguous()
+                layer_bytes = (k.numel() + v.numel()) * 2
+                copies = max(1, min(64, -(-(512 << 20) // layer_bytes)))
+                lay = [(k, v)] + [(k.clone(), v.clone()) for _ in range(copies - 1)]
+                dws_b = C.saga_dense_workspace_size(B, h_q, h_k, 2, d, S, dt)
+                ws_b = C.saga_atopn_workspace_size(B, h_q, h_k, 2, d, N, S, dt)
+                dws = saga.new_workspace(dws_b, dev)
+                ws = saga.new_workspace(ws_b, dev)
+                tau = torch.empty((B, h_q), dtype=torch.float32, device=dev)
+
+                def full(i):
+                    k_, v_ = lay[i % copies]
+                    st = C.saga_dense_attn(q, k_, v_, lens, out, B, h_q, h_k, 2, d, sh, S, dt,
+                                           dws, dws_b)
+                    assert st == C.SAGA_OK, st
+
+                def exact(i):
+                    k_, v_ = lay[i % copies]
+                    st = C.saga_decode_attn(q, k_, v_, lens, out, B, h_q, h_k, 2, d, N, sh, S,
+                                            dt, ws, ws_b)
+                    assert st == C.SAGA_OK, st
+
+                def atopn(i):
+                    k_, v_ = lay[i % copies]
+                    if i % ATOPN_EVERY == 0:
+                        st = C.saga_atopn_calibrate(q, k_, v_, lens, out, B, h_q, h_k, 2, d, N,
+                                                    sh, S, dt, ws, ws_b, tau)
+                    else:
+                        st = C.saga_atopn_attn(qd, k_, v_, lens, out, B, h_q, h_k, 2, d, N, sh,
+                                               S, dt, ws, ws_b, tau)
+                    assert st == C.SAGA_OK, st
+
+                n_at = max(args.steps, ATOPN_EVERY) // ATOPN_EVERY * ATOPN_EVERY
+                res = {"full": timed(full, args.steps), "exact_topN": timed(exact, args.steps)}
+                for i in range(3):
+                    atopn(i)
+                torch.cuda.synchronize()
+                t0 = time.perf_counter()
+                for i in range(n_at):
+                    atopn(i)
+                torch.cuda.synchronize()
+                res["atopn_n32"] = (time.perf_counter() - t0) * 1e6 / n_at
+                kv_bytes = (h_k + 2) * B * S * d * 2
+                for attn, us in res.items():
+                    cell = {"B": B, "S": S, "heads": heads, "h_k": h_k, "h_v": 2, "attn": attn,
+                            "us_per_step": round(us, 2), "layer_copies": copies,
+                            "full_kv_GBps": round(kv_bytes / (us * 1e-6) / 1e9, 1)}
+                    cells.append(cell)
+                    print(json.dumps(cell), flush=True)
+                del lay, dws, ws, k
+                torch.cuda.empty_cache()
+            del q, qd, k22, v, lens, out
+            torch.cuda.empty_cache()
+
+    # Table 7 layout: speedup over GQA full at the same batch size and context
+    ctxs = sorted({c["S"] for c in cells})
+    print("\nper-step latency (us) and speedup over GQA full at the same B and S", file=sys.stderr)
+    for B in sorted({c["B"] for c in cells}):
+        base = {c["S"]: c["us_per_step"] for c in cells
+                if c["B"] == B and c["heads"] == "GQA" and c["attn"] == "full"}
+        print(f"B={B:<3d} {'heads':5s} {'attn':11s} " +
+              " ".join(f"{s // 1024:>5d}K" for s in ctxs), file=sys.stderr)
+        for heads in ("GQA", "SAGA"):
+            for attn in ("full", "exact_topN", "atopn_n32"):
+                row = {c["S"]: c["us_per_step"] for c in cells
+                       if c["B"] == B and c["heads"] == heads and c["attn"] == attn}
+                print(f"      {heads:5s} {attn:11s} " +
+                      " ".join(f"{base[s] / row[s]:6.2f}" for s in ctxs) + "   (" +
+                      " ".join(f"{row[s]:.0f}" for s in ctxs) + " us)", file=sys.stderr)
+
+
+if __name__ == "__main__":
+    main()
