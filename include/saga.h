@@ -102,7 +102,9 @@ saga_status saga_decode_attn(const void* q, const void* k_cache, const void* v_c
  * per-chunk candidate extraction; on the top-M path both are stamped by that
  * dispatch itself, so 1 - 0 is the kernel's run time, without launch
  * latency), 2 after top-N selection, 3 after the value gather (the end of the
- * call). The events are created by the caller (timing enabled); a null event
+ * call). On the top-M path selection and gather are one dispatch, so 2 and 3
+ * are both recorded after it. The events are created by the caller (timing
+ * enabled); a null event
  * or n_events outside 0..4 gives SAGA_ERR_INVALID_ARG.
  */
 saga_status saga_decode_attn_timed(const void* q, const void* k_cache, const void* v_cache,

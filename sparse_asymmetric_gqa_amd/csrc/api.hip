@@ -138,11 +138,14 @@ saga_status decode(const void* q, const void* k_cache, const void* v_cache,
                                              pm.n > 1 ? pm.ev[1] : nullptr),
                      "kscan_topm");
         if (s != SAGA_OK) return s;
-        s = from_hip(saga::launch_select_union(tm, seq_lens, B, h_q, h_k, d, N, S_max,
-                                               w.sel_idx, w.sel_val, w.row_max, w.row_cnt,
-                                               idx_out, w.row_flag, q, k_cache, w.scores, ss,
-                                               bf16, stream), "select_union");
+        // selection and value gather in one dispatch: the kept lists stay in LDS
+        s = from_hip(saga::launch_select_pv(tm, seq_lens, B, h_q, h_k, h_v, d, N, S_max,
+                                            w.sel_idx, w.sel_val, w.row_max, w.row_cnt, idx_out,
+                                            w.row_flag, q, k_cache, v_cache, w.scores, ss, out,
+                                            bf16, stream), "select_pv");
         if (s != SAGA_OK) return s;
+        if ((s = pm.mark(2, stream)) != SAGA_OK) return s;
+        return pm.mark(3, stream);
     } else {
         if ((s = pm.mark(0, stream)) != SAGA_OK) return s;
         s = from_hip(saga::launch_kscan(q, k_cache, seq_lens, w.scores, ss, B, h_q, h_k, d,

@@ -7,14 +7,12 @@
 // One workgroup per (b, i) row, walking its kept list in blocks of
 // kPvEntries (a whole list of up to 2048 is one block). Per block its 256
 // threads stage positions and weights exp(s - m) in LDS (m = the row's
-// largest kept logit), then every wave streams its share of value rows with
-// 16-byte loads, LPR lanes per row, in batches of 8 rows per lane that are
-// double-buffered (the next batch is in flight while one is summed); the sums
-// stay in registers and the row ends with out = acc / l, so no merge pass is
+// largest kept logit), then stream the value rows (gather.h); the sums stay
+// in registers and the row ends with out = acc / l, so no merge pass is
 // needed. The g_v heads that
 // share a value head are mapped to the same XCD at neighbouring times so value
 // rows they have in common are served from that XCD's L2.
-#include "saga_internal.h"
+#include "gather.h"
 
 namespace saga {
 using namespace dev;
@@ -22,32 +20,19 @@ using namespace dev;
 namespace {
 
 constexpr int kPvThreads = 256;
-constexpr int kPvWaves = kPvThreads / 64;
 
-// logical workgroup id from the hardware one: hardware ids are dealt to the 8
-// XCDs round-robin, so give XCD x the contiguous logical range [x*Q, (x+1)*Q).
-__device__ inline int xcd_logical(int hw, int total) {
-    const int q = (total + 7) >> 3;
-    return (hw & 7) * q + (hw >> 3);
-}
 
 template <typename T, int DH>
 __global__ __launch_bounds__(kPvThreads) void pv_sparse(
     const T* __restrict__ v, const int32_t* __restrict__ sel_idx, const float* __restrict__ sel_val,
     const float* __restrict__ row_max, const int32_t* __restrict__ row_cnt,
     float* __restrict__ out, int h_q, int h_v, int N, int64_t S_max, int total) {
-    using R = Row16<T>;
-    constexpr int EPL = R::EPL;
-    constexpr int LPR = DH / EPL;          // lanes per value row
-    constexpr int RPI = 64 / LPR;          // rows per wave instruction
-    constexpr int STEP = kPvWaves * RPI;   // rows per workgroup step
-    constexpr int UNR = 8;                 // row steps per batch (one load each per lane)
-    constexpr int BATCH = STEP * UNR;
-    static_assert(kPvEntries % BATCH == 0, "a block is whole batches");
+    using G = Gather<T, DH>;
+    static_assert(kPvThreads == kGatherThreads, "one gather workgroup per row");
+    static_assert(kPvEntries % G::BATCH == 0, "a block is whole batches");
     __shared__ int32_t s_pos[kPvEntries];
     __shared__ float s_w[kPvEntries];
-    __shared__ float s_red[kPvWaves][DH];
-    __shared__ float s_l[kPvWaves];
+    __shared__ float s_red[G::NW * DH + G::NW];
 
     const int lid = xcd_logical((int)blockIdx.x, total);
     if (lid >= total) return;
@@ -58,8 +43,6 @@ __global__ __launch_bounds__(kPvThreads) void pv_sparse(
     const int vh = i / g_v;
     const int cnt = row_cnt[row];
     const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = tid >> 6;
     float* o = out + (int64_t)row * DH;
     if (cnt <= 0) {   // no kept entry (L_b = 0): out = 0
         for (int c = tid; c < DH; c += kPvThreads) o[c] = 0.f;
@@ -67,12 +50,9 @@ __global__ __launch_bounds__(kPvThreads) void pv_sparse(
     }
     const float m = row_max[row];
     const T* vb = v + (int64_t)(b * h_v + vh) * S_max * DH;
-    const int rg = lane / LPR;
-    const int sub = lane - rg * LPR;
-    const int first = wave * RPI + rg;
-    float acc[EPL];
+    float acc[G::EPL];
 #pragma unroll
-    for (int c = 0; c < EPL; ++c) acc[c] = 0.f;
+    for (int c = 0; c < G::EPL; ++c) acc[c] = 0.f;
     float lsum = 0.f;   // thread tid's share of l, blocks in order
 #pragma unroll 1
     for (int e0 = 0; e0 < cnt; e0 += kPvEntries) {
@@ -93,60 +73,10 @@ __global__ __launch_bounds__(kPvThreads) void pv_sparse(
             lsum += w;
         }
         __syncthreads();
-        // value rows in batches of UNR steps, double-buffered: batch j + 1 is
-        // requested before batch j is used
-        const int nb = (ne + BATCH - 1) / BATCH;
-        u32x4 ra[UNR], rb[UNR];
-        auto issue = [&](u32x4 (&dst)[UNR], int j) {
-            j = j < nb ? j : nb - 1;   // past the last batch: re-read it (never used)
-#pragma unroll
-            for (int k = 0; k < UNR; ++k) {
-                const int e = j * BATCH + first + k * STEP;
-                dst[k] = *reinterpret_cast<const u32x4*>(vb + (int64_t)s_pos[e] * DH + sub * EPL);
-            }
-        };
-        auto use = [&](const u32x4 (&src)[UNR], int j) {
-#pragma unroll
-            for (int k = 0; k < UNR; ++k) {
-                const float wt = s_w[j * BATCH + first + k * STEP];   // 0 past ne
-                float f[EPL];
-                R::cvt(src[k], f);
-#pragma unroll
-                for (int c = 0; c < EPL; ++c) acc[c] += wt * f[c];
-            }
-        };
-        issue(ra, 0);
-#pragma unroll 1
-        for (int j = 0; j < nb; j += 2) {
-            issue(rb, j + 1);
-            use(ra, j);
-            issue(ra, j + 2);
-            if (j + 1 < nb) use(rb, j + 1);   // uniform
-        }
+        G::run(vb, s_pos, s_w, ne, acc);
         __syncthreads();   // the block's LDS lists are reused by the next block
     }
-    // l: thread shares summed over lanes, then waves (fixed order)
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) lsum += __shfl_xor(lsum, off, 64);
-    if (lane == 0) s_l[wave] = lsum;
-    // acc: reduce over the row-groups of the wave, then over waves
-#pragma unroll
-    for (int off = LPR; off < 64; off <<= 1)
-#pragma unroll
-        for (int c = 0; c < EPL; ++c) acc[c] += __shfl_xor(acc[c], off, 64);
-    if (rg == 0)
-#pragma unroll
-        for (int c = 0; c < EPL; ++c) s_red[wave][sub * EPL + c] = acc[c];
-    __syncthreads();
-    float l = 0.f;
-#pragma unroll
-    for (int w = 0; w < kPvWaves; ++w) l += s_l[w];
-    for (int c = tid; c < DH; c += kPvThreads) {
-        float sacc = 0.f;
-#pragma unroll
-        for (int w = 0; w < kPvWaves; ++w) sacc += s_red[w][c];
-        o[c] = sacc / l;   // l >= 1: the largest kept logit has weight 1
-    }
+    G::finish(acc, lsum, s_red, o);
 }
 
 }  // namespace

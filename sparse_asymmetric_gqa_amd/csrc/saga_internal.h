@@ -101,6 +101,15 @@ hipError_t launch_atopn_tau(const float* sel_val, const int32_t* row_cnt, const 
                             const int32_t* lens, int B, int h_q, int N, int64_t S_max, float* tau,
                             hipStream_t st);
 
+// Union select fused with the value gather: writes out[B][h_q][d] directly
+// (sel_idx / sel_val only for rows the general code takes).
+hipError_t launch_select_pv(const TopmOut& tm, const int32_t* lens, int B, int h_q, int h_k,
+                            int h_v, int d, int N, int64_t S_max, int32_t* sel_idx,
+                            float* sel_val, float* row_max, int32_t* row_cnt, int32_t* idx_out,
+                            int32_t* row_flag, const void* q, const void* k, const void* v,
+                            float* scores, int64_t s_stride, float* out, bool bf16,
+                            hipStream_t st);
+
 hipError_t launch_pv_sparse(const void* v, const int32_t* sel_idx, const float* sel_val,
                             const float* row_max, const int32_t* row_cnt, float* out, int B,
                             int h_q, int h_v, int d, int N, int64_t S_max, bool bf16,

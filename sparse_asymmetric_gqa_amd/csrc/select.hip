@@ -30,7 +30,7 @@
 //             the rest take the general code (union_row), which also
 //             recomputes the head's logits and selects on them densely when
 //             the check fails, so the result is always exact.
-#include "saga_internal.h"
+#include "gather.h"
 
 namespace saga {
 using namespace dev;
@@ -571,20 +571,34 @@ __host__ __device__ constexpr size_t select_stage_offset() {
 // bound, which only costs the rare rows that need it. Dynamic LDS:
 // max(sizeof(UnionShared), select_stage_offset() + 8 nst) bytes, nst >= the
 // kept entries of any fast-path row, a multiple of 4.
-template <typename T, int DH, int KPT>
+//
+// FUSE: the same workgroup then forms the softmax weights of the kept entries
+// and gathers their value rows (gather.h), writing out[row] directly: the
+// kept list never leaves LDS on the fast path (sel_idx / sel_val are not
+// written; idx_out is, when given). Rows are then mapped XCD-aware so the
+// g_v query heads of a value head share that XCD's L2. Rows of the general
+// code write their list to memory first and read it back after a fence.
+// Dynamic LDS with FUSE adds the gather's reduction area after the staging:
+// nst a multiple of 256 and max(sizeof(UnionShared), select_stage_offset() +
+// 8 nst + 4 (4 DH + 4)) bytes.
+template <typename T, int DH, int KPT, bool FUSE>
 __global__ __launch_bounds__(kUnionThreads, 4) void select_union(
     const uint2* __restrict__ cand, const uint4* __restrict__ cand_meta,
     const int32_t* __restrict__ lens, int h_q, int h_k, int N, int64_t S_max, int nchunk, int nst,
     int32_t* __restrict__ sel_idx, float* __restrict__ sel_val, float* __restrict__ row_max,
     int32_t* __restrict__ row_cnt, int32_t* __restrict__ idx_out, int32_t* __restrict__ row_flag,
     const T* __restrict__ q, const T* __restrict__ k, float* __restrict__ scores,
-    int64_t s_stride, float scale) {
+    int64_t s_stride, float scale, const T* __restrict__ v, float* __restrict__ out, int h_v,
+    int rows) {
     static_assert(KPT % 2 == 0, "entries are loaded in pairs");
     constexpr int NT = kUnionThreads;
+    using G = Gather<T, DH>;
+    static_assert(!FUSE || NT == kGatherThreads, "one gather workgroup per row");
     extern __shared__ __attribute__((aligned(16))) unsigned char sel_lds[];
     FastShared& F = *reinterpret_cast<FastShared*>(sel_lds);
     UnionShared& U = *reinterpret_cast<UnionShared*>(sel_lds);
-    const int row = blockIdx.x;
+    const int row = FUSE ? xcd_logical((int)blockIdx.x, rows) : (int)blockIdx.x;
+    if (FUSE && row >= rows) return;   // the grid is rounded up to whole XCD shares
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -592,181 +606,251 @@ __global__ __launch_bounds__(kUnionThreads, 4) void select_union(
     const int64_t L = clamp_len(lens[b], S_max);
     const int n_eff = (int)((int64_t)N < L ? (int64_t)N : L);
     const int nch = (int)((L + kScanChunk - 1) / kScanChunk);
+    // fused gather: the value head's rows, the staged lists and the reduction area
+    const T* vb = v + (int64_t)(b * h_v + (row - b * h_q) / (h_q / h_v)) * S_max * DH;
+    int32_t* g_pos = reinterpret_cast<int32_t*>(sel_lds + select_stage_offset());
+    float* g_w = reinterpret_cast<float*>(g_pos + nst);
+    float* g_red = g_w + nst;
     auto general = [&] {
         union_row<T, DH>(row, U, cand, cand_meta, lens, h_q, h_k, N, S_max, nchunk, sel_idx,
                          sel_val, row_max, row_cnt, idx_out, row_flag, q, k, scores, s_stride,
                          scale);
-    };
-    if (n_eff == 0 || nch > NT) {   // no kept entry, or too many chunks: the general code
-        general();
-        return;
-    }
-    int32_t* oi = sel_idx + (int64_t)row * N;
-    float* ov = sel_val + (int64_t)row * N;
-    int32_t* ou = idx_out ? idx_out + (int64_t)row * N : nullptr;
-    int32_t* st_idx = reinterpret_cast<int32_t*>(sel_lds + select_stage_offset());
-    float* st_val = reinterpret_cast<float*>(st_idx + nst);
-
-    F.hist[0][tid] = 0u;
-    // this thread's run of its chunk's list
-    const int tpc = NT / nch;
-    const int c = tid / tpc;
-    const int sub = tid - c * tpc;
-    const bool cv = c < nch;
-    const uint4 m = cand_meta[(int64_t)row * nchunk + (cv ? c : nch - 1)];
-    const uint32_t cnt = cv ? m.y : 0u;
-    const uint32_t P = (((cnt + (uint32_t)tpc - 1u) / (uint32_t)tpc) + 1u) & ~1u;
-    const uint32_t j0 = (uint32_t)sub * P;
-    const uint32_t mine = cnt > j0 ? (cnt - j0 < P ? cnt - j0 : P) : 0u;
-    const uint32_t npair = (mine + 1u) >> 1;
-    // lists start at even pool entries and runs at even offsets: 16-byte
-    // aligned; pairs past the run re-read its last pair (an empty run reads
-    // the pool's first pair), so every load is unconditional and in bounds
-    const uint4* run = reinterpret_cast<const uint4*>(cand + ((((uint64_t)m.w << 32) | m.x) + j0));
-    uint4 ev[KPT / 2];
-#pragma unroll
-    for (int p = 0; p < KPT / 2; ++p) {
-        const uint4* a = npair ? run + ((uint32_t)p < npair ? (uint32_t)p : npair - 1u)
-                               : reinterpret_cast<const uint4*>(cand);
-        ev[p] = *a;
-    }
-    uint32_t key[KPT];
-    int32_t pos[KPT];
-    uint32_t kmax = 0;
-#pragma unroll
-    for (int s = 0; s < KPT; ++s) {
-        const uint4 e = ev[s >> 1];
-        const bool v = (uint32_t)s < mine;   // empty slots hold key 0, below every real key
-        pos[s] = (int32_t)((s & 1) ? e.z : e.x);
-        key[s] = v ? ((s & 1) ? e.w : e.y) : 0u;
-        kmax = key[s] > kmax ? key[s] : kmax;
-    }
-    {
-        const uint32_t wk = wave_umax(kmax);
-        const uint32_t wc = wave_umax(cv ? m.z : 0u);
-        const uint32_t wo = wave_umax(P > (uint32_t)KPT ? 1u : 0u);
-        if (lane == 0) F.red[wave] = make_uint4(wk, wc, wo, 0u);
-    }
-    __syncthreads();
-    uint32_t maxcut = 0, ovf = 0;
-    kmax = 0;
-#pragma unroll
-    for (int w = 0; w < NT / 64; ++w) {
-        const uint4 r = F.red[w];
-        kmax = r.x > kmax ? r.x : kmax;
-        maxcut = r.y > maxcut ? r.y : maxcut;
-        ovf |= r.z;
-    }
-    uint32_t lo = maxcut > 1u ? maxcut : 1u;
-    uint32_t hi = kmax;
-    if (ovf != 0u || hi < lo) {   // uniform; hi < lo: no key reaches the largest cutoff
-        __syncthreads();
-        general();
-        return;
-    }
-
-    // histogram descent for T
-    uint32_t need = (uint32_t)n_eff, Tk = 0;
-#pragma unroll 1
-    for (int pass = 0;; ++pass) {
-        uint32_t* h = F.hist[pass % 3];
-        F.hist[(pass + 1) % 3][tid] = 0u;   // last read two passes ago
-        const uint32_t span = hi - lo;
-        const int nb = span ? 32 - __clz((int)span) : 0;
-        const int shift = nb > 8 ? nb - 8 : 0;
-#pragma unroll
-        for (int s = 0; s < KPT; ++s)
-            if (key[s] >= lo && key[s] <= hi)
-                __hip_atomic_fetch_add(h + ((key[s] - lo) >> shift), 1u, __ATOMIC_RELAXED,
-                                       __HIP_MEMORY_SCOPE_WORKGROUP);
-        __syncthreads();
-        // lane l holds bins 255-4l (top) down to 252-4l; every wave scans all
-        const uint4 hv = reinterpret_cast<const uint4*>(h)[63 - lane];
-        const uint32_t lsum = (hv.x + hv.y) + (hv.z + hv.w);
-        uint32_t total;
-        const uint32_t incl = wave_incl_scan(lsum, total);   // keys in bins >= 252-4l
-        if (pass == 0 && total < need) {   // uniform: the proof fails
+        if constexpr (FUSE) {
+            // the list union_row wrote, read back in blocks of nst entries
+            __threadfence();
             __syncthreads();
-            general();
-            return;
+            float* o = out + (int64_t)row * DH;
+            const int cnt = __hip_atomic_load(row_cnt + row, __ATOMIC_RELAXED,
+                                              __HIP_MEMORY_SCOPE_AGENT);
+            if (cnt <= 0) {   // no kept entry (L_b = 0): out = 0
+                for (int c = tid; c < DH; c += NT) o[c] = 0.f;
+                return;
+            }
+            const float mrow = __hip_atomic_load(row_max + row, __ATOMIC_RELAXED,
+                                                 __HIP_MEMORY_SCOPE_AGENT);
+            float acc[G::EPL];
+#pragma unroll
+            for (int c = 0; c < G::EPL; ++c) acc[c] = 0.f;
+            float lsum = 0.f;
+#pragma unroll 1
+            for (int e0 = 0; e0 < cnt; e0 += nst) {
+                const int ne = cnt - e0 < nst ? cnt - e0 : nst;
+                for (int e = tid; e < nst; e += NT) {
+                    int32_t pos = 0;
+                    float w = 0.f;
+                    if (e < ne) {
+                        pos = __hip_atomic_load(sel_idx + (int64_t)row * N + e0 + e,
+                                                __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                        pos = pos < 0 ? 0 : (pos >= S_max ? (int32_t)(S_max - 1) : pos);
+                        w = __expf(__hip_atomic_load(sel_val + (int64_t)row * N + e0 + e,
+                                                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) -
+                                   mrow);
+                    }
+                    g_pos[e] = pos;
+                    g_w[e] = w;
+                    lsum += w;
+                }
+                __syncthreads();
+                G::run(vb, g_pos, g_w, ne, acc);
+                __syncthreads();
+            }
+            G::finish(acc, lsum, g_red, o);
         }
-        const uint32_t above0 = incl - lsum;
-        const uint64_t hit = ballot(incl >= need && above0 < need);
-        const int hl = (int)__builtin_ctzll(hit);   // exactly one lane
-        uint32_t bin = 255u - 4u * (uint32_t)lane, above = above0, inbin = hv.w;
-        if (above + hv.w < need) {
-            above += hv.w; bin -= 1u; inbin = hv.z;
-            if (above + hv.z < need) {
-                above += hv.z; bin -= 1u; inbin = hv.y;
-                if (above + hv.y < need) { above += hv.y; bin -= 1u; inbin = hv.x; }
+    };
+    // The fast path returns false, with every thread past a barrier, when the
+    // row needs the general code; that call sits outside it so the fast path's
+    // register arrays are dead across it.
+    auto fast = [&]() -> bool {
+        int32_t* oi = sel_idx + (int64_t)row * N;
+        float* ov = sel_val + (int64_t)row * N;
+        int32_t* ou = idx_out ? idx_out + (int64_t)row * N : nullptr;
+        int32_t* st_idx = reinterpret_cast<int32_t*>(sel_lds + select_stage_offset());
+        float* st_val = reinterpret_cast<float*>(st_idx + nst);
+
+        F.hist[0][tid] = 0u;
+        // this thread's run of its chunk's list
+        const int tpc = NT / nch;
+        const int c = tid / tpc;
+        const int sub = tid - c * tpc;
+        const bool cv = c < nch;
+        const uint4 m = cand_meta[(int64_t)row * nchunk + (cv ? c : nch - 1)];
+        const uint32_t cnt = cv ? m.y : 0u;
+        const uint32_t P = (((cnt + (uint32_t)tpc - 1u) / (uint32_t)tpc) + 1u) & ~1u;
+        const uint32_t j0 = (uint32_t)sub * P;
+        const uint32_t mine = cnt > j0 ? (cnt - j0 < P ? cnt - j0 : P) : 0u;
+        const uint32_t npair = (mine + 1u) >> 1;
+        // lists start at even pool entries and runs at even offsets: 16-byte
+        // aligned; pairs past the run re-read its last pair (an empty run reads
+        // the pool's first pair), so every load is unconditional and in bounds
+        const uint4* run = reinterpret_cast<const uint4*>(cand + ((((uint64_t)m.w << 32) | m.x) + j0));
+        uint4 ev[KPT / 2];
+    #pragma unroll
+        for (int p = 0; p < KPT / 2; ++p) {
+            const uint4* a = npair ? run + ((uint32_t)p < npair ? (uint32_t)p : npair - 1u)
+                                   : reinterpret_cast<const uint4*>(cand);
+            ev[p] = *a;
+        }
+        uint32_t key[KPT];
+        int32_t pos[KPT];
+        uint32_t kmax = 0;
+    #pragma unroll
+        for (int s = 0; s < KPT; ++s) {
+            const uint4 e = ev[s >> 1];
+            const bool v = (uint32_t)s < mine;   // empty slots hold key 0, below every real key
+            pos[s] = (int32_t)((s & 1) ? e.z : e.x);
+            key[s] = v ? ((s & 1) ? e.w : e.y) : 0u;
+            kmax = key[s] > kmax ? key[s] : kmax;
+        }
+        {
+            const uint32_t wk = wave_umax(kmax);
+            const uint32_t wc = wave_umax(cv ? m.z : 0u);
+            const uint32_t wo = wave_umax(P > (uint32_t)KPT ? 1u : 0u);
+            if (lane == 0) F.red[wave] = make_uint4(wk, wc, wo, 0u);
+        }
+        __syncthreads();
+        uint32_t maxcut = 0, ovf = 0;
+        kmax = 0;
+    #pragma unroll
+        for (int w = 0; w < NT / 64; ++w) {
+            const uint4 r = F.red[w];
+            kmax = r.x > kmax ? r.x : kmax;
+            maxcut = r.y > maxcut ? r.y : maxcut;
+            ovf |= r.z;
+        }
+        uint32_t lo = maxcut > 1u ? maxcut : 1u;
+        uint32_t hi = kmax;
+        if (ovf != 0u || hi < lo) {   // uniform; hi < lo: no key reaches the largest cutoff
+            __syncthreads();
+            return false;
+        }
+
+        // histogram descent for T
+        uint32_t need = (uint32_t)n_eff, Tk = 0;
+    #pragma unroll 1
+        for (int pass = 0;; ++pass) {
+            uint32_t* h = F.hist[pass % 3];
+            F.hist[(pass + 1) % 3][tid] = 0u;   // last read two passes ago
+            const uint32_t span = hi - lo;
+            const int nb = span ? 32 - __clz((int)span) : 0;
+            const int shift = nb > 8 ? nb - 8 : 0;
+    #pragma unroll
+            for (int s = 0; s < KPT; ++s)
+                if (key[s] >= lo && key[s] <= hi)
+                    __hip_atomic_fetch_add(h + ((key[s] - lo) >> shift), 1u, __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_WORKGROUP);
+            __syncthreads();
+            // lane l holds bins 255-4l (top) down to 252-4l; every wave scans all
+            const uint4 hv = reinterpret_cast<const uint4*>(h)[63 - lane];
+            const uint32_t lsum = (hv.x + hv.y) + (hv.z + hv.w);
+            uint32_t total;
+            const uint32_t incl = wave_incl_scan(lsum, total);   // keys in bins >= 252-4l
+            if (pass == 0 && total < need) {   // uniform: the proof fails
+                __syncthreads();
+                return false;
+            }
+            const uint32_t above0 = incl - lsum;
+            const uint64_t hit = ballot(incl >= need && above0 < need);
+            const int hl = (int)__builtin_ctzll(hit);   // exactly one lane
+            uint32_t bin = 255u - 4u * (uint32_t)lane, above = above0, inbin = hv.w;
+            if (above + hv.w < need) {
+                above += hv.w; bin -= 1u; inbin = hv.z;
+                if (above + hv.z < need) {
+                    above += hv.z; bin -= 1u; inbin = hv.y;
+                    if (above + hv.y < need) { above += hv.y; bin -= 1u; inbin = hv.x; }
+                }
+            }
+            bin = (uint32_t)__builtin_amdgcn_readlane((int)bin, hl);
+            above = (uint32_t)__builtin_amdgcn_readlane((int)above, hl);
+            inbin = (uint32_t)__builtin_amdgcn_readlane((int)inbin, hl);
+            need -= above;
+            lo += bin << shift;
+            const uint32_t wmask = (1u << shift) - 1u;
+            hi = hi - lo <= wmask ? hi : lo + wmask;
+            if (inbin == need || shift == 0) {   // keys >= lo are exactly N_eff, or the bin is one key
+                Tk = lo;
+                break;
             }
         }
-        bin = (uint32_t)__builtin_amdgcn_readlane((int)bin, hl);
-        above = (uint32_t)__builtin_amdgcn_readlane((int)above, hl);
-        inbin = (uint32_t)__builtin_amdgcn_readlane((int)inbin, hl);
-        need -= above;
-        lo += bin << shift;
-        const uint32_t wmask = (1u << shift) - 1u;
-        hi = hi - lo <= wmask ? hi : lo + wmask;
-        if (inbin == need || shift == 0) {   // keys >= lo are exactly N_eff, or the bin is one key
-            Tk = lo;
-            break;
-        }
-    }
 
-    // compaction: keys > T, then the first krem keys == T in position order
-    uint32_t ngt = 0, neq = 0;
-#pragma unroll
-    for (int s = 0; s < KPT; ++s) {
-        ngt += key[s] > Tk ? 1u : 0u;
-        neq += key[s] == Tk ? 1u : 0u;
-    }
-    const uint32_t packed = ngt | (neq << 16);   // each sum <= 256 KPT < 2^16
-    uint32_t wtot;
-    const uint32_t pincl = wave_incl_scan(packed, wtot);
-    if (lane == 0) F.scan[wave] = wtot;
-    __syncthreads();
-    uint32_t before = pincl - packed, tot = 0;
-#pragma unroll
-    for (int w = 0; w < NT / 64; ++w) {
-        const uint32_t x = F.scan[w];
-        before += w < wave ? x : 0u;
-        tot += x;
-    }
-    const uint32_t krem = (uint32_t)n_eff - (tot & 0xFFFFu);
-    uint32_t eq_seen = before >> 16;
-    uint32_t slot = (before & 0xFFFFu) + (eq_seen < krem ? eq_seen : krem);
-#pragma unroll
-    for (int s = 0; s < KPT; ++s) {
-        const bool eq = key[s] == Tk;
-        const bool keep = key[s] > Tk || (eq && eq_seen < krem);
-        eq_seen += eq ? 1u : 0u;
-        if (keep) {   // slot < N_eff by construction
-            st_idx[slot] = pos[s];
-            st_val[slot] = key_float(key[s]);
+        // compaction: keys > T, then the first krem keys == T in position order
+        uint32_t ngt = 0, neq = 0;
+    #pragma unroll
+        for (int s = 0; s < KPT; ++s) {
+            ngt += key[s] > Tk ? 1u : 0u;
+            neq += key[s] == Tk ? 1u : 0u;
         }
-        slot += keep ? 1u : 0u;
-    }
-    __syncthreads();
-    const bool v4 = (((uintptr_t)oi | (uintptr_t)ov | (uintptr_t)ou) & 15u) == 0;
-    const int n4 = v4 ? n_eff / 4 : 0;
-    for (int j = tid; j < n4; j += NT) {
-        const int4 vi = reinterpret_cast<const int4*>(st_idx)[j];
-        reinterpret_cast<int4*>(oi)[j] = vi;
-        reinterpret_cast<float4*>(ov)[j] = reinterpret_cast<const float4*>(st_val)[j];
-        if (ou) reinterpret_cast<int4*>(ou)[j] = vi;
-    }
-    for (int j = 4 * n4 + tid; j < N; j += NT) {
-        const bool kept = j < n_eff;
-        oi[j] = kept ? st_idx[j] : -1;
-        ov[j] = kept ? st_val[j] : -__builtin_inff();
-        if (ou) ou[j] = kept ? st_idx[j] : -1;
-    }
-    if (tid == 0) {
-        row_max[row] = key_float(kmax);
-        row_cnt[row] = n_eff;
-        row_flag[row] = 0;
-    }
+        const uint32_t packed = ngt | (neq << 16);   // each sum <= 256 KPT < 2^16
+        uint32_t wtot;
+        const uint32_t pincl = wave_incl_scan(packed, wtot);
+        if (lane == 0) F.scan[wave] = wtot;
+        __syncthreads();
+        uint32_t before = pincl - packed, tot = 0;
+    #pragma unroll
+        for (int w = 0; w < NT / 64; ++w) {
+            const uint32_t x = F.scan[w];
+            before += w < wave ? x : 0u;
+            tot += x;
+        }
+        const uint32_t krem = (uint32_t)n_eff - (tot & 0xFFFFu);
+        uint32_t eq_seen = before >> 16;
+        uint32_t slot = (before & 0xFFFFu) + (eq_seen < krem ? eq_seen : krem);
+    #pragma unroll
+        for (int s = 0; s < KPT; ++s) {
+            const bool eq = key[s] == Tk;
+            const bool keep = key[s] > Tk || (eq && eq_seen < krem);
+            eq_seen += eq ? 1u : 0u;
+            if (keep) {   // slot < N_eff by construction
+                st_idx[slot] = pos[s];
+                st_val[slot] = key_float(key[s]);
+            }
+            slot += keep ? 1u : 0u;
+        }
+        __syncthreads();
+        if (tid == 0) {
+            row_max[row] = key_float(kmax);
+            row_cnt[row] = n_eff;
+            row_flag[row] = 0;
+        }
+        if constexpr (FUSE) {
+            // weights of the staged entries in place; the gather reads positions
+            // and weights up to nst (weight 0, row 0 past n_eff)
+            if (ou)
+                for (int j = tid; j < N; j += NT) ou[j] = j < n_eff ? st_idx[j] : -1;
+            const float mrow = key_float(kmax);
+            float lsum = 0.f;
+            for (int j = tid; j < nst; j += NT) {
+                const bool kept = j < n_eff;
+                const float w = kept ? __expf(st_val[j] - mrow) : 0.f;
+                if (!kept) st_idx[j] = 0;
+                st_val[j] = w;
+                lsum += w;
+            }
+            __syncthreads();
+            float acc[G::EPL];
+    #pragma unroll
+            for (int c = 0; c < G::EPL; ++c) acc[c] = 0.f;
+            G::run(vb, st_idx, st_val, n_eff, acc);
+            G::finish(acc, lsum, g_red, out + (int64_t)row * DH);
+            return true;
+        }
+        const bool v4 = (((uintptr_t)oi | (uintptr_t)ov | (uintptr_t)ou) & 15u) == 0;
+        const int n4 = v4 ? n_eff / 4 : 0;
+        for (int j = tid; j < n4; j += NT) {
+            const int4 vi = reinterpret_cast<const int4*>(st_idx)[j];
+            reinterpret_cast<int4*>(oi)[j] = vi;
+            reinterpret_cast<float4*>(ov)[j] = reinterpret_cast<const float4*>(st_val)[j];
+            if (ou) reinterpret_cast<int4*>(ou)[j] = vi;
+        }
+        for (int j = 4 * n4 + tid; j < N; j += NT) {
+            const bool kept = j < n_eff;
+            oi[j] = kept ? st_idx[j] : -1;
+            ov[j] = kept ? st_val[j] : -__builtin_inff();
+            if (ou) ou[j] = kept ? st_idx[j] : -1;
+        }
+
+        return true;
+    };
+    if (n_eff == 0 || nch > NT || !fast()) general();   // no kept entry, too many chunks, or no proof
 }
 
 // ---- Atop-N: stale-threshold selection and calibration ---------------------------
@@ -1094,15 +1178,18 @@ hipError_t launch_select(const float* scores, int64_t s_stride, const int32_t* l
     return go_dense<32>(scores, s_stride, lens, B, h_q, N, S_max, sel_idx, sel_val, row_max, row_cnt, idx_out, st);
 }
 
-hipError_t launch_select_union(const TopmOut& tm, const int32_t* lens, int B, int h_q, int h_k,
-                               int d, int N, int64_t S_max, int32_t* sel_idx, float* sel_val,
-                               float* row_max, int32_t* row_cnt, int32_t* idx_out,
-                               int32_t* row_flag, const void* q, const void* k, float* scores,
-                               int64_t s_stride, bool bf16, hipStream_t st) {
+namespace {
+
+template <bool FUSE>
+hipError_t go_select_union(const TopmOut& tm, const int32_t* lens, int B, int h_q, int h_k, int d,
+                           int N, int64_t S_max, int32_t* sel_idx, float* sel_val,
+                           float* row_max, int32_t* row_cnt, int32_t* idx_out, int32_t* row_flag,
+                           const void* q, const void* k, float* scores, int64_t s_stride,
+                           bool bf16, const void* v, float* out, int h_v, hipStream_t st) {
     const int nchunk = (int)((S_max + kScanChunk - 1) / kScanChunk);
     const int rows = B * h_q;
     const float scale = (float)(1.0 / __builtin_sqrt((double)d));
-    // Registers per thread for the fast path: the longest run, an even
+    // Register slots per thread for the fast path: the longest run, an even
     // ceil(per_chunk / tpc) with tpc = floor(256 / chunks) threads per chunk
     // and up to per_chunk = 1.25 (1.5 share + 16) keys in a full chunk's list
     // (share = N * 1024 / L); rows with longer runs take the general code.
@@ -1112,21 +1199,23 @@ hipError_t launch_select_union(const TopmOut& tm, const int32_t* lens, int B, in
     const int64_t tpc = nchunk <= kUnionThreads ? kUnionThreads / nchunk : 1;
     const int64_t slots = (((per_chunk + tpc - 1) / tpc) + 1) & ~(int64_t)1;
     // staged kept entries: N_eff <= N, and <= the 256 KPT keys in registers
-    auto lds_for = [&](int kpt) -> size_t {
-        int64_t nst = (int64_t)N < (int64_t)kUnionThreads * kpt ? (int64_t)N : (int64_t)kUnionThreads * kpt;
-        nst = (nst + 3) & ~(int64_t)3;
-        const size_t fast = select_stage_offset() + (size_t)nst * 8;
-        return fast > sizeof(UnionShared) ? fast : sizeof(UnionShared);
-    };
+    // (the fused gather reads them in whole batches: a multiple of 256)
     auto nst_for = [&](int kpt) -> int {
         int64_t nst = (int64_t)N < (int64_t)kUnionThreads * kpt ? (int64_t)N : (int64_t)kUnionThreads * kpt;
-        return (int)((nst + 3) & ~(int64_t)3);
+        return (int)(FUSE ? (nst + 255) & ~(int64_t)255 : (nst + 3) & ~(int64_t)3);
     };
+    auto lds_for = [&](int kpt) -> size_t {
+        size_t fast = select_stage_offset() + (size_t)nst_for(kpt) * 8;
+        if (FUSE) fast += (size_t)(4 * d + 4) * sizeof(float);
+        return fast > sizeof(UnionShared) ? fast : sizeof(UnionShared);
+    };
+    const unsigned grid = FUSE ? (unsigned)(((rows + 7) / 8) * 8) : (unsigned)rows;
 #define SAGA_SU(T, D, KPT)                                                                       \
-    hipLaunchKernelGGL((select_union<T, D, KPT>), dim3((unsigned)rows), dim3(kUnionThreads),       \
+    hipLaunchKernelGGL((select_union<T, D, KPT, FUSE>), dim3(grid), dim3(kUnionThreads),          \
                        (unsigned)lds_for(KPT), st, tm.cand, tm.meta, lens, h_q, h_k, N, S_max,     \
                        nchunk, nst_for(KPT), sel_idx, sel_val, row_max, row_cnt, idx_out, row_flag, \
-                       (const T*)q, (const T*)k, scores, s_stride, scale)
+                       (const T*)q, (const T*)k, scores, s_stride, scale, (const T*)v, out, h_v,   \
+                       rows)
 #define SAGA_SU_K(T, D)                                                                          \
     if (slots <= 8) SAGA_SU(T, D, 8);                                                            \
     else if (slots <= 16) SAGA_SU(T, D, 16);                                                     \
@@ -1139,6 +1228,29 @@ hipError_t launch_select_union(const TopmOut& tm, const int32_t* lens, int B, in
 #undef SAGA_SU_K
 #undef SAGA_SU
     return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_select_union(const TopmOut& tm, const int32_t* lens, int B, int h_q, int h_k,
+                               int d, int N, int64_t S_max, int32_t* sel_idx, float* sel_val,
+                               float* row_max, int32_t* row_cnt, int32_t* idx_out,
+                               int32_t* row_flag, const void* q, const void* k, float* scores,
+                               int64_t s_stride, bool bf16, hipStream_t st) {
+    return go_select_union<false>(tm, lens, B, h_q, h_k, d, N, S_max, sel_idx, sel_val, row_max,
+                                  row_cnt, idx_out, row_flag, q, k, scores, s_stride, bf16,
+                                  nullptr, nullptr, 1, st);
+}
+
+hipError_t launch_select_pv(const TopmOut& tm, const int32_t* lens, int B, int h_q, int h_k,
+                            int h_v, int d, int N, int64_t S_max, int32_t* sel_idx,
+                            float* sel_val, float* row_max, int32_t* row_cnt, int32_t* idx_out,
+                            int32_t* row_flag, const void* q, const void* k, const void* v,
+                            float* scores, int64_t s_stride, float* out, bool bf16,
+                            hipStream_t st) {
+    return go_select_union<true>(tm, lens, B, h_q, h_k, d, N, S_max, sel_idx, sel_val, row_max,
+                                 row_cnt, idx_out, row_flag, q, k, scores, s_stride, bf16, v, out,
+                                 h_v, st);
 }
 
 hipError_t launch_select_thresh(const TopmOut& tm, const int32_t* lens, const float* tau, int B,
