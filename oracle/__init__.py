@@ -6,7 +6,10 @@ cpu_baseline leg may import this package. The product path never does.
 The C source (oracle.c) restates "More Value per Key: Asymmetric Sparse
 Attention for Faster LLM Decoding": Eq. 2 logits, Eq. 6 top-N selection,
 Eq. 7 softmax over the kept entries and their value rows, §3.2 SAGA head
-counts, App. B head blocks. This wrapper only marshals numpy arrays.
+counts, App. B head blocks; the stale-threshold selector of §3.1 / App. C.1;
+and "SparQ Attention: Bandwidth-Efficient LLM Inference" Steps 1-3 (with its
+GQA modifications) as an approximate scorer in front of the same selector.
+This wrapper only marshals numpy arrays.
 
 Inputs: q [B][h_q][d], k [B][h_k][S_max][d], v [B][h_v][S_max][d] as float32
 or as uint16 bf16 bit patterns; seq_lens int32 [B].
@@ -54,8 +57,11 @@ def _load():
                                                vp, i]
         lib.oracle_atopn_attn.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i64, i, i, vp, vp, i64,
                                           vp, vp, vp, vp, vp, vp, i]
+        lib.oracle_sparq_attn.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i64, i, i, i, i, vp, vp,
+                                          i64, vp, vp, vp, vp, vp, vp, vp, i]
         for f in (lib.oracle_topn_attn, lib.oracle_dense_attn, lib.oracle_logits,
-                  lib.oracle_attend_given, lib.oracle_atopn_calibrate, lib.oracle_atopn_attn):
+                  lib.oracle_attend_given, lib.oracle_atopn_calibrate, lib.oracle_atopn_attn,
+                  lib.oracle_sparq_attn):
             f.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -196,3 +202,40 @@ def atopn_attn(q, k, v, seq_lens, N, tau, pairs=None, threads=0):
         raise ValueError("oracle_atopn_attn: bad arguments")
     return {"out": out, "idx": idx, "sel": sel, "above": above, "theta": theta, "psum": psum,
             "threads": rc}
+
+
+def sparq_attn(q, k, v, seq_lens, N, r, local=0, vmean=None, pairs=None, scores=False,
+               threads=0):
+    """SparQ-style step: approximate scores over the r kept query dims of the
+    key head's group, the last `local` positions always kept plus the N - local
+    best-scored of the rest, exact attention over the kept set, and the mean
+    value reallocation when vmean [B][h_v][d] is given.
+
+    Returns dict: out [P][d], idx [P][N] int32 (ascending, -1 pad), alpha [P],
+    tau [P] (0 when the approximate scores are all 0), zthr [P] (smallest
+    kept approximate score of the non-local part, NaN if none), dims [P][r]
+    (ascending), zhat [P][S_max] (only with scores=True; NaN past L), threads.
+    """
+    q, k, v, lens, dt, B, h_q, h_k, h_v, d, S = _prep(q, k, v, seq_lens)
+    pr, P = _pairs(pairs, B, h_q)
+    vm = None
+    if vmean is not None:
+        vm = np.ascontiguousarray(np.asarray(vmean, dtype=np.float64).reshape(B, h_v, d))
+    out = np.empty((P, d))
+    idx = np.empty((P, N), dtype=np.int32)
+    alpha = np.empty(P)
+    tau = np.empty(P)
+    zthr = np.empty(P)
+    dims = np.empty((P, r), dtype=np.int32)
+    zhat = np.empty((P, S)) if scores else None
+    rc = _load().oracle_sparq_attn(_p(q), _p(k), _p(v), _p(lens), B, h_q, h_k, h_v, d, S, dt,
+                                   int(N), int(r), int(local), _p(vm), _p(pr), P, _p(out),
+                                   _p(idx), _p(alpha), _p(tau), _p(zthr), _p(dims), _p(zhat),
+                                   int(threads))
+    if rc < 0:
+        raise ValueError("oracle_sparq_attn: bad arguments")
+    res = {"out": out, "idx": idx, "alpha": alpha, "tau": tau, "zthr": zthr, "dims": dims,
+           "threads": rc}
+    if scores:
+        res["zhat"] = zhat
+    return res

@@ -46,7 +46,13 @@
  *   - no position reaching tau: the output is 0 (a softmax over an empty set
  *     is undefined).
  *
- * Parity pins live in tests/test_oracle_pins.py (closed forms, library
+ * SparQ-style approximate scoring in front of the same selector ("SparQ
+ * Attention: Bandwidth-Efficient LLM Inference", Steps 1-3 with the GQA
+ * modifications), the last function of this file; its readings are listed
+ * in its own comment.
+ *
+ * Parity pins live in tests/test_oracle_pins.py, tests/test_oracle_atopn_pins.py
+ * and tests/test_oracle_sparq_pins.py (closed forms, library
  * reductions, brute force); every function below is pinned there.
  */
 #include <math.h>
@@ -387,6 +393,126 @@ int oracle_atopn_attn(const void* q, const void* k, const void* v, const int32_t
         }
         attend(&P, b, i, all, n, out + j * d, psum + j);
         free(all);
+    }
+    return bad ? -1 : used;
+}
+
+/*
+ * SparQ-style approximate scoring feeding the top-N selector ("SparQ
+ * Attention: Bandwidth-Efficient LLM Inference", Steps 1-3 with the GQA
+ * modifications), on the SAGA head layout. Per pair (b, i), key head kh:
+ *   Step 1  u[c] = sum over the g_k query heads of the key head of |q[c]|;
+ *           dims = the r largest u[c] (equal values: lower c first);
+ *           tau = sqrt(d * sum_{c in dims} |q_i[c]| / sum_c |q_i[c]|);
+ *           zhat_t = sum_{c in dims} q_i[c] K[t][c] / tau (zhat = 0 when
+ *           the query has no mass on dims);
+ *           shat = softmax(zhat) over all L positions.
+ *   Step 2  the last l_eff = min(l, L) positions are always kept (local
+ *           window); of the first L' = L - l_eff positions the N - l with the
+ *           largest zhat are kept (equal values: lower position first).
+ *           Then the exact Eq. 7 attention (logits q.K / sqrt(d)) over the
+ *           kept set gives y3.
+ *   Step 3  alpha = sum of shat over the kept set; out = alpha y3 +
+ *           (1 - alpha) vmean[b][vh] when vmean is given, else out = y3.
+ * Requires 0 <= l <= N and 1 <= r <= d. L = 0 keeps nothing: out = 0,
+ * alpha = 0. Per pair outputs: out[d], idx[N] (ascending, -1 pad),
+ * alpha, tau (0 when zhat = 0), zthr = the smallest kept zhat of the scored
+ * (non-local) part (NaN if none), dims[r] (ascending), and, when zhat is not
+ * NULL, zhat[S_max] (NaN past L). vmean is [B][h_v][d] (fp64) or NULL.
+ * Returns threads used or -1.
+ */
+int oracle_sparq_attn(const void* q, const void* k, const void* v, const int32_t* lens,
+                      int B, int h_q, int h_k, int h_v, int d, int64_t S_max, int dtype, int N,
+                      int r, int l, const double* vmean, const int64_t* pairs, int64_t npairs,
+                      double* out, int32_t* idx, double* alpha, double* tau, double* zthr,
+                      int32_t* dims, double* zhat, int nthreads) {
+    problem_t P = {q, k, v, lens, B, h_q, h_k, h_v, d, S_max, dtype};
+    if (check(&P) || N < 1 || r < 1 || r > d || l < 0 || l > N) return -1;
+    if (!pairs) npairs = (int64_t)B * h_q;
+    const int g = h_q / h_k;
+    int used = set_threads(nthreads);
+    int bad = 0;
+    #pragma omp parallel for schedule(dynamic, 1) reduction(|:bad)
+    for (int64_t j = 0; j < npairs; ++j) {
+        int b, i;
+        pair_of(&P, pairs, j, &b, &i);
+        if (b < 0 || b >= B || i < 0 || i >= h_q) { bad = 1; continue; }
+        const int kh = key_head(&P, i), vh = value_head(&P, i);
+        const int64_t L = seq_len(&P, b);
+        scored_t* all = (scored_t*)malloc(sizeof(scored_t) * (size_t)(L > 0 ? L : 1));
+        scored_t* u = (scored_t*)malloc(sizeof(scored_t) * (size_t)d);
+        char* in_dims = (char*)calloc((size_t)d, 1);
+        if (!all || !u || !in_dims) { bad = 1; free(all); free(u); free(in_dims); continue; }
+        /* Step 1: the group's query-magnitude ranking and the r kept dims */
+        for (int c = 0; c < d; ++c) {
+            double s = 0.0;
+            for (int jj = kh * g; jj < (kh + 1) * g; ++jj)
+                s += fabs(elem(q, dtype, ((int64_t)b * h_q + jj) * d + c));
+            u[c].s = s;
+            u[c].t = c;
+        }
+        qsort(u, (size_t)d, sizeof(scored_t), by_logit_desc);
+        for (int e = 0; e < r; ++e) in_dims[u[e].t] = 1;
+        for (int c = 0, e = 0; c < d; ++c) if (in_dims[c]) dims[j * r + e++] = c;
+        const int64_t qo = ((int64_t)b * h_q + i) * d;
+        double num = 0.0, den = 0.0;
+        for (int c = 0; c < d; ++c) {
+            const double a = fabs(elem(q, dtype, qo + c));
+            den += a;
+            if (in_dims[c]) num += a;
+        }
+        const double tq = num > 0.0 ? sqrt((double)d * num / den) : 0.0;
+        tau[j] = tq;
+        for (int64_t t = 0; t < L; ++t) {
+            double acc = 0.0;
+            if (num > 0.0) {
+                const int64_t ko = (((int64_t)b * h_k + kh) * S_max + t) * d;
+                for (int c = 0; c < d; ++c)
+                    if (in_dims[c]) acc += elem(q, dtype, qo + c) * elem(k, dtype, ko + c);
+                acc /= tq;
+            }
+            all[t].s = acc;
+            all[t].t = t;
+        }
+        if (zhat)
+            for (int64_t t = 0; t < S_max; ++t) zhat[j * S_max + t] = t < L ? all[t].s : NAN;
+        const double lse = L > 0 ? log_sum_exp(all, L) : NAN;
+        /* Step 2: local window, then the top N - l of the scored prefix */
+        const int64_t lw = L < l ? L : l;
+        const int64_t Lp = L - lw;
+        const int64_t ns = (int64_t)(N - l) < Lp ? (int64_t)(N - l) : Lp;
+        qsort(all, (size_t)Lp, sizeof(scored_t), by_logit_desc);
+        zthr[j] = ns > 0 ? all[ns - 1].s : NAN;
+        int64_t n = 0;
+        for (int64_t e = 0; e < ns; ++e) all[n++] = all[e];
+        for (int64_t t = Lp; t < L; ++t) {   /* zhat of the local positions, for alpha */
+            double acc = 0.0;
+            if (num > 0.0) {
+                const int64_t ko = (((int64_t)b * h_k + kh) * S_max + t) * d;
+                for (int c = 0; c < d; ++c)
+                    if (in_dims[c]) acc += elem(q, dtype, qo + c) * elem(k, dtype, ko + c);
+                acc /= tq;
+            }
+            all[n].s = acc;
+            all[n].t = t;
+            ++n;
+        }
+        qsort(all, (size_t)n, sizeof(scored_t), by_pos);
+        double a = 0.0;
+        for (int64_t e = 0; e < n; ++e) a += exp(all[e].s - lse);
+        alpha[j] = a;
+        for (int64_t e = 0; e < N; ++e) idx[j * N + e] = e < n ? (int32_t)all[e].t : -1;
+        /* exact logits of the kept set, then Eq. 7 */
+        for (int64_t e = 0; e < n; ++e) all[e].s = logit(&P, b, i, all[e].t);
+        double psum;
+        attend(&P, b, i, all, n, out + j * d, &psum);
+        if (vmean && n > 0)   /* Step 3: mean value reallocation */
+            for (int c = 0; c < d; ++c)
+                out[j * d + c] = a * out[j * d + c] +
+                                 (1.0 - a) * vmean[((int64_t)b * h_v + vh) * d + c];
+        free(all);
+        free(u);
+        free(in_dims);
     }
     return bad ? -1 : used;
 }
