@@ -176,6 +176,54 @@ saga_status saga_atopn_attn(const void* q, const void* k_cache, const void* v_ca
                             const float* tau, int32_t* idx_out, int32_t* count_out);
 
 /*
+ * SparQ-style approximate scoring in front of the top-N selector ("SparQ
+ * Attention: Bandwidth-Efficient LLM Inference", Steps 1-3 with the GQA
+ * modifications), on the SAGA head layout. Per (b, key head): the r dims
+ * with the largest sum of |q| over the key head's g query heads (equal sums:
+ * lower dim first). Per (b, query head i):
+ *   - approximate logits over those dims only, zhat_t = <q_i, K_t>_dims / tau
+ *     with tau = sqrt(d |q_i on dims|_1 / |q_i|_1) (all 0 when q_i has no
+ *     mass on the dims), read from kt_cache;
+ *   - the last min(local, L_b) positions are always kept; of the first
+ *     L_b - min(local, L_b) positions the N - local with the largest zhat
+ *     (equal values: lower position first);
+ *   - exact attention (Eq. 7, logits q.K / sqrt(d) from k_cache) over the
+ *     kept set gives y3;
+ *   - alpha = sum over the kept set of softmax(zhat) (normalised over all L_b
+ *     positions); out = alpha y3 + (1 - alpha) v_mean[b][vh] when v_mean is
+ *     given, else out = y3. The pages keep the running value mean across
+ *     steps and drop this mix for GQA models.
+ *
+ * Arguments as for saga_decode_attn, plus:
+ *   kt_cache  device, the cache dtype, [B][h_k][d][S_max]: the same keys as
+ *             k_cache, S-contiguous (the pages' second copy of K); only the r
+ *             kept dims of each key head are read, rows t < L_b.
+ *   r         1 <= r <= d.        local  0 <= local <= N.
+ *   v_mean    nullable, device fp32 [B][h_v][d].
+ *   idx_out   nullable, int32 [B][h_q][N]: the kept positions, ascending, -1 pad.
+ *   alpha_out nullable, fp32 [B][h_q].
+ *   dims_out  nullable, int32 [B][h_k][r]: the kept dims, ascending.
+ * Two kernels on `stream` (the set-up of the dims and temperatures, then the
+ * scan of the kept columns into candidate lists), then one dispatch per row
+ * for selection, exact rescoring and the value gather. The workspace is
+ * saga_sparq_workspace_size bytes (256-byte aligned). A row with L_b = 0
+ * gets out = 0 and alpha = 0. SAGA_ERR_INVALID_ARG: a null required pointer,
+ * r or local out of range, q / k_cache / kt_cache / v_cache not 16-byte
+ * aligned, v_mean not 4-byte aligned, and the saga_decode_attn checks.
+ * SAGA_ERR_UNSUPPORTED: h_q / h_k > 16, S_max > 512 Ki, N > 4096, or S_max
+ * not a multiple of 16 bytes' worth of elements (8 bf16, 4 fp32).
+ */
+size_t saga_sparq_workspace_size(int B, int h_q, int h_k, int h_v, int d, int N, int r,
+                                 int64_t S_max, saga_dtype dtype);
+
+saga_status saga_sparq_attn(const void* q, const void* k_cache, const void* kt_cache,
+                            const void* v_cache, const int32_t* seq_lens, float* out, int B,
+                            int h_q, int h_k, int h_v, int d, int N, int r, int local,
+                            const float* v_mean, hipStream_t stream, int64_t S_max,
+                            saga_dtype dtype, void* workspace, size_t workspace_bytes,
+                            int32_t* idx_out, float* alpha_out, int32_t* dims_out);
+
+/*
  * The K-scan step alone (§2.1 Eq. 2 with the App. B key-head map): writes the
  * fp32 logits scores[B][h_q][S_max] for t < L_b; entries t >= L_b are left
  * untouched. Same argument rules as saga_decode_attn (h_v is not involved).

@@ -9,8 +9,8 @@ from ._binding import (  # noqa: F401
     SAGA_ERR_WORKSPACE, SAGA_F32, SAGA_OK, SagaError, lib, saga_atopn_attn, saga_atopn_calibrate,
     saga_atopn_workspace_size, saga_debug_fallback_rows,
     saga_debug_scores, saga_decode_attn, saga_decode_attn_timed,
-    saga_dense_attn, saga_dense_workspace_size, saga_status_string, saga_workspace_size,
-    status_string)
+    saga_dense_attn, saga_dense_workspace_size, saga_sparq_attn, saga_sparq_workspace_size,
+    saga_status_string, saga_workspace_size, status_string)
 from .tensors import (  # noqa: F401
     atopn_attn, atopn_calibrate, atopn_workspace_size, debug_scores, decode_attn, dense_attn,
-    dense_workspace_size, new_workspace, workspace_size)
+    dense_workspace_size, new_workspace, sparq_attn, sparq_workspace_size, workspace_size)

@@ -24,7 +24,7 @@ SAGA_BF16 = 1
 
 EXPORTS = ("saga_workspace_size", "saga_decode_attn", "saga_decode_attn_timed",
            "saga_dense_workspace_size", "saga_atopn_workspace_size", "saga_atopn_calibrate",
-           "saga_atopn_attn",
+           "saga_atopn_attn", "saga_sparq_workspace_size", "saga_sparq_attn",
            "saga_dense_attn", "saga_debug_scores", "saga_debug_fallback_rows",
            "saga_status_string")
 
@@ -69,6 +69,11 @@ def _load() -> ctypes.CDLL:
     lib.saga_atopn_attn.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, vp, i64, i, vp, sz, vp,
                                     vp, vp]
     lib.saga_atopn_attn.restype = i
+    lib.saga_sparq_workspace_size.argtypes = [i, i, i, i, i, i, i, i64, i]
+    lib.saga_sparq_workspace_size.restype = sz
+    lib.saga_sparq_attn.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, vp, vp, i64,
+                                    i, vp, sz, vp, vp, vp]
+    lib.saga_sparq_attn.restype = i
     lib.saga_status_string.argtypes = [i]
     lib.saga_status_string.restype = ctypes.c_char_p
     return lib
@@ -158,3 +163,17 @@ def saga_atopn_attn(q, k_cache, v_cache, seq_lens, out, B, h_q, h_k, h_v, d, N, 
                                    _ptr(out), B, h_q, h_k, h_v, d, N, _ptr(stream), S_max, dtype,
                                    _ptr(workspace), workspace_bytes, _ptr(tau), _ptr(idx_out),
                                    _ptr(count_out)))
+
+
+def saga_sparq_workspace_size(B, h_q, h_k, h_v, d, N, r, S_max, dtype) -> int:
+    return int(lib.saga_sparq_workspace_size(B, h_q, h_k, h_v, d, N, r, S_max, dtype))
+
+
+def saga_sparq_attn(q, k_cache, kt_cache, v_cache, seq_lens, out, B, h_q, h_k, h_v, d, N, r,
+                    local, v_mean, stream, S_max, dtype, workspace, workspace_bytes, idx_out=None,
+                    alpha_out=None, dims_out=None) -> int:
+    return int(lib.saga_sparq_attn(_ptr(q), _ptr(k_cache), _ptr(kt_cache), _ptr(v_cache),
+                                   _ptr(seq_lens), _ptr(out), B, h_q, h_k, h_v, d, N, r, local,
+                                   _ptr(v_mean), _ptr(stream), S_max, dtype, _ptr(workspace),
+                                   workspace_bytes, _ptr(idx_out), _ptr(alpha_out),
+                                   _ptr(dims_out)))

@@ -15,7 +15,7 @@ namespace saga {
 static size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
 Workspace carve(void* base, int B, int h_q, int h_k, int d, int N, int64_t S_max,
-                bool dense) {
+                bool dense, SparqWs* sq, int esize) {
     Workspace w{};
     char* p = static_cast<char*>(base);
     size_t off = 0;
@@ -37,6 +37,13 @@ Workspace carve(void* base, int B, int h_q, int h_k, int d, int N, int64_t S_max
         w.sel_val = reinterpret_cast<float*>(take(rows * (size_t)N * sizeof(float)));
         w.row_max = reinterpret_cast<float*>(take(rows * sizeof(float)));
         w.row_cnt = reinterpret_cast<int32_t*>(take(rows * sizeof(int32_t)));
+        if (sq) {
+            const size_t kr = (size_t)B * (size_t)h_k;
+            sq->dims = reinterpret_cast<int32_t*>(take(kr * (size_t)d * sizeof(int32_t)));
+            sq->qop = take(kr * (size_t)(d / 16) * 64 * 4 * (size_t)esize);
+            sq->inv_tau = reinterpret_cast<float*>(take(rows * sizeof(float)));
+            sq->qm = reinterpret_cast<float*>(take(rows * (size_t)d * sizeof(float)));
+        }
     } else {
         const size_t nsplit = (size_t)dense_nsplit(S_max, h_q / h_k);
         w.part = reinterpret_cast<float*>(take(rows * nsplit * (size_t)(d + 2) * sizeof(float)));
@@ -303,6 +310,56 @@ saga_status saga_atopn_attn(const void* q, const void* k_cache, const void* v_ca
     return from_hip(saga::launch_pv_sparse(v_cache, w.sel_idx, w.sel_val, w.row_max, w.row_cnt,
                                            out, B, h_q, h_v, d, cap, S_max, bf16, stream),
                     "pv_sparse");
+}
+
+size_t saga_sparq_workspace_size(int B, int h_q, int h_k, int h_v, int d, int N, int r,
+                                 int64_t S_max, saga_dtype dtype) {
+    if (check_shape(B, h_q, h_k, h_v, d, S_max, dtype) != SAGA_OK) return 0;
+    if (N < 1 || N > (1 << 29) || r < 1 || r > d) return 0;
+    saga::SparqWs sw{};
+    return saga::carve(nullptr, B, h_q, h_k, d, N, S_max, false, &sw,
+                       dtype == SAGA_BF16 ? 2 : 4).bytes;
+}
+
+saga_status saga_sparq_attn(const void* q, const void* k_cache, const void* kt_cache,
+                            const void* v_cache, const int32_t* seq_lens, float* out, int B,
+                            int h_q, int h_k, int h_v, int d, int N, int r, int local,
+                            const float* v_mean, hipStream_t stream, int64_t S_max,
+                            saga_dtype dtype, void* workspace, size_t workspace_bytes,
+                            int32_t* idx_out, float* alpha_out, int32_t* dims_out) {
+    if (!q || !k_cache || !kt_cache || !v_cache || !seq_lens || !out) return SAGA_ERR_INVALID_ARG;
+    saga_status s = check_shape(B, h_q, h_k, h_v, d, S_max, dtype);
+    if (s != SAGA_OK) return s;
+    if (N < 1 || N > (1 << 29) || r < 1 || r > d || local < 0 || local > N)
+        return SAGA_ERR_INVALID_ARG;
+    if (!aligned16(q) || !aligned16(k_cache) || !aligned16(kt_cache) || !aligned16(v_cache) ||
+        (reinterpret_cast<uintptr_t>(v_mean) & 3u))
+        return SAGA_ERR_INVALID_ARG;
+    const int esize = dtype == SAGA_BF16 ? 2 : 4;
+    // the scan reads 16-byte pieces of the S-contiguous copy's rows
+    if (!saga::use_union_path(h_q, h_k, S_max) || !saga::sparq_select_fits(N) ||
+        S_max % (16 / esize) != 0)
+        return SAGA_ERR_UNSUPPORTED;
+    saga::SparqWs sw{};
+    const saga::Workspace need = saga::carve(nullptr, B, h_q, h_k, d, N, S_max, false, &sw, esize);
+    if (!workspace || workspace_bytes < need.bytes || (reinterpret_cast<uintptr_t>(workspace) & 255u))
+        return SAGA_ERR_WORKSPACE;
+    const saga::Workspace w = saga::carve(workspace, B, h_q, h_k, d, N, S_max, false, &sw, esize);
+    const bool bf16 = dtype == SAGA_BF16;
+    clear_stale_error();
+    // Step 1 on the kept dims into candidate lists with chunk statistics (the
+    // window is ranked by nobody), then Steps 2-3 in one dispatch per row
+    const saga::TopmOut tm{w.cand, w.cand_meta, N - local, w.cand_stat};
+    s = from_hip(saga::launch_sparq_scan(q, kt_cache, seq_lens, tm, sw, B, h_q, h_k, d, r, local,
+                                         S_max, bf16, dims_out, stream),
+                 "sparq_scan");
+    if (s != SAGA_OK) return s;
+    return from_hip(saga::launch_select_sparq(tm, sw, seq_lens, B, h_q, h_k, h_v, d, N, local,
+                                              S_max, w.sel_idx, w.sel_val, w.row_max, w.row_cnt,
+                                              idx_out, w.row_flag, q, k_cache, v_cache, w.scores,
+                                              saga::score_stride(S_max), v_mean, out, alpha_out,
+                                              bf16, stream),
+                    "select_sparq");
 }
 
 saga_status saga_debug_scores(const void* q, const void* k_cache, const int32_t* seq_lens,

@@ -77,7 +77,9 @@ struct Gather {
 
     // out[c] = (sum of acc over the workgroup)[c] / l; lsum is each thread's
     // share of l (summed in a fixed order). red: LDS [NW][DH] + [NW] floats.
-    __device__ static void finish(float (&acc)[EPL], float lsum, float* red, float* o) {
+    // With vm (nullable, [DH]): out[c] = alpha (sum / l) + (1 - alpha) vm[c].
+    __device__ static void finish(float (&acc)[EPL], float lsum, float* red, float* o,
+                                  float alpha = 1.f, const float* vm = nullptr) {
         const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
         const int rg = lane / LPR;
         const int sub = lane - rg * LPR;
@@ -101,7 +103,73 @@ struct Gather {
             float sacc = 0.f;
 #pragma unroll
             for (int w = 0; w < NW; ++w) sacc += s_red[w * DH + c];
-            o[c] = sacc / l;   // l >= 1: the largest kept logit has weight 1
+            const float y = sacc / l;   // l >= 1: the largest kept logit has weight 1
+            o[c] = vm ? alpha * y + (1.f - alpha) * vm[c] : y;
+        }
+    }
+};
+
+// Dot products of gathered key rows with two query vectors, in the lane layout
+// of Gather: for each entry e < n of the LDS list pos, za[e] = <qa, K[pos[e]]>
+// (written to LDS by the row's first lane) and zb = <qb, K[pos[e]]>. Each lane
+// holds its EPL columns of qa and qb; the row's LPR lanes sum their partial
+// dots by butterfly. Accumulates, per thread, se += exp(zb - shift) and
+// mz = max(mz, za) over the entries whose first lane it is.
+template <typename T, int DH>
+struct KeyDots {
+    using G = Gather<T, DH>;
+    using R = typename G::R;
+    static constexpr int EPL = G::EPL, LPR = G::LPR, STEP = G::STEP, UNR = G::UNR,
+                         BATCH = G::BATCH, RPI = G::RPI, NW = G::NW;
+    __device__ static void run(const T* __restrict__ kb, const int32_t* pos, int n,
+                               const float (&qa)[EPL], const float (&qb)[EPL], float* za,
+                               float shift, float& se, float& mz) {
+        const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+        const int rg = lane / LPR;
+        const int sub = lane - rg * LPR;
+        const int first = wave * RPI + rg;
+        const int nb = (n + BATCH - 1) / BATCH;
+        if (nb == 0) return;   // uniform
+        u32x4 ra[UNR], rb[UNR];
+        auto issue = [&](u32x4 (&dst)[UNR], int j) {
+            j = j < nb ? j : nb - 1;   // past the last batch: re-read it (never used)
+#pragma unroll
+            for (int k = 0; k < UNR; ++k) {
+                const int e = j * BATCH + first + k * STEP;
+                dst[k] = *reinterpret_cast<const u32x4*>(kb + (int64_t)pos[e] * DH + sub * EPL);
+            }
+        };
+        auto use = [&](const u32x4 (&src)[UNR], int j) {
+#pragma unroll
+            for (int k = 0; k < UNR; ++k) {
+                const int e = j * BATCH + first + k * STEP;
+                float f[EPL];
+                R::cvt(src[k], f);
+                float da = 0.f, db = 0.f;
+#pragma unroll
+                for (int c = 0; c < EPL; ++c) {
+                    da = fmaf(qa[c], f[c], da);
+                    db = fmaf(qb[c], f[c], db);
+                }
+#pragma unroll
+                for (int off = 1; off < LPR; off <<= 1) {
+                    da += __shfl_xor(da, off, 64);
+                    db += __shfl_xor(db, off, 64);
+                }
+                if (sub == 0 && e < n) {
+                    za[e] = da;
+                    se += __expf(db - shift);
+                    mz = fmaxf(mz, da);
+                }
+            }
+        };
+        issue(ra, 0);
+#pragma unroll 1
+        for (int j = 0; j < nb; j += 2) {
+            issue(rb, j + 1);
+            use(ra, j);
+            issue(ra, j + 2);
+            if (j + 1 < nb) use(rb, j + 1);   // uniform
         }
     }
 };

@@ -34,6 +34,14 @@ struct Workspace {
     size_t bytes;
 };
 
+// SparQ-style scoring state per call (written by the scan's set-up kernel):
+struct SparqWs {
+    int32_t* dims;     // [B*h_k][RP]   kept query dims, ascending, -1 padded (RP = round_up(r, 16))
+    void* qop;         // [B*h_k][d/16][64] x 4 elements of the cache type: the scan's query operand
+    float* inv_tau;    // [B*h_q]       1 / tau (0: no query mass on the dims)
+    float* qm;         // [B*h_q][d]    q / tau on the dims, 0 elsewhere
+};
+
 inline int num_chunks(int64_t S_max) { return (int)((S_max + kScanChunk - 1) / kScanChunk); }
 
 // Whether saga_decode_attn takes the top-M K-scan + union select path.
@@ -41,8 +49,10 @@ bool use_union_path(int h_q, int h_k, int64_t S_max);
 int max_union_chunks();
 
 // Carve the decode workspace (dense == false) or the dense one out of `base`
-// (base may be null to only compute the size).
-Workspace carve(void* base, int B, int h_q, int h_k, int d, int N, int64_t S_max, bool dense);
+// (base may be null to only compute the size). With sq, the SparQ state
+// follows the decode part (esize: bytes per cache element).
+Workspace carve(void* base, int B, int h_q, int h_k, int d, int N, int64_t S_max, bool dense,
+                SparqWs* sq = nullptr, int esize = 2);
 
 // Dense attention: positions per work item for a key group of g query heads,
 // and chunks (partials) per (b, i) row.
@@ -109,6 +119,26 @@ hipError_t launch_select_pv(const TopmOut& tm, const int32_t* lens, int B, int h
                             int32_t* row_flag, const void* q, const void* k, const void* v,
                             float* scores, int64_t s_stride, float* out, bool bf16,
                             hipStream_t st);
+
+// SparQ-style scoring (h_q / h_k <= 16): the set-up kernel (dims, 1 / tau,
+// qm, the scan operand; dims_out nullable [B*h_k][r]) and the scan of the r
+// kept columns of kt [B][h_k][d][S_max] into candidate lists (tm.N = N - local,
+// tm.stat required); positions of the last `local` are left out of the lists.
+hipError_t launch_sparq_scan(const void* q, const void* kt, const int32_t* lens, const TopmOut& tm,
+                             const SparqWs& sw, int B, int h_q, int h_k, int d, int r, int local,
+                             int64_t S_max, bool bf16, int32_t* dims_out, hipStream_t st);
+
+// Union select over the SparQ candidate lists, the window appended, exact
+// rescoring of the kept rows, the value gather and Step 3's mix with vmean
+// (nullable [B][h_v][d]) into out; alpha_out (nullable) [B*h_q].
+hipError_t launch_select_sparq(const TopmOut& tm, const SparqWs& sw, const int32_t* lens, int B,
+                               int h_q, int h_k, int h_v, int d, int N, int local, int64_t S_max,
+                               int32_t* sel_idx, float* sel_val, float* row_max, int32_t* row_cnt,
+                               int32_t* idx_out, int32_t* row_flag, const void* q, const void* k,
+                               const void* v, float* scores, int64_t s_stride, const float* vmean,
+                               float* out, float* alpha_out, bool bf16, hipStream_t st);
+// Whether launch_select_sparq can stage N kept entries in LDS.
+bool sparq_select_fits(int N);
 
 hipError_t launch_pv_sparse(const void* v, const int32_t* sel_idx, const float* sel_val,
                             const float* row_max, const int32_t* row_cnt, float* out, int B,

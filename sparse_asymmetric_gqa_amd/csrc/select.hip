@@ -380,15 +380,17 @@ __global__ __launch_bounds__(kSelectThreads) void select_dense(
 // ---- union select over the top-M candidate lists ----------------------------------
 // Fallback logits of one head, VALU, written to a dense row: lane-parallel over
 // positions, q staged in LDS as fp32.
+// With qf (fp32 [DH], nullable) the query is taken from qf instead of q.
 template <typename T, int DH>
 __device__ void head_logits(const T* __restrict__ q, const T* __restrict__ k, int b, int i,
                             int h_q, int h_k, int64_t S_max, int64_t L, float scale,
-                            float* __restrict__ out, float* qs) {
+                            float* __restrict__ out, float* qs, const float* qf = nullptr) {
     const int g = h_q / h_k;
     const int kh = i / g;
     const T* qr = q + (int64_t)(b * h_q + i) * DH;
     for (int c = threadIdx.x; c < DH; c += kUnionThreads) {
-        if (sizeof(T) == 2) qs[c] = __uint_as_float((uint32_t)((const uint16_t*)qr)[c] << 16);
+        if (qf) qs[c] = qf[c];
+        else if (sizeof(T) == 2) qs[c] = __uint_as_float((uint32_t)((const uint16_t*)qr)[c] << 16);
         else qs[c] = ((const float*)qr)[c];
     }
     __syncthreads();
@@ -433,7 +435,8 @@ __device__ void union_row(
     int N, int64_t S_max, int nchunk, int32_t* __restrict__ sel_idx, float* __restrict__ sel_val,
     float* __restrict__ row_max, int32_t* __restrict__ row_cnt, int32_t* __restrict__ idx_out,
     int32_t* __restrict__ row_flag, const T* __restrict__ q, const T* __restrict__ k,
-    float* __restrict__ scores, int64_t s_stride, float scale) {
+    float* __restrict__ scores, int64_t s_stride, float scale, int64_t L, int n_eff,
+    const float* qf) {
     constexpr int NT = kUnionThreads;
     constexpr int NW = NT / 64;
     constexpr int KPT = kUnionKPT;
@@ -444,8 +447,7 @@ __device__ void union_row(
     const int b = row / h_q;
     const int i = row - b * h_q;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int64_t L = clamp_len(lens[b], S_max);
-    const int n_eff = (int)((int64_t)N < L ? (int64_t)N : L);
+    (void)lens;
     int32_t* oi = sel_idx + (int64_t)row * N;
     float* ov = sel_val + (int64_t)row * N;
     int32_t* ou = idx_out ? idx_out + (int64_t)row * N : nullptr;
@@ -517,8 +519,8 @@ __device__ void union_row(
     if (!ok) {
         // dense fallback: this head's logits over all L positions, then a full select
         float* srow = scores + (int64_t)row * s_stride;
-        head_logits<T, DH>(q, k, b, i, h_q, h_k, S_max, L, scale, srow,
-                           reinterpret_cast<float*>(sh.hist));
+        head_logits<T, DH>(q, k, b, i, h_q, h_k, S_max, L, qf ? 1.f : scale, srow,
+                           reinterpret_cast<float*>(sh.hist), qf);
         using Src = DenseSrc<KPT, NW>;
         const Src src{srow, L};
         const int ntiles = (int)((L + Src::CAP - 1) / Src::CAP);
@@ -535,6 +537,59 @@ __device__ void union_row(
         row_cnt[row] = n_eff;
         row_flag[row] = ok ? 0 : 1;
     }
+}
+
+// LSE of a row from its chunks' {max, sum exp(z - max)}: M + log sum_c s_c
+// e^(m_c - M), M = max_c m_c. Also the largest chunk cutoff. Uniform results.
+struct RowStats {
+    float M, lse;
+    uint32_t maxcut;
+};
+__device__ inline RowStats row_stats(const float2* __restrict__ stat, const uint4* __restrict__ meta,
+                                     int nch, uint4* red, float* redf) {
+    constexpr int NT = kUnionThreads;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    uint32_t km = 0, cm = 0;
+    for (int c = tid; c < nch; c += NT) {
+        const uint32_t kx = float_key(stat[c].x);
+        km = kx > km ? kx : km;
+        const uint32_t cu = meta[c].z;
+        cm = cu > cm ? cu : cm;
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        const uint32_t y = (uint32_t)__shfl_xor((int)km, o, 64);
+        const uint32_t z = (uint32_t)__shfl_xor((int)cm, o, 64);
+        km = y > km ? y : km;
+        cm = z > cm ? z : cm;
+    }
+    if (lane == 0) red[wave] = make_uint4(km, cm, 0u, 0u);
+    __syncthreads();
+    km = 0;
+    cm = 0;
+#pragma unroll
+    for (int w = 0; w < NT / 64; ++w) {
+        km = red[w].x > km ? red[w].x : km;
+        cm = red[w].y > cm ? red[w].y : cm;
+    }
+    RowStats r;
+    r.M = key_float(km);
+    r.maxcut = cm;
+    float se = 0.f;
+    for (int c = tid; c < nch; c += NT) {
+        const float2 st = stat[c];
+        se += st.y * __expf(st.x - r.M);
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) se += __shfl_xor(se, o, 64);
+    if (lane == 0) redf[wave] = se;
+    __syncthreads();
+    float S = 0.f;
+#pragma unroll
+    for (int w = 0; w < NT / 64; ++w) S += redf[w];
+    r.lse = r.M + __logf(S);
+    return r;
 }
 
 // ---- union select, one workgroup per row -------------------------------------------
@@ -572,7 +627,25 @@ __host__ __device__ constexpr size_t select_stage_offset() {
 // max(sizeof(UnionShared), select_stage_offset() + 8 nst) bytes, nst >= the
 // kept entries of any fast-path row, a multiple of 4.
 //
-// FUSE: the same workgroup then forms the softmax weights of the kept entries
+// SparQ-style inputs of the select (MODE 2; empty for the other modes, so
+// they carry no extra kernel arguments).
+template <int MODE> struct SqArg {};
+template <> struct SqArg<2> {
+    const float* qm;        // [rows][DH] q / tau on the kept dims (the approximate logits)
+    const float2* stat;     // [rows][nchunk] chunk softmax statistics of those logits
+    int local;              // window: the last min(local, L) positions are always kept
+    const float* vmean;     // nullable [B][h_v][DH] running value means (Step 3)
+    float* alpha_out;       // nullable [rows]
+};
+template <int MODE> __device__ inline int sq_local(const SqArg<MODE>&) { return 0; }
+__device__ inline int sq_local(const SqArg<2>& a) { return a.local; }
+template <int MODE> __device__ inline const float* sq_qm(const SqArg<MODE>&, int, int) { return nullptr; }
+__device__ inline const float* sq_qm(const SqArg<2>& a, int row, int dh) {
+    return a.qm + (int64_t)row * dh;
+}
+
+// MODE 0 writes the kept lists (sel_idx / sel_val / idx_out).
+// MODE 1 (fused): the same workgroup then forms the softmax weights of the kept entries
 // and gathers their value rows (gather.h), writing out[row] directly: the
 // kept list never leaves LDS on the fast path (sel_idx / sel_val are not
 // written; idx_out is, when given). Rows are then mapped XCD-aware so the
@@ -581,7 +654,14 @@ __host__ __device__ constexpr size_t select_stage_offset() {
 // Dynamic LDS with FUSE adds the gather's reduction area after the staging:
 // nst a multiple of 256 and max(sizeof(UnionShared), select_stage_offset() +
 // 8 nst + 4 (4 DH + 4)) bytes.
-template <typename T, int DH, int KPT, bool FUSE>
+// MODE 2 (SparQ): the candidates rank approximate logits over the first
+// L - min(local, L) positions, N - local of them are kept and the window is
+// appended; the kept key rows are then gathered to rescore them exactly
+// (logits q.K / sqrt(d), and the approximate ones for alpha, the approximate
+// softmax mass of the kept set over the row's log-sum-exp from the chunk
+// statistics), and the value gather mixes in vmean with weight 1 - alpha. The
+// whole kept list (N entries) is staged in LDS: nst >= N.
+template <typename T, int DH, int KPT, int MODE>
 __global__ __launch_bounds__(kUnionThreads, 4) void select_union(
     const uint2* __restrict__ cand, const uint4* __restrict__ cand_meta,
     const int32_t* __restrict__ lens, int h_q, int h_k, int N, int64_t S_max, int nchunk, int nst,
@@ -589,22 +669,28 @@ __global__ __launch_bounds__(kUnionThreads, 4) void select_union(
     int32_t* __restrict__ row_cnt, int32_t* __restrict__ idx_out, int32_t* __restrict__ row_flag,
     const T* __restrict__ q, const T* __restrict__ k, float* __restrict__ scores,
     int64_t s_stride, float scale, const T* __restrict__ v, float* __restrict__ out, int h_v,
-    int rows) {
+    int rows, SqArg<MODE> sq) {
     static_assert(KPT % 2 == 0, "entries are loaded in pairs");
+    constexpr bool FUSE = MODE == 1;
+    constexpr bool SPQ = MODE == 2;
     constexpr int NT = kUnionThreads;
     using G = Gather<T, DH>;
-    static_assert(!FUSE || NT == kGatherThreads, "one gather workgroup per row");
+    static_assert(MODE == 0 || NT == kGatherThreads, "one gather workgroup per row");
     extern __shared__ __attribute__((aligned(16))) unsigned char sel_lds[];
     FastShared& F = *reinterpret_cast<FastShared*>(sel_lds);
     UnionShared& U = *reinterpret_cast<UnionShared*>(sel_lds);
-    const int row = FUSE ? xcd_logical((int)blockIdx.x, rows) : (int)blockIdx.x;
-    if (FUSE && row >= rows) return;   // the grid is rounded up to whole XCD shares
+    const int row = MODE ? xcd_logical((int)blockIdx.x, rows) : (int)blockIdx.x;
+    if (MODE && row >= rows) return;   // the grid is rounded up to whole XCD shares
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int b = row / h_q;
-    const int64_t L = clamp_len(lens[b], S_max);
-    const int n_eff = (int)((int64_t)N < L ? (int64_t)N : L);
+    const int64_t Lrow = clamp_len(lens[b], S_max);
+    // ranked positions [0, L) and the count kept from them (SparQ: the window is not ranked)
+    const int local = sq_local(sq);
+    const int64_t L = SPQ ? Lrow - (local < Lrow ? local : Lrow) : Lrow;
+    const int n_rank = SPQ ? N - local : N;
+    const int n_eff = (int)((int64_t)n_rank < L ? (int64_t)n_rank : L);
     const int nch = (int)((L + kScanChunk - 1) / kScanChunk);
     // fused gather: the value head's rows, the staged lists and the reduction area
     const T* vb = v + (int64_t)(b * h_v + (row - b * h_q) / (h_q / h_v)) * S_max * DH;
@@ -613,8 +699,8 @@ __global__ __launch_bounds__(kUnionThreads, 4) void select_union(
     float* g_red = g_w + nst;
     auto general = [&] {
         union_row<T, DH>(row, U, cand, cand_meta, lens, h_q, h_k, N, S_max, nchunk, sel_idx,
-                         sel_val, row_max, row_cnt, idx_out, row_flag, q, k, scores, s_stride,
-                         scale);
+                         sel_val, row_max, row_cnt, SPQ ? nullptr : idx_out, row_flag, q, k,
+                         scores, s_stride, scale, L, n_eff, sq_qm(sq, row, DH));
         if constexpr (FUSE) {
             // the list union_row wrote, read back in blocks of nst entries
             __threadfence();
@@ -833,6 +919,7 @@ __global__ __launch_bounds__(kUnionThreads, 4) void select_union(
             G::finish(acc, lsum, g_red, out + (int64_t)row * DH);
             return true;
         }
+        if constexpr (SPQ) return true;   // the list stays staged for the SparQ tail
         const bool v4 = (((uintptr_t)oi | (uintptr_t)ov | (uintptr_t)ou) & 15u) == 0;
         const int n4 = v4 ? n_eff / 4 : 0;
         for (int j = tid; j < n4; j += NT) {
@@ -850,7 +937,98 @@ __global__ __launch_bounds__(kUnionThreads, 4) void select_union(
 
         return true;
     };
-    if (n_eff == 0 || nch > NT || !fast()) general();   // no kept entry, too many chunks, or no proof
+    if constexpr (!SPQ) {
+        if (n_eff == 0 || nch > NT || !fast()) general();   // no kept entry, too many chunks, or no proof
+        return;
+    } else {
+        int32_t* st_idx = g_pos;
+        float* st_val = g_w;
+        if (n_eff == 0 && tid == 0) {   // nothing ranked (only the window, or L_b = 0)
+            row_max[row] = -__builtin_inff();
+            row_cnt[row] = 0;
+            row_flag[row] = 0;
+        }
+        if (n_eff > 0 && (nch > NT || !fast())) {
+            // the general code writes the list; read it back into the stage
+            general();
+            __threadfence();
+            __syncthreads();
+            for (int e = tid; e < n_eff; e += NT) {
+                int32_t p = __hip_atomic_load(sel_idx + (int64_t)row * N + e, __ATOMIC_RELAXED,
+                                              __HIP_MEMORY_SCOPE_AGENT);
+                st_idx[e] = p < 0 ? 0 : (p >= L ? (int32_t)(L - 1) : p);
+            }
+        }
+        // the window follows the ranked entries (all below L); pad with row 0
+        const int n = n_eff + (int)(Lrow - L);
+        for (int e = n_eff + tid; e < nst; e += NT) st_idx[e] = e < n ? (int32_t)(L + (e - n_eff)) : 0;
+        __syncthreads();
+        if (idx_out)
+            for (int e = tid; e < N; e += NT) idx_out[(int64_t)row * N + e] = e < n ? st_idx[e] : -1;
+        float* o = out + (int64_t)row * DH;
+        if (n == 0) {   // L_b = 0: nothing kept
+            for (int c = tid; c < DH; c += NT) o[c] = 0.f;
+            if (sq.alpha_out && tid == 0) sq.alpha_out[row] = 0.f;
+            return;
+        }
+        // log-sum-exp of the approximate logits over all L_b positions
+        float* sred = g_red + 4 * DH + 4;   // [4] uint4 + [4] + [8] floats past the gather's area
+        const int nchr = (int)((Lrow + kScanChunk - 1) / kScanChunk);
+        const RowStats rs = row_stats(sq.stat + (int64_t)row * nchunk,
+                                      cand_meta + (int64_t)row * nchunk, nchr,
+                                      reinterpret_cast<uint4*>(sred), sred + 16);
+        // exact logits of the kept rows, and alpha from their approximate ones
+        using KD = KeyDots<T, DH>;
+        const int i = row - b * h_q;
+        const T* kb = k + (int64_t)(b * h_k + i / (h_q / h_k)) * S_max * DH;
+        float qa[G::EPL], qb[G::EPL];
+        {
+            const int sub = lane % G::LPR;
+            const T* qr = q + (int64_t)row * DH + sub * G::EPL;
+            const float* qmr = sq.qm + (int64_t)row * DH + sub * G::EPL;
+#pragma unroll
+            for (int c = 0; c < G::EPL; ++c) {
+                float x;
+                if constexpr (sizeof(T) == 2)
+                    x = __uint_as_float((uint32_t)reinterpret_cast<const uint16_t*>(qr)[c] << 16);
+                else
+                    x = reinterpret_cast<const float*>(qr)[c];
+                qa[c] = x * scale;
+                qb[c] = qmr[c];
+            }
+        }
+        float se = 0.f, mz = -__builtin_inff();
+        KD::run(kb, st_idx, n, qa, qb, st_val, rs.lse, se, mz);
+        se = wave_fsum(se);
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) mz = fmaxf(mz, __shfl_xor(mz, off, 64));
+        if (lane == 0) {
+            sred[20 + wave] = se;
+            sred[24 + wave] = mz;
+        }
+        __syncthreads();
+        float alpha = 0.f, zmax = -__builtin_inff();
+#pragma unroll
+        for (int w = 0; w < NT / 64; ++w) {
+            alpha += sred[20 + w];
+            zmax = fmaxf(zmax, sred[24 + w]);
+        }
+        float lsum = 0.f;
+        for (int e = tid; e < nst; e += NT) {
+            const float wgt = e < n ? __expf(st_val[e] - zmax) : 0.f;
+            st_val[e] = wgt;
+            lsum += wgt;
+        }
+        __syncthreads();
+        float acc[G::EPL];
+#pragma unroll
+        for (int c = 0; c < G::EPL; ++c) acc[c] = 0.f;
+        G::run(vb, st_idx, st_val, n, acc);
+        const int vh = i / (h_q / h_v);
+        G::finish(acc, lsum, g_red, o, alpha,
+                  sq.vmean ? sq.vmean + (int64_t)(b * h_v + vh) * DH : nullptr);
+        if (sq.alpha_out && tid == 0) sq.alpha_out[row] = alpha;
+    }
 }
 
 // ---- Atop-N: stale-threshold selection and calibration ---------------------------
@@ -860,58 +1038,6 @@ __global__ __launch_bounds__(kUnionThreads, 4) void select_union(
 // log-sum-exp of the row's logits -- at most 2N of them (the first 2N in
 // position order here), and attend over those.
 
-// LSE of a row from its chunks' {max, sum exp(z - max)}: M + log sum_c s_c
-// e^(m_c - M), M = max_c m_c. Also the largest chunk cutoff. Uniform results.
-struct RowStats {
-    float M, lse;
-    uint32_t maxcut;
-};
-__device__ inline RowStats row_stats(const float2* __restrict__ stat, const uint4* __restrict__ meta,
-                                     int nch, uint4* red, float* redf) {
-    constexpr int NT = kUnionThreads;
-    const int tid = threadIdx.x, lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    uint32_t km = 0, cm = 0;
-    for (int c = tid; c < nch; c += NT) {
-        const uint32_t kx = float_key(stat[c].x);
-        km = kx > km ? kx : km;
-        const uint32_t cu = meta[c].z;
-        cm = cu > cm ? cu : cm;
-    }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-        const uint32_t y = (uint32_t)__shfl_xor((int)km, o, 64);
-        const uint32_t z = (uint32_t)__shfl_xor((int)cm, o, 64);
-        km = y > km ? y : km;
-        cm = z > cm ? z : cm;
-    }
-    if (lane == 0) red[wave] = make_uint4(km, cm, 0u, 0u);
-    __syncthreads();
-    km = 0;
-    cm = 0;
-#pragma unroll
-    for (int w = 0; w < NT / 64; ++w) {
-        km = red[w].x > km ? red[w].x : km;
-        cm = red[w].y > cm ? red[w].y : cm;
-    }
-    RowStats r;
-    r.M = key_float(km);
-    r.maxcut = cm;
-    float se = 0.f;
-    for (int c = tid; c < nch; c += NT) {
-        const float2 st = stat[c];
-        se += st.y * __expf(st.x - r.M);
-    }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) se += __shfl_xor(se, o, 64);
-    if (lane == 0) redf[wave] = se;
-    __syncthreads();
-    float S = 0.f;
-#pragma unroll
-    for (int w = 0; w < NT / 64; ++w) S += redf[w];
-    r.lse = r.M + __logf(S);
-    return r;
-}
 
 struct ThreshShared {
     uint4 red[kUnionThreads / 64];
@@ -1180,42 +1306,52 @@ hipError_t launch_select(const float* scores, int64_t s_stride, const int32_t* l
 
 namespace {
 
-template <bool FUSE>
+// Kept entries the SparQ select stages in LDS at most.
+constexpr int kSparqMaxN = 4096;
+
+template <int MODE>
 hipError_t go_select_union(const TopmOut& tm, const int32_t* lens, int B, int h_q, int h_k, int d,
                            int N, int64_t S_max, int32_t* sel_idx, float* sel_val,
                            float* row_max, int32_t* row_cnt, int32_t* idx_out, int32_t* row_flag,
                            const void* q, const void* k, float* scores, int64_t s_stride,
-                           bool bf16, const void* v, float* out, int h_v, hipStream_t st) {
+                           bool bf16, const void* v, float* out, int h_v,
+                           const SqArg<MODE>& sq, hipStream_t st) {
     const int nchunk = (int)((S_max + kScanChunk - 1) / kScanChunk);
     const int rows = B * h_q;
     const float scale = (float)(1.0 / __builtin_sqrt((double)d));
     // Register slots per thread for the fast path: the longest run, an even
     // ceil(per_chunk / tpc) with tpc = floor(256 / chunks) threads per chunk
     // and up to per_chunk = 1.25 (1.5 share + 16) keys in a full chunk's list
-    // (share = N * 1024 / L); rows with longer runs take the general code.
-    const double share = (double)N * kScanChunk / (double)S_max;
+    // (share = N * 1024 / L, N the ranked count); rows with longer runs take
+    // the general code.
+    int n_rank = N;
+    if constexpr (MODE == 2) n_rank = N - sq.local;
+    const double share = (double)n_rank * kScanChunk / (double)S_max;
     int64_t per_chunk = (int64_t)(1.25 * (1.5 * share + 16.0)) + 1;
     per_chunk = per_chunk < kScanChunk ? per_chunk : kScanChunk;
     const int64_t tpc = nchunk <= kUnionThreads ? kUnionThreads / nchunk : 1;
     const int64_t slots = (((per_chunk + tpc - 1) / tpc) + 1) & ~(int64_t)1;
     // staged kept entries: N_eff <= N, and <= the 256 KPT keys in registers
-    // (the fused gather reads them in whole batches: a multiple of 256)
+    // (the gathers read them in whole batches: a multiple of 256); SparQ
+    // stages the whole list, window included
     auto nst_for = [&](int kpt) -> int {
+        if (MODE == 2) return (int)round_up(N, 256);
         int64_t nst = (int64_t)N < (int64_t)kUnionThreads * kpt ? (int64_t)N : (int64_t)kUnionThreads * kpt;
-        return (int)(FUSE ? (nst + 255) & ~(int64_t)255 : (nst + 3) & ~(int64_t)3);
+        return (int)(MODE == 1 ? (nst + 255) & ~(int64_t)255 : (nst + 3) & ~(int64_t)3);
     };
     auto lds_for = [&](int kpt) -> size_t {
         size_t fast = select_stage_offset() + (size_t)nst_for(kpt) * 8;
-        if (FUSE) fast += (size_t)(4 * d + 4) * sizeof(float);
+        if (MODE >= 1) fast += (size_t)(4 * d + 4) * sizeof(float);
+        if (MODE == 2) fast += 32 * sizeof(float);
         return fast > sizeof(UnionShared) ? fast : sizeof(UnionShared);
     };
-    const unsigned grid = FUSE ? (unsigned)(((rows + 7) / 8) * 8) : (unsigned)rows;
+    const unsigned grid = MODE ? (unsigned)(((rows + 7) / 8) * 8) : (unsigned)rows;
 #define SAGA_SU(T, D, KPT)                                                                       \
-    hipLaunchKernelGGL((select_union<T, D, KPT, FUSE>), dim3(grid), dim3(kUnionThreads),          \
+    hipLaunchKernelGGL((select_union<T, D, KPT, MODE>), dim3(grid), dim3(kUnionThreads),          \
                        (unsigned)lds_for(KPT), st, tm.cand, tm.meta, lens, h_q, h_k, N, S_max,     \
                        nchunk, nst_for(KPT), sel_idx, sel_val, row_max, row_cnt, idx_out, row_flag, \
                        (const T*)q, (const T*)k, scores, s_stride, scale, (const T*)v, out, h_v,   \
-                       rows)
+                       rows, sq)
 #define SAGA_SU_K(T, D)                                                                          \
     if (slots <= 8) SAGA_SU(T, D, 8);                                                            \
     else if (slots <= 16) SAGA_SU(T, D, 16);                                                     \
@@ -1237,9 +1373,9 @@ hipError_t launch_select_union(const TopmOut& tm, const int32_t* lens, int B, in
                                float* row_max, int32_t* row_cnt, int32_t* idx_out,
                                int32_t* row_flag, const void* q, const void* k, float* scores,
                                int64_t s_stride, bool bf16, hipStream_t st) {
-    return go_select_union<false>(tm, lens, B, h_q, h_k, d, N, S_max, sel_idx, sel_val, row_max,
-                                  row_cnt, idx_out, row_flag, q, k, scores, s_stride, bf16,
-                                  nullptr, nullptr, 1, st);
+    return go_select_union<0>(tm, lens, B, h_q, h_k, d, N, S_max, sel_idx, sel_val, row_max,
+                              row_cnt, idx_out, row_flag, q, k, scores, s_stride, bf16, nullptr,
+                              nullptr, 1, SqArg<0>{}, st);
 }
 
 hipError_t launch_select_pv(const TopmOut& tm, const int32_t* lens, int B, int h_q, int h_k,
@@ -1248,9 +1384,23 @@ hipError_t launch_select_pv(const TopmOut& tm, const int32_t* lens, int B, int h
                             int32_t* row_flag, const void* q, const void* k, const void* v,
                             float* scores, int64_t s_stride, float* out, bool bf16,
                             hipStream_t st) {
-    return go_select_union<true>(tm, lens, B, h_q, h_k, d, N, S_max, sel_idx, sel_val, row_max,
-                                 row_cnt, idx_out, row_flag, q, k, scores, s_stride, bf16, v, out,
-                                 h_v, st);
+    return go_select_union<1>(tm, lens, B, h_q, h_k, d, N, S_max, sel_idx, sel_val, row_max,
+                              row_cnt, idx_out, row_flag, q, k, scores, s_stride, bf16, v, out,
+                              h_v, SqArg<1>{}, st);
+}
+
+bool sparq_select_fits(int N) { return N >= 1 && N <= kSparqMaxN; }
+
+hipError_t launch_select_sparq(const TopmOut& tm, const SparqWs& sw, const int32_t* lens, int B,
+                               int h_q, int h_k, int h_v, int d, int N, int local, int64_t S_max,
+                               int32_t* sel_idx, float* sel_val, float* row_max, int32_t* row_cnt,
+                               int32_t* idx_out, int32_t* row_flag, const void* q, const void* k,
+                               const void* v, float* scores, int64_t s_stride, const float* vmean,
+                               float* out, float* alpha_out, bool bf16, hipStream_t st) {
+    const SqArg<2> sq{sw.qm, tm.stat, local, vmean, alpha_out};
+    return go_select_union<2>(tm, lens, B, h_q, h_k, d, N, S_max, sel_idx, sel_val, row_max,
+                              row_cnt, idx_out, row_flag, q, k, scores, s_stride, bf16, v, out,
+                              h_v, sq, st);
 }
 
 hipError_t launch_select_thresh(const TopmOut& tm, const int32_t* lens, const float* tau, int B,

@@ -1,0 +1,252 @@
+// Top-M candidate extraction shared by the K-scan kernels that keep logits
+// on chip (kscan_topm, sparq_topm): the consumer side of the producer /
+// consumer workgroup, its list sink, and the persistent-grid helpers.
+#ifndef SAGA_TOPM_H
+#define SAGA_TOPM_H
+#include "kstream.h"
+
+namespace saga {
+using namespace dev;
+
+namespace {
+
+constexpr int kConsumers = 8;      // extracting waves of kscan_topm
+constexpr int kTopmThreads = 64 * (kWaves + kConsumers);
+// Candidates of one head staged in its own LDS row before the global write:
+// entries [0, kStageMax) hold data, [kStageMax, kStageMax + 64) are per-lane
+// sinks for the branch-free writes of entries that are not kept.
+constexpr uint32_t kStageMax = kScanChunk / 2 - 64;
+constexpr size_t kTopmLdsBytes = 160 * 1024;   // LDS of a gfx950 CU: one workgroup per CU
+
+// Candidate extraction of head n of item `it` by one consumer wave, from the
+// head's key row in LDS (every offset of the row was written for this item, 0
+// past the chunk's end). Lane l takes offsets [16 l, 16 l + 16), so lane order
+// is position order. The cutoff is a key with M <= count(key >= cutoff) <=
+// M + M/4 where one is found within a bracket of 2^12, else the largest probed
+// key with count >= M. The search starts from the cutoff this wave found for
+// the same head on its previous item (the workgroup walks consecutive chunks
+// of a row, so that is usually close), gallops away from it and bisects;
+// without a previous cutoff it bisects the whole key range. Counts are
+// per-lane vector sums reduced once per probe. Positions at or after
+// local_from (a window the caller keeps anyway) count in the chunk statistics
+// but are left out of the ranking and of the list.
+// The keys at or above the cutoff are then written in position order: a
+// prefix scan of the per-lane counts gives each lane its first slot.
+// Destination of the candidate lists of one workgroup: the workgroup's pool
+// range (entries from `base`), filled in order through an LDS cursor; the
+// first `cap` entries are staged in LDS (`stg`) and written out once, at the
+// end of the kernel, so that no list store competes with the K stream.
+struct ListSink {
+    uint2* pool;        // global: the workgroup's range
+    uint64_t base;      // its first entry (absolute index into the pool)
+    uint2* stg;         // LDS staging of entries [0, cap)
+    uint32_t cap;
+    uint32_t* cursor;   // LDS: next free entry (relative to base)
+    uint32_t* used;     // LDS: end of the staged lists
+    uint4* meta_stg;    // LDS: metadata records of the first kMetaStage (item, head) pairs
+    uint32_t* meta_slot;   // LDS: their slots
+};
+constexpr int kMetaStage = 256;
+
+template <typename T>
+__device__ inline void extract(const Item<T>& it, int n, uint32_t M, uint32_t* row,
+                               uint32_t* warm, const ListSink& sink, int local, int lane, int g,
+                               int h_q, int nchunk, const TopmOut& tm, int local_from) {
+    uint32_t kk[16];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const u32x4 v = *reinterpret_cast<const u32x4*>(row + 16 * lane + 4 * j);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) kk[4 * j + c] = v[c];
+    }
+    const uint32_t guess = warm[n];
+    __builtin_amdgcn_s_waitcnt(0xc07f);   // keys are in registers before the row is reused
+    if (tm.stat) {   // uniform
+        // the chunk's softmax statistics for this head: its largest logit and
+        // the sum of exp(logit - largest); empty slots hold key 0, below
+        // every real key, and are left out of the sum
+        uint32_t kx = 0;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) kx = kk[e] > kx ? kk[e] : kx;
+        const float mx = key_float(wave_umax(kx));
+        float se = 0.f;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) se += kk[e] != 0u ? __expf(key_float(kk[e]) - mx) : 0.f;
+        se = wave_fsum(se);
+        if (lane == 0)
+            tm.stat[(int64_t)(it.b * h_q + it.kh * g + n) * nchunk + it.chunk] = make_float2(mx, se);
+    }
+    if (local_from < it.c0 + it.n) {   // uniform: positions from local_from on are not ranked
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+            if (it.c0 + 16 * lane + e >= local_from) kk[e] = 0u;
+    }
+    auto count_ge = [&](uint32_t x) -> uint32_t {
+        uint32_t c[4] = {0u, 0u, 0u, 0u};   // independent partial sums
+#pragma unroll
+        for (int e = 0; e < 16; ++e) c[e & 3] += kk[e] >= x ? 1u : 0u;
+        return wave_sum((c[0] + c[1]) + (c[2] + c[3]));
+    };
+    uint32_t cut = 0;   // publish everything when the chunk holds <= M keys
+    if ((uint32_t)it.n > M) {
+        const uint32_t hi = M + (M >> 2);
+        // Invariant of the search: count(key >= a) >= M (a = 0 counts every
+        // slot) and count(key >= z) < M (z = 2^32, as a 64-bit bound).
+        uint32_t a = 0;
+        uint64_t z = 1ull << 32;
+        bool done = false;
+        if (guess != 0u) {
+            // gallop from the previous cutoff in steps that double from 2^18
+            // (about 3 % of the value for an fp32 logit) until the count
+            // crosses M, then bisect between the last two probes
+            uint32_t c = count_ge(guess);
+            if (c >= M && c <= hi) {
+                cut = guess;
+                done = true;
+            } else if (c > hi) {
+                a = guess;
+                uint64_t step = 1ull << 18;
+#pragma unroll 1
+                while (true) {
+                    const uint64_t x = (uint64_t)a + step;
+                    if (x >= z) break;
+                    c = count_ge((uint32_t)x);
+                    if (c < M) { z = x; break; }
+                    a = (uint32_t)x;
+                    if (c <= hi) { cut = a; done = true; break; }
+                    step <<= 1;
+                }
+            } else {
+                z = guess;
+                uint64_t step = 1ull << 18;
+#pragma unroll 1
+                while (true) {
+                    if ((uint64_t)a + step >= z) break;
+                    const uint32_t x = (uint32_t)(z - step);
+                    c = count_ge(x);
+                    if (c >= M) {
+                        a = x;
+                        if (c <= hi) { cut = a; done = true; }
+                        break;
+                    }
+                    z = x;
+                    step <<= 1;
+                }
+            }
+        }
+        if (!done) {
+            // bisection of [a, z) down to a width of 2^12
+#pragma unroll 1
+            while (z - a > (1ull << 12)) {
+                const uint32_t x = (uint32_t)(a + ((z - a) >> 1));
+                const uint32_t c = count_ge(x);
+                if (c >= M) {
+                    a = x;
+                    if (c <= hi) break;
+                } else {
+                    z = x;
+                }
+            }
+            cut = a;
+        }
+        if (lane == 0) warm[n] = cut;
+    }
+    const uint32_t lo = cut > 1u ? cut : 1u;   // key 0 marks an empty slot
+    uint32_t kc = 0;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) kc += kk[e] >= lo ? 1u : 0u;
+    uint32_t total;
+    const uint32_t first = wave_incl_scan(kc, total) - kc;
+    const int64_t slot = ((int64_t)(it.b * h_q + it.kh * g + n) * nchunk + it.chunk);
+    // the list goes to the next free (16-byte aligned) place of the
+    // workgroup's range: staged in LDS while it fits, else stored directly
+    uint32_t off = 0;
+    if (lane == 0) off = atomicAdd(sink.cursor, (total + 1u) & ~1u);
+    off = __builtin_amdgcn_readfirstlane(off);
+    const bool staged_lds = off + total <= sink.cap;
+    if (staged_lds && lane == 0) atomicMax(sink.used, off + total);
+    uint2* dst = staged_lds ? sink.stg + off : sink.pool + off;
+    uint32_t pos0 = (uint32_t)(it.c0 + 16 * lane);
+    asm volatile("" : "+v"(pos0));   // positions are formed at each store, not held in registers
+    if (total <= kStageMax) {
+        uint2* stage = reinterpret_cast<uint2*>(row);
+        uint32_t at = first;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            const uint32_t keep = kk[e] >= lo ? 1u : 0u;
+            stage[keep ? at : kStageMax + lane] = make_uint2(pos0 + e, kk[e]);
+            at += keep;
+        }
+        __builtin_amdgcn_s_waitcnt(0xc07f);
+        for (uint32_t j = 2 * lane; j < total; j += 128) {
+            u32x4 v2;
+            const uint2 a0 = stage[j];
+            const uint2 a1 = j + 1 < total ? stage[j + 1] : make_uint2(0u, 0u);
+            v2[0] = a0.x; v2[1] = a0.y; v2[2] = a1.x; v2[3] = a1.y;
+            *reinterpret_cast<u32x4*>(dst + j) = v2;   // dst + j is 16-byte aligned (j even)
+        }
+        __builtin_amdgcn_s_waitcnt(0xc07f);   // the head's row is reused as soon as this returns
+    } else {
+        uint32_t at = first;
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+            if (kk[e] >= lo) dst[at++] = make_uint2(pos0 + e, kk[e]);
+    }
+    if (lane == 0) {
+        const uint64_t abs_off = sink.base + off;
+        const uint4 m = make_uint4((uint32_t)abs_off, total, cut, (uint32_t)(abs_off >> 32));
+        const int e = local * g + n;   // staged while it fits, like the lists
+        if (e < kMetaStage) {
+            sink.meta_stg[e] = m;
+            sink.meta_slot[e] = (uint32_t)slot;
+        } else {
+            tm.meta[slot] = m;
+        }
+    }
+}
+
+int cu_count() {
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (!cached[dev]) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            n <= 0)
+            n = 256;
+        cached[dev] = n;
+    }
+    return cached[dev];
+}
+
+// Persistent grid: as many workgroups as can be resident at once (so none of
+// them waits for another to finish all of its work before starting), at most
+// one per work item. Residency per CU is queried once per kernel and LDS size.
+template <typename K>
+int resident_grid(K kern, int threads, size_t lds, int nwork) {
+    static const void* cached_k[16] = {nullptr};
+    static int cached_lds[16] = {0};
+    static int cached_blocks[16] = {0};
+    int per_cu = 0;
+    for (int i = 0; i < 16; ++i)
+        if (cached_k[i] == (const void*)kern && cached_lds[i] == (int)lds) per_cu = cached_blocks[i];
+    if (per_cu == 0) {
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, threads, lds) !=
+                hipSuccess ||
+            per_cu <= 0)
+            per_cu = 1;
+        for (int i = 0; i < 16; ++i)
+            if (cached_k[i] == nullptr) {
+                cached_k[i] = (const void*)kern;
+                cached_lds[i] = (int)lds;
+                cached_blocks[i] = per_cu;
+                break;
+            }
+    }
+    const int grid = cu_count() * per_cu;
+    return grid < nwork ? grid : nwork;
+}
+
+}  // namespace
+}  // namespace saga
+#endif

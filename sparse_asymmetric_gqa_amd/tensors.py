@@ -155,3 +155,36 @@ def atopn_attn(q, k_cache, v_cache, seq_lens, N, tau, *, out=None, workspace=Non
     if st != C.SAGA_OK:
         raise C.SagaError(st, "saga_atopn_attn")
     return out
+
+
+def sparq_workspace_size(q, k_cache, v_cache, seq_lens, N, r) -> int:
+    B, h_q, h_k, h_v, d, S = _shapes(q, k_cache, v_cache, seq_lens)
+    return C.saga_sparq_workspace_size(B, h_q, h_k, h_v, d, N, r, S, _dtype_code(q))
+
+
+def sparq_attn(q, k_cache, kt_cache, v_cache, seq_lens, N, r, local=0, *, v_mean=None, out=None,
+               workspace=None, idx_out=None, alpha_out=None, dims_out=None, stream=None):
+    """SparQ-style step: approximate scores over r query dims from kt_cache
+    ([B][h_k][d][S_max], the keys S-contiguous), the last `local` positions
+    always kept, exact attention over the kept set, optional mean-value mix
+    with v_mean (float32 [B][h_v][d]). Returns out (float32 [B][h_q][d])."""
+    B, h_q, h_k, h_v, d, S = _shapes(q, k_cache, v_cache, seq_lens)
+    if tuple(kt_cache.shape) != (B, h_k, d, S) or kt_cache.dtype != q.dtype:
+        raise ValueError("kt_cache must be [B][h_k][d][S_max] in the cache dtype")
+    if not kt_cache.is_cuda or not kt_cache.is_contiguous():
+        raise ValueError("kt_cache must be a contiguous device tensor")
+    if v_mean is not None and (v_mean.dtype != torch.float32 or tuple(v_mean.shape) != (B, h_v, d)
+                               or not v_mean.is_cuda or not v_mean.is_contiguous()):
+        raise ValueError("v_mean must be a contiguous float32 device tensor [B][h_v][d]")
+    dt = _dtype_code(q)
+    if workspace is None:
+        workspace = new_workspace(C.saga_sparq_workspace_size(B, h_q, h_k, h_v, d, N, r, S, dt),
+                                  q.device)
+    if out is None:
+        out = torch.empty((B, h_q, d), dtype=torch.float32, device=q.device)
+    st = C.saga_sparq_attn(q, k_cache, kt_cache, v_cache, seq_lens, out, B, h_q, h_k, h_v, d, N,
+                           r, local, v_mean, _stream(stream), S, dt, workspace, workspace.numel(),
+                           idx_out, alpha_out, dims_out)
+    if st != C.SAGA_OK:
+        raise C.SagaError(st, "saga_sparq_attn")
+    return out

@@ -159,3 +159,54 @@ def test_atopn_workspace_holds_2N_slots():
         assert n % 256 == 0 and n >= ws(*args)
         assert n >= ws(B, h_q, h_k, h_v, d, 2 * N, S, dt) - 256
     assert aw(1, 4, 1, 2, 72, 10, 100, 1) == 0 and aw(1, 4, 1, 2, 64, 0, 100, 1) == 0
+
+
+def _sparq(**kw):
+    a = dict(q=FAKE, k=FAKE, kt=FAKE, v=FAKE, lens=FAKE, out=FAKE, B=2, h_q=8, h_k=2, h_v=4, d=64,
+             N=16, r=8, local=4, vm=None, stream=None, S=104, dt=saga.SAGA_BF16, ws=FAKE * 16,
+             wsb=1 << 40)
+    a.update(kw)
+    return saga.saga_sparq_attn(a["q"], a["k"], a["kt"], a["v"], a["lens"], a["out"], a["B"],
+                                a["h_q"], a["h_k"], a["h_v"], a["d"], a["N"], a["r"], a["local"],
+                                a["vm"], a["stream"], a["S"], a["dt"], a["ws"], a["wsb"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(kt=None), saga.SAGA_ERR_INVALID_ARG),
+    (dict(q=None), saga.SAGA_ERR_INVALID_ARG),
+    (dict(v=None), saga.SAGA_ERR_INVALID_ARG),
+    (dict(out=None), saga.SAGA_ERR_INVALID_ARG),
+    (dict(r=0), saga.SAGA_ERR_INVALID_ARG),
+    (dict(r=65), saga.SAGA_ERR_INVALID_ARG),           # r > d
+    (dict(local=-1), saga.SAGA_ERR_INVALID_ARG),
+    (dict(local=17), saga.SAGA_ERR_INVALID_ARG),       # local > N
+    (dict(N=0, local=0), saga.SAGA_ERR_INVALID_ARG),
+    (dict(kt=FAKE + 8), saga.SAGA_ERR_INVALID_ARG),    # misaligned
+    (dict(vm=FAKE + 2), saga.SAGA_ERR_INVALID_ARG),    # v_mean not 4-byte aligned
+    (dict(h_k=8, h_v=4), saga.SAGA_ERR_INVALID_ARG),
+    (dict(d=96, r=8), saga.SAGA_ERR_UNSUPPORTED),
+    (dict(h_q=64, h_k=2, h_v=4), saga.SAGA_ERR_UNSUPPORTED),     # key group of 32
+    (dict(S=600000), saga.SAGA_ERR_UNSUPPORTED),                  # > 512 chunks
+    (dict(N=5000, local=0), saga.SAGA_ERR_UNSUPPORTED),           # kept list beyond LDS staging
+    (dict(S=100), saga.SAGA_ERR_UNSUPPORTED),                     # bf16 rows not 16-byte pieces
+    (dict(S=102, dt=saga.SAGA_F32), saga.SAGA_ERR_UNSUPPORTED),
+    (dict(ws=None), saga.SAGA_ERR_WORKSPACE),
+    (dict(wsb=1024), saga.SAGA_ERR_WORKSPACE),
+    (dict(ws=FAKE * 16 + 16), saga.SAGA_ERR_WORKSPACE),
+])
+def test_sparq_rejects_bad_arguments_on_host(kw, code):
+    assert _sparq(**kw) == code
+
+
+def test_sparq_workspace_extends_the_decode_workspace():
+    sw, ws = saga.saga_sparq_workspace_size, saga.saga_workspace_size
+    for B, h_q, h_k, h_v, d, N, S, dt in [(64, 12, 1, 2, 128, 1024, 32768, 1),
+                                          (3, 6, 2, 2, 64, 7, 40, 0)]:
+        n = sw(B, h_q, h_k, h_v, d, N, 16, S, dt)
+        base = ws(B, h_q, h_k, h_v, d, N, S, dt)
+        assert n % 256 == 0 and n > base
+        # dims, the scan operand, 1/tau and q/tau: bounded by their largest sizes
+        e = 2 if dt == 1 else 4
+        extra = B * h_k * d * 4 + B * h_k * (d // 16) * 64 * 4 * e + B * h_q * 4 + B * h_q * d * 4
+        assert n <= base + extra + 4 * 256
+    assert sw(1, 4, 1, 2, 64, 10, 0, 100, 1) == 0 and sw(1, 4, 1, 2, 64, 10, 65, 100, 1) == 0
