@@ -123,7 +123,7 @@ __global__ __launch_bounds__(256) void kscan(const T* __restrict__ q, const T* _
 // ---- top-M mode: producer / consumer workgroup --------------------------------------
 
 // LDS layout of kscan_topm (32-bit words):
-//   keys [2][g][kScanChunk]   double-buffered key rows of the current items
+//   keys [2][g][kKeyRow]     double-buffered key rows of the current items
 //   warm [g]                  previous cutoff per head
 //   cursor, used, pad [4]     list cursor and end of the staged lists
 //   meta_stg [kMetaStage] uint4, meta_slot [kMetaStage]   staged metadata
@@ -134,7 +134,7 @@ constexpr bool topm_xp() { return sizeof(T) == 2; }
 template <typename T, int DH>
 __host__ __device__ constexpr size_t topm_lds_words(int g) {
     // every area starts 16-byte aligned
-    return (size_t)2 * g * kScanChunk + ((g + 4 + 3) & ~3) + 5 * kMetaStage +
+    return (size_t)2 * g * kKeyRow + ((g + 4 + 3) & ~3) + 5 * kMetaStage +
            (topm_xp<T>() ? (size_t)kWaves * 16 * DH * sizeof(T) / 4 : 0);
 }
 
@@ -151,9 +151,9 @@ __global__ __launch_bounds__(kTopmThreads, 1) void kscan_topm(
     const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));   // wave-uniform
     const bool producer = wave < kWaves;
     uint32_t* keys = lds;
-    uint32_t* warm = lds + 2 * g * kScanChunk;
+    uint32_t* warm = lds + 2 * g * kKeyRow;
     uint32_t* cursor = warm + g;   // cursor[0]: next free entry, cursor[1]: end of staged lists
-    uint32_t* meta_words = lds + 2 * g * kScanChunk + ((g + 4 + 3) & ~3);
+    uint32_t* meta_words = lds + 2 * g * kKeyRow + ((g + 4 + 3) & ~3);
     uint32_t* xtile_words = meta_words + 5 * kMetaStage;
     const uint32_t fixed_words = (uint32_t)topm_lds_words<T, DH>(g);
 
@@ -209,7 +209,7 @@ __global__ __launch_bounds__(kTopmThreads, 1) void kscan_topm(
                                 : wend;
         if (producer && have_cur) {
             {
-                uint32_t* kbuf = keys + (t & 1) * g * kScanChunk;
+                uint32_t* kbuf = keys + (t & 1) * g * kKeyRow;
                 {
                     const int n = sm.r16;   // next item's query operand (nx == cur after the last)
 #pragma unroll
@@ -229,7 +229,7 @@ __global__ __launch_bounds__(kTopmThreads, 1) void kscan_topm(
                         u32x4 kv;
 #pragma unroll
                         for (int e = 0; e < 4; ++e) kv[e] = (e < rem) ? float_key(acc[e]) : 0u;
-                        *reinterpret_cast<u32x4*>(&kbuf[sm.r16 * kScanChunk + off]) = kv;
+                        *reinterpret_cast<u32x4*>(&kbuf[sm.r16 * kKeyRow + off]) = kv;
                     }
                 };
                 // Every stage of the chunk runs, so each key row is fully
@@ -267,12 +267,12 @@ __global__ __launch_bounds__(kTopmThreads, 1) void kscan_topm(
             const uint32_t M = share >= (float)(kScanChunk / 2)
                                    ? (uint32_t)kScanChunk
                                    : (uint32_t)__builtin_ceilf(1.5f * share) + 16u;
-            uint32_t* kbuf = keys + ((t + 1) & 1) * g * kScanChunk;
+            uint32_t* kbuf = keys + ((t + 1) & 1) * g * kKeyRow;
             const int first = have_cur ? wave - kWaves : wave;
             const int step = have_cur ? kConsumers : kWaves + kConsumers;
 #pragma unroll 1
             for (int n = first; n < g; n += step)
-                extract(prev, n, M, kbuf + n * kScanChunk, warm, sink, t - 1, lane, g, h_q,
+                extract(prev, n, M, kbuf + n * kKeyRow, warm, sink, t - 1, lane, g, h_q,
                         nchunk, tm, prev.L);
         }
         lds_barrier();   // keys of item t are complete; buffer (t - 1) & 1 is free again

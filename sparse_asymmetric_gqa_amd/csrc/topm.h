@@ -16,6 +16,10 @@ constexpr int kTopmThreads = 64 * (kWaves + kConsumers);
 // entries [0, kStageMax) hold data, [kStageMax, kStageMax + 64) are per-lane
 // sinks for the branch-free writes of entries that are not kept.
 constexpr uint32_t kStageMax = kScanChunk / 2 - 64;
+// Words per head key row in LDS: one 16-byte slot beyond the chunk, so that
+// the 16 heads written by one 16-lane store start in distinct bank groups
+// (rows exactly 4 KiB apart would put all 16 lanes on one bank).
+constexpr int kKeyRow = kScanChunk + 4;
 constexpr size_t kTopmLdsBytes = 160 * 1024;   // LDS of a gfx950 CU: one workgroup per CU
 
 // Candidate extraction of head n of item `it` by one consumer wave, from the
@@ -165,7 +169,16 @@ __device__ inline void extract(const Item<T>& it, int n, uint32_t M, uint32_t* r
     off = __builtin_amdgcn_readfirstlane(off);
     const bool staged_lds = off + total <= sink.cap;
     if (staged_lds && lane == 0) atomicMax(sink.used, off + total);
-    uint2* dst = staged_lds ? sink.stg + off : sink.pool + off;
+    // The destination is LDS or global memory (uniformly): typed pointers
+    // for each, so that no store becomes a flat store (whose completion the
+    // waits below would otherwise have to cover).
+    typedef uint32_t v2u __attribute__((ext_vector_type(2)));
+    typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+    typedef __attribute__((address_space(3))) v2u lds_v2u;
+    typedef __attribute__((address_space(1))) u32x4 glb_u32x4;
+    typedef __attribute__((address_space(1))) v2u glb_v2u;
+    lds_v2u* dst_l = (lds_v2u*)(sink.stg + off);
+    glb_v2u* dst_g = (glb_v2u*)(sink.pool + off);
     uint32_t pos0 = (uint32_t)(it.c0 + 16 * lane);
     asm volatile("" : "+v"(pos0));   // positions are formed at each store, not held in registers
     if (total <= kStageMax) {
@@ -183,14 +196,22 @@ __device__ inline void extract(const Item<T>& it, int n, uint32_t M, uint32_t* r
             const uint2 a0 = stage[j];
             const uint2 a1 = j + 1 < total ? stage[j + 1] : make_uint2(0u, 0u);
             v2[0] = a0.x; v2[1] = a0.y; v2[2] = a1.x; v2[3] = a1.y;
-            *reinterpret_cast<u32x4*>(dst + j) = v2;   // dst + j is 16-byte aligned (j even)
+            // dst + j is 16-byte aligned (j even)
+            if (staged_lds) *(lds_u32x4*)(dst_l + j) = v2;
+            else *(glb_u32x4*)(dst_g + j) = v2;
         }
         __builtin_amdgcn_s_waitcnt(0xc07f);   // the head's row is reused as soon as this returns
     } else {
         uint32_t at = first;
+        if (staged_lds) {
 #pragma unroll
-        for (int e = 0; e < 16; ++e)
-            if (kk[e] >= lo) dst[at++] = make_uint2(pos0 + e, kk[e]);
+            for (int e = 0; e < 16; ++e)
+                if (kk[e] >= lo) dst_l[at++] = v2u{pos0 + e, kk[e]};
+        } else {
+#pragma unroll
+            for (int e = 0; e < 16; ++e)
+                if (kk[e] >= lo) dst_g[at++] = v2u{pos0 + e, kk[e]};
+        }
     }
     if (lane == 0) {
         const uint64_t abs_off = sink.base + off;
