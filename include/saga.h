@@ -224,6 +224,95 @@ saga_status saga_sparq_attn(const void* q, const void* k_cache, const void* kt_c
                             int32_t* idx_out, float* alpha_out, int32_t* dims_out);
 
 /*
+ * GQA -> SAGA key-head merge ("More Value per Key", §4: Eqs. 13-17, Lemma 4.1,
+ * Theorem 4.2; proof in App. A; strategies of App. B.1, Eq. 35). An offline
+ * tool, not a decode call: it turns one attention module of a GQA teacher
+ * with h_kt = 2 h_k^S key heads into h_k^S merged key heads.
+ *
+ * Inputs (device, bf16 only, 16-byte aligned, linear-layer storage
+ * [out features][in features]):
+ *   x   [L][D]         hidden states of L calibration tokens
+ *   wq  [h_q * d][D]   query projection; query head j uses teacher key head
+ *                      j / (h_q / h_kt) (contiguous blocks, App. B Eq. 29)
+ *   wk  [h_kt * d][D]  teacher key projection
+ * Outputs (device, caller-owned):
+ *   merged_k  float32 [h_kt / 2][d][D]  merged key head i (storage layout)
+ *             for matched pair i: M(a, b) = (W_a S_a + W_b S_b)(S_a + S_b)^+
+ *             (Eq. 15) for SAGA_MERGE_LOGIT, the average (W_a + W_b) / 2 for
+ *             the other two strategies
+ *   sigma     int32 [h_kt]  the pairing: merged head i = teacher heads
+ *             (sigma[2i], sigma[2i+1]), sigma[2i] < sigma[2i+1], pairs by
+ *             increasing first head (App. B's sigma; feed it to
+ *             saga_merge_permute)
+ *   pair_w    nullable float64 [h_kt][h_kt]  weights the matching ran on:
+ *             w(a, b) of Eq. 16 (LOGIT), ||X W_a - X W_b||_F^2 of Eq. 35
+ *             (KEY), zeros (SEQUENTIAL); diagonal 0
+ *   objective nullable float64 [1]  Eq. 14's objective for the returned
+ *             pairing and merges (for LOGIT its minimum, Theorem 4.2)
+ *   stats     nullable float32 [h_kt*d*d + (h_kt*d)^2]  S_r = sum over the
+ *             query heads j of key head r of (X W_Q^j)^T (X W_Q^j) (Eq. 21),
+ *             then H = (X W_K)^T (X W_K)
+ * strategy: SAGA_MERGE_LOGIT = the §4 method (minimum-weight perfect matching
+ * on Eq. 16, merges by Eq. 15); SAGA_MERGE_KEY = matching on Eq. 35 and
+ * averaged pairs; SAGA_MERGE_SEQUENTIAL = pairs (0,1), (2,3), ... averaged.
+ * The pseudo-inverse treats eigenvalues of S_a + S_b at or below
+ * 2^-23 d lambda_max as zero (the resolution of fp32-accumulated statistics);
+ * equal-weight matchings resolve to the lowest partner of the lowest head.
+ * Arithmetic: X^T X on bf16 MFMA with fp32 accumulation, the statistics in
+ * fp32, the per-pair algebra and the matching in fp64.
+ * Limits: D and d multiples of 16, 16 <= d <= 128, h_kt even with
+ * 2 <= h_kt <= 24, h_q a multiple of h_kt, L >= 1, D <= 46340; otherwise
+ * SAGA_ERR_UNSUPPORTED (dtype other than SAGA_BF16 too). Null required
+ * pointers, bad strategy or misaligned inputs: SAGA_ERR_INVALID_ARG; a
+ * workspace below saga_key_merge_workspace_size: SAGA_ERR_WORKSPACE.
+ * saga_key_merge_workspace_size returns 0 for unsupported shapes.
+ */
+typedef enum {
+    SAGA_MERGE_LOGIT = 0,
+    SAGA_MERGE_KEY = 1,
+    SAGA_MERGE_SEQUENTIAL = 2
+} saga_merge_strategy;
+
+size_t saga_key_merge_workspace_size(int64_t L, int D, int h_q, int h_kt, int d);
+
+saga_status saga_key_merge(const void* x, const void* wq, const void* wk, int64_t L, int D,
+                           int h_q, int h_kt, int d, saga_merge_strategy strategy,
+                           saga_dtype dtype, float* merged_k, int32_t* sigma, double* pair_w,
+                           double* objective, float* stats, void* workspace,
+                           size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * saga_key_merge with up to 4 events recorded on `stream` after the phases:
+ * [0] X^T X, [1] statistics S and H, [2] per-pair closed forms and weights,
+ * [3] matching and merged projections. n_events outside 0..4 (or events null
+ * with n_events > 0): SAGA_ERR_INVALID_ARG.
+ */
+saga_status saga_key_merge_timed(const void* x, const void* wq, const void* wk, int64_t L,
+                                 int D, int h_q, int h_kt, int d,
+                                 saga_merge_strategy strategy, saga_dtype dtype,
+                                 float* merged_k, int32_t* sigma, double* pair_w,
+                                 double* objective, float* stats, void* workspace,
+                                 size_t workspace_bytes, hipStream_t stream,
+                                 hipEvent_t* events, int n_events);
+
+/*
+ * App. B's induced permutations (Eqs. 28-34) for a pairing sigma (device
+ * int32 [h_kt], a permutation of 0 .. h_kt - 1, e.g. from saga_key_merge):
+ *   wv_out head block i  = wv head block sigma[i]          ([h_kt*d][D])
+ *   wq_out head block k  = wq head block pi_Q(k)           ([h_q*d][D])
+ *   wo_out column block k = wo column block pi_Q(k)        ([D][h_q*d])
+ * with pi_Q(k) = sigma[k / g] g + k % g, g = h_q / h_kt. A copy in `dtype`
+ * (bf16 or float32); outputs must not overlap the inputs. D * esize and
+ * d * esize must be multiples of 16 bytes (else SAGA_ERR_UNSUPPORTED);
+ * pointers 16-byte aligned (else SAGA_ERR_INVALID_ARG). sigma is read on the
+ * device and must hold a permutation (not checked).
+ */
+saga_status saga_merge_permute(const int32_t* sigma, const void* wq, const void* wv,
+                               const void* wo, int D, int h_q, int h_kt, int d,
+                               saga_dtype dtype, void* wq_out, void* wv_out, void* wo_out,
+                               hipStream_t stream);
+
+/*
  * The K-scan step alone (§2.1 Eq. 2 with the App. B key-head map): writes the
  * fp32 logits scores[B][h_q][S_max] for t < L_b; entries t >= L_b are left
  * untouched. Same argument rules as saga_decode_attn (h_v is not involved).

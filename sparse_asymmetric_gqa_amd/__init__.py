@@ -10,7 +10,10 @@ from ._binding import (  # noqa: F401
     saga_atopn_workspace_size, saga_debug_fallback_rows,
     saga_debug_scores, saga_decode_attn, saga_decode_attn_timed,
     saga_dense_attn, saga_dense_workspace_size, saga_sparq_attn, saga_sparq_workspace_size,
-    saga_status_string, saga_workspace_size, status_string)
+    saga_status_string, saga_workspace_size, status_string, SAGA_MERGE_KEY, SAGA_MERGE_LOGIT,
+    SAGA_MERGE_SEQUENTIAL, saga_key_merge, saga_key_merge_timed, saga_key_merge_workspace_size,
+    saga_merge_permute)
 from .tensors import (  # noqa: F401
     atopn_attn, atopn_calibrate, atopn_workspace_size, debug_scores, decode_attn, dense_attn,
-    dense_workspace_size, new_workspace, sparq_attn, sparq_workspace_size, workspace_size)
+    dense_workspace_size, key_merge, key_merge_workspace_size, merge_permute, new_workspace,
+    sparq_attn, sparq_workspace_size, workspace_size)

@@ -26,7 +26,8 @@ EXPORTS = ("saga_workspace_size", "saga_decode_attn", "saga_decode_attn_timed",
            "saga_dense_workspace_size", "saga_atopn_workspace_size", "saga_atopn_calibrate",
            "saga_atopn_attn", "saga_sparq_workspace_size", "saga_sparq_attn",
            "saga_dense_attn", "saga_debug_scores", "saga_debug_fallback_rows",
-           "saga_status_string")
+           "saga_key_merge_workspace_size", "saga_key_merge", "saga_key_merge_timed",
+           "saga_merge_permute", "saga_status_string")
 
 
 class SagaError(RuntimeError):
@@ -74,6 +75,16 @@ def _load() -> ctypes.CDLL:
     lib.saga_sparq_attn.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, vp, vp, i64,
                                     i, vp, sz, vp, vp, vp]
     lib.saga_sparq_attn.restype = i
+    lib.saga_key_merge_workspace_size.argtypes = [i64, i, i, i, i]
+    lib.saga_key_merge_workspace_size.restype = sz
+    lib.saga_key_merge.argtypes = [vp, vp, vp, i64, i, i, i, i, i, i, vp, vp, vp, vp, vp, vp, sz,
+                                   vp]
+    lib.saga_key_merge.restype = i
+    lib.saga_key_merge_timed.argtypes = [vp, vp, vp, i64, i, i, i, i, i, i, vp, vp, vp, vp, vp,
+                                         vp, sz, vp, vp, i]
+    lib.saga_key_merge_timed.restype = i
+    lib.saga_merge_permute.argtypes = [vp, vp, vp, vp, i, i, i, i, i, vp, vp, vp, vp]
+    lib.saga_merge_permute.restype = i
     lib.saga_status_string.argtypes = [i]
     lib.saga_status_string.restype = ctypes.c_char_p
     return lib
@@ -177,3 +188,35 @@ def saga_sparq_attn(q, k_cache, kt_cache, v_cache, seq_lens, out, B, h_q, h_k, h
                                    _ptr(v_mean), _ptr(stream), S_max, dtype, _ptr(workspace),
                                    workspace_bytes, _ptr(idx_out), _ptr(alpha_out),
                                    _ptr(dims_out)))
+
+
+SAGA_MERGE_LOGIT, SAGA_MERGE_KEY, SAGA_MERGE_SEQUENTIAL = 0, 1, 2
+
+
+def saga_key_merge_workspace_size(L, D, h_q, h_kt, d) -> int:
+    return int(lib.saga_key_merge_workspace_size(L, D, h_q, h_kt, d))
+
+
+def saga_key_merge(x, wq, wk, L, D, h_q, h_kt, d, strategy, dtype, merged_k, sigma, pair_w,
+                   objective, stats, workspace, workspace_bytes, stream) -> int:
+    return int(lib.saga_key_merge(_ptr(x), _ptr(wq), _ptr(wk), L, D, h_q, h_kt, d, strategy,
+                                  dtype, _ptr(merged_k), _ptr(sigma), _ptr(pair_w),
+                                  _ptr(objective), _ptr(stats), _ptr(workspace),
+                                  workspace_bytes, _ptr(stream)))
+
+
+def saga_key_merge_timed(x, wq, wk, L, D, h_q, h_kt, d, strategy, dtype, merged_k, sigma,
+                         pair_w, objective, stats, workspace, workspace_bytes, stream, events,
+                         n_events) -> int:
+    return int(lib.saga_key_merge_timed(_ptr(x), _ptr(wq), _ptr(wk), L, D, h_q, h_kt, d,
+                                        strategy, dtype, _ptr(merged_k), _ptr(sigma),
+                                        _ptr(pair_w), _ptr(objective), _ptr(stats),
+                                        _ptr(workspace), workspace_bytes, _ptr(stream),
+                                        events, n_events))
+
+
+def saga_merge_permute(sigma, wq, wv, wo, D, h_q, h_kt, d, dtype, wq_out, wv_out, wo_out,
+                       stream) -> int:
+    return int(lib.saga_merge_permute(_ptr(sigma), _ptr(wq), _ptr(wv), _ptr(wo), D, h_q, h_kt,
+                                      d, dtype, _ptr(wq_out), _ptr(wv_out), _ptr(wo_out),
+                                      _ptr(stream)))

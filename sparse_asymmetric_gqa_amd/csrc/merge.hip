@@ -1,0 +1,1003 @@
+// GQA -> SAGA key-head merge on MI355X (gfx950).
+//
+// "More Value per Key: Asymmetric Sparse Attention for Faster LLM Decoding",
+// §4 (Eqs. 13-18, Lemma 4.1, Theorem 4.2), App. A (Eqs. 19-27), App. B
+// (induced permutations, Eqs. 28-34; B.1 merge strategies, Eq. 35).
+//
+// The merge needs, per teacher key head r, S_r = sum_{j in Q_r} (X W_Q^j)^T
+// (X W_Q^j) and the realized-key Gram H = (X W_K)^T (X W_K). Both are
+// contractions of C = X^T X with the projections, so the path is
+//   1. syrk_partial / syrk_reduce: C = X^T X (bf16 MFMA, fp32 accumulation;
+//      upper-triangle 256 x 256 tiles, token range split over workgroups,
+//      partials summed in a fixed order);
+//   2. nt_gemm: F = W C for all query and key heads, then S and H from F
+//      (fp32 MFMA);
+//   3. merge_pairs: per pair (a, b), in fp64, P = S_a + S_b is diagonalised by
+//      cyclic Jacobi rotations held in LDS; replaying the recorded rotations
+//      gives Y = P^+ S_a and Z = P^+ S_b (the transposes of the coefficients
+//      of Eq. 15: M(a, b) = W_a Y^T + W_b Z^T), and the pair weight of Eq. 16
+//      follows from the identity
+//        L_{a,b}(M(a, b)) = <Z Delta, S_a Z> + <Y Delta, S_b Y>,
+//      Delta = (X W_a - X W_b)^T (X W_a - X W_b) (App. A's trace form with
+//      Y^T + Z^T = P P^+ substituted);
+//   4. matching: minimum-weight perfect matching (Theorem 4.2) by dynamic
+//      programming over head subsets, one launch per subset size;
+//   5. merge_apply: the merged projections of the matched pairs.
+// saga_merge_permute applies App. B's head permutations to W_Q, W_V, W_O.
+#include "saga.h"
+#include "saga_internal.h"
+
+#include <stdint.h>
+
+namespace saga {
+namespace {
+using namespace dev;
+
+typedef short v4s __attribute__((ext_vector_type(4)));
+typedef short v8s __attribute__((ext_vector_type(8)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) v4s lds_v4s;
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// ---- sizes -----------------------------------------------------------------
+constexpr int kSyrkThreads = 512;    // 8 waves: 2 (rows) x 4 (columns) of 128 x 64
+constexpr int kBlk = 256;            // C tile edge (features)
+constexpr int kStageTok = 64;        // tokens per LDS stage
+constexpr int kRowBytes = kBlk * 2;  // one token's 256 features in bf16
+constexpr int kSyrkLds = 2 * 2 * kStageTok * kRowBytes;   // 2 stages x 2 operands
+constexpr int kTargetCus = 256;      // MI355X compute units: splits fill one wave of them
+constexpr int kNtThreads = 256;
+constexpr int kPairThreads = 512;
+constexpr int kMaxSweeps = 24;       // Jacobi sweeps recorded per pair
+constexpr int kMaxHeads = 24;        // teacher key heads the subset DP takes (2^24 states)
+
+__host__ __device__ inline int n_blocks(int D) { return (D + kBlk - 1) / kBlk; }
+__host__ __device__ inline int n_tiles(int D) { return n_blocks(D) * (n_blocks(D) + 1) / 2; }
+inline int n_splits(int64_t L, int D) {
+    const int nt = n_tiles(D);
+    int64_t s = kTargetCus / nt;
+    if (s < 1) s = 1;
+    const int64_t stages = (L + kStageTok - 1) / kStageTok;
+    if (s > stages) s = stages > 0 ? stages : 1;
+    return (int)s;
+}
+inline int64_t split_len(int64_t L, int ns) {
+    return round_up((L + ns - 1) / ns, kStageTok);
+}
+
+// logical workgroup id from the hardware one (total a multiple of 8): the
+// hardware deals ids to the 8 XCDs round-robin, so XCD x gets the contiguous
+// logical range [x total / 8, (x + 1) total / 8) and the workgroups that share
+// a token range share that XCD's L2.
+__device__ inline int xcd_logical(int hw, int total) {
+    return (hw & 7) * (total >> 3) + (hw >> 3);
+}
+
+// ---- 1. C = X^T X ------------------------------------------------------------
+// XOR swizzle of the 16-byte units of a staged token row: the transposing
+// reads of a 16-lane group cover 4 consecutive rows x 32 bytes, and the two
+// groups served together differ in row bit 3; both land on distinct banks.
+__device__ inline int unit_swz(int row) { return 2 * (row & 3) + 8 * ((row >> 3) & 1); }
+
+// 8 consecutive tokens (rows kbase .. kbase + 7) of features 16 nb + (lane % 16):
+// the operand of one 16x16x32 MFMA (A and B use the same token order).
+__device__ inline v8bf syrk_frag(const char* buf, int kbase, int nb, int lane) {
+    const int G = lane >> 4, i = lane & 15, a = i & 3, j = i >> 2;
+    const int unit = 2 * nb + (a >> 1);
+    const int r0 = kbase + 8 * G + j, r1 = r0 + 4;
+    const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_v4s*)(buf + r0 * kRowBytes + ((unit ^ unit_swz(r0)) << 4) + 8 * (a & 1)));
+    const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_v4s*)(buf + r1 * kRowBytes + ((unit ^ unit_swz(r1)) << 4) + 8 * (a & 1)));
+    const v8s t = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    return __builtin_bit_cast(v8bf, t);
+}
+
+__device__ inline void tile_of(int t, int nb, int& bi, int& bj) {
+    bi = 0;
+    while (t >= nb - bi) {
+        t -= nb - bi;
+        ++bi;
+    }
+    bj = bi + t;
+}
+
+// One workgroup: tile (bi <= bj) of C over the tokens of one split. The 8
+// waves hold 128 x 64 of the 256 x 256 tile each. Partials are written in
+// MFMA fragment order: [split][tile][wave][8 x 4 blocks][64 lanes] x f32x4.
+__global__ __launch_bounds__(kSyrkThreads, 1) void syrk_partial(
+        const uint16_t* __restrict__ x, int64_t L, int D, int ntile, int nsplit,
+        int64_t slen, int grid_total, f32x4* __restrict__ part) {
+    extern __shared__ __attribute__((aligned(16))) char smem[];
+    const int total = ntile * nsplit;
+    const int logical = xcd_logical(blockIdx.x, grid_total);
+    if (logical >= total) return;
+    const int split = logical / ntile, tile = logical - split * ntile;
+    const int nb = n_blocks(D);
+    int bi, bj;
+    tile_of(tile, nb, bi, bj);
+    const bool diag = bi == bj;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave & 1, wn = wave >> 1;
+    const int64_t t_beg = (int64_t)split * slen;
+    int64_t t_end = t_beg + slen;
+    if (t_end > L) t_end = L;
+    const int nstage = t_end > t_beg ? (int)((t_end - t_beg + kStageTok - 1) / kStageTok) : 0;
+
+    // loader: unit u = tid + 512 h of a stage, row u / 32, 16-byte unit u % 32
+    constexpr int kUnits = kStageTok * 32 / kSyrkThreads;   // per operand per thread
+    const uint16_t* src[2] = {x + (int64_t)bi * kBlk, x + (int64_t)bj * kBlk};
+    u32x4 reg[2][kUnits];
+    auto load_stage = [&](int s) {
+#pragma unroll
+        for (int op = 0; op < 2; ++op) {
+            if (op == 1 && diag) break;
+#pragma unroll
+            for (int h = 0; h < kUnits; ++h) {
+                const int u = tid + kSyrkThreads * h, row = u >> 5, un = u & 31;
+                const int64_t tok = t_beg + (int64_t)s * kStageTok + row;
+                const int col = (op ? bj : bi) * kBlk + un * 8;
+                const bool ok = tok < t_end && col < D;
+                const uint16_t* p = ok ? src[op] + tok * D + un * 8 : x;
+                reg[op][h] = *reinterpret_cast<const u32x4*>(p);
+                if (!ok) reg[op][h] = u32x4{0u, 0u, 0u, 0u};
+            }
+        }
+    };
+    auto store_stage = [&](int buf) {
+#pragma unroll
+        for (int op = 0; op < 2; ++op) {
+            if (op == 1 && diag) break;
+            char* base = smem + (buf * 2 + op) * (kStageTok * kRowBytes);
+#pragma unroll
+            for (int h = 0; h < kUnits; ++h) {
+                const int u = tid + kSyrkThreads * h, row = u >> 5, un = u & 31;
+                *reinterpret_cast<u32x4*>(base + row * kRowBytes + ((un ^ unit_swz(row)) << 4)) =
+                    reg[op][h];
+            }
+        }
+    };
+
+    f32x4 acc[8][4];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    if (nstage > 0) {
+        load_stage(0);
+        store_stage(0);
+    }
+    __syncthreads();
+    for (int s = 0; s < nstage; ++s) {
+        const bool more = s + 1 < nstage;
+        if (more) load_stage(s + 1);
+        const char* abuf = smem + ((s & 1) * 2) * (kStageTok * kRowBytes);
+        const char* bbuf = diag ? abuf : abuf + kStageTok * kRowBytes;
+#pragma unroll
+        for (int kk = 0; kk < kStageTok / 32; ++kk) {
+            v8bf bf[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) bf[j] = syrk_frag(bbuf, 32 * kk, wn * 4 + j, lane);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const v8bf af = syrk_frag(abuf, 32 * kk, wm * 8 + i, lane);
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bf[j], acc[i][j], 0,
+                                                                        0, 0);
+            }
+        }
+        if (more) store_stage((s + 1) & 1);
+        __syncthreads();
+    }
+    f32x4* out = part + (((int64_t)split * ntile + tile) * 8 + wave) * 32 * 64;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) out[(i * 4 + j) * 64 + lane] = acc[i][j];
+}
+
+// C[D][D] (both triangles) = sum over splits of the partials, in split order.
+__global__ __launch_bounds__(256) void syrk_reduce(const f32x4* __restrict__ part, int D,
+                                                   int ntile, int nsplit,
+                                                   float* __restrict__ C) {
+    const int64_t slots = (int64_t)ntile * 8 * 32 * 64;
+    const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (idx >= slots) return;
+    f32x4 s = part[idx];
+    for (int k = 1; k < nsplit; ++k) s += part[idx + k * slots];
+    const int lane = (int)(idx & 63), blk = (int)((idx >> 6) & 31);
+    const int wave = (int)((idx >> 11) & 7), tile = (int)(idx >> 14);
+    int bi, bj;
+    tile_of(tile, n_blocks(D), bi, bj);
+    const int i = blk >> 2, j = blk & 3;
+    const int row0 = bi * kBlk + (wave & 1) * 128 + 16 * i + 4 * (lane >> 4);
+    const int col = bj * kBlk + (wave >> 1) * 64 + 16 * j + (lane & 15);
+    if (col >= D) return;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const int row = row0 + e;
+        if (row >= D) break;
+        C[(int64_t)row * D + col] = s[e];
+        if (bi != bj) C[(int64_t)col * D + row] = s[e];
+    }
+}
+
+// ---- 2. out[z] = sum_p A_p B_p^T (fp32 MFMA) -----------------------------------
+// out[z][i][j] = sum_{p < nsum} sum_k A[a0 + z*azs + p*aps + i][k] * B[b0 + ...][k],
+// A bf16 or f32, B f32, rows of length K (K % 16 == 0, M and N multiples of 16).
+struct NtJob {
+    const void* A;
+    const float* B;
+    float* out;
+    int64_t lda, ldb, ldo;         // row strides (elements)
+    int64_t a_zs, b_zs, o_zs;      // batch strides: rows of A and B, elements of out
+    int64_t a_ps, b_ps;            // rows per sum term
+    int M, N, K, nsum;
+    int kspl;                      // K splits: block z = batch * kspl + split, each
+                                   // split writing its own output (partials)
+};
+
+template <typename TA>
+__device__ inline f32x4 load4(const TA* p);
+template <>
+__device__ inline f32x4 load4<float>(const float* p) {
+    return *reinterpret_cast<const f32x4*>(p);
+}
+template <>
+__device__ inline f32x4 load4<uint16_t>(const uint16_t* p) {
+    const u32x2 v = *reinterpret_cast<const u32x2*>(p);
+    return f32x4{__uint_as_float(v[0] << 16), __uint_as_float(v[0] & 0xffff0000u),
+                 __uint_as_float(v[1] << 16), __uint_as_float(v[1] & 0xffff0000u)};
+}
+
+// 64 x 64 output tile per workgroup, 32 x 32 per wave (2 x 2 blocks of 16).
+template <typename TA>
+__global__ __launch_bounds__(kNtThreads) void nt_gemm(NtJob job) {
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    const int z = blockIdx.z / job.kspl, ks = blockIdx.z - z * job.kspl;
+    const int kper = job.K / job.kspl, kbeg = ks * kper;
+    const int i0 = blockIdx.y * 64 + (wave & 1) * 32, j0 = blockIdx.x * 64 + (wave >> 1) * 32;
+    const TA* A = static_cast<const TA*>(job.A) + z * job.a_zs * job.lda + kbeg;
+    const float* B = job.B + z * job.b_zs * job.ldb + kbeg;
+    const int G = lane >> 4, r = lane & 15;
+    bool rok[2], cok[2];
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+        rok[b] = i0 + 16 * b < job.M;
+        cok[b] = j0 + 16 * b < job.N;
+    }
+    f32x4 acc[2][2];
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int b = 0; b < 2; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int p = 0; p < job.nsum; ++p) {
+        const TA* ap[2];
+        const float* bp[2];
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+            ap[b] = A + (p * job.a_ps + (rok[b] ? i0 + 16 * b + r : 0)) * job.lda + 4 * G;
+            bp[b] = B + (p * job.b_ps + (cok[b] ? j0 + 16 * b + r : 0)) * job.ldb + 4 * G;
+        }
+        f32x4 av[2], bv[2];
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+            av[b] = load4<TA>(ap[b]);
+            bv[b] = load4<float>(bp[b]);
+        }
+        for (int k = 0; k < kper; k += 16) {
+            f32x4 an[2], bn[2];
+            const bool more = k + 16 < kper;
+            if (more) {
+#pragma unroll
+                for (int b = 0; b < 2; ++b) {
+                    an[b] = load4<TA>(ap[b] + k + 16);
+                    bn[b] = load4<float>(bp[b] + k + 16);
+                }
+            }
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+#pragma unroll
+                for (int a = 0; a < 2; ++a)
+#pragma unroll
+                    for (int b = 0; b < 2; ++b)
+                        acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[a][s], bv[b][s],
+                                                                         acc[a][b], 0, 0, 0);
+            if (more) {
+#pragma unroll
+                for (int b = 0; b < 2; ++b) {
+                    av[b] = an[b];
+                    bv[b] = bn[b];
+                }
+            }
+        }
+    }
+    float* o = job.out + (int64_t)blockIdx.z * job.o_zs;
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+            if (!rok[a] || !cok[b]) continue;
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                o[(int64_t)(i0 + 16 * a + 4 * G + e) * job.ldo + j0 + 16 * b + r] = acc[a][b][e];
+        }
+}
+
+// out[r][e] = sum_{t < nt} part[r * nt + t][e], in t order
+__global__ __launch_bounds__(256) void sum_parts(const float* __restrict__ part, int nt,
+                                                 int64_t E, int R, float* __restrict__ out) {
+    const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (idx >= E * R) return;
+    const int64_t r = idx / E, e = idx - r * E;
+    float s = 0.f;
+    for (int t = 0; t < nt; ++t) s += part[(r * nt + t) * E + e];
+    out[idx] = s;
+}
+
+// ---- 3. per-pair algebra (fp64) ------------------------------------------------
+struct PairOut {
+    double w_logit;   // Eq. 16
+    double w_key;     // Eq. 35: tr(Delta)
+    double l_avg;     // Eq. 13 at the average of the two heads: tr(Delta P) / 4
+    double sweeps;    // Jacobi sweeps run
+};
+
+__device__ inline void pair_of_index(int p, int n, int& a, int& b) {
+    a = 0;
+    while (p >= n - 1 - a) {
+        p -= n - 1 - a;
+        ++a;
+    }
+    b = a + 1 + p;
+}
+
+// round r (0 .. d-2) of the cyclic tournament on d players: pair k
+__device__ inline void tourney(int r, int k, int d, int& p, int& q) {
+    const int m = d - 1;
+    int u, v;
+    if (k == 0) {
+        u = r;
+        v = m;
+    } else {
+        u = (r + k) % m;
+        v = (r - k + m) % m;
+    }
+    p = u < v ? u : v;
+    q = u < v ? v : u;
+}
+
+__device__ inline double block_sum(double v, double* red) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+    const int w = threadIdx.x >> 6;
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) red[w] = v;
+    __syncthreads();
+    double s = 0.0;
+    for (int i = 0; i < (int)(blockDim.x >> 6); ++i) s += red[i];
+    return s;
+}
+
+struct PairArgs {
+    const float* S;      // [n][d][d]
+    const float* H;      // [n d][n d]
+    double* Y;           // [npairs][d][d]  P^+ S_a
+    double* Z;           // [npairs][d][d]  P^+ S_b
+    double2* rec;        // [npairs][kMaxSweeps][d - 1][d / 2]  (c, s)
+    PairOut* out;        // [npairs]
+    int n, d, strategy;
+};
+
+// Delta(k, j) of pair (a, b) from the realized-key Gram
+__device__ inline double delta_at(const float* H, int hd, int a, int b, int d, int k, int j) {
+    const int64_t ra = (int64_t)(a * d + k) * hd, rb = (int64_t)(b * d + k) * hd;
+    return ((double)H[ra + a * d + j] - (double)H[ra + b * d + j]) -
+           ((double)H[rb + a * d + j] - (double)H[rb + b * d + j]);
+}
+
+// Replay the recorded rotations on the d x d matrix in LDS (row stride d + 1):
+// forward applies J^T from the left in recording order, backward applies J
+// from the left in reverse order. cs is a double-buffered staging area.
+__device__ void replay(double* Ym, int d, const double2* rec, int nrounds, bool forward,
+                       double2* cs) {
+    const int np = d / 2, tid = threadIdx.x;
+    auto round_at = [&](int i) { return forward ? i : nrounds - 1 - i; };
+    if (nrounds == 0) return;
+    if (tid < np) cs[tid] = rec[(int64_t)round_at(0) * np + tid];
+    __syncthreads();
+    for (int i = 0; i < nrounds; ++i) {
+        double2 nx = double2{1.0, 0.0};
+        if (i + 1 < nrounds && tid < np) nx = rec[(int64_t)round_at(i + 1) * np + tid];
+        const int rr = round_at(i) % (d - 1);
+        const double2* cur = cs + (i & 1) * 64;
+        for (int idx = tid; idx < np * d; idx += kPairThreads) {
+            const int k = idx / d, col = idx - k * d;
+            int p, q;
+            tourney(rr, k, d, p, q);
+            const double c = cur[k].x, s = cur[k].y;
+            const double yp = Ym[p * (d + 1) + col], yq = Ym[q * (d + 1) + col];
+            if (forward) {
+                Ym[p * (d + 1) + col] = c * yp - s * yq;
+                Ym[q * (d + 1) + col] = s * yp + c * yq;
+            } else {
+                Ym[p * (d + 1) + col] = c * yp + s * yq;
+                Ym[q * (d + 1) + col] = -s * yp + c * yq;
+            }
+        }
+        if (i + 1 < nrounds && tid < np) cs[((i + 1) & 1) * 64 + tid] = nx;
+        __syncthreads();
+    }
+}
+
+// doubles of the matrix region: the Jacobi matrix, or the four GEMM panels
+__host__ __device__ inline int pair_matrix_words(int d) {
+    const int jac = d * (d + 1), gem = 2 * (64 * 17 + 16 * 65);
+    return jac > gem ? jac : gem;
+}
+
+// One workgroup per pair (a, b), a < b.
+__global__ __launch_bounds__(kPairThreads) void merge_pairs(PairArgs pa) {
+    extern __shared__ __attribute__((aligned(16))) char smem_raw[];
+    const int d = pa.d, np = d / 2, ld = d + 1, tid = threadIdx.x;
+    const int pidx = blockIdx.x;
+    int a, b;
+    pair_of_index(pidx, pa.n, a, b);
+    double* Am = reinterpret_cast<double*>(smem_raw);   // [d][d + 1], later GEMM panels
+    double2* cs = reinterpret_cast<double2*>(Am + pair_matrix_words(d));   // [2][64]
+    double* lam = reinterpret_cast<double*>(cs + 128);       // [d]
+    double* red = lam + 128;                                  // [16]
+    int* flag = reinterpret_cast<int*>(red + 16);
+    const int hd = pa.n * d;
+    const float* Sa = pa.S + (int64_t)a * d * d;
+    const float* Sb = pa.S + (int64_t)b * d * d;
+    double* Y = pa.Y + (int64_t)pidx * d * d;
+    double* Z = pa.Z + (int64_t)pidx * d * d;
+
+    // tr(Delta), tr(Delta P); P into LDS
+    double t1 = 0.0, t2 = 0.0;
+    for (int idx = tid; idx < d * d; idx += kPairThreads) {
+        const int i = idx / d, j = idx - i * d;
+        const double P = (double)Sa[idx] + (double)Sb[idx];
+        const double dl = delta_at(pa.H, hd, a, b, d, i, j);
+        Am[i * ld + j] = P;
+        t2 += dl * P;
+        if (i == j) t1 += dl;
+    }
+    const double trd = block_sum(t1, red);
+    const double trdp = block_sum(t2, red);
+
+    if (pa.strategy != 0) {
+        for (int idx = tid; idx < d * d; idx += kPairThreads) {
+            const int i = idx / d, j = idx - i * d;
+            Y[idx] = Z[idx] = i == j ? 0.5 : 0.0;
+        }
+        if (tid == 0) pa.out[pidx] = PairOut{0.0, trd, 0.25 * trdp, 0.0};
+        return;
+    }
+
+    // cyclic Jacobi (rotations zero one off-diagonal pair each; a round
+    // rotates d / 2 disjoint pairs at once)
+    double2* rec = pa.rec + (int64_t)pidx * kMaxSweeps * (d - 1) * np;
+    int sweeps = 0;
+    for (; sweeps < kMaxSweeps; ++sweeps) {
+        double off = 0.0, dia = 0.0;
+        for (int idx = tid; idx < d * d; idx += kPairThreads) {
+            const int i = idx / d, j = idx - i * d;
+            const double v = Am[i * ld + j];
+            if (i == j)
+                dia += v * v;
+            else
+                off += v * v;
+        }
+        off = block_sum(off, red);
+        dia = block_sum(dia, red);
+        // off-diagonal norm at the rounding level of a d x d fp64 matrix: done
+        if (!(off > (double)d * d * 0x1p-104 * (off + dia))) break;
+        for (int r = 0; r < d - 1; ++r) {
+            if (tid < np) {
+                int p, q;
+                tourney(r, tid, d, p, q);
+                const double apq = Am[p * ld + q];
+                double c = 1.0, s = 0.0;
+                if (apq != 0.0) {
+                    const double tau = (Am[q * ld + q] - Am[p * ld + p]) / (2.0 * apq);
+                    const double at = fabs(tau);
+                    double t = at > 1e150 ? 0.5 / at : 1.0 / (at + sqrt(1.0 + tau * tau));
+                    if (tau < 0.0) t = -t;
+                    c = 1.0 / sqrt(1.0 + t * t);
+                    s = t * c;
+                }
+                cs[tid] = double2{c, s};
+                rec[((int64_t)sweeps * (d - 1) + r) * np + tid] = double2{c, s};
+            }
+            __syncthreads();
+            for (int blk = tid; blk < np * np; blk += kPairThreads) {
+                const int k = blk / np, l = blk - k * np;
+                int pk, qk, pl, ql;
+                tourney(r, k, d, pk, qk);
+                tourney(r, l, d, pl, ql);
+                const double ck = cs[k].x, sk = cs[k].y, cl = cs[l].x, sl = cs[l].y;
+                const double x00 = Am[pk * ld + pl], x01 = Am[pk * ld + ql];
+                const double x10 = Am[qk * ld + pl], x11 = Am[qk * ld + ql];
+                const double y00 = ck * x00 - sk * x10, y01 = ck * x01 - sk * x11;
+                const double y10 = sk * x00 + ck * x10, y11 = sk * x01 + ck * x11;
+                double z00 = cl * y00 - sl * y01, z01 = sl * y00 + cl * y01;
+                double z10 = cl * y10 - sl * y11, z11 = sl * y10 + cl * y11;
+                if (k == l) z01 = z10 = 0.0;
+                Am[pk * ld + pl] = z00;
+                Am[pk * ld + ql] = z01;
+                Am[qk * ld + pl] = z10;
+                Am[qk * ld + ql] = z11;
+            }
+            __syncthreads();
+        }
+    }
+    // eigenvalues, cutoff (2^-23 d lambda_max), reciprocals
+    double lmax = 0.0;
+    for (int i = 0; i < d; ++i) lmax = fmax(lmax, Am[i * ld + i]);
+    const double cut = 0x1p-23 * d * lmax;
+    __syncthreads();
+    if (tid == 0) *flag = 0;
+    __syncthreads();
+    if (tid < d) {
+        const double l = Am[tid * ld + tid];
+        lam[tid] = l > cut ? 1.0 / l : 0.0;
+        if (!(l > cut)) atomicOr(flag, 1);
+    }
+    __syncthreads();
+    const bool trunc = *flag != 0;
+    const int nrounds = sweeps * (d - 1);
+
+    // Y = P^+ S_a = V Lambda^+ V^T S_a
+    for (int pass = 0; pass < (trunc ? 2 : 1); ++pass) {
+        for (int idx = tid; idx < d * d; idx += kPairThreads) {
+            const int i = idx / d, j = idx - i * d;
+            Am[i * ld + j] = pass == 0 ? (double)Sa[idx] : (i == j ? 1.0 : 0.0);
+        }
+        __syncthreads();
+        replay(Am, d, rec, nrounds, true, cs);
+        for (int idx = tid; idx < d * d; idx += kPairThreads) {
+            const int i = idx / d, j = idx - i * d;
+            // pass 1 forms P P^+ = V diag(lambda > cut) V^T
+            Am[i * ld + j] *= pass == 0 ? lam[i] : (lam[i] != 0.0 ? 1.0 : 0.0);
+        }
+        __syncthreads();
+        replay(Am, d, rec, nrounds, false, cs);
+        for (int idx = tid; idx < d * d; idx += kPairThreads) {
+            const int i = idx / d, j = idx - i * d;
+            if (pass == 0)
+                Y[idx] = Am[i * ld + j];
+            else
+                Z[idx] = Am[i * ld + j];
+        }
+        __syncthreads();
+    }
+    // Z = P^+ S_b = P P^+ - Y  (P P^+ = I without truncation)
+    for (int idx = tid; idx < d * d; idx += kPairThreads) {
+        const int i = idx / d, j = idx - i * d;
+        const double e = trunc ? Z[idx] : (i == j ? 1.0 : 0.0);
+        Z[idx] = e - Y[idx];
+    }
+    __threadfence_block();
+    __syncthreads();
+
+    // w = <Z Delta, S_a Z> + <Y Delta, S_b Y>, 64 x 64 output tiles, k panels of 16
+    double* As1 = Am;                 // [64][17]
+    double* Bs1 = As1 + 64 * 17;      // [16][65]
+    double* As2 = Bs1 + 16 * 65;
+    double* Bs2 = As2 + 64 * 17;
+    const int tr = tid >> 3, tc = (tid & 7) * 8;
+    double dot = 0.0;
+    for (int term = 0; term < 2; ++term) {
+        const double* L1 = term == 0 ? Z : Y;    // left of X1 = L1 Delta, right of X2 = S L1
+        const float* Sm = term == 0 ? Sa : Sb;
+        for (int ti = 0; ti < d; ti += 64)
+            for (int tj = 0; tj < d; tj += 64) {
+                double acc1[8], acc2[8];
+#pragma unroll
+                for (int x = 0; x < 8; ++x) acc1[x] = acc2[x] = 0.0;
+                for (int k0 = 0; k0 < d; k0 += 16) {
+                    for (int e = tid; e < 1024; e += kPairThreads) {
+                        const int ar = e >> 4, ak = e & 15;          // A panels [64][16]
+                        const int i = ti + ar, k = k0 + ak;
+                        As1[ar * 17 + ak] = i < d ? L1[(int64_t)i * d + k] : 0.0;
+                        As2[ar * 17 + ak] = i < d ? (double)Sm[(int64_t)i * d + k] : 0.0;
+                        const int bk = e >> 6, bc = e & 63;          // B panels [16][64]
+                        const int j = tj + bc, kb = k0 + bk;
+                        Bs1[bk * 65 + bc] = j < d ? delta_at(pa.H, hd, a, b, d, kb, j) : 0.0;
+                        Bs2[bk * 65 + bc] = j < d ? L1[(int64_t)kb * d + j] : 0.0;
+                    }
+                    __syncthreads();
+#pragma unroll
+                    for (int kk = 0; kk < 16; ++kk) {
+                        const double a1 = As1[tr * 17 + kk], a2 = As2[tr * 17 + kk];
+#pragma unroll
+                        for (int x = 0; x < 8; ++x) {
+                            acc1[x] += a1 * Bs1[kk * 65 + tc + x];
+                            acc2[x] += a2 * Bs2[kk * 65 + tc + x];
+                        }
+                    }
+                    __syncthreads();
+                }
+#pragma unroll
+                for (int x = 0; x < 8; ++x) dot += acc1[x] * acc2[x];
+            }
+    }
+    dot = block_sum(dot, red + 8);
+    if (tid == 0) pa.out[pidx] = PairOut{dot, trd, 0.25 * trdp, (double)sweeps};
+}
+
+// ---- 4. matching ----------------------------------------------------------------
+struct MatchWs {
+    double* w;        // [n][n] weights the matching runs on
+    double* dp;       // [2^n]
+    int8_t* ch;       // [2^n]  partner of the lowest head of the mask
+    int32_t* pairs;   // [n]    matched pairs (a, b) by increasing a
+};
+
+__global__ __launch_bounds__(256) void match_weights(const PairOut* po, int n, int strategy,
+                                                     MatchWs m) {
+    const int np = n * (n - 1) / 2;
+    for (int p = threadIdx.x; p < np; p += 256) {
+        int a, b;
+        pair_of_index(p, n, a, b);
+        const double v = strategy == 0 ? po[p].w_logit : (strategy == 1 ? po[p].w_key : 0.0);
+        m.w[a * n + b] = v;
+        m.w[b * n + a] = v;
+    }
+    for (int i = threadIdx.x; i < n; i += 256) m.w[i * n + i] = 0.0;
+    if (threadIdx.x == 0) m.dp[0] = 0.0;
+}
+
+__global__ __launch_bounds__(256) void match_layer(int n, int pop, MatchWs m) {
+    const int64_t mask = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (mask >= ((int64_t)1 << n) || __popcll((uint64_t)mask) != pop) return;
+    const int i = __ffsll((unsigned long long)mask) - 1;
+    double best = 0.0;
+    int bj = -1;
+    for (int j = i + 1; j < n; ++j) {
+        if (!((mask >> j) & 1)) continue;
+        const double v = m.w[i * n + j] + m.dp[mask ^ ((int64_t)1 << i) ^ ((int64_t)1 << j)];
+        if (bj < 0 || v < best) {
+            best = v;
+            bj = j;
+        }
+    }
+    m.dp[mask] = best;
+    m.ch[mask] = (int8_t)bj;
+}
+
+__global__ void match_finish(const PairOut* po, int n, int strategy, MatchWs m,
+                             int32_t* __restrict__ sigma, double* __restrict__ pair_w,
+                             double* __restrict__ objective) {
+    if (pair_w)
+        for (int e = threadIdx.x; e < n * n; e += blockDim.x) pair_w[e] = m.w[e];
+    if (threadIdx.x != 0) return;
+    int64_t mask = ((int64_t)1 << n) - 1;
+    double obj = 0.0;
+    for (int i = 0; i < n / 2; ++i) {
+        int a, b;
+        if (strategy == 2) {
+            a = 2 * i;
+            b = 2 * i + 1;
+        } else {
+            a = __ffsll((unsigned long long)mask) - 1;
+            b = m.ch[mask];
+            mask ^= ((int64_t)1 << a) | ((int64_t)1 << b);
+        }
+        m.pairs[2 * i] = a;
+        m.pairs[2 * i + 1] = b;
+        sigma[2 * i] = a;
+        sigma[2 * i + 1] = b;
+        const int p = a * n - a * (a + 1) / 2 + (b - a - 1);
+        obj += strategy == 0 ? po[p].w_logit : po[p].l_avg;
+    }
+    if (objective) *objective = obj;
+}
+
+// ---- 5. merged projections ----------------------------------------------------
+// merged[i][c][k] = sum_e Y[c][e] Wk[a d + e][k] + Z[c][e] Wk[b d + e][k]
+__global__ __launch_bounds__(256) void merge_apply(const uint16_t* __restrict__ wk,
+                                                   const double* __restrict__ Y,
+                                                   const double* __restrict__ Z,
+                                                   const int32_t* __restrict__ pairs, int n,
+                                                   int d, int D, float* __restrict__ merged) {
+    const int k = blockIdx.x * 256 + threadIdx.x;
+    const int c = blockIdx.y, i = blockIdx.z;
+    if (k >= D) return;
+    const int a = pairs[2 * i], b = pairs[2 * i + 1];
+    const int p = a * n - a * (a + 1) / 2 + (b - a - 1);
+    const double* y = Y + ((int64_t)p * d + c) * d;
+    const double* z = Z + ((int64_t)p * d + c) * d;
+    const uint16_t* wa = wk + (int64_t)a * d * D + k;
+    const uint16_t* wb = wk + (int64_t)b * d * D + k;
+    double s = 0.0;
+    for (int e = 0; e < d; ++e) {
+        const double va = (double)__uint_as_float((uint32_t)wa[(int64_t)e * D] << 16);
+        const double vb = (double)__uint_as_float((uint32_t)wb[(int64_t)e * D] << 16);
+        s += y[e] * va + z[e] * vb;
+    }
+    merged[((int64_t)i * d + c) * D + k] = (float)s;
+}
+
+// ---- App. B: induced permutations ------------------------------------------------
+// Copies in 16-byte units: W_Q's head blocks and W_V's head blocks (rows of
+// D elements), W_O's column blocks (d elements inside each of its D rows).
+__global__ __launch_bounds__(256) void merge_permute(const int32_t* __restrict__ sigma,
+                                                     const u32x4* __restrict__ wq,
+                                                     const u32x4* __restrict__ wv,
+                                                     const u32x4* __restrict__ wo,
+                                                     int D, int h_q, int h_kt, int d, int esize,
+                                                     u32x4* __restrict__ wq_o,
+                                                     u32x4* __restrict__ wv_o,
+                                                     u32x4* __restrict__ wo_o) {
+    const int g = h_q / h_kt;
+    const int64_t urow = (int64_t)D * esize / 16;           // units per W_Q / W_V row
+    const int64_t uhead = (int64_t)d * esize / 16;          // units per head block of W_O rows
+    const int64_t nq = (int64_t)h_q * d * urow, nv = (int64_t)h_kt * d * urow;
+    const int64_t no = (int64_t)D * h_q * uhead;
+    const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (idx < nq) {
+        const int64_t row = idx / urow, u = idx - row * urow;
+        const int kq = (int)(row / d), e = (int)(row - (int64_t)kq * d);
+        const int src = sigma[kq / g] * g + kq % g;
+        wq_o[idx] = wq[((int64_t)src * d + e) * urow + u];
+    } else if (idx < nq + nv) {
+        const int64_t t = idx - nq;
+        const int64_t row = t / urow, u = t - row * urow;
+        const int kv = (int)(row / d), e = (int)(row - (int64_t)kv * d);
+        wv_o[t] = wv[((int64_t)sigma[kv] * d + e) * urow + u];
+    } else if (idx < nq + nv + no) {
+        const int64_t t = idx - nq - nv;
+        const int64_t per_row = (int64_t)h_q * uhead;
+        const int64_t row = t / per_row, rem = t - row * per_row;
+        const int kq = (int)(rem / uhead);
+        const int64_t u = rem - (int64_t)kq * uhead;
+        const int src = sigma[kq / g] * g + kq % g;
+        wo_o[t] = wo[row * per_row + (int64_t)src * uhead + u];
+    }
+}
+
+}  // namespace
+
+// ---- host side -------------------------------------------------------------------
+struct MergeWs {
+    f32x4* part;
+    float *C, *F, *S, *H, *part_s, *part_h;
+    double *Y, *Z;
+    double2* rec;
+    PairOut* po;
+    MatchWs m;
+    size_t bytes;
+};
+
+// K splits giving about 256 workgroups for `tiles` output tiles (K / splits a
+// multiple of 16)
+static int k_splits(int K, int tiles) {
+    int s = (256 + tiles - 1) / tiles;
+    while (s > 1 && (K % s || (K / s) % 16 || K / s < 64)) --s;
+    return s;
+}
+
+static size_t al256(size_t x) { return (x + 255) / 256 * 256; }
+
+static MergeWs carve_merge(void* base, int64_t L, int D, int h_q, int h_kt, int d) {
+    MergeWs w{};
+    char* p = static_cast<char*>(base);
+    size_t off = 0;
+    auto take = [&](size_t bytes) -> char* {
+        char* r = p ? p + off : nullptr;
+        off += al256(bytes);
+        return r;
+    };
+    const int nt = n_tiles(D), ns = n_splits(L, D);
+    const size_t np = (size_t)h_kt * (h_kt - 1) / 2;
+    w.part = reinterpret_cast<f32x4*>(take((size_t)ns * nt * 8 * 32 * 64 * sizeof(f32x4)));
+    w.C = reinterpret_cast<float*>(take((size_t)D * D * 4));
+    w.F = reinterpret_cast<float*>(take((size_t)(h_q + h_kt) * d * D * 4));
+    w.S = reinterpret_cast<float*>(take((size_t)h_kt * d * d * 4));
+    w.H = reinterpret_cast<float*>(take((size_t)h_kt * d * h_kt * d * 4));
+    {
+        const int tq = ((d + 63) / 64) * ((d + 63) / 64), hk = h_kt * d;
+        const int th = ((hk + 63) / 64) * ((hk + 63) / 64);
+        w.part_s = reinterpret_cast<float*>(take((size_t)h_q * k_splits(D, h_q * tq) * d * d * 4));
+        w.part_h = reinterpret_cast<float*>(take((size_t)k_splits(D, th) * hk * hk * 4));
+    }
+    w.Y = reinterpret_cast<double*>(take(np * d * d * 8));
+    w.Z = reinterpret_cast<double*>(take(np * d * d * 8));
+    w.rec = reinterpret_cast<double2*>(take(np * kMaxSweeps * (d - 1) * (d / 2) * 16));
+    w.po = reinterpret_cast<PairOut*>(take(np * sizeof(PairOut)));
+    w.m.w = reinterpret_cast<double*>(take((size_t)h_kt * h_kt * 8));
+    w.m.dp = reinterpret_cast<double*>(take(((size_t)1 << h_kt) * 8));
+    w.m.ch = reinterpret_cast<int8_t*>(take((size_t)1 << h_kt));
+    w.m.pairs = reinterpret_cast<int32_t*>(take((size_t)h_kt * 4));
+    w.bytes = off;
+    return w;
+}
+
+static size_t pair_lds(int d) {
+    return (size_t)pair_matrix_words(d) * 8 + 128 * 16 + 128 * 8 + 16 * 8 + 16;
+}
+
+static bool merge_shape_ok(int64_t L, int D, int h_q, int h_kt, int d) {
+    return L >= 1 && D >= 16 && D % 16 == 0 && d >= 16 && d <= 128 && d % 16 == 0 &&
+           h_kt >= 2 && h_kt % 2 == 0 && h_kt <= kMaxHeads && h_q >= h_kt && h_q % h_kt == 0 &&
+           (int64_t)D * D <= ((int64_t)1 << 31);
+}
+
+static hipError_t set_lds(const void* fn, size_t bytes) {
+    return hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+}
+
+static NtJob nt_job(const void* A, const float* B, float* out, int64_t lda, int64_t ldb,
+                    int64_t ldo, int M, int N, int K) {
+    NtJob j{};
+    j.A = A;
+    j.B = B;
+    j.out = out;
+    j.lda = lda;
+    j.ldb = ldb;
+    j.ldo = ldo;
+    j.M = M;
+    j.N = N;
+    j.K = K;
+    j.nsum = 1;
+    j.kspl = 1;
+    return j;
+}
+
+static void launch_nt(const NtJob& j, int nz, hipStream_t st) {
+    dim3 grid((j.N + 63) / 64, (j.M + 63) / 64, nz);
+    hipLaunchKernelGGL(nt_gemm<uint16_t>, grid, dim3(kNtThreads), 0, st, j);
+}
+
+}  // namespace saga
+
+using namespace saga;
+
+extern "C" size_t saga_key_merge_workspace_size(int64_t L, int D, int h_q, int h_kt, int d) {
+    if (!merge_shape_ok(L, D, h_q, h_kt, d)) return 0;
+    return carve_merge(nullptr, L, D, h_q, h_kt, d).bytes;
+}
+
+static saga_status key_merge_impl(const void* x, const void* wq, const void* wk, int64_t L,
+                                  int D, int h_q, int h_kt, int d, int strategy, int dtype,
+                                  float* merged, int32_t* sigma, double* pair_w,
+                                  double* objective, float* stats, void* workspace,
+                                  size_t workspace_bytes, hipStream_t st, hipEvent_t* ev,
+                                  int nev) {
+    if (!x || !wq || !wk || !merged || !sigma) return SAGA_ERR_INVALID_ARG;
+    if (strategy < 0 || strategy > 2 || nev < 0 || nev > 4 || (nev > 0 && !ev))
+        return SAGA_ERR_INVALID_ARG;
+    if (L < 1 || D < 1 || d < 1 || h_q < 1 || h_kt < 2 || h_kt % 2 || h_q % h_kt)
+        return SAGA_ERR_INVALID_ARG;
+    if (dtype != SAGA_BF16 || !merge_shape_ok(L, D, h_q, h_kt, d)) return SAGA_ERR_UNSUPPORTED;
+    if ((reinterpret_cast<uintptr_t>(x) | reinterpret_cast<uintptr_t>(wq) |
+         reinterpret_cast<uintptr_t>(wk)) & 15)
+        return SAGA_ERR_INVALID_ARG;
+    const MergeWs probe = carve_merge(nullptr, L, D, h_q, h_kt, d);
+    if (!workspace || workspace_bytes < probe.bytes) return SAGA_ERR_WORKSPACE;
+    MergeWs w = carve_merge(workspace, L, D, h_q, h_kt, d);
+    static bool lds_set = false;
+    if (!lds_set) {
+        if (set_lds(reinterpret_cast<const void*>(syrk_partial), kSyrkLds) != hipSuccess ||
+            set_lds(reinterpret_cast<const void*>(merge_pairs), pair_lds(128)) != hipSuccess)
+            return SAGA_ERR_HIP;
+        lds_set = true;
+    }
+    bool ok = true;
+    auto mark = [&](int i) {
+        if (i < nev) ok = hipEventRecord(ev[i], st) == hipSuccess && ok;
+    };
+    // 1. C = X^T X
+    const int nt = n_tiles(D), ns = n_splits(L, D);
+    const int total = nt * ns, grid = (int)round_up(total, 8);
+    hipLaunchKernelGGL(syrk_partial, dim3(grid), dim3(kSyrkThreads), kSyrkLds, st,
+                       static_cast<const uint16_t*>(x), L, D, nt, ns, split_len(L, ns), grid,
+                       w.part);
+    const int64_t slots = (int64_t)nt * 8 * 32 * 64;
+    hipLaunchKernelGGL(syrk_reduce, dim3((unsigned)((slots + 255) / 256)), dim3(256), 0, st,
+                       w.part, D, nt, ns, w.C);
+    mark(0);
+    // 2. F = [W_Q; W_K] C, then S and H
+    const int g = h_q / h_kt;
+    float* Fq = w.F;
+    float* Fk = w.F + (int64_t)h_q * d * D;
+    launch_nt(nt_job(wq, w.C, Fq, D, D, D, h_q * d, D, D), 1, st);
+    launch_nt(nt_job(wk, w.C, Fk, D, D, D, h_kt * d, D, D), 1, st);
+    // S: one output per (query head, K split), summed per key head in a fixed order
+    const int tq = ((d + 63) / 64) * ((d + 63) / 64);
+    const int ks_s = k_splits(D, h_q * tq);
+    NtJob js = nt_job(wq, Fq, w.part_s, D, D, d, d, d, D);
+    js.a_zs = js.b_zs = d;
+    js.o_zs = (int64_t)d * d;
+    js.kspl = ks_s;
+    launch_nt(js, h_q * ks_s, st);
+    hipLaunchKernelGGL(sum_parts, dim3((unsigned)(((int64_t)h_kt * d * d + 255) / 256)), dim3(256),
+                       0, st, w.part_s, g * ks_s, (int64_t)d * d, h_kt, w.S);
+    const int hk = h_kt * d, th = ((hk + 63) / 64) * ((hk + 63) / 64);
+    const int ks_h = k_splits(D, th);
+    NtJob jh = nt_job(wk, Fk, w.part_h, D, D, hk, hk, hk, D);
+    jh.o_zs = (int64_t)hk * hk;
+    jh.kspl = ks_h;
+    launch_nt(jh, ks_h, st);
+    hipLaunchKernelGGL(sum_parts, dim3((unsigned)(((int64_t)hk * hk + 255) / 256)), dim3(256), 0,
+                       st, w.part_h, ks_h, (int64_t)hk * hk, 1, w.H);
+    if (stats) {
+        ok = hipMemcpyAsync(stats, w.S, (size_t)h_kt * d * d * 4, hipMemcpyDeviceToDevice,
+                            st) == hipSuccess && ok;
+        ok = hipMemcpyAsync(stats + (size_t)h_kt * d * d, w.H, (size_t)h_kt * d * h_kt * d * 4,
+                            hipMemcpyDeviceToDevice, st) == hipSuccess && ok;
+    }
+    mark(1);
+    // 3. pairs
+    PairArgs pa{w.S, w.H, w.Y, w.Z, w.rec, w.po, h_kt, d, strategy};
+    const int npairs = h_kt * (h_kt - 1) / 2;
+    hipLaunchKernelGGL(merge_pairs, dim3(npairs), dim3(kPairThreads), pair_lds(d), st, pa);
+    mark(2);
+    // 4. matching, 5. merged projections
+    hipLaunchKernelGGL(match_weights, dim3(1), dim3(256), 0, st, w.po, h_kt, strategy, w.m);
+    if (strategy != 2) {
+        const unsigned mb = (unsigned)((((int64_t)1 << h_kt) + 255) / 256);
+        for (int k = 1; k <= h_kt / 2; ++k)
+            hipLaunchKernelGGL(match_layer, dim3(mb), dim3(256), 0, st, h_kt, 2 * k, w.m);
+    }
+    hipLaunchKernelGGL(match_finish, dim3(1), dim3(256), 0, st, w.po, h_kt, strategy, w.m, sigma,
+                       pair_w, objective);
+    hipLaunchKernelGGL(merge_apply, dim3((D + 255) / 256, d, h_kt / 2), dim3(256), 0, st,
+                       static_cast<const uint16_t*>(wk), w.Y, w.Z, w.m.pairs, h_kt, d, D, merged);
+    mark(3);
+    return hipGetLastError() == hipSuccess && ok ? SAGA_OK : SAGA_ERR_HIP;
+}
+
+extern "C" saga_status saga_key_merge(const void* x, const void* wq, const void* wk, int64_t L,
+                                      int D, int h_q, int h_kt, int d,
+                                      saga_merge_strategy strategy, saga_dtype dtype,
+                                      float* merged_k, int32_t* sigma, double* pair_w,
+                                      double* objective, float* stats, void* workspace,
+                                      size_t workspace_bytes, hipStream_t stream) {
+    return key_merge_impl(x, wq, wk, L, D, h_q, h_kt, d, (int)strategy, (int)dtype, merged_k,
+                          sigma, pair_w, objective, stats, workspace, workspace_bytes, stream,
+                          nullptr, 0);
+}
+
+extern "C" saga_status saga_key_merge_timed(const void* x, const void* wq, const void* wk,
+                                            int64_t L, int D, int h_q, int h_kt, int d,
+                                            saga_merge_strategy strategy, saga_dtype dtype,
+                                            float* merged_k,
+                                            int32_t* sigma, double* pair_w, double* objective,
+                                            float* stats, void* workspace,
+                                            size_t workspace_bytes, hipStream_t stream,
+                                            hipEvent_t* events, int n_events) {
+    return key_merge_impl(x, wq, wk, L, D, h_q, h_kt, d, (int)strategy, (int)dtype, merged_k,
+                          sigma, pair_w, objective, stats, workspace, workspace_bytes, stream,
+                          events, n_events);
+}
+
+extern "C" saga_status saga_merge_permute(const int32_t* sigma, const void* wq, const void* wv,
+                                          const void* wo, int D, int h_q, int h_kt, int d,
+                                          saga_dtype dtype, void* wq_out, void* wv_out,
+                                          void* wo_out,
+                                          hipStream_t stream) {
+    if (!sigma || !wq || !wv || !wo || !wq_out || !wv_out || !wo_out) return SAGA_ERR_INVALID_ARG;
+    if (D < 1 || d < 1 || h_q < 1 || h_kt < 1 || h_q % h_kt) return SAGA_ERR_INVALID_ARG;
+    if (dtype != SAGA_BF16 && dtype != SAGA_F32) return SAGA_ERR_INVALID_ARG;
+    const int esize = dtype == SAGA_BF16 ? 2 : 4;
+    if (((int64_t)D * esize) % 16 || ((int64_t)d * esize) % 16) return SAGA_ERR_UNSUPPORTED;
+    const uintptr_t al = reinterpret_cast<uintptr_t>(wq) | reinterpret_cast<uintptr_t>(wv) |
+                         reinterpret_cast<uintptr_t>(wo) | reinterpret_cast<uintptr_t>(wq_out) |
+                         reinterpret_cast<uintptr_t>(wv_out) | reinterpret_cast<uintptr_t>(wo_out);
+    if (al & 15) return SAGA_ERR_INVALID_ARG;
+    const int64_t units = ((int64_t)h_q * d * D * 2 + (int64_t)h_kt * d * D) * esize / 16;
+    hipLaunchKernelGGL(merge_permute, dim3((unsigned)((units + 255) / 256)), dim3(256), 0, stream,
+                       sigma, static_cast<const u32x4*>(wq), static_cast<const u32x4*>(wv),
+                       static_cast<const u32x4*>(wo), D, h_q, h_kt, d, esize,
+                       static_cast<u32x4*>(wq_out), static_cast<u32x4*>(wv_out),
+                       static_cast<u32x4*>(wo_out));
+    return hipGetLastError() == hipSuccess ? SAGA_OK : SAGA_ERR_HIP;
+}

@@ -188,3 +188,58 @@ def sparq_attn(q, k_cache, kt_cache, v_cache, seq_lens, N, r, local=0, *, v_mean
     if st != C.SAGA_OK:
         raise C.SagaError(st, "saga_sparq_attn")
     return out
+
+
+_STRATEGIES = {"logit": C.SAGA_MERGE_LOGIT, "key": C.SAGA_MERGE_KEY,
+               "sequential": C.SAGA_MERGE_SEQUENTIAL}
+
+
+def key_merge_workspace_size(L, D, h_q, h_kt, d) -> int:
+    return C.saga_key_merge_workspace_size(L, D, h_q, h_kt, d)
+
+
+def key_merge(x, wq, wk, h_q, h_kt, strategy="logit", *, workspace=None, pair_w=None,
+              objective=None, stats=None, stream=None):
+    """GQA -> SAGA key-head merge of one attention module (bf16 device tensors
+    x [L][D], wq [h_q*d][D], wk [h_kt*d][D]). Returns (merged_k float32
+    [h_kt/2][d][D], sigma int32 [h_kt]); pair_w (float64 [h_kt][h_kt]),
+    objective (float64 [1]) and stats (float32 [h_kt*d*d + (h_kt*d)^2]) are
+    filled when given."""
+    for name, t in (("x", x), ("wq", wq), ("wk", wk)):
+        if not t.is_cuda or not t.is_contiguous() or t.dtype != torch.bfloat16:
+            raise ValueError(f"{name} must be a contiguous bf16 device tensor")
+    L, D = x.shape
+    if wq.shape[1] != D or wk.shape[1] != D or wq.shape[0] % h_q or wk.shape[0] % h_kt:
+        raise ValueError("wq must be [h_q*d][D] and wk [h_kt*d][D]")
+    d = wq.shape[0] // h_q
+    if wk.shape[0] != h_kt * d:
+        raise ValueError("wq and wk head dimensions differ")
+    if workspace is None:
+        n = C.saga_key_merge_workspace_size(L, D, h_q, h_kt, d)
+        if n == 0:
+            raise C.SagaError(C.SAGA_ERR_UNSUPPORTED, "saga_key_merge_workspace_size")
+        workspace = new_workspace(n, x.device)
+    merged = torch.empty((h_kt // 2, d, D), dtype=torch.float32, device=x.device)
+    sigma = torch.empty((h_kt,), dtype=torch.int32, device=x.device)
+    st = C.saga_key_merge(x, wq, wk, L, D, h_q, h_kt, d, _STRATEGIES[strategy], C.SAGA_BF16,
+                          merged, sigma, pair_w, objective, stats, workspace, workspace.numel(),
+                          _stream(stream))
+    if st != C.SAGA_OK:
+        raise C.SagaError(st, "saga_key_merge")
+    return merged, sigma
+
+
+def merge_permute(sigma, wq, wv, wo, h_q, h_kt, *, stream=None):
+    """App. B's induced permutations: returns (wq', wv', wo') for the pairing
+    sigma (int32 device [h_kt]); wq [h_q*d][D], wv [h_kt*d][D], wo [D][h_q*d]."""
+    D = wq.shape[1]
+    d = wq.shape[0] // h_q
+    dt = _dtype_code(wq)
+    for t in (wq, wv, wo):
+        if not t.is_cuda or not t.is_contiguous() or t.dtype != wq.dtype:
+            raise ValueError("weights must be contiguous device tensors of one dtype")
+    outs = [torch.empty_like(t) for t in (wq, wv, wo)]
+    st = C.saga_merge_permute(sigma, wq, wv, wo, D, h_q, h_kt, d, dt, *outs, _stream(stream))
+    if st != C.SAGA_OK:
+        raise C.SagaError(st, "saga_merge_permute")
+    return tuple(outs)

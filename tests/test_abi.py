@@ -210,3 +210,61 @@ def test_sparq_workspace_extends_the_decode_workspace():
         extra = B * h_k * d * 4 + B * h_k * (d // 16) * 64 * 4 * e + B * h_q * 4 + B * h_q * d * 4
         assert n <= base + extra + 4 * 256
     assert sw(1, 4, 1, 2, 64, 10, 0, 100, 1) == 0 and sw(1, 4, 1, 2, 64, 10, 65, 100, 1) == 0
+
+
+def _merge(**kw):
+    a = dict(x=FAKE, wq=FAKE, wk=FAKE, L=700, D=512, h_q=8, h_kt=4, d=64, strat=0,
+             dt=saga.SAGA_BF16, merged=FAKE, sigma=FAKE, pw=None, obj=None, stats=None,
+             ws=FAKE * 16, wsb=1 << 40)
+    a.update(kw)
+    return saga.saga_key_merge(a["x"], a["wq"], a["wk"], a["L"], a["D"], a["h_q"], a["h_kt"],
+                               a["d"], a["strat"], a["dt"], a["merged"], a["sigma"], a["pw"],
+                               a["obj"], a["stats"], a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(x=None), saga.SAGA_ERR_INVALID_ARG),
+    (dict(wk=None), saga.SAGA_ERR_INVALID_ARG),
+    (dict(merged=None), saga.SAGA_ERR_INVALID_ARG),
+    (dict(sigma=None), saga.SAGA_ERR_INVALID_ARG),
+    (dict(strat=3), saga.SAGA_ERR_INVALID_ARG),
+    (dict(h_kt=3, h_q=6), saga.SAGA_ERR_INVALID_ARG),     # odd teacher key-head count
+    (dict(h_q=6), saga.SAGA_ERR_INVALID_ARG),             # h_q not a multiple of h_kt
+    (dict(L=0), saga.SAGA_ERR_INVALID_ARG),
+    (dict(x=FAKE + 8), saga.SAGA_ERR_INVALID_ARG),        # misaligned
+    (dict(dt=saga.SAGA_F32), saga.SAGA_ERR_UNSUPPORTED),
+    (dict(d=144, h_q=8), saga.SAGA_ERR_UNSUPPORTED),      # beyond the LDS Jacobi matrix
+    (dict(d=40), saga.SAGA_ERR_UNSUPPORTED),              # not a multiple of 16
+    (dict(D=500), saga.SAGA_ERR_UNSUPPORTED),
+    (dict(h_kt=26, h_q=26), saga.SAGA_ERR_UNSUPPORTED),   # beyond the subset DP
+    (dict(ws=None), saga.SAGA_ERR_WORKSPACE),
+    (dict(wsb=4096), saga.SAGA_ERR_WORKSPACE),
+])
+def test_key_merge_rejects_bad_arguments_on_host(kw, code):
+    assert _merge(**kw) == code
+
+
+def test_key_merge_timed_and_permute_reject_on_host():
+    tm = saga.saga_key_merge_timed
+    args = (FAKE, FAKE, FAKE, 700, 512, 8, 4, 64, 0, saga.SAGA_BF16, FAKE, FAKE, None, None, None,
+            FAKE * 16, 1 << 40, None)
+    assert tm(*args, None, 1) == saga.SAGA_ERR_INVALID_ARG
+    assert tm(*args, None, 5) == saga.SAGA_ERR_INVALID_ARG
+    pm = saga.saga_merge_permute
+    ok = (FAKE, FAKE, FAKE, FAKE, 512, 8, 4, 64, saga.SAGA_BF16, FAKE * 2, FAKE * 3, FAKE * 4,
+          None)
+    assert pm(None, *ok[1:]) == saga.SAGA_ERR_INVALID_ARG
+    assert pm(*ok[:4], 512, 6, 4, 64, *ok[8:]) == saga.SAGA_ERR_INVALID_ARG      # h_q % h_kt
+    assert pm(*ok[:4], 512, 8, 4, 60, *ok[8:]) == saga.SAGA_ERR_UNSUPPORTED      # 120-byte blocks
+    assert pm(*ok[:4], 512, 8, 4, 64, 7, *ok[9:]) == saga.SAGA_ERR_INVALID_ARG   # dtype
+    assert pm(*ok[:9], FAKE * 2 + 8, *ok[10:]) == saga.SAGA_ERR_INVALID_ARG     # misaligned
+
+
+def test_key_merge_workspace_size():
+    mw = saga.saga_key_merge_workspace_size
+    assert mw(700, 512, 8, 4, 64) > 0 and mw(700, 512, 8, 4, 64) % 256 == 0
+    # one 256 x 256 fp32 X^T X partial per (tile, split), then C, W C, the
+    # statistics, the rotation records and the per-pair matrices
+    n = mw(131072, 2048, 32, 8, 64)
+    assert 36 * 7 * 256 * 256 * 4 < n < 36 * 7 * 256 * 256 * 4 + (96 << 20)
+    assert mw(700, 512, 8, 3, 64) == 0 and mw(700, 512, 8, 4, 136) == 0 and mw(0, 512, 8, 4, 64) == 0
