@@ -282,9 +282,10 @@ saga_status saga_key_merge(const void* x, const void* wq, const void* wk, int64_
                            size_t workspace_bytes, hipStream_t stream);
 
 /*
- * saga_key_merge with up to 4 events recorded on `stream` after the phases:
- * [0] X^T X, [1] statistics S and H, [2] per-pair closed forms and weights,
- * [3] matching and merged projections. n_events outside 0..4 (or events null
+ * saga_key_merge with up to 5 events recorded on `stream` after the phases:
+ * [0] X^T X partial products (one dispatch), [1] their reduction to X^T X,
+ * [2] statistics S and H, [3] per-pair closed forms and weights, [4]
+ * matching and merged projections. n_events outside 0..5 (or events null
  * with n_events > 0): SAGA_ERR_INVALID_ARG.
  */
 saga_status saga_key_merge_timed(const void* x, const void* wq, const void* wk, int64_t L,

@@ -207,12 +207,18 @@ def saga_key_merge(x, wq, wk, L, D, h_q, h_kt, d, strategy, dtype, merged_k, sig
 
 def saga_key_merge_timed(x, wq, wk, L, D, h_q, h_kt, d, strategy, dtype, merged_k, sigma,
                          pair_w, objective, stats, workspace, workspace_bytes, stream, events,
-                         n_events) -> int:
+                         n_events=None) -> int:
+    """events: a sequence of hipEvent_t handles (ints), or None."""
+    if events is None:
+        arr, n = None, int(n_events or 0)
+    else:
+        n = len(events) if n_events is None else int(n_events)
+        arr = (ctypes.c_void_p * max(1, len(events)))(*[ctypes.c_void_p(int(e)) for e in events])
     return int(lib.saga_key_merge_timed(_ptr(x), _ptr(wq), _ptr(wk), L, D, h_q, h_kt, d,
                                         strategy, dtype, _ptr(merged_k), _ptr(sigma),
                                         _ptr(pair_w), _ptr(objective), _ptr(stats),
                                         _ptr(workspace), workspace_bytes, _ptr(stream),
-                                        events, n_events))
+                                        arr, n))
 
 
 def saga_merge_permute(sigma, wq, wv, wo, D, h_q, h_kt, d, dtype, wq_out, wv_out, wo_out,

@@ -344,7 +344,7 @@ struct PairOut {
     double w_logit;   // Eq. 16
     double w_key;     // Eq. 35: tr(Delta)
     double l_avg;     // Eq. 13 at the average of the two heads: tr(Delta P) / 4
-    double sweeps;    // Jacobi sweeps run
+    double sweeps;    // Jacobi sweeps run (0: the Gauss-Jordan path)
 };
 
 __device__ inline void pair_of_index(int p, int n, int& a, int& b) {
@@ -388,6 +388,7 @@ struct PairArgs {
     const float* H;      // [n d][n d]
     double* Y;           // [npairs][d][d]  P^+ S_a
     double* Z;           // [npairs][d][d]  P^+ S_b
+    double* Dl;          // [npairs][d][d]  Delta
     double2* rec;        // [npairs][kMaxSweeps][d - 1][d / 2]  (c, s)
     PairOut* out;        // [npairs]
     int n, d, strategy;
@@ -434,55 +435,245 @@ __device__ void replay(double* Ym, int d, const double2* rec, int nrounds, bool 
     }
 }
 
-// doubles of the matrix region: the Jacobi matrix, or the four GEMM panels
+// Two sums over the workgroup at once (one pair of barriers).
+__device__ inline void block_sum2(double& x, double& y, double* red) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        x += __shfl_xor(x, o);
+        y += __shfl_xor(y, o);
+    }
+    const int w = threadIdx.x >> 6;
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) {
+        red[2 * w] = x;
+        red[2 * w + 1] = y;
+    }
+    __syncthreads();
+    x = y = 0.0;
+    for (int i = 0; i < (int)(blockDim.x >> 6); ++i) {
+        x += red[2 * i];
+        y += red[2 * i + 1];
+    }
+}
+
+// Largest eigenvalue of the symmetric d x d matrix in LDS (row stride ld) by
+// power iteration from a fixed start vector (4 threads per row); the estimate
+// is the Rayleigh quotient of the last iterate.
+__device__ double power_max(const double* Am, int d, int ld, double* v, double* w,
+                            double* red, int iters) {
+    const int tid = threadIdx.x, row = tid >> 2, q = tid & 3;
+    if (tid < d) v[tid] = 1.0 + 0.125 * (tid % 5);
+    __syncthreads();
+    double nv = block_sum(tid < d ? v[tid] * v[tid] : 0.0, red);
+    double rq = 0.0;
+    for (int it = 0; it < iters; ++it) {
+        double y = 0.0;
+        if (row < d) {
+            const double* r_ = Am + row * ld;
+#pragma unroll 8
+            for (int j = q; j < d; j += 4) y += r_[j] * v[j];
+        }
+        y += __shfl_xor(y, 1);
+        y += __shfl_xor(y, 2);
+        const bool own = q == 0 && row < d;
+        double vy = own ? v[row] * y : 0.0, yy = own ? y * y : 0.0;
+        if (own) w[row] = y;
+        block_sum2(vy, yy, red);
+        rq = vy / nv;
+        if (!(yy > 0.0) || !isfinite(yy)) return yy == 0.0 ? 0.0 : rq;
+        const double sc = 1.0 / sqrt(yy);
+        if (tid < d) v[tid] = w[tid] * sc;
+        nv = 1.0;
+        __syncthreads();
+    }
+    return rq;
+}
+
+// In-place Gauss-Jordan inversion of the symmetric positive definite d x d
+// matrix in LDS (no pivoting; every pivot is a Schur-complement diagonal).
+// Step k: A[i][j] -= A[i][k] A[k][j] / A[k][k] for every element, then row k
+// becomes A[k][j] / A[k][k], column k -A[i][k] / A[k][k] and the pivot
+// 1 / A[k][k]. Thread (ig, j) keeps elements (4 t + ig, j) in registers for
+// the whole elimination; column k and row k are broadcast through LDS, the
+// column stored so that each thread's factors are contiguous. Returns the
+// smallest pivot (<= 0 or NaN: not positive definite).
+__device__ double gj_invert(double* Am, int d, int ld, double* fcol, double* rowk) {
+    constexpr int R = 128 / (kPairThreads / 128);   // rows per thread (d <= 128)
+    const int tid = threadIdx.x, j = tid & 127, ig = tid >> 7;
+    const bool act = j < d;
+    double v[R];
+#pragma unroll
+    for (int t = 0; t < R; ++t) {
+        const int i = 4 * t + ig;
+        v[t] = act && i < d ? Am[i * ld + j] : 0.0;
+    }
+    const double* myf = fcol + ig * R;
+    double minpiv = INFINITY;
+    for (int k = 0; k < d; ++k) {
+        if (act && j == k)
+#pragma unroll
+            for (int t = 0; t < R; ++t) fcol[ig * R + t] = v[t];
+        if (act && (k & 3) == ig) {
+            double r = 0.0;
+#pragma unroll
+            for (int t = 0; t < R; ++t) r = t == (k >> 2) ? v[t] : r;
+            rowk[j] = r;
+        }
+        __syncthreads();
+        const double pk = rowk[k];
+        minpiv = fmin(minpiv, pk);
+        const double piv = 1.0 / pk;
+        if (act) {
+            const double rj = rowk[j] * piv;
+#pragma unroll
+            for (int t = 0; t < R; ++t) v[t] -= myf[t] * rj;
+            if (j == k)
+#pragma unroll
+                for (int t = 0; t < R; ++t) v[t] = -myf[t] * piv;
+            if ((k & 3) == ig) {
+                const double nv = j == k ? piv : rj;
+#pragma unroll
+                for (int t = 0; t < R; ++t) v[t] = t == (k >> 2) ? nv : v[t];
+            }
+        }
+        __syncthreads();
+    }
+#pragma unroll
+    for (int t = 0; t < R; ++t) {
+        const int i = 4 * t + ig;
+        if (act && i < d) Am[i * ld + j] = v[t];
+    }
+    __syncthreads();
+    return minpiv;
+}
+
+__device__ inline double ldd(const double* p) { return *p; }
+__device__ inline double ldd(const float* p) { return (double)*p; }
+
+// Workgroup GEMM over d x d row-major matrices in global memory, 64 x 64
+// output tiles: C1 = A1 B1 (and C2 = A2 B2 when DUAL). Each thread holds 4
+// rows x 2 columns of a tile; 16-wide k panels are double-buffered in LDS
+// (pan: 2 x (DUAL ? 4 : 2) panels of [16][68] doubles, A panels stored
+// k-major) while the next panel is loaded into registers. DUAL returns this
+// thread's share of sum(C1 .* C2); otherwise C1 is stored to out and 0 returned.
+constexpr int kPanLd = 68;
+constexpr int kPanWords = 16 * kPanLd;
+template <bool DUAL, typename TA1, typename TB1, typename TA2, typename TB2>
+__device__ double wg_gemm(int d, const TA1* A1, const TB1* B1, const TA2* A2, const TB2* B2,
+                          double* out, double* pan) {
+    constexpr int NP = DUAL ? 4 : 2;
+    const int tid = threadIdx.x, tr = (tid >> 5) * 4, tc = (tid & 31) * 2;
+    // this thread's two elements of every panel: A (row ar, k ak), B (k bk, col bc)
+    const int ar0 = tid >> 4, ak = tid & 15, ar1 = ar0 + 32;
+    const int bk0 = tid >> 6, bc = tid & 63, bk1 = bk0 + 8;
+    const int npan = d / 16;
+    double dot = 0.0;
+    for (int ti = 0; ti < d; ti += 64)
+        for (int tj = 0; tj < d; tj += 64) {
+            double acc1[4][2], acc2[4][2];
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+#pragma unroll
+                for (int c = 0; c < 2; ++c) acc1[r][c] = acc2[r][c] = 0.0;
+            const bool a0 = ti + ar0 < d, a1 = ti + ar1 < d, bb = tj + bc < d;
+            const int64_t ra0 = (int64_t)(a0 ? ti + ar0 : 0) * d + ak;
+            const int64_t ra1 = (int64_t)(a1 ? ti + ar1 : 0) * d + ak;
+            const int64_t rb0 = (int64_t)bk0 * d + (bb ? tj + bc : 0);
+            const int64_t rb1 = (int64_t)bk1 * d + (bb ? tj + bc : 0);
+            double x0, x1, y0, y1, u0 = 0, u1 = 0, w0 = 0, w1 = 0;
+            x0 = ldd(A1 + ra0);
+            x1 = ldd(A1 + ra1);
+            y0 = ldd(B1 + rb0);
+            y1 = ldd(B1 + rb1);
+            if constexpr (DUAL) {
+                u0 = ldd(A2 + ra0);
+                u1 = ldd(A2 + ra1);
+                w0 = ldd(B2 + rb0);
+                w1 = ldd(B2 + rb1);
+            }
+            for (int p = 0; p < npan; ++p) {
+                double* base = pan + (p & 1) * NP * kPanWords;
+                base[ak * kPanLd + ar0] = a0 ? x0 : 0.0;
+                base[ak * kPanLd + ar1] = a1 ? x1 : 0.0;
+                base[kPanWords + bk0 * kPanLd + bc] = bb ? y0 : 0.0;
+                base[kPanWords + bk1 * kPanLd + bc] = bb ? y1 : 0.0;
+                if constexpr (DUAL) {
+                    base[2 * kPanWords + ak * kPanLd + ar0] = a0 ? u0 : 0.0;
+                    base[2 * kPanWords + ak * kPanLd + ar1] = a1 ? u1 : 0.0;
+                    base[3 * kPanWords + bk0 * kPanLd + bc] = bb ? w0 : 0.0;
+                    base[3 * kPanWords + bk1 * kPanLd + bc] = bb ? w1 : 0.0;
+                }
+                __syncthreads();
+                if (p + 1 < npan) {   // next panel in flight while this one is used
+                    const int64_t ko = (int64_t)16 * (p + 1), kr = ko * d;
+                    x0 = ldd(A1 + ra0 + ko);
+                    x1 = ldd(A1 + ra1 + ko);
+                    y0 = ldd(B1 + rb0 + kr);
+                    y1 = ldd(B1 + rb1 + kr);
+                    if constexpr (DUAL) {
+                        u0 = ldd(A2 + ra0 + ko);
+                        u1 = ldd(A2 + ra1 + ko);
+                        w0 = ldd(B2 + rb0 + kr);
+                        w1 = ldd(B2 + rb1 + kr);
+                    }
+                }
+#pragma unroll
+                for (int kk = 0; kk < 16; ++kk) {
+                    const double* ap = base + kk * kPanLd + tr;
+                    const double* bp = base + kPanWords + kk * kPanLd + tc;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+#pragma unroll
+                        for (int c = 0; c < 2; ++c) acc1[r][c] += ap[r] * bp[c];
+                    if constexpr (DUAL) {
+                        const double* ap2 = base + 2 * kPanWords + kk * kPanLd + tr;
+                        const double* bp2 = base + 3 * kPanWords + kk * kPanLd + tc;
+#pragma unroll
+                        for (int r = 0; r < 4; ++r)
+#pragma unroll
+                            for (int c = 0; c < 2; ++c) acc2[r][c] += ap2[r] * bp2[c];
+                    }
+                }
+            }
+            __syncthreads();
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+#pragma unroll
+                for (int c = 0; c < 2; ++c) {
+                    const int i = ti + tr + r, jj = tj + tc + c;
+                    if (i < d && jj < d) {
+                        if constexpr (DUAL)
+                            dot += acc1[r][c] * acc2[r][c];
+                        else
+                            out[(int64_t)i * d + jj] = acc1[r][c];
+                    }
+                }
+        }
+    return dot;
+}
+
+// doubles of the matrix region: the Jacobi matrix, or the GEMM panels
 __host__ __device__ inline int pair_matrix_words(int d) {
-    const int jac = d * (d + 1), gem = 2 * (64 * 17 + 16 * 65);
+    const int jac = d * (d + 1), gem = 2 * 4 * kPanWords;
     return jac > gem ? jac : gem;
 }
 
-// One workgroup per pair (a, b), a < b.
-__global__ __launch_bounds__(kPairThreads) void merge_pairs(PairArgs pa) {
-    extern __shared__ __attribute__((aligned(16))) char smem_raw[];
-    const int d = pa.d, np = d / 2, ld = d + 1, tid = threadIdx.x;
-    const int pidx = blockIdx.x;
-    int a, b;
-    pair_of_index(pidx, pa.n, a, b);
-    double* Am = reinterpret_cast<double*>(smem_raw);   // [d][d + 1], later GEMM panels
-    double2* cs = reinterpret_cast<double2*>(Am + pair_matrix_words(d));   // [2][64]
-    double* lam = reinterpret_cast<double*>(cs + 128);       // [d]
-    double* red = lam + 128;                                  // [16]
-    int* flag = reinterpret_cast<int*>(red + 16);
-    const int hd = pa.n * d;
-    const float* Sa = pa.S + (int64_t)a * d * d;
-    const float* Sb = pa.S + (int64_t)b * d * d;
-    double* Y = pa.Y + (int64_t)pidx * d * d;
-    double* Z = pa.Z + (int64_t)pidx * d * d;
-
-    // tr(Delta), tr(Delta P); P into LDS
-    double t1 = 0.0, t2 = 0.0;
+// P^+ S_a into Y and P^+ S_b into Z through the eigen-decomposition of
+// P = S_a + S_b: cyclic Jacobi rotations on the matrix in LDS (a round rotates
+// d / 2 disjoint index pairs), each round's rotations recorded in rec, then
+// replayed on S_a (and on I when eigenvalues fall at or below the cutoff
+// 2^-23 d lambda_max, to form P P^+). Returns the sweeps run.
+__device__ int jacobi_pinv(double* Am, int d, const float* Sa, const float* Sb, double* Y,
+                           double* Z, double2* rec, double2* cs, double* lam, double* red,
+                           int* flag) {
+    const int np = d / 2, ld = d + 1, tid = threadIdx.x;
     for (int idx = tid; idx < d * d; idx += kPairThreads) {
         const int i = idx / d, j = idx - i * d;
-        const double P = (double)Sa[idx] + (double)Sb[idx];
-        const double dl = delta_at(pa.H, hd, a, b, d, i, j);
-        Am[i * ld + j] = P;
-        t2 += dl * P;
-        if (i == j) t1 += dl;
+        Am[i * ld + j] = (double)Sa[idx] + (double)Sb[idx];
     }
-    const double trd = block_sum(t1, red);
-    const double trdp = block_sum(t2, red);
-
-    if (pa.strategy != 0) {
-        for (int idx = tid; idx < d * d; idx += kPairThreads) {
-            const int i = idx / d, j = idx - i * d;
-            Y[idx] = Z[idx] = i == j ? 0.5 : 0.0;
-        }
-        if (tid == 0) pa.out[pidx] = PairOut{0.0, trd, 0.25 * trdp, 0.0};
-        return;
-    }
-
+    __syncthreads();
     // cyclic Jacobi (rotations zero one off-diagonal pair each; a round
     // rotates d / 2 disjoint pairs at once)
-    double2* rec = pa.rec + (int64_t)pidx * kMaxSweeps * (d - 1) * np;
     int sweeps = 0;
     for (; sweeps < kMaxSweeps; ++sweeps) {
         double off = 0.0, dia = 0.0;
@@ -583,51 +774,98 @@ __global__ __launch_bounds__(kPairThreads) void merge_pairs(PairArgs pa) {
         const double e = trunc ? Z[idx] : (i == j ? 1.0 : 0.0);
         Z[idx] = e - Y[idx];
     }
-    __threadfence_block();
+    return sweeps;
+}
+
+// One workgroup per pair (a, b), a < b.
+__global__ __launch_bounds__(kPairThreads) void merge_pairs(PairArgs pa) {
+    extern __shared__ __attribute__((aligned(16))) char smem_raw[];
+    const int d = pa.d, np = d / 2, ld = d + 1, tid = threadIdx.x;
+    const int pidx = blockIdx.x;
+    int a, b;
+    pair_of_index(pidx, pa.n, a, b);
+    double* Am = reinterpret_cast<double*>(smem_raw);   // [d][d + 1], later GEMM panels
+    double2* cs = reinterpret_cast<double2*>(Am + pair_matrix_words(d));   // [2][64]
+    double* lam = reinterpret_cast<double*>(cs + 128);       // [d]
+    double* va = lam + 128;                                   // [d] power-iteration vector,
+    double* vb = va + 128;                                    // [d] Gauss-Jordan buffers
+    double* red = vb + 128;                                   // [16]
+    int* flag = reinterpret_cast<int*>(red + 16);
+    const int hd = pa.n * d;
+    const float* Sa = pa.S + (int64_t)a * d * d;
+    const float* Sb = pa.S + (int64_t)b * d * d;
+    double* Y = pa.Y + (int64_t)pidx * d * d;
+    double* Z = pa.Z + (int64_t)pidx * d * d;
+    double* Dl = pa.Dl + (int64_t)pidx * d * d;
+
+    // Delta to global, P into LDS; tr(Delta), tr(Delta P), ||P||_F^2
+    double t1 = 0.0, t2 = 0.0, t3 = 0.0;
+    for (int idx = tid; idx < d * d; idx += kPairThreads) {
+        const int i = idx / d, j = idx - i * d;
+        const double P = (double)Sa[idx] + (double)Sb[idx];
+        const double dl = delta_at(pa.H, hd, a, b, d, i, j);
+        Am[i * ld + j] = P;
+        Dl[idx] = dl;
+        t2 += dl * P;
+        t3 += P * P;
+        if (i == j) t1 += dl;
+    }
+    block_sum2(t1, t2, red);
+    const double trd = t1, trdp = t2;
+    const double pf2 = block_sum(t3, red);
+
+    if (pa.strategy != 0) {
+        for (int idx = tid; idx < d * d; idx += kPairThreads) {
+            const int i = idx / d, j = idx - i * d;
+            Y[idx] = Z[idx] = i == j ? 0.5 : 0.0;
+        }
+        if (tid == 0) pa.out[pidx] = PairOut{0.0, trd, 0.25 * trdp, 0.0};
+        return;
+    }
+
+    // Positive definite P with every eigenvalue well above the pseudo-inverse
+    // cutoff 2^-23 d lambda_max: P^+ = P^{-1}, by Gauss-Jordan. The smallest
+    // eigenvalue is bounded below by 1 / ||P^{-1}||_F; only when that bound
+    // does not settle it is it estimated by power iteration on P^{-1}. When P
+    // is not clearly regular, the eigen-decomposition decides which
+    // eigenvalues count as zero.
+    const double lmax_p = power_max(Am, d, ld, va, vb, red, 12);
+    const double minpiv = gj_invert(Am, d, ld, va, vb);
+    double q2 = 0.0;
+    for (int idx = tid; idx < d * d; idx += kPairThreads) {
+        const int i = idx / d, j = idx - i * d;
+        const double v = Am[i * ld + j];
+        q2 += v * v;
+    }
+    const double pinv_f = sqrt(block_sum(q2, red));
+    const double cut4 = 4.0 * 0x1p-23 * d * lmax_p;
+    bool regular = minpiv > 0.0 && isfinite(pinv_f) && pinv_f > 0.0 && pf2 > 0.0;
+    if (regular && !(1.0 / pinv_f > cut4)) {
+        const double linv = power_max(Am, d, ld, va, vb, red, 40);   // 1 / lambda_min
+        regular = isfinite(linv) && linv > 0.0 && 1.0 / linv > cut4;
+    }
+    int sweeps = 0;
+    if (regular) {
+        for (int idx = tid; idx < d * d; idx += kPairThreads) {
+            const int i = idx / d, j = idx - i * d;
+            Z[idx] = Am[i * ld + j];
+        }
+        __syncthreads();
+        wg_gemm<false>(d, Z, Sa, Z, Sa, Y, Am);     // Y = P^{-1} S_a
+        __syncthreads();
+        for (int idx = tid; idx < d * d; idx += kPairThreads) {
+            const int i = idx / d, j = idx - i * d;
+            Z[idx] = (i == j ? 1.0 : 0.0) - Y[idx];
+        }
+    } else {
+        sweeps = jacobi_pinv(Am, d, Sa, Sb, Y, Z, pa.rec + (int64_t)pidx * kMaxSweeps * (d - 1) * np,
+                             cs, lam, red, flag);
+    }
     __syncthreads();
 
-    // w = <Z Delta, S_a Z> + <Y Delta, S_b Y>, 64 x 64 output tiles, k panels of 16
-    double* As1 = Am;                 // [64][17]
-    double* Bs1 = As1 + 64 * 17;      // [16][65]
-    double* As2 = Bs1 + 16 * 65;
-    double* Bs2 = As2 + 64 * 17;
-    const int tr = tid >> 3, tc = (tid & 7) * 8;
-    double dot = 0.0;
-    for (int term = 0; term < 2; ++term) {
-        const double* L1 = term == 0 ? Z : Y;    // left of X1 = L1 Delta, right of X2 = S L1
-        const float* Sm = term == 0 ? Sa : Sb;
-        for (int ti = 0; ti < d; ti += 64)
-            for (int tj = 0; tj < d; tj += 64) {
-                double acc1[8], acc2[8];
-#pragma unroll
-                for (int x = 0; x < 8; ++x) acc1[x] = acc2[x] = 0.0;
-                for (int k0 = 0; k0 < d; k0 += 16) {
-                    for (int e = tid; e < 1024; e += kPairThreads) {
-                        const int ar = e >> 4, ak = e & 15;          // A panels [64][16]
-                        const int i = ti + ar, k = k0 + ak;
-                        As1[ar * 17 + ak] = i < d ? L1[(int64_t)i * d + k] : 0.0;
-                        As2[ar * 17 + ak] = i < d ? (double)Sm[(int64_t)i * d + k] : 0.0;
-                        const int bk = e >> 6, bc = e & 63;          // B panels [16][64]
-                        const int j = tj + bc, kb = k0 + bk;
-                        Bs1[bk * 65 + bc] = j < d ? delta_at(pa.H, hd, a, b, d, kb, j) : 0.0;
-                        Bs2[bk * 65 + bc] = j < d ? L1[(int64_t)kb * d + j] : 0.0;
-                    }
-                    __syncthreads();
-#pragma unroll
-                    for (int kk = 0; kk < 16; ++kk) {
-                        const double a1 = As1[tr * 17 + kk], a2 = As2[tr * 17 + kk];
-#pragma unroll
-                        for (int x = 0; x < 8; ++x) {
-                            acc1[x] += a1 * Bs1[kk * 65 + tc + x];
-                            acc2[x] += a2 * Bs2[kk * 65 + tc + x];
-                        }
-                    }
-                    __syncthreads();
-                }
-#pragma unroll
-                for (int x = 0; x < 8; ++x) dot += acc1[x] * acc2[x];
-            }
-    }
+    // w = <Z Delta, S_a Z> + <Y Delta, S_b Y>
+    double dot = wg_gemm<true>(d, Z, Dl, Sa, Z, nullptr, Am);
+    dot += wg_gemm<true>(d, Y, Dl, Sb, Y, nullptr, Am);
     dot = block_sum(dot, red + 8);
     if (tid == 0) pa.out[pidx] = PairOut{dot, trd, 0.25 * trdp, (double)sweeps};
 }
@@ -769,7 +1007,7 @@ __global__ __launch_bounds__(256) void merge_permute(const int32_t* __restrict__
 struct MergeWs {
     f32x4* part;
     float *C, *F, *S, *H, *part_s, *part_h;
-    double *Y, *Z;
+    double *Y, *Z, *Dl;
     double2* rec;
     PairOut* po;
     MatchWs m;
@@ -810,6 +1048,7 @@ static MergeWs carve_merge(void* base, int64_t L, int D, int h_q, int h_kt, int 
     }
     w.Y = reinterpret_cast<double*>(take(np * d * d * 8));
     w.Z = reinterpret_cast<double*>(take(np * d * d * 8));
+    w.Dl = reinterpret_cast<double*>(take(np * d * d * 8));
     w.rec = reinterpret_cast<double2*>(take(np * kMaxSweeps * (d - 1) * (d / 2) * 16));
     w.po = reinterpret_cast<PairOut*>(take(np * sizeof(PairOut)));
     w.m.w = reinterpret_cast<double*>(take((size_t)h_kt * h_kt * 8));
@@ -821,7 +1060,7 @@ static MergeWs carve_merge(void* base, int64_t L, int D, int h_q, int h_kt, int 
 }
 
 static size_t pair_lds(int d) {
-    return (size_t)pair_matrix_words(d) * 8 + 128 * 16 + 128 * 8 + 16 * 8 + 16;
+    return (size_t)pair_matrix_words(d) * 8 + 128 * 16 + 3 * 128 * 8 + 16 * 8 + 16;
 }
 
 static bool merge_shape_ok(int64_t L, int D, int h_q, int h_kt, int d) {
@@ -872,7 +1111,7 @@ static saga_status key_merge_impl(const void* x, const void* wq, const void* wk,
                                   size_t workspace_bytes, hipStream_t st, hipEvent_t* ev,
                                   int nev) {
     if (!x || !wq || !wk || !merged || !sigma) return SAGA_ERR_INVALID_ARG;
-    if (strategy < 0 || strategy > 2 || nev < 0 || nev > 4 || (nev > 0 && !ev))
+    if (strategy < 0 || strategy > 2 || nev < 0 || nev > 5 || (nev > 0 && !ev))
         return SAGA_ERR_INVALID_ARG;
     if (L < 1 || D < 1 || d < 1 || h_q < 1 || h_kt < 2 || h_kt % 2 || h_q % h_kt)
         return SAGA_ERR_INVALID_ARG;
@@ -900,10 +1139,11 @@ static saga_status key_merge_impl(const void* x, const void* wq, const void* wk,
     hipLaunchKernelGGL(syrk_partial, dim3(grid), dim3(kSyrkThreads), kSyrkLds, st,
                        static_cast<const uint16_t*>(x), L, D, nt, ns, split_len(L, ns), grid,
                        w.part);
+    mark(0);
     const int64_t slots = (int64_t)nt * 8 * 32 * 64;
     hipLaunchKernelGGL(syrk_reduce, dim3((unsigned)((slots + 255) / 256)), dim3(256), 0, st,
                        w.part, D, nt, ns, w.C);
-    mark(0);
+    mark(1);
     // 2. F = [W_Q; W_K] C, then S and H
     const int g = h_q / h_kt;
     float* Fq = w.F;
@@ -934,12 +1174,12 @@ static saga_status key_merge_impl(const void* x, const void* wq, const void* wk,
         ok = hipMemcpyAsync(stats + (size_t)h_kt * d * d, w.H, (size_t)h_kt * d * h_kt * d * 4,
                             hipMemcpyDeviceToDevice, st) == hipSuccess && ok;
     }
-    mark(1);
+    mark(2);
     // 3. pairs
-    PairArgs pa{w.S, w.H, w.Y, w.Z, w.rec, w.po, h_kt, d, strategy};
+    PairArgs pa{w.S, w.H, w.Y, w.Z, w.Dl, w.rec, w.po, h_kt, d, strategy};
     const int npairs = h_kt * (h_kt - 1) / 2;
     hipLaunchKernelGGL(merge_pairs, dim3(npairs), dim3(kPairThreads), pair_lds(d), st, pa);
-    mark(2);
+    mark(3);
     // 4. matching, 5. merged projections
     hipLaunchKernelGGL(match_weights, dim3(1), dim3(256), 0, st, w.po, h_kt, strategy, w.m);
     if (strategy != 2) {
@@ -951,7 +1191,7 @@ static saga_status key_merge_impl(const void* x, const void* wq, const void* wk,
                        pair_w, objective);
     hipLaunchKernelGGL(merge_apply, dim3((D + 255) / 256, d, h_kt / 2), dim3(256), 0, st,
                        static_cast<const uint16_t*>(wk), w.Y, w.Z, w.m.pairs, h_kt, d, D, merged);
-    mark(3);
+    mark(4);
     return hipGetLastError() == hipSuccess && ok ? SAGA_OK : SAGA_ERR_HIP;
 }
 

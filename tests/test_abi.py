@@ -249,7 +249,7 @@ def test_key_merge_timed_and_permute_reject_on_host():
     args = (FAKE, FAKE, FAKE, 700, 512, 8, 4, 64, 0, saga.SAGA_BF16, FAKE, FAKE, None, None, None,
             FAKE * 16, 1 << 40, None)
     assert tm(*args, None, 1) == saga.SAGA_ERR_INVALID_ARG
-    assert tm(*args, None, 5) == saga.SAGA_ERR_INVALID_ARG
+    assert tm(*args, None, 6) == saga.SAGA_ERR_INVALID_ARG
     pm = saga.saga_merge_permute
     ok = (FAKE, FAKE, FAKE, FAKE, 512, 8, 4, 64, saga.SAGA_BF16, FAKE * 2, FAKE * 3, FAKE * 4,
           None)
