@@ -10,8 +10,9 @@
 //   1. syrk_partial / syrk_reduce: C = X^T X (bf16 MFMA, fp32 accumulation;
 //      upper-triangle 256 x 256 tiles, token range split over workgroups,
 //      partials summed in a fixed order);
-//   2. nt_gemm: F = W C for all query and key heads, then S and H from F
-//      (fp32 MFMA);
+//   2. nt_bf16x3: F = W C for all query and key heads (bf16 MFMA on C split
+//      into three bf16 parts, fp32 accuracy); nt_gemm: S and H from F (fp32
+//      MFMA);
 //   3. merge_pairs: per pair (a, b), in fp64, P = S_a + S_b is diagonalised by
 //      cyclic Jacobi rotations held in LDS; replaying the recorded rotations
 //      gives Y = P^+ S_a and Z = P^+ S_b (the transposes of the coefficients
@@ -199,10 +200,20 @@ __global__ __launch_bounds__(kSyrkThreads, 1) void syrk_partial(
         for (int j = 0; j < 4; ++j) out[(i * 4 + j) * 64 + lane] = acc[i][j];
 }
 
-// C[D][D] (both triangles) = sum over splits of the partials, in split order.
+// bf16 nearest-even of an fp32 value, as bits and as the value it stands for
+__device__ inline uint16_t bf16_bits(float f) {
+    const uint32_t u = __float_as_uint(f);
+    return (uint16_t)((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
+}
+__device__ inline float bf16_val(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+// C[D][D] (both triangles) = sum over splits of the partials, in split order,
+// stored as three bf16 matrices Cs[0] + Cs[1] + Cs[2] = C: each part is the
+// rounding of what the previous parts leave, so the three carry C's 24-bit
+// significand (the residues are exact in fp32).
 __global__ __launch_bounds__(256) void syrk_reduce(const f32x4* __restrict__ part, int D,
                                                    int ntile, int nsplit,
-                                                   float* __restrict__ C) {
+                                                   uint16_t* __restrict__ Cs) {
     const int64_t slots = (int64_t)ntile * 8 * 32 * 64;
     const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (idx >= slots) return;
@@ -220,12 +231,127 @@ __global__ __launch_bounds__(256) void syrk_reduce(const f32x4* __restrict__ par
     for (int e = 0; e < 4; ++e) {
         const int row = row0 + e;
         if (row >= D) break;
-        C[(int64_t)row * D + col] = s[e];
-        if (bi != bj) C[(int64_t)col * D + row] = s[e];
+        float r = s[e];
+        const int64_t dd = (int64_t)D * D;
+#pragma unroll
+        for (int q = 0; q < 3; ++q) {
+            const uint16_t hb = bf16_bits(r);
+            Cs[q * dd + (int64_t)row * D + col] = hb;
+            if (bi != bj) Cs[q * dd + (int64_t)col * D + row] = hb;
+            r -= bf16_val(hb);
+        }
     }
 }
 
 // ---- 2. out[z] = sum_p A_p B_p^T (fp32 MFMA) -----------------------------------
+// F[m][n] = sum_k A[m][k] (B0 + B1 + B2)[n][k] on bf16 MFMA (16x16x32, fp32
+// accumulation): A bf16 [M][K] (the projections: rows m < M0 of A0, then
+// rows of A1, so that query and key heads share one launch), B the three bf16 parts of
+// C [N][K]. Products of bf16 values are exact in fp32, so F carries fp32
+// accuracy. Workgroup tile 128 x 128 (8 waves of 64 x 32), k steps of 32
+// staged through LDS (double-buffered; rows of 32 elements with the 16-byte
+// units XOR-swizzled by row / 4, so the 16-lane groups of a fragment read
+// hit distinct banks). M, N and K are multiples of 16.
+constexpr int kF3Threads = 512;
+constexpr int kF3Tile = 128;
+constexpr int kF3RowB = 64;                                 // 32 bf16 per staged row
+constexpr int kF3Stage = 4 * kF3Tile * kF3RowB;             // A + three B parts: 32 KB
+constexpr int kF3Lds = 2 * kF3Stage;
+
+__device__ inline int f3_swz(int row, int unit) { return unit ^ ((row >> 2) & 3); }
+
+__global__ __launch_bounds__(kF3Threads) void nt_bf16x3(const uint16_t* __restrict__ A0,
+                                                        const uint16_t* __restrict__ A1, int M0,
+                                                        const uint16_t* __restrict__ Bs, int M,
+                                                        int N, int K, float* __restrict__ F) {
+    extern __shared__ __attribute__((aligned(16))) char smem3[];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int m0 = blockIdx.y * kF3Tile, n0 = blockIdx.x * kF3Tile;
+    const int wm = (wave & 1) * 64, wn = (wave >> 1) * 32;
+    // loader: unit u = tid + 512 h, h < 4: matrix u / 512 (0 = A, 1..3 = B parts),
+    // row (u / 4) % 128, 16-byte unit u % 4 of the 32-element k step
+    constexpr int NU = 4 * kF3Tile * 4 / kF3Threads;
+    const int64_t nk = (int64_t)N * K;
+    // this thread's units: fixed rows and matrices, k advancing by 32 per step
+    const uint16_t* src[NU];
+    bool rok[NU];
+    int uoff[NU], ukk[NU];
+#pragma unroll
+    for (int h = 0; h < NU; ++h) {
+        const int u = tid + kF3Threads * h, mat = u >> 9, row = (u >> 2) & 127, un = u & 3;
+        const int grow = (mat == 0 ? m0 : n0) + row;
+        rok[h] = grow < (mat == 0 ? M : N);
+        const int r = rok[h] ? grow : 0;
+        src[h] = mat == 0 ? (r < M0 ? A0 + (int64_t)r * K : A1 + (int64_t)(r - M0) * K)
+                          : Bs + (mat - 1) * nk + (int64_t)r * K;
+        ukk[h] = un * 8;
+        uoff[h] = (mat * kF3Tile + row) * kF3RowB + (f3_swz(row, un) << 4);
+    }
+    u32x4 reg[NU];
+    const int nstep = (K + 31) / 32;
+    auto load = [&](int st) {
+#pragma unroll
+        for (int h = 0; h < NU; ++h) {
+            const int k = 32 * st + ukk[h];
+            const bool ok = rok[h] && k < K;
+            reg[h] = *reinterpret_cast<const u32x4*>(src[h] + (ok ? k : 0));
+            if (!ok) reg[h] = u32x4{0u, 0u, 0u, 0u};
+        }
+    };
+    auto store = [&](int buf) {
+#pragma unroll
+        for (int h = 0; h < NU; ++h)
+            *reinterpret_cast<u32x4*>(smem3 + buf * kF3Stage + uoff[h]) = reg[h];
+    };
+    // fragment: rows r0 + (lane % 16), k = 8 (lane / 16) .. + 7 of the staged step
+    auto frag = [&](const char* base, int mat, int r0) {
+        const int row = r0 + (lane & 15), un = lane >> 4;
+        const u32x4 v = *reinterpret_cast<const u32x4*>(base + (mat * kF3Tile + row) * kF3RowB +
+                                                        (f3_swz(row, un) << 4));
+        return __builtin_bit_cast(v8bf, v);
+    };
+    f32x4 acc[4][2];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    load(0);
+    store(0);
+    __syncthreads();
+    for (int s = 0; s < nstep; ++s) {
+        const bool more = s + 1 < nstep;
+        if (more) load(s + 1);
+        const char* base = smem3 + (s & 1) * kF3Stage;
+        v8bf af[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) af[i] = frag(base, 0, wm + 16 * i);
+#pragma unroll
+        for (int q = 1; q <= 3; ++q)
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const v8bf bf = frag(base, q, wn + 16 * j);
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bf, acc[i][j], 0,
+                                                                        0, 0);
+            }
+        if (more) store((s + 1) & 1);
+        __syncthreads();
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int col = n0 + wn + 16 * j + (lane & 15);
+            const int rb = m0 + wm + 16 * i + 4 * (lane >> 4);
+            if (col >= N) continue;
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                if (rb + e < M) F[(int64_t)(rb + e) * N + col] = acc[i][j][e];
+        }
+}
+
 // out[z][i][j] = sum_{p < nsum} sum_k A[a0 + z*azs + p*aps + i][k] * B[b0 + ...][k],
 // A bf16 or f32, B f32, rows of length K (K % 16 == 0, M and N multiples of 16).
 struct NtJob {
@@ -1006,7 +1132,8 @@ __global__ __launch_bounds__(256) void merge_permute(const int32_t* __restrict__
 // ---- host side -------------------------------------------------------------------
 struct MergeWs {
     f32x4* part;
-    float *C, *F, *S, *H, *part_s, *part_h;
+    uint16_t* Cs;      // X^T X as three bf16 parts [3][D][D]
+    float *F, *S, *H, *part_s, *part_h;
     double *Y, *Z, *Dl;
     double2* rec;
     PairOut* po;
@@ -1036,7 +1163,7 @@ static MergeWs carve_merge(void* base, int64_t L, int D, int h_q, int h_kt, int 
     const int nt = n_tiles(D), ns = n_splits(L, D);
     const size_t np = (size_t)h_kt * (h_kt - 1) / 2;
     w.part = reinterpret_cast<f32x4*>(take((size_t)ns * nt * 8 * 32 * 64 * sizeof(f32x4)));
-    w.C = reinterpret_cast<float*>(take((size_t)D * D * 4));
+    w.Cs = reinterpret_cast<uint16_t*>(take((size_t)3 * D * D * 2));
     w.F = reinterpret_cast<float*>(take((size_t)(h_q + h_kt) * d * D * 4));
     w.S = reinterpret_cast<float*>(take((size_t)h_kt * d * d * 4));
     w.H = reinterpret_cast<float*>(take((size_t)h_kt * d * h_kt * d * 4));
@@ -1125,6 +1252,7 @@ static saga_status key_merge_impl(const void* x, const void* wq, const void* wk,
     static bool lds_set = false;
     if (!lds_set) {
         if (set_lds(reinterpret_cast<const void*>(syrk_partial), kSyrkLds) != hipSuccess ||
+            set_lds(reinterpret_cast<const void*>(nt_bf16x3), kF3Lds) != hipSuccess ||
             set_lds(reinterpret_cast<const void*>(merge_pairs), pair_lds(128)) != hipSuccess)
             return SAGA_ERR_HIP;
         lds_set = true;
@@ -1142,14 +1270,17 @@ static saga_status key_merge_impl(const void* x, const void* wq, const void* wk,
     mark(0);
     const int64_t slots = (int64_t)nt * 8 * 32 * 64;
     hipLaunchKernelGGL(syrk_reduce, dim3((unsigned)((slots + 255) / 256)), dim3(256), 0, st,
-                       w.part, D, nt, ns, w.C);
+                       w.part, D, nt, ns, w.Cs);
     mark(1);
     // 2. F = [W_Q; W_K] C, then S and H
     const int g = h_q / h_kt;
     float* Fq = w.F;
     float* Fk = w.F + (int64_t)h_q * d * D;
-    launch_nt(nt_job(wq, w.C, Fq, D, D, D, h_q * d, D, D), 1, st);
-    launch_nt(nt_job(wk, w.C, Fk, D, D, D, h_kt * d, D, D), 1, st);
+    // F = [W_Q; W_K] C in one launch, bf16 MFMA on the three parts of C
+    const int mrows = (h_q + h_kt) * d;
+    hipLaunchKernelGGL(nt_bf16x3, dim3((D + kF3Tile - 1) / kF3Tile, (mrows + kF3Tile - 1) / kF3Tile),
+                       dim3(kF3Threads), kF3Lds, st, static_cast<const uint16_t*>(wq),
+                       static_cast<const uint16_t*>(wk), h_q * d, w.Cs, mrows, D, D, w.F);
     // S: one output per (query head, K split), summed per key head in a fixed order
     const int tq = ((d + 63) / 64) * ((d + 63) / 64);
     const int ks_s = k_splits(D, h_q * tq);
