@@ -31,7 +31,7 @@ constexpr size_t kTopmLdsBytes = 160 * 1024;   // LDS of a gfx950 CU: one workgr
 // the same head on its previous item (the workgroup walks consecutive chunks
 // of a row, so that is usually close), gallops away from it and bisects;
 // without a previous cutoff it bisects the whole key range. Counts are
-// per-lane vector sums reduced once per probe. Positions at or after
+// scalar popcounts of per-key lane masks. Positions at or after
 // local_from (a window the caller keeps anyway) count in the chunk statistics
 // but are left out of the ranking and of the list.
 // The keys at or above the cutoff are then written in position order: a
@@ -85,11 +85,13 @@ __device__ inline void extract(const Item<T>& it, int n, uint32_t M, uint32_t* r
         for (int e = 0; e < 16; ++e)
             if (it.c0 + 16 * lane + e >= local_from) kk[e] = 0u;
     }
+    // count over the wave of keys >= x: one compare per key into a lane mask
+    // and its scalar popcount (no per-lane sums to reduce across lanes)
     auto count_ge = [&](uint32_t x) -> uint32_t {
-        uint32_t c[4] = {0u, 0u, 0u, 0u};   // independent partial sums
+        uint32_t c = 0u;
 #pragma unroll
-        for (int e = 0; e < 16; ++e) c[e & 3] += kk[e] >= x ? 1u : 0u;
-        return wave_sum((c[0] + c[1]) + (c[2] + c[3]));
+        for (int e = 0; e < 16; ++e) c += (uint32_t)__builtin_popcountll(__ballot(kk[e] >= x));
+        return __builtin_amdgcn_readfirstlane(c);
     };
     uint32_t cut = 0;   // publish everything when the chunk holds <= M keys
     if ((uint32_t)it.n > M) {
