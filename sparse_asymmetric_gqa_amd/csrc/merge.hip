@@ -470,7 +470,8 @@ struct PairOut {
     double w_logit;   // Eq. 16
     double w_key;     // Eq. 35: tr(Delta)
     double l_avg;     // Eq. 13 at the average of the two heads: tr(Delta P) / 4
-    double sweeps;    // Jacobi sweeps run (0: the Gauss-Jordan path)
+    double sweeps;    // Jacobi sweeps run
+    double gj;        // 1: P inverted by Gauss-Jordan (Y, Z formed by pair_yz)
 };
 
 __device__ inline void pair_of_index(int p, int n, int& a, int& b) {
@@ -515,6 +516,8 @@ struct PairArgs {
     double* Y;           // [npairs][d][d]  P^+ S_a
     double* Z;           // [npairs][d][d]  P^+ S_b
     double* Dl;          // [npairs][d][d]  Delta
+    double* Pinv;        // [npairs][d][d]  P^{-1} (Gauss-Jordan path)
+    double* part;        // [npairs][2 tiles]  loss partials per (term, output tile)
     double2* rec;        // [npairs][kMaxSweeps][d - 1][d / 2]  (c, s)
     PairOut* out;        // [npairs]
     int n, d, strategy;
@@ -676,8 +679,8 @@ __device__ double gj_invert(double* Am, int d, int ld, double* fcol, double* row
 __device__ inline double ldd(const double* p) { return *p; }
 __device__ inline double ldd(const float* p) { return (double)*p; }
 
-// Workgroup GEMM over d x d row-major matrices in global memory, 64 x 64
-// output tiles: C1 = A1 B1 (and C2 = A2 B2 when DUAL). Each thread holds 4
+// Workgroup GEMM over d x d row-major matrices in global memory, one 64 x 64
+// output tile (ti, tj) per call: C1 = A1 B1 (and C2 = A2 B2 when DUAL). Each thread holds 4
 // rows x 2 columns of a tile; 16-wide k panels are double-buffered in LDS
 // (pan: 2 x (DUAL ? 4 : 2) panels of [16][68] doubles, A panels stored
 // k-major) while the next panel is loaded into registers. DUAL returns this
@@ -685,8 +688,8 @@ __device__ inline double ldd(const float* p) { return (double)*p; }
 constexpr int kPanLd = 68;
 constexpr int kPanWords = 16 * kPanLd;
 template <bool DUAL, typename TA1, typename TB1, typename TA2, typename TB2>
-__device__ double wg_gemm(int d, const TA1* A1, const TB1* B1, const TA2* A2, const TB2* B2,
-                          double* out, double* pan) {
+__device__ double tile_gemm(int d, int ti, int tj, const TA1* A1, const TB1* B1, const TA2* A2,
+                            const TB2* B2, double* out, double* pan) {
     constexpr int NP = DUAL ? 4 : 2;
     const int tid = threadIdx.x, tr = (tid >> 5) * 4, tc = (tid & 31) * 2;
     // this thread's two elements of every panel: A (row ar, k ak), B (k bk, col bc)
@@ -694,8 +697,7 @@ __device__ double wg_gemm(int d, const TA1* A1, const TB1* B1, const TA2* A2, co
     const int bk0 = tid >> 6, bc = tid & 63, bk1 = bk0 + 8;
     const int npan = d / 16;
     double dot = 0.0;
-    for (int ti = 0; ti < d; ti += 64)
-        for (int tj = 0; tj < d; tj += 64) {
+    {
             double acc1[4][2], acc2[4][2];
 #pragma unroll
             for (int r = 0; r < 4; ++r)
@@ -775,6 +777,15 @@ __device__ double wg_gemm(int d, const TA1* A1, const TB1* B1, const TA2* A2, co
                     }
                 }
         }
+    return dot;
+}
+
+template <bool DUAL, typename TA1, typename TB1, typename TA2, typename TB2>
+__device__ double wg_gemm(int d, const TA1* A1, const TB1* B1, const TA2* A2, const TB2* B2,
+                          double* out, double* pan) {
+    double dot = 0.0;
+    for (int ti = 0; ti < d; ti += 64)
+        for (int tj = 0; tj < d; tj += 64) dot += tile_gemm<DUAL>(d, ti, tj, A1, B1, A2, B2, out, pan);
     return dot;
 }
 
@@ -971,29 +982,59 @@ __global__ __launch_bounds__(kPairThreads) void merge_pairs(PairArgs pa) {
         regular = isfinite(linv) && linv > 0.0 && 1.0 / linv > cut4;
     }
     int sweeps = 0;
-    if (regular) {
+    if (regular) {   // Y = P^{-1} S_a and Z = I - Y follow, tile by tile, in pair_yz
+        double* Pi = pa.Pinv + (int64_t)pidx * d * d;
         for (int idx = tid; idx < d * d; idx += kPairThreads) {
             const int i = idx / d, j = idx - i * d;
-            Z[idx] = Am[i * ld + j];
-        }
-        __syncthreads();
-        wg_gemm<false>(d, Z, Sa, Z, Sa, Y, Am);     // Y = P^{-1} S_a
-        __syncthreads();
-        for (int idx = tid; idx < d * d; idx += kPairThreads) {
-            const int i = idx / d, j = idx - i * d;
-            Z[idx] = (i == j ? 1.0 : 0.0) - Y[idx];
+            Pi[idx] = Am[i * ld + j];
         }
     } else {
         sweeps = jacobi_pinv(Am, d, Sa, Sb, Y, Z, pa.rec + (int64_t)pidx * kMaxSweeps * (d - 1) * np,
                              cs, lam, red, flag);
     }
-    __syncthreads();
+    if (tid == 0) pa.out[pidx] = PairOut{0.0, trd, 0.25 * trdp, (double)sweeps, regular ? 1.0 : 0.0};
+}
 
-    // w = <Z Delta, S_a Z> + <Y Delta, S_b Y>
-    double dot = wg_gemm<true>(d, Z, Dl, Sa, Z, nullptr, Am);
-    dot += wg_gemm<true>(d, Y, Dl, Sb, Y, nullptr, Am);
-    dot = block_sum(dot, red + 8);
-    if (tid == 0) pa.out[pidx] = PairOut{dot, trd, 0.25 * trdp, (double)sweeps};
+// Tile-parallel stages of the pair algebra: one 64 x 64 output tile per
+// workgroup. pair_yz forms Y = P^{-1} S_a and Z = I - Y for the pairs that
+// took the Gauss-Jordan path; pair_loss evaluates the two terms of
+// w = <Z Delta, S_a Z> + <Y Delta, S_b Y> per tile into `part`, summed in a
+// fixed order by match_weights.
+__global__ __launch_bounds__(kPairThreads) void pair_yz(PairArgs pa) {
+    extern __shared__ __attribute__((aligned(16))) char smem_raw[];
+    const int pidx = blockIdx.x, d = pa.d, nt = (d + 63) / 64;
+    if (pa.strategy != 0 || pa.out[pidx].gj == 0.0) return;   // uniform
+    int a, b;
+    pair_of_index(pidx, pa.n, a, b);
+    const int ti = (blockIdx.y / nt) * 64, tj = (blockIdx.y % nt) * 64;
+    double* Y = pa.Y + (int64_t)pidx * d * d;
+    double* Z = pa.Z + (int64_t)pidx * d * d;
+    tile_gemm<false>(d, ti, tj, pa.Pinv + (int64_t)pidx * d * d, pa.S + (int64_t)a * d * d,
+                     pa.Pinv, pa.S, Y, reinterpret_cast<double*>(smem_raw));
+    __syncthreads();
+    for (int e = threadIdx.x; e < 64 * 64; e += kPairThreads) {
+        const int i = ti + (e >> 6), j = tj + (e & 63);
+        if (i < d && j < d) Z[(int64_t)i * d + j] = (i == j ? 1.0 : 0.0) - Y[(int64_t)i * d + j];
+    }
+}
+
+__global__ __launch_bounds__(kPairThreads) void pair_loss(PairArgs pa) {
+    extern __shared__ __attribute__((aligned(16))) char smem_raw[];
+    const int pidx = blockIdx.x, d = pa.d, nt = (d + 63) / 64, t2 = nt * nt;
+    if (pa.strategy != 0) return;
+    int a, b;
+    pair_of_index(pidx, pa.n, a, b);
+    const int term = blockIdx.y / t2, tile = blockIdx.y % t2;
+    const int ti = (tile / nt) * 64, tj = (tile % nt) * 64;
+    const double* Y = pa.Y + (int64_t)pidx * d * d;
+    const double* Z = pa.Z + (int64_t)pidx * d * d;
+    const double* Dl = pa.Dl + (int64_t)pidx * d * d;
+    const double* L1 = term == 0 ? Z : Y;
+    const float* Sm = pa.S + (int64_t)(term == 0 ? a : b) * d * d;
+    double* pan = reinterpret_cast<double*>(smem_raw);
+    double dot = tile_gemm<true>(d, ti, tj, L1, Dl, Sm, L1, nullptr, pan);
+    dot = block_sum(dot, pan + 8 * kPanWords);
+    if (threadIdx.x == 0) pa.part[(int64_t)pidx * 2 * t2 + blockIdx.y] = dot;
 }
 
 // ---- 4. matching ----------------------------------------------------------------
@@ -1004,9 +1045,17 @@ struct MatchWs {
     int32_t* pairs;   // [n]    matched pairs (a, b) by increasing a
 };
 
-__global__ __launch_bounds__(256) void match_weights(const PairOut* po, int n, int strategy,
-                                                     MatchWs m) {
+__global__ __launch_bounds__(256) void match_weights(PairOut* po, const double* part, int t2,
+                                                     int n, int strategy, MatchWs m) {
     const int np = n * (n - 1) / 2;
+    if (strategy == 0) {
+        for (int p = threadIdx.x; p < np; p += 256) {
+            double w = 0.0;
+            for (int y = 0; y < 2 * t2; ++y) w += part[(int64_t)p * 2 * t2 + y];
+            po[p].w_logit = w;
+        }
+        __syncthreads();
+    }
     for (int p = threadIdx.x; p < np; p += 256) {
         int a, b;
         pair_of_index(p, n, a, b);
@@ -1134,7 +1183,7 @@ struct MergeWs {
     f32x4* part;
     uint16_t* Cs;      // X^T X as three bf16 parts [3][D][D]
     float *F, *S, *H, *part_s, *part_h;
-    double *Y, *Z, *Dl;
+    double *Y, *Z, *Dl, *Pinv, *lpart;
     double2* rec;
     PairOut* po;
     MatchWs m;
@@ -1176,6 +1225,8 @@ static MergeWs carve_merge(void* base, int64_t L, int D, int h_q, int h_kt, int 
     w.Y = reinterpret_cast<double*>(take(np * d * d * 8));
     w.Z = reinterpret_cast<double*>(take(np * d * d * 8));
     w.Dl = reinterpret_cast<double*>(take(np * d * d * 8));
+    w.Pinv = reinterpret_cast<double*>(take(np * d * d * 8));
+    w.lpart = reinterpret_cast<double*>(take(np * 2 * (size_t)((d + 63) / 64) * ((d + 63) / 64) * 8));
     w.rec = reinterpret_cast<double2*>(take(np * kMaxSweeps * (d - 1) * (d / 2) * 16));
     w.po = reinterpret_cast<PairOut*>(take(np * sizeof(PairOut)));
     w.m.w = reinterpret_cast<double*>(take((size_t)h_kt * h_kt * 8));
@@ -1253,6 +1304,8 @@ static saga_status key_merge_impl(const void* x, const void* wq, const void* wk,
     if (!lds_set) {
         if (set_lds(reinterpret_cast<const void*>(syrk_partial), kSyrkLds) != hipSuccess ||
             set_lds(reinterpret_cast<const void*>(nt_bf16x3), kF3Lds) != hipSuccess ||
+            set_lds(reinterpret_cast<const void*>(pair_loss), 8 * kPanWords * 8 + 16 * 8) !=
+                hipSuccess ||
             set_lds(reinterpret_cast<const void*>(merge_pairs), pair_lds(128)) != hipSuccess)
             return SAGA_ERR_HIP;
         lds_set = true;
@@ -1307,12 +1360,17 @@ static saga_status key_merge_impl(const void* x, const void* wq, const void* wk,
     }
     mark(2);
     // 3. pairs
-    PairArgs pa{w.S, w.H, w.Y, w.Z, w.Dl, w.rec, w.po, h_kt, d, strategy};
+    PairArgs pa{w.S, w.H, w.Y, w.Z, w.Dl, w.Pinv, w.lpart, w.rec, w.po, h_kt, d, strategy};
     const int npairs = h_kt * (h_kt - 1) / 2;
+    const int t2 = ((d + 63) / 64) * ((d + 63) / 64);
     hipLaunchKernelGGL(merge_pairs, dim3(npairs), dim3(kPairThreads), pair_lds(d), st, pa);
+    hipLaunchKernelGGL(pair_yz, dim3(npairs, t2), dim3(kPairThreads), 4 * kPanWords * 8, st, pa);
+    hipLaunchKernelGGL(pair_loss, dim3(npairs, 2 * t2), dim3(kPairThreads),
+                       8 * kPanWords * 8 + 16 * 8, st, pa);
     mark(3);
     // 4. matching, 5. merged projections
-    hipLaunchKernelGGL(match_weights, dim3(1), dim3(256), 0, st, w.po, h_kt, strategy, w.m);
+    hipLaunchKernelGGL(match_weights, dim3(1), dim3(256), 0, st, w.po, w.lpart, t2, h_kt, strategy,
+                       w.m);
     if (strategy != 2) {
         const unsigned mb = (unsigned)((((int64_t)1 << h_kt) + 255) / 256);
         for (int k = 1; k <= h_kt / 2; ++k)
