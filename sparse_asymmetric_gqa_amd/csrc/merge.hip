@@ -622,56 +622,74 @@ __device__ double power_max(const double* Am, int d, int ld, double* v, double* 
 // matrix in LDS (no pivoting; every pivot is a Schur-complement diagonal).
 // Step k: A[i][j] -= A[i][k] A[k][j] / A[k][k] for every element, then row k
 // becomes A[k][j] / A[k][k], column k -A[i][k] / A[k][k] and the pivot
-// 1 / A[k][k]. Thread (ig, j) keeps elements (4 t + ig, j) in registers for
-// the whole elimination; column k and row k are broadcast through LDS, the
-// column stored so that each thread's factors are contiguous. Returns the
-// smallest pivot (<= 0 or NaN: not positive definite).
+// 1 / A[k][k]. Thread (rb, cb) keeps the 4 x 8 block at rows 4 rb, columns
+// 8 cb in registers for the whole elimination; column k and row k are
+// broadcast through LDS (each thread reads its 4 + 8 factors as vectors).
+// Returns the smallest pivot (<= 0 or NaN: not positive definite).
 __device__ double gj_invert(double* Am, int d, int ld, double* fcol, double* rowk) {
-    constexpr int R = 128 / (kPairThreads / 128);   // rows per thread (d <= 128)
-    const int tid = threadIdx.x, j = tid & 127, ig = tid >> 7;
-    const bool act = j < d;
-    double v[R];
+    const int tid = threadIdx.x, rb = tid >> 4, cb = tid & 15;
+    const int r0 = 4 * rb, c0 = 8 * cb;
+    const bool act = r0 < d && c0 < d;   // d is a multiple of 16: blocks are whole
+    double v[4][8];
 #pragma unroll
-    for (int t = 0; t < R; ++t) {
-        const int i = 4 * t + ig;
-        v[t] = act && i < d ? Am[i * ld + j] : 0.0;
-    }
-    const double* myf = fcol + ig * R;
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int c = 0; c < 8; ++c) v[r][c] = act ? Am[(r0 + r) * ld + c0 + c] : 0.0;
     double minpiv = INFINITY;
     for (int k = 0; k < d; ++k) {
-        if (act && j == k)
+        const int kc = k & 7, kr = k & 3;   // uniform
+        const bool colk = act && (k >> 3) == cb, rowkk = act && (k >> 2) == rb;
+        if (colk)
 #pragma unroll
-            for (int t = 0; t < R; ++t) fcol[ig * R + t] = v[t];
-        if (act && (k & 3) == ig) {
-            double r = 0.0;
+            for (int c = 0; c < 8; ++c)
+                if (c == kc)
 #pragma unroll
-            for (int t = 0; t < R; ++t) r = t == (k >> 2) ? v[t] : r;
-            rowk[j] = r;
-        }
+                    for (int r = 0; r < 4; ++r) fcol[r0 + r] = v[r][c];
+        if (rowkk)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                if (r == kr)
+#pragma unroll
+                    for (int c = 0; c < 8; ++c) rowk[c0 + c] = v[r][c];
         __syncthreads();
         const double pk = rowk[k];
         minpiv = fmin(minpiv, pk);
         const double piv = 1.0 / pk;
         if (act) {
-            const double rj = rowk[j] * piv;
+            double f[4], rj[8];
 #pragma unroll
-            for (int t = 0; t < R; ++t) v[t] -= myf[t] * rj;
-            if (j == k)
+            for (int r = 0; r < 4; ++r) f[r] = fcol[r0 + r];
 #pragma unroll
-                for (int t = 0; t < R; ++t) v[t] = -myf[t] * piv;
-            if ((k & 3) == ig) {
-                const double nv = j == k ? piv : rj;
+            for (int c = 0; c < 8; ++c) rj[c] = rowk[c0 + c] * piv;
 #pragma unroll
-                for (int t = 0; t < R; ++t) v[t] = t == (k >> 2) ? nv : v[t];
-            }
+            for (int r = 0; r < 4; ++r)
+#pragma unroll
+                for (int c = 0; c < 8; ++c) v[r][c] -= f[r] * rj[c];
+            if (colk)
+#pragma unroll
+                for (int c = 0; c < 8; ++c)
+                    if (c == kc)
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) v[r][c] = -f[r] * piv;
+            if (rowkk)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    if (r == kr) {
+#pragma unroll
+                        for (int c = 0; c < 8; ++c) v[r][c] = rj[c];
+                        if (colk)
+#pragma unroll
+                            for (int c = 0; c < 8; ++c)
+                                if (c == kc) v[r][c] = piv;
+                    }
         }
         __syncthreads();
     }
+    if (act)
 #pragma unroll
-    for (int t = 0; t < R; ++t) {
-        const int i = 4 * t + ig;
-        if (act && i < d) Am[i * ld + j] = v[t];
-    }
+        for (int r = 0; r < 4; ++r)
+#pragma unroll
+            for (int c = 0; c < 8; ++c) Am[(r0 + r) * ld + c0 + c] = v[r][c];
     __syncthreads();
     return minpiv;
 }
@@ -961,12 +979,11 @@ __global__ __launch_bounds__(kPairThreads) void merge_pairs(PairArgs pa) {
     }
 
     // Positive definite P with every eigenvalue well above the pseudo-inverse
-    // cutoff 2^-23 d lambda_max: P^+ = P^{-1}, by Gauss-Jordan. The smallest
-    // eigenvalue is bounded below by 1 / ||P^{-1}||_F; only when that bound
-    // does not settle it is it estimated by power iteration on P^{-1}. When P
-    // is not clearly regular, the eigen-decomposition decides which
-    // eigenvalues count as zero.
-    const double lmax_p = power_max(Am, d, ld, va, vb, red, 12);
+    // cutoff 2^-23 d lambda_max: P^+ = P^{-1}, by Gauss-Jordan. The Frobenius
+    // norms of P and P^{-1} bound the extreme eigenvalues; only when those
+    // bounds do not settle it are the eigenvalues estimated by power
+    // iteration. When P is not clearly regular, the eigen-decomposition
+    // decides which eigenvalues count as zero.
     const double minpiv = gj_invert(Am, d, ld, va, vb);
     double q2 = 0.0;
     for (int idx = tid; idx < d * d; idx += kPairThreads) {
@@ -975,15 +992,30 @@ __global__ __launch_bounds__(kPairThreads) void merge_pairs(PairArgs pa) {
         q2 += v * v;
     }
     const double pinv_f = sqrt(block_sum(q2, red));
-    const double cut4 = 4.0 * 0x1p-23 * d * lmax_p;
+    double* Pi = pa.Pinv + (int64_t)pidx * d * d;
     bool regular = minpiv > 0.0 && isfinite(pinv_f) && pinv_f > 0.0 && pf2 > 0.0;
-    if (regular && !(1.0 / pinv_f > cut4)) {
+    // lambda_min >= 1 / ||P^{-1}||_F and lambda_max <= ||P||_F: that settles it
+    // unless the conditioning is within a factor of about d of the cutoff
+    if (regular && !(1.0 / pinv_f > 4.0 * 0x1p-23 * d * sqrt(pf2))) {
+        // estimate both extreme eigenvalues: power iteration on P^{-1}, then
+        // on P reloaded from the statistics (P^{-1} waits in global memory)
         const double linv = power_max(Am, d, ld, va, vb, red, 40);   // 1 / lambda_min
-        regular = isfinite(linv) && linv > 0.0 && 1.0 / linv > cut4;
+        for (int idx = tid; idx < d * d; idx += kPairThreads) {
+            const int i = idx / d, j = idx - i * d;
+            Pi[idx] = Am[i * ld + j];
+            Am[i * ld + j] = (double)Sa[idx] + (double)Sb[idx];
+        }
+        __syncthreads();
+        const double lmax_p = power_max(Am, d, ld, va, vb, red, 40);
+        regular = isfinite(linv) && linv > 0.0 && 1.0 / linv > 4.0 * 0x1p-23 * d * lmax_p;
+        for (int idx = tid; idx < d * d; idx += kPairThreads) {
+            const int i = idx / d, j = idx - i * d;
+            Am[i * ld + j] = Pi[idx];
+        }
+        __syncthreads();
     }
     int sweeps = 0;
     if (regular) {   // Y = P^{-1} S_a and Z = I - Y follow, tile by tile, in pair_yz
-        double* Pi = pa.Pinv + (int64_t)pidx * d * d;
         for (int idx = tid; idx < d * d; idx += kPairThreads) {
             const int i = idx / d, j = idx - i * d;
             Pi[idx] = Am[i * ld + j];
