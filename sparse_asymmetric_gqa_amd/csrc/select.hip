@@ -685,6 +685,11 @@ __global__ __launch_bounds__(kUnionThreads, 4) void select_union(
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int b = row / h_q;
+    // this thread's chunk record for a full-length row, requested together with
+    // the length (the usual case needs no second round trip)
+    const int tpc_full = nchunk <= NT ? NT / nchunk : 1;
+    const int c_full = tid / tpc_full < nchunk ? tid / tpc_full : nchunk - 1;
+    const uint4 m_full = cand_meta[(int64_t)row * nchunk + c_full];
     const int64_t Lrow = clamp_len(lens[b], S_max);
     // ranked positions [0, L) and the count kept from them (SparQ: the window is not ranked)
     const int local = sq_local(sq);
@@ -759,7 +764,7 @@ __global__ __launch_bounds__(kUnionThreads, 4) void select_union(
         const int c = tid / tpc;
         const int sub = tid - c * tpc;
         const bool cv = c < nch;
-        const uint4 m = cand_meta[(int64_t)row * nchunk + (cv ? c : nch - 1)];
+        const uint4 m = nch == nchunk ? m_full : cand_meta[(int64_t)row * nchunk + (cv ? c : nch - 1)];
         const uint32_t cnt = cv ? m.y : 0u;
         const uint32_t P = (((cnt + (uint32_t)tpc - 1u) / (uint32_t)tpc) + 1u) & ~1u;
         const uint32_t j0 = (uint32_t)sub * P;
@@ -880,6 +885,9 @@ __global__ __launch_bounds__(kUnionThreads, 4) void select_union(
         const uint32_t krem = (uint32_t)n_eff - (tot & 0xFFFFu);
         uint32_t eq_seen = before >> 16;
         uint32_t slot = (before & 0xFFFFu) + (eq_seen < krem ? eq_seen : krem);
+        // fused gather: the staged value is already the softmax weight
+        // exp(logit - row max), and the slots past N_eff are cleared here
+        const float mrow = key_float(kmax);
     #pragma unroll
         for (int s = 0; s < KPT; ++s) {
             const bool eq = key[s] == Tk;
@@ -887,10 +895,19 @@ __global__ __launch_bounds__(kUnionThreads, 4) void select_union(
             eq_seen += eq ? 1u : 0u;
             if (keep) {   // slot < N_eff by construction
                 st_idx[slot] = pos[s];
-                st_val[slot] = key_float(key[s]);
+                if constexpr (FUSE) {
+                    st_val[slot] = __expf(key_float(key[s]) - mrow);
+                } else {
+                    st_val[slot] = key_float(key[s]);
+                }
             }
             slot += keep ? 1u : 0u;
         }
+        if constexpr (FUSE)
+            for (int j = n_eff + tid; j < nst; j += NT) {
+                st_idx[j] = 0;
+                st_val[j] = 0.f;
+            }
         __syncthreads();
         if (tid == 0) {
             row_max[row] = key_float(kmax);
@@ -902,16 +919,10 @@ __global__ __launch_bounds__(kUnionThreads, 4) void select_union(
             // and weights up to nst (weight 0, row 0 past n_eff)
             if (ou)
                 for (int j = tid; j < N; j += NT) ou[j] = j < n_eff ? st_idx[j] : -1;
-            const float mrow = key_float(kmax);
+            // the weights summed slot by slot (the order the unfused value
+            // gather uses, so both give the same bits)
             float lsum = 0.f;
-            for (int j = tid; j < nst; j += NT) {
-                const bool kept = j < n_eff;
-                const float w = kept ? __expf(st_val[j] - mrow) : 0.f;
-                if (!kept) st_idx[j] = 0;
-                st_val[j] = w;
-                lsum += w;
-            }
-            __syncthreads();
+            for (int j = tid; j < nst; j += NT) lsum += st_val[j];
             float acc[G::EPL];
     #pragma unroll
             for (int c = 0; c < G::EPL; ++c) acc[c] = 0.f;
