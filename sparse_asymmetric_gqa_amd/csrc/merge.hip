@@ -30,6 +30,8 @@
 
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace saga {
 namespace {
 using namespace dev;
@@ -37,15 +39,16 @@ using namespace dev;
 typedef short v4s __attribute__((ext_vector_type(4)));
 typedef short v8s __attribute__((ext_vector_type(8)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) v4s lds_v4s;
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 // ---- sizes -----------------------------------------------------------------
 constexpr int kSyrkThreads = 512;    // 8 waves: 2 (rows) x 4 (columns) of 128 x 64
 constexpr int kBlk = 256;            // C tile edge (features)
-constexpr int kStageTok = 64;        // tokens per LDS stage
+constexpr int kStageTok = 32;        // tokens per LDS stage
 constexpr int kRowBytes = kBlk * 2;  // one token's 256 features in bf16
-constexpr int kSyrkLds = 2 * 2 * kStageTok * kRowBytes;   // 2 stages x 2 operands
+constexpr int kStageBytes = kStageTok * kRowBytes;         // one operand of one stage
 constexpr int kTargetCus = 256;      // MI355X compute units: splits fill one wave of them
 constexpr int kNtThreads = 256;
 constexpr int kPairThreads = 512;
@@ -75,17 +78,25 @@ __device__ inline int xcd_logical(int hw, int total) {
 }
 
 // ---- 1. C = X^T X ------------------------------------------------------------
+// On gfx950 the 32x32x16 bf16 MFMA does twice the work of the 16x16x32 one in
+// the same issue time (measured: 2.4 against 1.3 PFLOP/s on independent
+// chains), so the Gram tiles are built from 32 x 32 blocks.
+//
 // XOR swizzle of the 16-byte units of a staged token row: the transposing
-// reads of a 16-lane group cover 4 consecutive rows x 32 bytes, and the two
-// groups served together differ in row bit 3; both land on distinct banks.
-__device__ inline int unit_swz(int row) { return 2 * (row & 3) + 8 * ((row >> 3) & 1); }
+// reads of the two 16-lane groups served together cover the same 4
+// consecutive rows x 64 bytes (two adjacent 16-feature blocks); rotating the
+// units by 4 per row puts the 16 row-unit pairs on distinct banks.
+__device__ inline int unit_swz(int row) { return 4 * (row & 3); }
 
-// 8 consecutive tokens (rows kbase .. kbase + 7) of features 16 nb + (lane % 16):
-// the operand of one 16x16x32 MFMA (A and B use the same token order).
-__device__ inline v8bf syrk_frag(const char* buf, int kbase, int nb, int lane) {
+// The operand of one 32x32x16 MFMA: lane l holds features 32 nb + (l % 32) of
+// the 8 consecutive tokens (rows) kbase + 8 (l / 32) .. + 7 (A and B use the
+// same token order, so the product is X^T X whatever the order within k).
+// Each 16-lane group reads 4 rows x 16 features per transposing read: group
+// G takes feature block 2 nb + (G & 1) and token half G >> 1.
+__device__ inline v8bf syrk_frag(const char* buf, int kbase, int nb32, int lane) {
     const int G = lane >> 4, i = lane & 15, a = i & 3, j = i >> 2;
-    const int unit = 2 * nb + (a >> 1);
-    const int r0 = kbase + 8 * G + j, r1 = r0 + 4;
+    const int unit = 2 * (2 * nb32 + (G & 1)) + (a >> 1);
+    const int r0 = kbase + 8 * (G >> 1) + j, r1 = r0 + 4;
     const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
         (lds_v4s*)(buf + r0 * kRowBytes + ((unit ^ unit_swz(r0)) << 4) + 8 * (a & 1)));
     const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
@@ -103,13 +114,51 @@ __device__ inline void tile_of(int t, int nb, int& bi, int& bj) {
     bj = bi + t;
 }
 
+// Stage buffers of the Gram tiles: 4 stages x 2 operands of [32 tokens][256
+// features] bf16, each its own LDS object so that the compiler can tell the
+// direct-to-LDS loads of one stage from the fragment reads of another.
+__shared__ __attribute__((aligned(16))) char sy0a[kStageBytes], sy0b[kStageBytes],
+    sy1a[kStageBytes], sy1b[kStageBytes], sy2a[kStageBytes], sy2b[kStageBytes],
+    sy3a[kStageBytes], sy3b[kStageBytes];
+template <int P>
+__device__ inline char* sy_buf(int op) {
+    if constexpr (P == 0) return op ? sy0b : sy0a;
+    if constexpr (P == 1) return op ? sy1b : sy1a;
+    if constexpr (P == 2) return op ? sy2b : sy2a;
+    return op ? sy3b : sy3a;
+}
+
+// Wait until at most n (0, 2, 4 or 8) of this wave's vector-memory operations
+// are outstanding, finish its LDS operations, then meet the workgroup. The
+// wait counts follow the load pipeline below; a plain __syncthreads would
+// wait for every load in flight.
+__device__ inline void sy_sync(int n) {
+    if (n >= 8)
+        asm volatile("s_waitcnt vmcnt(8)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    else if (n >= 4)
+        asm volatile("s_waitcnt vmcnt(4)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    else if (n >= 2)
+        asm volatile("s_waitcnt vmcnt(2)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    else
+        asm volatile("s_waitcnt vmcnt(0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 // One workgroup: tile (bi <= bj) of C over the tokens of one split. The 8
-// waves hold 128 x 64 of the 256 x 256 tile each. Partials are written in
-// MFMA fragment order: [split][tile][wave][8 x 4 blocks][64 lanes] x f32x4.
+// waves hold 128 x 64 of the 256 x 256 tile each, as 4 x 2 blocks of 32 x 32.
+// Token stages of 32 rows stream into four LDS stage buffers with
+// direct-to-LDS loads issued three stages ahead, so about 96 KB per CU are in
+// flight from the MALL or HBM while the MFMAs work on the current stage. A
+// stage with tokens past the split or features past D (only the last stage
+// of a split, or every stage of a tile at a ragged edge) is loaded through
+// registers instead, with the missing values set to zero, one stage ahead.
+// A diagonal tile stages its rows once per operand as well, so that every
+// fragment read names a single stage buffer (a read through a pointer that
+// may name either would make the compiler wait for every load in flight).
+// Partials are written in MFMA fragment order:
+// [split][tile][wave][4 x 2 blocks][4 quarters][64 lanes] x f32x4.
 __global__ __launch_bounds__(kSyrkThreads, 1) void syrk_partial(
         const uint16_t* __restrict__ x, int64_t L, int D, int ntile, int nsplit,
         int64_t slen, int grid_total, f32x4* __restrict__ part) {
-    extern __shared__ __attribute__((aligned(16))) char smem[];
     const int total = ntile * nsplit;
     const int logical = xcd_logical(blockIdx.x, grid_total);
     if (logical >= total) return;
@@ -117,40 +166,60 @@ __global__ __launch_bounds__(kSyrkThreads, 1) void syrk_partial(
     const int nb = n_blocks(D);
     int bi, bj;
     tile_of(tile, nb, bi, bj);
-    const bool diag = bi == bj;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave & 1, wn = wave >> 1;
     const int64_t t_beg = (int64_t)split * slen;
     int64_t t_end = t_beg + slen;
     if (t_end > L) t_end = L;
-    const int nstage = t_end > t_beg ? (int)((t_end - t_beg + kStageTok - 1) / kStageTok) : 0;
-
-    // loader: unit u = tid + 512 h of a stage, row u / 32, 16-byte unit u % 32
-    constexpr int kUnits = kStageTok * 32 / kSyrkThreads;   // per operand per thread
+    const int64_t ntok = t_end > t_beg ? t_end - t_beg : 0;
+    const int nstage = (int)((ntok + kStageTok - 1) / kStageTok);
+    // stages [0, nfull) are whole and take the direct path
+    const bool cols_whole = (bi + 1) * kBlk <= D && (bj + 1) * kBlk <= D;
+    const int nfull = cols_whole ? (int)(ntok / kStageTok) : 0;
+    constexpr int per_stage = 4;      // direct loads per wave per stage
     const uint16_t* src[2] = {x + (int64_t)bi * kBlk, x + (int64_t)bj * kBlk};
-    u32x4 reg[2][kUnits];
-    auto load_stage = [&](int s) {
+
+    // direct loads: wave w moves row pairs 2 w and 2 w + 1 of each operand;
+    // lane l fills 16-byte slot l % 32 of row 2 pr + l / 32, which holds the
+    // row's unit (slot ^ unit_swz(row))
+    auto issue = [&](int s, auto P) {
+        constexpr int p = decltype(P)::value;
 #pragma unroll
         for (int op = 0; op < 2; ++op) {
-            if (op == 1 && diag) break;
+            char* base = sy_buf<p>(op);
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int pr = 2 * wave + h, row = 2 * pr + (lane >> 5);
+                const int un = (lane & 31) ^ unit_swz(row);
+                const uint16_t* g = src[op] + (t_beg + (int64_t)s * kStageTok + row) * D + un * 8;
+                __builtin_amdgcn_global_load_lds(
+                    (__attribute__((address_space(1))) void*)g,
+                    (__attribute__((address_space(3))) void*)(base + pr * 1024), 16, 0, 0);
+            }
+        }
+    };
+    // register path: unit u = tid + 512 h of a stage, row u / 32, unit u % 32
+    auto copy_stage = [&](int s, auto P) {
+        constexpr int p = decltype(P)::value;
+        constexpr int kUnits = kStageTok * 32 / kSyrkThreads;
+        u32x4 reg[2][kUnits];
+#pragma unroll
+        for (int op = 0; op < 2; ++op) {
 #pragma unroll
             for (int h = 0; h < kUnits; ++h) {
                 const int u = tid + kSyrkThreads * h, row = u >> 5, un = u & 31;
                 const int64_t tok = t_beg + (int64_t)s * kStageTok + row;
                 const int col = (op ? bj : bi) * kBlk + un * 8;
                 const bool ok = tok < t_end && col < D;
-                const uint16_t* p = ok ? src[op] + tok * D + un * 8 : x;
-                reg[op][h] = *reinterpret_cast<const u32x4*>(p);
+                const uint16_t* g = ok ? src[op] + tok * D + un * 8 : x;
+                reg[op][h] = *reinterpret_cast<const u32x4*>(g);
                 if (!ok) reg[op][h] = u32x4{0u, 0u, 0u, 0u};
             }
         }
-    };
-    auto store_stage = [&](int buf) {
 #pragma unroll
         for (int op = 0; op < 2; ++op) {
-            if (op == 1 && diag) break;
-            char* base = smem + (buf * 2 + op) * (kStageTok * kRowBytes);
+            char* base = sy_buf<p>(op);
 #pragma unroll
             for (int h = 0; h < kUnits; ++h) {
                 const int u = tid + kSyrkThreads * h, row = u >> 5, un = u & 31;
@@ -159,45 +228,71 @@ __global__ __launch_bounds__(kSyrkThreads, 1) void syrk_partial(
             }
         }
     };
+    // direct loads of this wave issued after stage t's: those of stages t + 1
+    // and t + 2 that exist
+    auto after = [&](int t) {
+        int n = nfull - (t + 1);
+        n = n < 0 ? 0 : n > 2 ? 2 : n;
+        return n * per_stage;
+    };
 
-    f32x4 acc[8][4];
+    f32x16 acc[4][2];
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
-    if (nstage > 0) {
-        load_stage(0);
-        store_stage(0);
-    }
-    __syncthreads();
-    for (int s = 0; s < nstage; ++s) {
-        const bool more = s + 1 < nstage;
-        if (more) load_stage(s + 1);
-        const char* abuf = smem + ((s & 1) * 2) * (kStageTok * kRowBytes);
-        const char* bbuf = diag ? abuf : abuf + kStageTok * kRowBytes;
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    using I2 = std::integral_constant<int, 2>;
+    using I3 = std::integral_constant<int, 3>;
+    if (0 < nfull) issue(0, I0{});
+    if (1 < nfull) issue(1, I1{});
+    if (2 < nfull) issue(2, I2{});
+    if (nstage > 0 && nfull == 0) copy_stage(0, I0{});
+    sy_sync(after(0));
+
+    auto step = [&](int s, auto P) {
+        constexpr int p = decltype(P)::value;
+        if (s + 3 < nfull) issue(s + 3, std::integral_constant<int, (p + 3) & 3>{});
+        const char* abuf = sy_buf<p>(0);
+        const char* bbuf = sy_buf<p>(1);
 #pragma unroll
-        for (int kk = 0; kk < kStageTok / 32; ++kk) {
-            v8bf bf[4];
+        for (int kk = 0; kk < kStageTok / 16; ++kk) {
+            v8bf bf[2];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) bf[j] = syrk_frag(bbuf, 32 * kk, wn * 4 + j, lane);
+            for (int j = 0; j < 2; ++j) bf[j] = syrk_frag(bbuf, 16 * kk, wn * 2 + j, lane);
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const v8bf af = syrk_frag(abuf, 32 * kk, wm * 8 + i, lane);
+            for (int i = 0; i < 4; ++i) {
+                const v8bf af = syrk_frag(abuf, 16 * kk, wm * 4 + i, lane);
 #pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bf[j], acc[i][j], 0,
+                for (int j = 0; j < 2; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bf[j], acc[i][j], 0,
                                                                         0, 0);
             }
         }
-        if (more) store_stage((s + 1) & 1);
-        __syncthreads();
+        if (s + 1 < nstage && s + 1 >= nfull)
+            copy_stage(s + 1, std::integral_constant<int, (p + 1) & 3>{});
+        sy_sync(after(s + 1));
+    };
+    for (int s = 0; s < nstage; s += 4) {
+        step(s, I0{});
+        if (s + 1 < nstage) step(s + 1, I1{});
+        if (s + 2 < nstage) step(s + 2, I2{});
+        if (s + 3 < nstage) step(s + 3, I3{});
     }
     f32x4* out = part + (((int64_t)split * ntile + tile) * 8 + wave) * 32 * 64;
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) out[(i * 4 + j) * 64 + lane] = acc[i][j];
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                out[((i * 2 + j) * 4 + q) * 64 + lane] =
+                    f32x4{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
+                          acc[i][j][4 * q + 3]};
 }
 
 // bf16 nearest-even of an fp32 value, as bits and as the value it stands for
@@ -219,13 +314,15 @@ __global__ __launch_bounds__(256) void syrk_reduce(const f32x4* __restrict__ par
     if (idx >= slots) return;
     f32x4 s = part[idx];
     for (int k = 1; k < nsplit; ++k) s += part[idx + k * slots];
-    const int lane = (int)(idx & 63), blk = (int)((idx >> 6) & 31);
+    // 32 x 32 accumulator layout: quarter q of lane l holds rows
+    // 8 q + 4 (l / 32) .. + 3 of column l % 32
+    const int lane = (int)(idx & 63), q = (int)((idx >> 6) & 3), blk = (int)((idx >> 8) & 7);
     const int wave = (int)((idx >> 11) & 7), tile = (int)(idx >> 14);
     int bi, bj;
     tile_of(tile, n_blocks(D), bi, bj);
-    const int i = blk >> 2, j = blk & 3;
-    const int row0 = bi * kBlk + (wave & 1) * 128 + 16 * i + 4 * (lane >> 4);
-    const int col = bj * kBlk + (wave >> 1) * 64 + 16 * j + (lane & 15);
+    const int i = blk >> 1, j = blk & 1;
+    const int row0 = bi * kBlk + (wave & 1) * 128 + 32 * i + 8 * q + 4 * (lane >> 5);
+    const int col = bj * kBlk + (wave >> 1) * 64 + 32 * j + (lane & 31);
     if (col >= D) return;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -625,6 +722,10 @@ __device__ double power_max(const double* Am, int d, int ld, double* v, double* 
 // 1 / A[k][k]. Thread (rb, cb) keeps the 4 x 8 block at rows 4 rb, columns
 // 8 cb in registers for the whole elimination; column k and row k are
 // broadcast through LDS (each thread reads its 4 + 8 factors as vectors).
+// The broadcast buffers alternate between two halves of fcol and rowk
+// ([2][d] each), so one barrier per step suffices: a thread writes step
+// k + 2's half only after the barrier of step k + 1, which every thread
+// passes after its reads of step k.
 // Returns the smallest pivot (<= 0 or NaN: not positive definite).
 __device__ double gj_invert(double* Am, int d, int ld, double* fcol, double* rowk) {
     const int tid = threadIdx.x, rb = tid >> 4, cb = tid & 15;
@@ -638,29 +739,35 @@ __device__ double gj_invert(double* Am, int d, int ld, double* fcol, double* row
     double minpiv = INFINITY;
     for (int k = 0; k < d; ++k) {
         const int kc = k & 7, kr = k & 3;   // uniform
+        double* fc = fcol + (k & 1) * d;
+        double* rk = rowk + (k & 1) * d;
         const bool colk = act && (k >> 3) == cb, rowkk = act && (k >> 2) == rb;
         if (colk)
 #pragma unroll
             for (int c = 0; c < 8; ++c)
                 if (c == kc)
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) fcol[r0 + r] = v[r][c];
+                    for (int r = 0; r < 4; ++r) fc[r0 + r] = v[r][c];
         if (rowkk)
 #pragma unroll
             for (int r = 0; r < 4; ++r)
                 if (r == kr)
 #pragma unroll
-                    for (int c = 0; c < 8; ++c) rowk[c0 + c] = v[r][c];
+                    for (int c = 0; c < 8; ++c) rk[c0 + c] = v[r][c];
         __syncthreads();
-        const double pk = rowk[k];
+        double f[4], rj[8];
+        if (act) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) f[r] = fc[r0 + r];
+#pragma unroll
+            for (int c = 0; c < 8; ++c) rj[c] = rk[c0 + c];
+        }
+        const double pk = rk[k];
         minpiv = fmin(minpiv, pk);
         const double piv = 1.0 / pk;
         if (act) {
-            double f[4], rj[8];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) f[r] = fcol[r0 + r];
-#pragma unroll
-            for (int c = 0; c < 8; ++c) rj[c] = rowk[c0 + c] * piv;
+            for (int c = 0; c < 8; ++c) rj[c] *= piv;
 #pragma unroll
             for (int r = 0; r < 4; ++r)
 #pragma unroll
@@ -683,7 +790,6 @@ __device__ double gj_invert(double* Am, int d, int ld, double* fcol, double* row
                                 if (c == kc) v[r][c] = piv;
                     }
         }
-        __syncthreads();
     }
     if (act)
 #pragma unroll
@@ -795,15 +901,6 @@ __device__ double tile_gemm(int d, int ti, int tj, const TA1* A1, const TB1* B1,
                     }
                 }
         }
-    return dot;
-}
-
-template <bool DUAL, typename TA1, typename TB1, typename TA2, typename TB2>
-__device__ double wg_gemm(int d, const TA1* A1, const TB1* B1, const TA2* A2, const TB2* B2,
-                          double* out, double* pan) {
-    double dot = 0.0;
-    for (int ti = 0; ti < d; ti += 64)
-        for (int tj = 0; tj < d; tj += 64) dot += tile_gemm<DUAL>(d, ti, tj, A1, B1, A2, B2, out, pan);
     return dot;
 }
 
@@ -942,9 +1039,9 @@ __global__ __launch_bounds__(kPairThreads) void merge_pairs(PairArgs pa) {
     double* Am = reinterpret_cast<double*>(smem_raw);   // [d][d + 1], later GEMM panels
     double2* cs = reinterpret_cast<double2*>(Am + pair_matrix_words(d));   // [2][64]
     double* lam = reinterpret_cast<double*>(cs + 128);       // [d]
-    double* va = lam + 128;                                   // [d] power-iteration vector,
-    double* vb = va + 128;                                    // [d] Gauss-Jordan buffers
-    double* red = vb + 128;                                   // [16]
+    double* va = lam + 128;                                   // [2][128] power-iteration
+    double* vb = va + 256;                                    // vectors, Gauss-Jordan buffers
+    double* red = vb + 256;                                   // [16]
     int* flag = reinterpret_cast<int*>(red + 16);
     const int hd = pa.n * d;
     const float* Sa = pa.S + (int64_t)a * d * d;
@@ -1270,7 +1367,7 @@ static MergeWs carve_merge(void* base, int64_t L, int D, int h_q, int h_kt, int 
 }
 
 static size_t pair_lds(int d) {
-    return (size_t)pair_matrix_words(d) * 8 + 128 * 16 + 3 * 128 * 8 + 16 * 8 + 16;
+    return (size_t)pair_matrix_words(d) * 8 + 128 * 16 + 5 * 128 * 8 + 16 * 8 + 16;
 }
 
 static bool merge_shape_ok(int64_t L, int D, int h_q, int h_kt, int d) {
@@ -1334,8 +1431,7 @@ static saga_status key_merge_impl(const void* x, const void* wq, const void* wk,
     MergeWs w = carve_merge(workspace, L, D, h_q, h_kt, d);
     static bool lds_set = false;
     if (!lds_set) {
-        if (set_lds(reinterpret_cast<const void*>(syrk_partial), kSyrkLds) != hipSuccess ||
-            set_lds(reinterpret_cast<const void*>(nt_bf16x3), kF3Lds) != hipSuccess ||
+        if (set_lds(reinterpret_cast<const void*>(nt_bf16x3), kF3Lds) != hipSuccess ||
             set_lds(reinterpret_cast<const void*>(pair_loss), 8 * kPanWords * 8 + 16 * 8) !=
                 hipSuccess ||
             set_lds(reinterpret_cast<const void*>(merge_pairs), pair_lds(128)) != hipSuccess)
@@ -1349,7 +1445,7 @@ static saga_status key_merge_impl(const void* x, const void* wq, const void* wk,
     // 1. C = X^T X
     const int nt = n_tiles(D), ns = n_splits(L, D);
     const int total = nt * ns, grid = (int)round_up(total, 8);
-    hipLaunchKernelGGL(syrk_partial, dim3(grid), dim3(kSyrkThreads), kSyrkLds, st,
+    hipLaunchKernelGGL(syrk_partial, dim3(grid), dim3(kSyrkThreads), 0, st,
                        static_cast<const uint16_t*>(x), L, D, nt, ns, split_len(L, ns), grid,
                        w.part);
     mark(0);

@@ -113,6 +113,10 @@ CASES = [
     MergeCase("ragged_llama_like", 777, 400, 16, 8, 64, seed=42),    # L % 64, D % 256 ragged
     MergeCase("qwen_like_d128", 333, 512, 12, 2, 128, seed=46),
     MergeCase("d32_six_heads", 1000, 272, 12, 6, 32, seed=43),
+    # splits of several 32-token stages (the load pipeline runs three stages
+    # ahead), a last split with a partial stage, empty splits, and a ragged
+    # feature block
+    MergeCase("deep_ragged", 20001, 400, 8, 4, 64, seed=47),
 ]
 
 
