@@ -716,16 +716,19 @@ __device__ double power_max(const double* Am, int d, int ld, double* v, double* 
 }
 
 // In-place Gauss-Jordan inversion of the symmetric positive definite d x d
-// matrix in LDS (no pivoting; every pivot is a Schur-complement diagonal).
-// Step k: A[i][j] -= A[i][k] A[k][j] / A[k][k] for every element, then row k
-// becomes A[k][j] / A[k][k], column k -A[i][k] / A[k][k] and the pivot
-// 1 / A[k][k]. Thread (rb, cb) keeps the 4 x 8 block at rows 4 rb, columns
-// 8 cb in registers for the whole elimination; column k and row k are
-// broadcast through LDS (each thread reads its 4 + 8 factors as vectors).
-// The broadcast buffers alternate between two halves of fcol and rowk
-// ([2][d] each), so one barrier per step suffices: a thread writes step
-// k + 2's half only after the barrier of step k + 1, which every thread
-// passes after its reads of step k.
+// matrix in LDS (no pivoting), eliminating 4 x 4 pivot blocks K:
+//   A_KK <- A_KK^{-1} =: Pi,            A_KJ <- Pi A_KJ,
+//   A_IJ <- A_IJ - A_IK Pi A_KJ,        A_IK <- -A_IK Pi      (I, J outside K),
+// which is four scalar steps at once (A[i][j] -= A[i][k] A[k][j] / A[k][k],
+// row k scaled by 1 / A[k][k], column k by -1 / A[k][k], pivot inverted) and
+// meets the same pivots, the Schur-complement diagonals. Every thread
+// inverts the 4 x 4 block itself by those scalar steps. Thread (rb, cb)
+// keeps the 4 x 8 block at rows 4 rb, columns 8 cb in registers for the
+// whole elimination; the column block [d][4] and the row block [4][d] of K
+// are broadcast through LDS, alternating between two halves of fcol and rowk
+// ([2][4 d] each) so that one barrier per block step suffices: a thread
+// writes step t + 2's half only after the barrier of step t + 1, which every
+// thread passes after its reads of step t.
 // Returns the smallest pivot (<= 0 or NaN: not positive definite).
 __device__ double gj_invert(double* Am, int d, int ld, double* fcol, double* rowk) {
     const int tid = threadIdx.x, rb = tid >> 4, cb = tid & 15;
@@ -737,58 +740,117 @@ __device__ double gj_invert(double* Am, int d, int ld, double* fcol, double* row
 #pragma unroll
         for (int c = 0; c < 8; ++c) v[r][c] = act ? Am[(r0 + r) * ld + c0 + c] : 0.0;
     double minpiv = INFINITY;
-    for (int k = 0; k < d; ++k) {
-        const int kc = k & 7, kr = k & 3;   // uniform
-        double* fc = fcol + (k & 1) * d;
-        double* rk = rowk + (k & 1) * d;
-        const bool colk = act && (k >> 3) == cb, rowkk = act && (k >> 2) == rb;
-        if (colk)
-#pragma unroll
-            for (int c = 0; c < 8; ++c)
-                if (c == kc)
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) fc[r0 + r] = v[r][c];
-        if (rowkk)
+    for (int kb = 0; kb < d / 4; ++kb) {
+        const int k0 = 4 * kb;
+        const bool hi = kb & 1;   // uniform: K is columns 4 .. 7 of its thread column
+        double* fc = fcol + (kb & 1) * 4 * d;   // [d][4]
+        double* rk = rowk + (kb & 1) * 4 * d;   // [4][d]
+        const bool colk = act && (kb >> 1) == cb, rowkk = act && kb == rb;
+        // (the halves of v are named by constant indices in separate branches:
+        // an index chosen at run time would put v in scratch memory)
+        if (colk && hi) {
 #pragma unroll
             for (int r = 0; r < 4; ++r)
-                if (r == kr)
 #pragma unroll
-                    for (int c = 0; c < 8; ++c) rk[c0 + c] = v[r][c];
-        __syncthreads();
-        double f[4], rj[8];
-        if (act) {
+                for (int m = 0; m < 4; ++m) fc[(r0 + r) * 4 + m] = v[r][4 + m];
+        } else if (colk) {
 #pragma unroll
-            for (int r = 0; r < 4; ++r) f[r] = fc[r0 + r];
+            for (int r = 0; r < 4; ++r)
 #pragma unroll
-            for (int c = 0; c < 8; ++c) rj[c] = rk[c0 + c];
+                for (int m = 0; m < 4; ++m) fc[(r0 + r) * 4 + m] = v[r][m];
         }
-        const double pk = rk[k];
-        minpiv = fmin(minpiv, pk);
-        const double piv = 1.0 / pk;
-        if (act) {
+        if (rowkk) {
 #pragma unroll
-            for (int c = 0; c < 8; ++c) rj[c] *= piv;
+            for (int m = 0; m < 4; ++m)
+#pragma unroll
+                for (int c = 0; c < 8; ++c) rk[m * d + c0 + c] = v[m][c];
+        }
+        __syncthreads();
+        double f[4][4];
+        if (act) {
 #pragma unroll
             for (int r = 0; r < 4; ++r)
 #pragma unroll
-                for (int c = 0; c < 8; ++c) v[r][c] -= f[r] * rj[c];
-            if (colk)
+                for (int m = 0; m < 4; ++m) f[r][m] = fc[(r0 + r) * 4 + m];
+        }
+        // Pi = A_KK^{-1} by four scalar Gauss-Jordan steps
+        double pi[4][4];
 #pragma unroll
-                for (int c = 0; c < 8; ++c)
-                    if (c == kc)
+        for (int m = 0; m < 4; ++m)
 #pragma unroll
-                        for (int r = 0; r < 4; ++r) v[r][c] = -f[r] * piv;
-            if (rowkk)
+            for (int n = 0; n < 4; ++n) pi[m][n] = rk[m * d + k0 + n];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const double pk = pi[q][q];
+            minpiv = fmin(minpiv, pk);
+            const double ip = 1.0 / pk;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                if (i == q) continue;
+                const double fi = pi[i][q] * ip;
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    if (j != q) pi[i][j] -= fi * pi[q][j];
+                pi[i][q] = -fi;
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                if (j != q) pi[q][j] *= ip;
+            pi[q][q] = ip;
+        }
+        if (act) {
+            // by halves of the thread's 8 columns: rj <- Pi A_KJ, then
+            // A_IJ -= A_IK (Pi A_KJ); rows of K take Pi A_KJ
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                double rj[4][4];
+#pragma unroll
+                for (int m = 0; m < 4; ++m)
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) rj[m][c] = rk[m * d + c0 + 4 * h + c];
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    double t[4];
+#pragma unroll
+                    for (int m = 0; m < 4; ++m)
+                        t[m] = pi[m][0] * rj[0][c] + pi[m][1] * rj[1][c] + pi[m][2] * rj[2][c] +
+                               pi[m][3] * rj[3][c];
+#pragma unroll
+                    for (int m = 0; m < 4; ++m) rj[m][c] = t[m];
+                }
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
-                    if (r == kr) {
 #pragma unroll
-                        for (int c = 0; c < 8; ++c) v[r][c] = rj[c];
-                        if (colk)
+                    for (int c = 0; c < 4; ++c)
+                        v[r][4 * h + c] -= f[r][0] * rj[0][c] + f[r][1] * rj[1][c] +
+                                           f[r][2] * rj[2][c] + f[r][3] * rj[3][c];
+                if (rowkk)
 #pragma unroll
-                            for (int c = 0; c < 8; ++c)
-                                if (c == kc) v[r][c] = piv;
-                    }
+                    for (int m = 0; m < 4; ++m)
+#pragma unroll
+                        for (int c = 0; c < 4; ++c) v[m][4 * h + c] = rj[m][c];
+            }
+            if (colk) {   // A_IK <- -A_IK Pi, and A_KK <- Pi in the rows of K
+                double e[4][4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+#pragma unroll
+                    for (int m = 0; m < 4; ++m)
+                        e[r][m] = rowkk ? pi[r][m]
+                                        : -(f[r][0] * pi[0][m] + f[r][1] * pi[1][m] +
+                                            f[r][2] * pi[2][m] + f[r][3] * pi[3][m]);
+                if (hi) {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+#pragma unroll
+                        for (int m = 0; m < 4; ++m) v[r][4 + m] = e[r][m];
+                } else {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+#pragma unroll
+                        for (int m = 0; m < 4; ++m) v[r][m] = e[r][m];
+                }
+            }
         }
     }
     if (act)
@@ -1039,9 +1101,9 @@ __global__ __launch_bounds__(kPairThreads) void merge_pairs(PairArgs pa) {
     double* Am = reinterpret_cast<double*>(smem_raw);   // [d][d + 1], later GEMM panels
     double2* cs = reinterpret_cast<double2*>(Am + pair_matrix_words(d));   // [2][64]
     double* lam = reinterpret_cast<double*>(cs + 128);       // [d]
-    double* va = lam + 128;                                   // [2][128] power-iteration
-    double* vb = va + 256;                                    // vectors, Gauss-Jordan buffers
-    double* red = vb + 256;                                   // [16]
+    double* va = lam + 128;                                   // [2][4][128] power-iteration
+    double* vb = va + 1024;                                   // vectors, Gauss-Jordan buffers
+    double* red = vb + 1024;                                  // [16]
     int* flag = reinterpret_cast<int*>(red + 16);
     const int hd = pa.n * d;
     const float* Sa = pa.S + (int64_t)a * d * d;
@@ -1367,7 +1429,7 @@ static MergeWs carve_merge(void* base, int64_t L, int D, int h_q, int h_kt, int 
 }
 
 static size_t pair_lds(int d) {
-    return (size_t)pair_matrix_words(d) * 8 + 128 * 16 + 5 * 128 * 8 + 16 * 8 + 16;
+    return (size_t)pair_matrix_words(d) * 8 + 128 * 16 + (128 + 2048) * 8 + 16 * 8 + 16;
 }
 
 static bool merge_shape_ok(int64_t L, int D, int h_q, int h_kt, int d) {
