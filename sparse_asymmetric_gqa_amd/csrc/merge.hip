@@ -256,7 +256,6 @@ __global__ __launch_bounds__(kSyrkThreads, 1) void syrk_partial(
 
     auto step = [&](int s, auto P) {
         constexpr int p = decltype(P)::value;
-        if (s + 3 < nfull) issue(s + 3, std::integral_constant<int, (p + 3) & 3>{});
         const char* abuf = sy_buf<p>(0);
         const char* bbuf = sy_buf<p>(1);
 #pragma unroll
@@ -272,6 +271,10 @@ __global__ __launch_bounds__(kSyrkThreads, 1) void syrk_partial(
                     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bf[j], acc[i][j], 0,
                                                                         0, 0);
             }
+            // the loads of stage s + 3 go out once this stage's first
+            // fragments are read
+            if (kk == 0 && s + 3 < nfull)
+                issue(s + 3, std::integral_constant<int, (p + 3) & 3>{});
         }
         if (s + 1 < nstage && s + 1 >= nfull)
             copy_stage(s + 1, std::integral_constant<int, (p + 1) & 3>{});
