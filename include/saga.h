@@ -334,6 +334,28 @@ saga_status saga_debug_fallback_rows(const void* workspace, size_t workspace_byt
                                      int h_q, int h_k, int h_v, int d, int N, int64_t S_max,
                                      saga_dtype dtype, int32_t* host_flags, hipStream_t stream);
 
+/*
+ * Bandwidth ceilings of the decode step's two memory access patterns, for
+ * benchmarks (they compute nothing of the method):
+ *   saga_debug_stream_read reads every byte of the device buffer `buf`
+ *   (bytes > 0, a multiple of 16, buf 16-byte aligned) once, sequentially,
+ *   as the K-scan reads the key cache; sink is a device uint32 that is never
+ *   written for real data.
+ *   saga_debug_gather_rows reads the value rows listed per (b, query head)
+ *   in idx int32 [B][h_q][N] (positions in [0, S_max); negative entries are
+ *   skipped) from v_cache [B][h_v][S_max][d], with the
+ *   decode path's gather loop and workgroup placement, and writes their mean
+ *   to out fp32 [B][h_q][d] (0 for an empty list): the value gather without
+ *   selection or softmax.
+ * Same argument checks as saga_decode_attn where they apply.
+ */
+saga_status saga_debug_stream_read(const void* buf, size_t bytes, uint32_t* sink,
+                                   hipStream_t stream);
+
+saga_status saga_debug_gather_rows(const void* v_cache, const int32_t* idx, float* out, int B,
+                                   int h_q, int h_v, int d, int N, hipStream_t stream,
+                                   int64_t S_max, saga_dtype dtype);
+
 /* Static English text for a status code (never NULL). */
 const char* saga_status_string(saga_status s);
 

@@ -5,9 +5,10 @@ adds torch-tensor convenience wrappers. Importing fails if libsaga.so has not
 been built: there is no CPU or eager fallback.
 """
 from ._binding import (  # noqa: F401
-    EXPORTS, LIB_PATH, SAGA_BF16, SAGA_ERR_HIP, SAGA_ERR_INVALID_ARG, SAGA_ERR_UNSUPPORTED,
-    SAGA_ERR_WORKSPACE, SAGA_F32, SAGA_OK, SagaError, lib, saga_atopn_attn, saga_atopn_calibrate,
-    saga_atopn_workspace_size, saga_debug_fallback_rows,
+    EXPORTS, LIB_PATH, SAGA_BF16, SAGA_ERR_HIP, SAGA_ERR_INVALID_ARG,
+    SAGA_ERR_UNSUPPORTED, SAGA_ERR_WORKSPACE, SAGA_F32, SAGA_OK, SagaError, lib, saga_atopn_attn, saga_atopn_calibrate,
+    saga_atopn_workspace_size, saga_debug_fallback_rows, saga_debug_gather_rows,
+    saga_debug_stream_read,
     saga_debug_scores, saga_decode_attn, saga_decode_attn_timed,
     saga_dense_attn, saga_dense_workspace_size, saga_sparq_attn, saga_sparq_workspace_size,
     saga_status_string, saga_workspace_size, status_string, SAGA_MERGE_KEY, SAGA_MERGE_LOGIT,

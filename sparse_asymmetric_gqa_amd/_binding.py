@@ -26,6 +26,7 @@ EXPORTS = ("saga_workspace_size", "saga_decode_attn", "saga_decode_attn_timed",
            "saga_dense_workspace_size", "saga_atopn_workspace_size", "saga_atopn_calibrate",
            "saga_atopn_attn", "saga_sparq_workspace_size", "saga_sparq_attn",
            "saga_dense_attn", "saga_debug_scores", "saga_debug_fallback_rows",
+           "saga_debug_stream_read", "saga_debug_gather_rows",
            "saga_key_merge_workspace_size", "saga_key_merge", "saga_key_merge_timed",
            "saga_merge_permute", "saga_status_string")
 
@@ -62,6 +63,10 @@ def _load() -> ctypes.CDLL:
     lib.saga_debug_scores.restype = i
     lib.saga_debug_fallback_rows.argtypes = [vp, sz, i, i, i, i, i, i, i64, i, vp, vp]
     lib.saga_debug_fallback_rows.restype = i
+    lib.saga_debug_stream_read.argtypes = [vp, sz, vp, vp]
+    lib.saga_debug_stream_read.restype = i
+    lib.saga_debug_gather_rows.argtypes = [vp, vp, vp, i, i, i, i, i, vp, i64, i]
+    lib.saga_debug_gather_rows.restype = i
     lib.saga_atopn_workspace_size.argtypes = [i, i, i, i, i, i, i64, i]
     lib.saga_atopn_workspace_size.restype = sz
     lib.saga_atopn_calibrate.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, vp, i64, i, vp, sz,
@@ -154,6 +159,15 @@ def saga_debug_fallback_rows(workspace, workspace_bytes, B, h_q, h_k, h_v, d, N,
     return int(lib.saga_debug_fallback_rows(_ptr(workspace), workspace_bytes, B, h_q, h_k, h_v,
                                             d, N, S_max, dtype,
                                             ctypes.c_void_p(host_flags.ctypes.data), _ptr(stream)))
+
+
+def saga_debug_stream_read(buf, nbytes, sink, stream) -> int:
+    return int(lib.saga_debug_stream_read(_ptr(buf), nbytes, _ptr(sink), _ptr(stream)))
+
+
+def saga_debug_gather_rows(v_cache, idx, out, B, h_q, h_v, d, N, stream, S_max, dtype) -> int:
+    return int(lib.saga_debug_gather_rows(_ptr(v_cache), _ptr(idx), _ptr(out), B, h_q, h_v, d,
+                                          N, _ptr(stream), S_max, dtype))
 
 
 def saga_atopn_workspace_size(B, h_q, h_k, h_v, d, N, S_max, dtype) -> int:

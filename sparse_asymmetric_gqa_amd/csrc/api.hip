@@ -374,6 +374,26 @@ saga_status saga_debug_scores(const void* q, const void* k_cache, const int32_t*
                                        S_max, dtype == SAGA_BF16, stream), "kscan");
 }
 
+saga_status saga_debug_stream_read(const void* buf, size_t bytes, uint32_t* sink,
+                                  hipStream_t stream) {
+    if (!buf || !sink || bytes < 16 || (bytes & 15) || !aligned16(buf))
+        return SAGA_ERR_INVALID_ARG;
+    clear_stale_error();
+    return from_hip(saga::launch_stream_read(buf, bytes, sink, stream), "stream_read");
+}
+
+saga_status saga_debug_gather_rows(const void* v_cache, const int32_t* idx, float* out, int B,
+                                   int h_q, int h_v, int d, int N, hipStream_t stream,
+                                   int64_t S_max, saga_dtype dtype) {
+    if (!v_cache || !idx || !out || N < 1) return SAGA_ERR_INVALID_ARG;
+    saga_status s = check_shape(B, h_q, h_v, h_v, d, S_max, dtype);
+    if (s != SAGA_OK) return s;
+    if (!aligned16(v_cache)) return SAGA_ERR_INVALID_ARG;
+    clear_stale_error();
+    return from_hip(saga::launch_gather_rows(v_cache, idx, out, B, h_q, h_v, d, N, S_max,
+                                             dtype == SAGA_BF16, stream), "gather_rows");
+}
+
 saga_status saga_debug_fallback_rows(const void* workspace, size_t workspace_bytes, int B,
                                      int h_q, int h_k, int h_v, int d, int N, int64_t S_max,
                                      saga_dtype dtype, int32_t* host_flags, hipStream_t stream) {

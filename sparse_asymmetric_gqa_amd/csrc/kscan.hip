@@ -330,12 +330,9 @@ hipError_t go_topm(const void* q, const void* k, const int32_t* lens, const Topm
     const size_t lds = kTopmLdsBytes;
     static_assert(topm_lds_words<T, DH>(16) * 4 + 8 * 1024 <= kTopmLdsBytes,
                   "staging area too small");
-    static bool attr_set = false;   // one per instantiation: allow > 64 KiB of dynamic LDS
-    if (!attr_set) {
-        if (hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
-            return hipGetLastError();
-        attr_set = true;
+    {   // allow > 64 KiB of dynamic LDS
+        const hipError_t e = allow_dynamic_lds(reinterpret_cast<const void*>(kern), lds);
+        if (e != hipSuccess) return e;
     }
     const int grid = resident_grid(kern, kTopmThreads, lds, nwork);
     if (ev0 || ev1)   // events stamped with the dispatch's own start and end

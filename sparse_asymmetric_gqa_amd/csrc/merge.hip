@@ -1441,10 +1441,6 @@ static bool merge_shape_ok(int64_t L, int D, int h_q, int h_kt, int d) {
            (int64_t)D * D <= ((int64_t)1 << 31);
 }
 
-static hipError_t set_lds(const void* fn, size_t bytes) {
-    return hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
-}
-
 static NtJob nt_job(const void* A, const float* B, float* out, int64_t lda, int64_t ldb,
                     int64_t ldo, int M, int N, int K) {
     NtJob j{};
@@ -1494,15 +1490,12 @@ static saga_status key_merge_impl(const void* x, const void* wq, const void* wk,
     const MergeWs probe = carve_merge(nullptr, L, D, h_q, h_kt, d);
     if (!workspace || workspace_bytes < probe.bytes) return SAGA_ERR_WORKSPACE;
     MergeWs w = carve_merge(workspace, L, D, h_q, h_kt, d);
-    static bool lds_set = false;
-    if (!lds_set) {
-        if (set_lds(reinterpret_cast<const void*>(nt_bf16x3), kF3Lds) != hipSuccess ||
-            set_lds(reinterpret_cast<const void*>(pair_loss), 8 * kPanWords * 8 + 16 * 8) !=
-                hipSuccess ||
-            set_lds(reinterpret_cast<const void*>(merge_pairs), pair_lds(128)) != hipSuccess)
-            return SAGA_ERR_HIP;
-        lds_set = true;
-    }
+    // dynamic LDS beyond 64 KiB, opted in once per device (thread-safe)
+    if (allow_dynamic_lds(reinterpret_cast<const void*>(nt_bf16x3), kF3Lds) != hipSuccess ||
+        allow_dynamic_lds(reinterpret_cast<const void*>(pair_loss), 8 * kPanWords * 8 + 16 * 8) !=
+            hipSuccess ||
+        allow_dynamic_lds(reinterpret_cast<const void*>(merge_pairs), pair_lds(128)) != hipSuccess)
+        return SAGA_ERR_HIP;
     bool ok = true;
     auto mark = [&](int i) {
         if (i < nev) ok = hipEventRecord(ev[i], st) == hipSuccess && ok;

@@ -14,6 +14,7 @@ constexpr int kScanChunk = SAGA_KSCAN_CHUNK;   // positions per K-scan workgroup
 constexpr int kPvEntries = 2048;     // kept entries staged per block of the sparse PV
 constexpr int kSelectThreads = 1024; // threads of one select workgroup
 constexpr int kMaxHeadGroup = 64;    // largest h_q / h_k and h_q / h_v supported
+constexpr int kMaxDevices = 64;      // device ordinals the host-side caches cover
 
 inline int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 
@@ -72,6 +73,13 @@ struct TopmOut {
     int N;             // the M of each chunk's list is sized for this N
     float2* stat;      // nullable: [B*h_q][nchunk] {max logit, sum of exp(logit - max)}
 };
+
+// ---- host-side launch caches (launch.hip; thread-safe, per current device) ----
+int cu_count();
+// Resident workgroups per CU of `kern` at this block size and dynamic LDS.
+int blocks_per_cu(const void* kern, int threads, size_t lds);
+// Opts `kern` in to `lds` bytes of dynamic LDS (> 64 KiB) once per device.
+hipError_t allow_dynamic_lds(const void* kern, size_t lds);
 
 // ---- launchers (defined next to their kernels) ------------------------------
 // All return hipGetLastError() after enqueueing.
@@ -144,6 +152,13 @@ hipError_t launch_pv_sparse(const void* v, const int32_t* sel_idx, const float* 
                             const float* row_max, const int32_t* row_cnt, float* out, int B,
                             int h_q, int h_v, int d, int N, int64_t S_max, bool bf16,
                             hipStream_t st);
+
+// Bandwidth ceilings (ceiling.hip): a sequential read of `bytes` (a multiple of
+// 16; sink: device uint32, written only in the impossible case), and a plain
+// gather of the value rows listed in idx [B*h_q][N] into out [B*h_q][d].
+hipError_t launch_stream_read(const void* p, size_t bytes, uint32_t* sink, hipStream_t st);
+hipError_t launch_gather_rows(const void* v, const int32_t* idx, float* out, int B, int h_q,
+                              int h_v, int d, int N, int64_t S_max, bool bf16, hipStream_t st);
 
 // Dense attention (every position, Eqs. 2-4): fused K stream, chunk softmax
 // and V stream into part [B][h_q][nchunk][d + 2], then the log-sum-exp merge

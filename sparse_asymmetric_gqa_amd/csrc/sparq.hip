@@ -424,12 +424,9 @@ hipError_t go_sparq_scan(const void* kt, const int32_t* lens, const TopmOut& tm,
     auto kern = &sparq_topm<T, DH, KT>;
     const size_t lds = kTopmLdsBytes;
     static_assert(sq_lds_words<T, DH>(16) * 4 + 8 * 1024 <= kTopmLdsBytes, "staging area too small");
-    static bool attr_set = false;   // one per instantiation: allow > 64 KiB of dynamic LDS
-    if (!attr_set) {
-        if (hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
-            return hipGetLastError();
-        attr_set = true;
+    {   // allow > 64 KiB of dynamic LDS
+        const hipError_t e = allow_dynamic_lds(reinterpret_cast<const void*>(kern), lds);
+        if (e != hipSuccess) return e;
     }
     const int grid = resident_grid(kern, kTopmThreads, lds, nwork);
     hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kTopmThreads), lds, st, (const T*)kt, lens,

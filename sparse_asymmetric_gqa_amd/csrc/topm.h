@@ -228,45 +228,12 @@ __device__ inline void extract(const Item<T>& it, int n, uint32_t M, uint32_t* r
     }
 }
 
-int cu_count() {
-    static int cached[64] = {0};
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-    if (!cached[dev]) {
-        int n = 0;
-        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-            n <= 0)
-            n = 256;
-        cached[dev] = n;
-    }
-    return cached[dev];
-}
-
 // Persistent grid: as many workgroups as can be resident at once (so none of
 // them waits for another to finish all of its work before starting), at most
-// one per work item. Residency per CU is queried once per kernel and LDS size.
+// one per work item.
 template <typename K>
 int resident_grid(K kern, int threads, size_t lds, int nwork) {
-    static const void* cached_k[16] = {nullptr};
-    static int cached_lds[16] = {0};
-    static int cached_blocks[16] = {0};
-    int per_cu = 0;
-    for (int i = 0; i < 16; ++i)
-        if (cached_k[i] == (const void*)kern && cached_lds[i] == (int)lds) per_cu = cached_blocks[i];
-    if (per_cu == 0) {
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, threads, lds) !=
-                hipSuccess ||
-            per_cu <= 0)
-            per_cu = 1;
-        for (int i = 0; i < 16; ++i)
-            if (cached_k[i] == nullptr) {
-                cached_k[i] = (const void*)kern;
-                cached_lds[i] = (int)lds;
-                cached_blocks[i] = per_cu;
-                break;
-            }
-    }
-    const int grid = cu_count() * per_cu;
+    const int grid = cu_count() * blocks_per_cu(reinterpret_cast<const void*>(kern), threads, lds);
     return grid < nwork ? grid : nwork;
 }
 

@@ -268,3 +268,4 @@ def test_key_merge_workspace_size():
     n = mw(131072, 2048, 32, 8, 64)
     assert 36 * 7 * 256 * 256 * 4 < n < 36 * 7 * 256 * 256 * 4 + (96 << 20)
     assert mw(700, 512, 8, 3, 64) == 0 and mw(700, 512, 8, 4, 136) == 0 and mw(0, 512, 8, 4, 64) == 0
+
