@@ -57,7 +57,9 @@ typedef enum {
                                    divide h_q, h_k > h_v, unknown dtype, misaligned tensor */
     SAGA_ERR_UNSUPPORTED = -2,  /* head dimension d other than 64 or 128; h_q / h_v > 64 */
     SAGA_ERR_WORKSPACE = -3,    /* workspace null or smaller than the size functions return */
-    SAGA_ERR_HIP = -4           /* a kernel launch failed (hipGetLastError) */
+    SAGA_ERR_HIP = -4,          /* a kernel launch failed (hipGetLastError) */
+    SAGA_ERR_TOO_LARGE = -5     /* saga_decode_attn_noalloc: the shape needs more scratch than
+                                   saga_noalloc_scratch_bytes() */
 } saga_status;
 
 typedef enum {
@@ -113,6 +115,34 @@ saga_status saga_decode_attn_timed(const void* q, const void* k_cache, const voi
                                    hipStream_t stream, int64_t S_max, saga_dtype dtype,
                                    void* workspace, size_t workspace_bytes, int32_t* idx_out,
                                    hipEvent_t* events, int n_events);
+
+/*
+ * saga_decode_attn for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc. Same arguments and results as saga_decode_attn, without the
+ * workspace: the scratch memory is a static device array of the library,
+ * saga_noalloc_scratch_bytes() bytes (128 MiB), one per GPU, held by every
+ * GPU the library runs on until the process ends. The call allocates
+ * nothing (no hipMalloc, no hipFree, no allocating library routine); on its
+ * first use on a device it looks up the array's device address once. The
+ * kernels run on the device of `stream` (the current device for the null
+ * stream).
+ *   - A shape whose saga_workspace_size exceeds saga_noalloc_scratch_bytes()
+ *     returns SAGA_ERR_TOO_LARGE and enqueues nothing.
+ *   - Every call on one GPU shares that GPU's array, which keeps the last
+ *     call's contents (the decode path rewrites everything it reads, so
+ *     nothing needs clearing). Calls that overlap in time on one GPU (on
+ *     different streams, or from different host threads without ordering)
+ *     race on the array: the caller must serialise them.
+ * Other errors as for saga_decode_attn.
+ */
+size_t saga_noalloc_scratch_bytes(void);
+
+saga_status saga_decode_attn_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                                     const int32_t* seq_lens, float* out,
+                                     int B, int h_q, int h_k, int h_v, int d, int N,
+                                     hipStream_t stream, int64_t S_max, saga_dtype dtype,
+                                     int32_t* idx_out);
 
 /*
  * Bytes of device workspace saga_dense_attn needs (host only; 0 on invalid

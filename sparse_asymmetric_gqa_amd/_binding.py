@@ -19,10 +19,12 @@ SAGA_ERR_INVALID_ARG = -1
 SAGA_ERR_UNSUPPORTED = -2
 SAGA_ERR_WORKSPACE = -3
 SAGA_ERR_HIP = -4
+SAGA_ERR_TOO_LARGE = -5
 SAGA_F32 = 0
 SAGA_BF16 = 1
 
 EXPORTS = ("saga_workspace_size", "saga_decode_attn", "saga_decode_attn_timed",
+           "saga_noalloc_scratch_bytes", "saga_decode_attn_noalloc",
            "saga_dense_workspace_size", "saga_atopn_workspace_size", "saga_atopn_calibrate",
            "saga_atopn_attn", "saga_sparq_workspace_size", "saga_sparq_attn",
            "saga_dense_attn", "saga_debug_scores", "saga_debug_fallback_rows",
@@ -57,6 +59,10 @@ def _load() -> ctypes.CDLL:
     lib.saga_decode_attn_timed.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, vp, i64, i, vp,
                                            sz, vp, vp, i]
     lib.saga_decode_attn_timed.restype = i
+    lib.saga_noalloc_scratch_bytes.argtypes = []
+    lib.saga_noalloc_scratch_bytes.restype = sz
+    lib.saga_decode_attn_noalloc.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, vp, i64, i, vp]
+    lib.saga_decode_attn_noalloc.restype = i
     lib.saga_dense_attn.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, vp, i64, i, vp, sz]
     lib.saga_dense_attn.restype = i
     lib.saga_debug_scores.argtypes = [vp, vp, vp, vp, i, i, i, i, vp, i64, i]
@@ -138,6 +144,17 @@ def saga_decode_attn_timed(q, k_cache, v_cache, seq_lens, out, B, h_q, h_k, h_v,
                                           _ptr(out), B, h_q, h_k, h_v, d, N, _ptr(stream), S_max,
                                           dtype, _ptr(workspace), workspace_bytes,
                                           _ptr(idx_out), arr, n))
+
+
+def saga_noalloc_scratch_bytes() -> int:
+    return int(lib.saga_noalloc_scratch_bytes())
+
+
+def saga_decode_attn_noalloc(q, k_cache, v_cache, seq_lens, out, B, h_q, h_k, h_v, d, N, stream,
+                             S_max, dtype, idx_out=None) -> int:
+    return int(lib.saga_decode_attn_noalloc(_ptr(q), _ptr(k_cache), _ptr(v_cache),
+                                            _ptr(seq_lens), _ptr(out), B, h_q, h_k, h_v, d, N,
+                                            _ptr(stream), S_max, dtype, _ptr(idx_out)))
 
 
 def saga_dense_attn(q, k_cache, v_cache, seq_lens, out, B, h_q, h_k, h_v, d, stream, S_max,

@@ -10,6 +10,8 @@
 #include <stdio.h>
 #include <stdlib.h>
 
+#include <mutex>
+
 namespace saga {
 
 static size_t align256(size_t x) { return (x + 255) / 256 * 256; }
@@ -171,6 +173,34 @@ saga_status decode(const void* q, const void* k_cache, const void* v_cache,
     return pm.mark(3, stream);
 }
 
+// ---- the no-allocation decode entry: a static device scratch buffer ----------
+// One array per GPU, part of the library's device code object (each GPU the
+// library runs on holds it until the process ends). Host code never passes
+// the array's name to a kernel: the name is a host-side stand-in. Its device
+// address is looked up once per device, with that device current, and kept.
+constexpr size_t kNoAllocScratchBytes = (size_t)128 << 20;
+__device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+std::once_flag g_scratch_once[saga::kMaxDevices];
+void* g_scratch_ptr[saga::kMaxDevices];
+
+// Device address of this device's scratch array (null on failure).
+void* scratch_address(int dev) {
+    std::call_once(g_scratch_once[dev], [dev] {
+        void* p = nullptr;
+        int cur = -1;
+        bool switched = false;
+        if (hipGetDevice(&cur) == hipSuccess && cur != dev)
+            switched = hipSetDevice(dev) == hipSuccess;
+        if (cur == dev || switched) {
+            if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess) p = nullptr;
+            if (switched) (void)hipSetDevice(cur);
+        }
+        g_scratch_ptr[dev] = p;
+    });
+    return g_scratch_ptr[dev];
+}
+
 }  // namespace
 
 extern "C" {
@@ -195,6 +225,32 @@ saga_status saga_decode_attn_timed(const void* q, const void* k_cache, const voi
         if (!events[i]) return SAGA_ERR_INVALID_ARG;
     return decode(q, k_cache, v_cache, seq_lens, out, B, h_q, h_k, h_v, d, N, stream, S_max,
                   dtype, workspace, workspace_bytes, idx_out, PhaseMarks{events, n_events});
+}
+
+size_t saga_noalloc_scratch_bytes(void) { return kNoAllocScratchBytes; }
+
+saga_status saga_decode_attn_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                                     const int32_t* seq_lens, float* out, int B, int h_q, int h_k,
+                                     int h_v, int d, int N, hipStream_t stream, int64_t S_max,
+                                     saga_dtype dtype, int32_t* idx_out) {
+    if (!q || !k_cache || !v_cache || !seq_lens || !out) return SAGA_ERR_INVALID_ARG;
+    saga_status s = check_shape(B, h_q, h_k, h_v, d, S_max, dtype);
+    if (s != SAGA_OK) return s;
+    if (N < 1) return SAGA_ERR_INVALID_ARG;
+    const size_t need = saga::carve(nullptr, B, h_q, h_k, d, N, S_max, false).bytes;
+    if (need > kNoAllocScratchBytes) return SAGA_ERR_TOO_LARGE;
+    // the device the kernels run on: the stream's, else the current one
+    int dev = -1;
+    if (stream) {
+        if (hipStreamGetDevice(stream, &dev) != hipSuccess) return SAGA_ERR_HIP;
+    } else if (hipGetDevice(&dev) != hipSuccess) {
+        return SAGA_ERR_HIP;
+    }
+    if (dev < 0 || dev >= saga::kMaxDevices) return SAGA_ERR_UNSUPPORTED;
+    void* ws = scratch_address(dev);
+    if (!ws) return SAGA_ERR_HIP;
+    return decode(q, k_cache, v_cache, seq_lens, out, B, h_q, h_k, h_v, d, N, stream, S_max,
+                  dtype, ws, kNoAllocScratchBytes, idx_out, PhaseMarks{nullptr, 0});
 }
 
 saga_status saga_dense_attn(const void* q, const void* k_cache, const void* v_cache,
@@ -425,6 +481,8 @@ const char* saga_status_string(saga_status s) {
         case SAGA_ERR_UNSUPPORTED: return "unsupported shape (d must be 64 or 128; head groups <= 64)";
         case SAGA_ERR_WORKSPACE: return "workspace missing, too small or not 256-byte aligned";
         case SAGA_ERR_HIP: return "HIP launch failure";
+        case SAGA_ERR_TOO_LARGE:
+            return "the shape needs more scratch than the static buffer of saga_decode_attn_noalloc";
     }
     return "unknown status";
 }

@@ -33,7 +33,7 @@ def test_exports_match_header():
 
 
 def test_status_strings():
-    for code in (0, -1, -2, -3, -4):
+    for code in (0, -1, -2, -3, -4, -5):
         s = saga.status_string(code)
         assert s and s != "unknown status"
     assert saga.status_string(7) == "unknown status"
@@ -269,3 +269,26 @@ def test_key_merge_workspace_size():
     assert 36 * 7 * 256 * 256 * 4 < n < 36 * 7 * 256 * 256 * 4 + (96 << 20)
     assert mw(700, 512, 8, 3, 64) == 0 and mw(700, 512, 8, 4, 136) == 0 and mw(0, 512, 8, 4, 64) == 0
 
+
+def test_noalloc_entry_checks_on_host():
+    """The no-allocation entry: its static scratch size, and every argument
+    check (including the scratch bound) decided on the host before any HIP call."""
+    assert saga.saga_noalloc_scratch_bytes() == 128 << 20
+    f = saga.saga_decode_attn_noalloc
+    base = [FAKE, FAKE, FAKE, FAKE, FAKE, 2, 8, 2, 4, 64, 16, None, 100, saga.SAGA_BF16, None]
+
+    def call(**kw):
+        a = list(base)
+        for k_, v_ in kw.items():
+            a[int(k_[1:])] = v_
+        return f(*a)
+    assert call(a0=None) == saga.SAGA_ERR_INVALID_ARG       # q
+    assert call(a4=None) == saga.SAGA_ERR_INVALID_ARG       # out
+    assert call(a10=0) == saga.SAGA_ERR_INVALID_ARG         # N
+    assert call(a7=4, a8=2) == saga.SAGA_ERR_INVALID_ARG    # h_k > h_v
+    assert call(a9=96) == saga.SAGA_ERR_UNSUPPORTED         # d
+    # a shape whose decode workspace exceeds the static buffer
+    big = saga.saga_workspace_size(64, 12, 1, 2, 128, 1024, 1 << 20, saga.SAGA_BF16)
+    assert big > saga.saga_noalloc_scratch_bytes()
+    assert call(a5=64, a6=12, a7=1, a8=2, a9=128, a10=1024, a12=1 << 20) == \
+        saga.SAGA_ERR_TOO_LARGE
