@@ -17,8 +17,10 @@ namespace saga {
 static size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
 Workspace carve(void* base, int B, int h_q, int h_k, int d, int N, int64_t S_max,
-                bool dense, SparqWs* sq, int esize) {
+                bool dense, int chunk, int nsplit, SparqWs* sq, int esize) {
     Workspace w{};
+    w.chunk = chunk;
+    w.nsplit = nsplit;
     char* p = static_cast<char*>(base);
     size_t off = 0;
     const size_t rows = (size_t)B * (size_t)h_q;
@@ -30,8 +32,8 @@ Workspace carve(void* base, int B, int h_q, int h_k, int d, int N, int64_t S_max
     if (!dense) {
         w.scores = reinterpret_cast<float*>(
             take(rows * (size_t)score_stride(S_max) * sizeof(float)));
-        const size_t nch = (size_t)num_chunks(S_max);
-        w.cand = reinterpret_cast<uint2*>(take(rows * nch * kScanChunk * sizeof(uint2)));
+        const size_t nch = (size_t)num_chunks(S_max, chunk);
+        w.cand = reinterpret_cast<uint2*>(take(rows * nch * (size_t)chunk * sizeof(uint2)));
         w.cand_meta = reinterpret_cast<uint4*>(take(rows * nch * sizeof(uint4)));
         w.cand_stat = reinterpret_cast<float2*>(take(rows * nch * sizeof(float2)));
         w.row_flag = reinterpret_cast<int32_t*>(take(rows * sizeof(int32_t)));
@@ -39,6 +41,11 @@ Workspace carve(void* base, int B, int h_q, int h_k, int d, int N, int64_t S_max
         w.sel_val = reinterpret_cast<float*>(take(rows * (size_t)N * sizeof(float)));
         w.row_max = reinterpret_cast<float*>(take(rows * sizeof(float)));
         w.row_cnt = reinterpret_cast<int32_t*>(take(rows * sizeof(int32_t)));
+        if (nsplit > 1) {
+            w.split_part = reinterpret_cast<float*>(
+                take(rows * (size_t)nsplit * (size_t)d * sizeof(float)));
+            w.split_cnt = reinterpret_cast<int32_t*>(take(rows * sizeof(int32_t)));
+        }
         if (sq) {
             const size_t kr = (size_t)B * (size_t)h_k;
             sq->dims = reinterpret_cast<int32_t*>(take(kr * (size_t)d * sizeof(int32_t)));
@@ -58,11 +65,26 @@ bool use_union_path(int h_q, int h_k, int64_t S_max) {
     return h_q / h_k <= 16 && num_chunks(S_max) <= max_union_chunks();
 }
 
+// The decode workspace of saga_decode_attn: K-scan chunk and value-gather
+// split chosen from the shape (the same choice at sizing and at launch).
+Workspace carve_decode(void* base, int B, int h_q, int h_k, int d, int N, int64_t S_max) {
+    const bool u = use_union_path(h_q, h_k, S_max);
+    return carve(base, B, h_q, h_k, d, N, S_max, false,
+                 u ? topm_chunk(B, h_k, S_max) : kScanChunk, u ? gather_split(B, h_q) : 1);
+}
+
+// The Atop-N workspace: the decode one with 2N kept slots per row.
+Workspace carve_atopn(void* base, int B, int h_q, int h_k, int d, int N, int64_t S_max) {
+    return carve(base, B, h_q, h_k, d, 2 * N, S_max, false, topm_chunk(B, h_k, S_max),
+                 gather_split(B, h_q));
+}
+
 }  // namespace saga
 
 namespace {
 
 using saga::kMaxHeadGroup;
+using saga::kScanChunk;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -99,13 +121,13 @@ extern "C" {
 size_t saga_workspace_size(int B, int h_q, int h_k, int h_v, int d, int N, int64_t S_max,
                            saga_dtype dtype) {
     if (check_shape(B, h_q, h_k, h_v, d, S_max, dtype) != SAGA_OK || N < 1) return 0;
-    return saga::carve(nullptr, B, h_q, h_k, d, N, S_max, false).bytes;
+    return saga::carve_decode(nullptr, B, h_q, h_k, d, N, S_max).bytes;
 }
 
 size_t saga_dense_workspace_size(int B, int h_q, int h_k, int h_v, int d, int64_t S_max,
                                  saga_dtype dtype) {
     if (check_shape(B, h_q, h_k, h_v, d, S_max, dtype) != SAGA_OK) return 0;
-    return saga::carve(nullptr, B, h_q, h_k, d, 1, S_max, true).bytes;
+    return saga::carve(nullptr, B, h_q, h_k, d, 1, S_max, true, kScanChunk, 1).bytes;
 }
 
 }  // extern "C"
@@ -131,17 +153,19 @@ saga_status decode(const void* q, const void* k_cache, const void* v_cache,
     if (s != SAGA_OK) return s;
     if (N < 1) return SAGA_ERR_INVALID_ARG;
     if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache)) return SAGA_ERR_INVALID_ARG;
-    const saga::Workspace need = saga::carve(nullptr, B, h_q, h_k, d, N, S_max, false);
+    const saga::Workspace need = saga::carve_decode(nullptr, B, h_q, h_k, d, N, S_max);
     if (!workspace || workspace_bytes < need.bytes || (reinterpret_cast<uintptr_t>(workspace) & 255u))
         return SAGA_ERR_WORKSPACE;
-    const saga::Workspace w = saga::carve(workspace, B, h_q, h_k, d, N, S_max, false);
+    const saga::Workspace w = saga::carve_decode(workspace, B, h_q, h_k, d, N, S_max);
     const bool bf16 = dtype == SAGA_BF16;
     const int64_t ss = saga::score_stride(S_max);
 
     clear_stale_error();
     if (saga::use_union_path(h_q, h_k, S_max)) {
         // events 0 and 1 carry the K-scan dispatch's own start and end
-        const saga::TopmOut tm{w.cand, w.cand_meta, N, nullptr};
+        // the K-scan clears the split counters the fused select + gather uses
+        const saga::TopmOut tm{w.cand, w.cand_meta, N, nullptr, w.chunk,
+                               w.nsplit > 1 ? w.split_cnt : nullptr, B * h_q};
         s = from_hip(saga::launch_kscan_topm(q, k_cache, seq_lens, tm, B, h_q, h_k, d, S_max,
                                              bf16, stream, pm.n > 0 ? pm.ev[0] : nullptr,
                                              pm.n > 1 ? pm.ev[1] : nullptr),
@@ -151,7 +175,9 @@ saga_status decode(const void* q, const void* k_cache, const void* v_cache,
         s = from_hip(saga::launch_select_pv(tm, seq_lens, B, h_q, h_k, h_v, d, N, S_max,
                                             w.sel_idx, w.sel_val, w.row_max, w.row_cnt, idx_out,
                                             w.row_flag, q, k_cache, v_cache, w.scores, ss, out,
-                                            bf16, stream), "select_pv");
+                                            bf16, w.nsplit, w.split_part, w.split_cnt, nullptr,
+                                            stream),
+                     "select_pv");
         if (s != SAGA_OK) return s;
         if ((s = pm.mark(2, stream)) != SAGA_OK) return s;
         return pm.mark(3, stream);
@@ -237,7 +263,7 @@ saga_status saga_decode_attn_noalloc(const void* q, const void* k_cache, const v
     saga_status s = check_shape(B, h_q, h_k, h_v, d, S_max, dtype);
     if (s != SAGA_OK) return s;
     if (N < 1) return SAGA_ERR_INVALID_ARG;
-    const size_t need = saga::carve(nullptr, B, h_q, h_k, d, N, S_max, false).bytes;
+    const size_t need = saga::carve_decode(nullptr, B, h_q, h_k, d, N, S_max).bytes;
     if (need > kNoAllocScratchBytes) return SAGA_ERR_TOO_LARGE;
     // the device the kernels run on: the stream's, else the current one
     int dev = -1;
@@ -262,10 +288,10 @@ saga_status saga_dense_attn(const void* q, const void* k_cache, const void* v_ca
     saga_status s = check_shape(B, h_q, h_k, h_v, d, S_max, dtype);
     if (s != SAGA_OK) return s;
     if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache)) return SAGA_ERR_INVALID_ARG;
-    const saga::Workspace need = saga::carve(nullptr, B, h_q, h_k, d, 1, S_max, true);
+    const saga::Workspace need = saga::carve(nullptr, B, h_q, h_k, d, 1, S_max, true, kScanChunk, 1);
     if (!workspace || workspace_bytes < need.bytes || (reinterpret_cast<uintptr_t>(workspace) & 255u))
         return SAGA_ERR_WORKSPACE;
-    const saga::Workspace w = saga::carve(workspace, B, h_q, h_k, d, 1, S_max, true);
+    const saga::Workspace w = saga::carve(workspace, B, h_q, h_k, d, 1, S_max, true, kScanChunk, 1);
     const bool bf16 = dtype == SAGA_BF16;
 
     clear_stale_error();
@@ -279,7 +305,7 @@ size_t saga_atopn_workspace_size(int B, int h_q, int h_k, int h_v, int d, int N,
     if (check_shape(B, h_q, h_k, h_v, d, S_max, dtype) != SAGA_OK || N < 1 || N > (1 << 29))
         return 0;
     // the decode workspace with kept lists of 2N slots per row
-    return saga::carve(nullptr, B, h_q, h_k, d, 2 * N, S_max, false).bytes;
+    return saga::carve_atopn(nullptr, B, h_q, h_k, d, N, S_max).bytes;
 }
 
 }  // extern "C"
@@ -297,11 +323,11 @@ saga_status atopn_prepare(const void* q, const void* k_cache, const void* v_cach
     if (N < 1 || N > (1 << 29)) return SAGA_ERR_INVALID_ARG;
     if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache)) return SAGA_ERR_INVALID_ARG;
     if (!saga::use_union_path(h_q, h_k, S_max)) return SAGA_ERR_UNSUPPORTED;
-    const saga::Workspace need = saga::carve(nullptr, B, h_q, h_k, d, 2 * N, S_max, false);
+    const saga::Workspace need = saga::carve_atopn(nullptr, B, h_q, h_k, d, N, S_max);
     if (!workspace || workspace_bytes < need.bytes ||
         (reinterpret_cast<uintptr_t>(workspace) & 255u))
         return SAGA_ERR_WORKSPACE;
-    w = saga::carve(workspace, B, h_q, h_k, d, 2 * N, S_max, false);
+    w = saga::carve_atopn(workspace, B, h_q, h_k, d, N, S_max);
     return SAGA_OK;
 }
 
@@ -321,22 +347,20 @@ saga_status saga_atopn_calibrate(const void* q, const void* k_cache, const void*
     const bool bf16 = dtype == SAGA_BF16;
     const int64_t ss = saga::score_stride(S_max);
     clear_stale_error();
-    // the exact top-N step, with per-chunk softmax statistics for tau
-    const saga::TopmOut tm{w.cand, w.cand_meta, N, w.cand_stat};
+    // the exact top-N step (the decode call's two kernels, with its chunk size
+    // and split), the K-scan also writing per-chunk softmax statistics and the
+    // fused select + gather also tau
+    const saga::TopmOut tm{w.cand, w.cand_meta, N, w.cand_stat, w.chunk,
+                           w.nsplit > 1 ? w.split_cnt : nullptr, B * h_q};
     s = from_hip(saga::launch_kscan_topm(q, k_cache, seq_lens, tm, B, h_q, h_k, d, S_max, bf16,
                                          stream), "kscan_topm");
     if (s != SAGA_OK) return s;
-    s = from_hip(saga::launch_select_union(tm, seq_lens, B, h_q, h_k, d, N, S_max, w.sel_idx,
-                                           w.sel_val, w.row_max, w.row_cnt, idx_out, w.row_flag,
-                                           q, k_cache, w.scores, ss, bf16, stream),
-                 "select_union");
-    if (s != SAGA_OK) return s;
-    s = from_hip(saga::launch_atopn_tau(w.sel_val, w.row_cnt, tm, seq_lens, B, h_q, N, S_max,
-                                        tau, stream), "atopn_tau");
-    if (s != SAGA_OK) return s;
-    return from_hip(saga::launch_pv_sparse(v_cache, w.sel_idx, w.sel_val, w.row_max, w.row_cnt,
-                                           out, B, h_q, h_v, d, N, S_max, bf16, stream),
-                    "pv_sparse");
+    return from_hip(saga::launch_select_pv(tm, seq_lens, B, h_q, h_k, h_v, d, N, S_max,
+                                           w.sel_idx, w.sel_val, w.row_max, w.row_cnt, idx_out,
+                                           w.row_flag, q, k_cache, v_cache, w.scores, ss, out,
+                                           bf16, w.nsplit, w.split_part, w.split_cnt, tau,
+                                           stream),
+                    "select_pv");
 }
 
 saga_status saga_atopn_attn(const void* q, const void* k_cache, const void* v_cache,
@@ -352,20 +376,20 @@ saga_status saga_atopn_attn(const void* q, const void* k_cache, const void* v_ca
     const int64_t ss = saga::score_stride(S_max);
     const int cap = 2 * N;
     clear_stale_error();
-    // candidate lists sized for up to 2N kept positions, with chunk statistics
-    const saga::TopmOut tm{w.cand, w.cand_meta, cap, w.cand_stat};
+    // candidate lists sized like the exact step's (the completeness check
+    // sends a row whose lists do not cover the threshold to the recompute),
+    // with chunk statistics; the K-scan also clears the split counters
+    const saga::TopmOut tm{w.cand, w.cand_meta, N, w.cand_stat, w.chunk,
+                           w.nsplit > 1 ? w.split_cnt : nullptr, B * h_q};
     s = from_hip(saga::launch_kscan_topm(q, k_cache, seq_lens, tm, B, h_q, h_k, d, S_max, bf16,
                                          stream), "kscan_topm");
     if (s != SAGA_OK) return s;
-    s = from_hip(saga::launch_select_thresh(tm, seq_lens, tau, B, h_q, h_k, d, cap, S_max,
-                                            w.sel_idx, w.sel_val, w.row_max, w.row_cnt, idx_out,
-                                            count_out, w.row_flag, q, k_cache, w.scores, ss,
-                                            bf16, stream),
-                 "select_thresh");
-    if (s != SAGA_OK) return s;
-    return from_hip(saga::launch_pv_sparse(v_cache, w.sel_idx, w.sel_val, w.row_max, w.row_cnt,
-                                           out, B, h_q, h_v, d, cap, S_max, bf16, stream),
-                    "pv_sparse");
+    return from_hip(saga::launch_select_thresh(tm, seq_lens, tau, B, h_q, h_k, h_v, d, cap, S_max,
+                                               w.sel_idx, w.sel_val, idx_out, count_out,
+                                               w.row_flag, q, k_cache, v_cache, w.scores, ss,
+                                               out, bf16, w.nsplit, w.split_part, w.split_cnt,
+                                               stream),
+                    "select_thresh");
 }
 
 size_t saga_sparq_workspace_size(int B, int h_q, int h_k, int h_v, int d, int N, int r,
@@ -373,7 +397,7 @@ size_t saga_sparq_workspace_size(int B, int h_q, int h_k, int h_v, int d, int N,
     if (check_shape(B, h_q, h_k, h_v, d, S_max, dtype) != SAGA_OK) return 0;
     if (N < 1 || N > (1 << 29) || r < 1 || r > d) return 0;
     saga::SparqWs sw{};
-    return saga::carve(nullptr, B, h_q, h_k, d, N, S_max, false, &sw,
+    return saga::carve(nullptr, B, h_q, h_k, d, N, S_max, false, kScanChunk, 1, &sw,
                        dtype == SAGA_BF16 ? 2 : 4).bytes;
 }
 
@@ -397,15 +421,17 @@ saga_status saga_sparq_attn(const void* q, const void* k_cache, const void* kt_c
         S_max % (16 / esize) != 0)
         return SAGA_ERR_UNSUPPORTED;
     saga::SparqWs sw{};
-    const saga::Workspace need = saga::carve(nullptr, B, h_q, h_k, d, N, S_max, false, &sw, esize);
+    const saga::Workspace need = saga::carve(nullptr, B, h_q, h_k, d, N, S_max, false, kScanChunk, 1, &sw,
+                                             esize);
     if (!workspace || workspace_bytes < need.bytes || (reinterpret_cast<uintptr_t>(workspace) & 255u))
         return SAGA_ERR_WORKSPACE;
-    const saga::Workspace w = saga::carve(workspace, B, h_q, h_k, d, N, S_max, false, &sw, esize);
+    const saga::Workspace w = saga::carve(workspace, B, h_q, h_k, d, N, S_max, false, kScanChunk, 1, &sw,
+                                          esize);
     const bool bf16 = dtype == SAGA_BF16;
     clear_stale_error();
     // Step 1 on the kept dims into candidate lists with chunk statistics (the
     // window is ranked by nobody), then Steps 2-3 in one dispatch per row
-    const saga::TopmOut tm{w.cand, w.cand_meta, N - local, w.cand_stat};
+    const saga::TopmOut tm{w.cand, w.cand_meta, N - local, w.cand_stat, kScanChunk, nullptr, 0};
     s = from_hip(saga::launch_sparq_scan(q, kt_cache, seq_lens, tm, sw, B, h_q, h_k, d, r, local,
                                          S_max, bf16, dims_out, stream),
                  "sparq_scan");
@@ -457,7 +483,7 @@ saga_status saga_debug_fallback_rows(const void* workspace, size_t workspace_byt
     saga_status s = check_shape(B, h_q, h_k, h_v, d, S_max, dtype);
     if (s != SAGA_OK) return s;
     if (N < 1) return SAGA_ERR_INVALID_ARG;
-    const saga::Workspace need = saga::carve(nullptr, B, h_q, h_k, d, N, S_max, false);
+    const saga::Workspace need = saga::carve_decode(nullptr, B, h_q, h_k, d, N, S_max);
     if (workspace_bytes < need.bytes) return SAGA_ERR_WORKSPACE;
     const size_t rows = (size_t)B * (size_t)h_q;
     if (!saga::use_union_path(h_q, h_k, S_max)) {
@@ -465,7 +491,7 @@ saga_status saga_debug_fallback_rows(const void* workspace, size_t workspace_byt
         return SAGA_OK;
     }
     const saga::Workspace w =
-        saga::carve(const_cast<void*>(workspace), B, h_q, h_k, d, N, S_max, false);
+        saga::carve_decode(const_cast<void*>(workspace), B, h_q, h_k, d, N, S_max);
     clear_stale_error();
     if (hipMemcpyAsync(host_flags, w.row_flag, rows * sizeof(int32_t), hipMemcpyDeviceToHost,
                        stream) != hipSuccess ||

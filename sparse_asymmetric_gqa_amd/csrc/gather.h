@@ -75,6 +75,53 @@ struct Gather {
         }
     }
 
+    // Sums of acc over the workgroup, written to dst[0 .. DH) (global memory,
+    // not yet divided by l) with device-scope stores, which write through the
+    // XCD's L2: one part of a row whose kept list is gathered by several
+    // workgroups. red: LDS [NW][DH] floats.
+    __device__ static void partial(float (&acc)[EPL], float* red, float* dst) {
+        const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+        const int rg = lane / LPR;
+        const int sub = lane - rg * LPR;
+#pragma unroll
+        for (int off = LPR; off < 64; off <<= 1)
+#pragma unroll
+            for (int c = 0; c < EPL; ++c) acc[c] += __shfl_xor(acc[c], off, 64);
+        if (rg == 0)
+#pragma unroll
+            for (int c = 0; c < EPL; ++c) red[wave * DH + sub * EPL + c] = acc[c];
+        __syncthreads();
+        for (int c = tid; c < DH; c += kGatherThreads) {
+            float sacc = 0.f;
+#pragma unroll
+            for (int w = 0; w < NW; ++w) sacc += red[w * DH + c];
+            __hip_atomic_store(dst + c, sacc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
+
+    // The row's output from its nparts partial sums src[p][DH] (written by
+    // other workgroups with device-scope stores, read here with device-scope
+    // loads, which do not hit a stale line of this XCD's L2), added in part
+    // order: out[c] = (sum_p src[p][c]) / l, with l reduced from the threads'
+    // shares lsum as in finish(). red: LDS [NW] floats.
+    __device__ static void merge(float lsum, float* red, const float* src, int nparts, float* o) {
+        const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) lsum += __shfl_xor(lsum, off, 64);
+        if (lane == 0) red[wave] = lsum;
+        __syncthreads();
+        float l = 0.f;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) l += red[w];
+        for (int c = tid; c < DH; c += kGatherThreads) {
+            float sacc = 0.f;
+            for (int p = 0; p < nparts; ++p)
+                sacc += __hip_atomic_load(src + p * DH + c, __ATOMIC_RELAXED,
+                                          __HIP_MEMORY_SCOPE_AGENT);
+            o[c] = sacc / l;
+        }
+    }
+
     // out[c] = (sum of acc over the workgroup)[c] / l; lsum is each thread's
     // share of l (summed in a fixed order). red: LDS [NW][DH] + [NW] floats.
     // With vm (nullable, [DH]): out[c] = alpha (sum / l) + (1 - alpha) vm[c].
@@ -108,6 +155,57 @@ struct Gather {
         }
     }
 };
+
+// The value gather of one row whose kept list is staged in LDS: positions
+// st_idx and softmax weights st_w for entries [0, n), zero weights (position
+// 0) on [n, nst), nst a multiple of Gather::BATCH. With nsplit == 1 the
+// workgroup gathers the whole list and writes o = sum / l. With nsplit > 1
+// it is part `part` of the row: it gathers the slice of whole batches
+// [part * per, (part + 1) * per) of the list, stores its partial sums in
+// split_part [row][nsplit][DH], and the part that finishes last (counted in
+// split_cnt[row], which starts at 0) adds the partials in part order and
+// writes o, so the bits do not depend on which part that is. l is summed from
+// the staged weights slot by slot in every part. red: LDS [NW][DH] + [NW]
+// floats; bcast: one LDS word. Every thread of the workgroup calls this.
+// The parts hand over through device-scope accesses only: the partial sums
+// are stored at device scope and every store has completed (vmcnt 0) before
+// the part's counter increment is issued; the last part reads them at device
+// scope after its increment returned. (An agent-scope fence would also write
+// back and invalidate the whole L2 of the XCD, which costs every workgroup
+// on it far more than these few hundred bytes.)
+template <typename T, int DH>
+__device__ __forceinline__ void gather_staged(const T* __restrict__ vb, const int32_t* st_idx, const float* st_w,
+                              int n, int nst, float* red, uint32_t* bcast, int row, int part,
+                              int nsplit, float* __restrict__ split_part,
+                              int32_t* __restrict__ split_cnt, float* __restrict__ o) {
+    using G = Gather<T, DH>;
+    const int tid = threadIdx.x;
+    float lsum = 0.f;
+    for (int j = tid; j < nst; j += kGatherThreads) lsum += st_w[j];
+    float acc[G::EPL];
+#pragma unroll
+    for (int c = 0; c < G::EPL; ++c) acc[c] = 0.f;
+    if (nsplit == 1) {
+        G::run(vb, st_idx, st_w, n, acc);
+        G::finish(acc, lsum, red, o);
+        return;
+    }
+    // whole batches per part, so that the gather's reads past a slice stay
+    // inside the staged, zero-weighted entries
+    const int per = ((n + nsplit - 1) / nsplit + G::BATCH - 1) / G::BATCH * G::BATCH;
+    const int e_lo = part * per < n ? part * per : n;
+    const int e_hi = e_lo + per < n ? e_lo + per : n;
+    G::run(vb, st_idx + e_lo, st_w + e_lo, e_hi - e_lo, acc);
+    G::partial(acc, red, split_part + ((int64_t)row * nsplit + part) * DH);
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this thread's stores have completed
+    __syncthreads();                      // ... and every other thread's
+    if (tid == 0)
+        *bcast = (uint32_t)__hip_atomic_fetch_add(split_cnt + row, 1, __ATOMIC_RELAXED,
+                                                  __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    if (*bcast == (uint32_t)(nsplit - 1))   // uniform: the last part merges
+        G::merge(lsum, red, split_part + (int64_t)row * nsplit * DH, nsplit, o);
+}
 
 // Dot products of gathered key rows with two query vectors, in the lane layout
 // of Gather: for each entry e < n of the LDS list pos, za[e] = <qa, K[pos[e]]>

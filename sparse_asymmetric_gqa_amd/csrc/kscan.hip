@@ -131,19 +131,20 @@ __global__ __launch_bounds__(256) void kscan(const T* __restrict__ q, const T* _
 //   stg  [..]                 staged candidate lists (uint2), the rest of the LDS
 template <typename T>
 constexpr bool topm_xp() { return sizeof(T) == 2; }
-template <typename T, int DH>
+template <typename T, int DH, int C>
 __host__ __device__ constexpr size_t topm_lds_words(int g) {
     // every area starts 16-byte aligned
-    return (size_t)2 * g * kKeyRow + ((g + 4 + 3) & ~3) + 5 * kMetaStage +
+    return (size_t)2 * g * key_row<C>() + ((g + 4 + 3) & ~3) + 5 * kMetaStage +
            (topm_xp<T>() ? (size_t)kWaves * 16 * DH * sizeof(T) / 4 : 0);
 }
 
-template <typename T, int DH>
+template <typename T, int DH, int C>
 __global__ __launch_bounds__(kTopmThreads, 1) void kscan_topm(
         const T* __restrict__ q, const T* __restrict__ k, const int32_t* __restrict__ lens,
         int h_q, int h_k, int64_t S_max, int nchunk, int nwork, float scale, TopmOut tm,
         uint32_t lds_bytes) {
     using S = Streamer<T, DH, 1, topm_xp<T>()>;
+    constexpr int KR = key_row<C>();
     constexpr int NS = S::NS;
     extern __shared__ uint32_t lds[];
     const int g = h_q / h_k;
@@ -151,22 +152,25 @@ __global__ __launch_bounds__(kTopmThreads, 1) void kscan_topm(
     const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));   // wave-uniform
     const bool producer = wave < kWaves;
     uint32_t* keys = lds;
-    uint32_t* warm = lds + 2 * g * kKeyRow;
+    uint32_t* warm = lds + 2 * g * KR;
     uint32_t* cursor = warm + g;   // cursor[0]: next free entry, cursor[1]: end of staged lists
-    uint32_t* meta_words = lds + 2 * g * kKeyRow + ((g + 4 + 3) & ~3);
+    uint32_t* meta_words = lds + 2 * g * KR + ((g + 4 + 3) & ~3);
     uint32_t* xtile_words = meta_words + 5 * kMetaStage;
-    const uint32_t fixed_words = (uint32_t)topm_lds_words<T, DH>(g);
+    const uint32_t fixed_words = (uint32_t)topm_lds_words<T, DH, C>(g);
 
+    // counters the next kernel of the call relies on starting at zero
+    if (tm.zero && blockIdx.x == 0)
+        for (int j = (int)threadIdx.x; j < tm.nzero; j += kTopmThreads) tm.zero[j] = 0;
     // The workgroup takes a contiguous range of items (consecutive chunks of a
     // row), so that each head's previous cutoff is a good first guess.
     const int per = (nwork + gridDim.x - 1) / gridDim.x;
     const int wbeg = blockIdx.x * per;
     const int wend = wbeg + per < nwork ? wbeg + per : nwork;
     if (wbeg >= wend) return;   // uniform over the workgroup
-    // The workgroup's pool range is the regions of its items (g kScanChunk
-    // entries each); its lists are packed from the start of that range.
+    // The workgroup's pool range is the regions of its items (g C entries
+    // each); its lists are packed from the start of that range.
     ListSink sink;
-    sink.base = (uint64_t)wbeg * g * kScanChunk;
+    sink.base = (uint64_t)wbeg * g * C;
     sink.pool = tm.cand + sink.base;
     sink.stg = reinterpret_cast<uint2*>(lds + fixed_words);
     sink.cap = ((lds_bytes / 4 - fixed_words) / 2) & ~1u;
@@ -177,7 +181,7 @@ __global__ __launch_bounds__(kTopmThreads, 1) void kscan_topm(
     auto len_of = [&](int b) { return lens[b]; };   // uniform index: a scalar load
 
     Item<T> cur;
-    int w = next_item<T, DH>(wbeg, 1, wend, nchunk, h_k, S_max, len_of, k, cur);
+    int w = next_item<T, DH, C>(wbeg, 1, wend, nchunk, h_k, S_max, len_of, k, cur);
     if (w >= wend) return;   // uniform over the workgroup
     S sm(wave, lane,
          reinterpret_cast<u32x4*>(xtile_words) + (wave < kWaves ? wave : 0) * (S::TILE_BYTES / 16));
@@ -204,12 +208,12 @@ __global__ __launch_bounds__(kTopmThreads, 1) void kscan_topm(
         const bool have_cur = w < wend;
         if (!have_cur && !have_prev) break;   // uniform
         Item<T> nx = cur;
-        const int wn = have_cur ? next_item<T, DH>(w + 1, 1, wend, nchunk, h_k, S_max, len_of, k,
+        const int wn = have_cur ? next_item<T, DH, C>(w + 1, 1, wend, nchunk, h_k, S_max, len_of, k,
                                                    nx)
                                 : wend;
         if (producer && have_cur) {
             {
-                uint32_t* kbuf = keys + (t & 1) * g * kKeyRow;
+                uint32_t* kbuf = keys + (t & 1) * g * KR;
                 {
                     const int n = sm.r16;   // next item's query operand (nx == cur after the last)
 #pragma unroll
@@ -229,14 +233,14 @@ __global__ __launch_bounds__(kTopmThreads, 1) void kscan_topm(
                         u32x4 kv;
 #pragma unroll
                         for (int e = 0; e < 4; ++e) kv[e] = (e < rem) ? float_key(acc[e]) : 0u;
-                        *reinterpret_cast<u32x4*>(&kbuf[sm.r16 * kKeyRow + off]) = kv;
+                        *reinterpret_cast<u32x4*>(&kbuf[sm.r16 * KR + off]) = kv;
                     }
                 };
                 // Every stage of the chunk runs, so each key row is fully
                 // rewritten; rows past the chunk clamp to its last row (cache
                 // hits). The first round is peeled off the loop (it waits for
                 // the query operand); the last round loads the next item.
-                constexpr int nst = kScanChunk / S::STAGE;
+                constexpr int nst = C / S::STAGE;
                 static_assert(nst % NS == 0 && nst >= 2 * NS, "chunk must span >= 2 rounds");
                 auto round = [&](int st) {
 #pragma unroll
@@ -263,16 +267,16 @@ __global__ __launch_bounds__(kTopmThreads, 1) void kscan_topm(
             // M: 1.5 times the chunk's expected share of the row's top N, plus
             // a margin (a heuristic: any M gives exact results, M only sets
             // how often the selector has to recompute a head)
-            const float share = (float)tm.N * (float)kScanChunk / (float)prev.L;
-            const uint32_t M = share >= (float)(kScanChunk / 2)
-                                   ? (uint32_t)kScanChunk
+            const float share = (float)tm.N * (float)C / (float)prev.L;
+            const uint32_t M = share >= (float)(C / 2)
+                                   ? (uint32_t)C
                                    : (uint32_t)__builtin_ceilf(1.5f * share) + 16u;
-            uint32_t* kbuf = keys + ((t + 1) & 1) * g * kKeyRow;
+            uint32_t* kbuf = keys + ((t + 1) & 1) * g * KR;
             const int first = have_cur ? wave - kWaves : wave;
             const int step = have_cur ? kConsumers : kWaves + kConsumers;
 #pragma unroll 1
             for (int n = first; n < g; n += step)
-                extract(prev, n, M, kbuf + n * kKeyRow, warm, sink, t - 1, lane, g, h_q,
+                extract<T, C>(prev, n, M, kbuf + n * KR, warm, sink, t - 1, lane, g, h_q,
                         nchunk, tm, prev.L);
         }
         lds_barrier();   // keys of item t are complete; buffer (t - 1) & 1 is free again
@@ -318,17 +322,17 @@ hipError_t go_dense(int nht, const void* q, const void* k, const int32_t* lens, 
     return hipGetLastError();
 }
 
-template <typename T, int DH>
+template <typename T, int DH, int C>
 hipError_t go_topm(const void* q, const void* k, const int32_t* lens, const TopmOut& tm, int B,
                    int h_q, int h_k, int64_t S_max, hipStream_t st, hipEvent_t ev0,
                    hipEvent_t ev1) {
-    const int nchunk = (int)((S_max + kScanChunk - 1) / kScanChunk);
+    const int nchunk = (int)((S_max + C - 1) / C);
     const int nwork = B * h_k * nchunk;
     const float scale = (float)(1.0 / __builtin_sqrt((double)DH));
-    auto kern = &kscan_topm<T, DH>;
+    auto kern = &kscan_topm<T, DH, C>;
     // the whole LDS: the key buffers, and the rest stages candidate lists
     const size_t lds = kTopmLdsBytes;
-    static_assert(topm_lds_words<T, DH>(16) * 4 + 8 * 1024 <= kTopmLdsBytes,
+    static_assert(topm_lds_words<T, DH, C>(16) * 4 + 8 * 1024 <= kTopmLdsBytes,
                   "staging area too small");
     {   // allow > 64 KiB of dynamic LDS
         const hipError_t e = allow_dynamic_lds(reinterpret_cast<const void*>(kern), lds);
@@ -363,11 +367,13 @@ hipError_t launch_kscan(const void* q, const void* k, const int32_t* lens, float
 hipError_t launch_kscan_topm(const void* q, const void* k, const int32_t* lens, const TopmOut& tm,
                              int B, int h_q, int h_k, int d, int64_t S_max, bool bf16,
                              hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
-    if (bf16)
-        return d == 64 ? go_topm<uint16_t, 64>(q, k, lens, tm, B, h_q, h_k, S_max, st, ev0, ev1)
-                       : go_topm<uint16_t, 128>(q, k, lens, tm, B, h_q, h_k, S_max, st, ev0, ev1);
-    return d == 64 ? go_topm<float, 64>(q, k, lens, tm, B, h_q, h_k, S_max, st, ev0, ev1)
-                   : go_topm<float, 128>(q, k, lens, tm, B, h_q, h_k, S_max, st, ev0, ev1);
+#define SAGA_TM(T, D)                                                                       \
+    (tm.chunk == 256 ? go_topm<T, D, 256>(q, k, lens, tm, B, h_q, h_k, S_max, st, ev0, ev1)   \
+                     : go_topm<T, D, kScanChunk>(q, k, lens, tm, B, h_q, h_k, S_max, st, ev0, ev1))
+    if (tm.chunk != 256 && tm.chunk != kScanChunk) return hipErrorInvalidValue;
+    if (bf16) return d == 64 ? SAGA_TM(uint16_t, 64) : SAGA_TM(uint16_t, 128);
+    return d == 64 ? SAGA_TM(float, 64) : SAGA_TM(float, 128);
+#undef SAGA_TM
 }
 
 }  // namespace saga

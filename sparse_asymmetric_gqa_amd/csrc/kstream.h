@@ -70,9 +70,9 @@ struct Item {
     int L, c0, n;      // cached length, first position, positions in the chunk
 };
 
-// First work item at or after w (stepping by `step`) whose chunk starts inside
-// its row; returns nwork when there is none.
-template <typename T, int DH, typename LenOf>
+// First work item at or after w (stepping by `step`) whose chunk of C
+// positions starts inside its row; returns nwork when there is none.
+template <typename T, int DH, int C = kScanChunk, typename LenOf>
 __device__ inline int next_item(int w, int step, int nwork, int nchunk, int h_k, int64_t S_max,
                                 LenOf&& len_of, const T* __restrict__ k, Item<T>& it) {
     for (; w < nwork; w += step) {
@@ -81,9 +81,9 @@ __device__ inline int next_item(int w, int step, int nwork, int nchunk, int h_k,
         it.b = it.bkh / h_k;
         it.kh = it.bkh - it.b * h_k;
         it.L = (int)clamp_len(len_of(it.b), S_max);
-        it.c0 = it.chunk * kScanChunk;
+        it.c0 = it.chunk * C;
         if (it.c0 < it.L) {
-            it.n = it.L - it.c0 < kScanChunk ? it.L - it.c0 : kScanChunk;
+            it.n = it.L - it.c0 < C ? it.L - it.c0 : C;
             it.kb = k + ((int64_t)it.bkh * S_max + it.c0) * DH;
             return w;
         }

@@ -23,7 +23,7 @@ inline int64_t score_stride(int64_t S_max) { return round_up(S_max, 16); }
 
 struct Workspace {
     float* scores;      // [B][h_q][score_stride]  logits (decode: wide key groups, fallback rows)
-    uint2* cand;        // candidate pool: B*h_k*nchunk items x g*kScanChunk entries
+    uint2* cand;        // candidate pool: B*h_k*nchunk items x g*chunk entries
     uint4* cand_meta;   // [B][h_q][nchunk]  {pool offset lo, count, cutoff, pool offset hi}
     float2* cand_stat;  // [B][h_q][nchunk]  {max logit, sum exp(logit - max)} (Atop-N)
     int32_t* row_flag;  // [B][h_q]   1 if the row took the dense fallback in the last call
@@ -32,6 +32,10 @@ struct Workspace {
     float* row_max;     // [B][h_q]   largest kept logit
     int32_t* row_cnt;   // [B][h_q]   N_eff
     float* part;        // dense: [B][h_q][nchunk][d + 2]  (m, l, acc[d]) per chunk
+    float* split_part;  // [B][h_q][nsplit][d]  value-gather partial sums (nsplit > 1)
+    int32_t* split_cnt; // [B][h_q]   parts of a row finished (nsplit > 1)
+    int chunk;          // positions per K-scan work item
+    int nsplit;         // value-gather workgroups per (b, i) row
     size_t bytes;
 };
 
@@ -43,17 +47,43 @@ struct SparqWs {
     float* qm;         // [B*h_q][d]    q / tau on the dims, 0 elsewhere
 };
 
-inline int num_chunks(int64_t S_max) { return (int)((S_max + kScanChunk - 1) / kScanChunk); }
+inline int num_chunks(int64_t S_max, int chunk = kScanChunk) {
+    return (int)((S_max + chunk - 1) / chunk);
+}
+
+// Positions per work item of the top-M K-scan: 1024, or 256 when a call has
+// fewer than 256 items of 1024 positions (too few to occupy the CUs) and its
+// rows fit in 256 chunks of 256.
+inline int topm_chunk(int B, int h_k, int64_t S_max) {
+    const int64_t items = (int64_t)B * h_k * num_chunks(S_max);
+    return (items < 256 && S_max <= 256 * 256) ? 256 : kScanChunk;
+}
+
+// Workgroups per (b, i) row of the fused select + value gather: rows are
+// split along their kept list when there are too few of them to occupy the
+// CUs (each part gathers a slice; the last part to finish merges the sums).
+constexpr int kMaxSplit = 8;
+inline int gather_split(int B, int h_q) {
+    const int rows = B * h_q;
+    const int p = rows >= 512 ? 1 : 512 / rows;
+    return p < kMaxSplit ? p : kMaxSplit;
+}
 
 // Whether saga_decode_attn takes the top-M K-scan + union select path.
 bool use_union_path(int h_q, int h_k, int64_t S_max);
 int max_union_chunks();
 
 // Carve the decode workspace (dense == false) or the dense one out of `base`
-// (base may be null to only compute the size). With sq, the SparQ state
+// (base may be null to only compute the size), for K-scan items of `chunk`
+// positions and `nsplit` value-gather parts per row. With sq, the SparQ state
 // follows the decode part (esize: bytes per cache element).
 Workspace carve(void* base, int B, int h_q, int h_k, int d, int N, int64_t S_max, bool dense,
-                SparqWs* sq = nullptr, int esize = 2);
+                int chunk, int nsplit, SparqWs* sq = nullptr, int esize = 2);
+
+// The decode workspace (chunk and split from the shape) and the Atop-N one
+// (2N kept slots per row).
+Workspace carve_decode(void* base, int B, int h_q, int h_k, int d, int N, int64_t S_max);
+Workspace carve_atopn(void* base, int B, int h_q, int h_k, int d, int N, int64_t S_max);
 
 // Dense attention: positions per work item for a key group of g query heads,
 // and chunks (partials) per (b, i) row.
@@ -62,7 +92,7 @@ int dense_nsplit(int64_t S_max, int g);   // ceil(S_max / dense_chunk(g))
 
 // Candidate lists published by the top-M K-scan. The workgroup that takes
 // work items [w0, w1) packs the lists of their heads, in any order, from pool
-// entry w0 * g * kScanChunk on (the items' regions bound the total). For slot
+// entry w0 * g * chunk on (the items' regions bound the total). For slot
 // (b*h_q + i, chunk): meta = {off_lo, cnt, cut, off_hi} with the list at
 // cand[off, off + cnt) = (position, key) ascending in position, off the 64-bit
 // absolute pool index, and cut = the chunk's cutoff key (every key of the
@@ -72,6 +102,9 @@ struct TopmOut {
     uint4* meta;       // [B*h_q][nchunk]
     int N;             // the M of each chunk's list is sized for this N
     float2* stat;      // nullable: [B*h_q][nchunk] {max logit, sum of exp(logit - max)}
+    int chunk;         // positions per work item (kScanChunk or 256)
+    int32_t* zero;     // nullable: nzero ints the K-scan clears before anything else
+    int nzero;
 };
 
 // ---- host-side launch caches (launch.hip; thread-safe, per current device) ----
@@ -97,36 +130,34 @@ hipError_t launch_select(const float* scores, int64_t s_stride, const int32_t* l
                          int h_q, int N, int64_t S_max, int32_t* sel_idx, float* sel_val,
                          float* row_max, int32_t* row_cnt, int32_t* idx_out, hipStream_t st);
 
-hipError_t launch_select_union(const TopmOut& tm, const int32_t* lens, int B, int h_q, int h_k,
-                               int d, int N, int64_t S_max, int32_t* sel_idx, float* sel_val,
-                               float* row_max, int32_t* row_cnt, int32_t* idx_out,
-                               int32_t* row_flag, const void* q, const void* k, float* scores,
-                               int64_t s_stride, bool bf16, hipStream_t st);
 
-// Atop-N stale-threshold selection (lists from launch_kscan_topm with stat):
-// keeps the positions with logit >= log(tau) + LSE, the first cap in position
-// order, into sel_idx / sel_val [B*h_q][cap]; count_out (nullable) gets the
-// count before the cap.
+
+// Atop-N stale-threshold selection fused with the value gather (lists from
+// launch_kscan_topm with stat): keeps the positions with logit >= log(tau) +
+// LSE, the first cap in position order, and writes out[B*h_q][d] (0 for a
+// row keeping none). idx_out (nullable) [B*h_q][cap]; count_out (nullable)
+// gets the count before the cap; sel_idx / sel_val [B*h_q][cap] serve rows
+// that recompute their logits. nsplit, split_part, split_cnt as for
+// launch_select_pv (tm.zero clears split_cnt).
 hipError_t launch_select_thresh(const TopmOut& tm, const int32_t* lens, const float* tau, int B,
-                                int h_q, int h_k, int d, int cap, int64_t S_max, int32_t* sel_idx,
-                                float* sel_val, float* row_max, int32_t* row_cnt,
-                                int32_t* idx_out, int32_t* count_out, int32_t* row_flag,
-                                const void* q, const void* k, float* scores, int64_t s_stride,
-                                bool bf16, hipStream_t st);
+                                int h_q, int h_k, int h_v, int d, int cap, int64_t S_max,
+                                int32_t* sel_idx, float* sel_val, int32_t* idx_out,
+                                int32_t* count_out, int32_t* row_flag, const void* q,
+                                const void* k, const void* v, float* scores, int64_t s_stride,
+                                float* out, bool bf16, int nsplit, float* split_part,
+                                int32_t* split_cnt, hipStream_t st);
 
-// Atop-N calibration after an exact top-N select: tau = exp(T - LSE) per row.
-hipError_t launch_atopn_tau(const float* sel_val, const int32_t* row_cnt, const TopmOut& tm,
-                            const int32_t* lens, int B, int h_q, int N, int64_t S_max, float* tau,
-                            hipStream_t st);
+
 
 // Union select fused with the value gather: writes out[B][h_q][d] directly
-// (sel_idx / sel_val only for rows the general code takes).
+// (sel_idx / sel_val only for rows the general code takes). With tau (and
+// tm.stat from the K-scan) also the Atop-N calibration tau [B*h_q].
 hipError_t launch_select_pv(const TopmOut& tm, const int32_t* lens, int B, int h_q, int h_k,
                             int h_v, int d, int N, int64_t S_max, int32_t* sel_idx,
                             float* sel_val, float* row_max, int32_t* row_cnt, int32_t* idx_out,
                             int32_t* row_flag, const void* q, const void* k, const void* v,
-                            float* scores, int64_t s_stride, float* out, bool bf16,
-                            hipStream_t st);
+                            float* scores, int64_t s_stride, float* out, bool bf16, int nsplit,
+                            float* split_part, int32_t* split_cnt, float* tau, hipStream_t st);
 
 // SparQ-style scoring (h_q / h_k <= 16): the set-up kernel (dims, 1 / tau,
 // qm, the scan operand; dims_out nullable [B*h_k][r]) and the scan of the r

@@ -436,7 +436,7 @@ __device__ void union_row(
     float* __restrict__ row_max, int32_t* __restrict__ row_cnt, int32_t* __restrict__ idx_out,
     int32_t* __restrict__ row_flag, const T* __restrict__ q, const T* __restrict__ k,
     float* __restrict__ scores, int64_t s_stride, float scale, int64_t L, int n_eff,
-    const float* qf) {
+    const float* qf, int chunk) {
     constexpr int NT = kUnionThreads;
     constexpr int NW = NT / 64;
     constexpr int KPT = kUnionKPT;
@@ -464,7 +464,7 @@ __device__ void union_row(
         }
         return;
     }
-    const int nch = (int)((L + kScanChunk - 1) / kScanChunk);
+    const int nch = (int)((L + chunk - 1) / chunk);
     const uint4* meta = cand_meta + (int64_t)row * nchunk;
 
     // exclusive prefix of the chunk counts: each thread sums a contiguous run
@@ -592,6 +592,20 @@ __device__ inline RowStats row_stats(const float2* __restrict__ stat, const uint
     return r;
 }
 
+// Atop-N calibration of one row (all threads of the workgroup): tau = exp(T -
+// LSE) with T the smallest kept logit, LSE from the row's chunk statistics;
+// NaN when nothing is kept. Written by thread 0 when `write`.
+__device__ inline void calib_tau(const float2* __restrict__ stat, const uint4* __restrict__ meta,
+                                 int nch, float T, bool any, uint4* red, float* redf, float* tau,
+                                 bool write) {
+    float t = __builtin_nanf("");
+    if (any) {   // uniform
+        const RowStats rs = row_stats(stat, meta, nch, red, redf);
+        t = __expf(T - rs.lse);
+    }
+    if (write && threadIdx.x == 0) *tau = t;
+}
+
 // ---- union select, one workgroup per row -------------------------------------------
 // Fast path, for rows of at most 256 chunks. tpc = floor(256 / chunks) threads
 // share each chunk's list: thread t takes chunk t / tpc and, within it, a run
@@ -630,6 +644,13 @@ __host__ __device__ constexpr size_t select_stage_offset() {
 // SparQ-style inputs of the select (MODE 2; empty for the other modes, so
 // they carry no extra kernel arguments).
 template <int MODE> struct SqArg {};
+// The fused decode step (MODE 1) as an Atop-N calibration step: with tau set,
+// the row's tau = exp(T - LSE) is written as well, T the smallest kept logit
+// and LSE the log-sum-exp of all logits from the chunk statistics.
+template <> struct SqArg<1> {
+    const float2* stat;     // nullable [rows][nchunk] chunk softmax statistics
+    float* tau;             // nullable [rows]
+};
 template <> struct SqArg<2> {
     const float* qm;        // [rows][DH] q / tau on the kept dims (the approximate logits)
     const float2* stat;     // [rows][nchunk] chunk softmax statistics of those logits
@@ -653,7 +674,14 @@ __device__ inline const float* sq_qm(const SqArg<2>& a, int row, int dh) {
 // code write their list to memory first and read it back after a fence.
 // Dynamic LDS with FUSE adds the gather's reduction area after the staging:
 // nst a multiple of 256 and max(sizeof(UnionShared), select_stage_offset() +
-// 8 nst + 4 (4 DH + 4)) bytes.
+// 8 nst + 4 (4 DH + 4)) bytes. With nsplit > 1 (few rows) each row has
+// nsplit workgroups: all of them run the same selection, each gathers its
+// slice of the kept list (whole gather batches, in position order) and
+// stores its partial sums in split_part [rows][nsplit][DH]; the part that
+// finishes last (split_cnt, cleared by the K-scan of the same call) adds
+// the partials in part order and writes the row, so the result does not
+// depend on which part finishes last. Rows of the general code are done
+// whole by part 0.
 // MODE 2 (SparQ): the candidates rank approximate logits over the first
 // L - min(local, L) positions, N - local of them are kept and the window is
 // appended; the kept key rows are then gathered to rescore them exactly
@@ -669,7 +697,8 @@ __global__ __launch_bounds__(kUnionThreads, 4) void select_union(
     int32_t* __restrict__ row_cnt, int32_t* __restrict__ idx_out, int32_t* __restrict__ row_flag,
     const T* __restrict__ q, const T* __restrict__ k, float* __restrict__ scores,
     int64_t s_stride, float scale, const T* __restrict__ v, float* __restrict__ out, int h_v,
-    int rows, SqArg<MODE> sq) {
+    int rows, SqArg<MODE> sq, int chunk, int nsplit, float* __restrict__ split_part,
+    int32_t* __restrict__ split_cnt) {
     static_assert(KPT % 2 == 0, "entries are loaded in pairs");
     constexpr bool FUSE = MODE == 1;
     constexpr bool SPQ = MODE == 2;
@@ -679,8 +708,11 @@ __global__ __launch_bounds__(kUnionThreads, 4) void select_union(
     extern __shared__ __attribute__((aligned(16))) unsigned char sel_lds[];
     FastShared& F = *reinterpret_cast<FastShared*>(sel_lds);
     UnionShared& U = *reinterpret_cast<UnionShared*>(sel_lds);
-    const int row = MODE ? xcd_logical((int)blockIdx.x, rows) : (int)blockIdx.x;
-    if (MODE && row >= rows) return;   // the grid is rounded up to whole XCD shares
+    // the nsplit parts of a row are adjacent logical workgroups
+    const int lid = MODE ? xcd_logical((int)blockIdx.x, rows * nsplit) : (int)blockIdx.x;
+    if (MODE && lid >= rows * nsplit) return;   // the grid is rounded up to whole XCD shares
+    const int row = lid / nsplit;
+    const int part = lid - row * nsplit;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -696,7 +728,7 @@ __global__ __launch_bounds__(kUnionThreads, 4) void select_union(
     const int64_t L = SPQ ? Lrow - (local < Lrow ? local : Lrow) : Lrow;
     const int n_rank = SPQ ? N - local : N;
     const int n_eff = (int)((int64_t)n_rank < L ? (int64_t)n_rank : L);
-    const int nch = (int)((L + kScanChunk - 1) / kScanChunk);
+    const int nch = (int)((L + chunk - 1) / chunk);
     // fused gather: the value head's rows, the staged lists and the reduction area
     const T* vb = v + (int64_t)(b * h_v + (row - b * h_q) / (h_q / h_v)) * S_max * DH;
     int32_t* g_pos = reinterpret_cast<int32_t*>(sel_lds + select_stage_offset());
@@ -705,7 +737,7 @@ __global__ __launch_bounds__(kUnionThreads, 4) void select_union(
     auto general = [&] {
         union_row<T, DH>(row, U, cand, cand_meta, lens, h_q, h_k, N, S_max, nchunk, sel_idx,
                          sel_val, row_max, row_cnt, SPQ ? nullptr : idx_out, row_flag, q, k,
-                         scores, s_stride, scale, L, n_eff, sq_qm(sq, row, DH));
+                         scores, s_stride, scale, L, n_eff, sq_qm(sq, row, DH), chunk);
         if constexpr (FUSE) {
             // the list union_row wrote, read back in blocks of nst entries
             __threadfence();
@@ -715,10 +747,28 @@ __global__ __launch_bounds__(kUnionThreads, 4) void select_union(
                                               __HIP_MEMORY_SCOPE_AGENT);
             if (cnt <= 0) {   // no kept entry (L_b = 0): out = 0
                 for (int c = tid; c < DH; c += NT) o[c] = 0.f;
+                if (sq.tau && tid == 0) sq.tau[row] = __builtin_nanf("");
                 return;
             }
             const float mrow = __hip_atomic_load(row_max + row, __ATOMIC_RELAXED,
                                                  __HIP_MEMORY_SCOPE_AGENT);
+            if (sq.tau) {   // uniform: T is the smallest of the kept logits
+                uint32_t mk = 0xFFFFFFFFu;
+                for (int e = tid; e < cnt; e += NT)
+                    mk = min(mk, float_key(__hip_atomic_load(sel_val + (int64_t)row * N + e,
+                                                             __ATOMIC_RELAXED,
+                                                             __HIP_MEMORY_SCOPE_AGENT)));
+                mk = ~wave_umax(~mk);
+                if (lane == 0) F.scan[wave] = mk;
+                __syncthreads();
+                mk = 0xFFFFFFFFu;
+#pragma unroll
+                for (int w = 0; w < NT / 64; ++w) mk = min(mk, F.scan[w]);
+                __syncthreads();
+                calib_tau(sq.stat + (int64_t)row * nchunk, cand_meta + (int64_t)row * nchunk, nch,
+                          key_float(mk), true, F.red, reinterpret_cast<float*>(F.scan),
+                          sq.tau + row, true);
+            }
             float acc[G::EPL];
 #pragma unroll
             for (int c = 0; c < G::EPL; ++c) acc[c] = 0.f;
@@ -888,11 +938,13 @@ __global__ __launch_bounds__(kUnionThreads, 4) void select_union(
         // fused gather: the staged value is already the softmax weight
         // exp(logit - row max), and the slots past N_eff are cleared here
         const float mrow = key_float(kmax);
+        uint32_t kmin = 0xFFFFFFFFu;   // the smallest kept key (Tk may lie below every key)
     #pragma unroll
         for (int s = 0; s < KPT; ++s) {
             const bool eq = key[s] == Tk;
             const bool keep = key[s] > Tk || (eq && eq_seen < krem);
             eq_seen += eq ? 1u : 0u;
+            kmin = keep && key[s] < kmin ? key[s] : kmin;
             if (keep) {   // slot < N_eff by construction
                 st_idx[slot] = pos[s];
                 if constexpr (FUSE) {
@@ -909,25 +961,32 @@ __global__ __launch_bounds__(kUnionThreads, 4) void select_union(
                 st_val[j] = 0.f;
             }
         __syncthreads();
-        if (tid == 0) {
+        if (tid == 0 && part == 0) {
             row_max[row] = key_float(kmax);
             row_cnt[row] = n_eff;
             row_flag[row] = 0;
         }
         if constexpr (FUSE) {
+            if (sq.tau) {   // uniform: T, the N_eff-th largest logit, is the smallest kept one
+                const uint32_t wm = ~wave_umax(~kmin);
+                if (lane == 0) F.scan[wave] = wm;
+                __syncthreads();
+                uint32_t mk = 0xFFFFFFFFu;
+    #pragma unroll
+                for (int w = 0; w < NT / 64; ++w) mk = min(mk, F.scan[w]);
+                // row_stats writes F.scan only after its first barrier
+                calib_tau(sq.stat + (int64_t)row * nchunk, cand_meta + (int64_t)row * nchunk,
+                          nch, key_float(mk), true, F.red, reinterpret_cast<float*>(F.scan),
+                          sq.tau + row, part == 0);
+            }
             // weights of the staged entries in place; the gather reads positions
             // and weights up to nst (weight 0, row 0 past n_eff)
-            if (ou)
+            if (ou && part == 0)
                 for (int j = tid; j < N; j += NT) ou[j] = j < n_eff ? st_idx[j] : -1;
             // the weights summed slot by slot (the order the unfused value
-            // gather uses, so both give the same bits)
-            float lsum = 0.f;
-            for (int j = tid; j < nst; j += NT) lsum += st_val[j];
-            float acc[G::EPL];
-    #pragma unroll
-            for (int c = 0; c < G::EPL; ++c) acc[c] = 0.f;
-            G::run(vb, st_idx, st_val, n_eff, acc);
-            G::finish(acc, lsum, g_red, out + (int64_t)row * DH);
+            // gather uses, so both give the same bits); nst is whole batches
+            gather_staged<T, DH>(vb, st_idx, st_val, n_eff, nst, g_red, &F.scan[0], row, part,
+                                 nsplit, split_part, split_cnt, out + (int64_t)row * DH);
             return true;
         }
         if constexpr (SPQ) return true;   // the list stays staged for the SparQ tail
@@ -949,7 +1008,10 @@ __global__ __launch_bounds__(kUnionThreads, 4) void select_union(
         return true;
     };
     if constexpr (!SPQ) {
-        if (n_eff == 0 || nch > NT || !fast()) general();   // no kept entry, too many chunks, or no proof
+        // no kept entry, too many chunks, or no proof: the general code, whole
+        // row in part 0 (the decision is the same in every part of the row)
+        if (n_eff == 0 || nch > NT || !fast())
+            if (part == 0) general();
         return;
     } else {
         int32_t* st_idx = g_pos;
@@ -984,7 +1046,7 @@ __global__ __launch_bounds__(kUnionThreads, 4) void select_union(
         }
         // log-sum-exp of the approximate logits over all L_b positions
         float* sred = g_red + 4 * DH + 4;   // [4] uint4 + [4] + [8] floats past the gather's area
-        const int nchr = (int)((Lrow + kScanChunk - 1) / kScanChunk);
+        const int nchr = (int)((Lrow + chunk - 1) / chunk);
         const RowStats rs = row_stats(sq.stat + (int64_t)row * nchunk,
                                       cand_meta + (int64_t)row * nchunk, nchr,
                                       reinterpret_cast<uint4*>(sred), sred + 16);
@@ -1059,56 +1121,93 @@ __host__ __device__ constexpr size_t thresh_stage_offset() {
     return (sizeof(ThreshShared) + 15) & ~(size_t)15;
 }
 
-// Stale-threshold selection, one workgroup per (b, i) row. cap = 2N output
-// slots per row. Fast path: the row's chunk lists are complete for the
-// threshold (every chunk cutoff <= theta: every key a chunk left out is below
-// its cutoff), at most 256 chunks, and runs of at most KPT entries per
-// thread (the layout of select_union); keys >= theta are counted, slotted by
-// one workgroup prefix scan (position order) and the first cap written.
-// Otherwise the head's logits are recomputed over all L positions and the
-// same rule applied to them (row_flag = 1). count_out = positions reaching
-// the threshold before the cap; a row keeping none gets row_cnt = 0.
-// Dynamic LDS: max(sizeof(UnionShared), thresh_stage_offset() + 8 cap4).
+// Stale-threshold selection fused with the value gather, one workgroup per
+// (b, i) row (nsplit per row when there are few rows, as for the exact
+// step). cap = 2N kept slots per row. Fast path: the row's chunk lists are
+// complete for the threshold (every chunk cutoff <= theta: every key a chunk
+// left out is below its cutoff), at most 256 chunks, and runs of at most KPT
+// entries per thread (the layout of select_union): the keys >= theta are
+// counted and slotted by one workgroup prefix scan in position order, the
+// first cap staged in LDS as positions and softmax weights (shifted by the
+// largest kept logit), and gathered (gather_staged). Otherwise part 0
+// recomputes the head's logits over all L positions, applies the same rule
+// (row_flag = 1), writes the list to sel_idx / sel_val [rows][cap], reads it
+// back into the staging and gathers it alone. count_out = positions reaching
+// the threshold before the cap; a row keeping none gets out = 0. idx_out
+// (nullable) [rows][cap]: the kept positions, -1 padded.
+// Dynamic LDS: max(sizeof(UnionShared), thresh_stage_offset() + 8 nst +
+// 4 (4 DH + 4)) bytes, nst = cap rounded up to 256.
 template <typename T, int DH, int KPT>
 __global__ __launch_bounds__(kUnionThreads, 4) void select_thresh(
     const uint2* __restrict__ cand, const uint4* __restrict__ cand_meta,
     const float2* __restrict__ cand_stat, const int32_t* __restrict__ lens,
-    const float* __restrict__ tau, int h_q, int h_k, int cap, int cap4, int64_t S_max,
-    int nchunk, int32_t* __restrict__ sel_idx, float* __restrict__ sel_val,
-    float* __restrict__ row_max, int32_t* __restrict__ row_cnt, int32_t* __restrict__ idx_out,
-    int32_t* __restrict__ count_out, int32_t* __restrict__ row_flag, const T* __restrict__ q,
-    const T* __restrict__ k, float* __restrict__ scores, int64_t s_stride, float scale) {
+    const float* __restrict__ tau, int h_q, int h_k, int h_v, int cap, int nst, int64_t S_max,
+    int nchunk, int chunk, int32_t* __restrict__ sel_idx, float* __restrict__ sel_val,
+    int32_t* __restrict__ idx_out, int32_t* __restrict__ count_out,
+    int32_t* __restrict__ row_flag, const T* __restrict__ q, const T* __restrict__ k,
+    float* __restrict__ scores, int64_t s_stride, float scale, const T* __restrict__ v,
+    float* __restrict__ out, int rows, int nsplit, float* __restrict__ split_part,
+    int32_t* __restrict__ split_cnt) {
     static_assert(KPT % 2 == 0, "entries are loaded in pairs");
     constexpr int NT = kUnionThreads;
+    static_assert(NT == kGatherThreads, "one gather workgroup per row");
     extern __shared__ __attribute__((aligned(16))) unsigned char thr_lds[];
     ThreshShared& F = *reinterpret_cast<ThreshShared*>(thr_lds);
     UnionShared& U = *reinterpret_cast<UnionShared*>(thr_lds);
-    const int row = blockIdx.x;
+    int32_t* st_idx = reinterpret_cast<int32_t*>(thr_lds + thresh_stage_offset());
+    float* st_w = reinterpret_cast<float*>(st_idx + nst);
+    float* g_red = st_w + nst;
+    const int lid = xcd_logical((int)blockIdx.x, rows * nsplit);
+    if (lid >= rows * nsplit) return;   // the grid is rounded up to whole XCD shares
+    const int row = lid / nsplit;
+    const int part = lid - row * nsplit;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int b = row / h_q;
+    const int i = row - b * h_q;
     const int64_t L = clamp_len(lens[b], S_max);
-    const int nch = (int)((L + kScanChunk - 1) / kScanChunk);
-    int32_t* oi = sel_idx + (int64_t)row * cap;
-    float* ov = sel_val + (int64_t)row * cap;
+    const int nch = (int)((L + chunk - 1) / chunk);
+    const T* vb = v + (int64_t)(b * h_v + i / (h_q / h_v)) * S_max * DH;
+    float* o = out + (int64_t)row * DH;
     int32_t* ou = idx_out ? idx_out + (int64_t)row * cap : nullptr;
-    auto finish = [&](int64_t total, float mx, int flag) {   // padding and row records
-        const int kept = (int)(total < cap ? total : cap);
-        for (int j = kept + tid; j < cap; j += NT) {
-            oi[j] = -1;
-            ov[j] = -__builtin_inff();
-            if (ou) ou[j] = -1;
-        }
+    // the row's records, by part 0: kept positions (staged, nk of them),
+    // the count before the cap, the recompute flag
+    auto records = [&](int nk, int64_t total, int flag) {
+        if (part != 0) return;
+        if (ou)
+            for (int j = tid; j < cap; j += NT) ou[j] = j < nk ? st_idx[j] : -1;
         if (tid == 0) {
-            row_max[row] = mx;
-            row_cnt[row] = kept;
             if (count_out) count_out[row] = (int32_t)(total < 0x7FFFFFFF ? total : 0x7FFFFFFF);
             row_flag[row] = flag;
         }
     };
+    // staged logits [0, nk) -> weights exp(z - largest staged logit); the
+    // rest of the staging (up to nst) zero-weighted at position 0
+    auto weigh = [&](int nk) {
+        uint32_t mk = 0;
+        for (int j = tid; j < nk; j += NT) mk = max(mk, float_key(st_w[j]));
+        mk = wave_umax(mk);
+        if (lane == 0) F.scan[wave] = mk;
+        __syncthreads();
+        mk = 0;
+#pragma unroll
+        for (int w = 0; w < NT / 64; ++w) mk = max(mk, F.scan[w]);
+        const float m = key_float(mk);
+        for (int j = tid; j < nst; j += NT) {
+            if (j < nk) {
+                st_w[j] = __expf(st_w[j] - m);
+            } else {
+                st_idx[j] = 0;
+                st_w[j] = 0.f;
+            }
+        }
+        __syncthreads();
+    };
     if (L == 0) {
-        finish(0, -__builtin_inff(), 0);
+        records(0, 0, 0);
+        if (part == 0)
+            for (int c = tid; c < DH; c += NT) o[c] = 0.f;
         return;
     }
     const uint4* meta = cand_meta + (int64_t)row * nchunk;
@@ -1188,38 +1287,42 @@ __global__ __launch_bounds__(kUnionThreads, 4) void select_thresh(
                 before += w < wave ? F.scan[w] : 0u;
                 total += F.scan[w];
             }
-            int32_t* st_idx = reinterpret_cast<int32_t*>(thr_lds + thresh_stage_offset());
-            float* st_val = reinterpret_cast<float*>(st_idx + cap4);
             uint32_t slot = before;
 #pragma unroll
             for (int e = 0; e < KPT; ++e) {
                 const bool keep = key[e] >= lo;
                 if (keep && slot < (uint32_t)cap) {
                     st_idx[slot] = pos[e];
-                    st_val[slot] = key_float(key[e]);
+                    st_w[slot] = key_float(key[e]);
                 }
                 slot += keep ? 1u : 0u;
             }
-            __syncthreads();
+            __syncthreads();   // every wave has read F.scan and staged its entries
             const int kept = (int)(total < (uint32_t)cap ? total : (uint32_t)cap);
-            for (int j = tid; j < kept; j += NT) {
-                oi[j] = st_idx[j];
-                ov[j] = st_val[j];
-                if (ou) ou[j] = st_idx[j];
+            records(kept, total, 0);
+            if (kept == 0) {   // uniform: nothing reaches the threshold
+                if (part == 0)
+                    for (int cc = tid; cc < DH; cc += NT) o[cc] = 0.f;
+                return;
             }
-            finish(total, M, 0);
+            weigh(kept);
+            gather_staged<T, DH>(vb, st_idx, st_w, kept, nst, g_red, &F.scan[0], row, part,
+                                 nsplit, split_part, split_cnt, o);
             return;
         }
     }
+    // general: part 0 recomputes the head's logits over all L positions and
+    // applies the same rule; the other parts have nothing to do
+    if (part != 0) return;
     const RowStats rs = row_stats(stat, meta, nch, F.red, F.redf);
     const float theta = t == t ? __logf(t) + rs.lse : __builtin_inff();
     const uint32_t lo = float_key(theta) > 1u ? float_key(theta) : 1u;
-    // general: the head's logits over all L positions, then the same rule
     __syncthreads();
     constexpr int KG = kUnionKPT;
     constexpr int NW = NT / 64;
     SelShared& sh = U.sh;
-    const int i = row - b * h_q;
+    int32_t* oi = sel_idx + (int64_t)row * cap;
+    float* ov = sel_val + (int64_t)row * cap;
     float* srow = scores + (int64_t)row * s_stride;
     head_logits<T, DH>(q, k, b, i, h_q, h_k, S_max, L, scale, srow,
                        reinterpret_cast<float*>(sh.hist));
@@ -1232,60 +1335,36 @@ __global__ __launch_bounds__(kUnionThreads, 4) void select_thresh(
 #pragma unroll 1
     for (int tile = 0; tile < ntiles; ++tile) {
         src.load(tile, gk, gp);
-        uint32_t c = 0;
+        uint32_t cc = 0;
 #pragma unroll
-        for (int e = 0; e < KG; ++e) c += gk[e] >= lo ? 1u : 0u;
-        c = wave_sum(c);
-        if (lane == 0) sh.wtot[wave] = c;
+        for (int e = 0; e < KG; ++e) cc += gk[e] >= lo ? 1u : 0u;
+        cc = wave_sum(cc);
+        if (lane == 0) sh.wtot[wave] = cc;
         __syncthreads();
 #pragma unroll
         for (int w = 0; w < NW; ++w) total += sh.wtot[w];
         __syncthreads();
     }
     // keys > lo - 1 = keys >= lo, first cap in position order
-    compact<NT, KG>(src, ntiles, lo - 1u, 0u, (uint32_t)cap, gk, gp, sh, oi, ov, ou);
+    compact<NT, KG>(src, ntiles, lo - 1u, 0u, (uint32_t)cap, gk, gp, sh, oi, ov, nullptr);
+    __threadfence();
     __syncthreads();
-    finish(total, rs.M, 1);
-}
-
-// Calibration: tau = exp(T - LSE) per row, T = the smallest kept logit of the
-// exact top-N step (its N_eff-th largest), LSE from the chunk statistics.
-// Rows with nothing kept get NaN.
-__global__ __launch_bounds__(kUnionThreads) void atopn_tau(
-    const float* __restrict__ sel_val, const int32_t* __restrict__ row_cnt,
-    const float2* __restrict__ cand_stat, const uint4* __restrict__ cand_meta,
-    const int32_t* __restrict__ lens, int h_q, int N, int64_t S_max, int nchunk,
-    float* __restrict__ tau) {
-    __shared__ ThreshShared F;
-    const int row = blockIdx.x;
-    const int tid = threadIdx.x, lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int cnt = row_cnt[row];
-    const int64_t L = clamp_len(lens[row / h_q], S_max);
-    if (cnt <= 0 || L == 0) {   // uniform
-        if (tid == 0) tau[row] = __builtin_nanf("");
+    const int kept = (int)(total < cap ? total : cap);
+    // the list back into the staging (cap <= nst) for the gather
+    for (int j = tid; j < kept; j += NT) {
+        int32_t pp = __hip_atomic_load(oi + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        st_idx[j] = pp < 0 ? 0 : (pp >= L ? (int32_t)(L - 1) : pp);
+        st_w[j] = __hip_atomic_load(ov + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __syncthreads();
+    records(kept, total, 1);
+    if (kept == 0) {
+        for (int cc = tid; cc < DH; cc += NT) o[cc] = 0.f;
         return;
     }
-    const int nch = (int)((L + kScanChunk - 1) / kScanChunk);
-    const RowStats rs = row_stats(cand_stat + (int64_t)row * nchunk, cand_meta + (int64_t)row * nchunk,
-                                  nch, F.red, F.redf);
-    uint32_t mk = 0xFFFFFFFFu;   // smallest kept key
-    for (int j = tid; j < cnt; j += kUnionThreads) {
-        const uint32_t kx = float_key(sel_val[(int64_t)row * N + j]);
-        mk = kx < mk ? kx : mk;
-    }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-        const uint32_t y = (uint32_t)__shfl_xor((int)mk, o, 64);
-        mk = y < mk ? y : mk;
-    }
-    if (lane == 0) F.scan[wave] = mk;
-    __syncthreads();
-    if (tid == 0) {
-#pragma unroll
-        for (int w = 0; w < kUnionThreads / 64; ++w) mk = F.scan[w] < mk ? F.scan[w] : mk;
-        tau[row] = __expf(key_float(mk) - rs.lse);
-    }
+    weigh(kept);
+    gather_staged<T, DH>(vb, st_idx, st_w, kept, nst, g_red, &F.scan[0], row, 0, 1, nullptr,
+                         nullptr, o);
 }
 
 template <int KPT>
@@ -1326,8 +1405,10 @@ hipError_t go_select_union(const TopmOut& tm, const int32_t* lens, int B, int h_
                            float* row_max, int32_t* row_cnt, int32_t* idx_out, int32_t* row_flag,
                            const void* q, const void* k, float* scores, int64_t s_stride,
                            bool bf16, const void* v, float* out, int h_v,
-                           const SqArg<MODE>& sq, hipStream_t st) {
-    const int nchunk = (int)((S_max + kScanChunk - 1) / kScanChunk);
+                           const SqArg<MODE>& sq, int nsplit, float* split_part,
+                           int32_t* split_cnt, hipStream_t st) {
+    const int chunk = tm.chunk;
+    const int nchunk = (int)((S_max + chunk - 1) / chunk);
     const int rows = B * h_q;
     const float scale = (float)(1.0 / __builtin_sqrt((double)d));
     // Register slots per thread for the fast path: the longest run, an even
@@ -1337,9 +1418,9 @@ hipError_t go_select_union(const TopmOut& tm, const int32_t* lens, int B, int h_
     // the general code.
     int n_rank = N;
     if constexpr (MODE == 2) n_rank = N - sq.local;
-    const double share = (double)n_rank * kScanChunk / (double)S_max;
+    const double share = (double)n_rank * chunk / (double)S_max;
     int64_t per_chunk = (int64_t)(1.25 * (1.5 * share + 16.0)) + 1;
-    per_chunk = per_chunk < kScanChunk ? per_chunk : kScanChunk;
+    per_chunk = per_chunk < chunk ? per_chunk : chunk;
     const int64_t tpc = nchunk <= kUnionThreads ? kUnionThreads / nchunk : 1;
     const int64_t slots = (((per_chunk + tpc - 1) / tpc) + 1) & ~(int64_t)1;
     // staged kept entries: N_eff <= N, and <= the 256 KPT keys in registers
@@ -1356,13 +1437,15 @@ hipError_t go_select_union(const TopmOut& tm, const int32_t* lens, int B, int h_
         if (MODE == 2) fast += 32 * sizeof(float);
         return fast > sizeof(UnionShared) ? fast : sizeof(UnionShared);
     };
-    const unsigned grid = MODE ? (unsigned)(((rows + 7) / 8) * 8) : (unsigned)rows;
+    if (MODE != 1) nsplit = 1;
+    const unsigned grid =
+        MODE ? (unsigned)(((rows * nsplit + 7) / 8) * 8) : (unsigned)rows;
 #define SAGA_SU(T, D, KPT)                                                                       \
     hipLaunchKernelGGL((select_union<T, D, KPT, MODE>), dim3(grid), dim3(kUnionThreads),          \
                        (unsigned)lds_for(KPT), st, tm.cand, tm.meta, lens, h_q, h_k, N, S_max,     \
                        nchunk, nst_for(KPT), sel_idx, sel_val, row_max, row_cnt, idx_out, row_flag, \
                        (const T*)q, (const T*)k, scores, s_stride, scale, (const T*)v, out, h_v,   \
-                       rows, sq)
+                       rows, sq, chunk, nsplit, split_part, split_cnt)
 #define SAGA_SU_K(T, D)                                                                          \
     if (slots <= 8) SAGA_SU(T, D, 8);                                                            \
     else if (slots <= 16) SAGA_SU(T, D, 16);                                                     \
@@ -1379,25 +1462,16 @@ hipError_t go_select_union(const TopmOut& tm, const int32_t* lens, int B, int h_
 
 }  // namespace
 
-hipError_t launch_select_union(const TopmOut& tm, const int32_t* lens, int B, int h_q, int h_k,
-                               int d, int N, int64_t S_max, int32_t* sel_idx, float* sel_val,
-                               float* row_max, int32_t* row_cnt, int32_t* idx_out,
-                               int32_t* row_flag, const void* q, const void* k, float* scores,
-                               int64_t s_stride, bool bf16, hipStream_t st) {
-    return go_select_union<0>(tm, lens, B, h_q, h_k, d, N, S_max, sel_idx, sel_val, row_max,
-                              row_cnt, idx_out, row_flag, q, k, scores, s_stride, bf16, nullptr,
-                              nullptr, 1, SqArg<0>{}, st);
-}
-
 hipError_t launch_select_pv(const TopmOut& tm, const int32_t* lens, int B, int h_q, int h_k,
                             int h_v, int d, int N, int64_t S_max, int32_t* sel_idx,
                             float* sel_val, float* row_max, int32_t* row_cnt, int32_t* idx_out,
                             int32_t* row_flag, const void* q, const void* k, const void* v,
-                            float* scores, int64_t s_stride, float* out, bool bf16,
-                            hipStream_t st) {
+                            float* scores, int64_t s_stride, float* out, bool bf16, int nsplit,
+                            float* split_part, int32_t* split_cnt, float* tau, hipStream_t st) {
+    const SqArg<1> cal{tau ? tm.stat : nullptr, tm.stat ? tau : nullptr};
     return go_select_union<1>(tm, lens, B, h_q, h_k, d, N, S_max, sel_idx, sel_val, row_max,
                               row_cnt, idx_out, row_flag, q, k, scores, s_stride, bf16, v, out,
-                              h_v, SqArg<1>{}, st);
+                              h_v, cal, nsplit, split_part, split_cnt, st);
 }
 
 bool sparq_select_fits(int N) { return N >= 1 && N <= kSparqMaxN; }
@@ -1411,40 +1485,42 @@ hipError_t launch_select_sparq(const TopmOut& tm, const SparqWs& sw, const int32
     const SqArg<2> sq{sw.qm, tm.stat, local, vmean, alpha_out};
     return go_select_union<2>(tm, lens, B, h_q, h_k, d, N, S_max, sel_idx, sel_val, row_max,
                               row_cnt, idx_out, row_flag, q, k, scores, s_stride, bf16, v, out,
-                              h_v, sq, st);
+                              h_v, sq, 1, nullptr, nullptr, st);
 }
 
 hipError_t launch_select_thresh(const TopmOut& tm, const int32_t* lens, const float* tau, int B,
-                                int h_q, int h_k, int d, int cap, int64_t S_max, int32_t* sel_idx,
-                                float* sel_val, float* row_max, int32_t* row_cnt,
-                                int32_t* idx_out, int32_t* count_out, int32_t* row_flag,
-                                const void* q, const void* k, float* scores, int64_t s_stride,
-                                bool bf16, hipStream_t st) {
-    const int nchunk = (int)((S_max + kScanChunk - 1) / kScanChunk);
+                                int h_q, int h_k, int h_v, int d, int cap, int64_t S_max,
+                                int32_t* sel_idx, float* sel_val, int32_t* idx_out,
+                                int32_t* count_out, int32_t* row_flag, const void* q,
+                                const void* k, const void* v, float* scores, int64_t s_stride,
+                                float* out, bool bf16, int nsplit, float* split_part,
+                                int32_t* split_cnt, hipStream_t st) {
+    const int chunk = tm.chunk;
+    const int nchunk = (int)((S_max + chunk - 1) / chunk);
     const int rows = B * h_q;
     const float scale = (float)(1.0 / __builtin_sqrt((double)d));
     // registers per thread: as for the union select, the lists sized for tm.N
-    const double share = (double)tm.N * kScanChunk / (double)S_max;
+    const double share = (double)tm.N * chunk / (double)S_max;
     int64_t per_chunk = (int64_t)(1.25 * (1.5 * share + 16.0)) + 1;
-    per_chunk = per_chunk < kScanChunk ? per_chunk : kScanChunk;
+    per_chunk = per_chunk < chunk ? per_chunk : chunk;
     const int64_t tpc = nchunk <= kUnionThreads ? kUnionThreads / nchunk : 1;
     const int64_t slots = (((per_chunk + tpc - 1) / tpc) + 1) & ~(int64_t)1;
-    const int cap4 = (cap + 3) & ~3;
-    size_t lds = thresh_stage_offset() + (size_t)cap4 * 8;
+    const int nst = (int)round_up(cap, 256);
+    size_t lds = thresh_stage_offset() + (size_t)nst * 8 + (size_t)(4 * d + 4) * sizeof(float);
     lds = lds > sizeof(UnionShared) ? lds : sizeof(UnionShared);
+    const unsigned grid = (unsigned)(((rows * nsplit + 7) / 8) * 8);
 #define SAGA_ST(T, D, KPT)                                                                       \
     {                                                                                            \
         auto kern = &select_thresh<T, D, KPT>;                                                   \
         if (lds > 64 * 1024) {                                                                   \
-            const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),        \
-                                                     hipFuncAttributeMaxDynamicSharedMemorySize, \
-                                                     (int)lds);                                  \
+            const hipError_t e = allow_dynamic_lds(reinterpret_cast<const void*>(kern), lds);    \
             if (e != hipSuccess) return e;                                                       \
         }                                                                                        \
-        hipLaunchKernelGGL(kern, dim3((unsigned)rows), dim3(kUnionThreads), (unsigned)lds, st,   \
-                           tm.cand, tm.meta, tm.stat, lens, tau, h_q, h_k, cap, cap4, S_max,     \
-                           nchunk, sel_idx, sel_val, row_max, row_cnt, idx_out, count_out,       \
-                           row_flag, (const T*)q, (const T*)k, scores, s_stride, scale);         \
+        hipLaunchKernelGGL(kern, dim3(grid), dim3(kUnionThreads), (unsigned)lds, st, tm.cand,    \
+                           tm.meta, tm.stat, lens, tau, h_q, h_k, h_v, cap, nst, S_max, nchunk,  \
+                           chunk, sel_idx, sel_val, idx_out, count_out, row_flag, (const T*)q,   \
+                           (const T*)k, scores, s_stride, scale, (const T*)v, out, rows, nsplit, \
+                           split_part, split_cnt);                                               \
     }
 #define SAGA_ST_K(T, D)                                                                          \
     if (slots <= 8) SAGA_ST(T, D, 8)                                                             \
@@ -1460,13 +1536,5 @@ hipError_t launch_select_thresh(const TopmOut& tm, const int32_t* lens, const fl
     return hipGetLastError();
 }
 
-hipError_t launch_atopn_tau(const float* sel_val, const int32_t* row_cnt, const TopmOut& tm,
-                            const int32_t* lens, int B, int h_q, int N, int64_t S_max, float* tau,
-                            hipStream_t st) {
-    const int nchunk = (int)((S_max + kScanChunk - 1) / kScanChunk);
-    hipLaunchKernelGGL(atopn_tau, dim3((unsigned)(B * h_q)), dim3(kUnionThreads), 0, st, sel_val,
-                       row_cnt, tm.stat, tm.meta, lens, h_q, N, S_max, nchunk, tau);
-    return hipGetLastError();
-}
 
 }  // namespace saga

@@ -13,19 +13,20 @@ namespace {
 constexpr int kConsumers = 8;      // extracting waves of kscan_topm
 constexpr int kTopmThreads = 64 * (kWaves + kConsumers);
 // Candidates of one head staged in its own LDS row before the global write:
-// entries [0, kStageMax) hold data, [kStageMax, kStageMax + 64) are per-lane
+// entries [0, stage_max) hold data, [stage_max, stage_max + 64) are per-lane
 // sinks for the branch-free writes of entries that are not kept.
-constexpr uint32_t kStageMax = kScanChunk / 2 - 64;
+template <int C> constexpr uint32_t stage_max() { return C / 2 - 64; }
 // Words per head key row in LDS: one 16-byte slot beyond the chunk, so that
 // the 16 heads written by one 16-lane store start in distinct bank groups
 // (rows exactly 4 KiB apart would put all 16 lanes on one bank).
-constexpr int kKeyRow = kScanChunk + 4;
+template <int C> constexpr int key_row() { return C + 4; }
+constexpr int kKeyRow = key_row<kScanChunk>();
 constexpr size_t kTopmLdsBytes = 160 * 1024;   // LDS of a gfx950 CU: one workgroup per CU
 
 // Candidate extraction of head n of item `it` by one consumer wave, from the
 // head's key row in LDS (every offset of the row was written for this item, 0
-// past the chunk's end). Lane l takes offsets [16 l, 16 l + 16), so lane order
-// is position order. The cutoff is a key with M <= count(key >= cutoff) <=
+// past the chunk's end). Lane l takes offsets [KPL l, KPL l + KPL), KPL = C / 64,
+// so lane order is position order. The cutoff is a key with M <= count(key >= cutoff) <=
 // M + M/4 where one is found within a bracket of 2^12, else the largest probed
 // key with count >= M. The search starts from the cutoff this wave found for
 // the same head on its previous item (the workgroup walks consecutive chunks
@@ -52,14 +53,17 @@ struct ListSink {
 };
 constexpr int kMetaStage = 256;
 
-template <typename T>
+template <typename T, int C = kScanChunk>
 __device__ inline void extract(const Item<T>& it, int n, uint32_t M, uint32_t* row,
                                uint32_t* warm, const ListSink& sink, int local, int lane, int g,
                                int h_q, int nchunk, const TopmOut& tm, int local_from) {
-    uint32_t kk[16];
+    constexpr int KPL = C / 64;   // keys per lane
+    static_assert(KPL % 4 == 0, "lanes read whole 16-byte key groups");
+    constexpr uint32_t kStageMax = stage_max<C>();
+    uint32_t kk[KPL];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const u32x4 v = *reinterpret_cast<const u32x4*>(row + 16 * lane + 4 * j);
+    for (int j = 0; j < KPL / 4; ++j) {
+        const u32x4 v = *reinterpret_cast<const u32x4*>(row + KPL * lane + 4 * j);
 #pragma unroll
         for (int c = 0; c < 4; ++c) kk[4 * j + c] = v[c];
     }
@@ -71,26 +75,26 @@ __device__ inline void extract(const Item<T>& it, int n, uint32_t M, uint32_t* r
         // every real key, and are left out of the sum
         uint32_t kx = 0;
 #pragma unroll
-        for (int e = 0; e < 16; ++e) kx = kk[e] > kx ? kk[e] : kx;
+        for (int e = 0; e < KPL; ++e) kx = kk[e] > kx ? kk[e] : kx;
         const float mx = key_float(wave_umax(kx));
         float se = 0.f;
 #pragma unroll
-        for (int e = 0; e < 16; ++e) se += kk[e] != 0u ? __expf(key_float(kk[e]) - mx) : 0.f;
+        for (int e = 0; e < KPL; ++e) se += kk[e] != 0u ? __expf(key_float(kk[e]) - mx) : 0.f;
         se = wave_fsum(se);
         if (lane == 0)
             tm.stat[(int64_t)(it.b * h_q + it.kh * g + n) * nchunk + it.chunk] = make_float2(mx, se);
     }
     if (local_from < it.c0 + it.n) {   // uniform: positions from local_from on are not ranked
 #pragma unroll
-        for (int e = 0; e < 16; ++e)
-            if (it.c0 + 16 * lane + e >= local_from) kk[e] = 0u;
+        for (int e = 0; e < KPL; ++e)
+            if (it.c0 + KPL * lane + e >= local_from) kk[e] = 0u;
     }
     // count over the wave of keys >= x: one compare per key into a lane mask
     // and its scalar popcount (no per-lane sums to reduce across lanes)
     auto count_ge = [&](uint32_t x) -> uint32_t {
         uint32_t c = 0u;
 #pragma unroll
-        for (int e = 0; e < 16; ++e) c += (uint32_t)__builtin_popcountll(__ballot(kk[e] >= x));
+        for (int e = 0; e < KPL; ++e) c += (uint32_t)__builtin_popcountll(__ballot(kk[e] >= x));
         return __builtin_amdgcn_readfirstlane(c);
     };
     uint32_t cut = 0;   // publish everything when the chunk holds <= M keys
@@ -160,7 +164,7 @@ __device__ inline void extract(const Item<T>& it, int n, uint32_t M, uint32_t* r
     const uint32_t lo = cut > 1u ? cut : 1u;   // key 0 marks an empty slot
     uint32_t kc = 0;
 #pragma unroll
-    for (int e = 0; e < 16; ++e) kc += kk[e] >= lo ? 1u : 0u;
+    for (int e = 0; e < KPL; ++e) kc += kk[e] >= lo ? 1u : 0u;
     uint32_t total;
     const uint32_t first = wave_incl_scan(kc, total) - kc;
     const int64_t slot = ((int64_t)(it.b * h_q + it.kh * g + n) * nchunk + it.chunk);
@@ -181,13 +185,13 @@ __device__ inline void extract(const Item<T>& it, int n, uint32_t M, uint32_t* r
     typedef __attribute__((address_space(1))) v2u glb_v2u;
     lds_v2u* dst_l = (lds_v2u*)(sink.stg + off);
     glb_v2u* dst_g = (glb_v2u*)(sink.pool + off);
-    uint32_t pos0 = (uint32_t)(it.c0 + 16 * lane);
+    uint32_t pos0 = (uint32_t)(it.c0 + KPL * lane);
     asm volatile("" : "+v"(pos0));   // positions are formed at each store, not held in registers
     if (total <= kStageMax) {
         uint2* stage = reinterpret_cast<uint2*>(row);
         uint32_t at = first;
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
+        for (int e = 0; e < KPL; ++e) {
             const uint32_t keep = kk[e] >= lo ? 1u : 0u;
             stage[keep ? at : kStageMax + lane] = make_uint2(pos0 + e, kk[e]);
             at += keep;
@@ -207,11 +211,11 @@ __device__ inline void extract(const Item<T>& it, int n, uint32_t M, uint32_t* r
         uint32_t at = first;
         if (staged_lds) {
 #pragma unroll
-            for (int e = 0; e < 16; ++e)
+            for (int e = 0; e < KPL; ++e)
                 if (kk[e] >= lo) dst_l[at++] = v2u{pos0 + e, kk[e]};
         } else {
 #pragma unroll
-            for (int e = 0; e < 16; ++e)
+            for (int e = 0; e < KPL; ++e)
                 if (kk[e] >= lo) dst_g[at++] = v2u{pos0 + e, kk[e]};
         }
     }

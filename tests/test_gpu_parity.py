@@ -135,6 +135,35 @@ def test_decode_small_shapes(shape):
     _run_decode(x, to_device(x), case, N, all_pairs(B, h_q), f"small{shape}")
 
 
+SMALL_BATCH = [
+    # (B, h_q, h_k, h_v, d, S_max, N, ragged): few K-scan items of 1024 positions
+    # (256-position items) and few rows (the value gather split along each
+    # row's kept list, merged by the part that finishes last)
+    (1, 12, 1, 2, 128, 8192, 1024, False),
+    (1, 12, 1, 2, 128, 65536, 1024, False),
+    (4, 12, 2, 2, 128, 16384, 1024, False),
+    (2, 12, 1, 2, 128, 40000, 2048, True),
+    (1, 4, 1, 2, 64, 300, 64, False),
+    (3, 16, 1, 8, 64, 5000, 512, True),
+]
+
+
+@pytest.mark.parametrize("shape", SMALL_BATCH)
+def test_small_batch_shapes(shape):
+    B, h_q, h_k, h_v, d, S, N, ragged = shape
+    case = synth.small_case(B=B, h_q=h_q, h_k=h_k, h_v=h_v, d=d, S_max=S, N=N, dtype="bf16",
+                            ragged=ragged, seed=97)
+    x = synth.make_inputs(case)
+    dx = to_device(x)
+    g1, o1 = _run_decode(x, dx, case, N, all_pairs(B, h_q), f"small-batch{shape}")
+    # the same call again gives the same bits (the merge order is fixed)
+    idx = torch.empty((B, h_q, N), dtype=torch.int32, device="cuda")
+    out = saga.decode_attn(dx["q"], dx["k"], dx["v"], dx["seq_lens"], N, idx_out=idx)
+    torch.cuda.synchronize()
+    assert np.array_equal(idx.reshape(-1, N).cpu().numpy(), g1)
+    assert np.array_equal(out.reshape(-1, d).cpu().numpy(), o1)
+
+
 @pytest.mark.parametrize("h_q", [4, 32])
 def test_select_multi_tile_rows(h_q):
     # rows longer than one register tile of the selector take the tiled path that
