@@ -354,11 +354,13 @@ saga_status saga_debug_scores(const void* q, const void* k_cache, const int32_t*
 
 /*
  * Diagnostic for tests: after a saga_decode_attn call on `stream` with the same
- * sizes and workspace, copies to host_flags[B*h_q] (host memory) 1 for every
- * query head whose kept set was settled by recomputing all of its logits
- * (its chunk candidate lists could not prove the top-N exact) and 0 otherwise.
- * Synchronises `stream`. Heads take that path only when their largest logits
- * crowd into a few chunks; the result is exact either way.
+ * sizes and workspace, copies to host_flags[B*h_q] (host memory), per query
+ * head: 0 when its kept set was settled from the chunk candidate lists, 2 when
+ * some chunks' lists could not prove the top-N exact and those chunks' logits
+ * were recomputed, 1 when all of its logits were recomputed (too many such
+ * chunks, more than half the row). Synchronises `stream`. Heads recompute
+ * only when their largest logits crowd into a few chunks (attention sinks, a
+ * recency window); the result is exact either way.
  */
 saga_status saga_debug_fallback_rows(const void* workspace, size_t workspace_bytes, int B,
                                      int h_q, int h_k, int h_v, int d, int N, int64_t S_max,

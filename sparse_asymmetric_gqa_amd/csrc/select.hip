@@ -377,6 +377,35 @@ __global__ __launch_bounds__(kSelectThreads) void select_dense(
     compact<NT, KPT>(src, ntiles, T, krem, (uint32_t)n_eff, key, pos, sh, oi, ov, ou);
 }
 
+// Load of a value another thread of this workgroup stored to global memory
+// before a barrier: a relaxed atomic of workgroup scope, so that it is a
+// vector load (never the scalar data cache, which vector stores do not
+// update) and needs no device-wide fence.
+template <typename V>
+__device__ inline V wg_load(const V* p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+
+// Scaled logit of one cached key row against the query staged in LDS as fp32.
+template <typename T, int DH>
+__device__ inline float row_logit(const T* __restrict__ kr, const float* qs, float scale) {
+    float acc = 0.f;
+    for (int c0 = 0; c0 < DH; c0 += 16 / (int)sizeof(T)) {
+        const u32x4 v = *reinterpret_cast<const u32x4*>(kr + c0);
+        if (sizeof(T) == 2) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                acc = fmaf(qs[c0 + 2 * e], __uint_as_float(v[e] << 16), acc);
+                acc = fmaf(qs[c0 + 2 * e + 1], __uint_as_float(v[e] & 0xFFFF0000u), acc);
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc = fmaf(qs[c0 + e], __uint_as_float(v[e]), acc);
+        }
+    }
+    return acc * scale;
+}
+
 // ---- union select over the top-M candidate lists ----------------------------------
 // Fallback logits of one head, VALU, written to a dense row: lane-parallel over
 // positions, q staged in LDS as fp32.
@@ -395,39 +424,124 @@ __device__ void head_logits(const T* __restrict__ q, const T* __restrict__ k, in
     }
     __syncthreads();
     const T* kb = k + (int64_t)(b * h_k + kh) * S_max * DH;
-    for (int64_t t = threadIdx.x; t < L; t += kUnionThreads) {
-        const T* kr = kb + t * DH;
-        float acc = 0.f;
-        for (int c0 = 0; c0 < DH; c0 += 16 / (int)sizeof(T)) {
-            const u32x4 v = *reinterpret_cast<const u32x4*>(kr + c0);
-            if (sizeof(T) == 2) {
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    acc = fmaf(qs[c0 + 2 * e], __uint_as_float(v[e] << 16), acc);
-                    acc = fmaf(qs[c0 + 2 * e + 1], __uint_as_float(v[e] & 0xFFFF0000u), acc);
-                }
-            } else {
-#pragma unroll
-                for (int e = 0; e < 4; ++e) acc = fmaf(qs[c0 + e], __uint_as_float(v[e]), acc);
-            }
-        }
-        out[t] = acc * scale;
-    }
+    for (int64_t t = threadIdx.x; t < L; t += kUnionThreads) out[t] = row_logit<T, DH>(kb + t * DH, qs, scale);
     __syncthreads();
 }
 
-// ---- union select, general code (one workgroup per row) ----------------------------
-// The union select over any number of candidates (register tiles), the
-// cutoff check, and the dense fallback that recomputes the head's logits when
-// the check fails. row_flag becomes 0 (settled from the candidates) or 1
-// (dense fallback).
+// LDS of the general code of the union select (and of the stale-threshold
+// select's recompute).
 struct UnionShared {
     SelShared sh;
     int32_t pref[kMaxChunks + 1];
     int64_t coff[kMaxChunks];
+    int32_t roff[kMaxChunks];   // chunk-local recompute: a chunk's place in the row's region, or -1
     uint32_t bad;
 };
 
+
+// Builds in us.pref / us.coff the union of one row's chunk candidate lists,
+// with every chunk whose cutoff is above `lim` replaced by all of its keys,
+// recomputed for this head (query qf when given, else the row's q with
+// `scale`) into the row's region of the logit workspace (srow, as (position,
+// key) pairs in ascending position). Returns the union's size, or -1 when
+// those chunks do not fit the region (half the row's positions); sets
+// `recomputed` when some chunk was replaced. lim = 0xFFFFFFFF keeps every
+// list. Every thread of the workgroup calls this; LDS: us.
+template <typename T, int DH>
+__device__ int64_t build_union(UnionShared& us, const uint2* __restrict__ cand,
+                               const uint4* __restrict__ meta, int nch, int chunk, int64_t L,
+                               uint32_t lim, const T* __restrict__ q, const T* __restrict__ k,
+                               const float* qf, float scale, float* srow, int64_t s_stride,
+                               int b, int i, int h_q, int h_k, int64_t S_max, bool& recomputed) {
+    constexpr int NT = kUnionThreads;
+    SelShared& sh = us.sh;
+    int32_t* pref = us.pref;
+    int64_t* coff = us.coff;
+    int32_t* roff = us.roff;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    // Exclusive prefix over the chunks of cnt(c) into dst[0 .. nch] (dst[nch]
+    // = the total): each thread sums a contiguous run of chunks.
+    const int per = (nch + NT - 1) / NT;
+    auto prefix = [&](auto&& cnt, int32_t* dst) -> int64_t {
+        int32_t run = 0;
+        for (int c = tid * per; c < nch && c < (tid + 1) * per; ++c) run += cnt(c);
+        int32_t incl = run;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const int32_t y = __shfl_up(incl, o, 64);
+            if (lane >= o) incl += y;
+        }
+        if (lane == 63) sh.wtot[wave] = (uint32_t)incl;
+        __syncthreads();
+        int32_t off = incl - run;
+        for (int w = 0; w < wave; ++w) off += (int32_t)sh.wtot[w];
+        for (int c = tid * per; c < nch && c < (tid + 1) * per; ++c) {
+            dst[c] = off;
+            off += cnt(c);
+        }
+        if (tid == NT - 1) dst[nch] = off;   // last thread's running sum = total
+        __syncthreads();
+        const int64_t tot = dst[nch];
+        __syncthreads();
+        return tot;
+    };
+    auto clen = [&](int c) -> int32_t {
+        const int64_t c0 = (int64_t)c * chunk;
+        return (int32_t)((L - c0) < chunk ? (L - c0) : chunk);
+    };
+    auto fails = [&](int c) -> bool { return meta[c].z > lim; };
+    recomputed = false;
+    int64_t nre = 0;
+    if (lim != 0xFFFFFFFFu) {   // uniform
+        nre = prefix([&](int c) { return fails(c) ? clen(c) : 0; }, roff);
+        if (nre > s_stride / 2) return -1;
+    }
+    uint2* region = reinterpret_cast<uint2*>(srow);
+    if (nre > 0) {   // uniform
+        recomputed = true;
+        float* qs = reinterpret_cast<float*>(sh.hist);   // the query as fp32 in LDS
+        const T* qr = q + (int64_t)(b * h_q + i) * DH;
+        for (int c = tid; c < DH; c += NT) {
+            if (qf) qs[c] = qf[c];
+            else if (sizeof(T) == 2) qs[c] = __uint_as_float((uint32_t)((const uint16_t*)qr)[c] << 16);
+            else qs[c] = ((const float*)qr)[c];
+        }
+        __syncthreads();
+        const float sc = qf ? 1.f : scale;
+        const T* kb = k + (int64_t)(b * h_k + i / (h_q / h_k)) * S_max * DH;
+#pragma unroll 1
+        for (int c = 0; c < nch; ++c) {
+            if (!fails(c)) continue;   // uniform
+            const int64_t c0 = (int64_t)c * chunk;
+            const int32_t n = clen(c);
+            uint2* dst = region + roff[c];
+            for (int j = tid; j < n; j += NT)
+                dst[j] = make_uint2((uint32_t)(c0 + j),
+                                    float_key(row_logit<T, DH>(kb + (c0 + j) * DH, qs, sc)));
+        }
+        __syncthreads();   // the region's stores, before any thread reads them
+    }
+    const int64_t rbase = (int64_t)(region - cand);
+    for (int c = tid; c < nch; c += NT) {
+        const uint4 m = meta[c];
+        coff[c] = nre > 0 && fails(c) ? rbase + roff[c] : (int64_t)(((uint64_t)m.w << 32) | m.x);
+    }
+    return prefix([&](int c) { return nre > 0 && fails(c) ? clen(c) : (int32_t)meta[c].y; },
+                  pref);
+}
+
+// ---- union select, general code (one workgroup per row) ----------------------------
+// The union select over any number of candidates (register tiles) and the
+// cutoff check. When the check fails, the chunks whose cutoff lies above the
+// union's key of rank N_eff are recomputed (build_union) and the select runs
+// again on the completed union: a chunk whose cutoff is at or below that key
+// (a lower bound of the true one, since the union is a subset of all keys) is
+// complete for the true threshold, as every key it left out is below its
+// cutoff; the recomputed chunks are complete by construction, so the second
+// result is exact. When the union held fewer than N_eff keys there is no
+// bound and every chunk that left keys out is recomputed. When too many
+// chunks would be recomputed, all of the head's logits are. row_flag: 0
+// settled from the lists, 2 some chunks recomputed, 1 all logits recomputed.
 template <typename T, int DH>
 __device__ void union_row(
     int row, UnionShared& us, const uint2* __restrict__ cand, const uint4* __restrict__ cand_meta,
@@ -436,17 +550,16 @@ __device__ void union_row(
     float* __restrict__ row_max, int32_t* __restrict__ row_cnt, int32_t* __restrict__ idx_out,
     int32_t* __restrict__ row_flag, const T* __restrict__ q, const T* __restrict__ k,
     float* __restrict__ scores, int64_t s_stride, float scale, int64_t L, int n_eff,
-    const float* qf, int chunk) {
+    const float* qf, int chunk, uint32_t& kmax_out) {
     constexpr int NT = kUnionThreads;
     constexpr int NW = NT / 64;
     constexpr int KPT = kUnionKPT;
     SelShared& sh = us.sh;
-    int32_t* pref = us.pref;
-    int64_t* coff = us.coff;
     uint32_t& bad = us.bad;
+    kmax_out = 0u;
     const int b = row / h_q;
     const int i = row - b * h_q;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x;
     (void)lens;
     int32_t* oi = sel_idx + (int64_t)row * N;
     float* ov = sel_val + (int64_t)row * N;
@@ -466,42 +579,22 @@ __device__ void union_row(
     }
     const int nch = (int)((L + chunk - 1) / chunk);
     const uint4* meta = cand_meta + (int64_t)row * nchunk;
-
-    // exclusive prefix of the chunk counts: each thread sums a contiguous run
-    const int per = (nch + NT - 1) / NT;
-    int32_t run = 0;
-    for (int c = tid * per; c < nch && c < (tid + 1) * per; ++c) {
-        const uint4 m = meta[c];
-        coff[c] = (int64_t)(((uint64_t)m.w << 32) | m.x);
-        run += (int32_t)m.y;
-    }
-    int32_t incl = run;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        const int32_t y = __shfl_up(incl, o, 64);
-        if (lane >= o) incl += y;
-    }
-    if (lane == 63) sh.wtot[wave] = (uint32_t)incl;
-    if (tid == 0) bad = 0u;
-    __syncthreads();
-    int32_t off = incl - run;
-    for (int w = 0; w < wave; ++w) off += (int32_t)sh.wtot[w];
-    for (int c = tid * per; c < nch && c < (tid + 1) * per; ++c) {
-        pref[c] = off;
-        off += (int32_t)meta[c].y;
-    }
-    if (tid == NT - 1) pref[nch] = off;   // last thread's running sum = total
-    __syncthreads();
-    const int64_t total = pref[nch];
-    __syncthreads();
-
+    float* srow = scores + (int64_t)row * s_stride;
     uint32_t key[KPT];
     int32_t pos[KPT];
     uint32_t thr = 0, krem = 0, kmax = 0;
-    bool ok = total >= n_eff;
-    if (ok) {
+    // select over the union built from `lim`; false (nothing written) when
+    // the union holds fewer than N_eff keys or does not fit
+    auto select = [&](uint32_t lim, bool check, bool& recomputed) -> bool {
+        const int64_t total = build_union<T, DH>(us, cand, meta, nch, chunk, L, lim, q, k, qf,
+                                                 scale, srow, s_stride, b, i, h_q, h_k, S_max,
+                                                 recomputed);
+        if (total < n_eff) {   // uniform (also -1: too many chunks to recompute)
+            thr = 0u;
+            return false;
+        }
         using Src = UnionSrc<KPT, NW>;
-        const Src src{cand, coff, pref, nch, total};
+        const Src src{cand, us.coff, us.pref, nch, total};
         const int ntiles = (int)((total + Src::CAP - 1) / Src::CAP);
         if (ntiles == 1) {
             src.load(0, key, pos);
@@ -509,16 +602,27 @@ __device__ void union_row(
         } else {
             find_threshold<NT, KPT>(src, ntiles, (uint32_t)n_eff, key, pos, sh, thr, krem, kmax);
         }
-        // exact iff every chunk's cutoff is <= the union's threshold key
-        for (int c = tid; c < nch; c += NT)
-            if (meta[c].z > thr) bad = 1u;
-        __syncthreads();
-        ok = bad == 0u;
-        if (ok) compact<NT, KPT>(src, ntiles, thr, krem, (uint32_t)n_eff, key, pos, sh, oi, ov, ou);
+        if (check) {   // exact iff every chunk's cutoff is <= the union's threshold key
+            if (tid == 0) bad = 0u;
+            __syncthreads();
+            for (int c = tid; c < nch; c += NT)
+                if (meta[c].z > thr) bad = 1u;
+            __syncthreads();
+            if (bad != 0u) return false;
+        }
+        compact<NT, KPT>(src, ntiles, thr, krem, (uint32_t)n_eff, key, pos, sh, oi, ov, ou);
+        return true;
+    };
+    bool rec = false;
+    int flag = 0;
+    bool ok = select(0xFFFFFFFFu, true, rec);
+    if (!ok) {
+        // thr is the union's key of rank N_eff, or 0 when there was none
+        ok = select(thr, false, rec);
+        flag = ok ? 2 : 1;
     }
     if (!ok) {
         // dense fallback: this head's logits over all L positions, then a full select
-        float* srow = scores + (int64_t)row * s_stride;
         head_logits<T, DH>(q, k, b, i, h_q, h_k, S_max, L, qf ? 1.f : scale, srow,
                            reinterpret_cast<float*>(sh.hist), qf);
         using Src = DenseSrc<KPT, NW>;
@@ -532,10 +636,11 @@ __device__ void union_row(
         }
         compact<NT, KPT>(src, ntiles, thr, krem, (uint32_t)n_eff, key, pos, sh, oi, ov, ou);
     }
+    kmax_out = kmax;   // uniform
     if (tid == 0) {
         row_max[row] = key_float(kmax);
         row_cnt[row] = n_eff;
-        row_flag[row] = ok ? 0 : 1;
+        row_flag[row] = flag;
     }
 }
 
@@ -735,29 +840,33 @@ __global__ __launch_bounds__(kUnionThreads, 4) void select_union(
     float* g_w = reinterpret_cast<float*>(g_pos + nst);
     float* g_red = g_w + nst;
     auto general = [&] {
+        uint32_t gkmax = 0u;
         union_row<T, DH>(row, U, cand, cand_meta, lens, h_q, h_k, N, S_max, nchunk, sel_idx,
                          sel_val, row_max, row_cnt, SPQ ? nullptr : idx_out, row_flag, q, k,
-                         scores, s_stride, scale, L, n_eff, sq_qm(sq, row, DH), chunk);
+                         scores, s_stride, scale, L, n_eff, sq_qm(sq, row, DH), chunk, gkmax);
         if constexpr (FUSE) {
-            // the list union_row wrote, read back in blocks of nst entries
-            __threadfence();
+            // the list union_row wrote, read back in blocks of nst entries by the
+            // same workgroup: its waves share one CU's caches, so completed
+            // stores and the barrier's workgroup-scope release / acquire order
+            // these global accesses (a device-scope fence would also write back
+            // and invalidate the XCD's whole L2, which every other workgroup on
+            // it pays for). The count and the row max come from registers, so
+            // every address below is bounded by the row's N slots whatever the
+            // memory holds.
+            __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this thread's stores have completed
             __syncthreads();
             float* o = out + (int64_t)row * DH;
-            const int cnt = __hip_atomic_load(row_cnt + row, __ATOMIC_RELAXED,
-                                              __HIP_MEMORY_SCOPE_AGENT);
+            const int cnt = n_eff;   // union_row keeps exactly N_eff <= N
             if (cnt <= 0) {   // no kept entry (L_b = 0): out = 0
                 for (int c = tid; c < DH; c += NT) o[c] = 0.f;
                 if (sq.tau && tid == 0) sq.tau[row] = __builtin_nanf("");
                 return;
             }
-            const float mrow = __hip_atomic_load(row_max + row, __ATOMIC_RELAXED,
-                                                 __HIP_MEMORY_SCOPE_AGENT);
+            const float mrow = key_float(gkmax);
             if (sq.tau) {   // uniform: T is the smallest of the kept logits
                 uint32_t mk = 0xFFFFFFFFu;
                 for (int e = tid; e < cnt; e += NT)
-                    mk = min(mk, float_key(__hip_atomic_load(sel_val + (int64_t)row * N + e,
-                                                             __ATOMIC_RELAXED,
-                                                             __HIP_MEMORY_SCOPE_AGENT)));
+                    mk = min(mk, float_key(wg_load(sel_val + (int64_t)row * N + e)));
                 mk = ~wave_umax(~mk);
                 if (lane == 0) F.scan[wave] = mk;
                 __syncthreads();
@@ -780,12 +889,9 @@ __global__ __launch_bounds__(kUnionThreads, 4) void select_union(
                     int32_t pos = 0;
                     float w = 0.f;
                     if (e < ne) {
-                        pos = __hip_atomic_load(sel_idx + (int64_t)row * N + e0 + e,
-                                                __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                        pos = wg_load(sel_idx + (int64_t)row * N + e0 + e);
                         pos = pos < 0 ? 0 : (pos >= S_max ? (int32_t)(S_max - 1) : pos);
-                        w = __expf(__hip_atomic_load(sel_val + (int64_t)row * N + e0 + e,
-                                                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) -
-                                   mrow);
+                        w = __expf(wg_load(sel_val + (int64_t)row * N + e0 + e) - mrow);
                     }
                     g_pos[e] = pos;
                     g_w[e] = w;
@@ -1022,13 +1128,14 @@ __global__ __launch_bounds__(kUnionThreads, 4) void select_union(
             row_flag[row] = 0;
         }
         if (n_eff > 0 && (nch > NT || !fast())) {
-            // the general code writes the list; read it back into the stage
+            // the general code writes the list; this workgroup reads it back into
+            // the stage (completed stores and the barrier order the global
+            // accesses within it; n_eff bounds the reads)
             general();
-            __threadfence();
+            __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
             __syncthreads();
             for (int e = tid; e < n_eff; e += NT) {
-                int32_t p = __hip_atomic_load(sel_idx + (int64_t)row * N + e, __ATOMIC_RELAXED,
-                                              __HIP_MEMORY_SCOPE_AGENT);
+                int32_t p = wg_load(sel_idx + (int64_t)row * N + e);
                 st_idx[e] = p < 0 ? 0 : (p >= L ? (int32_t)(L - 1) : p);
             }
         }
@@ -1130,9 +1237,10 @@ __host__ __device__ constexpr size_t thresh_stage_offset() {
 // counted and slotted by one workgroup prefix scan in position order, the
 // first cap staged in LDS as positions and softmax weights (shifted by the
 // largest kept logit), and gathered (gather_staged). Otherwise part 0
-// recomputes the head's logits over all L positions, applies the same rule
-// (row_flag = 1), writes the list to sel_idx / sel_val [rows][cap], reads it
-// back into the staging and gathers it alone. count_out = positions reaching
+// recomputes the chunks whose cutoff lies above theta (row_flag = 2; all of
+// the head's logits when too many do, row_flag = 1), applies the same rule,
+// writes the list to sel_idx / sel_val [rows][cap], reads it back into the
+// staging and gathers it alone. count_out = positions reaching
 // the threshold before the cap; a row keeping none gets out = 0. idx_out
 // (nullable) [rows][cap]: the kept positions, -1 padded.
 // Dynamic LDS: max(sizeof(UnionShared), thresh_stage_offset() + 8 nst +
@@ -1311,12 +1419,15 @@ __global__ __launch_bounds__(kUnionThreads, 4) void select_thresh(
             return;
         }
     }
-    // general: part 0 recomputes the head's logits over all L positions and
-    // applies the same rule; the other parts have nothing to do
+    // general: part 0 completes the row's union for theta -- every chunk
+    // whose cutoff lies above it recomputed whole (build_union; all of the
+    // head's logits when too many are) -- and applies the same rule; the
+    // other parts have nothing to do
     if (part != 0) return;
     const RowStats rs = row_stats(stat, meta, nch, F.red, F.redf);
     const float theta = t == t ? __logf(t) + rs.lse : __builtin_inff();
-    const uint32_t lo = float_key(theta) > 1u ? float_key(theta) : 1u;
+    const uint32_t tk = float_key(theta);
+    const uint32_t lo = tk > 1u ? tk : 1u;
     __syncthreads();
     constexpr int KG = kUnionKPT;
     constexpr int NW = NT / 64;
@@ -1324,40 +1435,52 @@ __global__ __launch_bounds__(kUnionThreads, 4) void select_thresh(
     int32_t* oi = sel_idx + (int64_t)row * cap;
     float* ov = sel_val + (int64_t)row * cap;
     float* srow = scores + (int64_t)row * s_stride;
-    head_logits<T, DH>(q, k, b, i, h_q, h_k, S_max, L, scale, srow,
-                       reinterpret_cast<float*>(sh.hist));
-    using Src = DenseSrc<KG, NW>;
-    const Src src{srow, L};
-    const int ntiles = (int)((L + Src::CAP - 1) / Src::CAP);
     uint32_t gk[KG];
     int32_t gp[KG];
     int64_t total = 0;
+    // keys >= lo over a source, counted, then the first cap compacted in
+    // position order (keys > lo - 1)
+    auto apply = [&](const auto& src, int ntiles) {
 #pragma unroll 1
-    for (int tile = 0; tile < ntiles; ++tile) {
-        src.load(tile, gk, gp);
-        uint32_t cc = 0;
+        for (int tile = 0; tile < ntiles; ++tile) {
+            src.load(tile, gk, gp);
+            uint32_t cc = 0;
 #pragma unroll
-        for (int e = 0; e < KG; ++e) cc += gk[e] >= lo ? 1u : 0u;
-        cc = wave_sum(cc);
-        if (lane == 0) sh.wtot[wave] = cc;
-        __syncthreads();
+            for (int e = 0; e < KG; ++e) cc += gk[e] >= lo ? 1u : 0u;
+            cc = wave_sum(cc);
+            if (lane == 0) sh.wtot[wave] = cc;
+            __syncthreads();
 #pragma unroll
-        for (int w = 0; w < NW; ++w) total += sh.wtot[w];
-        __syncthreads();
+            for (int w = 0; w < NW; ++w) total += sh.wtot[w];
+            __syncthreads();
+        }
+        compact<NT, KG>(src, ntiles, lo - 1u, 0u, (uint32_t)cap, gk, gp, sh, oi, ov, nullptr);
+    };
+    bool rec = false;
+    const int64_t nu = build_union<T, DH>(U, cand, meta, nch, chunk, L, tk, q, k, nullptr, scale,
+                                          srow, s_stride, b, i, h_q, h_k, S_max, rec);
+    int flag = 2;
+    if (nu >= 0) {   // uniform
+        using Src = UnionSrc<KG, NW>;
+        apply(Src{cand, U.coff, U.pref, nch, nu}, (int)((nu + Src::CAP - 1) / Src::CAP));
+    } else {
+        flag = 1;
+        head_logits<T, DH>(q, k, b, i, h_q, h_k, S_max, L, scale, srow,
+                           reinterpret_cast<float*>(sh.hist));
+        using Src = DenseSrc<KG, NW>;
+        apply(Src{srow, L}, (int)((L + Src::CAP - 1) / Src::CAP));
     }
-    // keys > lo - 1 = keys >= lo, first cap in position order
-    compact<NT, KG>(src, ntiles, lo - 1u, 0u, (uint32_t)cap, gk, gp, sh, oi, ov, nullptr);
-    __threadfence();
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): the compacted list's stores completed
     __syncthreads();
-    const int kept = (int)(total < cap ? total : cap);
+    const int kept = (int)(total < cap ? total : cap);   // from registers: bounds the reads
     // the list back into the staging (cap <= nst) for the gather
     for (int j = tid; j < kept; j += NT) {
-        int32_t pp = __hip_atomic_load(oi + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        int32_t pp = wg_load(oi + j);
         st_idx[j] = pp < 0 ? 0 : (pp >= L ? (int32_t)(L - 1) : pp);
-        st_w[j] = __hip_atomic_load(ov + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        st_w[j] = wg_load(ov + j);
     }
     __syncthreads();
-    records(kept, total, 1);
+    records(kept, total, flag);
     if (kept == 0) {
         for (int cc = tid; cc < DH; cc += NT) o[cc] = 0.f;
         return;

@@ -30,7 +30,7 @@ _SRC = os.path.join(_HERE, "gen.c")
 _LIB = os.path.join(_HERE, "libsynth.so")
 
 # sub-stream ids
-STREAM_Q, STREAM_K, STREAM_V, STREAM_HEAVY, STREAM_LENS = 0, 1, 2, 3, 4
+STREAM_Q, STREAM_K, STREAM_V, STREAM_HEAVY, STREAM_LENS, STREAM_WINDOW = 0, 1, 2, 3, 4, 5
 
 
 def build(force: bool = True) -> str:
@@ -83,6 +83,11 @@ class Case:
     heavy: str            # "fixed8" (8 rows per head) or "pct1" (floor(1% of L_b))
     heavy_factor: float
     ragged: bool = False  # lengths uniform in [S/2, S] per batch row
+    # "uniform": heavy-hitter rows spread over all positions (the recipe above).
+    # "recency_sink": attention concentrated the way trained models often
+    # concentrate it -- on the first positions (sinks) and on a window of the
+    # most recent ones -- on top of the uniform recipe (see _concentrate).
+    structure: str = "uniform"
 
     def with_heads(self, h_k: int, h_v: int, seed: int | None = None) -> "Case":
         return replace(self, h_k=h_k, h_v=h_v, seed=self.seed if seed is None else seed)
@@ -100,6 +105,20 @@ CASES = {
                                 5, "pct1", 3.0),
 }
 CASE_ORDER = list(CASES)
+
+# Concentrated-attention variants (not BASELINE configs): the same shapes with
+# sink and recency structure, for the selector's worst case.
+CONCENTRATED = {
+    "qwen25_1p5b_b64_32k_recency": replace(CASES["qwen25_1p5b_b64_32k"],
+                                           name="qwen25_1p5b_b64_32k_recency",
+                                           structure="recency_sink"),
+    "llama32_1b_8to4_recency": replace(CASES["llama32_1b_8to4"],
+                                       name="llama32_1b_8to4_recency", structure="recency_sink"),
+}
+# sink positions, window length, and the logit gains aimed at (expected value
+# for a window row at full strength, and for a sink row)
+SINK_ROWS, WINDOW_ROWS = 4, 1024
+WINDOW_GAIN, SINK_GAIN = 2.8, 5.0
 
 # Dense (full-attention) baselines at the same shapes: (h_k, h_v) pairs.
 DENSE_BASELINES = {
@@ -156,7 +175,52 @@ def make_inputs(case: Case, lens: np.ndarray | None = None) -> dict:
     q = normal_tensor(case.seed, STREAM_Q, (B, case.h_q, case.d), case.dtype)
     k = normal_tensor(case.seed, STREAM_K, (B, case.h_k, S, case.d), case.dtype, scale)
     v = normal_tensor(case.seed, STREAM_V, (B, case.h_v, S, case.d), case.dtype)
+    if case.structure == "recency_sink":
+        _concentrate(case, q, k, lens)
+    elif case.structure != "uniform":
+        raise ValueError(case.structure)
     return {"q": q, "k": k, "v": v, "seq_lens": lens, "heavy_scale": scale}
+
+
+def _concentrate(case: Case, q: np.ndarray, k: np.ndarray, lens: np.ndarray) -> None:
+    """Sink and recency structure, in place on k (input construction only).
+
+    For every (b, key head) let u be the unit vector along the sum of the
+    group's g = h_q / h_k query rows. The first SINK_ROWS positions get
+    + a_s u and each position t of the last WINDOW_ROWS positions of the row
+    gets + a_w r_t u, r_t uniform in [0.5, 1] from stream (seed, 5) at
+    counter (b h_k + kh) 2^32 + t, with a = gain sqrt(g): a query row of the
+    group has an expected component sqrt(d / g) along u, so a shift of a along
+    u raises its scaled logit <q, K> / sqrt(d) by about a / sqrt(g) = gain
+    (times r_t). Rows are modified in fp64 from their stored values and
+    rounded back to the storage dtype.
+    """
+    B, h_q, d = q.shape
+    h_k, S = k.shape[1], k.shape[2]
+    g = h_q // h_k
+    qf = as_f32(q).astype(np.float64)
+    a_w = WINDOW_GAIN * np.sqrt(g)
+    a_s = SINK_GAIN * np.sqrt(g)
+    for b in range(B):
+        L = int(lens[b])
+        if L == 0:
+            continue
+        for kh in range(h_k):
+            qs = qf[b, kh * g:(kh + 1) * g].sum(axis=0)
+            u = qs / max(np.linalg.norm(qs), 1e-30)
+            t0 = max(0, L - WINDOW_ROWS)
+            draws = np.empty(L - t0, dtype=np.uint64)
+            _load().synth_draws(case.seed, STREAM_WINDOW, ((b * h_k + kh) << 32) + t0, L - t0,
+                                _ptr(draws))
+            r = 0.5 + 0.5 * (draws >> np.uint64(11)).astype(np.float64) / float(1 << 53)
+            gain = np.zeros(L)
+            gain[t0:] = a_w * r
+            ns = min(SINK_ROWS, L)
+            gain[:ns] = np.maximum(gain[:ns], a_s)
+            rows = np.nonzero(gain)[0]
+            kr = as_f32(k[b, kh, rows]).astype(np.float64) + gain[rows, None] * u[None, :]
+            k[b, kh, rows] = kr.astype(np.float32) if k.dtype == np.float32 else \
+                f32_to_bf16_bits(kr.astype(np.float32))
 
 
 def small_case(name="small", B=2, h_q=8, h_k=2, h_v=4, d=64, S_max=300, N=40, dtype="bf16",

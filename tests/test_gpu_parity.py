@@ -367,7 +367,36 @@ def test_clustered_top_entries_take_exact_fallback():
     check_index_sets(g_idx, ref, x, pairs, 300)
     check_outputs(out.reshape(-1, 64).cpu().numpy(), g_idx, x, pairs, 2e-3)
     assert set(g_idx[0].tolist()) == set(range(300))
-    assert flags[:4].tolist() == [1, 1, 1, 1] and flags[4:].tolist() == [0, 0, 0, 0]
+    # row 0's heads recompute their first chunk only (2); row 1 settles from the lists (0)
+    assert flags[:4].tolist() == [2, 2, 2, 2] and flags[4:].tolist() == [0, 0, 0, 0]
+
+
+@pytest.mark.parametrize("name", list(synth.CONCENTRATED))
+def test_concentrated_attention(name):
+    # sinks and a recency window: a large share of each head's top-N sits in the
+    # last chunk, beyond what its candidate list carries; those heads recompute
+    # that chunk only (flag 2) and stay exact
+    case = synth.CONCENTRATED[name]
+    x = synth.make_inputs(case)
+    dx = to_device(x)
+    ws = saga.new_workspace(saga.workspace_size(dx["q"], dx["k"], dx["v"], dx["seq_lens"],
+                                                case.N), "cuda")
+    _say(f"[concentrated] {name}")
+    idx = torch.empty((case.B, case.h_q, case.N), dtype=torch.int32, device="cuda")
+    out = saga.decode_attn(dx["q"], dx["k"], dx["v"], dx["seq_lens"], case.N, workspace=ws,
+                           idx_out=idx)
+    torch.cuda.synchronize()
+    flags = _fallback_flags(dx, ws, case, case.N)
+    pairs = all_pairs(case.B, case.h_q)
+    ref = oracle.topn_attn(x["q"], x["k"], x["v"], x["seq_lens"], case.N, pairs=pairs)
+    g_idx = idx.reshape(-1, case.N).cpu().numpy()
+    nbad, ndiff = check_index_sets(g_idx, ref, x, pairs, case.N)
+    err = check_outputs(out.reshape(-1, case.d).cpu().numpy(), g_idx, x, pairs,
+                        tol_for(case.dtype))
+    counts = np.bincount(flags, minlength=3)
+    _say(f"    rows={len(pairs)} differing-rows={nbad} sym-diff={ndiff} max|err|={err:.2e} "
+         f"settled={counts[0]} chunk-recompute={counts[2]} full-recompute={counts[1]}")
+    assert counts[2] > 0 and counts[1] == 0
 
 
 def test_workloads_report_fallback_rows():

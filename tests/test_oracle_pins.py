@@ -287,3 +287,29 @@ def test_bad_arguments_are_rejected():
     v = np.zeros((1, 2, 4, 8), np.float32)
     with pytest.raises(ValueError):
         oracle.attend_given(q, k, v, np.array([4], np.int32), np.array([[0, 4], [1, 2]]))
+
+
+def test_concentrated_generator_crowds_the_top_n_into_the_recent_chunk():
+    """The sink / recency variant of the generator (input construction only):
+    on a reduced batch of each variant, the oracle's top-N sets put a large
+    share of every head's kept positions in the last 1024 positions and keep
+    the sink positions, which is the structure the variant stands for."""
+    import synth
+    for name in synth.CONCENTRATED:
+        case = synth.replace(synth.CONCENTRATED[name], B=4)
+        x = synth.make_inputs(case)
+        r = oracle.topn_attn(x["q"], x["k"], x["v"], x["seq_lens"], case.N)
+        share, sinks = [], []
+        for j in range(case.B * case.h_q):
+            L = int(x["seq_lens"][j // case.h_q])
+            kept = r["idx"][j][r["idx"][j] >= 0]
+            share.append(np.mean(kept >= L - synth.WINDOW_ROWS))
+            sinks.append(np.sum(kept < synth.SINK_ROWS))
+        assert np.median(share) >= 0.4, (name, np.median(share))
+        assert np.mean(np.array(share) >= 0.3) >= 0.75, name
+        assert np.mean(sinks) >= 3.0, name
+        # the uniform recipe has no such structure
+        u = synth.make_inputs(synth.replace(case, structure="uniform"))
+        ru = oracle.topn_attn(u["q"], u["k"], u["v"], u["seq_lens"], case.N)
+        L0 = int(u["seq_lens"][0])
+        assert np.mean(ru["idx"][0] >= L0 - synth.WINDOW_ROWS) < 0.2
