@@ -256,6 +256,65 @@ __device__ void find_threshold_bisect(uint32_t n_eff, const uint32_t (&key)[KPT]
     __syncthreads();
 }
 
+// The key of rank `need` (from the top) among the keys the 256 threads hold
+// in registers, by histogram descent: each pass spreads the keys of the
+// current range [lo, hi] over 256 LDS bins with shared-memory atomics, every
+// wave scans all bins itself (4 per lane, a DPP prefix) and picks the bin
+// holding rank `need`, so a pass costs one barrier and narrows the range by
+// 8 bits. Requires every key above hi to be absent and at least `need` keys
+// in [lo, hi]. Returns a T with count(key >= T) >= need > count(key > T)
+// when the final bin is a single key value, or the lower end of a bin with
+// count(key >= T) == need exactly. hist: 3 x 256 LDS words (rotated, so a
+// pass clears the bins read two passes earlier).
+template <int KPT>
+__device__ uint32_t descend(const uint32_t (&key)[KPT], uint32_t need, uint32_t lo, uint32_t hi,
+                            uint32_t* hist) {
+    const int tid = threadIdx.x, lane = tid & 63;
+    hist[tid] = 0u;
+    __syncthreads();
+#pragma unroll 1
+    for (int pass = 0;; ++pass) {
+        uint32_t* h = hist + 256 * (pass % 3);
+        hist[256 * ((pass + 1) % 3) + tid] = 0u;   // last read two passes ago
+        const uint32_t span = hi - lo;
+        const int nb = span ? 32 - __clz((int)span) : 0;
+        const int shift = nb > 8 ? nb - 8 : 0;
+#pragma unroll
+        for (int s = 0; s < KPT; ++s)
+            if (key[s] >= lo && key[s] <= hi)
+                __hip_atomic_fetch_add(h + ((key[s] - lo) >> shift), 1u, __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_WORKGROUP);
+        __syncthreads();
+        // lane l holds bins 255-4l (top) down to 252-4l; every wave scans all
+        const uint4 hv = reinterpret_cast<const uint4*>(h)[63 - lane];
+        const uint32_t lsum = (hv.x + hv.y) + (hv.z + hv.w);
+        uint32_t total;
+        const uint32_t incl = wave_incl_scan(lsum, total);   // keys in bins >= 252-4l
+        const uint32_t above0 = incl - lsum;
+        const uint64_t hit = ballot(incl >= need && above0 < need);
+        const int hl = (int)__builtin_ctzll(hit);   // exactly one lane
+        uint32_t bin = 255u - 4u * (uint32_t)lane, above = above0, inbin = hv.w;
+        if (above + hv.w < need) {
+            above += hv.w; bin -= 1u; inbin = hv.z;
+            if (above + hv.z < need) {
+                above += hv.z; bin -= 1u; inbin = hv.y;
+                if (above + hv.y < need) { above += hv.y; bin -= 1u; inbin = hv.x; }
+            }
+        }
+        bin = (uint32_t)__builtin_amdgcn_readlane((int)bin, hl);
+        above = (uint32_t)__builtin_amdgcn_readlane((int)above, hl);
+        inbin = (uint32_t)__builtin_amdgcn_readlane((int)inbin, hl);
+        need -= above;
+        lo += bin << shift;
+        const uint32_t wmask = (1u << shift) - 1u;
+        hi = hi - lo <= wmask ? hi : lo + wmask;
+        if (inbin == need || shift == 0) {   // keys >= lo are exactly need, or one key value
+            __syncthreads();   // every wave has read this pass's bins
+            return lo;
+        }
+    }
+}
+
 // Keep keys > T and the first krem keys == T, in ascending position order.
 template <int NT, int KPT, class Src>
 __device__ void compact(const Src& src, int ntiles, uint32_t T, uint32_t krem, uint32_t n_eff,
@@ -434,7 +493,7 @@ struct UnionShared {
     SelShared sh;
     int32_t pref[kMaxChunks + 1];
     int64_t coff[kMaxChunks];
-    int32_t roff[kMaxChunks];   // chunk-local recompute: a chunk's place in the row's region, or -1
+    int32_t roff[kMaxChunks + 1];   // chunk-local recompute: a chunk's place in the row's region, or -1
     uint32_t bad;
 };
 
@@ -448,7 +507,7 @@ struct UnionShared {
 // `recomputed` when some chunk was replaced. lim = 0xFFFFFFFF keeps every
 // list. Every thread of the workgroup calls this; LDS: us.
 template <typename T, int DH>
-__device__ int64_t build_union(UnionShared& us, const uint2* __restrict__ cand,
+__device__ __attribute__((noinline)) int64_t build_union(UnionShared& us, const uint2* __restrict__ cand,
                                const uint4* __restrict__ meta, int nch, int chunk, int64_t L,
                                uint32_t lim, const T* __restrict__ q, const T* __restrict__ k,
                                const float* qf, float scale, float* srow, int64_t s_stride,
@@ -495,7 +554,13 @@ __device__ int64_t build_union(UnionShared& us, const uint2* __restrict__ cand,
     if (lim != 0xFFFFFFFFu) {   // uniform
         nre = prefix([&](int c) { return fails(c) ? clen(c) : 0; }, roff);
         if (nre > s_stride / 2) return -1;
+        // from here on roff[c] < 0 marks a chunk that keeps its list (LDS, so
+        // the loops below read no chunk record from memory)
+        for (int c = tid; c < nch; c += NT)
+            if (!fails(c)) roff[c] = -1;
+        __syncthreads();
     }
+    auto redo = [&](int c) -> bool { return nre > 0 && roff[c] >= 0; };
     uint2* region = reinterpret_cast<uint2*>(srow);
     if (nre > 0) {   // uniform
         recomputed = true;
@@ -509,25 +574,58 @@ __device__ int64_t build_union(UnionShared& us, const uint2* __restrict__ cand,
         __syncthreads();
         const float sc = qf ? 1.f : scale;
         const T* kb = k + (int64_t)(b * h_k + i / (h_q / h_k)) * S_max * DH;
+        // Coalesced: LPR lanes share a key row, each taking one 16-byte piece
+        // and its slice of the query, and a butterfly over them gives the dot
+        // product; UNR rows per lane group are in flight at once.
+        constexpr int EPL = 16 / (int)sizeof(T);   // elements per piece
+        constexpr int LPR = DH / EPL;              // lanes per row
+        constexpr int RPW = 64 / LPR;              // rows per wave instruction
+        constexpr int UNR = 8;
+        constexpr int STEP = (NT / 64) * RPW;      // rows per workgroup step
+        const int rg = lane / LPR, sub = lane - rg * LPR;
+        float qv[EPL];
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) qv[e] = qs[sub * EPL + e] * sc;
 #pragma unroll 1
         for (int c = 0; c < nch; ++c) {
-            if (!fails(c)) continue;   // uniform
+            if (roff[c] < 0) continue;   // uniform (LDS)
             const int64_t c0 = (int64_t)c * chunk;
             const int32_t n = clen(c);
             uint2* dst = region + roff[c];
-            for (int j = tid; j < n; j += NT)
-                dst[j] = make_uint2((uint32_t)(c0 + j),
-                                    float_key(row_logit<T, DH>(kb + (c0 + j) * DH, qs, sc)));
+            const T* kc = kb + c0 * DH + sub * EPL;
+#pragma unroll 1
+            for (int base = wave * RPW; base < n; base += STEP * UNR) {   // uniform per wave
+                const int r0 = base + rg;
+                u32x4 v[UNR];
+#pragma unroll
+                for (int u = 0; u < UNR; ++u) {
+                    int r = r0 + u * STEP;
+                    r = r < n ? r : n - 1;   // past the chunk: re-read its last row (unused)
+                    v[u] = *reinterpret_cast<const u32x4*>(kc + (int64_t)r * DH);
+                }
+#pragma unroll
+                for (int u = 0; u < UNR; ++u) {
+                    float f[EPL];
+                    Row16<T>::cvt(v[u], f);
+                    float acc = 0.f;
+#pragma unroll
+                    for (int e = 0; e < EPL; ++e) acc = fmaf(qv[e], f[e], acc);
+#pragma unroll
+                    for (int o = 1; o < LPR; o <<= 1) acc += __shfl_xor(acc, o, 64);
+                    const int r = r0 + u * STEP;
+                    if (sub == 0 && r < n)
+                        dst[r] = make_uint2((uint32_t)(c0 + r), float_key(acc));
+                }
+            }
         }
         __syncthreads();   // the region's stores, before any thread reads them
     }
     const int64_t rbase = (int64_t)(region - cand);
     for (int c = tid; c < nch; c += NT) {
         const uint4 m = meta[c];
-        coff[c] = nre > 0 && fails(c) ? rbase + roff[c] : (int64_t)(((uint64_t)m.w << 32) | m.x);
+        coff[c] = redo(c) ? rbase + roff[c] : (int64_t)(((uint64_t)m.w << 32) | m.x);
     }
-    return prefix([&](int c) { return nre > 0 && fails(c) ? clen(c) : (int32_t)meta[c].y; },
-                  pref);
+    return prefix([&](int c) { return redo(c) ? clen(c) : (int32_t)meta[c].y; }, pref);
 }
 
 // ---- union select, general code (one workgroup per row) ----------------------------
@@ -543,7 +641,7 @@ __device__ int64_t build_union(UnionShared& us, const uint2* __restrict__ cand,
 // chunks would be recomputed, all of the head's logits are. row_flag: 0
 // settled from the lists, 2 some chunks recomputed, 1 all logits recomputed.
 template <typename T, int DH>
-__device__ void union_row(
+__device__ __attribute__((noinline)) void union_row(
     int row, UnionShared& us, const uint2* __restrict__ cand, const uint4* __restrict__ cand_meta,
     const int32_t* __restrict__ lens, int h_q, int h_k,
     int N, int64_t S_max, int nchunk, int32_t* __restrict__ sel_idx, float* __restrict__ sel_val,
@@ -580,11 +678,10 @@ __device__ void union_row(
     const int nch = (int)((L + chunk - 1) / chunk);
     const uint4* meta = cand_meta + (int64_t)row * nchunk;
     float* srow = scores + (int64_t)row * s_stride;
-    uint32_t key[KPT];
-    int32_t pos[KPT];
     uint32_t thr = 0, krem = 0, kmax = 0;
     // select over the union built from `lim`; false (nothing written) when
-    // the union holds fewer than N_eff keys or does not fit
+    // the union holds fewer than N_eff keys or does not fit. The key registers
+    // live inside, so that nothing large is live across the union's build.
     auto select = [&](uint32_t lim, bool check, bool& recomputed) -> bool {
         const int64_t total = build_union<T, DH>(us, cand, meta, nch, chunk, L, lim, q, k, qf,
                                                  scale, srow, s_stride, b, i, h_q, h_k, S_max,
@@ -593,12 +690,49 @@ __device__ void union_row(
             thr = 0u;
             return false;
         }
+        uint32_t key[KPT];
+        int32_t pos[KPT];
         using Src = UnionSrc<KPT, NW>;
         const Src src{cand, us.coff, us.pref, nch, total};
         const int ntiles = (int)((total + Src::CAP - 1) / Src::CAP);
         if (ntiles == 1) {
+            // the union in registers: histogram descent for its key of rank
+            // N_eff, then T = the smallest key at or above that bound and
+            // krem = N_eff - count(key > T)
             src.load(0, key, pos);
-            find_threshold_bisect<NT, KPT>((uint32_t)n_eff, key, sh, thr, krem, kmax);
+            const int wave = tid >> 6, lane = tid & 63;
+            uint32_t mx = 0;
+#pragma unroll
+            for (int j = 0; j < KPT; ++j) mx = key[j] > mx ? key[j] : mx;
+            mx = wave_umax(mx);
+            if (lane == 0) sh.wtot[wave] = mx;
+            __syncthreads();
+            kmax = 0;
+#pragma unroll
+            for (int w = 0; w < NW; ++w) kmax = sh.wtot[w] > kmax ? sh.wtot[w] : kmax;
+            __syncthreads();
+            const uint32_t tb = descend<KPT>(key, (uint32_t)n_eff, 1u, kmax, sh.hist);
+            uint32_t mn = 0xFFFFFFFFu;
+#pragma unroll
+            for (int j = 0; j < KPT; ++j) mn = key[j] >= tb && key[j] < mn ? key[j] : mn;
+            mn = ~wave_umax(~mn);
+            if (lane == 0) sh.wtot[wave] = mn;
+            __syncthreads();
+            thr = 0xFFFFFFFFu;
+#pragma unroll
+            for (int w = 0; w < NW; ++w) thr = sh.wtot[w] < thr ? sh.wtot[w] : thr;
+            __syncthreads();
+            uint32_t gt = 0;
+#pragma unroll
+            for (int j = 0; j < KPT; ++j) gt += key[j] > thr ? 1u : 0u;
+            gt = wave_sum(gt);
+            if (lane == 0) sh.wtot[wave] = gt;
+            __syncthreads();
+            gt = 0;
+#pragma unroll
+            for (int w = 0; w < NW; ++w) gt += sh.wtot[w];
+            krem = (uint32_t)n_eff - gt;
+            __syncthreads();
         } else {
             find_threshold<NT, KPT>(src, ntiles, (uint32_t)n_eff, key, pos, sh, thr, krem, kmax);
         }
@@ -613,18 +747,23 @@ __device__ void union_row(
         compact<NT, KPT>(src, ntiles, thr, krem, (uint32_t)n_eff, key, pos, sh, oi, ov, ou);
         return true;
     };
+    // first the lists as published, with the cutoff check; then, if that
+    // fails, the union completed for thr (the union's key of rank N_eff, or 0
+    // when there was none), which needs no check
     bool rec = false;
+    bool ok = false;
     int flag = 0;
-    bool ok = select(0xFFFFFFFFu, true, rec);
-    if (!ok) {
-        // thr is the union's key of rank N_eff, or 0 when there was none
-        ok = select(thr, false, rec);
-        flag = ok ? 2 : 1;
+#pragma unroll 1
+    for (int attempt = 0; attempt < 2 && !ok; ++attempt) {
+        ok = select(attempt == 0 ? 0xFFFFFFFFu : thr, attempt == 0, rec);
+        if (attempt == 1) flag = ok ? 2 : 1;
     }
     if (!ok) {
         // dense fallback: this head's logits over all L positions, then a full select
         head_logits<T, DH>(q, k, b, i, h_q, h_k, S_max, L, qf ? 1.f : scale, srow,
                            reinterpret_cast<float*>(sh.hist), qf);
+        uint32_t key[KPT];
+        int32_t pos[KPT];
         using Src = DenseSrc<KPT, NW>;
         const Src src{srow, L};
         const int ntiles = (int)((L + Src::CAP - 1) / Src::CAP);
