@@ -376,10 +376,11 @@ saga_status saga_atopn_attn(const void* q, const void* k_cache, const void* v_ca
     const int64_t ss = saga::score_stride(S_max);
     const int cap = 2 * N;
     clear_stale_error();
-    // candidate lists sized like the exact step's (the completeness check
-    // sends a row whose lists do not cover the threshold to the recompute),
-    // with chunk statistics; the K-scan also clears the split counters
-    const saga::TopmOut tm{w.cand, w.cand_meta, N, w.cand_stat, w.chunk,
+    // candidate lists sized for 1.5 N kept entries (a drifted query keeps
+    // more than the N of its calibration; the completeness check sends a row
+    // whose lists do not cover the threshold to the recompute), with chunk
+    // statistics; the K-scan also clears the split counters
+    const saga::TopmOut tm{w.cand, w.cand_meta, N + N / 2, w.cand_stat, w.chunk,
                            w.nsplit > 1 ? w.split_cnt : nullptr, B * h_q};
     s = from_hip(saga::launch_kscan_topm(q, k_cache, seq_lens, tm, B, h_q, h_k, d, S_max, bf16,
                                          stream), "kscan_topm");

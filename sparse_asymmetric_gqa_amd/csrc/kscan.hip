@@ -126,6 +126,7 @@ __global__ __launch_bounds__(256) void kscan(const T* __restrict__ q, const T* _
 //   keys [2][g][kKeyRow]     double-buffered key rows of the current items
 //   warm [g]                  previous cutoff per head
 //   cursor, used, pad [4]     list cursor and end of the staged lists
+//   flo [g], flo_tag [g]      lowest cutoff of the row's earlier chunks per head, its row tag
 //   meta_stg [kMetaStage] uint4, meta_slot [kMetaStage]   staged metadata
 //   xtile [kWaves][16 rows]   producers' transpose buffers (bf16 only)
 //   stg  [..]                 staged candidate lists (uint2), the rest of the LDS
@@ -134,7 +135,7 @@ constexpr bool topm_xp() { return sizeof(T) == 2; }
 template <typename T, int DH, int C>
 __host__ __device__ constexpr size_t topm_lds_words(int g) {
     // every area starts 16-byte aligned
-    return (size_t)2 * g * key_row<C>() + ((g + 4 + 3) & ~3) + 5 * kMetaStage +
+    return (size_t)2 * g * key_row<C>() + ((3 * g + 4 + 3) & ~3) + 5 * kMetaStage +
            (topm_xp<T>() ? (size_t)kWaves * 16 * DH * sizeof(T) / 4 : 0);
 }
 
@@ -154,7 +155,8 @@ __global__ __launch_bounds__(kTopmThreads, 1) void kscan_topm(
     uint32_t* keys = lds;
     uint32_t* warm = lds + 2 * g * KR;
     uint32_t* cursor = warm + g;   // cursor[0]: next free entry, cursor[1]: end of staged lists
-    uint32_t* meta_words = lds + 2 * g * KR + ((g + 4 + 3) & ~3);
+    uint32_t* flo = cursor + 4;    // flo[g], then flo_tag[g]
+    uint32_t* meta_words = lds + 2 * g * KR + ((3 * g + 4 + 3) & ~3);
     uint32_t* xtile_words = meta_words + 5 * kMetaStage;
     const uint32_t fixed_words = (uint32_t)topm_lds_words<T, DH, C>(g);
 
@@ -195,7 +197,10 @@ __global__ __launch_bounds__(kTopmThreads, 1) void kscan_topm(
         for (int s = 0; s < NS; ++s) sm.load(s, cur, s);
     } else {
         for (int n = wave - kWaves; n < g; n += kConsumers)
-            if (lane == 0) warm[n] = 0u;
+            if (lane == 0) {
+                warm[n] = 0u;
+                flo[g + n] = 0u;   // no row yet
+            }
         if (threadIdx.x == 64 * kWaves) cursor[0] = cursor[1] = 0u;
     }
     lds_barrier();
@@ -277,7 +282,7 @@ __global__ __launch_bounds__(kTopmThreads, 1) void kscan_topm(
 #pragma unroll 1
             for (int n = first; n < g; n += step)
                 extract<T, C>(prev, n, M, kbuf + n * KR, warm, sink, t - 1, lane, g, h_q,
-                        nchunk, tm, prev.L);
+                        nchunk, tm, prev.L, flo);
         }
         lds_barrier();   // keys of item t are complete; buffer (t - 1) & 1 is free again
         prev = cur;

@@ -53,10 +53,21 @@ struct ListSink {
 };
 constexpr int kMetaStage = 256;
 
+//
+// Hot chunks (flo != nullptr): flo[n] holds the lowest cutoff of the earlier
+// chunks of the same (b, key head) row that this workgroup extracted, tagged
+// in flo_tag[n] = 1 + b h_q + kh g (flo_tag = flo + g). A chunk whose cutoff
+// lies well above that floor -- by more than a quarter of the distance from
+// its cutoff to its largest key, in logit units -- holds more of the row's
+// top keys than its M suggest (a recency window, a block of sinks); its list
+// then reaches down to the floor, so that the selector does not have to
+// recompute it. Any cutoff keeps the result exact: every key left out is
+// still below the cutoff the chunk publishes.
 template <typename T, int C = kScanChunk>
 __device__ inline void extract(const Item<T>& it, int n, uint32_t M, uint32_t* row,
                                uint32_t* warm, const ListSink& sink, int local, int lane, int g,
-                               int h_q, int nchunk, const TopmOut& tm, int local_from) {
+                               int h_q, int nchunk, const TopmOut& tm, int local_from,
+                               uint32_t* flo = nullptr) {
     constexpr int KPL = C / 64;   // keys per lane
     static_assert(KPL % 4 == 0, "lanes read whole 16-byte key groups");
     constexpr uint32_t kStageMax = stage_max<C>();
@@ -161,7 +172,27 @@ __device__ inline void extract(const Item<T>& it, int n, uint32_t M, uint32_t* r
         }
         if (lane == 0) warm[n] = cut;
     }
-    const uint32_t lo = cut > 1u ? cut : 1u;   // key 0 marks an empty slot
+    uint32_t pub = cut;   // the published cutoff
+    if (flo && cut != 0u) {   // uniform
+        uint32_t* flo_tag = flo + g;
+        const uint32_t tag = 1u + (uint32_t)(it.b * h_q + it.kh * g);
+        const bool same = flo_tag[n] == tag;
+        const uint32_t fl = flo[n];
+        if (same && fl < cut) {
+            uint32_t kx = 0;
+#pragma unroll
+            for (int e = 0; e < KPL; ++e) kx = kk[e] > kx ? kk[e] : kx;
+            const float fm = key_float(wave_umax(kx));
+            const float fc = key_float(cut), ff = key_float(fl);
+            if (fc - ff > 0.25f * (fm - fc)) pub = fl;
+        }
+        __builtin_amdgcn_s_waitcnt(0xc07f);   // every lane has read flo before lane 0 writes it
+        if (lane == 0) {
+            flo[n] = same && fl < cut ? fl : cut;
+            flo_tag[n] = tag;
+        }
+    }
+    const uint32_t lo = pub > 1u ? pub : 1u;   // key 0 marks an empty slot
     uint32_t kc = 0;
 #pragma unroll
     for (int e = 0; e < KPL; ++e) kc += kk[e] >= lo ? 1u : 0u;
@@ -221,7 +252,7 @@ __device__ inline void extract(const Item<T>& it, int n, uint32_t M, uint32_t* r
     }
     if (lane == 0) {
         const uint64_t abs_off = sink.base + off;
-        const uint4 m = make_uint4((uint32_t)abs_off, total, cut, (uint32_t)(abs_off >> 32));
+        const uint4 m = make_uint4((uint32_t)abs_off, total, pub, (uint32_t)(abs_off >> 32));
         const int e = local * g + n;   // staged while it fits, like the lists
         if (e < kMetaStage) {
             sink.meta_stg[e] = m;
