@@ -851,11 +851,11 @@ __device__ inline void calib_tau(const float2* __restrict__ stat, const uint4* _
 }
 
 // ---- union select, one workgroup per row -------------------------------------------
-// Fast path, for rows of at most 256 chunks. tpc = floor(256 / chunks) threads
-// share each chunk's list: thread t takes chunk t / tpc and, within it, a run
-// of P consecutive entries (P even, so the run starts on a 16-byte boundary
-// and is read with 16-byte loads straight from the list the chunk's meta entry
-// points at). Thread order is therefore position order. The union's key of
+// Fast path, for rows of at most 256 chunks whose union of lists holds at most
+// 256 KPT entries: thread t takes entries [KPT t, KPT t + KPT) of the lists
+// laid end to end (load_union_fast), read with 16-byte loads straight from the
+// lists the chunks' records point at. Thread order is therefore position
+// order. The union's key of
 // rank N_eff, T, is searched in [max chunk cutoff, max key]: the count of keys
 // at or above the lower end being >= N_eff is exactly the proof that every
 // chunk cutoff is <= T, so the result is exact. The search is a histogram
@@ -866,14 +866,118 @@ __device__ inline void calib_tau(const float2* __restrict__ stat, const uint4* _
 // keys at or above a bin's lower end are exactly N_eff. Compaction is one
 // workgroup prefix scan of the packed (above T, equal to T) counts: equal keys
 // at T are taken in position order. The kept entries are staged in LDS and
-// written with 16-byte stores. Rows the fast path cannot take (a run longer
-// than KPT, or the proof failing) go through union_row in the same workgroup:
+// written with 16-byte stores. Rows the fast path cannot take (a union larger
+// than 256 KPT, or the proof failing) go through union_row in the same workgroup:
 // the multi-tile union select, or the dense recompute.
+// One wave's copy of a row's union layout for the fast path: where chunk c's
+// list starts in the pool (even; bit 0 set when its length is odd) and the
+// exclusive prefix of the lengths rounded up to even. Each wave builds its own
+// copy, so no workgroup barrier is needed before the list loads.
+struct WaveUnion {
+    int64_t coff[kUnionThreads];
+    uint32_t pref[kUnionThreads + 1];
+};
 struct FastShared {
     uint32_t hist[3][kUnionThreads];       // one bin per thread, three in rotation
     uint4 red[kUnionThreads / 64];         // wave maxima: max key, max cutoff, overflow
     uint32_t scan[kUnionThreads / 64];     // wave totals of the compaction scan
+    WaveUnion wu[kUnionThreads / 64];
 };
+
+// Chunk records of a row, requested at kernel start before the row length is
+// known: lane l holds chunks [l cpl, l cpl + cpl), cpl = ceil(nchunk / 64)
+// (at most 4: the fast path takes rows of at most 256 chunks).
+struct ChunkRecs {
+    uint4 m[4];
+    int cpl;
+};
+template <class Rec>
+__device__ inline ChunkRecs load_chunk_recs(const Rec* __restrict__ rec, int nchunk, int lane) {
+    ChunkRecs r;
+    r.cpl = (nchunk + 63) >> 6;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int c = lane * r.cpl + j;
+        r.m[j] = make_uint4(0u, 0u, 0u, 0u);
+        if (j < r.cpl && c < nchunk) r.m[j] = rec[c];
+    }
+    return r;
+}
+
+// Fast-path load of a row's union of chunk lists (nch <= 256 chunks): thread
+// t takes entries [KPT t, KPT t + KPT) of the lists laid end to end in chunk
+// order, so thread order is position order and any split of the union among
+// the chunks fits as long as the union holds at most 256 KPT entries (a chunk
+// that published its whole list, a recency window say, included). Lists
+// start at even pool entries and are allocated in whole pairs: with the
+// lengths rounded up to even every pair below is one aligned 16-byte load
+// inside the list's allocation; the pad entry of an odd list and every slot
+// past the union read as key 0 (below every real key). Returns the union's
+// size (uniform); maxcut = the largest chunk cutoff. wu: this wave's LDS.
+template <int KPT>
+__device__ inline uint32_t load_union_fast(const uint2* __restrict__ cand, const ChunkRecs& cr,
+                                           int nch, WaveUnion& wu, uint32_t& maxcut,
+                                           uint32_t (&key)[KPT], int32_t (&pos)[KPT]) {
+    const int tid = threadIdx.x, lane = tid & 63;
+    uint32_t run = 0, mc = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int c = lane * cr.cpl + j;
+        if (j < cr.cpl && c < nch) {
+            run += (cr.m[j].y + 1u) & ~1u;
+            mc = cr.m[j].z > mc ? cr.m[j].z : mc;
+        }
+    }
+    uint32_t tot;
+    uint32_t at = wave_incl_scan(run, tot) - run;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int c = lane * cr.cpl + j;
+        if (j < cr.cpl && c < nch) {
+            wu.pref[c] = at;
+            wu.coff[c] = (int64_t)(((uint64_t)cr.m[j].w << 32) | cr.m[j].x) | (int64_t)(cr.m[j].y & 1u);
+            at += (cr.m[j].y + 1u) & ~1u;
+        }
+    }
+    if (lane == 0) wu.pref[nch] = tot;
+    maxcut = wave_umax(mc);
+    // this wave's LDS stores are complete before its lanes read each other's
+    __builtin_amdgcn_s_waitcnt(0xc07f);
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+    const uint32_t e0 = (uint32_t)(KPT * tid);
+    int c = 0;
+    if (e0 < tot) {   // the last chunk whose range starts at or before e0
+        int hi = nch;
+        while (hi - c > 1) {
+            const int mid = (c + hi) >> 1;
+            if (wu.pref[mid] <= e0) c = mid; else hi = mid;
+        }
+    }
+    uint4 ev[KPT / 2];
+    uint32_t vm = 0;   // bit s: slot s holds an entry
+#pragma unroll
+    for (int p = 0; p < KPT / 2; ++p) {
+        const uint32_t j = e0 + 2u * (uint32_t)p;
+        const uint4* a = reinterpret_cast<const uint4*>(cand);   // past the union: unused
+        if (j < tot) {
+            while (wu.pref[c + 1] <= j) ++c;
+            const int64_t cw = wu.coff[c];
+            const uint32_t off = j - wu.pref[c];
+            const uint32_t tl = wu.pref[c + 1] - wu.pref[c] - (uint32_t)(cw & 1);
+            a = reinterpret_cast<const uint4*>(cand + ((cw & ~(int64_t)1) + off));
+            vm |= (off < tl ? 1u : 0u) << (2 * p);
+            vm |= (off + 1u < tl ? 1u : 0u) << (2 * p + 1);
+        }
+        ev[p] = *a;
+    }
+#pragma unroll
+    for (int s = 0; s < KPT; ++s) {
+        const uint4 e = ev[s >> 1];
+        pos[s] = (int32_t)((s & 1) ? e.z : e.x);
+        key[s] = (vm >> s) & 1u ? ((s & 1) ? e.w : e.y) : 0u;
+    }
+    return tot;
+}
 // The fast path's output staging (indices, then logits) follows FastShared.
 __host__ __device__ constexpr size_t select_stage_offset() {
     return (sizeof(FastShared) + 15) & ~(size_t)15;
@@ -961,8 +1065,10 @@ __global__ __launch_bounds__(kUnionThreads, 4) void select_union(
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int b = row / h_q;
-    // this thread's chunk record for a full-length row, requested together with
-    // the length (the usual case needs no second round trip)
+    // the row's chunk records, requested together with the length (no second
+    // round trip before the list loads): lane l's chunks, and this thread's
+    // chunk in the per-chunk layout of a full-length row
+    const ChunkRecs crec = load_chunk_recs(cand_meta + (int64_t)row * nchunk, nchunk, lane);
     const int tpc_full = nchunk <= NT ? NT / nchunk : 1;
     const int c_full = tid / tpc_full < nchunk ? tid / tpc_full : nchunk - 1;
     const uint4 m_full = cand_meta[(int64_t)row * nchunk + c_full];
@@ -1054,44 +1160,60 @@ __global__ __launch_bounds__(kUnionThreads, 4) void select_union(
         float* st_val = reinterpret_cast<float*>(st_idx + nst);
 
         F.hist[0][tid] = 0u;
-        // this thread's run of its chunk's list
-        const int tpc = NT / nch;
-        const int c = tid / tpc;
-        const int sub = tid - c * tpc;
-        const bool cv = c < nch;
-        const uint4 m = nch == nchunk ? m_full : cand_meta[(int64_t)row * nchunk + (cv ? c : nch - 1)];
-        const uint32_t cnt = cv ? m.y : 0u;
-        const uint32_t P = (((cnt + (uint32_t)tpc - 1u) / (uint32_t)tpc) + 1u) & ~1u;
-        const uint32_t j0 = (uint32_t)sub * P;
-        const uint32_t mine = cnt > j0 ? (cnt - j0 < P ? cnt - j0 : P) : 0u;
-        const uint32_t npair = (mine + 1u) >> 1;
-        // lists start at even pool entries and runs at even offsets: 16-byte
-        // aligned; pairs past the run re-read its last pair (an empty run reads
-        // the pool's first pair), so every load is unconditional and in bounds
-        const uint4* run = reinterpret_cast<const uint4*>(cand + ((((uint64_t)m.w << 32) | m.x) + j0));
-        uint4 ev[KPT / 2];
-    #pragma unroll
-        for (int p = 0; p < KPT / 2; ++p) {
-            const uint4* a = npair ? run + ((uint32_t)p < npair ? (uint32_t)p : npair - 1u)
-                                   : reinterpret_cast<const uint4*>(cand);
-            ev[p] = *a;
-        }
+        // this thread's KPT entries of the union, in position order: when every
+        // chunk's list fits the runs of its tpc = 256 / chunks threads (the
+        // usual case), thread t takes a run of P consecutive entries of chunk
+        // t / tpc (P even, so runs start on 16-byte boundaries); otherwise the
+        // lists are laid end to end (load_union_fast)
         uint32_t key[KPT];
         int32_t pos[KPT];
+        uint32_t wcut, wo;
+        const int tpc = NT / nch;
+        uint32_t lmax = 0;
+    #pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int cj = lane * crec.cpl + j;
+            if (j < crec.cpl && cj < nch) lmax = crec.m[j].y > lmax ? crec.m[j].y : lmax;
+        }
+        lmax = wave_umax(lmax);
+        if (((((lmax + (uint32_t)tpc - 1u) / (uint32_t)tpc) + 1u) & ~1u) <= (uint32_t)KPT) {
+            const int c = tid / tpc;
+            const int sub = tid - c * tpc;
+            const bool cv = c < nch;
+            const uint4 m = nch == nchunk ? m_full : cand_meta[(int64_t)row * nchunk + (cv ? c : nch - 1)];
+            const uint32_t cnt = cv ? m.y : 0u;
+            const uint32_t P = (((cnt + (uint32_t)tpc - 1u) / (uint32_t)tpc) + 1u) & ~1u;
+            const uint32_t j0 = (uint32_t)sub * P;
+            const uint32_t mine = cnt > j0 ? (cnt - j0 < P ? cnt - j0 : P) : 0u;
+            const uint32_t npair = (mine + 1u) >> 1;
+            // pairs past the run re-read its last pair (an empty run reads the
+            // pool's first pair), so every load is unconditional and in bounds
+            const uint4* run = reinterpret_cast<const uint4*>(cand + ((((uint64_t)m.w << 32) | m.x) + j0));
+            uint4 ev[KPT / 2];
+    #pragma unroll
+            for (int p = 0; p < KPT / 2; ++p) {
+                const uint4* a = npair ? run + ((uint32_t)p < npair ? (uint32_t)p : npair - 1u)
+                                       : reinterpret_cast<const uint4*>(cand);
+                ev[p] = *a;
+            }
+    #pragma unroll
+            for (int s = 0; s < KPT; ++s) {
+                const uint4 e = ev[s >> 1];
+                pos[s] = (int32_t)((s & 1) ? e.z : e.x);
+                key[s] = (uint32_t)s < mine ? ((s & 1) ? e.w : e.y) : 0u;
+            }
+            wcut = wave_umax(cv ? m.z : 0u);
+            wo = 0u;
+        } else {
+            const uint32_t utot = load_union_fast<KPT>(cand, crec, nch, F.wu[wave], wcut, key, pos);
+            wo = utot > (uint32_t)(NT * KPT) ? 1u : 0u;   // does not fit
+        }
         uint32_t kmax = 0;
     #pragma unroll
-        for (int s = 0; s < KPT; ++s) {
-            const uint4 e = ev[s >> 1];
-            const bool v = (uint32_t)s < mine;   // empty slots hold key 0, below every real key
-            pos[s] = (int32_t)((s & 1) ? e.z : e.x);
-            key[s] = v ? ((s & 1) ? e.w : e.y) : 0u;
-            kmax = key[s] > kmax ? key[s] : kmax;
-        }
+        for (int s = 0; s < KPT; ++s) kmax = key[s] > kmax ? key[s] : kmax;
         {
             const uint32_t wk = wave_umax(kmax);
-            const uint32_t wc = wave_umax(cv ? m.z : 0u);
-            const uint32_t wo = wave_umax(P > (uint32_t)KPT ? 1u : 0u);
-            if (lane == 0) F.red[wave] = make_uint4(wk, wc, wo, 0u);
+            if (lane == 0) F.red[wave] = make_uint4(wk, wcut, wo, 0u);
         }
         __syncthreads();
         uint32_t maxcut = 0, ovf = 0;
@@ -1255,7 +1377,7 @@ __global__ __launch_bounds__(kUnionThreads, 4) void select_union(
     if constexpr (!SPQ) {
         // no kept entry, too many chunks, or no proof: the general code, whole
         // row in part 0 (the decision is the same in every part of the row)
-        if (n_eff == 0 || nch > NT || !fast())
+        if (n_eff == 0 || nch > NT || crec.cpl > 4 || !fast())
             if (part == 0) general();
         return;
     } else {
@@ -1266,7 +1388,7 @@ __global__ __launch_bounds__(kUnionThreads, 4) void select_union(
             row_cnt[row] = 0;
             row_flag[row] = 0;
         }
-        if (n_eff > 0 && (nch > NT || !fast())) {
+        if (n_eff > 0 && (nch > NT || crec.cpl > 4 || !fast())) {
             // the general code writes the list; this workgroup reads it back into
             // the stage (completed stores and the barrier order the global
             // accesses within it; n_eff bounds the reads)
@@ -1362,6 +1484,7 @@ struct ThreshShared {
     uint4 red[kUnionThreads / 64];
     float redf[kUnionThreads / 64];
     uint32_t scan[kUnionThreads / 64];
+    WaveUnion wu[kUnionThreads / 64];
 };
 __host__ __device__ constexpr size_t thresh_stage_offset() {
     return (sizeof(ThreshShared) + 15) & ~(size_t)15;
@@ -1413,6 +1536,19 @@ __global__ __launch_bounds__(kUnionThreads, 4) void select_thresh(
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int b = row / h_q;
     const int i = row - b * h_q;
+    // the row's chunk records and statistics, requested together with the
+    // length (lane l: chunks [l cpl, l cpl + cpl))
+    const ChunkRecs crec = load_chunk_recs(cand_meta + (int64_t)row * nchunk, nchunk, lane);
+    const int tpc_full = nchunk <= NT ? NT / nchunk : 1;
+    const int c_full = tid / tpc_full < nchunk ? tid / tpc_full : nchunk - 1;
+    const uint4 m_full = cand_meta[(int64_t)row * nchunk + c_full];
+    float2 cst[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int c = lane * crec.cpl + j;
+        cst[j] = make_float2(0.f, 0.f);
+        if (j < crec.cpl && c < nchunk) cst[j] = cand_stat[(int64_t)row * nchunk + c];
+    }
     const int64_t L = clamp_len(lens[b], S_max);
     const int nch = (int)((L + chunk - 1) / chunk);
     const T* vb = v + (int64_t)(b * h_v + i / (h_q / h_v)) * S_max * DH;
@@ -1460,70 +1596,82 @@ __global__ __launch_bounds__(kUnionThreads, 4) void select_thresh(
     const uint4* meta = cand_meta + (int64_t)row * nchunk;
     const float2* stat = cand_stat + (int64_t)row * nchunk;
     const float t = tau[row];
-    if (nch <= NT) {
-        // Fast path, rows of at most 256 chunks: each thread's chunk record and
-        // statistics in one round, then its run of the chunk's list (as in
-        // select_union) requested before the reductions that give the LSE.
+    if (nch <= NT && crec.cpl <= 4) {
+        // Fast path, rows of at most 256 chunks whose union fits 256 KPT
+        // entries: the union loaded as in select_union (per-chunk runs when
+        // every list fits them, else laid end to end), and the row's largest
+        // cutoff and LSE formed by every wave alike from the chunk records and
+        // statistics its lanes hold, so no workgroup barrier comes before the
+        // count.
+        uint32_t key[KPT];
+        int32_t pos[KPT];
+        uint32_t mc = 0, lmax = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int cj = lane * crec.cpl + j;
+            if (j < crec.cpl && cj < nch) {
+                mc = crec.m[j].z > mc ? crec.m[j].z : mc;
+                lmax = crec.m[j].y > lmax ? crec.m[j].y : lmax;
+            }
+        }
+        const uint32_t maxcut = wave_umax(mc);
+        lmax = wave_umax(lmax);
         const int tpc = NT / nch;
-        const int c = tid / tpc;
-        const int sub = tid - c * tpc;
-        const bool cv = c < nch;
-        const uint4 m = meta[cv ? c : nch - 1];
-        const float2 cs = stat[cv ? c : nch - 1];
-        const uint32_t cnt = cv ? m.y : 0u;
-        const uint32_t P = (((cnt + (uint32_t)tpc - 1u) / (uint32_t)tpc) + 1u) & ~1u;
-        const uint32_t j0 = (uint32_t)sub * P;
-        const uint32_t mine = cnt > j0 ? (cnt - j0 < P ? cnt - j0 : P) : 0u;
-        const uint32_t npair = (mine + 1u) >> 1;
-        const uint4* run = reinterpret_cast<const uint4*>(cand + ((((uint64_t)m.w << 32) | m.x) + j0));
-        uint4 ev[KPT / 2];
+        bool fits = true;
+        if (((((lmax + (uint32_t)tpc - 1u) / (uint32_t)tpc) + 1u) & ~1u) <= (uint32_t)KPT) {
+            const int c = tid / tpc;
+            const int sub = tid - c * tpc;
+            const bool cv = c < nch;
+            const uint4 m = nch == nchunk ? m_full : meta[cv ? c : nch - 1];
+            const uint32_t cnt = cv ? m.y : 0u;
+            const uint32_t P = (((cnt + (uint32_t)tpc - 1u) / (uint32_t)tpc) + 1u) & ~1u;
+            const uint32_t j0 = (uint32_t)sub * P;
+            const uint32_t mine = cnt > j0 ? (cnt - j0 < P ? cnt - j0 : P) : 0u;
+            const uint32_t npair = (mine + 1u) >> 1;
+            const uint4* run = reinterpret_cast<const uint4*>(cand + ((((uint64_t)m.w << 32) | m.x) + j0));
+            uint4 ev[KPT / 2];
 #pragma unroll
-        for (int p2 = 0; p2 < KPT / 2; ++p2) {
-            const uint4* a = npair ? run + ((uint32_t)p2 < npair ? (uint32_t)p2 : npair - 1u)
-                                   : reinterpret_cast<const uint4*>(cand);
-            ev[p2] = *a;
-        }
-        // max chunk logit, max cutoff and overflow over the workgroup
-        const bool lead = cv && sub == 0;
-        {
-            const uint32_t wk = wave_umax(lead ? float_key(cs.x) : 0u);
-            const uint32_t wc = wave_umax(lead ? m.z : 0u);
-            const uint32_t wo = wave_umax(P > (uint32_t)KPT ? 1u : 0u);
-            if (lane == 0) F.red[wave] = make_uint4(wk, wc, wo, 0u);
-        }
-        __syncthreads();
-        uint32_t km = 0, maxcut = 0, ovf = 0;
-#pragma unroll
-        for (int w = 0; w < NT / 64; ++w) {
-            const uint4 r = F.red[w];
-            km = r.x > km ? r.x : km;
-            maxcut = r.y > maxcut ? r.y : maxcut;
-            ovf |= r.z;
-        }
-        const float M = key_float(km);
-        {
-            const float se = wave_fsum(lead ? cs.y * __expf(cs.x - M) : 0.f);
-            if (lane == 0) F.redf[wave] = se;
-        }
-        __syncthreads();
-        float S = 0.f;
-#pragma unroll
-        for (int w = 0; w < NT / 64; ++w) S += F.redf[w];
-        // theta = log(tau) + LSE; tau = 0 keeps every position, NaN keeps none
-        const float theta = t == t ? __logf(t) + (M + __logf(S)) : __builtin_inff();
-        const uint32_t tk = float_key(theta);
-        const uint32_t lo = tk > 1u ? tk : 1u;   // key 0 marks an empty slot
-        if (ovf == 0u && maxcut <= tk) {   // uniform: lists fit and are complete for theta
-            uint32_t key[KPT];
-            int32_t pos[KPT];
-            uint32_t ng = 0;
+            for (int p2 = 0; p2 < KPT / 2; ++p2) {
+                const uint4* a = npair ? run + ((uint32_t)p2 < npair ? (uint32_t)p2 : npair - 1u)
+                                       : reinterpret_cast<const uint4*>(cand);
+                ev[p2] = *a;
+            }
 #pragma unroll
             for (int e = 0; e < KPT; ++e) {
                 const uint4 x = ev[e >> 1];
                 pos[e] = (int32_t)((e & 1) ? x.z : x.x);
                 key[e] = (uint32_t)e < mine ? ((e & 1) ? x.w : x.y) : 0u;
-                ng += key[e] >= lo ? 1u : 0u;
             }
+        } else {
+            uint32_t mc2;
+            fits = load_union_fast<KPT>(cand, crec, nch, F.wu[wave], mc2, key, pos) <=
+                   (uint32_t)(NT * KPT);
+        }
+        uint32_t kx = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int c = lane * crec.cpl + j;
+            if (j < crec.cpl && c < nch) {
+                const uint32_t kc = float_key(cst[j].x);
+                kx = kc > kx ? kc : kx;
+            }
+        }
+        const float M = key_float(wave_umax(kx));
+        float se = 0.f;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int c = lane * crec.cpl + j;
+            if (j < crec.cpl && c < nch) se += cst[j].y * __expf(cst[j].x - M);
+        }
+        const float S = wave_fsum(se);
+        // theta = log(tau) + LSE; tau = 0 keeps every position, NaN keeps none
+        const float theta = t == t ? __logf(t) + (M + __logf(S)) : __builtin_inff();
+        const uint32_t tk = float_key(theta);
+        const uint32_t lo = tk > 1u ? tk : 1u;   // key 0 marks an empty slot
+        if (fits && maxcut <= tk) {   // uniform: fits, complete for theta
+            uint32_t ng = 0;
+#pragma unroll
+            for (int e = 0; e < KPT; ++e) ng += key[e] >= lo ? 1u : 0u;
             uint32_t wt;
             const uint32_t incl = wave_incl_scan(ng, wt);
             if (lane == 0) F.scan[wave] = wt;

@@ -54,15 +54,15 @@ struct ListSink {
 constexpr int kMetaStage = 256;
 
 //
-// Hot chunks (flo != nullptr): flo[n] holds the lowest cutoff of the earlier
+// Row floor (flo != nullptr): flo[n] holds the lowest cutoff of the earlier
 // chunks of the same (b, key head) row that this workgroup extracted, tagged
 // in flo_tag[n] = 1 + b h_q + kh g (flo_tag = flo + g). A chunk whose cutoff
-// lies well above that floor -- by more than a quarter of the distance from
-// its cutoff to its largest key, in logit units -- holds more of the row's
-// top keys than its M suggest (a recency window, a block of sinks); its list
-// then reaches down to the floor, so that the selector does not have to
-// recompute it. Any cutoff keeps the result exact: every key left out is
-// still below the cutoff the chunk publishes.
+// lies above that floor publishes every key down to the floor instead: a
+// chunk that holds more of the row's top keys than its M suggest (a recency
+// window, a block of sinks) then needs no recompute in the selector, while a
+// chunk like its neighbours gains only the few keys between the two cutoffs.
+// Any cutoff keeps the result exact: every key left out is still below the
+// cutoff the chunk publishes.
 template <typename T, int C = kScanChunk>
 __device__ inline void extract(const Item<T>& it, int n, uint32_t M, uint32_t* row,
                                uint32_t* warm, const ListSink& sink, int local, int lane, int g,
@@ -178,14 +178,7 @@ __device__ inline void extract(const Item<T>& it, int n, uint32_t M, uint32_t* r
         const uint32_t tag = 1u + (uint32_t)(it.b * h_q + it.kh * g);
         const bool same = flo_tag[n] == tag;
         const uint32_t fl = flo[n];
-        if (same && fl < cut) {
-            uint32_t kx = 0;
-#pragma unroll
-            for (int e = 0; e < KPL; ++e) kx = kk[e] > kx ? kk[e] : kx;
-            const float fm = key_float(wave_umax(kx));
-            const float fc = key_float(cut), ff = key_float(fl);
-            if (fc - ff > 0.25f * (fm - fc)) pub = fl;
-        }
+        if (same && fl < cut) pub = fl;
         __builtin_amdgcn_s_waitcnt(0xc07f);   // every lane has read flo before lane 0 writes it
         if (lane == 0) {
             flo[n] = same && fl < cut ? fl : cut;
