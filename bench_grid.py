@@ -13,7 +13,8 @@ Every row is full (L_b = S). Inputs are the seeded synthetic caches of
 synth/ (N(0,1) values, 1% heavy-hitter key rows); SAGA's key cache is the
 GQA cache's first key head. Each timing cycles through enough copies of the
 layer's caches to exceed 512 MB, so no call finds the previous call's data in
-the last-level cache. Prints one JSON line per cell and a table of per-step
+the last-level cache, after SETTLE_MS of untimed calls (the clock ramp after
+the host-side input set-up). Prints one JSON line per cell and a table of per-step
 latency (us) and speedup over GQA full.
 
 Usage: python bench_grid.py [--steps K] [--batches 1,4,16] [--contexts 8192,...]
@@ -30,6 +31,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 ATOPN_EVERY = 32
+SETTLE_MS = 40
 
 
 def main():
@@ -58,9 +60,21 @@ def main():
     def bf16_dev(a):
         return torch.from_numpy(np.ascontiguousarray(a)).view(torch.bfloat16).to(dev)
 
+    def settle(fn):
+        # after the host has built a cell's inputs the GPU has sat idle, and its
+        # clocks take about 10 ms of work to reach their steady level: untimed
+        # calls for SETTLE_MS before every timed loop
+        torch.cuda.synchronize()
+        s0 = time.perf_counter()
+        i = 0
+        while (time.perf_counter() - s0) * 1e3 < SETTLE_MS:
+            for _ in range(8):
+                fn(i)
+                i += 1
+            torch.cuda.synchronize()
+
     def timed(fn, n):
-        for i in range(3):
-            fn(i)
+        settle(fn)
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for i in range(n):
@@ -119,8 +133,8 @@ def main():
 
                 n_at = max(args.steps, ATOPN_EVERY) // ATOPN_EVERY * ATOPN_EVERY
                 res = {"full": timed(full, args.steps), "exact_topN": timed(exact, args.steps)}
-                for i in range(3):
-                    atopn(i)
+                settle(atopn)
+                atopn(0)   # a calibration first, so that every timed stale step has a tau
                 torch.cuda.synchronize()
                 t0 = time.perf_counter()
                 for i in range(n_at):
