@@ -13,10 +13,14 @@
 //   2. nt_bf16x3: F = W C for all query and key heads (bf16 MFMA on C split
 //      into three bf16 parts, fp32 accuracy); nt_gemm: S and H from F (fp32
 //      MFMA);
-//   3. merge_pairs: per pair (a, b), in fp64, P = S_a + S_b is diagonalised by
-//      cyclic Jacobi rotations held in LDS; replaying the recorded rotations
-//      gives Y = P^+ S_a and Z = P^+ S_b (the transposes of the coefficients
-//      of Eq. 15: M(a, b) = W_a Y^T + W_b Z^T), and the pair weight of Eq. 16
+//   3. merge_pairs: per pair (a, b), in fp64, Y = P^+ S_a and Z = P^+ S_b for
+//      P = S_a + S_b (the transposes of the coefficients of Eq. 15: M(a, b) =
+//      W_a Y^T + W_b Z^T). A pair whose P is clearly regular (every
+//      eigenvalue well above the pseudo-inverse cutoff, from the Frobenius
+//      norms of P and its inverse, or else a power-iteration estimate) takes
+//      P^+ = P^{-1} by Gauss-Jordan elimination; any other pair is
+//      diagonalised by cyclic Jacobi rotations held in LDS, whose recorded
+//      rotations are replayed to apply P^+. The pair weight of Eq. 16
 //      follows from the identity
 //        L_{a,b}(M(a, b)) = <Z Delta, S_a Z> + <Y Delta, S_b Y>,
 //      Delta = (X W_a - X W_b)^T (X W_a - X W_b) (App. A's trace form with
