@@ -193,6 +193,17 @@ def test_union_rows_routed_to_the_general_code():
     _run_decode(x, to_device(x), case, 512, all_pairs(1, 4), "257 chunks")
 
 
+def test_rows_beyond_the_union_path():
+    # more than 512 chunks of 1024 positions: the decode call takes the dense
+    # logit path (K-scan to fp32 logits, dense select, sparse PV) even for a key
+    # group of 12; one row of 600000 positions, one just past the limit
+    case = synth.small_case(B=2, h_q=12, h_k=1, h_v=2, d=64, S_max=600000, N=1024,
+                            dtype="bf16", seed=67)
+    lens = np.array([600000, 524289], np.int32)
+    x = synth.make_inputs(case, lens)
+    _run_decode(x, to_device(x), case, 1024, all_pairs(2, 12), "beyond union path")
+
+
 def test_ragged_edge_lengths_and_nan_tail():
     case = synth.small_case(B=10, h_q=4, h_k=1, h_v=2, d=64, S_max=1030, N=16, dtype="bf16",
                             seed=47)
