@@ -1013,8 +1013,7 @@ __device__ inline const float* sq_qm(const SqArg<2>& a, int row, int dh) {
     return a.qm + (int64_t)row * dh;
 }
 
-// MODE 0 writes the kept lists (sel_idx / sel_val / idx_out).
-// MODE 1 (fused): the same workgroup then forms the softmax weights of the kept entries
+// MODE 1 (fused): the workgroup forms the softmax weights of the kept entries
 // and gathers their value rows (gather.h), writing out[row] directly: the
 // kept list never leaves LDS on the fast path (sel_idx / sel_val are not
 // written; idx_out is, when given). Rows are then mapped XCD-aware so the
@@ -1052,13 +1051,14 @@ __global__ __launch_bounds__(kUnionThreads, 4) void select_union(
     constexpr bool SPQ = MODE == 2;
     constexpr int NT = kUnionThreads;
     using G = Gather<T, DH>;
-    static_assert(MODE == 0 || NT == kGatherThreads, "one gather workgroup per row");
+    static_assert(MODE == 1 || MODE == 2, "fused decode / calibration, or SparQ");
+    static_assert(NT == kGatherThreads, "one gather workgroup per row");
     extern __shared__ __attribute__((aligned(16))) unsigned char sel_lds[];
     FastShared& F = *reinterpret_cast<FastShared*>(sel_lds);
     UnionShared& U = *reinterpret_cast<UnionShared*>(sel_lds);
     // the nsplit parts of a row are adjacent logical workgroups
-    const int lid = MODE ? xcd_logical((int)blockIdx.x, rows * nsplit) : (int)blockIdx.x;
-    if (MODE && lid >= rows * nsplit) return;   // the grid is rounded up to whole XCD shares
+    const int lid = xcd_logical((int)blockIdx.x, rows * nsplit);
+    if (lid >= rows * nsplit) return;   // the grid is rounded up to whole XCD shares
     const int row = lid / nsplit;
     const int part = lid - row * nsplit;
     const int tid = threadIdx.x;
@@ -1153,8 +1153,6 @@ __global__ __launch_bounds__(kUnionThreads, 4) void select_union(
     // row needs the general code; that call sits outside it so the fast path's
     // register arrays are dead across it.
     auto fast = [&]() -> bool {
-        int32_t* oi = sel_idx + (int64_t)row * N;
-        float* ov = sel_val + (int64_t)row * N;
         int32_t* ou = idx_out ? idx_out + (int64_t)row * N : nullptr;
         int32_t* st_idx = reinterpret_cast<int32_t*>(sel_lds + select_stage_offset());
         float* st_val = reinterpret_cast<float*>(st_idx + nst);
@@ -1356,23 +1354,7 @@ __global__ __launch_bounds__(kUnionThreads, 4) void select_union(
                                  nsplit, split_part, split_cnt, out + (int64_t)row * DH);
             return true;
         }
-        if constexpr (SPQ) return true;   // the list stays staged for the SparQ tail
-        const bool v4 = (((uintptr_t)oi | (uintptr_t)ov | (uintptr_t)ou) & 15u) == 0;
-        const int n4 = v4 ? n_eff / 4 : 0;
-        for (int j = tid; j < n4; j += NT) {
-            const int4 vi = reinterpret_cast<const int4*>(st_idx)[j];
-            reinterpret_cast<int4*>(oi)[j] = vi;
-            reinterpret_cast<float4*>(ov)[j] = reinterpret_cast<const float4*>(st_val)[j];
-            if (ou) reinterpret_cast<int4*>(ou)[j] = vi;
-        }
-        for (int j = 4 * n4 + tid; j < N; j += NT) {
-            const bool kept = j < n_eff;
-            oi[j] = kept ? st_idx[j] : -1;
-            ov[j] = kept ? st_val[j] : -__builtin_inff();
-            if (ou) ou[j] = kept ? st_idx[j] : -1;
-        }
-
-        return true;
+        return true;   // SparQ: the list stays staged for the tail
     };
     if constexpr (!SPQ) {
         // no kept entry, too many chunks, or no proof: the general code, whole
@@ -1839,17 +1821,16 @@ hipError_t go_select_union(const TopmOut& tm, const int32_t* lens, int B, int h_
     auto nst_for = [&](int kpt) -> int {
         if (MODE == 2) return (int)round_up(N, 256);
         int64_t nst = (int64_t)N < (int64_t)kUnionThreads * kpt ? (int64_t)N : (int64_t)kUnionThreads * kpt;
-        return (int)(MODE == 1 ? (nst + 255) & ~(int64_t)255 : (nst + 3) & ~(int64_t)3);
+        return (int)((nst + 255) & ~(int64_t)255);
     };
     auto lds_for = [&](int kpt) -> size_t {
         size_t fast = select_stage_offset() + (size_t)nst_for(kpt) * 8;
-        if (MODE >= 1) fast += (size_t)(4 * d + 4) * sizeof(float);
+        fast += (size_t)(4 * d + 4) * sizeof(float);
         if (MODE == 2) fast += 32 * sizeof(float);
         return fast > sizeof(UnionShared) ? fast : sizeof(UnionShared);
     };
     if (MODE != 1) nsplit = 1;
-    const unsigned grid =
-        MODE ? (unsigned)(((rows * nsplit + 7) / 8) * 8) : (unsigned)rows;
+    const unsigned grid = (unsigned)(((rows * nsplit + 7) / 8) * 8);
 #define SAGA_SU(T, D, KPT)                                                                       \
     hipLaunchKernelGGL((select_union<T, D, KPT, MODE>), dim3(grid), dim3(kUnionThreads),          \
                        (unsigned)lds_for(KPT), st, tm.cand, tm.meta, lens, h_q, h_k, N, S_max,     \
