@@ -17,13 +17,6 @@ using namespace dev;
 
 constexpr int kGatherThreads = 256;
 
-// logical workgroup id from the hardware one: hardware ids are dealt to the 8
-// XCDs round-robin, so give XCD x the contiguous logical range [x*Q, (x+1)*Q).
-__device__ inline int xcd_logical(int hw, int total) {
-    const int q = (total + 7) >> 3;
-    return (hw & 7) * q + (hw >> 3);
-}
-
 template <typename T, int DH>
 struct Gather {
     using R = Row16<T>;

@@ -164,9 +164,16 @@ __global__ __launch_bounds__(kTopmThreads, 1) void kscan_topm(
     if (tm.zero && blockIdx.x == 0)
         for (int j = (int)threadIdx.x; j < tm.nzero; j += kTopmThreads) tm.zero[j] = 0;
     // The workgroup takes a contiguous range of items (consecutive chunks of a
-    // row), so that each head's previous cutoff is a good first guess.
+    // row), so that each head's previous cutoff is a good first guess. Ranges
+    // are dealt XCD-blocked: the workgroups of one XCD take consecutive ranges,
+    // i.e. whole rows of the batch, and the fused select places those rows on
+    // the same XCD (its lists are then read from that XCD's L2); a row's
+    // costly chunks (a recency window with a long list) are spread over all
+    // XCDs instead of landing on the same two.
     const int per = (nwork + gridDim.x - 1) / gridDim.x;
-    const int wbeg = blockIdx.x * per;
+    const int wr = gridDim.x % 8 == 0 ? xcd_logical((int)blockIdx.x, (int)gridDim.x)
+                                      : (int)blockIdx.x;
+    const int wbeg = wr * per;
     const int wend = wbeg + per < nwork ? wbeg + per : nwork;
     if (wbeg >= wend) return;   // uniform over the workgroup
     // The workgroup's pool range is the regions of its items (g C entries

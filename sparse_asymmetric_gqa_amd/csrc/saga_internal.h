@@ -317,6 +317,15 @@ __device__ inline float wave_fsum(float v) {
             __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 63)));
 }
 
+// Logical workgroup id from the hardware one: hardware ids are dealt to the
+// 8 XCDs round-robin, so give XCD x the contiguous logical range [x Q,
+// (x + 1) Q), Q = ceil(total / 8). A permutation of [0, total) when total is
+// a multiple of 8 (grids are rounded up to that, or keep the identity).
+__device__ inline int xcd_logical(int hw, int total) {
+    const int q = (total + 7) >> 3;
+    return (hw & 7) * q + (hw >> 3);
+}
+
 }  // namespace dev
 }  // namespace saga
 #endif

@@ -236,7 +236,10 @@ __global__ __launch_bounds__(kTopmThreads, 1) void sparq_topm(
     float* itab = reinterpret_cast<float*>(dtab + DH);   // 1 / tau of the row's heads
 
     const int per = (nwork + gridDim.x - 1) / gridDim.x;
-    const int wbeg = blockIdx.x * per;
+    // ranges dealt XCD-blocked, as in kscan_topm
+    const int wr = gridDim.x % 8 == 0 ? xcd_logical((int)blockIdx.x, (int)gridDim.x)
+                                      : (int)blockIdx.x;
+    const int wbeg = wr * per;
     const int wend = wbeg + per < nwork ? wbeg + per : nwork;
     if (wbeg >= wend) return;   // uniform over the workgroup
     ListSink sink;
