@@ -92,7 +92,7 @@ struct Gather {
         }
     }
 
-    // The row's output from its nparts partial sums src[p][DH] (written by
+    // The row's output from its nparts (1 .. kMaxSplit) partial sums src[p][DH] (written by
     // other workgroups with device-scope stores, read here with device-scope
     // loads, which do not hit a stale line of this XCD's L2), added in part
     // order: out[c] = (sum_p src[p][c]) / l, with l reduced from the threads'
@@ -107,10 +107,18 @@ struct Gather {
 #pragma unroll
         for (int w = 0; w < NW; ++w) l += red[w];
         for (int c = tid; c < DH; c += kGatherThreads) {
+            // all parts are requested before the first is added, so the row
+            // waits for one memory round trip rather than one per part; part
+            // indices past nparts re-read the last part and are not added
+            float v[kMaxSplit];
+#pragma unroll
+            for (int p = 0; p < kMaxSplit; ++p)
+                v[p] = __hip_atomic_load(src + (p < nparts ? p : nparts - 1) * DH + c,
+                                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             float sacc = 0.f;
-            for (int p = 0; p < nparts; ++p)
-                sacc += __hip_atomic_load(src + p * DH + c, __ATOMIC_RELAXED,
-                                          __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+            for (int p = 0; p < kMaxSplit; ++p)
+                if (p < nparts) sacc += v[p];
             o[c] = sacc / l;
         }
     }
