@@ -58,14 +58,24 @@ struct Gather {
                 for (int c = 0; c < EPL; ++c) acc[c] += wt * f[c];
             }
         };
+        // Whole pairs of batches per iteration, both summed unconditionally,
+        // and scheduling barriers between the phases: a batch's loads are then
+        // issued before the other batch's sums (a conditional sum lets the
+        // compiler move its loads down into it, and every batch would wait
+        // for all loads in flight). An odd last batch is summed after the loop.
         issue(ra, 0);
 #pragma unroll 1
-        for (int j = 0; j < nb; j += 2) {
+        for (int j = 0; j + 1 < nb; j += 2) {
             issue(rb, j + 1);
+            __builtin_amdgcn_sched_barrier(0);
             use(ra, j);
+            __builtin_amdgcn_sched_barrier(0);
             issue(ra, j + 2);
-            if (j + 1 < nb) use(rb, j + 1);   // uniform
+            __builtin_amdgcn_sched_barrier(0);
+            use(rb, j + 1);
+            __builtin_amdgcn_sched_barrier(0);
         }
+        if (nb & 1) use(ra, nb - 1);   // uniform
     }
 
     // Sums of acc over the workgroup, written to dst[0 .. DH) (global memory,
@@ -262,14 +272,19 @@ struct KeyDots {
                 }
             }
         };
-        issue(ra, 0);
+        issue(ra, 0);   // pairs of batches, phases in order, as in Gather::run
 #pragma unroll 1
-        for (int j = 0; j < nb; j += 2) {
+        for (int j = 0; j + 1 < nb; j += 2) {
             issue(rb, j + 1);
+            __builtin_amdgcn_sched_barrier(0);
             use(ra, j);
+            __builtin_amdgcn_sched_barrier(0);
             issue(ra, j + 2);
-            if (j + 1 < nb) use(rb, j + 1);   // uniform
+            __builtin_amdgcn_sched_barrier(0);
+            use(rb, j + 1);
+            __builtin_amdgcn_sched_barrier(0);
         }
+        if (nb & 1) use(ra, nb - 1);   // uniform
     }
 };
 
