@@ -35,6 +35,18 @@ using namespace dev;
 
 namespace {
 
+// Consumer waves of the scan's workgroup (after the kWaves producers). The
+// stream of r columns is short, so an item's time is the consumers'
+// extraction: a chain of dependent LDS and wave-reduction steps that leaves
+// the SIMDs about half idle at three waves each. Where the producers fit in
+// 128 registers (bf16, r <= 32) a fourth wave per SIMD runs twelve
+// consumers, one per query head of a 12-head group and item; other shapes
+// keep the eight of kscan_topm.
+template <typename T, int KT>
+constexpr int sq_consumers() { return sizeof(T) == 2 && KT <= 2 ? 12 : kConsumers; }
+template <typename T, int KT>
+constexpr int sq_threads() { return 64 * (kWaves + sq_consumers<T, KT>()); }
+
 typedef short v4s __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4s lds_v4s;
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -210,13 +222,15 @@ __host__ __device__ constexpr size_t sq_lds_words(int g) {
 // item's sub-tiles form straight-line code: the compiler then counts the
 // loads in flight exactly instead of waiting for all of them at a loop head.
 template <typename T, int DH, int KT>
-__global__ __launch_bounds__(kTopmThreads, 1) void sparq_topm(
+__global__ __launch_bounds__((sq_threads<T, KT>()), 1) void sparq_topm(
         const T* __restrict__ kt, const int32_t* __restrict__ lens, int h_q, int h_k,
         int64_t S_max, int nchunk, int nwork, int RP, int local,
         const int32_t* __restrict__ dims, const typename SqOp<T>::Q* __restrict__ qop,
         const float* __restrict__ inv_tau, TopmOut tm, uint32_t lds_bytes) {
     using TL = SqTile<T>;
     using Q = typename SqOp<T>::Q;
+    constexpr int NC = sq_consumers<T, KT>();
+    constexpr int NTH = sq_threads<T, KT>();
     constexpr int NL = TL::NL;
     constexpr int KTM = DH / 16;
     extern __shared__ uint32_t lds[];
@@ -257,7 +271,7 @@ __global__ __launch_bounds__(kTopmThreads, 1) void sparq_topm(
     int w = next_item<T, DH>(wbeg, 1, wend, nchunk, h_k, S_max, len_of, kt, cur);
     if (w >= wend) return;   // uniform over the workgroup
     if (!producer) {
-        for (int n = wave - kWaves; n < g; n += kConsumers)
+        for (int n = wave - kWaves; n < g; n += NC)
             if (lane == 0) warm[n] = 0u;
         if (threadIdx.x == 64 * kWaves) cursor[0] = cursor[1] = 0u;
     }
@@ -399,7 +413,7 @@ __global__ __launch_bounds__(kTopmThreads, 1) void sparq_topm(
         while (w < wend) {
             Item<T> nx = cur;
             const int wn = next_item<T, DH>(w + 1, 1, wend, nchunk, h_k, S_max, len_of, kt, nx);
-            if (t > 0) extract_item(prev, t - 1, wave - kWaves, kConsumers);
+            if (t > 0) extract_item(prev, t - 1, wave - kWaves, NC);
             lds_barrier();   // keys of item t are complete; buffer (t - 1) & 1 is free again
             prev = cur;
             last = cur;
@@ -409,14 +423,14 @@ __global__ __launch_bounds__(kTopmThreads, 1) void sparq_topm(
         }
     }
     // the last item, shared by all waves
-    extract_item(last, t - 1, wave, kWaves + kConsumers);
+    extract_item(last, t - 1, wave, kWaves + NC);
     lds_barrier();
     const uint32_t used = (sink.used[0] + 1u) & ~1u;
     const u32x4* s4 = reinterpret_cast<const u32x4*>(sink.stg);
     u32x4* d4 = reinterpret_cast<u32x4*>(sink.pool);
-    for (uint32_t j = threadIdx.x; j < used / 2; j += kTopmThreads) d4[j] = s4[j];
+    for (uint32_t j = threadIdx.x; j < used / 2; j += NTH) d4[j] = s4[j];
     const int nmeta = t * g < kMetaStage ? t * g : kMetaStage;   // items 0 .. t-1
-    for (int e = (int)threadIdx.x; e < nmeta; e += kTopmThreads)
+    for (int e = (int)threadIdx.x; e < nmeta; e += NTH)
         tm.meta[sink.meta_slot[e]] = sink.meta_stg[e];
 }
 
@@ -431,8 +445,9 @@ hipError_t go_sparq_scan(const void* kt, const int32_t* lens, const TopmOut& tm,
         const hipError_t e = allow_dynamic_lds(reinterpret_cast<const void*>(kern), lds);
         if (e != hipSuccess) return e;
     }
-    const int grid = resident_grid(kern, kTopmThreads, lds, nwork);
-    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kTopmThreads), lds, st, (const T*)kt, lens,
+    constexpr int nth = sq_threads<T, KT>();
+    const int grid = resident_grid(kern, nth, lds, nwork);
+    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(nth), lds, st, (const T*)kt, lens,
                        h_q, h_k, S_max, nchunk, nwork, RP, local, sw.dims,
                        reinterpret_cast<const typename SqOp<T>::Q*>(sw.qop), sw.inv_tau, tm,
                        (uint32_t)lds);
