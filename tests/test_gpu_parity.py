@@ -145,6 +145,12 @@ SMALL_BATCH = [
     (2, 12, 1, 2, 128, 40000, 2048, True),
     (1, 4, 1, 2, 64, 300, 64, False),
     (3, 16, 1, 8, 64, 5000, 512, True),
+    # rows that give every split count from 3 to 7 (512 / rows parts per row)
+    (10, 16, 1, 2, 64, 2000, 256, True),     # 160 rows: 3 parts
+    (8, 16, 2, 4, 64, 2500, 300, True),      # 128 rows: 4 parts
+    (8, 12, 1, 2, 128, 3000, 512, True),     # 96 rows: 5 parts
+    (7, 12, 1, 2, 128, 1500, 200, False),    # 84 rows: 6 parts
+    (6, 12, 1, 2, 64, 4000, 700, False),     # 72 rows: 7 parts
 ]
 
 
