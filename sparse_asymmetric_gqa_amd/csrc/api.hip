@@ -17,7 +17,7 @@ namespace saga {
 static size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
 Workspace carve(void* base, int B, int h_q, int h_k, int d, int N, int64_t S_max,
-                bool dense, int chunk, int nsplit, SparqWs* sq, int esize) {
+                bool dense, int chunk, int nsplit, SparqWs* sq) {
     Workspace w{};
     w.chunk = chunk;
     w.nsplit = nsplit;
@@ -46,13 +46,7 @@ Workspace carve(void* base, int B, int h_q, int h_k, int d, int N, int64_t S_max
                 take(rows * (size_t)nsplit * (size_t)d * sizeof(float)));
             w.split_cnt = reinterpret_cast<int32_t*>(take(rows * sizeof(int32_t)));
         }
-        if (sq) {
-            const size_t kr = (size_t)B * (size_t)h_k;
-            sq->dims = reinterpret_cast<int32_t*>(take(kr * (size_t)d * sizeof(int32_t)));
-            sq->qop = take(kr * (size_t)(d / 16) * 64 * 4 * (size_t)esize);
-            sq->inv_tau = reinterpret_cast<float*>(take(rows * sizeof(float)));
-            sq->qm = reinterpret_cast<float*>(take(rows * (size_t)d * sizeof(float)));
-        }
+        if (sq) sq->qm = reinterpret_cast<float*>(take(rows * (size_t)d * sizeof(float)));
     } else {
         const size_t nsplit = (size_t)dense_nsplit(S_max, h_q / h_k);
         w.part = reinterpret_cast<float*>(take(rows * nsplit * (size_t)(d + 2) * sizeof(float)));
@@ -398,8 +392,7 @@ size_t saga_sparq_workspace_size(int B, int h_q, int h_k, int h_v, int d, int N,
     if (check_shape(B, h_q, h_k, h_v, d, S_max, dtype) != SAGA_OK) return 0;
     if (N < 1 || N > (1 << 29) || r < 1 || r > d) return 0;
     saga::SparqWs sw{};
-    return saga::carve(nullptr, B, h_q, h_k, d, N, S_max, false, kScanChunk, 1, &sw,
-                       dtype == SAGA_BF16 ? 2 : 4).bytes;
+    return saga::carve(nullptr, B, h_q, h_k, d, N, S_max, false, kScanChunk, 1, &sw).bytes;
 }
 
 saga_status saga_sparq_attn(const void* q, const void* k_cache, const void* kt_cache,
@@ -422,12 +415,10 @@ saga_status saga_sparq_attn(const void* q, const void* k_cache, const void* kt_c
         S_max % (16 / esize) != 0)
         return SAGA_ERR_UNSUPPORTED;
     saga::SparqWs sw{};
-    const saga::Workspace need = saga::carve(nullptr, B, h_q, h_k, d, N, S_max, false, kScanChunk, 1, &sw,
-                                             esize);
+    const saga::Workspace need = saga::carve(nullptr, B, h_q, h_k, d, N, S_max, false, kScanChunk, 1, &sw);
     if (!workspace || workspace_bytes < need.bytes || (reinterpret_cast<uintptr_t>(workspace) & 255u))
         return SAGA_ERR_WORKSPACE;
-    const saga::Workspace w = saga::carve(workspace, B, h_q, h_k, d, N, S_max, false, kScanChunk, 1, &sw,
-                                          esize);
+    const saga::Workspace w = saga::carve(workspace, B, h_q, h_k, d, N, S_max, false, kScanChunk, 1, &sw);
     const bool bf16 = dtype == SAGA_BF16;
     clear_stale_error();
     // Step 1 on the kept dims into candidate lists with chunk statistics (the

@@ -41,10 +41,7 @@ struct Workspace {
 
 // SparQ-style scoring state per call (written by the scan's set-up kernel):
 struct SparqWs {
-    int32_t* dims;     // [B*h_k][RP]   kept query dims, ascending, -1 padded (RP = round_up(r, 16))
-    void* qop;         // [B*h_k][d/16][64] x 4 elements of the cache type: the scan's query operand
-    float* inv_tau;    // [B*h_q]       1 / tau (0: no query mass on the dims)
-    float* qm;         // [B*h_q][d]    q / tau on the dims, 0 elsewhere
+    float* qm;         // [B*h_q][d]    q / tau on the kept dims, 0 elsewhere (written by the scan)
 };
 
 inline int num_chunks(int64_t S_max, int chunk = kScanChunk) {
@@ -76,9 +73,9 @@ int max_union_chunks();
 // Carve the decode workspace (dense == false) or the dense one out of `base`
 // (base may be null to only compute the size), for K-scan items of `chunk`
 // positions and `nsplit` value-gather parts per row. With sq, the SparQ state
-// follows the decode part (esize: bytes per cache element).
+// follows the decode part.
 Workspace carve(void* base, int B, int h_q, int h_k, int d, int N, int64_t S_max, bool dense,
-                int chunk, int nsplit, SparqWs* sq = nullptr, int esize = 2);
+                int chunk, int nsplit, SparqWs* sq = nullptr);
 
 // The decode workspace (chunk and split from the shape) and the Atop-N one
 // (2N kept slots per row).

@@ -2,14 +2,16 @@
 // Bandwidth-Efficient LLM Inference", Step 1 with its GQA modification),
 // feeding the top-M candidate lists of the exact path's selector.
 //
-// sparq_prep, one workgroup per (b, key head):
-//   u[c] = sum over the key head's g query heads of |q[c]| (fp32, heads in
-//   order); the r dims of largest u (equal sums: lower dim first), ascending,
-//   -1 padded to RP = round_up(r, 16); per query head the inverse temperature
-//   1 / tau = sqrt(|q|_1 / (d |q on dims|_1)), 0 when the head has no mass on
-//   the dims (its approximate scores are then all 0); qm = q / tau on the
-//   dims and 0 elsewhere (used by the selector to rescore kept rows); and the
-//   scan's matrix-core operand per 16-dim slice and lane.
+// The set-up of Step 1, per (b, key head) row: u[c] = sum over the key
+// head's g query heads of |q[c]| (fp32, heads in order); the r dims of
+// largest u (equal sums: lower dim first), ascending, -1 padded to
+// RP = round_up(r, 16); per query head the inverse temperature
+// 1 / tau = sqrt(|q|_1 / (d |q on dims|_1)), 0 when the head has no mass on
+// the dims (its approximate scores are then all 0); qm = q / tau on the dims
+// and 0 elsewhere (used by the selector to rescore kept rows); and the scan's
+// matrix-core operand per 16-dim slice and lane. Each producer wave of the
+// scan computes it for the rows it streams (sq_row_setup), so no dispatch
+// precedes the scan.
 //
 // sparq_topm: the producer / consumer workgroup of kscan_topm with the same
 // consumers (topm.h), but the producers stream only the r kept columns of the
@@ -29,6 +31,8 @@
 // window are ranked by nobody: the consumers count them in the chunk's
 // softmax statistics and then drop them (the selector keeps them anyway).
 #include "topm.h"
+
+#include <type_traits>
 
 namespace saga {
 using namespace dev;
@@ -58,105 +62,205 @@ template <typename T> struct SqOp;
 template <> struct SqOp<uint16_t> { using Q = u32x2; };
 template <> struct SqOp<float> { using Q = u32x4; };
 
-// One 256-thread workgroup per (b, key head). The group's g query rows are
-// staged in LDS as fp32 with one batch of loads; every later step reads LDS.
-constexpr int kPrepThreads = 256;
-
-template <typename T, int DH>
-__global__ __launch_bounds__(kPrepThreads) void sparq_prep(const T* __restrict__ q, int h_q,
-                                                           int h_k, int r, int RP,
-                                                           int32_t* __restrict__ dims,
-                                                           typename SqOp<T>::Q* __restrict__ qop,
-                                                           float* __restrict__ inv_tau,
-                                                           float* __restrict__ qm,
-                                                           int32_t* __restrict__ dims_out) {
-    constexpr int EV = 16 / (int)sizeof(T);   // elements per 16-byte load
-    __shared__ float qs[16 * DH];             // g <= 16 query rows
-    __shared__ float us[DH];
-    __shared__ int32_t keep[DH];
-    __shared__ int32_t sd[DH];
-    const int bkh = blockIdx.x;
-    const int b = bkh / h_k, kh = bkh - (bkh / h_k) * h_k;
-    const int g = h_q / h_k;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const T* qg = q + (int64_t)(b * h_q + kh * g) * DH;
-    for (int x = tid; x < g * DH / EV; x += kPrepThreads) {
-        const u32x4 v = reinterpret_cast<const u32x4*>(qg)[x];
-        if constexpr (sizeof(T) == 2) {
+// Step 1 set-up of one (b, key head) row, computed by one producer wave of the
+// scan on its own (no workgroup barrier, so the consumers never wait for it).
+// With c = lane + 64 i the lane's dims:
+//   u[c] = sum over the g query heads, in head order, of |q[c]| (fp32);
+//   dims = the r dims of largest u (equal sums: lower dim first), ascending,
+//          -1 padded to RP, into the wave's table dtab (which holds u first);
+//   1 / tau per head = sqrt(|q|_1 / (d |q on dims|_1)), 0 when the head has no
+//          mass on the dims (its approximate scores are then all 0): per-lane
+//          sums over the lane's dims in order, reduced over the wave, into
+//          itab (0 for heads >= g);
+//   qk   = the scan's query operand per 16-dim slice.
+// `writer` (the workgroup that scans the row's first chunk) also writes
+// qm = q / tau on the dims and 0 elsewhere (the selector rescores kept rows
+// with it) and, when asked, the dims in dims_out [r].
+// A call of its own (it runs once per row), so the item loop's registers are
+// not shared with it; its pointers carry their address spaces, since a
+// called function cannot infer them (it would use flat accesses).
+typedef __attribute__((address_space(3))) int32_t lds_i32;
+typedef __attribute__((address_space(3))) float lds_f32;
+template <typename T> using glb = __attribute__((address_space(1))) T;
+template <typename T, int DH, int KT>
+__device__ __noinline__ void sq_row_setup(const glb<T>* __restrict__ qg, int g, int r, int RP,
+                                          int lane, lds_i32* dtab, lds_f32* itab,
+                                          typename SqOp<T>::Q (&qk)[KT], bool writer,
+                                          glb<float>* __restrict__ qm_out,
+                                          glb<int32_t>* __restrict__ dims_out) {
+    constexpr int CPL = DH / 64;   // dims per lane
+    constexpr int GM = 16;         // g <= 16 query heads per key head
+    auto qval = [&](int j, int c) -> float {
+        if constexpr (sizeof(T) == 2)
+            return __uint_as_float((uint32_t)qg[(int64_t)j * DH + c] << 16);
+        else
+            return qg[(int64_t)j * DH + c];
+    };
+    // the g query rows at the lane's dims, all requested before the first use
+    // (bf16: a lane's dims packed in one register, its raw bits). The loads
+    // are unconditional (rows past g re-read row g - 1 and are zeroed after):
+    // a load whose register another path zeroes is waited for on the spot.
+    uint32_t qp[GM];
+    float qf[GM][CPL];
 #pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                qs[x * EV + 2 * c] = __uint_as_float(v[c] << 16);
-                qs[x * EV + 2 * c + 1] = __uint_as_float(v[c] & 0xFFFF0000u);
-            }
+    for (int j = 0; j < GM; ++j) {
+        const int jj = j < g ? j : g - 1;
+        if constexpr (sizeof(T) == 2) {
+            const uint32_t lo = (uint32_t)qg[(int64_t)jj * DH + lane];
+            const uint32_t hi = CPL == 2 ? (uint32_t)qg[(int64_t)jj * DH + lane + 64] : 0u;
+            qp[j] = lo | (hi << 16);
         } else {
 #pragma unroll
-            for (int c = 0; c < 4; ++c) qs[x * EV + c] = __uint_as_float(v[c]);
+            for (int i = 0; i < CPL; ++i) qf[j][i] = qval(jj, lane + 64 * i);
         }
     }
-    __syncthreads();
-    // u[c]: summed magnitudes over the group, heads in order
-    if (tid < DH) {
-        float u = 0.f;
-        for (int j = 0; j < g; ++j) u += fabsf(qs[j * DH + tid]);
-        us[tid] = u;
+#pragma unroll
+    for (int j = 0; j < GM; ++j) {
+        if (j < g) continue;   // uniform
+        qp[j] = 0u;
+#pragma unroll
+        for (int i = 0; i < CPL; ++i) qf[j][i] = 0.f;
     }
-    __syncthreads();
-    // rank of dim c: dims with a larger sum, or an equal sum and a lower index
-    if (tid < DH) {
-        const float u = us[tid];
-        int rank = 0;
-        for (int c2 = 0; c2 < DH; ++c2) {
-            const float v = us[c2];
-            rank += (v > u || (v == u && c2 < tid)) ? 1 : 0;
+    auto qv = [&](int j, int i) -> float {
+        if constexpr (sizeof(T) == 2)
+            return __uint_as_float(i == 0 ? qp[j] << 16 : qp[j] & 0xFFFF0000u);
+        else
+            return qf[j][i];
+    };
+    float u[CPL];
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) {
+        u[i] = 0.f;
+#pragma unroll
+        for (int j = 0; j < GM; ++j)
+            if (j < g) u[i] += fabsf(qv(j, i));   // uniform; heads in order
+    }
+    // The kept dims: with K the r-th largest of the d sums (order-preserving
+    // keys, found bit by bit from the top: the largest K with at least r sums
+    // at or above it), every dim above K and the first r - count(above K)
+    // dims equal to K in dim order -- exactly the dims whose rank (larger
+    // sums, or equal sums at lower dims) is below r.
+    uint32_t ku[CPL];
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) ku[i] = float_key(u[i]);
+    auto count_ge = [&](uint32_t x) -> uint32_t {
+        uint32_t c = 0;
+#pragma unroll
+        for (int i = 0; i < CPL; ++i) c += (uint32_t)__builtin_popcountll(ballot(ku[i] >= x));
+        return c;
+    };
+    uint32_t kth = 0u;
+#pragma unroll 4
+    for (int bit = 31; bit >= 0; --bit) {
+        const uint32_t cand = kth | (1u << bit);
+        if (count_ge(cand) >= (uint32_t)r) kth = cand;   // uniform
+    }
+    uint32_t n_gt = 0;
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) n_gt += (uint32_t)__builtin_popcountll(ballot(ku[i] > kth));
+    const uint32_t n_eq = (uint32_t)r - n_gt;   // ties kept, lowest dims first
+    bool keep[CPL];
+    uint64_t km[CPL];
+    uint32_t eq_before = 0;
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) {
+        const uint64_t me = ballot(ku[i] == kth);
+        keep[i] = ku[i] > kth || (ku[i] == kth && eq_before + lanes_below(me) < n_eq);
+        eq_before += (uint32_t)__builtin_popcountll(me);
+        km[i] = ballot(keep[i]);
+    }
+    // ascending list of the kept dims: a kept dim's place is the number of
+    // kept dims below it
+    for (int e = r + lane; e < RP; e += 64) dtab[e] = -1;
+    uint32_t below = 0;
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) {
+        const int c = lane + 64 * i;
+        if (keep[i]) {
+            const uint32_t at = below + lanes_below(km[i]);
+            dtab[at] = c;
+            if (writer && dims_out) dims_out[at] = c;
         }
-        keep[tid] = rank < r ? 1 : 0;
+        below += (uint32_t)__builtin_popcountll(km[i]);
     }
-    __syncthreads();
-    // ascending list of the kept dims, -1 padded to RP
-    if (tid < DH && keep[tid]) {
-        int at = 0;
-        for (int c2 = 0; c2 < tid; ++c2) at += keep[c2];
-        sd[at] = tid;
-        if (dims_out) dims_out[(int64_t)bkh * r + at] = tid;
-    }
-    for (int e = r + tid; e < RP; e += kPrepThreads) sd[e] = -1;
-    __syncthreads();
-    for (int e = tid; e < RP; e += kPrepThreads) dims[(int64_t)bkh * RP + e] = sd[e];
-    // per head (one wave each, in turn): inverse temperature and q / tau on the dims
-    for (int j = wave; j < g; j += kPrepThreads / 64) {
-        float num = 0.f, den = 0.f;
-        for (int c = lane; c < DH; c += 64) {
-            const float a = fabsf(qs[j * DH + c]);
+    // per head: 1 / tau. The lane's partial sums of every head first, then
+    // their wave sums for all heads together (wave_fsum's tree and order, so
+    // the bits are the same), then each head's 1 / tau in lane j; heads past
+    // g have no mass and get 0
+    float xd[GM], xn[GM];
+#pragma unroll
+    for (int j = 0; j < GM; ++j) {
+        float den = 0.f, num = 0.f;
+#pragma unroll
+        for (int i = 0; i < CPL; ++i) {
+            const float a = fabsf(qv(j, i));
             den += a;
-            num += keep[c] ? a : 0.f;
+            num += keep[i] ? a : 0.f;
         }
-        num = wave_fsum(num);
-        den = wave_fsum(den);
-        const float inv = num > 0.f ? sqrtf(den / ((float)DH * num)) : 0.f;
-        const int i = b * h_q + kh * g + j;
-        if (lane == 0) inv_tau[i] = inv;
-        for (int c = lane; c < DH; c += 64) qm[(int64_t)i * DH + c] = keep[c] ? qs[j * DH + c] * inv : 0.f;
+        xd[j] = den;
+        xn[j] = num;
     }
-    // the scan's query operand, one slice of 16 dims per wave in turn
+    auto dpp_step = [&](float (&x)[GM], auto ctrl) {
+#pragma unroll
+        for (int j = 0; j < GM; ++j)
+            x[j] += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x[j]),
+                                                               decltype(ctrl)::value, 0xf, 0xf,
+                                                               false));
+    };
+    dpp_step(xd, std::integral_constant<int, 0x111>{});
+    dpp_step(xn, std::integral_constant<int, 0x111>{});
+    dpp_step(xd, std::integral_constant<int, 0x112>{});
+    dpp_step(xn, std::integral_constant<int, 0x112>{});
+    dpp_step(xd, std::integral_constant<int, 0x114>{});
+    dpp_step(xn, std::integral_constant<int, 0x114>{});
+    dpp_step(xd, std::integral_constant<int, 0x118>{});
+    dpp_step(xn, std::integral_constant<int, 0x118>{});
+    auto total = [](float x) {
+        return (__int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 15)) +
+                __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 31))) +
+               (__int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 47)) +
+                __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 63)));
+    };
+    float myden = 0.f, mynum = 0.f;
+#pragma unroll
+    for (int j = 0; j < GM; ++j) {
+        const float dj = total(xd[j]), nj = total(xn[j]);
+        myden = lane == j ? dj : myden;
+        mynum = lane == j ? nj : mynum;
+    }
+    const float myinv = mynum > 0.f ? sqrtf(myden / ((float)DH * mynum)) : 0.f;
+    if (lane < GM) itab[lane] = myinv;
+    if (writer)   // qm from the workgroup that writes it
+#pragma unroll
+        for (int j = 0; j < GM; ++j) {
+            const float inv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(myinv), j));
+            if (j < g)   // uniform
+#pragma unroll
+                for (int i = 0; i < CPL; ++i)
+                    qm_out[(int64_t)j * DH + lane + 64 * i] = keep[i] ? qv(j, i) * inv : 0.f;
+        }
+    __builtin_amdgcn_s_waitcnt(0xc07f);   // the dims are in the table before they are read back
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+    // the scan's query operand, one slice of 16 dims at a time
     const int hd = lane & 15, G = lane >> 4;
-    for (int kt = wave; kt < RP / 16; kt += kPrepThreads / 64) {
+#pragma unroll
+    for (int kt = 0; kt < KT; ++kt) {
         uint32_t w[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            const int c = sd[16 * kt + 4 * G + e];
-            const float x = (hd < g && c >= 0) ? qs[hd * DH + c] : 0.f;
-            // qs holds the stored values exactly; back to the cache type
+            const int c = dtab[16 * kt + 4 * G + e];
+            const float xl = qval(hd < g ? hd : 0, c >= 0 ? c : 0);   // in bounds, unconditional
+            const float x = (hd < g && c >= 0) ? xl : 0.f;
+            // the cache's own values: back to its type exactly
             w[e] = sizeof(T) == 2 ? (__float_as_uint(x) >> 16) : __float_as_uint(x);
         }
-        typename SqOp<T>::Q o;
         if constexpr (sizeof(T) == 2) {
-            o[0] = w[0] | (w[1] << 16);
-            o[1] = w[2] | (w[3] << 16);
+            qk[kt][0] = w[0] | (w[1] << 16);
+            qk[kt][1] = w[2] | (w[3] << 16);
         } else {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) o[e] = w[e];
+            for (int e = 0; e < 4; ++e) qk[kt][e] = w[e];
         }
-        qop[((int64_t)bkh * (DH / 16) + kt) * 64 + lane] = o;
     }
 }
 
@@ -225,14 +329,13 @@ template <typename T, int DH, int KT>
 __global__ __launch_bounds__((sq_threads<T, KT>()), 1) void sparq_topm(
         const T* __restrict__ kt, const int32_t* __restrict__ lens, int h_q, int h_k,
         int64_t S_max, int nchunk, int nwork, int RP, int local,
-        const int32_t* __restrict__ dims, const typename SqOp<T>::Q* __restrict__ qop,
-        const float* __restrict__ inv_tau, TopmOut tm, uint32_t lds_bytes) {
+        const T* __restrict__ q, int r, float* __restrict__ qm, int32_t* __restrict__ dims_out,
+        TopmOut tm, uint32_t lds_bytes) {
     using TL = SqTile<T>;
     using Q = typename SqOp<T>::Q;
     constexpr int NC = sq_consumers<T, KT>();
     constexpr int NTH = sq_threads<T, KT>();
     constexpr int NL = TL::NL;
-    constexpr int KTM = DH / 16;
     extern __shared__ uint32_t lds[];
     const int g = h_q / h_k;
     const int lane = threadIdx.x & 63;
@@ -256,6 +359,22 @@ __global__ __launch_bounds__((sq_threads<T, KT>()), 1) void sparq_topm(
     const int wbeg = wr * per;
     const int wend = wbeg + per < nwork ? wbeg + per : nwork;
     if (wbeg >= wend) return;   // uniform over the workgroup
+    if (producer && wave == 0) {
+        // The row whose chunk 0 is item bkh nchunk of this range has its
+        // set-up outputs (qm, the dims) written by this workgroup. A row with
+        // no positions (L_b = 0) has no item to scan, so its outputs are
+        // written here, the tables being rewritten before any item uses them.
+        for (int bkh = (wbeg + nchunk - 1) / nchunk; bkh * nchunk < wend; ++bkh) {
+            const int b = bkh / h_k;
+            if (clamp_len(lens[b], S_max) > 0) continue;   // uniform
+            const int64_t qrow = (int64_t)(b * h_q + (bkh - b * h_k) * g) * DH;
+            Q qs[KT];
+            sq_row_setup<T, DH, KT>((const glb<T>*)(q + qrow), g, r, RP, lane, (lds_i32*)dtab,
+                                    (lds_f32*)itab, qs, true, (glb<float>*)(qm + qrow),
+                                    (glb<int32_t>*)(dims_out ? dims_out + (int64_t)bkh * r
+                                                             : nullptr));
+        }
+    }
     ListSink sink;
     sink.base = (uint64_t)wbeg * g * kScanChunk;
     sink.pool = tm.cand + sink.base;
@@ -276,20 +395,14 @@ __global__ __launch_bounds__((sq_threads<T, KT>()), 1) void sparq_topm(
         if (threadIdx.x == 64 * kWaves) cursor[0] = cursor[1] = 0u;
     }
 
-    // producer state: four sub-tiles in flight (one per 64-position step),
-    // their accumulators, and the query operand of the current slice
+    // producer state: four sub-tiles in flight (one per 64-position step) and
+    // their accumulators, declared per row (so they are not live across the
+    // row's set-up), and the query operand of the row.
     // Loads are unconditional (pieces past L or of pad dims read an in-bounds
     // address) and masked when written to the tile: a load whose destination
     // could also be written by another path would make the compiler wait for
     // it on the spot.
-    u32x4 sr[4][NL];
-    uint32_t vm[4];   // valid pieces of each stage
-    f32x4 acc[4][4];
-#pragma unroll
-    for (int s = 0; s < 4; ++s)
-#pragma unroll
-        for (int nb = 0; nb < 4; ++nb) acc[s][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
-    Q qk[KT];         // the row's query operand, one per slice (loaded once per row)
+    Q qk[KT];         // the row's query operand, one per slice
     const int hd = lane & 15;
     auto ktb = [&](const Item<T>& it) { return kt + (int64_t)it.bkh * DH * S_max; };
     auto load = [&](u32x4 (&dst)[NL], uint32_t& valid, const Item<T>& it, int slice, int st) {
@@ -308,9 +421,6 @@ __global__ __launch_bounds__((sq_threads<T, KT>()), 1) void sparq_topm(
             dst[h] = *reinterpret_cast<const u32x4*>(base + (ok ? pos : 0));
         }
         valid = m;
-    };
-    auto qop_of = [&](const Item<T>& it, int slice) {
-        return qop[((int64_t)it.bkh * KTM + slice) * 64 + lane];
     };
     lds_barrier();
 
@@ -339,13 +449,23 @@ __global__ __launch_bounds__((sq_threads<T, KT>()), 1) void sparq_topm(
 #pragma unroll 1
         while (w < wend) {
             const int row = cur.bkh;
-            // the row's dims and 1 / tau into this wave's tables (through LDS, so
-            // that no register of the item loop waits on these loads), its query
-            // operand, and the first item's first slice
-            for (int c = lane; c < RP; c += 64) dtab[c] = dims[(int64_t)row * RP + c];
-            if (lane < 16) itab[lane] = lane < g ? inv_tau[cur.b * h_q + cur.kh * g + lane] : 0.f;
+            // the row's Step 1 set-up (dims and 1 / tau into this wave's tables,
+            // the query operand), then the first item's first slice; the row's
+            // first chunk is scanned by exactly one workgroup, whose wave 0
+            // writes qm and the dims
+            const int64_t qrow = (int64_t)(cur.b * h_q + cur.kh * g) * DH;
+            sq_row_setup<T, DH, KT>((const glb<T>*)(q + qrow), g, r, RP, lane, (lds_i32*)dtab,
+                                    (lds_f32*)itab, qk, cur.chunk == 0 && wave == 0,
+                                    (glb<float>*)(qm + qrow),
+                                    (glb<int32_t>*)(dims_out ? dims_out + (int64_t)row * r
+                                                             : nullptr));
+            u32x4 sr[4][NL];
+            uint32_t vm[4];   // valid pieces of each stage
+            f32x4 acc[4][4];
 #pragma unroll
-            for (int sl = 0; sl < KT; ++sl) qk[sl] = qop_of(cur, sl);
+            for (int s = 0; s < 4; ++s)
+#pragma unroll
+                for (int nb = 0; nb < 4; ++nb) acc[s][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int s = 0; s < 4; ++s) load(sr[s], vm[s], cur, 0, s);
             // inner loop: the row's items; each one's last slice loads the next's first
@@ -435,9 +555,9 @@ __global__ __launch_bounds__((sq_threads<T, KT>()), 1) void sparq_topm(
 }
 
 template <typename T, int DH, int KT>
-hipError_t go_sparq_scan(const void* kt, const int32_t* lens, const TopmOut& tm, const SparqWs& sw,
-                         int h_q, int h_k, int64_t S_max, int nchunk, int nwork, int RP, int local,
-                         hipStream_t st) {
+hipError_t go_sparq_scan(const void* q, const void* kt, const int32_t* lens, const TopmOut& tm,
+                         const SparqWs& sw, int h_q, int h_k, int64_t S_max, int nchunk, int nwork,
+                         int r, int RP, int local, int32_t* dims_out, hipStream_t st) {
     auto kern = &sparq_topm<T, DH, KT>;
     const size_t lds = kTopmLdsBytes;
     static_assert(sq_lds_words<T, DH>(16) * 4 + 8 * 1024 <= kTopmLdsBytes, "staging area too small");
@@ -448,9 +568,8 @@ hipError_t go_sparq_scan(const void* kt, const int32_t* lens, const TopmOut& tm,
     constexpr int nth = sq_threads<T, KT>();
     const int grid = resident_grid(kern, nth, lds, nwork);
     hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(nth), lds, st, (const T*)kt, lens,
-                       h_q, h_k, S_max, nchunk, nwork, RP, local, sw.dims,
-                       reinterpret_cast<const typename SqOp<T>::Q*>(sw.qop), sw.inv_tau, tm,
-                       (uint32_t)lds);
+                       h_q, h_k, S_max, nchunk, nwork, RP, local, (const T*)q, r, sw.qm,
+                       dims_out, tm, (uint32_t)lds);
     return hipGetLastError();
 }
 
@@ -461,16 +580,10 @@ hipError_t go_sparq(const void* q, const void* kt, const int32_t* lens, const To
     const int nchunk = (int)((S_max + kScanChunk - 1) / kScanChunk);
     const int nwork = B * h_k * nchunk;
     const int RP = (int)round_up(r, 16);
-    hipLaunchKernelGGL((sparq_prep<T, DH>), dim3((unsigned)(B * h_k)), dim3(kPrepThreads), 0, st,
-                       (const T*)q, h_q, h_k, r, RP, sw.dims,
-                       reinterpret_cast<typename SqOp<T>::Q*>(sw.qop), sw.inv_tau, sw.qm,
-                       dims_out);
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
 #define SAGA_SQ(KT)                                                                                \
     case KT:                                                                                       \
         return go_sparq_scan<T, DH, (KT <= DH / 16 ? KT : DH / 16)>(                               \
-            kt, lens, tm, sw, h_q, h_k, S_max, nchunk, nwork, RP, local, st);
+            q, kt, lens, tm, sw, h_q, h_k, S_max, nchunk, nwork, r, RP, local, dims_out, st);
     switch (RP / 16) {
         SAGA_SQ(1) SAGA_SQ(2) SAGA_SQ(3) SAGA_SQ(4) SAGA_SQ(5) SAGA_SQ(6) SAGA_SQ(7) SAGA_SQ(8)
         default: return hipErrorInvalidValue;
