@@ -233,9 +233,10 @@ saga_status saga_atopn_attn(const void* q, const void* k_cache, const void* v_ca
  *   idx_out   nullable, int32 [B][h_q][N]: the kept positions, ascending, -1 pad.
  *   alpha_out nullable, fp32 [B][h_q].
  *   dims_out  nullable, int32 [B][h_k][r]: the kept dims, ascending.
- * Two kernels on `stream` (the set-up of the dims and temperatures, then the
- * scan of the kept columns into candidate lists), then one dispatch per row
- * for selection, exact rescoring and the value gather. The workspace is
+ * Two dispatches on `stream`: the scan of the kept columns into candidate
+ * lists (each of its workgroups derives the dims and temperatures of the rows
+ * it scans), then one dispatch per row for selection, exact rescoring and the
+ * value gather. The workspace is
  * saga_sparq_workspace_size bytes (256-byte aligned). A row with L_b = 0
  * gets out = 0 and alpha = 0. SAGA_ERR_INVALID_ARG: a null required pointer,
  * r or local out of range, q / k_cache / kt_cache / v_cache not 16-byte
