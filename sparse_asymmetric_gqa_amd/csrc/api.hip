@@ -48,7 +48,7 @@ Workspace carve(void* base, int B, int h_q, int h_k, int d, int N, int64_t S_max
         }
         if (sq) sq->qm = reinterpret_cast<float*>(take(rows * (size_t)d * sizeof(float)));
     } else {
-        const size_t nsplit = (size_t)dense_nsplit(S_max, h_q / h_k);
+        const size_t nsplit = (size_t)dense_nsplit(B, h_k, S_max, h_q / h_k);
         w.part = reinterpret_cast<float*>(take(rows * nsplit * (size_t)(d + 2) * sizeof(float)));
     }
     w.bytes = off;

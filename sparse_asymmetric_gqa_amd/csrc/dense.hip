@@ -29,8 +29,13 @@ namespace {
 constexpr int kDenseThreads = 64 * kWaves;
 constexpr int kDenseMaxHeadsPerPass = 8;   // query heads accumulated per pass over V
 
-// positions per work item: the chunk's logits of 16 NHT heads stay in LDS
-__host__ __device__ constexpr int dense_chunk_for(int nht) { return nht == 1 ? 512 : 256; }
+// Positions per work item (the chunk's logits of 16 NHT heads stay in LDS):
+// key groups of up to 16 heads take the longest chunk of 1024, 512 or 256
+// positions that still gives at least kDenseMinItems work items (fewer,
+// longer items move the same bytes with less per-item set-up and fewer
+// partials to merge; short calls need the items to spread over the CUs);
+// wider groups take 256.
+constexpr int kDenseMinItems = 128;
 
 template <typename T, int DH>
 constexpr bool dense_xp() { return sizeof(T) == 2; }
@@ -90,7 +95,7 @@ __device__ inline float wave_fmax(float x) {
     return x;
 }
 
-template <typename T, int DH, int NHT>
+template <typename T, int DH, int NHT, int C>
 __global__ __launch_bounds__(kDenseThreads) void dense_attn(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const int32_t* __restrict__ lens, float* __restrict__ part, int h_q, int h_k, int h_v,
@@ -98,7 +103,6 @@ __global__ __launch_bounds__(kDenseThreads) void dense_attn(
     constexpr bool XP = dense_xp<T, DH>();
     using S = Streamer<T, DH, NHT, XP>;
     constexpr int NS = S::NS;
-    constexpr int C = dense_chunk_for(NHT);
     constexpr int nst = C / S::STAGE;
     static_assert(C % S::STAGE == 0 && nst % NS == 0 && nst >= 2 * NS,
                   "a chunk must span at least two rounds of stages");
@@ -349,13 +353,13 @@ __global__ __launch_bounds__(kDenseThreads) void dense_attn(
             float* s = sc + u * SR;
             float mx = -__builtin_inff();
     #pragma unroll
-            for (int t = lane; t < C; t += 64) mx = fmaxf(mx, s[t]);
+            for (int j = 0; j < C / 64; ++j) mx = fmaxf(mx, s[lane + 64 * j]);
             mx = wave_fmax(mx);   // finite: row 0 of the chunk is live
             float l = 0.f;
     #pragma unroll
-            for (int t = lane; t < C; t += 64) {
-                const float p = __expf(s[t] - mx);
-                s[t] = p;
+            for (int j = 0; j < C / 64; ++j) {
+                const float p = __expf(s[lane + 64 * j] - mx);
+                s[lane + 64 * j] = p;
                 l += p;
             }
             l = wave_fsum(l);
@@ -472,16 +476,15 @@ __global__ __launch_bounds__(DH) void dense_merge(const float* __restrict__ part
     out[(int64_t)row * DH + c] = den > 0.f ? num / den : 0.f;
 }
 
-template <typename T, int DH, int NHT>
+template <typename T, int DH, int NHT, int C>
 hipError_t go_dense(const void* q, const void* k, const void* v, const int32_t* lens, float* part,
                     int B, int h_q, int h_k, int h_v, int64_t S_max, hipStream_t st) {
-    constexpr int C = dense_chunk_for(NHT);
     const int g = h_q / h_k;
-    const int nchunk = dense_nsplit(S_max, g);
+    const int nchunk = (int)((S_max + C - 1) / C);
     const size_t lds = dense_logit_bytes(g, C) + dense_aux_bytes<T, DH>();
     static_assert(16 * NHT * C * sizeof(float) + dense_aux_bytes<T, DH>() <= 160 * 1024,
                   "logits of 16 NHT heads must fit the LDS");
-    auto kern = &dense_attn<T, DH, NHT>;
+    auto kern = &dense_attn<T, DH, NHT, C>;
     if (lds > 64 * 1024) {
         const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                                  hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -500,16 +503,29 @@ hipError_t go_dense_g(const void* q, const void* k, const void* v, const int32_t
                       float* part, int B, int h_q, int h_k, int h_v, int64_t S_max,
                       hipStream_t st) {
     const int g = h_q / h_k;
-    if (g <= 16) return go_dense<T, DH, 1>(q, k, v, lens, part, B, h_q, h_k, h_v, S_max, st);
-    if (g <= 32) return go_dense<T, DH, 2>(q, k, v, lens, part, B, h_q, h_k, h_v, S_max, st);
-    return go_dense<T, DH, 4>(q, k, v, lens, part, B, h_q, h_k, h_v, S_max, st);
+    if (g <= 16) {
+        const int C = dense_chunk(B, h_k, S_max, g);
+        if (C == 1024)
+            return go_dense<T, DH, 1, 1024>(q, k, v, lens, part, B, h_q, h_k, h_v, S_max, st);
+        if (C == 512)
+            return go_dense<T, DH, 1, 512>(q, k, v, lens, part, B, h_q, h_k, h_v, S_max, st);
+        return go_dense<T, DH, 1, 256>(q, k, v, lens, part, B, h_q, h_k, h_v, S_max, st);
+    }
+    if (g <= 32) return go_dense<T, DH, 2, 256>(q, k, v, lens, part, B, h_q, h_k, h_v, S_max, st);
+    return go_dense<T, DH, 4, 256>(q, k, v, lens, part, B, h_q, h_k, h_v, S_max, st);
 }
 
 }  // namespace
 
-int dense_chunk(int g) { return dense_chunk_for(g <= 16 ? 1 : g <= 32 ? 2 : 4); }
-int dense_nsplit(int64_t S_max, int g) {
-    const int C = dense_chunk(g);
+int dense_chunk(int B, int h_k, int64_t S_max, int g) {
+    if (g > 16) return 256;
+    const int64_t rows = (int64_t)B * h_k;
+    for (int C = 1024; C > 256; C /= 2)
+        if (rows * ((S_max + C - 1) / C) >= kDenseMinItems) return C;
+    return 256;
+}
+int dense_nsplit(int B, int h_k, int64_t S_max, int g) {
+    const int C = dense_chunk(B, h_k, S_max, g);
     return (int)((S_max + C - 1) / C);
 }
 
@@ -525,8 +541,8 @@ hipError_t launch_dense_attn(const void* q, const void* k, const void* v, const 
                     : go_dense_g<float, 128>(q, k, v, lens, part, B, h_q, h_k, h_v, S_max, st);
     if (e != hipSuccess) return e;
     const int g = h_q / h_k;
-    const int nchunk = dense_nsplit(S_max, g);
-    const int C = dense_chunk(g);
+    const int nchunk = dense_nsplit(B, h_k, S_max, g);
+    const int C = dense_chunk(B, h_k, S_max, g);
     if (d == 64)
         hipLaunchKernelGGL((dense_merge<64>), dim3((unsigned)(B * h_q)), dim3(64), 0, st, part,
                            nchunk, C, lens, S_max, out, h_q);

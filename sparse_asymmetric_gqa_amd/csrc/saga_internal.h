@@ -82,10 +82,11 @@ Workspace carve(void* base, int B, int h_q, int h_k, int d, int N, int64_t S_max
 Workspace carve_decode(void* base, int B, int h_q, int h_k, int d, int N, int64_t S_max);
 Workspace carve_atopn(void* base, int B, int h_q, int h_k, int d, int N, int64_t S_max);
 
-// Dense attention: positions per work item for a key group of g query heads,
-// and chunks (partials) per (b, i) row.
-int dense_chunk(int g);
-int dense_nsplit(int64_t S_max, int g);   // ceil(S_max / dense_chunk(g))
+// Dense attention: positions per work item for a call's shape (B rows of h_k
+// key heads, key groups of g query heads), and chunks (partials) per (b, i)
+// row.
+int dense_chunk(int B, int h_k, int64_t S_max, int g);
+int dense_nsplit(int B, int h_k, int64_t S_max, int g);   // ceil(S_max / dense_chunk(...))
 
 // Candidate lists published by the top-M K-scan. The workgroup that takes
 // work items [w0, w1) packs the lists of their heads, in any order, from pool
