@@ -105,9 +105,12 @@ def test_workspace_sizes():
         assert ws(B, h_q, args[2], args[3], d, N + 300, S, 1) >= n
         assert ws(B, h_q, args[2], args[3], d, N, S + 5000, 1) >= n
     dw = saga.saga_dense_workspace_size
-    # one (m, l, acc[d]) partial per row and chunk of 512 positions (key groups
-    # of up to 16 heads) or 256 positions (wider key groups)
-    assert dw(64, 12, 2, 2, 128, 32768, 1) >= 64 * 12 * 64 * 130 * 4
+    # one (m, l, acc[d]) partial per row and chunk: 1024 positions where that
+    # still gives 128 (b, key head, chunk) items, else 512 or 256 (key groups
+    # of up to 16 heads); 256 positions for wider key groups
+    assert dw(64, 12, 2, 2, 128, 32768, 1) >= 64 * 12 * 32 * 130 * 4
+    assert dw(1, 12, 2, 2, 128, 32768, 1) >= 12 * 64 * 130 * 4      # 512: 128 items
+    assert dw(1, 12, 1, 2, 128, 8192, 1) >= 12 * 32 * 130 * 4       # 256: 32 items
     assert dw(1, 64, 1, 2, 64, 1000, 1) >= 64 * 4 * 66 * 4
     assert dw(1, 4, 1, 2, 64, 1025, 0) >= dw(1, 4, 1, 2, 64, 1000, 0)
     assert dw(1, 4, 1, 2, 72, 10, 1) == 0
