@@ -29,13 +29,15 @@ namespace {
 constexpr int kDenseThreads = 64 * kWaves;
 constexpr int kDenseMaxHeadsPerPass = 8;   // query heads accumulated per pass over V
 
-// Positions per work item (the chunk's logits of 16 NHT heads stay in LDS):
-// key groups of up to 16 heads take the longest chunk of 1024, 512 or 256
-// positions that still gives at least kDenseMinItems work items (fewer,
-// longer items move the same bytes with less per-item set-up and fewer
-// partials to merge; short calls need the items to spread over the CUs);
-// wider groups take 256.
-constexpr int kDenseMinItems = 128;
+// Positions per work item (the chunk's logits of 16 NHT heads stay in LDS).
+// Key groups of up to 16 heads take a chunk of 1024, 512 or 256 positions:
+// among those that leave at most kDenseMaxParts partials per row for the
+// merge (one workgroup per row reads them), the
+// longest that still gives one work item per CU, else the shortest. Longer
+// items move the same bytes with less per-item set-up; short calls need
+// enough items to occupy the CUs. Wider groups take 256.
+constexpr int kDenseMinItems = 256;   // the CUs of an MI355X
+constexpr int kDenseMaxParts = 128;
 
 template <typename T, int DH>
 constexpr bool dense_xp() { return sizeof(T) == 2; }
@@ -450,30 +452,55 @@ __global__ __launch_bounds__(kDenseThreads) void dense_attn(
 
 // out[row] = sum_s acc_s e^(m_s - M) / sum_s l_s e^(m_s - M) over the live
 // chunks s of the row (every live chunk has l >= 1: its largest logit has
-// weight 1); a row with no live chunk (L_b = 0) gets 0.
+// weight 1); a row with no live chunk (L_b = 0) gets 0. One workgroup per
+// row: kMergeGroups groups of DH threads (one per column) take every
+// kMergeGroups-th chunk each, so a long row's partials are read with that
+// many loads in flight per column; the groups' sums, each relative to the
+// group's own largest m, are then combined in group order.
+constexpr int kMergeGroups = 8;
 template <int DH>
-__global__ __launch_bounds__(DH) void dense_merge(const float* __restrict__ part, int nchunk,
-                                                 int C, const int32_t* __restrict__ lens,
-                                                 int64_t S_max, float* __restrict__ out,
-                                                 int h_q) {
+__global__ __launch_bounds__(DH * kMergeGroups) void dense_merge(
+    const float* __restrict__ part, int nchunk, int C, const int32_t* __restrict__ lens,
+    int64_t S_max, float* __restrict__ out, int h_q) {
+    constexpr int G = kMergeGroups;
+    __shared__ float s_m[G], s_den[G], s_num[G][DH];
     const int row = blockIdx.x;
-    const int c = threadIdx.x;
+    const int c = threadIdx.x % DH;
+    const int grp = threadIdx.x / DH;
     const int64_t L = clamp_len(lens[row / h_q], S_max);
     const int64_t live = (L + C - 1) / C;
     const int ns = (int)(live < nchunk ? live : nchunk);
     const float* p = part + (int64_t)row * nchunk * (DH + 2);
-    float M = -__builtin_inff();
-#pragma unroll 8
-    for (int s = 0; s < ns; ++s) M = fmaxf(M, p[s * (DH + 2)]);
+    float m = -__builtin_inff();
+#pragma unroll 4
+    for (int s = grp; s < ns; s += G) m = fmaxf(m, p[s * (DH + 2)]);
     float num = 0.f, den = 0.f;
-#pragma unroll 8
-    for (int s = 0; s < ns; ++s) {
+#pragma unroll 4
+    for (int s = grp; s < ns; s += G) {
         const float* r = p + s * (DH + 2);
-        const float f = __expf(r[0] - M);
+        const float f = __expf(r[0] - m);
         den += r[1] * f;
         num += r[2 + c] * f;
     }
-    out[(int64_t)row * DH + c] = den > 0.f ? num / den : 0.f;
+    if (c == 0) {
+        s_m[grp] = m;
+        s_den[grp] = den;
+    }
+    s_num[grp][c] = num;
+    __syncthreads();
+    if (grp != 0) return;
+    float M = -__builtin_inff();
+#pragma unroll
+    for (int j = 0; j < G; ++j) M = fmaxf(M, s_m[j]);
+    float n_ = 0.f, d_ = 0.f;
+#pragma unroll
+    for (int j = 0; j < G; ++j)
+        if (s_m[j] > -__builtin_inff()) {   // a group with no chunk adds nothing
+            const float f = __expf(s_m[j] - M);
+            d_ += s_den[j] * f;
+            n_ += s_num[j][c] * f;
+        }
+    out[(int64_t)row * DH + c] = d_ > 0.f ? n_ / d_ : 0.f;
 }
 
 template <typename T, int DH, int NHT, int C>
@@ -520,9 +547,14 @@ hipError_t go_dense_g(const void* q, const void* k, const void* v, const int32_t
 int dense_chunk(int B, int h_k, int64_t S_max, int g) {
     if (g > 16) return 256;
     const int64_t rows = (int64_t)B * h_k;
-    for (int C = 1024; C > 256; C /= 2)
-        if (rows * ((S_max + C - 1) / C) >= kDenseMinItems) return C;
-    return 256;
+    int shortest = 1024;   // when even 1024 leaves more partials than the cap
+    for (int C = 1024; C >= 256; C /= 2) {
+        const int64_t parts = (S_max + C - 1) / C;
+        if (parts > kDenseMaxParts) break;
+        if (rows * parts >= kDenseMinItems) return C;
+        shortest = C;
+    }
+    return shortest;
 }
 int dense_nsplit(int B, int h_k, int64_t S_max, int g) {
     const int C = dense_chunk(B, h_k, S_max, g);
@@ -544,10 +576,12 @@ hipError_t launch_dense_attn(const void* q, const void* k, const void* v, const 
     const int nchunk = dense_nsplit(B, h_k, S_max, g);
     const int C = dense_chunk(B, h_k, S_max, g);
     if (d == 64)
-        hipLaunchKernelGGL((dense_merge<64>), dim3((unsigned)(B * h_q)), dim3(64), 0, st, part,
+        hipLaunchKernelGGL((dense_merge<64>), dim3((unsigned)(B * h_q)),
+                           dim3(64 * kMergeGroups), 0, st, part,
                            nchunk, C, lens, S_max, out, h_q);
     else
-        hipLaunchKernelGGL((dense_merge<128>), dim3((unsigned)(B * h_q)), dim3(128), 0, st, part,
+        hipLaunchKernelGGL((dense_merge<128>), dim3((unsigned)(B * h_q)),
+                           dim3(128 * kMergeGroups), 0, st, part,
                            nchunk, C, lens, S_max, out, h_q);
     return hipGetLastError();
 }
