@@ -148,8 +148,9 @@ saga_status saga_decode_attn_noalloc(const void* q, const void* k_cache, const v
  * Bytes of device workspace saga_dense_attn needs (host only; 0 on invalid
  * arguments): one (max logit, weight sum, weighted value sum[d]) fp32 partial
  * per (b, query head) and chunk of cached positions; logits never go to
- * memory. The chunk is 1024, 512 or 256 positions, the longest that gives at
- * least 128 (b, key head, chunk) items (256 when h_q / h_k > 16), so the size
+ * memory. The chunk is 1024, 512 or 256 positions (256 when h_q / h_k > 16):
+ * among those leaving at most 128 chunks per row, the longest that gives at
+ * least 256 (b, key head, chunk) items, else the shortest; so the size
  * depends on B and h_k as well as S_max.
  */
 size_t saga_dense_workspace_size(int B, int h_q, int h_k, int h_v, int d, int64_t S_max,
