@@ -90,6 +90,11 @@ DENSE_SMALL = [
     (1, 32, 1, 4, 64, 900, "bf16", [900]),              # key group of 32 (256-position chunks)
     (1, 64, 1, 2, 128, 600, "f32", [600]),              # key group of 64, value group of 32
     (2, 16, 1, 8, 64, 1024, "bf16", [1024, 0]),         # empty row -> 0
+    # shapes whose item count picks the longer chunks (1024 and 512 positions)
+    (8, 8, 4, 4, 128, 8500, "bf16", [8500, 5000, 1025, 1024, 1023, 1, 0, 3000]),
+    (2, 4, 2, 2, 128, 33000, "bf16", [33000, 16385]),   # 512 positions, 65 partials per row
+    (16, 4, 1, 2, 64, 17000, "f32",
+     [17000, 16999, 9000, 1024, 1025, 2048, 1, 511, 513, 4000, 17000, 300, 12000, 7, 15000, 0]),
 ]
 
 
