@@ -303,3 +303,44 @@ def test_noalloc_entry_checks_on_host():
     assert big > saga.saga_noalloc_scratch_bytes()
     assert call(a5=64, a6=12, a7=1, a8=2, a9=128, a10=1024, a12=1 << 20) == \
         saga.SAGA_ERR_TOO_LARGE
+
+
+def test_dense_chunk_rule():
+    # The dense workspace holds B h_q (d + 2) floats per chunk of the row, so
+    # its size gives the chunk count the library picked. The rule: among the
+    # chunk lengths 1024, 512 and 256 that leave at most 128 chunks per row,
+    # the longest giving at least 256 (b, key head, chunk) items, else the
+    # shortest of them (1024 when even that leaves more than 128); key groups
+    # wider than 16 always take 256.
+    dw = saga.saga_dense_workspace_size
+
+    def expected(B, h_k, S, g):
+        if g > 16:
+            return 256
+        shortest = 1024
+        for C in (1024, 512, 256):
+            parts = -(-S // C)
+            if parts > 128:
+                break
+            if B * h_k * parts >= 256:
+                return C
+            shortest = C
+        return shortest
+
+    rng = __import__("random").Random(5)
+    shapes = [(1, 12, 1, 2, 8192), (1, 12, 2, 2, 32768), (16, 12, 1, 2, 8192),
+              (64, 12, 2, 2, 32768), (1, 12, 1, 2, 131072), (2, 64, 1, 2, 5000)]
+    for _ in range(60):
+        h_k = rng.choice([1, 2, 4])
+        g = rng.choice([1, 2, 4, 8, 16, 32])
+        shapes.append((rng.choice([1, 2, 3, 4, 8, 16, 64]), h_k * g, h_k,
+                       h_k * rng.choice([1, 2]), rng.randint(1, 140000)))
+    for B, h_q, h_k, h_v, S in shapes:
+        if h_q % h_v or h_q // h_v > 64:
+            continue
+        d = 128
+        n = dw(B, h_q, h_k, h_v, d, S, 1)
+        C = expected(B, h_k, S, h_q // h_k)
+        need = B * h_q * (-(-S // C)) * (d + 2) * 4
+        # the partials are the dense workspace's only area (256-byte aligned)
+        assert n == (need + 255) // 256 * 256, (B, h_q, h_k, h_v, S, C, n, need)
