@@ -380,9 +380,10 @@ hipError_t launch_kscan_topm(const void* q, const void* k, const int32_t* lens, 
                              int B, int h_q, int h_k, int d, int64_t S_max, bool bf16,
                              hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
 #define SAGA_TM(T, D)                                                                       \
-    (tm.chunk == 256 ? go_topm<T, D, 256>(q, k, lens, tm, B, h_q, h_k, S_max, st, ev0, ev1)   \
-                     : go_topm<T, D, kScanChunk>(q, k, lens, tm, B, h_q, h_k, S_max, st, ev0, ev1))
-    if (tm.chunk != 256 && tm.chunk != kScanChunk) return hipErrorInvalidValue;
+    (tm.chunk == 256   ? go_topm<T, D, 256>(q, k, lens, tm, B, h_q, h_k, S_max, st, ev0, ev1)  \
+     : tm.chunk == 512 ? go_topm<T, D, 512>(q, k, lens, tm, B, h_q, h_k, S_max, st, ev0, ev1)  \
+                       : go_topm<T, D, kScanChunk>(q, k, lens, tm, B, h_q, h_k, S_max, st, ev0, ev1))
+    if (tm.chunk != 256 && tm.chunk != 512 && tm.chunk != kScanChunk) return hipErrorInvalidValue;
     if (bf16) return d == 64 ? SAGA_TM(uint16_t, 64) : SAGA_TM(uint16_t, 128);
     return d == 64 ? SAGA_TM(float, 64) : SAGA_TM(float, 128);
 #undef SAGA_TM

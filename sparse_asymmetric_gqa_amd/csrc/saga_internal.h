@@ -48,12 +48,17 @@ inline int num_chunks(int64_t S_max, int chunk = kScanChunk) {
     return (int)((S_max + chunk - 1) / chunk);
 }
 
-// Positions per work item of the top-M K-scan: 1024, or 256 when a call has
-// fewer than 256 items of 1024 positions (too few to occupy the CUs) and its
-// rows fit in 256 chunks of 256.
+// Positions per work item of the top-M K-scan: 1024 when that gives at
+// least 256 items (one per CU); else 512 where that does, with rows of at
+// most 256 chunks (the union select's fast path); else 256 for rows of up to
+// 64 Ki positions, 512 up to 128 Ki. Shorter items fill the CUs of a short
+// call; 512 rather than 256 keeps the candidate lists shorter where it can.
 inline int topm_chunk(int B, int h_k, int64_t S_max) {
-    const int64_t items = (int64_t)B * h_k * num_chunks(S_max);
-    return (items < 256 && S_max <= 256 * 256) ? 256 : kScanChunk;
+    const int64_t rows = (int64_t)B * h_k;
+    if (rows * num_chunks(S_max) >= 256) return kScanChunk;
+    if (S_max <= 256 * 512 && rows * num_chunks(S_max, 512) >= 256) return 512;
+    if (S_max <= 256 * 256) return 256;
+    return S_max <= 256 * 512 ? 512 : kScanChunk;
 }
 
 // Workgroups per (b, i) row of the fused select + value gather: rows are
@@ -100,7 +105,7 @@ struct TopmOut {
     uint4* meta;       // [B*h_q][nchunk]
     int N;             // the M of each chunk's list is sized for this N
     float2* stat;      // nullable: [B*h_q][nchunk] {max logit, sum of exp(logit - max)}
-    int chunk;         // positions per work item (kScanChunk or 256)
+    int chunk;         // positions per work item (kScanChunk, 512 or 256)
     int32_t* zero;     // nullable: nzero ints the K-scan clears before anything else
     int nzero;
 };

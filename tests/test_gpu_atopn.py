@@ -101,6 +101,7 @@ SHAPES = [
     (3, 12, 1, 2, 128, 5000, 300, "bf16", True),
     (2, 16, 1, 8, 64, 4100, 256, "bf16", False),
     (1, 6, 2, 3, 64, 777, 40, "bf16", False),       # a value head spanning two key heads
+    (4, 12, 1, 2, 128, 32768, 1024, "bf16", True),  # 512-position K-scan items
 ]
 
 

@@ -156,6 +156,10 @@ SMALL_BATCH = [
     (8, 12, 1, 2, 128, 3000, 512, True),     # 96 rows: 5 parts
     (7, 12, 1, 2, 128, 1500, 200, False),    # 84 rows: 6 parts
     (6, 12, 1, 2, 64, 4000, 700, False),     # 72 rows: 7 parts
+    # 512-position K-scan items: 1024-position ones would leave CUs idle, and
+    # rows longer than 64 Ki positions do not fit 256 items of 256
+    (4, 12, 1, 2, 128, 32768, 1024, True),
+    (1, 12, 1, 2, 128, 100000, 1024, True),
 ]
 
 
