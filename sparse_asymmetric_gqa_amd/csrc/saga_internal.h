@@ -67,7 +67,7 @@ inline int topm_chunk(int B, int h_k, int64_t S_max) {
 constexpr int kMaxSplit = 8;
 inline int gather_split(int B, int h_q) {
     const int rows = B * h_q;
-    const int p = rows >= 512 ? 1 : 512 / rows;
+    const int p = rows >= 256 ? 1 : 256 / rows;
     return p < kMaxSplit ? p : kMaxSplit;
 }
 

@@ -150,12 +150,13 @@ SMALL_BATCH = [
     (2, 12, 1, 2, 128, 40000, 2048, True),
     (1, 4, 1, 2, 64, 300, 64, False),
     (3, 16, 1, 8, 64, 5000, 512, True),
-    # rows that give every split count from 3 to 7 (512 / rows parts per row)
-    (10, 16, 1, 2, 64, 2000, 256, True),     # 160 rows: 3 parts
-    (8, 16, 2, 4, 64, 2500, 300, True),      # 128 rows: 4 parts
-    (8, 12, 1, 2, 128, 3000, 512, True),     # 96 rows: 5 parts
-    (7, 12, 1, 2, 128, 1500, 200, False),    # 84 rows: 6 parts
-    (6, 12, 1, 2, 64, 4000, 700, False),     # 72 rows: 7 parts
+    # rows that give every split count from 2 to 7 (256 / rows parts per row)
+    (8, 12, 1, 2, 128, 3000, 512, True),     # 96 rows: 2 parts
+    (5, 16, 1, 2, 64, 2000, 256, True),      # 80 rows: 3 parts
+    (4, 16, 2, 4, 64, 2500, 300, True),      # 64 rows: 4 parts
+    (4, 12, 1, 2, 128, 3000, 512, True),     # 48 rows: 5 parts
+    (5, 8, 1, 2, 128, 1500, 200, False),     # 40 rows: 6 parts
+    (3, 12, 1, 2, 64, 4000, 700, False),     # 36 rows: 7 parts
     # 512-position K-scan items: 1024-position ones would leave CUs idle, and
     # rows longer than 64 Ki positions do not fit 256 items of 256
     (4, 12, 1, 2, 128, 32768, 1024, True),
