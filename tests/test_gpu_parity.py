@@ -429,6 +429,37 @@ def test_concentrated_attention(name):
     assert counts[1] == 0
 
 
+@pytest.mark.parametrize("B", [4, 1])
+def test_concentrated_attention_small_batch(B):
+    # the same sink and recency structure at batch sizes whose K-scan items are
+    # 512 (B = 4) or 256 (B = 1) positions, one item per workgroup: the window's
+    # chunks have no earlier chunk of their row to lend a floor, so heads may
+    # recompute chunks (flag 2), but the kept sets and outputs match the oracle
+    from dataclasses import replace
+    case = replace(synth.CASES["qwen25_1p5b_b64_32k"], B=B, name=f"recency_b{B}",
+                   structure="recency_sink")
+    x = synth.make_inputs(case)
+    dx = to_device(x)
+    _say(f"[concentrated] small batch B={B}")
+    ws = saga.new_workspace(saga.workspace_size(dx["q"], dx["k"], dx["v"], dx["seq_lens"],
+                                                case.N), "cuda")
+    idx = torch.empty((case.B, case.h_q, case.N), dtype=torch.int32, device="cuda")
+    out = saga.decode_attn(dx["q"], dx["k"], dx["v"], dx["seq_lens"], case.N, workspace=ws,
+                           idx_out=idx)
+    torch.cuda.synchronize()
+    flags = _fallback_flags(dx, ws, case, case.N)
+    pairs = all_pairs(case.B, case.h_q)
+    ref = oracle.topn_attn(x["q"], x["k"], x["v"], x["seq_lens"], case.N, pairs=pairs)
+    g_idx = idx.reshape(-1, case.N).cpu().numpy()
+    nbad, ndiff = check_index_sets(g_idx, ref, x, pairs, case.N)
+    err = check_outputs(out.reshape(-1, case.d).cpu().numpy(), g_idx, x, pairs,
+                        tol_for(case.dtype))
+    counts = np.bincount(flags, minlength=3)
+    _say(f"    differing-rows={nbad} sym-diff={ndiff} max|err|={err:.2e} "
+         f"settled={counts[0]} chunk-recompute={counts[2]} full-recompute={counts[1]}")
+    assert counts[1] == 0
+
+
 def test_workloads_report_fallback_rows():
     for name in ("llama32_1b_8to4", "qwen25_1p5b_2to1_ragged", "qwen25_1p5b_b64_32k"):
         case = synth.CASES[name]
